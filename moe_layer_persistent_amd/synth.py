@@ -1,0 +1,253 @@
+"""Seeded synthetic inputs for one MoE decoder layer (batch-1 verify step).
+
+This module is the only code that both the HIP path (tests, bench) and the
+oracle consume.  It holds workload shapes, a seeded random-tensor recipe and
+the NVFP4 *encoder* used to store synthetic expert weights; none of the layer
+arithmetic (norm, projections, RoPE, attention, routing, dequantisation,
+SwiGLU, combine) lives here.
+
+Shapes follow the model the pages describe (orcarouter.ai English post,
+"Where the kernel boundary sits": 62 decoder layers, 46 sliding-window over
+2,048 tokens and 16 global; every token routed to 8 of 256 experts stored in
+4-bit NVFP4, some layers in bf16; a pooler before the experts and an unpooler
+after them; 16 verified tokens per step).  Hidden size, head counts, head_dim,
+pooled and intermediate widths are not printed on the pages; the values below
+are the workload definitions this implementation is measured on.
+
+Recipe (all tensors seeded by (workload id, layer, tensor id[, expert])):
+  * activations x ~ N(0, 1), fp32 [T, hidden]
+  * norm gains gamma ~ N(1, 0.02^2), stored bf16
+  * every weight matrix ~ N(0, 0.02^2): dense ones stored bf16 (round to
+    nearest even), expert matrices either bf16 or NVFP4-encoded (below)
+  * KV history ~ N(0, 1), stored bf16, slots [0, pos); slots >= pos hold
+    N(0, 1) filler that the step must overwrite (written slots) or leave alone
+  * NVFP4 encoding of a matrix w [N, K]: tensor scale ts = amax|w| / (6*448);
+    per 16-element block scale s = E4M3(amax_blk / (6*ts)) rounded to nearest
+    even and clamped to 448; code = E2M1 grid point nearest to w / (s*ts),
+    ties to the even code, saturating at +-6; s == 0 gives code 0.  Two codes
+    per byte, the even k in the low nibble.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Dict, Optional
+
+import torch
+
+NVFP4 = 0
+BF16 = 1
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    wid: int                 # workload id (seed component)
+    name: str
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    pooled: int
+    inter: int               # width of the SwiGLU output (K of the down projection)
+    n_experts: int
+    top_k: int
+    expert_dtype: int        # NVFP4 or BF16
+    n_shards: int            # expert N-dimension shards (1 = whole layer)
+    window: int              # 0 = global attention
+    pos: int                 # tokens already in the KV cache
+    T: int                   # verify tokens in this step
+    n_layers: int = 1
+    fp32_masters: bool = False   # tiny case: weights drawn fp32, device copy bf16
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+    @property
+    def inter_local(self) -> int:      # gate/up rows held by this GPU
+        return self.inter // self.n_shards
+
+    @property
+    def pooled_local(self) -> int:     # down-projection rows held by this GPU
+        return self.pooled // self.n_shards
+
+    @property
+    def qkv_rows(self) -> int:
+        return (self.n_q_heads + 2 * self.n_kv_heads) * self.head_dim
+
+    @property
+    def kv_capacity(self) -> int:
+        return self.pos + 16
+
+    def layer_window(self, layer: int) -> int:
+        """Stack workloads: layer l is global iff l % 4 == 0 (16 of 62)."""
+        if self.n_layers == 1:
+            return self.window
+        return 0 if layer % 4 == 0 else 2048
+
+    def with_(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS: Dict[str, Workload] = {
+    # tiny single layer: the oracle finishes it in well under a second
+    "tiny": Workload(0, "tiny", 256, 4, 1, 64, 128, 256, 32, 4, NVFP4, 1, 0, 128, 1,
+                     fp32_masters=True),
+    # full-width sliding-window layer, NVFP4 experts
+    "swa_fp4": Workload(1, "swa_fp4", 8192, 64, 8, 128, 4096, 4096, 256, 8, NVFP4, 1, 2048, 8192, 16),
+    # full-width global layer with a long history
+    "global_fp4": Workload(2, "global_fp4", 8192, 64, 8, 128, 4096, 4096, 256, 8, NVFP4, 1, 0, 32768, 16),
+    # full-width sliding-window layer, bf16 experts
+    "swa_bf16": Workload(3, "swa_bf16", 8192, 64, 8, 128, 4096, 4096, 256, 8, BF16, 1, 2048, 8192, 16),
+    # one GPU's TP8 share of the 62-layer stack (heads / 8, expert N / 8)
+    "stack_tp8": Workload(4, "stack_tp8", 8192, 8, 1, 128, 4096, 4096, 256, 8, NVFP4, 8, 2048, 4096, 16,
+                          n_layers=62),
+}
+
+# tensor ids (seed components)
+_TID = dict(x=1, gamma1=2, w_qkv=3, w_o=4, gamma2=5, w_router=6, w_pool=7, w_unpool=8,
+            k_cache=9, v_cache=10, w_gate=11, w_up=12, w_down=13, x_shared=14)
+
+
+def seed_of(w: Workload, layer: int, tensor: str, expert: int = -1) -> int:
+    return ((w.wid * 1_000_003 + layer * 1_009 + _TID[tensor]) * 4_099 + (expert + 1)) & 0x7FFF_FFFF_FFFF
+
+
+def _gen(seed: int, device) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    return g
+
+
+def randn(shape, seed: int, device, std: float = 1.0, mean: float = 0.0) -> torch.Tensor:
+    t = torch.randn(shape, generator=_gen(seed, device), device=device, dtype=torch.float32)
+    if std != 1.0:
+        t.mul_(std)
+    if mean != 0.0:
+        t.add_(mean)
+    return t
+
+
+# ---------------------------------------------------------------------------------------------
+# NVFP4 encoder (storage format for synthetic weights; the decoder is what is under test)
+# ---------------------------------------------------------------------------------------------
+_E2M1_GRID = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+_E2M1_MIDS = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+
+
+def encode_nvfp4(w: torch.Tensor):
+    """w fp32 [..., N, K] -> (codes uint8 [..., N, K/2], scales uint8 [..., N, K/16], ts fp32 [...])."""
+    assert w.shape[-1] % 16 == 0
+    lead = w.shape[:-2]
+    N, K = w.shape[-2], w.shape[-1]
+    w = w.float()
+    amax = w.abs().flatten(-2).amax(-1)                                    # [...]
+    ts = (amax / (6.0 * 448.0)).float()
+    ts = torch.where(ts > 0, ts, torch.ones_like(ts))
+    blk = w.reshape(*lead, N, K // 16, 16)
+    bmax = blk.abs().amax(-1)                                               # [..., N, K/16]
+    s = (bmax / (6.0 * ts[..., None, None])).clamp(0.0, 448.0)
+    s8 = s.to(torch.float8_e4m3fn)
+    s_val = s8.float()
+    denom = (s_val * ts[..., None, None])[..., None]                        # [..., N, K/16, 1]
+    q = torch.where(denom > 0, blk / torch.where(denom > 0, denom, torch.ones_like(denom)),
+                    torch.zeros_like(blk))
+    mag = q.abs().clamp(max=6.0)
+    mids = _E2M1_MIDS.to(w.device)
+    lo = torch.bucketize(mag, mids, right=False)       # ties -> lower grid point
+    hi = torch.bucketize(mag, mids, right=True)        # ties -> upper grid point
+    idx = torch.where(lo == hi, lo, torch.where(lo % 2 == 0, lo, hi))
+    code = idx.to(torch.uint8)
+    code = torch.where((q < 0) & (idx > 0), code | 8, code)
+    code = code.reshape(*lead, N, K)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    return packed.contiguous(), s8.view(torch.uint8).contiguous(), ts.contiguous()
+
+
+# ---------------------------------------------------------------------------------------------
+# layer inputs
+# ---------------------------------------------------------------------------------------------
+def make_layer(w: Workload, layer: int = 0, device="cpu", routing: str = "iid",
+               experts: bool = True) -> Dict[str, torch.Tensor]:
+    """All inputs of one layer step as torch tensors on `device`.
+
+    routing="iid": x ~ N(0,1) i.i.d. per token.  routing="shared": x_t = a*z + b*n_t with one
+    seeded z shared by the T tokens, which concentrates routing on fewer distinct experts.
+    """
+    dev = torch.device(device)
+    H, D = w.hidden, w.head_dim
+    t: Dict[str, torch.Tensor] = {}
+    if routing == "iid":
+        t["x"] = randn((w.T, H), seed_of(w, layer, "x"), dev)
+    else:
+        z = randn((1, H), seed_of(w, layer, "x_shared"), dev)
+        n = randn((w.T, H), seed_of(w, layer, "x"), dev)
+        t["x"] = (0.97 * z + 0.243 * n).contiguous()
+
+    def dense(name, shape):
+        m = randn(shape, seed_of(w, layer, name), dev, std=0.02)
+        return m.to(torch.bfloat16)
+
+    t["gamma1"] = randn((H,), seed_of(w, layer, "gamma1"), dev, std=0.02, mean=1.0).to(torch.bfloat16)
+    t["gamma2"] = randn((H,), seed_of(w, layer, "gamma2"), dev, std=0.02, mean=1.0).to(torch.bfloat16)
+    t["w_qkv"] = dense("w_qkv", (w.qkv_rows, H))
+    t["w_o"] = dense("w_o", (H, w.n_q_heads * D))
+    t["w_router"] = dense("w_router", (w.n_experts, H))
+    t["w_pool"] = dense("w_pool", (w.pooled, H))
+    t["w_unpool"] = dense("w_unpool", (H, w.pooled))
+    C = w.kv_capacity
+    t["k_cache"] = randn((w.n_kv_heads, C, D), seed_of(w, layer, "k_cache"), dev).to(torch.bfloat16)
+    t["v_cache"] = randn((w.n_kv_heads, C, D), seed_of(w, layer, "v_cache"), dev).to(torch.bfloat16)
+    if experts:
+        t.update(make_experts(w, layer, dev))
+    return t
+
+
+def expert_shapes(w: Workload):
+    """(rows, K) of the gate, up and down matrices of one expert."""
+    return {"gate": (w.inter_local, w.pooled), "up": (w.inter_local, w.pooled),
+            "down": (w.pooled_local, w.inter)}
+
+
+def make_experts(w: Workload, layer: int, device) -> Dict[str, torch.Tensor]:
+    dev = torch.device(device)
+    out: Dict[str, torch.Tensor] = {}
+    for mat, (N, K) in expert_shapes(w).items():
+        tid = "w_" + mat
+        if w.expert_dtype == BF16:
+            full = torch.empty((w.n_experts, N, K), dtype=torch.bfloat16, device=dev)
+            for e in range(w.n_experts):
+                full[e] = randn((N, K), seed_of(w, layer, tid, e), dev, std=0.02).to(torch.bfloat16)
+            out[mat] = full
+        else:
+            codes = torch.empty((w.n_experts, N, K // 2), dtype=torch.uint8, device=dev)
+            scales = torch.empty((w.n_experts, N, K // 16), dtype=torch.uint8, device=dev)
+            ts = torch.empty((w.n_experts,), dtype=torch.float32, device=dev)
+            for e in range(w.n_experts):
+                m = randn((N, K), seed_of(w, layer, tid, e), dev, std=0.02)
+                if w.fp32_masters:
+                    # the device receives bf16 copies of fp32 masters; encode those
+                    m = m.to(torch.bfloat16).float()
+                c, s, tsc = encode_nvfp4(m)
+                codes[e], scales[e], ts[e] = c, s, tsc
+            out[mat + "_codes"], out[mat + "_scales"], out[mat + "_ts"] = codes, scales, ts
+    return out
+
+
+def fp32_masters(w: Workload, layer: int = 0) -> Dict[str, torch.Tensor]:
+    """The fp32 master weights of a tiny workload (drift report only)."""
+    dev = torch.device("cpu")
+    H, D = w.hidden, w.head_dim
+    m = {
+        "w_qkv": randn((w.qkv_rows, H), seed_of(w, layer, "w_qkv"), dev, std=0.02),
+        "w_o": randn((H, w.n_q_heads * D), seed_of(w, layer, "w_o"), dev, std=0.02),
+        "w_router": randn((w.n_experts, H), seed_of(w, layer, "w_router"), dev, std=0.02),
+        "w_pool": randn((w.pooled, H), seed_of(w, layer, "w_pool"), dev, std=0.02),
+        "w_unpool": randn((H, w.pooled), seed_of(w, layer, "w_unpool"), dev, std=0.02),
+    }
+    return m
+
+
+def small_workload(**kw) -> Workload:
+    """A reduced shape for fast tests (several tiles plus a ragged tail)."""
+    base = dict(wid=7, name="small", hidden=512, n_q_heads=8, n_kv_heads=2, head_dim=64, pooled=256,
+                inter=384, n_experts=16, top_k=4, expert_dtype=NVFP4, n_shards=1, window=40, pos=70, T=5)
+    base.update(kw)
+    return Workload(**base)

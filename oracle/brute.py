@@ -1,0 +1,198 @@
+"""Loop-only oracle of the same layer step, for tiny shapes.
+
+Test infrastructure only (see the package docstring).
+
+Every quantity is a Python float (IEEE binary64) computed with explicit loops:
+per token, per head, per key, per output feature, per reduction index.  It
+re-derives each definition (bf16 rounding, E2M1 / E4M3 decoding, RMSNorm,
+rotate-half RoPE, windowed causal attention, top-k routing with the lower index
+winning ties, SwiGLU experts, combine, residuals) from the written rules and
+does not call into ``layer.py`` or ``formats.py``, so that the vectorised
+oracle can be checked against it.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, List
+
+
+def r_bf16(v: float) -> float:
+    """Nearest bf16 value, ties to even (8 significant bits, min exponent -126)."""
+    if v == 0.0 or math.isinf(v) or math.isnan(v):
+        return v
+    mant, ex = math.frexp(v)          # v = mant * 2**ex, 0.5 <= |mant| < 1
+    # value = mant * 2**ex; keep 8 significant bits -> step 2**(ex-8), not below 2**-133
+    step_exp = max(ex - 8, -133)
+    n = v / (2.0 ** step_exp)
+    n_r = round(n)                    # Python round(): ties to even
+    out = n_r * (2.0 ** step_exp)
+    if abs(out) >= 2.0 ** 128:
+        return math.copysign(math.inf, v)
+    return out
+
+
+def fp4_elem(code: int) -> float:
+    negative = (code >> 3) & 1
+    exp_field = (code >> 1) & 3
+    man = code & 1
+    if exp_field == 0:
+        mag = 0.5 * man
+    else:
+        mag = (2.0 ** (exp_field - 1)) * (1.0 + 0.5 * man)
+    return -mag if negative else mag
+
+
+def fp8_scale(b: int) -> float:
+    negative = (b >> 7) & 1
+    exp_field = (b >> 3) & 15
+    man = b & 7
+    if exp_field == 15 and man == 7:
+        return math.nan
+    if exp_field == 0:
+        mag = (man / 8.0) * 2.0 ** -6
+    else:
+        mag = (1.0 + man / 8.0) * 2.0 ** (exp_field - 7)
+    return -mag if negative else mag
+
+
+def _nvfp4_row_elem(codes_row, scales_row, ts: float, k: int) -> float:
+    byte = int(codes_row[k // 2])
+    code = (byte & 15) if k % 2 == 0 else (byte >> 4)
+    return fp4_elem(code) * fp8_scale(int(scales_row[k // 16])) * ts
+
+
+def _dot(a, b) -> float:
+    s = 0.0
+    for i in range(len(a)):
+        s += a[i] * b[i]
+    return s
+
+
+def _norm_round(vec: List[float], gamma: List[float], eps: float) -> List[float]:
+    n = len(vec)
+    ss = 0.0
+    for v in vec:
+        ss += v * v
+    inv = 1.0 / math.sqrt(ss / n + eps)
+    return [r_bf16(vec[i] * inv * gamma[i]) for i in range(n)]
+
+
+def _rotate(vec: List[float], position: int, theta: float) -> List[float]:
+    D = len(vec)
+    half = D // 2
+    out = [0.0] * D
+    for i in range(half):
+        angle = position * theta ** (-(2.0 * i) / D)
+        c, s = math.cos(angle), math.sin(angle)
+        out[i] = vec[i] * c - vec[i + half] * s
+        out[i + half] = vec[i + half] * c + vec[i] * s
+    return out
+
+
+def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool = True) -> Dict:
+    """Same contract as layer.layer_step on tiny inputs given as nested lists / arrays.
+
+    expert_raw(e) returns {"gate": (codes, scales, ts) | W, "up": ..., "down": ...}.
+    """
+    x = [[float(v) for v in row] for row in inp["x"]]
+    T, H = len(x), len(x[0])
+    Hq, Hkv, D = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    E, K = dims.n_experts, dims.top_k
+    w_qkv = inp["w_qkv"]
+    C = len(inp["k_cache"][0])
+    kc = [[[float(inp["k_cache"][g][j][d]) for d in range(D)] for j in range(C)] for g in range(Hkv)]
+    vc = [[[float(inp["v_cache"][g][j][d]) for d in range(D)] for j in range(C)] for g in range(Hkv)]
+
+    # RMSNorm 1, QKV projection, RoPE, rounding, cache write
+    q_all, k_all, v_all = [], [], []
+    for t in range(T):
+        xn = _norm_round(x[t], [float(v) for v in inp["gamma1"]], dims.rms_eps)
+        row = [_dot(xn, [float(v) for v in w_qkv[n]]) for n in range(len(w_qkv))]
+        qh = [_rotate(row[h * D:(h + 1) * D], pos + t, dims.rope_theta) for h in range(Hq)]
+        kh = [_rotate(row[(Hq + g) * D:(Hq + g + 1) * D], pos + t, dims.rope_theta) for g in range(Hkv)]
+        vh = [row[(Hq + Hkv + g) * D:(Hq + Hkv + g + 1) * D] for g in range(Hkv)]
+        q_all.append([[r_bf16(v) for v in qv] for qv in qh])
+        k_all.append([[r_bf16(v) for v in kv] for kv in kh])
+        v_all.append([[r_bf16(v) for v in vv] for vv in vh])
+        for g in range(Hkv):
+            kc[g][pos + t] = list(k_all[t][g])
+            vc[g][pos + t] = list(v_all[t][g])
+
+    # attention, o-projection, residual
+    group = Hq // Hkv
+    h_all = []
+    for t in range(T):
+        p = pos + t
+        o_flat = []
+        for hh in range(Hq):
+            g = hh // group
+            keys = [j for j in range(0, p + 1) if window == 0 or j > p - window]
+            scores = [_dot(q_all[t][hh], kc[g][j]) / math.sqrt(D) for j in keys]
+            mx = max(scores)
+            ws = [math.exp(s - mx) for s in scores]
+            tot = sum(ws)
+            for d in range(D):
+                acc = 0.0
+                for i, j in enumerate(keys):
+                    acc += ws[i] / tot * vc[g][j][d]
+                o_flat.append(r_bf16(acc))
+        h_row = []
+        for n in range(H):
+            h_row.append(x[t][n] + _dot(o_flat, [float(v) for v in inp["w_o"][n]]))
+        h_all.append(h_row)
+
+    # MoE block
+    il = dims.inter // dims.n_shards
+    plc = dims.pooled // dims.n_shards
+    rk = dims.shard_rank
+    y, idx_all, gate_all, logit_all = [], [], [], []
+    for t in range(T):
+        hn = _norm_round(h_all[t], [float(v) for v in inp["gamma2"]], dims.rms_eps)
+        logits = [_dot(hn, [float(v) for v in inp["w_router"][e]]) for e in range(E)]
+        remaining = list(range(E))
+        chosen = []
+        for _ in range(K):
+            best = remaining[0]
+            for e in remaining[1:]:
+                if logits[e] > logits[best]:      # strict: equal logits keep the lower index
+                    best = e
+            chosen.append(best)
+            remaining.remove(best)
+        mx = max(logits[e] for e in chosen)
+        ex = [math.exp(logits[e] - mx) for e in chosen]
+        gates = [v / sum(ex) for v in ex]
+        pl = [r_bf16(_dot(hn, [float(v) for v in inp["w_pool"][pp]])) for pp in range(dims.pooled)]
+        m_acc = [0.0] * dims.pooled
+        for slot, e in enumerate(chosen):
+            raw = expert_raw(e)
+            a = [0.0] * dims.inter
+            for i in range(il):
+                if nvfp4:
+                    gsum = 0.0
+                    usum = 0.0
+                    gc, gs, gts = raw["gate"]
+                    uc, us, uts = raw["up"]
+                    for kk in range(dims.pooled):
+                        gsum += pl[kk] * _nvfp4_row_elem(gc[i], gs[i], float(gts), kk)
+                        usum += pl[kk] * _nvfp4_row_elem(uc[i], us[i], float(uts), kk)
+                else:
+                    gsum = _dot(pl, [float(v) for v in raw["gate"][i]])
+                    usum = _dot(pl, [float(v) for v in raw["up"][i]])
+                sig = gsum / (1.0 + math.exp(-gsum)) if gsum > -700 else 0.0
+                a[rk * il + i] = r_bf16(sig * usum)
+            for pp in range(plc):
+                if nvfp4:
+                    dc, ds, dts = raw["down"]
+                    dsum = 0.0
+                    for kk in range(dims.inter):
+                        dsum += a[kk] * _nvfp4_row_elem(dc[pp], ds[pp], float(dts), kk)
+                else:
+                    dsum = _dot(a, [float(v) for v in raw["down"][pp]])
+                m_acc[rk * plc + pp] += gates[slot] * dsum
+        m = [r_bf16(v) for v in m_acc]
+        y.append([h_all[t][n] + _dot(m, [float(v) for v in inp["w_unpool"][n]]) for n in range(H)])
+        idx_all.append(chosen)
+        gate_all.append(gates)
+        logit_all.append(logits)
+    return dict(y=y, idx=idx_all, gates=gate_all, logits=logit_all, k_new=k_all, v_new=v_all,
+                h=h_all)

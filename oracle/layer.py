@@ -1,0 +1,252 @@
+"""Vectorised fp64 oracle of one MoE decoder layer's batch-1 speculative-verify step.
+
+Test infrastructure only (see the package docstring).
+
+What the step computes (orcarouter.ai English post, "Where the kernel boundary
+sits" and "The draft model got faster too"; aicoder.com news item, "Key
+Takeaways"): one decoder layer of a mixture-of-experts model verifying T <= 16
+draft tokens of one request in a single pass.  The launch covers the QKV
+projection and the KV-cache write, attention (sliding window over the last
+2,048 tokens, or global), the dense GEMMs, routing of each token to 8 of 256
+experts, a pooler projection that shrinks each token vector before the experts,
+the expert GEMMs and an unpooler that restores the width afterwards.
+
+Where the pages are silent the plainest reading is taken (each one is listed
+with its rationale in the design notes):
+  * pre-norm block: h = x + Attn(RMSNorm1(x)); y = h + MoE(RMSNorm2(h)); no biases
+  * RMSNorm: v * (mean(v^2) + eps)^-1/2 * gamma
+  * RoPE, rotate-half pairing (i, i + D/2), theta = 10000, position pos + t,
+    on q and k of every layer
+  * key j visible to the token at position p iff j <= p and (W == 0 or j > p - W)
+  * GQA: q head h reads kv head floor(h * Hkv / Hq); score scale 1/sqrt(D)
+  * router on the normalised hidden state: fp32-or-better logits, top-k by
+    logit descending with ties to the lower expert index, gates = softmax over
+    the k selected logits, in selection order
+  * SwiGLU expert: a = silu(x Wg^T) * (x Wu^T); d = a Wd^T
+  * combine: m_t = sum over the token's k slots, in selection order, of gate * d
+  * expert N-sharding (one GPU's share): gate/up keep rows
+    [rank*I/S, (rank+1)*I/S) of the intermediate width, the SwiGLU output is
+    zero outside that slice; down keeps rows [rank*P/S, ...) of the pooled
+    width and its output is zero elsewhere (zero padding stands in for the
+    cross-GPU gathers).
+Precision contract: everything in fp64 except bf16 rounding r() of the values
+the device stores as bf16 operands: xn, q and k after RoPE, v, the attention
+output o, hn, the pooled vector pl, the SwiGLU output a and the combined
+vector m.  The residual stream (x, h, y) and the router logits stay wide.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Callable, Dict, Optional, Tuple
+
+import numpy as np
+
+from .formats import bf16_round, nvfp4_dequant
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    hidden: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    pooled: int
+    inter: int
+    n_experts: int
+    top_k: int
+    n_shards: int = 1
+    shard_rank: int = 0
+    rms_eps: float = 1e-6
+    rope_theta: float = 10000.0
+
+
+# --------------------------------------------------------------------------------------------
+# the steps, one function each
+# --------------------------------------------------------------------------------------------
+def rmsnorm(v: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of each row, before rounding: v * (mean(v^2) + eps)^-1/2 * gamma."""
+    ms = np.mean(v * v, axis=-1, keepdims=True)
+    return v / np.sqrt(ms + eps) * gamma[None, :]
+
+
+def rope(vec: np.ndarray, positions: np.ndarray, theta: float) -> np.ndarray:
+    """Rotate-half RoPE: vec [T, nh, D], positions [T] -> rotated [T, nh, D].
+
+    Pair (i, i + D/2) is rotated by angle position * theta^(-2i/D).
+    """
+    D = vec.shape[-1]
+    half = D // 2
+    inv_freq = theta ** (-(2.0 * np.arange(half, dtype=np.float64)) / D)
+    ang = positions.astype(np.float64)[:, None] * inv_freq[None, :]       # [T, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    a, b = vec[..., :half], vec[..., half:]
+    return np.concatenate([a * c - b * s, b * c + a * s], axis=-1)
+
+
+def visible_range(p: int, window: int) -> Tuple[int, int]:
+    """Half-open range [lo, p+1) of key positions visible to the token at position p."""
+    lo = 0 if window == 0 else max(0, p - window + 1)
+    return lo, p + 1
+
+
+def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: int,
+              window: int) -> np.ndarray:
+    """GQA attention of the T new tokens over the (already updated) cache.
+
+    q [T, Hq, D] (bf16 values), caches [Hkv, C, D] -> o [T, Hq, D] (not rounded).
+    Full score vector per query, its global max, exact normaliser.
+    """
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[0]
+    grp = Hq // Hkv
+    o = np.zeros((T, Hq, D))
+    scale = 1.0 / np.sqrt(D)
+    for t in range(T):
+        lo, hi = visible_range(pos + t, window)
+        for g in range(Hkv):
+            heads = slice(g * grp, (g + 1) * grp)
+            K = k_cache[g, lo:hi]                     # [nk, D]
+            V = v_cache[g, lo:hi]
+            s = (q[t, heads] @ K.T) * scale           # [grp, nk]
+            s = s - s.max(axis=1, keepdims=True)
+            p = np.exp(s)
+            p /= p.sum(axis=1, keepdims=True)
+            o[t, heads] = p @ V
+    return o
+
+
+def route(logits: np.ndarray, k: int):
+    """Top-k per token by logit descending, ties to the lower expert index.
+
+    Returns idx [T, k] (selection order), gates [T, k] (softmax over the selected
+    logits) and gap [T] = k-th selected logit - (k+1)-th (inf when k == E).
+    """
+    T, E = logits.shape
+    idx = np.zeros((T, k), dtype=np.int64)
+    gap = np.full(T, np.inf)
+    for t in range(T):
+        order = np.lexsort((np.arange(E), -logits[t]))      # primary: -logit, then index
+        idx[t] = order[:k]
+        if k < E:
+            gap[t] = logits[t, order[k - 1]] - logits[t, order[k]]
+    sel = np.take_along_axis(logits, idx, axis=1)
+    z = np.exp(sel - sel.max(axis=1, keepdims=True))
+    gates = z / z.sum(axis=1, keepdims=True)
+    return idx, gates, gap
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    with np.errstate(over="ignore"):
+        return z / (1.0 + np.exp(-z))
+
+
+ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+def nvfp4_experts(get_raw: Callable[[int], dict]) -> ExpertFn:
+    """Expert accessor from raw NVFP4 storage.
+
+    get_raw(e) returns {"gate": (codes, scales, ts), "up": (...), "down": (...)}.
+    """
+    def fn(e: int):
+        raw = get_raw(e)
+        return tuple(nvfp4_dequant(*raw[m]) for m in ("gate", "up", "down"))
+    return fn
+
+
+def bf16_experts(get_raw: Callable[[int], dict]) -> ExpertFn:
+    """get_raw(e) returns {"gate": W, "up": W, "down": W} as fp64 arrays of bf16 values."""
+    def fn(e: int):
+        raw = get_raw(e)
+        return tuple(np.asarray(raw[m], dtype=np.float64) for m in ("gate", "up", "down"))
+    return fn
+
+
+def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
+               dims: Dims) -> Tuple[np.ndarray, np.ndarray]:
+    """One token through one expert (this GPU's shard).  Returns (a [inter], d [pooled])."""
+    il = dims.inter // dims.n_shards
+    plc = dims.pooled // dims.n_shards
+    r = dims.shard_rank
+    g = Wg @ pl_t
+    u = Wu @ pl_t
+    a = np.zeros(dims.inter)
+    a[r * il:(r + 1) * il] = bf16_round(silu(g) * u)
+    d = np.zeros(dims.pooled)
+    d[r * plc:(r + 1) * plc] = Wd @ a
+    return a, d
+
+
+# --------------------------------------------------------------------------------------------
+# the whole step
+# --------------------------------------------------------------------------------------------
+def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, experts: ExpertFn,
+               force_idx: Optional[np.ndarray] = None, moe_tokens=None) -> Dict[str, np.ndarray]:
+    """One layer step.  `inp` holds fp64 arrays (bf16-valued weights):
+    x [T,H], gamma1 [H], w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq*D], gamma2 [H], w_router [E,H],
+    w_pool [P,H], w_unpool [H,P], k_cache/v_cache [Hkv, C, D].
+
+    force_idx [T, k] replaces the router's choice (gates are then the softmax over those
+    logits).  moe_tokens limits the expert and unpooler work to a subset of tokens (y rows of
+    the other tokens are returned as NaN); everything else is computed for all tokens.
+    Returns y, the written K/V rows, routing and every intermediate.
+    """
+    x = np.asarray(inp["x"], dtype=np.float64)
+    T, H = x.shape
+    Hq, Hkv, D = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    out: Dict[str, np.ndarray] = {}
+
+    # attention block
+    xn = bf16_round(rmsnorm(x, inp["gamma1"], dims.rms_eps))
+    qkv = xn @ inp["w_qkv"].T
+    q = qkv[:, :Hq * D].reshape(T, Hq, D)
+    k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
+    v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
+    positions = pos + np.arange(T)
+    q_r = bf16_round(rope(q, positions, dims.rope_theta))
+    k_r = bf16_round(rope(k, positions, dims.rope_theta))
+    v_r = bf16_round(v)
+    k_cache = np.array(inp["k_cache"], dtype=np.float64, copy=True)
+    v_cache = np.array(inp["v_cache"], dtype=np.float64, copy=True)
+    for t in range(T):
+        k_cache[:, pos + t] = k_r[t]
+        v_cache[:, pos + t] = v_r[t]
+    o = bf16_round(attention(q_r, k_cache, v_cache, pos, window))
+    h = x + o.reshape(T, Hq * D) @ inp["w_o"].T
+
+    # MoE block
+    hn = bf16_round(rmsnorm(h, inp["gamma2"], dims.rms_eps))
+    logits = hn @ inp["w_router"].T
+    idx, gates, gap = route(logits, dims.top_k)
+    if force_idx is not None:
+        idx = np.asarray(force_idx, dtype=np.int64)
+        sel = np.take_along_axis(logits, idx, axis=1)
+        z = np.exp(sel - sel.max(axis=1, keepdims=True))
+        gates = z / z.sum(axis=1, keepdims=True)
+    pl = bf16_round(hn @ inp["w_pool"].T)
+
+    toks = range(T) if moe_tokens is None else list(moe_tokens)
+    m = np.full((T, dims.pooled), np.nan)
+    a_all = np.full((T, dims.top_k, dims.inter), np.nan)
+    d_all = np.full((T, dims.top_k, dims.pooled), np.nan)
+    needed = sorted({int(idx[t, kk]) for t in toks for kk in range(dims.top_k)})
+    for e in needed:                              # one expert's weights resident at a time
+        Wg, Wu, Wd = experts(e)
+        for t in toks:
+            for kk in range(dims.top_k):
+                if idx[t, kk] == e:
+                    a_all[t, kk], d_all[t, kk] = expert_out(pl[t], Wg, Wu, Wd, dims)
+    for t in toks:
+        acc = np.zeros(dims.pooled)
+        for kk in range(dims.top_k):              # selection order
+            acc = acc + gates[t, kk] * d_all[t, kk]
+        m[t] = bf16_round(acc)
+    y = np.full((T, H), np.nan)
+    tl = list(toks)
+    y[tl] = h[tl] + m[tl] @ inp["w_unpool"].T
+
+    out.update(y=y, xn=xn, q=q_r, k_new=k_r, v_new=v_r, o=o, h=h, hn=hn, logits=logits,
+               idx=idx, gates=gates, gap=gap, pl=pl, a=a_all, d=d_all, m=m,
+               k_cache=k_cache, v_cache=v_cache)
+    return out

@@ -1,0 +1,270 @@
+"""Pins of the layer oracle (CPU only).
+
+The vectorised oracle (oracle/layer.py) is checked against: closed forms
+(RMSNorm of a constant vector, RoPE at position 0 and a hand-derived rotation),
+library routines (torch rms_norm, scaled_dot_product_attention with an explicit
+mask, torch.topk), invariants (norm preservation, relative positions, window
+and causal masks, routing), a special case (top-k = E is a dense softmax
+mixture computed here with einsum) and the loop-only oracle (oracle/brute.py)
+on tiny shapes.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import brute, formats, layer
+from moe_layer_persistent_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- RMSNorm
+def test_rmsnorm_constant_vector_closed_form():
+    H, eps = 64, 1e-6
+    gamma = np.linspace(0.5, 1.5, H)
+    for c in (-3.0, 0.25, 7.0):
+        out = layer.rmsnorm(np.full((1, H), c), gamma, eps)
+        np.testing.assert_allclose(out[0], c / math.sqrt(c * c + eps) * gamma, rtol=1e-15)
+
+
+def test_rmsnorm_matches_torch():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal((5, 96)) * 3
+    g = 1 + 0.02 * rng.standard_normal(96)
+    want = torch.nn.functional.rms_norm(torch.tensor(x), (96,), torch.tensor(g), eps=1e-6).numpy()
+    np.testing.assert_allclose(layer.rmsnorm(x, g, 1e-6), want, rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_position_zero_is_identity_and_norm_preserved():
+    rng = np.random.default_rng(1)
+    v = rng.standard_normal((3, 2, 16))
+    np.testing.assert_array_equal(layer.rope(v, np.zeros(3, dtype=int), 10000.0), v)
+    r = layer.rope(v, np.array([5, 999, 123456]), 10000.0)
+    np.testing.assert_allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(v, axis=-1), rtol=1e-13)
+
+
+def test_rope_relative_position():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((1, 1, 32))
+    k = rng.standard_normal((1, 1, 32))
+    def dot(m, n):
+        return float(np.sum(layer.rope(q, np.array([m]), 1e4) * layer.rope(k, np.array([n]), 1e4)))
+    for (m, n, s) in [(3, 1, 10), (100, 40, 777), (0, 9, 5)]:
+        assert abs(dot(m, n) - dot(m + s, n + s)) < 1e-10
+
+
+def test_rope_hand_example():
+    """D = 4, theta = 1e4, position 1: pair (0, 2) turns by 1 rad, pair (1, 3) by 0.01 rad."""
+    v = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    got = layer.rope(v, np.array([1]), 10000.0)[0, 0]
+    c1, s1, c2, s2 = math.cos(1.0), math.sin(1.0), math.cos(0.01), math.sin(0.01)
+    want = [1 * c1 - 3 * s1, 2 * c2 - 4 * s2, 3 * c1 + 1 * s1, 4 * c2 + 2 * s2]
+    np.testing.assert_allclose(got, want, rtol=1e-15)
+
+
+# ---------------------------------------------------------------- attention
+def _sdpa_reference(q, kc, vc, pos, window):
+    """torch SDPA with an explicit boolean mask, per (token, head), fp64 on the CPU."""
+    T, Hq, D = q.shape
+    Hkv, C, _ = kc.shape
+    grp = Hq // Hkv
+    out = np.zeros_like(q)
+    for h in range(Hq):
+        g = h // grp
+        mask = torch.zeros(T, C, dtype=torch.bool)
+        for t in range(T):
+            p = pos + t
+            for j in range(C):
+                mask[t, j] = j <= p and (window == 0 or j > p - window)
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(q[None, :, h]), torch.tensor(kc[None, g]), torch.tensor(vc[None, g]),
+            attn_mask=mask[None])
+        out[:, h] = o[0].numpy()
+    return out
+
+
+@pytest.mark.parametrize("window", [0, 1, 5])
+def test_attention_matches_sdpa(window):
+    rng = np.random.default_rng(4)
+    T, Hq, Hkv, D, pos = 4, 6, 2, 8, 9
+    C = pos + T + 3
+    q = rng.standard_normal((T, Hq, D))
+    kc = rng.standard_normal((Hkv, C, D))
+    vc = rng.standard_normal((Hkv, C, D))
+    np.testing.assert_allclose(layer.attention(q, kc, vc, pos, window),
+                               _sdpa_reference(q, kc, vc, pos, window), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_invisible_keys_do_not_matter():
+    rng = np.random.default_rng(5)
+    T, Hq, Hkv, D, pos, W = 3, 4, 2, 8, 20, 6
+    C = pos + T + 4
+    q = rng.standard_normal((T, Hq, D))
+    kc = rng.standard_normal((Hkv, C, D))
+    vc = rng.standard_normal((Hkv, C, D))
+    base = layer.attention(q, kc, vc, pos, W)
+    for t in range(T):
+        lo, hi = layer.visible_range(pos + t, W)
+        assert hi - lo == min(W, pos + t + 1)
+    kc2, vc2 = kc.copy(), vc.copy()
+    lo0, _ = layer.visible_range(pos, W)
+    kc2[:, :lo0] = 99.0                     # before every token's window
+    vc2[:, :lo0] = -99.0
+    kc2[:, pos + T:] = 55.0                 # future slots
+    vc2[:, pos + T:] = 55.0
+    np.testing.assert_array_equal(layer.attention(q, kc2, vc2, pos, W), base)
+    # the last new key is in the future of token 0 only: changing it must leave token 0 alone
+    kc3 = kc.copy()
+    kc3[:, pos + T - 1] += 3.0
+    np.testing.assert_array_equal(layer.attention(q, kc3, vc, pos, W)[0], base[0])
+
+
+def test_attention_single_key_and_equal_keys():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((1, 2, 8))
+    kc = rng.standard_normal((1, 4, 8))
+    vc = rng.standard_normal((1, 4, 8))
+    o = layer.attention(q, kc, vc, pos=0, window=0)         # only key 0 is visible
+    np.testing.assert_array_equal(o[0, 0], vc[0, 0])
+    kc_eq = np.repeat(kc[:, :1], 4, axis=1)
+    o = layer.attention(q, kc_eq, vc, pos=3, window=0)
+    np.testing.assert_allclose(o[0, 1], vc[0].mean(axis=0), rtol=1e-13)
+
+
+# ---------------------------------------------------------------- routing
+def test_route_golden_ties():
+    vals = {}
+    for line in open(os.path.join(GOLDEN, "router_ties.txt")):
+        if line.strip() and not line.startswith("#"):
+            k, *v = line.split()
+            vals[k] = v
+    logits = np.array([[float(v) for v in vals["logits"]]])
+    idx, gates, gap = layer.route(logits, int(vals["k"][0]))
+    assert idx[0].tolist() == [int(v) for v in vals["idx"]]
+    np.testing.assert_allclose(gates[0], 1 / 3, rtol=1e-15)
+    assert gap[0] == 2.0          # 3rd selected (5) minus the best unselected (3)
+
+
+def test_route_invariants_and_topk():
+    rng = np.random.default_rng(7)
+    logits = rng.standard_normal((16, 256))
+    idx, gates, gap = layer.route(logits, 8)
+    for t in range(16):
+        assert len(set(idx[t])) == 8
+        sel = logits[t, idx[t]]
+        assert np.all(np.diff(sel) < 0)
+        assert np.min(sel) >= np.max(np.delete(logits[t], idx[t]))
+        vals, ind = torch.topk(torch.tensor(logits[t]), 8)
+        assert ind.tolist() == idx[t].tolist()
+        assert abs(gap[t] - (sel[-1] - np.sort(logits[t])[-9])) < 1e-15
+    np.testing.assert_allclose(gates.sum(axis=1), 1.0, rtol=1e-14)
+    assert np.all(np.diff(gates, axis=1) <= 0)
+
+
+# ---------------------------------------------------------------- whole layer
+def _np_inputs(w: synth.Workload, layer_id=0, routing="iid"):
+    t = synth.make_layer(w, layer_id, "cpu", routing=routing)
+    f = {k: v.double().numpy() if v.dtype in (torch.float32, torch.bfloat16) else v.numpy()
+         for k, v in t.items()}
+    return t, f
+
+
+def _dims(w: synth.Workload):
+    return layer.Dims(w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pooled, w.inter,
+                      w.n_experts, w.top_k, w.n_shards, 0, w.rms_eps, w.rope_theta)
+
+
+def _raw_getter(f, w):
+    if w.expert_dtype == synth.NVFP4:
+        return lambda e: {m: (f[m + "_codes"][e], f[m + "_scales"][e], float(f[m + "_ts"][e]))
+                          for m in ("gate", "up", "down")}
+    return lambda e: {m: f[m][e] for m in ("gate", "up", "down")}
+
+
+def _experts(f, w):
+    getter = _raw_getter(f, w)
+    return layer.nvfp4_experts(getter) if w.expert_dtype == synth.NVFP4 else layer.bf16_experts(getter)
+
+
+TINY_SHAPES = [
+    dict(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, pooled=32, inter=64, n_experts=8, top_k=3,
+         window=5, pos=9, T=3),
+    dict(hidden=48, n_q_heads=2, n_kv_heads=1, head_dim=8, pooled=32, inter=32, n_experts=6, top_k=2,
+         window=0, pos=4, T=2, expert_dtype=synth.BF16),
+    dict(hidden=64, n_q_heads=4, n_kv_heads=1, head_dim=16, pooled=64, inter=64, n_experts=8, top_k=2,
+         window=3, pos=6, T=4, n_shards=2),
+]
+
+
+@pytest.mark.parametrize("shape", TINY_SHAPES)
+def test_layer_matches_bruteforce(shape):
+    w = synth.small_workload(**shape)
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    got = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w))
+    ref = brute.layer_step(f, dims, w.pos, w.window, _raw_getter(f, w),
+                           nvfp4=w.expert_dtype == synth.NVFP4)
+    assert got["idx"].tolist() == ref["idx"]
+    np.testing.assert_allclose(got["logits"], np.array(ref["logits"]), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["k_new"], np.array(ref["k_new"]), rtol=0, atol=0)
+    np.testing.assert_allclose(got["v_new"], np.array(ref["v_new"]), rtol=0, atol=0)
+    np.testing.assert_allclose(got["h"], np.array(ref["h"]), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["y"], np.array(ref["y"]), rtol=1e-9, atol=1e-10)
+
+
+def test_tiny_workload_matches_bruteforce():
+    w = synth.WORKLOADS["tiny"]
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    got = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w))
+    ref = brute.layer_step(f, dims, w.pos, w.window, _raw_getter(f, w), nvfp4=True)
+    assert got["idx"].tolist() == ref["idx"]
+    np.testing.assert_allclose(got["y"], np.array(ref["y"]), rtol=1e-9, atol=1e-10)
+    assert np.isfinite(got["y"]).all()
+
+
+def test_full_topk_is_dense_softmax_mixture():
+    """With k = E the MoE block is sum_e softmax(logits)_e * expert_e(pl): computed here directly."""
+    w = synth.small_workload(hidden=64, n_q_heads=2, n_kv_heads=1, head_dim=16, pooled=32, inter=64,
+                             n_experts=5, top_k=5, window=0, pos=3, T=2)
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    out = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w))
+    experts = [_experts(f, w)(e) for e in range(5)]
+    Wg = np.stack([e[0] for e in experts])
+    Wu = np.stack([e[1] for e in experts])
+    Wd = np.stack([e[2] for e in experts])
+    lg = out["hn"] @ f["w_router"].T
+    prob = np.exp(lg - lg.max(axis=1, keepdims=True))
+    prob /= prob.sum(axis=1, keepdims=True)
+    g = np.einsum("eik,tk->tei", Wg, out["pl"])
+    u = np.einsum("eik,tk->tei", Wu, out["pl"])
+    a = formats.bf16_round(g / (1 + np.exp(-g)) * u)
+    d = np.einsum("epi,tei->tep", Wd, a)
+    m = formats.bf16_round(np.einsum("te,tep->tp", prob, d))
+    y = out["h"] + m @ f["w_unpool"].T
+    np.testing.assert_allclose(out["y"], y, rtol=1e-10, atol=1e-10)
+
+
+def test_force_idx_reproduces_router_choice():
+    w = synth.small_workload(**TINY_SHAPES[0])
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    a = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w))
+    b = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w), force_idx=a["idx"])
+    np.testing.assert_array_equal(a["y"], b["y"])
+
+
+def test_cache_write_set_is_exact():
+    w = synth.small_workload(**TINY_SHAPES[0])
+    _, f = _np_inputs(w)
+    out = layer.layer_step(f, _dims(w), w.pos, w.window, _experts(f, w))
+    changed = np.any(out["k_cache"] != f["k_cache"], axis=-1)
+    written = np.zeros_like(changed)
+    written[:, w.pos:w.pos + w.T] = True
+    assert not np.any(changed & ~written)
+    np.testing.assert_array_equal(out["k_cache"][:, w.pos:w.pos + w.T].transpose(1, 0, 2), out["k_new"])
