@@ -1,0 +1,192 @@
+/*
+ * moel.h -- C ABI of the MI355X (gfx950) MoE decoder-layer verify step.
+ *
+ * One call runs one decoder layer of a mixture-of-experts model for the batch-1
+ * speculative-verify step: T <= 16 draft tokens of one request go through
+ *   RMSNorm -> QKV projection + rotate-half RoPE + KV-cache write -> GQA attention
+ *   (sliding window or global) -> o-projection + residual -> RMSNorm -> top-k router
+ *   and pooler -> SwiGLU experts (NVFP4 or bf16) -> weighted combine -> unpooler +
+ *   residual
+ * as a single persistent launch (orcarouter.ai English post, "Where the kernel boundary
+ * sits": one launch per decoder layer covering attention, the dense GEMMs, the expert
+ * GEMMs and the combine; "The draft model got faster too": 16 tokens verified in one
+ * pass; aicoder.com news item, "Key Takeaways": batch 1 only).  The same computation is
+ * also available as a chain of one kernel per step (moel_layer_decode_unfused), kept as
+ * an ablation and as the fallback target.
+ *
+ * Conventions (all entry points):
+ *   - Tensor pointers are DEVICE pointers (HIP global memory) owned by the caller unless
+ *     stated otherwise.  The library keeps no reference to them after a call returns.
+ *   - Every call validates its arguments on the host first.  On any error nothing is
+ *     launched and no caller buffer is touched; the return code says why.
+ *   - Launching calls are asynchronous on `stream` (a hipStream_t; NULL = default stream).
+ *   - Floating point: weights and the KV cache are bf16 (or NVFP4 for experts); the
+ *     residual stream x / y is fp32.  No float atomics are used: results are bitwise
+ *     reproducible for identical inputs.
+ *   - No C++ exceptions cross this boundary.
+ */
+#ifndef MOEL_H
+#define MOEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOEL_MAX_TOKENS 16
+#define MOEL_ABI_VERSION 1
+
+typedef enum moel_status {
+  MOEL_OK = 0,
+  MOEL_ERR_ARG = -1,         /* null pointer, bad count, T/pos/window out of range      */
+  MOEL_ERR_SHAPE = -2,       /* config shape the kernels do not support                 */
+  MOEL_ERR_ALIGN = -3,       /* pointer not 16-byte aligned                             */
+  MOEL_ERR_HIP = -4,         /* a HIP runtime call failed                               */
+  MOEL_ERR_TIMEOUT = -5,     /* a device-side wait exceeded its bound (plan status)     */
+  MOEL_ERR_ABORTED = -6,     /* the plan's abort word was set (plan status)             */
+  MOEL_ERR_UNSUPPORTED = -7  /* no suitable device (not gfx950 / no cooperative launch) */
+} moel_status;
+
+typedef enum moel_expert_dtype {
+  MOEL_EXPERT_NVFP4 = 0,     /* E2M1 codes, E4M3 scale per 16 elements, fp32 per matrix */
+  MOEL_EXPERT_BF16 = 1
+} moel_expert_dtype;
+
+/* Shape of one layer.  Sharded configurations hold one GPU's share of the experts'
+ * N dimension: gate/up keep inter/n_shards rows, down keeps pooled/n_shards rows (the
+ * slice of rank shard_rank); the missing slices are zero, standing in for the cross-GPU
+ * gathers (orcarouter.ai English post, "Where the kernel boundary sits": both MoE GEMMs
+ * sharded on N).  Head counts are the GPU's own (e.g. 8 q / 1 kv for a TP8 share). */
+typedef struct moel_config {
+  int32_t hidden;         /* H; multiple of 256                                          */
+  int32_t n_q_heads;      /* Hq; multiple of n_kv_heads                                  */
+  int32_t n_kv_heads;     /* Hkv                                                         */
+  int32_t head_dim;       /* D; 64 or 128                                                */
+  int32_t pooled;         /* P; multiple of 128 (and of 64 * n_shards)                   */
+  int32_t inter;          /* I (SwiGLU width, K of the down projection); multiple of 128 */
+  int32_t n_experts;      /* E; multiple of 16, <= 512                                   */
+  int32_t top_k;          /* k; 1..8, <= E                                               */
+  int32_t expert_dtype;   /* moel_expert_dtype                                           */
+  int32_t n_shards;       /* 1 = whole layer                                             */
+  int32_t shard_rank;     /* 0 <= shard_rank < n_shards                                  */
+  int32_t kv_capacity;    /* slots per kv head in the caller's cache                     */
+  float rms_eps;          /* RMSNorm epsilon                                             */
+  float rope_theta;       /* RoPE base                                                   */
+} moel_config;
+
+/* Layer weights in the kernels' packed layouts (see the moel_pack_* calls).  All device
+ * pointers, 16-byte aligned, caller-owned. */
+typedef struct moel_weights {
+  const void* gamma1;     /* bf16 [H]            attention RMSNorm gain                  */
+  const void* gamma2;     /* bf16 [H]            MoE RMSNorm gain                        */
+  const void* w_qkv;      /* packed dense, QKV   [(Hq+2Hkv)*D, H] (pack with rope heads) */
+  const void* w_o;        /* packed dense        [H, Hq*D]                               */
+  const void* w_router;   /* packed dense        [E, H]                                  */
+  const void* w_pool;     /* packed dense        [P, H]                                  */
+  const void* w_unpool;   /* packed dense        [H, P]                                  */
+  const void* w_gate;     /* packed experts      [E][inter/n_shards, P]                  */
+  const void* w_up;       /* packed experts      [E][inter/n_shards, P]                  */
+  const void* w_down;     /* packed experts      [E][pooled/n_shards, I]                 */
+  const float* ts_gate;   /* fp32 [E] tensor scales (NVFP4 only, else NULL)              */
+  const float* ts_up;
+  const float* ts_down;
+} moel_weights;
+
+/* Optional outputs for tests and profiling; any member may be NULL. */
+typedef struct moel_debug {
+  int32_t* expert_idx;    /* [T, k] selected experts, selection order                    */
+  float* gates;           /* [T, k] softmax over the selected logits                     */
+  float* router_logits;   /* [T, E] fp32                                                 */
+  uint64_t* timestamps;   /* [n_workgroups, MOEL_N_STAMPS] s_memrealtime ticks (100 MHz) */
+} moel_debug;
+
+#define MOEL_N_STAMPS 16
+
+typedef struct moel_plan moel_plan;
+
+/* --- host-only helpers (no GPU needed) ------------------------------------------- */
+
+const char* moel_status_string(int32_t status);
+int32_t moel_abi_version(void);
+
+/* Checks that `cfg` is a shape the kernels support.  Pure host code. */
+moel_status moel_validate_config(const moel_config* cfg);
+
+/* Checks the per-call arguments of moel_layer_decode against `cfg`: 1 <= T <= 16,
+ * pos >= 0, pos + T <= kv_capacity, window >= 0, non-NULL 16-byte-aligned pointers,
+ * y not aliasing x.  Pure host code (pointers are only compared, never dereferenced). */
+moel_status moel_validate_call(const moel_config* cfg, const moel_weights* w,
+                               const void* k_cache, const void* v_cache, const float* x,
+                               int32_t T, int32_t pos, int32_t window, const float* y);
+
+/* Bytes of the packed layouts (equal to the canonical bytes of the same matrix, plus at
+ * most 1 KiB of zero padding per 64-row tile for NVFP4 when K is not a multiple of 256). */
+size_t moel_packed_dense_bytes(int32_t N, int32_t K);
+size_t moel_packed_experts_bytes(const moel_config* cfg, int32_t which /*0 gate,1 up,2 down*/);
+
+/* --- plan ------------------------------------------------------------------------- */
+
+/* Validates cfg, selects the current HIP device, allocates the plan's workspace once
+ * (activation scratch, barrier words, status word, RoPE cos/sin table computed on the
+ * host in fp64 and stored fp32) and chooses the work decomposition.  *out is set only
+ * on success.  Not for the hot path. */
+moel_status moel_plan_create(const moel_config* cfg, moel_plan** out);
+moel_status moel_plan_destroy(moel_plan* plan);
+
+/* Number of workgroups of the persistent launch (one per compute unit). */
+int32_t moel_plan_workgroups(const moel_plan* plan);
+
+/* Reads the device-side status word (blocks until `plan`'s work on the device is done):
+ * MOEL_OK, MOEL_ERR_TIMEOUT or MOEL_ERR_ABORTED.  A non-OK status is cleared (and the
+ * plan's barrier words reset) by this call. */
+moel_status moel_plan_status(moel_plan* plan);
+
+/* Sets (1) or clears (0) the plan's abort word.  While set, launched kernels skip all
+ * work, leave every caller buffer untouched and report MOEL_ERR_ABORTED. */
+moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* stream);
+
+/* --- weight packing (one-time, not on the hot path) --------------------------------- */
+
+/* Dense bf16 matrix [N, K] row-major -> packed layout (16-row tiles, 32-element k steps,
+ * one 1 KiB block per (tile, step)).  rope_head_dim > 0 interleaves the rows of every
+ * rope_head_dim-row head pairwise (i, i + D/2) so that rotation partners are adjacent;
+ * pass head_dim for w_qkv and 0 otherwise.  N % 16 == 0, K % 32 == 0. */
+moel_status moel_pack_dense(const void* src, int32_t N, int32_t K, int32_t rope_head_dim,
+                            void* dst, void* stream);
+
+/* Experts of one matrix kind (0 gate, 1 up, 2 down) -> packed layout.
+ *   NVFP4: codes uint8 [E, N, K/2] (even k in the low nibble) and scales uint8 E4M3
+ *          [E, N, K/16] -> 64-row tiles: per tile the 16-byte codes of each row per
+ *          32-element step, then the 16 block scales of each row per 256-element chunk.
+ *   bf16:  src [E, N, K] (scales NULL) -> the dense layout per expert. */
+moel_status moel_pack_experts(const moel_config* cfg, int32_t which, const void* src,
+                              const void* scales, void* dst, void* stream);
+
+/* --- the layer step -------------------------------------------------------------- */
+
+/* One verify step of one layer, as ONE persistent cooperative launch.
+ *   k_cache, v_cache: bf16 [Hkv, kv_capacity, D]; slots [pos, pos+T) of every kv head
+ *                     are overwritten with the new (rotated, rounded) keys / values;
+ *                     every other byte is left untouched.
+ *   x: fp32 [T, H] input residual stream;  y: fp32 [T, H] output (must not alias x).
+ *   pos: tokens already in the cache (token t sits at position pos + t).
+ *   window: 0 = global attention; W > 0: token at position p sees keys j with
+ *           p - W < j <= p.
+ *   dbg: optional outputs (NULL = none). */
+moel_status moel_layer_decode(moel_plan* plan, const moel_weights* w, void* k_cache,
+                              void* v_cache, const float* x, int32_t T, int32_t pos,
+                              int32_t window, float* y, const moel_debug* dbg, void* stream);
+
+/* Same arguments and results, as a chain of one kernel per step. */
+moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, void* k_cache,
+                                      void* v_cache, const float* x, int32_t T, int32_t pos,
+                                      int32_t window, float* y, const moel_debug* dbg,
+                                      void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEL_H */

@@ -1,0 +1,209 @@
+"""ctypes binding of libmoel.so (argument marshalling only; every step runs in the HIP kernels).
+
+Names follow include/moel.h.  Tensors are torch tensors on the GPU; the library only
+receives their device pointers and the current HIP stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmoel.so")
+
+MOEL_OK = 0
+MOEL_ERR_ARG = -1
+MOEL_ERR_SHAPE = -2
+MOEL_ERR_ALIGN = -3
+MOEL_ERR_HIP = -4
+MOEL_ERR_TIMEOUT = -5
+MOEL_ERR_ABORTED = -6
+MOEL_ERR_UNSUPPORTED = -7
+MOEL_EXPERT_NVFP4 = 0
+MOEL_EXPERT_BF16 = 1
+MOEL_N_STAMPS = 16
+
+
+class MoelError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {status_string(code)} ({code})")
+        self.code = code
+
+
+class Config(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "hidden", "n_q_heads", "n_kv_heads", "head_dim", "pooled", "inter", "n_experts", "top_k",
+        "expert_dtype", "n_shards", "shard_rank", "kv_capacity")] + [
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "gamma1", "gamma2", "w_qkv", "w_o", "w_router", "w_pool", "w_unpool", "w_gate", "w_up",
+        "w_down", "ts_gate", "ts_up", "ts_down")]
+
+
+class Debug(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("expert_idx", "gates", "router_logits", "timestamps")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m moe_layer_persistent_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER
+        sigs = {
+            "moel_status_string": (ctypes.c_char_p, [i32]),
+            "moel_abi_version": (i32, []),
+            "moel_validate_config": (i32, [P(Config)]),
+            "moel_validate_call": (i32, [P(Config), P(Weights), vp, vp, vp, i32, i32, i32, vp]),
+            "moel_packed_dense_bytes": (sz, [i32, i32]),
+            "moel_packed_experts_bytes": (sz, [P(Config), i32]),
+            "moel_plan_create": (i32, [P(Config), P(vp)]),
+            "moel_plan_destroy": (i32, [vp]),
+            "moel_plan_workgroups": (i32, [vp]),
+            "moel_plan_status": (i32, [vp]),
+            "moel_plan_set_abort": (i32, [vp, i32, vp]),
+            "moel_pack_dense": (i32, [vp, i32, i32, i32, vp, vp]),
+            "moel_pack_experts": (i32, [P(Config), i32, vp, vp, vp, vp]),
+            "moel_layer_decode": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, P(Debug), vp]),
+            "moel_layer_decode_unfused": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, P(Debug), vp]),
+        }
+        for name, (res, args) in sigs.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(code: int) -> str:
+    return lib().moel_status_string(code).decode()
+
+
+def _check(code: int, what: str):
+    if code != MOEL_OK:
+        raise MoelError(code, what)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def config_from_workload(w, kv_capacity: Optional[int] = None) -> Config:
+    return Config(w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pooled, w.inter, w.n_experts,
+                  w.top_k, w.expert_dtype, w.n_shards, 0,
+                  w.kv_capacity if kv_capacity is None else kv_capacity, w.rms_eps, w.rope_theta)
+
+
+class LayerWeights:
+    """Packed weights of one layer (device tensors owned here) and their moel_weights struct."""
+
+    def __init__(self, packed: Dict[str, torch.Tensor], ts: Dict[str, Optional[torch.Tensor]]):
+        self.packed = packed
+        self.ts = ts
+        self.struct = Weights(
+            _ptr(packed["gamma1"]), _ptr(packed["gamma2"]), _ptr(packed["w_qkv"]), _ptr(packed["w_o"]),
+            _ptr(packed["w_router"]), _ptr(packed["w_pool"]), _ptr(packed["w_unpool"]),
+            _ptr(packed["w_gate"]), _ptr(packed["w_up"]), _ptr(packed["w_down"]),
+            _ptr(ts["gate"]), _ptr(ts["up"]), _ptr(ts["down"]))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.packed.values())
+
+
+class Plan:
+    def __init__(self, cfg: Config):
+        self.cfg = cfg
+        h = ctypes.c_void_p()
+        _check(lib().moel_plan_create(ctypes.byref(cfg), ctypes.byref(h)), "moel_plan_create")
+        self.handle = h
+
+    def close(self):
+        if self.handle:
+            lib().moel_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def workgroups(self) -> int:
+        return lib().moel_plan_workgroups(self.handle)
+
+    def status(self) -> int:
+        return lib().moel_plan_status(self.handle)
+
+    def set_abort(self, flag: bool, stream=None):
+        _check(lib().moel_plan_set_abort(self.handle, int(flag), _stream(stream)), "moel_plan_set_abort")
+
+    # ---- packing -------------------------------------------------------------------------
+    def pack_dense(self, src: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.Tensor:
+        assert src.dtype == torch.bfloat16 and src.is_contiguous() and src.dim() == 2
+        N, K = src.shape
+        dst = torch.empty(lib().moel_packed_dense_bytes(N, K), dtype=torch.uint8, device=src.device)
+        _check(lib().moel_pack_dense(_ptr(src), N, K, rope_head_dim, _ptr(dst), _stream(stream)),
+               "moel_pack_dense")
+        return dst
+
+    def pack_experts(self, which: int, src: torch.Tensor, scales: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+        assert src.is_contiguous() and (scales is None or scales.is_contiguous())
+        n = lib().moel_packed_experts_bytes(ctypes.byref(self.cfg), which)
+        dst = torch.empty(n, dtype=torch.uint8, device=src.device)
+        _check(lib().moel_pack_experts(ctypes.byref(self.cfg), which, _ptr(src), _ptr(scales), _ptr(dst),
+                                       _stream(stream)), "moel_pack_experts")
+        return dst
+
+    def pack_layer(self, t: Dict[str, torch.Tensor], stream=None) -> LayerWeights:
+        """Packs the canonical tensors of synth.make_layer into the kernels' layouts."""
+        c = self.cfg
+        packed = {
+            "gamma1": t["gamma1"].contiguous(), "gamma2": t["gamma2"].contiguous(),
+            "w_qkv": self.pack_dense(t["w_qkv"], rope_head_dim=c.head_dim, stream=stream),
+            "w_o": self.pack_dense(t["w_o"], stream=stream),
+            "w_router": self.pack_dense(t["w_router"], stream=stream),
+            "w_pool": self.pack_dense(t["w_pool"], stream=stream),
+            "w_unpool": self.pack_dense(t["w_unpool"], stream=stream),
+        }
+        ts = {"gate": None, "up": None, "down": None}
+        for which, m in enumerate(("gate", "up", "down")):
+            if c.expert_dtype == MOEL_EXPERT_BF16:
+                packed["w_" + m] = self.pack_experts(which, t[m], None, stream=stream)
+            else:
+                packed["w_" + m] = self.pack_experts(which, t[m + "_codes"], t[m + "_scales"], stream=stream)
+                ts[m] = t[m + "_ts"].contiguous()
+        return LayerWeights(packed, ts)
+
+    # ---- the step ------------------------------------------------------------------------
+    def layer_decode(self, lw: LayerWeights, k_cache: torch.Tensor, v_cache: torch.Tensor, x: torch.Tensor,
+                     pos: int, window: int, y: torch.Tensor, dbg: Optional[Dict[str, torch.Tensor]] = None,
+                     fused: bool = True, stream=None, T: Optional[int] = None) -> None:
+        T = x.shape[0] if T is None else T
+        d = None
+        if dbg is not None:
+            d = Debug(_ptr(dbg.get("expert_idx")), _ptr(dbg.get("gates")), _ptr(dbg.get("router_logits")),
+                      _ptr(dbg.get("timestamps")))
+        fn = lib().moel_layer_decode if fused else lib().moel_layer_decode_unfused
+        _check(fn(self.handle, ctypes.byref(lw.struct), _ptr(k_cache), _ptr(v_cache), _ptr(x), T, pos, window,
+                  _ptr(y), None if d is None else ctypes.byref(d), _stream(stream)),
+               "moel_layer_decode" if fused else "moel_layer_decode_unfused")

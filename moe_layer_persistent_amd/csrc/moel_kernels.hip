@@ -1,0 +1,517 @@
+// Kernels (persistent layer launch, one-kernel-per-step chain, weight packing) and the
+// host side of the C ABI declared in include/moel.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "../../include/moel.h"
+#include "moel_phases.h"
+
+using namespace moel;
+
+// =========================================================================================
+// device: persistent launch
+// =========================================================================================
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_abort;
+  const int wg = blockIdx.x;
+  if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
+  __syncthreads();
+  const bool run = s_abort == 0;
+  unsigned bar = 0;
+  auto sync = [&]() {
+    bar += (unsigned)p.nwg;
+    grid_barrier(p, bar);
+  };
+  if (run) phase_norm1(p, wg);
+  stamp(p, kPhNorm1);
+  sync();
+  if (run) phase_qkv(p, wg, smem);
+  stamp(p, kPhQkv);
+  sync();
+  if (run) phase_attn<D>(p, wg, smem);
+  stamp(p, kPhAttn);
+  sync();
+  if (run) phase_attn_merge(p, wg);
+  stamp(p, kPhAttnMerge);
+  sync();
+  if (run) phase_oproj(p, wg, smem);
+  stamp(p, kPhOproj);
+  sync();
+  if (run) phase_router_pool(p, wg, smem);
+  stamp(p, kPhRouterPool);
+  sync();
+  if (run) {
+    compute_routing(p, route_tables(smem), wg == 0);
+    phase_experts<true>(p, wg, smem);
+  }
+  stamp(p, kPhGemm1);
+  sync();
+  if (run) phase_experts<false>(p, wg, smem);
+  stamp(p, kPhGemm2);
+  sync();
+  if (run) phase_combine(p, wg, smem);
+  stamp(p, kPhCombine);
+  sync();
+  if (run) phase_unpool(p, wg, smem);
+  stamp(p, kPhUnpool);
+  // leave: the last workgroup out resets the barrier words for the next launch
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    if (!run && wg == 0)
+      __hip_atomic_store(p.ctrl + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned prev =
+        __hip_atomic_fetch_add(p.ctrl + kExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (prev == (unsigned)p.nwg - 1) {
+      __hip_atomic_store(p.ctrl + kBar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(p.ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+// =========================================================================================
+// device: one kernel per step (ablation / fallback chain)
+// =========================================================================================
+template <int PH, int D>
+__global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int s_abort;
+  const int wg = blockIdx.x;
+  if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
+  __syncthreads();
+  if (s_abort) {
+    if (wg == 0 && threadIdx.x == 0)
+      __hip_atomic_store(p.ctrl + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return;
+  }
+  if constexpr (PH == kPhNorm1) phase_norm1(p, wg);
+  if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
+  if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
+  if constexpr (PH == kPhAttnMerge) phase_attn_merge(p, wg);
+  if constexpr (PH == kPhOproj) phase_oproj(p, wg, smem);
+  if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, smem);
+  if constexpr (PH == kPhGemm1) {
+    compute_routing(p, route_tables(smem), wg == 0);
+    phase_experts<true>(p, wg, smem);
+  }
+  if constexpr (PH == kPhGemm2) {
+    compute_routing(p, route_tables(smem), false);
+    phase_experts<false>(p, wg, smem);
+  }
+  if constexpr (PH == kPhCombine) {
+    compute_routing(p, route_tables(smem), false);
+    phase_combine(p, wg, smem);
+  }
+  if constexpr (PH == kPhUnpool) phase_unpool(p, wg, smem);
+  stamp(p, PH);
+}
+
+// =========================================================================================
+// device: weight packing and small utilities
+// =========================================================================================
+__global__ void k_pack_dense(const uint16_t* __restrict__ src, int N, int K, int rope_D,
+                             uint8_t* __restrict__ dst, size_t nchunks) {
+  const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nchunks) return;
+  const int S = K / 32;
+  const int lane = (int)(c % 64);
+  const size_t step = (c / 64) % S;
+  const size_t tile = c / (64 * (size_t)S);
+  const int R = (int)(tile * 16 + (lane & 15));
+  int row = R;
+  if (rope_D > 0) {
+    const int head = R / rope_D, r = R % rope_D;
+    row = head * rope_D + (r >> 1) + (r & 1) * (rope_D / 2);
+  }
+  const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)row * K + step * 32 + 8 * (lane >> 4));
+  *reinterpret_cast<u32x4*>(dst + c * 16) = v;
+}
+
+// one thread per (expert, 64-row tile, k pair, lane)
+__global__ void k_pack_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales,
+                             int N, int K, uint8_t* __restrict__ dst, size_t nthreads) {
+  const size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= nthreads) return;
+  const int lane = (int)(c % 64);
+  const size_t pairs = K / 64;
+  const size_t pp = (c / 64) % pairs;
+  const size_t tile_all = c / (64 * pairs);  // expert * (N/64) + tile
+  const size_t row_all = tile_all * 64 + lane;
+  const uint8_t* crow = codes + row_all * (size_t)(K / 2);
+  const uint8_t* srow = scales + row_all * (size_t)(K / 16);
+  uint8_t* out = dst + tile_all * (size_t)(36 * K) + pp * 2304;
+  *reinterpret_cast<u32x4*>(out + lane * 16) = *reinterpret_cast<const u32x4*>(crow + (2 * pp) * 16);
+  *reinterpret_cast<u32x4*>(out + 1024 + lane * 16) =
+      *reinterpret_cast<const u32x4*>(crow + (2 * pp + 1) * 16);
+  *reinterpret_cast<uint32_t*>(out + 2048 + lane * 4) = *reinterpret_cast<const uint32_t*>(srow + pp * 4);
+}
+
+__global__ void k_set_word(unsigned* w, unsigned v) { *w = v; }
+
+// =========================================================================================
+// host
+// =========================================================================================
+struct moel_plan {
+  moel_config cfg;
+  int device;
+  int nwg;
+  int grp;
+  void* ws;
+  size_t ws_bytes;
+  LayerParams base;  // shape + scratch pointers
+  size_t lds_fused;
+  size_t lds_phase[kNumPhases];
+};
+
+namespace {
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int D>
+size_t attn_lds() { return sizeof(AttnLds<D>); }
+
+size_t lds_for_phase(int ph, int D) {
+  size_t body = 0;
+  switch (ph) {
+    case kPhNorm1: case kPhAttnMerge: case kPhCombine: body = 0; break;
+    case kPhAttn: body = D == 64 ? attn_lds<64>() : attn_lds<128>(); break;
+    case kPhGemm1: case kPhGemm2: body = sizeof(Fp4Lds) > sizeof(DenseLds) ? sizeof(Fp4Lds) : sizeof(DenseLds); break;
+    default: body = sizeof(DenseLds); break;
+  }
+  return kRouteBytes + body;
+}
+
+bool hip_ok(hipError_t e) {
+  if (e != hipSuccess) {
+    if (std::getenv("MOEL_LOG")) std::fprintf(stderr, "moel: HIP error %s\n", hipGetErrorString(e));
+    return false;
+  }
+  return true;
+}
+
+template <int D>
+const void* fused_fn() { return reinterpret_cast<const void*>(&k_layer_fused<D>); }
+
+template <int D>
+const void* phase_fn(int ph) {
+  switch (ph) {
+    case 0: return reinterpret_cast<const void*>(&k_layer_phase<0, D>);
+    case 1: return reinterpret_cast<const void*>(&k_layer_phase<1, D>);
+    case 2: return reinterpret_cast<const void*>(&k_layer_phase<2, D>);
+    case 3: return reinterpret_cast<const void*>(&k_layer_phase<3, D>);
+    case 4: return reinterpret_cast<const void*>(&k_layer_phase<4, D>);
+    case 5: return reinterpret_cast<const void*>(&k_layer_phase<5, D>);
+    case 6: return reinterpret_cast<const void*>(&k_layer_phase<6, D>);
+    case 7: return reinterpret_cast<const void*>(&k_layer_phase<7, D>);
+    case 8: return reinterpret_cast<const void*>(&k_layer_phase<8, D>);
+    default: return reinterpret_cast<const void*>(&k_layer_phase<9, D>);
+  }
+}
+
+moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                         const float* x, int32_t T, int32_t pos, int32_t window, float* y,
+                         const moel_debug* dbg, LayerParams& p) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  moel_status st = moel_validate_call(&plan->cfg, w, k_cache, v_cache, x, T, pos, window, y);
+  if (st != MOEL_OK) return st;
+  p = plan->base;
+  p.T = T;
+  p.pos = pos;
+  p.window = window;
+  const int lo = window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
+  const int nkeys = pos + T - lo;
+  int maxc = plan->nwg / plan->cfg.n_kv_heads;
+  if (maxc < 1) maxc = 1;
+  int nch = (nkeys + 255) / 256;
+  if (nch > maxc) nch = maxc;
+  if (nch < 1) nch = 1;
+  const int chunk = (nkeys + nch - 1) / nch;
+  p.attn_lo = lo;
+  p.attn_nkeys = nkeys;
+  p.attn_chunk = chunk;
+  p.attn_nchunks = (nkeys + chunk - 1) / chunk;
+  p.gamma1 = static_cast<const uint16_t*>(w->gamma1);
+  p.gamma2 = static_cast<const uint16_t*>(w->gamma2);
+  p.w_qkv = static_cast<const uint8_t*>(w->w_qkv);
+  p.w_o = static_cast<const uint8_t*>(w->w_o);
+  p.w_router = static_cast<const uint8_t*>(w->w_router);
+  p.w_pool = static_cast<const uint8_t*>(w->w_pool);
+  p.w_unpool = static_cast<const uint8_t*>(w->w_unpool);
+  p.w_gate = static_cast<const uint8_t*>(w->w_gate);
+  p.w_up = static_cast<const uint8_t*>(w->w_up);
+  p.w_down = static_cast<const uint8_t*>(w->w_down);
+  p.ts_gate = w->ts_gate;
+  p.ts_up = w->ts_up;
+  p.ts_down = w->ts_down;
+  p.k_cache = static_cast<uint16_t*>(k_cache);
+  p.v_cache = static_cast<uint16_t*>(v_cache);
+  p.x = x;
+  p.y = y;
+  p.dbg_idx = dbg ? dbg->expert_idx : nullptr;
+  p.dbg_gates = dbg ? dbg->gates : nullptr;
+  p.dbg_logits = dbg ? dbg->router_logits : nullptr;
+  p.dbg_ts = dbg ? reinterpret_cast<unsigned long long*>(dbg->timestamps) : nullptr;
+  return MOEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
+  if (out == nullptr) return MOEL_ERR_ARG;
+  moel_status st = moel_validate_config(cfg);
+  if (st != MOEL_OK) return st;
+  int dev = 0;
+  if (!hip_ok(hipGetDevice(&dev))) return MOEL_ERR_UNSUPPORTED;
+  hipDeviceProp_t prop;
+  if (!hip_ok(hipGetDeviceProperties(&prop, dev))) return MOEL_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOEL_ERR_UNSUPPORTED;
+  int coop = 0;
+  hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (!coop) return MOEL_ERR_UNSUPPORTED;
+
+  moel_plan* plan = new (std::nothrow) moel_plan();
+  if (plan == nullptr) return MOEL_ERR_HIP;
+  plan->cfg = *cfg;
+  plan->device = dev;
+  plan->nwg = prop.multiProcessorCount;
+  plan->grp = cfg->n_q_heads / cfg->n_kv_heads;
+  const int nwg = plan->nwg, D = cfg->head_dim, Hq = cfg->n_q_heads, H = cfg->hidden;
+  const int P = cfg->pooled, I = cfg->inter, E = cfg->n_experts, k = cfg->top_k;
+
+  // workspace layout
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t o_ctrl = take(256);
+  const size_t o_ss1 = take((size_t)nwg * kMaxT * 4);
+  const size_t o_ss2 = take((size_t)nwg * kMaxT * 4);
+  const size_t o_q = take((size_t)kMaxT * Hq * D * 2);
+  const size_t o_ao = take((size_t)nwg * plan->grp * kMaxT * D * 4);
+  const size_t o_aml = take((size_t)nwg * plan->grp * kMaxT * 2 * 4);
+  const size_t o_o = take((size_t)kMaxT * Hq * D * 2);
+  const size_t o_h = take((size_t)kMaxT * H * 4);
+  const size_t o_lg = take((size_t)kMaxT * E * 4);
+  const size_t o_pl = take((size_t)kMaxT * P * 2);
+  const size_t o_a = take((size_t)kMaxT * k * I * 2);
+  const size_t o_d = take((size_t)kMaxT * k * P * 4);
+  const size_t o_m = take((size_t)kMaxT * P * 2);
+  const size_t o_cos = take((size_t)cfg->kv_capacity * (D / 2) * 4);
+  const size_t o_sin = take((size_t)cfg->kv_capacity * (D / 2) * 4);
+  plan->ws_bytes = off;
+  if (!hip_ok(hipMalloc(&plan->ws, off))) {
+    delete plan;
+    return MOEL_ERR_HIP;
+  }
+  char* ws = static_cast<char*>(plan->ws);
+  if (!hip_ok(hipMemset(ws, 0, off))) {
+    hipFree(plan->ws);
+    delete plan;
+    return MOEL_ERR_HIP;
+  }
+  // RoPE table: angle = position * theta^(-2i/D), evaluated in double, stored as float
+  {
+    const size_t n = (size_t)cfg->kv_capacity * (D / 2);
+    float* hc = static_cast<float*>(std::malloc(n * 4));
+    float* hs = static_cast<float*>(std::malloc(n * 4));
+    if (hc == nullptr || hs == nullptr) {
+      std::free(hc);
+      std::free(hs);
+      hipFree(plan->ws);
+      delete plan;
+      return MOEL_ERR_HIP;
+    }
+    for (int i = 0; i < D / 2; ++i) {
+      const double f = std::pow((double)cfg->rope_theta, -(2.0 * i) / (double)D);
+      for (int ps = 0; ps < cfg->kv_capacity; ++ps) {
+        const double a = (double)ps * f;
+        hc[(size_t)ps * (D / 2) + i] = (float)std::cos(a);
+        hs[(size_t)ps * (D / 2) + i] = (float)std::sin(a);
+      }
+    }
+    const bool ok = hip_ok(hipMemcpy(ws + o_cos, hc, n * 4, hipMemcpyHostToDevice)) &&
+                    hip_ok(hipMemcpy(ws + o_sin, hs, n * 4, hipMemcpyHostToDevice));
+    std::free(hc);
+    std::free(hs);
+    if (!ok) {
+      hipFree(plan->ws);
+      delete plan;
+      return MOEL_ERR_HIP;
+    }
+  }
+  LayerParams& b = plan->base;
+  std::memset(&b, 0, sizeof(b));
+  b.H = H;
+  b.Hq = Hq;
+  b.Hkv = cfg->n_kv_heads;
+  b.D = D;
+  b.P = P;
+  b.I = I;
+  b.E = E;
+  b.topk = k;
+  b.n_shards = cfg->n_shards;
+  b.rank = cfg->shard_rank;
+  b.I_loc = I / cfg->n_shards;
+  b.P_loc = P / cfg->n_shards;
+  b.kv_cap = cfg->kv_capacity;
+  b.expert_dtype = cfg->expert_dtype;
+  b.eps = cfg->rms_eps;
+  b.nwg = nwg;
+  b.stride_gate = moel_packed_experts_bytes(cfg, 0) / (size_t)E;
+  b.stride_up = moel_packed_experts_bytes(cfg, 1) / (size_t)E;
+  b.stride_down = moel_packed_experts_bytes(cfg, 2) / (size_t)E;
+  b.ctrl = reinterpret_cast<unsigned*>(ws + o_ctrl);
+  b.ss1 = reinterpret_cast<float*>(ws + o_ss1);
+  b.ss2 = reinterpret_cast<float*>(ws + o_ss2);
+  b.q_buf = reinterpret_cast<uint16_t*>(ws + o_q);
+  b.attn_o = reinterpret_cast<float*>(ws + o_ao);
+  b.attn_ml = reinterpret_cast<float*>(ws + o_aml);
+  b.o_buf = reinterpret_cast<uint16_t*>(ws + o_o);
+  b.h_buf = reinterpret_cast<float*>(ws + o_h);
+  b.logits = reinterpret_cast<float*>(ws + o_lg);
+  b.pl = reinterpret_cast<uint16_t*>(ws + o_pl);
+  b.a_buf = reinterpret_cast<uint16_t*>(ws + o_a);
+  b.d_buf = reinterpret_cast<float*>(ws + o_d);
+  b.m_buf = reinterpret_cast<uint16_t*>(ws + o_m);
+  b.rope_cos = reinterpret_cast<const float*>(ws + o_cos);
+  b.rope_sin = reinterpret_cast<const float*>(ws + o_sin);
+
+  // LDS budgets
+  size_t mx = 0;
+  for (int ph = 0; ph < kNumPhases; ++ph) {
+    plan->lds_phase[ph] = lds_for_phase(ph, D);
+    if (plan->lds_phase[ph] > mx) mx = plan->lds_phase[ph];
+  }
+  plan->lds_fused = mx;
+  bool ok = true;
+  if (D == 64) {
+    ok = ok && hip_ok(hipFuncSetAttribute(fused_fn<64>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)mx));
+    for (int ph = 0; ph < kNumPhases; ++ph)
+      ok = ok && hip_ok(hipFuncSetAttribute(phase_fn<64>(ph), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            (int)plan->lds_phase[ph]));
+  } else {
+    ok = ok && hip_ok(hipFuncSetAttribute(fused_fn<128>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)mx));
+    for (int ph = 0; ph < kNumPhases; ++ph)
+      ok = ok && hip_ok(hipFuncSetAttribute(phase_fn<128>(ph), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            (int)plan->lds_phase[ph]));
+  }
+  if (!ok) {
+    hipFree(plan->ws);
+    delete plan;
+    return MOEL_ERR_HIP;
+  }
+  if (std::getenv("MOEL_LOG"))
+    std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu\n",
+                 H, Hq, cfg->n_kv_heads, D, P, I, E, k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx);
+  *out = plan;
+  return MOEL_OK;
+}
+
+moel_status moel_plan_destroy(moel_plan* plan) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  hipError_t e = hipFree(plan->ws);
+  delete plan;
+  return e == hipSuccess ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+int32_t moel_plan_workgroups(const moel_plan* plan) { return plan ? plan->nwg : 0; }
+
+moel_status moel_plan_status(moel_plan* plan) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  if (!hip_ok(hipDeviceSynchronize())) return MOEL_ERR_HIP;
+  unsigned words[4] = {0, 0, 0, 0};
+  if (!hip_ok(hipMemcpy(words, plan->base.ctrl, sizeof(words), hipMemcpyDeviceToHost))) return MOEL_ERR_HIP;
+  if (words[kStatus] == 0) return MOEL_OK;
+  const unsigned keep_abort = words[kAbort];
+  unsigned clear[4] = {0, 0, 0, keep_abort};
+  if (!hip_ok(hipMemcpy(plan->base.ctrl, clear, sizeof(clear), hipMemcpyHostToDevice))) return MOEL_ERR_HIP;
+  return words[kStatus] == MOEL_DEV_TIMEOUT ? MOEL_ERR_TIMEOUT : MOEL_ERR_ABORTED;
+}
+
+moel_status moel_plan_set_abort(moel_plan* plan, int32_t flag, void* stream) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  hipLaunchKernelGGL(k_set_word, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),
+                     plan->base.ctrl + kAbort, flag ? 1u : 0u);
+  return hip_ok(hipGetLastError()) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+moel_status moel_pack_dense(const void* src, int32_t N, int32_t K, int32_t rope_head_dim, void* dst,
+                            void* stream) {
+  if (src == nullptr || dst == nullptr || N <= 0 || K <= 0) return MOEL_ERR_ARG;
+  if (N % 16 != 0 || K % 32 != 0) return MOEL_ERR_SHAPE;
+  if (rope_head_dim < 0 || (rope_head_dim > 0 && (N % rope_head_dim != 0 || rope_head_dim % 2 != 0)))
+    return MOEL_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return MOEL_ERR_ALIGN;
+  const size_t n = (size_t)N * K / 8;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(k_pack_dense, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<const uint16_t*>(src), N, K, rope_head_dim, static_cast<uint8_t*>(dst), n);
+  return hip_ok(hipGetLastError()) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+moel_status moel_pack_experts(const moel_config* cfg, int32_t which, const void* src, const void* scales,
+                              void* dst, void* stream) {
+  moel_status st = moel_validate_config(cfg);
+  if (st != MOEL_OK) return st;
+  if (which < 0 || which > 2 || src == nullptr || dst == nullptr) return MOEL_ERR_ARG;
+  const int E = cfg->n_experts;
+  const int N = which < 2 ? cfg->inter / cfg->n_shards : cfg->pooled / cfg->n_shards;
+  const int K = which < 2 ? cfg->pooled : cfg->inter;
+  if ((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15) return MOEL_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (cfg->expert_dtype == MOEL_EXPERT_BF16) {
+    const size_t n = (size_t)E * N * K / 8;  // dense layout of the stacked [E*N, K] matrix
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(k_pack_dense, dim3(blocks), dim3(256), 0, s, static_cast<const uint16_t*>(src), E * N, K,
+                       0, static_cast<uint8_t*>(dst), n);
+  } else {
+    if (scales == nullptr) return MOEL_ERR_ARG;
+    if (reinterpret_cast<uintptr_t>(scales) & 3) return MOEL_ERR_ALIGN;
+    const size_t n = (size_t)E * (N / 64) * (K / 64) * 64;
+    const unsigned blocks = (unsigned)((n + 255) / 256);
+    hipLaunchKernelGGL(k_pack_nvfp4, dim3(blocks), dim3(256), 0, s, static_cast<const uint8_t*>(src),
+                       static_cast<const uint8_t*>(scales), N, K, static_cast<uint8_t*>(dst), n);
+  }
+  return hip_ok(hipGetLastError()) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+moel_status moel_layer_decode(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                              const float* x, int32_t T, int32_t pos, int32_t window, float* y,
+                              const moel_debug* dbg, void* stream) {
+  LayerParams p;
+  moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, y, dbg, p);
+  if (st != MOEL_OK) return st;
+  void* args[] = {&p};
+  const void* fn = plan->cfg.head_dim == 64 ? fused_fn<64>() : fused_fn<128>();
+  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(plan->nwg), dim3(kThreads), args,
+                                            (unsigned)plan->lds_fused, static_cast<hipStream_t>(stream));
+  return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                                      const float* x, int32_t T, int32_t pos, int32_t window, float* y,
+                                      const moel_debug* dbg, void* stream) {
+  LayerParams p;
+  moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, y, dbg, p);
+  if (st != MOEL_OK) return st;
+  void* args[] = {&p};
+  for (int ph = 0; ph < kNumPhases; ++ph) {
+    const void* fn = plan->cfg.head_dim == 64 ? phase_fn<64>(ph) : phase_fn<128>(ph);
+    hipError_t e = hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_phase[ph],
+                                   static_cast<hipStream_t>(stream));
+    if (!hip_ok(e)) return MOEL_ERR_HIP;
+  }
+  return MOEL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,81 @@
+// Kernel argument block shared by the host launcher and the device phases.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+#define MOEL_N_STAMPS_DEV 16
+#define MOEL_DEV_TIMEOUT 1u
+#define MOEL_DEV_ABORTED 2u
+
+namespace moel {
+
+// Phase ids: index of the timestamp slot written at the end of each phase, and of the
+// unfused chain's kernels.
+enum Phase {
+  kPhNorm1 = 0,     // per-workgroup partial sums of x^2
+  kPhQkv = 1,       // QKV projection + RoPE + q store + KV-cache write
+  kPhAttn = 2,      // attention partials per (kv head, key chunk)
+  kPhAttnMerge = 3, // merge of the key-chunk partials -> o (bf16)
+  kPhOproj = 4,     // o-projection + residual -> h, partial sums of h^2
+  kPhRouterPool = 5,// router logits and pooler
+  kPhGemm1 = 6,     // routing tables + expert gate/up + SwiGLU -> a (bf16)
+  kPhGemm2 = 7,     // expert down projection -> d (fp32)
+  kPhCombine = 8,   // gate-weighted combine over a token's slots -> m (bf16)
+  kPhUnpool = 9,    // unpooler + residual -> y
+  kNumPhases = 10
+};
+
+struct LayerParams {
+  // shape
+  int H, Hq, Hkv, D, P, I, E, topk;
+  int n_shards, rank, I_loc, P_loc, kv_cap, expert_dtype;
+  float eps;
+  // call
+  int T, pos, window;
+  int nwg;
+  // attention decomposition (per call)
+  int attn_lo, attn_nkeys, attn_chunk, attn_nchunks;
+  // weights (packed)
+  const uint16_t* gamma1;
+  const uint16_t* gamma2;
+  const uint8_t* w_qkv;
+  const uint8_t* w_o;
+  const uint8_t* w_router;
+  const uint8_t* w_pool;
+  const uint8_t* w_unpool;
+  const uint8_t* w_gate;
+  const uint8_t* w_up;
+  const uint8_t* w_down;
+  const float* ts_gate;
+  const float* ts_up;
+  const float* ts_down;
+  size_t stride_gate, stride_up, stride_down;  // packed bytes per expert
+  // caches and io
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  const float* x;
+  float* y;
+  const float* rope_cos;  // [kv_cap][D/2]
+  const float* rope_sin;
+  // scratch (plan workspace)
+  float* ss1;       // [nwg][16]
+  float* ss2;       // [nwg][16]
+  uint16_t* q_buf;  // [16][Hq*D]
+  float* attn_o;    // [items][grp][16][D]
+  float* attn_ml;   // [items][grp][16][2]
+  uint16_t* o_buf;  // [16][Hq*D]
+  float* h_buf;     // [16][H]
+  float* logits;    // [16][E]
+  uint16_t* pl;     // [16][P]
+  uint16_t* a_buf;  // [16*topk][I]
+  float* d_buf;     // [16*topk][P]
+  uint16_t* m_buf;  // [16][P]
+  unsigned* ctrl;   // barrier counter, exit counter, status, abort
+  // debug (optional)
+  int* dbg_idx;
+  float* dbg_gates;
+  float* dbg_logits;
+  unsigned long long* dbg_ts;
+};
+
+}  // namespace moel

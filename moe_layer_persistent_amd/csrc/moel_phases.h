@@ -1,0 +1,906 @@
+// The steps of one MoE decoder layer's verify pass as workgroup-level device functions.
+//
+// Every phase is written for a grid of `nwg` workgroups of 512 threads (8 wavefronts) and
+// splits its work by workgroup index, so the same function serves both the persistent
+// launch (phases separated by grid barriers) and the one-kernel-per-step chain.
+//
+// Packed weight layouts (produced by the pack kernels in moel_kernels.hip):
+//   dense bf16 [N, K]  : 16-row tiles; per tile K/32 steps of 1 KiB; in a step, lane l holds
+//                        the 8 bf16 of row (l % 16), k = 32*step + 8*(l / 16) + 0..7 -- the
+//                        B operand of one 16x16x32 MFMA.
+//   NVFP4 expert [N, K]: 64-row tiles; per tile K/64 "pairs" of 2304 bytes: two 1 KiB code
+//                        steps (lane l: 32 codes of row l, k = 32*step + 0..31, low nibble
+//                        first) then 256 bytes of scales (lane l: the 4 E4M3 block scales of
+//                        row l covering the pair's 64 k).
+#pragma once
+#include "moel_device.h"
+
+namespace moel {
+
+// ------------------------------------------------------------------------------------------
+// LDS layout: routing tables at offset 0 (kept across the MoE phases of the persistent
+// launch), phase scratch after them.
+// ------------------------------------------------------------------------------------------
+struct RouteTables {
+  int idx[kMaxT * 8];          // [T][k] selected expert per slot (slot = t*k + kappa)
+  float gate[kMaxT * 8];       // [T][k]
+  int n_active;                // distinct experts hit by the step
+  int active_e[kMaxT * 8];     // ascending expert ids
+  int active_off[kMaxT * 8 + 1];
+  int slots[kMaxT * 8];        // slots grouped by expert (ascending), slots ascending within
+  int cnt[512];                // per-expert slot count
+  int off[512];                // per-expert first position in `slots`
+  int rank[512];               // per-expert index into active_e (valid when cnt > 0)
+};
+constexpr int kRouteBytes = (sizeof(RouteTables) + 255) & ~255;
+
+__device__ __forceinline__ RouteTables& route_tables(char* smem) {
+  return *reinterpret_cast<RouteTables*>(smem);
+}
+__device__ __forceinline__ char* phase_smem(char* smem) { return smem + kRouteBytes; }
+
+// ------------------------------------------------------------------------------------------
+// RMSNorm statistics
+// ------------------------------------------------------------------------------------------
+// Partial sums of x^2 over this workgroup's slice of the hidden dimension, per token.
+__device__ void phase_norm1(const LayerParams& p, int wg) {
+  const int tid = threadIdx.x;
+  const int t = tid >> 5, sub = tid & 31;  // 16 tokens x 32 lanes
+  const int k0 = (int)((long)wg * p.H / p.nwg), k1 = (int)((long)(wg + 1) * p.H / p.nwg);
+  float s = 0.f;
+  if (t < p.T)
+    for (int k = k0 + sub; k < k1; k += 32) {
+      float v = p.x[(size_t)t * p.H + k];
+      s = fmaf(v, v, s);
+    }
+#pragma unroll
+  for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
+  if (sub == 0) p.ss1[wg * kMaxT + t] = s;
+}
+
+// rstd of every token from the per-workgroup partial sums, in a fixed summation order
+// (32 interleaved subsets, then the subsets in order).  `tmp` is 32*16 floats of LDS,
+// `out` 16 floats of LDS.  Returns this lane's token's value.
+__device__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp, float* out) {
+  const int t = threadIdx.x & 15, q = threadIdx.x >> 4;  // q = 0..31
+  float s = 0.f;
+  for (int w = q; w < nwg; w += 32) s += ss[w * kMaxT + t];
+  tmp[q * kMaxT + t] = s;
+  lds_barrier();
+  if (threadIdx.x < kMaxT) {
+    float a = 0.f;
+    for (int j = 0; j < 32; ++j) a += tmp[j * kMaxT + threadIdx.x];
+    out[threadIdx.x] = 1.0f / sqrtf(a / (float)H + eps);
+  }
+  lds_barrier();
+  return out[lane_id() & 15];
+}
+
+// ------------------------------------------------------------------------------------------
+// A-operand sources of the dense contractions: lane supplies A[token][k .. k+7] as 8 bf16.
+// ------------------------------------------------------------------------------------------
+struct ANorm {  // r(v * rstd * gamma) computed on the fly from an fp32 row
+  const float* v;
+  int ld;
+  const uint16_t* gamma;
+  float rstd;  // of this lane's token
+  int T;
+  __device__ __forceinline__ u32x4 load(int tok, int k) const {
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (tok < T) {
+      const float* src = v + (size_t)tok * ld + k;
+      float4 a = *reinterpret_cast<const float4*>(src);
+      float4 b = *reinterpret_cast<const float4*>(src + 4);
+      u32x4 g = ldg16(gamma + k);
+      r[0] = pack2bf(a.x * rstd * bf_lo(g[0]), a.y * rstd * bf_hi(g[0]));
+      r[1] = pack2bf(a.z * rstd * bf_lo(g[1]), a.w * rstd * bf_hi(g[1]));
+      r[2] = pack2bf(b.x * rstd * bf_lo(g[2]), b.y * rstd * bf_hi(g[2]));
+      r[3] = pack2bf(b.z * rstd * bf_lo(g[3]), b.w * rstd * bf_hi(g[3]));
+    }
+    return r;
+  }
+};
+struct ABf16 {  // a stored bf16 row
+  const uint16_t* v;
+  int ld;
+  int T;
+  __device__ __forceinline__ u32x4 load(int tok, int k) const {
+    u32x4 r = {0u, 0u, 0u, 0u};
+    if (tok < T) r = ldg16(v + (size_t)tok * ld + k);
+    return r;
+  }
+};
+
+// ------------------------------------------------------------------------------------------
+// Dense contraction over a workgroup's rows: out[tok][row] = sum_k A[tok][k] * W[row][k].
+// Rows are assigned in octets (8 rows) so that half tiles never share a cache line.
+// Up to 4 tiles of 16 rows per pass; the 8 waves split K; partials meet in LDS.
+// On return `fin` holds [tile j][row r][tok] sums for tiles t_first .. t_first+ntiles-1.
+// ------------------------------------------------------------------------------------------
+struct DenseLds {
+  f32x4 red[kWaves * 4 * 64];   // 32 KiB
+  float fin[4 * 16 * kMaxT];    // 4 KiB
+  float aux[4 * 16 * kMaxT];    // 4 KiB (epilogue scratch)
+};
+
+template <class ASrc>
+__device__ void dense_pass(const uint8_t* w0, int tiles0, const uint8_t* w1, int K, int t_first,
+                           int ntiles, int oct_lo, int oct_hi, const ASrc& A, DenseLds& L) {
+  const int lane = lane_id(), wv = wave_id();
+  const int S = K >> 5;
+  const int nkw = S < kWaves ? S : kWaves;
+  f32x4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (wv < nkw) {
+    const int sa = wv * S / nkw, sb = (wv + 1) * S / nkw;
+    const int tok = lane & 15, kq = 8 * (lane >> 4);
+    const uint8_t* base[4];
+    bool on[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int t = t_first + j;
+      const int oct = 2 * t + ((lane & 15) >> 3);
+      on[j] = (j < ntiles) && oct >= oct_lo && oct < oct_hi;
+      base[j] = (t < tiles0 ? w0 + (size_t)t * S * 1024 : w1 + (size_t)(t - tiles0) * S * 1024) +
+                lane * 16;
+    }
+    // two-stage software pipeline over k steps
+    u32x4 a_cur = A.load(tok, 32 * sa + kq), w_cur[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w_cur[j] = on[j] ? ldg_stream(base[j] + (size_t)sa * 1024) : u32x4{0u, 0u, 0u, 0u};
+    for (int s = sa; s < sb; ++s) {
+      u32x4 a_nxt = {0u, 0u, 0u, 0u}, w_nxt[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w_nxt[j] = u32x4{0u, 0u, 0u, 0u};
+      if (s + 1 < sb) {
+        a_nxt = A.load(tok, 32 * (s + 1) + kq);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (on[j]) w_nxt[j] = ldg_stream(base[j] + (size_t)(s + 1) * 1024);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < ntiles) acc[j] = mfma16x16x32(a_cur, w_cur[j], acc[j]);
+      a_cur = a_nxt;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w_cur[j] = w_nxt[j];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) L.red[(wv * 4 + j) * 64 + lane] = acc[j];
+  }
+  lds_barrier();
+  for (int e = threadIdx.x; e < ntiles * 256; e += kThreads) {
+    const int j = e >> 8, ln = (e >> 2) & 63, r = e & 3;
+    float s = 0.f;
+    for (int w = 0; w < nkw; ++w) s += L.red[(w * 4 + j) * 64 + ln][r];
+    const int tok = 4 * (ln >> 4) + r, row = ln & 15;
+    L.fin[(j * 16 + row) * kMaxT + tok] = s;
+  }
+  lds_barrier();
+}
+
+// Octet range of a workgroup for a contraction with `tiles` 16-row tiles.
+__device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo, int& hi) {
+  const int n = 2 * tiles;
+  lo = (int)((long)wg * n / nwg);
+  hi = (int)((long)(wg + 1) * n / nwg);
+}
+
+// Runs dense_pass over the workgroup's rows in groups of <= 4 tiles and calls
+// epi(L, t_first, ntiles, oct_lo, oct_hi) after each group.
+template <class ASrc, class Epi>
+__device__ void dense_phase(const uint8_t* w0, int tiles0, const uint8_t* w1, int tiles1, int K,
+                            int wg, int nwg, const ASrc& A, DenseLds& L, Epi&& epi) {
+  int lo, hi;
+  octet_range(tiles0 + tiles1, wg, nwg, lo, hi);
+  if (lo >= hi) {
+    epi(L, 0, 0, lo, hi);
+    return;
+  }
+  const int tf = lo >> 1, tl = (hi - 1) >> 1;
+  for (int t = tf; t <= tl; t += 4) {
+    const int nt = (tl - t + 1) < 4 ? (tl - t + 1) : 4;
+    dense_pass(w0, tiles0, w1, K, t, nt, lo, hi, A, L);
+    epi(L, t, nt, lo, hi);
+    lds_barrier();
+  }
+}
+
+__device__ __forceinline__ bool octet_in(int row, int lo, int hi) {
+  const int o = row >> 3;
+  return o >= lo && o < hi;
+}
+
+// ------------------------------------------------------------------------------------------
+// QKV projection + RoPE + q store + KV-cache write.  w_qkv rows are packed with the
+// rotation partners (i, i + D/2) of every head interleaved: packed row 2i <-> canonical i,
+// packed row 2i+1 <-> canonical i + D/2.
+// ------------------------------------------------------------------------------------------
+__device__ void phase_qkv(const LayerParams& p, int wg, char* smem) {
+  DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
+  const float rs = wg_rstd(p.ss1, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
+  ANorm A{p.x, p.H, p.gamma1, rs, p.T};
+  const int tiles = (p.Hq + 2 * p.Hkv) * p.D / 16;
+  const int half = p.D >> 1;
+  dense_phase(p.w_qkv, tiles, nullptr, 0, p.H, wg, p.nwg, A, L,
+              [&](DenseLds& L, int tf, int nt, int lo, int hi) {
+                for (int e = threadIdx.x; e < nt * 8 * kMaxT; e += kThreads) {
+                  const int j = e / (8 * kMaxT), pr = (e / kMaxT) & 7, t = e % kMaxT;
+                  const int R = (tf + j) * 16 + 2 * pr;  // packed row (even)
+                  if (t >= p.T || !octet_in(R, lo, hi)) continue;
+                  const float a = L.fin[(j * 16 + 2 * pr) * kMaxT + t];
+                  const float b = L.fin[(j * 16 + 2 * pr + 1) * kMaxT + t];
+                  const int head = R / p.D, i = (R % p.D) >> 1;
+                  const int ps = p.pos + t;
+                  if (head < p.Hq + p.Hkv) {
+                    const float c = p.rope_cos[(size_t)ps * half + i];
+                    const float s = p.rope_sin[(size_t)ps * half + i];
+                    const float ra = a * c - b * s, rb = b * c + a * s;
+                    if (head < p.Hq) {
+                      uint16_t* q = p.q_buf + (size_t)t * p.Hq * p.D + head * p.D;
+                      q[i] = f2bf(ra);
+                      q[i + half] = f2bf(rb);
+                    } else {
+                      uint16_t* k = p.k_cache + ((size_t)(head - p.Hq) * p.kv_cap + ps) * p.D;
+                      k[i] = f2bf(ra);
+                      k[i + half] = f2bf(rb);
+                    }
+                  } else {
+                    uint16_t* v = p.v_cache + ((size_t)(head - p.Hq - p.Hkv) * p.kv_cap + ps) * p.D;
+                    v[i] = f2bf(a);
+                    v[i + half] = f2bf(b);
+                  }
+                }
+              });
+}
+
+// ------------------------------------------------------------------------------------------
+// Attention partials.  Item = (kv head g, key chunk c); each wave is one q head of the group.
+// S^T = K Q^T on MFMA (keys as rows), softmax in fp32 with the exact max of each 256-key
+// sub-chunk and an online rescale between sub-chunks, O += P V on MFMA.
+// ------------------------------------------------------------------------------------------
+template <int D>
+struct AttnLds {
+  static constexpr int KS = D + 8;        // Ks row stride (bf16 elements)
+  static constexpr int VS = 256 + 8;      // Vt row stride
+  uint16_t Ks[256 * KS];
+  uint16_t Vt[D * VS];
+};
+
+template <int D>
+__device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
+  AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(phase_smem(smem));
+  constexpr int KS = AttnLds<D>::KS, VS = AttnLds<D>::VS;
+  constexpr int NS = D / 32;   // MFMA k-steps over the head dim
+  constexpr int ND = D / 16;   // output d tiles
+  const int lane = lane_id(), wv = wave_id();
+  const int grp = p.Hq / p.Hkv;
+  const int nitems = p.Hkv * p.attn_nchunks;
+  const float scale = 1.0f / sqrtf((float)D);
+  const float NEG = -__builtin_inff();
+  const int gq = lane >> 4, tq = lane & 15;
+  for (int it = wg; it < nitems; it += p.nwg) {
+    const int g = it % p.Hkv, c = it / p.Hkv;
+    const int kb = p.attn_lo + c * p.attn_chunk;
+    int ke = kb + p.attn_chunk;
+    if (ke > p.attn_lo + p.attn_nkeys) ke = p.attn_lo + p.attn_nkeys;
+    const bool act = wv < grp;
+    const int h = g * grp + wv;
+    u32x4 qf[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qf[s] = u32x4{0u, 0u, 0u, 0u};
+      if (act && tq < p.T)
+        qf[s] = ldg16(p.q_buf + (size_t)tq * p.Hq * D + h * D + 32 * s + 8 * gq);
+    }
+    float m_run = NEG, l_run = 0.f;
+    f32x4 O[ND];
+#pragma unroll
+    for (int d = 0; d < ND; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int ptok = p.pos + tq;
+    for (int sb = kb; sb < ke; sb += 256) {
+      const int nk = (ke - sb) < 256 ? (ke - sb) : 256;
+      lds_barrier();
+      // stage K (row-major) and V (transposed) of this sub-chunk
+      const uint16_t* kg = p.k_cache + ((size_t)g * p.kv_cap + sb) * D;
+      const uint16_t* vg = p.v_cache + ((size_t)g * p.kv_cap + sb) * D;
+      for (int ci = threadIdx.x; ci < 256 * (D / 8); ci += kThreads) {
+        const int row = ci / (D / 8), c8 = (ci % (D / 8)) * 8;
+        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+        if (row < nk) {
+          kv = ldg16(kg + (size_t)row * D + c8);
+          vv = ldg16(vg + (size_t)row * D + c8);
+        }
+        *reinterpret_cast<u32x4*>(&L.Ks[row * KS + c8]) = kv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          L.Vt[(c8 + 2 * j) * VS + row] = (uint16_t)(vv[j] & 0xffffu);
+          L.Vt[(c8 + 2 * j + 1) * VS + row] = (uint16_t)(vv[j] >> 16);
+        }
+      }
+      lds_barrier();
+      if (act) {
+        f32x4 S[16];
+#pragma unroll
+        for (int kt = 0; kt < 16; ++kt) {
+          S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (kt * 16 < nk) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s) {
+              u32x4 ka = *reinterpret_cast<const u32x4*>(&L.Ks[(kt * 16 + tq) * KS + 32 * s + 8 * gq]);
+              S[kt] = mfma16x16x32(ka, qf[s], S[kt]);
+            }
+          }
+        }
+        // mask + scale; lane holds keys kt*16 + 4*gq + r of token tq
+        float mx = NEG;
+#pragma unroll
+        for (int kt = 0; kt < 16; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int j = sb + kt * 16 + 4 * gq + r;
+            const bool vis = tq < p.T && (j - sb) < nk && j <= ptok && (p.window == 0 || j > ptok - p.window);
+            const float v = vis ? S[kt][r] * scale : NEG;
+            S[kt][r] = v;
+            mx = fmaxf(mx, v);
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m_new = fmaxf(m_run, mx);
+        const bool none = (m_new == NEG);
+        const float alpha = none ? 1.f : __expf(m_run - m_new);
+        float ls = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 16; ++kt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = none ? 0.f : __expf(S[kt][r] - m_new);
+            S[kt][r] = e;
+            ls += e;
+          }
+        ls += __shfl_xor(ls, 16);
+        ls += __shfl_xor(ls, 32);
+        l_run = l_run * alpha + ls;
+        m_run = m_new;
+        float ao[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ao[r] = __shfl(alpha, 4 * gq + r);
+#pragma unroll
+        for (int d = 0; d < ND; ++d)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) O[d][r] *= ao[r];
+#pragma unroll
+        for (int kp = 0; kp < 8; ++kp) {
+          if (kp * 32 < nk) {
+            u32x4 pa;
+            pa[0] = pack2bf(S[2 * kp][0], S[2 * kp][1]);
+            pa[1] = pack2bf(S[2 * kp][2], S[2 * kp][3]);
+            pa[2] = pack2bf(S[2 * kp + 1][0], S[2 * kp + 1][1]);
+            pa[3] = pack2bf(S[2 * kp + 1][2], S[2 * kp + 1][3]);
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+              const uint16_t* vr = &L.Vt[(16 * d + tq) * VS + kp * 32 + 4 * gq];
+              u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
+              u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
+              u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
+              O[d] = mfma16x16x32(pa, vb, O[d]);
+            }
+          }
+        }
+      }
+    }
+    if (act) {
+      float* op = p.attn_o + ((size_t)(it * grp + wv) * kMaxT) * D;
+#pragma unroll
+      for (int d = 0; d < ND; ++d)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) op[(4 * gq + r) * D + 16 * d + tq] = O[d][r];
+      if (lane < 16) {
+        float* ml = p.attn_ml + ((size_t)(it * grp + wv) * kMaxT + lane) * 2;
+        ml[0] = m_run;
+        ml[1] = l_run;
+      }
+    }
+  }
+}
+
+// Merge the key-chunk partials of every (token, q head) row -> o (bf16).
+__device__ void phase_attn_merge(const LayerParams& p, int wg) {
+  const int grp = p.Hq / p.Hkv;
+  const int total = p.T * p.Hq * p.D;
+  for (int e = wg * kThreads + threadIdx.x; e < total; e += p.nwg * kThreads) {
+    const int d = e % p.D, h = (e / p.D) % p.Hq, t = e / (p.D * p.Hq);
+    const int g = h / grp, w = h % grp;
+    float M = -__builtin_inff();
+    for (int c = 0; c < p.attn_nchunks; ++c) {
+      const int it = c * p.Hkv + g;
+      M = fmaxf(M, p.attn_ml[((size_t)(it * grp + w) * kMaxT + t) * 2]);
+    }
+    float num = 0.f, den = 0.f;
+    for (int c = 0; c < p.attn_nchunks; ++c) {
+      const int it = c * p.Hkv + g;
+      const float* ml = p.attn_ml + ((size_t)(it * grp + w) * kMaxT + t) * 2;
+      if (ml[0] == -__builtin_inff()) continue;
+      const float wgt = __expf(ml[0] - M);
+      num += wgt * p.attn_o[((size_t)(it * grp + w) * kMaxT + t) * p.D + d];
+      den += wgt * ml[1];
+    }
+    p.o_buf[(size_t)t * p.Hq * p.D + h * p.D + d] = f2bf(num / den);
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// o-projection + residual -> h (fp32), and per-workgroup partial sums of h^2.
+// ------------------------------------------------------------------------------------------
+__device__ void phase_oproj(const LayerParams& p, int wg, char* smem) {
+  DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
+  ABf16 A{p.o_buf, p.Hq * p.D, p.T};
+  float part = 0.f;  // thread t < 16 accumulates token t over the workgroup's rows
+  dense_phase(p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, p.nwg, A, L,
+              [&](DenseLds& L, int tf, int nt, int lo, int hi) {
+                for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
+                  const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
+                  const int n = (tf + j) * 16 + r;
+                  float hv = 0.f;
+                  if (t < p.T && octet_in(n, lo, hi)) {
+                    hv = p.x[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
+                    p.h_buf[(size_t)t * p.H + n] = hv;
+                  }
+                  L.aux[(j * 16 + r) * kMaxT + t] = hv;
+                }
+                lds_barrier();
+                if (threadIdx.x < kMaxT)
+                  for (int j = 0; j < nt; ++j)
+                    for (int r = 0; r < 16; ++r) {
+                      const float hv = L.aux[(j * 16 + r) * kMaxT + threadIdx.x];
+                      part = fmaf(hv, hv, part);
+                    }
+              });
+  if (threadIdx.x < kMaxT) p.ss2[wg * kMaxT + threadIdx.x] = part;
+}
+
+// ------------------------------------------------------------------------------------------
+// Router logits (fp32) and pooler (bf16) from hn = r(h * rstd2 * gamma2), one contraction
+// over the stacked rows [router; pooler].
+// ------------------------------------------------------------------------------------------
+__device__ void phase_router_pool(const LayerParams& p, int wg, char* smem) {
+  DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
+  const float rs = wg_rstd(p.ss2, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
+  ANorm A{p.h_buf, p.H, p.gamma2, rs, p.T};
+  const int te = p.E / 16;
+  dense_phase(p.w_router, te, p.w_pool, p.P / 16, p.H, wg, p.nwg, A, L,
+              [&](DenseLds& L, int tf, int nt, int lo, int hi) {
+                for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
+                  const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
+                  const int n = (tf + j) * 16 + r;
+                  if (t >= p.T || !octet_in(n, lo, hi)) continue;
+                  const float v = L.fin[(j * 16 + r) * kMaxT + t];
+                  if (n < p.E) {
+                    p.logits[t * p.E + n] = v;
+                    if (p.dbg_logits) p.dbg_logits[t * p.E + n] = v;
+                  } else {
+                    p.pl[(size_t)t * p.P + (n - p.E)] = f2bf(v);
+                  }
+                }
+              });
+}
+
+// ------------------------------------------------------------------------------------------
+// Routing: top-k per token (logit descending, ties to the lower expert index), gates =
+// softmax over the selected logits, and per-expert slot lists.  Computed redundantly by
+// every workgroup from the same logits, so all agree bit for bit.
+// ------------------------------------------------------------------------------------------
+__device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write_debug) {
+  const int lane = lane_id(), wv = wave_id();
+  const int nslot = p.T * p.topk;
+  const float NEG = -__builtin_inff();
+  for (int t = wv; t < p.T; t += kWaves) {
+    float v[8];
+    bool taken[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = lane + 64 * j;
+      v[j] = e < p.E ? p.logits[t * p.E + e] : NEG;
+      taken[j] = e >= p.E;
+    }
+    float sel0 = 0.f, esum = 0.f;
+    for (int r = 0; r < p.topk; ++r) {
+      float bv = NEG;
+      int bi = 0x7fffffff;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e = lane + 64 * j;
+        if (!taken[j] && (bi == 0x7fffffff || v[j] > bv)) {
+          bv = v[j];
+          bi = e;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o);
+        const int oi = __shfl_xor(bi, o);
+        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if ((bi & 63) == lane && (bi >> 6) == j) taken[j] = true;
+      if (r == 0) sel0 = bv;
+      const float ex = __expf(bv - sel0);
+      esum += ex;
+      if (lane == 0) {
+        R.idx[t * p.topk + r] = bi;
+        R.gate[t * p.topk + r] = ex;  // normalised below
+      }
+    }
+    if (lane == 0)
+      for (int r = 0; r < p.topk; ++r) R.gate[t * p.topk + r] /= esum;
+  }
+  lds_barrier();
+  // per-expert counts and the slot lists
+  for (int e = threadIdx.x; e < p.E; e += kThreads) {
+    int c = 0;
+    for (int s = 0; s < nslot; ++s) c += (R.idx[s] == e);
+    R.cnt[e] = c;
+  }
+  lds_barrier();
+  if (wv == 0) {
+    // exclusive scans over experts of (count) and (count > 0): lane owns a contiguous chunk
+    const int per = (p.E + 63) / 64;
+    const int e0 = lane * per;
+    int sc = 0, sa = 0;
+    for (int e = e0; e < e0 + per && e < p.E; ++e) {
+      sc += R.cnt[e];
+      sa += R.cnt[e] > 0;
+    }
+    int ic = sc, ia = sa;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int yc = __shfl_up(ic, o), ya = __shfl_up(ia, o);
+      if (lane >= o) {
+        ic += yc;
+        ia += ya;
+      }
+    }
+    int oc = ic - sc, oa = ia - sa;
+    for (int e = e0; e < e0 + per && e < p.E; ++e) {
+      R.off[e] = oc;
+      R.rank[e] = oa;
+      oc += R.cnt[e];
+      oa += R.cnt[e] > 0;
+    }
+    if (lane == 63) {
+      R.n_active = ia;
+      R.active_off[ia] = ic;
+    }
+  }
+  lds_barrier();
+  for (int e = threadIdx.x; e < p.E; e += kThreads) {
+    if (R.cnt[e] == 0) continue;
+    const int u = R.rank[e];
+    R.active_e[u] = e;
+    R.active_off[u] = R.off[e];
+    int j = R.off[e];
+    for (int s = 0; s < nslot; ++s)
+      if (R.idx[s] == e) R.slots[j++] = s;
+  }
+  if (write_debug) {
+    for (int s = threadIdx.x; s < nslot; s += kThreads) {
+      if (p.dbg_idx) p.dbg_idx[s] = R.idx[s];
+      if (p.dbg_gates) p.dbg_gates[s] = R.gate[s];
+    }
+  }
+  lds_barrier();
+}
+
+// ------------------------------------------------------------------------------------------
+// NVFP4 experts on 4x4x4 MFMA: a wavefront lane owns one weight row; the activation of up to
+// 4 tokens is broadcast from one 4-lane block to all 16 blocks (CBSZ=4, ABID selects the
+// 4-element k slice).  The E4M3 block scale multiplies each 16-k partial in fp32.
+// G = token groups of 4 (1..4), NM = matrices sharing the activation (2 = gate+up, 1 = down).
+// ------------------------------------------------------------------------------------------
+struct Fp4Lds {
+  float red[kWaves * 64 * 32];   // [wave][lane][NM*16 + g*4 + r], 64 KiB
+};
+
+template <int NM, int G>
+struct Fp4Pair {
+  u32x4 c[NM][2];   // codes of the pair's two 32-k steps
+  uint32_t sc[NM];  // 4 block scales of the pair
+  u32x2 a[G];       // activation: lane 4b+i holds A[token 4g+i][k0 + 4b .. +3]
+};
+
+template <int NM, int G>
+__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const* wt, int pr,
+                                              const uint16_t* const* arow, int k0) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const uint8_t* b = wt[m] + (size_t)pr * 2304;
+    f.c[m][0] = ldg_stream(b + lane * 16);
+    f.c[m][1] = ldg_stream(b + 1024 + lane * 16);
+    f.sc[m] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + 2048) + lane);
+  }
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    f.a[g] = u32x2{0u, 0u};
+    if (arow[g] != nullptr) f.a[g] = ldg8(arow[g] + k0 + 4 * (lane >> 2));
+  }
+}
+
+template <int H, int J, int NM, int G>
+__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, f32x4 (&acc)[NM][G]) {
+  // block q = 2*H + J (16 k): MFMAs with ABID = 8*H + 4*J + u, u = 0..3
+#pragma unroll
+  for (int m = 0; m < NM; ++m) {
+    const uint32_t w0 = f.c[m][H][2 * J], w1 = f.c[m][H][2 * J + 1];
+    u32x2 b[4];
+    b[0] = u32x2{fp4x2_to_bf16x2<0>(w0), fp4x2_to_bf16x2<1>(w0)};
+    b[1] = u32x2{fp4x2_to_bf16x2<2>(w0), fp4x2_to_bf16x2<3>(w0)};
+    b[2] = u32x2{fp4x2_to_bf16x2<0>(w1), fp4x2_to_bf16x2<1>(w1)};
+    b[3] = u32x2{fp4x2_to_bf16x2<2>(w1), fp4x2_to_bf16x2<3>(w1)};
+    const float s = e4m3_to_f32<2 * H + J>(f.sc[m]);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      f32x4 P = f32x4{0.f, 0.f, 0.f, 0.f};
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 0>(f.a[g], b[0], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 1>(f.a[g], b[1], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 2>(f.a[g], b[2], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 3>(f.a[g], b[3], P);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[m][g][r] = fmaf(s, P[r], acc[m][g][r]);
+    }
+  }
+}
+
+template <int NM, int G>
+__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, bool second,
+                                                 f32x4 (&acc)[NM][G]) {
+  fp4_mfma_block<0, 0>(f, acc);
+  fp4_mfma_block<0, 1>(f, acc);
+  if (second) {
+    fp4_mfma_block<1, 0>(f, acc);
+    fp4_mfma_block<1, 1>(f, acc);
+  }
+}
+
+// One expert's run of 64-row tiles [ta, tb) for this workgroup.
+//   GATEUP: NM = 2, activation = pl rows of the expert's tokens, out a = r(silu(g)*u)
+//   else  : NM = 1, activation = a rows of the expert's slots,   out d (fp32)
+template <bool GATEUP, int G>
+__device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int u, int ta, int tb,
+                                 Fp4Lds& L) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  const int lane = lane_id(), wv = wave_id();
+  const int e = R.active_e[u];
+  const int s_lo = R.active_off[u], n_e = R.active_off[u + 1] - s_lo;
+  const int K = GATEUP ? p.P : p.I;
+  const int S = K >> 5, Sp = (S + 1) >> 1;  // 32-k steps, pairs
+  const int nkw = Sp < kWaves ? Sp : kWaves;
+  const int pa = wv * Sp / nkw, pb = (wv + 1) * Sp / nkw;
+  const bool kw = wv < nkw;
+  const size_t tile_bytes = (size_t)32 * K + (size_t)4 * K;  // 64 rows: K/2 + K/16 bytes each
+  const uint8_t* wb[NM];
+  if (GATEUP) {
+    wb[0] = p.w_gate + (size_t)e * p.stride_gate;
+    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up;
+  } else {
+    wb[0] = p.w_down + (size_t)e * p.stride_down;
+  }
+  // activation rows of this lane's tokens (lane 4b+i -> token slot 4g+i)
+  const uint16_t* arow[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int j = 4 * g + (lane & 3);
+    arow[g] = nullptr;
+    if (j < n_e) {
+      const int slot = R.slots[s_lo + j];
+      arow[g] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
+    }
+  }
+  const int npt = pb - pa;  // pairs per tile for this wave
+  const int total = kw ? (tb - ta) * npt : 0;
+  Fp4Pair<NM, G> cur, nxt;
+  auto issue = [&](Fp4Pair<NM, G>& f, int n) {
+    const int ti = ta + n / npt, pr = pa + n % npt;
+    const uint8_t* wt[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes;
+    fp4_pair_load<NM, G>(f, wt, pr, arow, 64 * pr);
+  };
+  if (total > 0) issue(cur, 0);
+  int n = 0;
+  for (int ti = ta; ti < tb; ++ti) {
+    f32x4 acc[NM][G];
+#pragma unroll
+    for (int m = 0; m < NM; ++m)
+#pragma unroll
+      for (int g = 0; g < G; ++g) acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (kw) {
+      for (int q = 0; q < npt; ++q, ++n) {
+        if (n + 1 < total) issue(nxt, n + 1);
+        const int pr = pa + q;
+        fp4_pair_compute<NM, G>(cur, 2 * pr + 1 < S, acc);
+        cur = nxt;
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) L.red[(wv * 64 + lane) * 32 + m * 16 + g * 4 + r] = acc[m][g][r];
+    }
+    lds_barrier();
+    // reduce over the k-waves in order; lane row = ti*64 + ln
+    for (int x = threadIdx.x; x < 64 * n_e; x += kThreads) {
+      const int ln = x & 63, j = x >> 6;
+      const int slot = R.slots[s_lo + j];
+      if (GATEUP) {
+        float gs = 0.f, us = 0.f;
+        for (int w = 0; w < nkw; ++w) {
+          gs += L.red[(w * 64 + ln) * 32 + j];
+          us += L.red[(w * 64 + ln) * 32 + 16 + j];
+        }
+        gs *= p.ts_gate[e];
+        us *= p.ts_up[e];
+        const float a = gs / (1.0f + __expf(-gs)) * us;
+        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 64 + ln] = f2bf(a);
+      } else {
+        float ds = 0.f;
+        for (int w = 0; w < nkw; ++w) ds += L.red[(w * 64 + ln) * 32 + j];
+        p.d_buf[(size_t)slot * p.P + p.rank * p.P_loc + ti * 64 + ln] = ds * p.ts_down[e];
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// ------------------------------------------------------------------------------------------
+// bf16 experts on 16x16x32 MFMA (the expert's <= 16 slots form the M tile).
+// ------------------------------------------------------------------------------------------
+template <bool GATEUP>
+__device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, int u, int ta, int tb,
+                                  DenseLds& L) {
+  constexpr int NM = GATEUP ? 2 : 1;
+  const int lane = lane_id(), wv = wave_id();
+  const int e = R.active_e[u];
+  const int s_lo = R.active_off[u], n_e = R.active_off[u + 1] - s_lo;
+  const int K = GATEUP ? p.P : p.I;
+  const int S = K >> 5;
+  const int nkw = S < kWaves ? S : kWaves;
+  const int sa = wv * S / nkw, sb = (wv + 1) * S / nkw;
+  const int rows = GATEUP ? p.I_loc : p.P_loc;
+  const uint8_t* wb[NM];
+  if (GATEUP) {
+    wb[0] = p.w_gate + (size_t)e * p.stride_gate;
+    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up;
+  } else {
+    wb[0] = p.w_down + (size_t)e * p.stride_down;
+  }
+  (void)rows;
+  const int jt = lane & 15;
+  const uint16_t* arow = nullptr;
+  if (jt < n_e) {
+    const int slot = R.slots[s_lo + jt];
+    arow = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
+  }
+  const int kq = 8 * (lane >> 4);
+  for (int ti = ta; ti < tb; ++ti) {
+    f32x4 acc[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (wv < nkw) {
+      const uint8_t* tb_[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) tb_[m] = wb[m] + (size_t)ti * S * 1024 + lane * 16;
+      u32x4 a_cur = arow ? ldg16(arow + 32 * sa + kq) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w_cur[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) w_cur[m] = ldg_stream(tb_[m] + (size_t)sa * 1024);
+      for (int s = sa; s < sb; ++s) {
+        u32x4 a_nxt = {0u, 0u, 0u, 0u}, w_nxt[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) w_nxt[m] = u32x4{0u, 0u, 0u, 0u};
+        if (s + 1 < sb) {
+          if (arow) a_nxt = ldg16(arow + 32 * (s + 1) + kq);
+#pragma unroll
+          for (int m = 0; m < NM; ++m) w_nxt[m] = ldg_stream(tb_[m] + (size_t)(s + 1) * 1024);
+        }
+#pragma unroll
+        for (int m = 0; m < NM; ++m) acc[m] = mfma16x16x32(a_cur, w_cur[m], acc[m]);
+        a_cur = a_nxt;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) w_cur[m] = w_nxt[m];
+      }
+#pragma unroll
+      for (int m = 0; m < NM; ++m) L.red[(wv * 4 + m) * 64 + lane] = acc[m];
+    }
+    lds_barrier();
+    // output element (slot j, row r): lane ln = 16*(j/4) + r holds it at component j%4
+    for (int x = threadIdx.x; x < 16 * n_e; x += kThreads) {
+      const int r = x & 15, j = x >> 4;
+      const int ln = 16 * (j >> 2) + r, c = j & 3;
+      const int slot = R.slots[s_lo + j];
+      if (GATEUP) {
+        float gs = 0.f, us = 0.f;
+        for (int w = 0; w < nkw; ++w) {
+          gs += L.red[(w * 4 + 0) * 64 + ln][c];
+          us += L.red[(w * 4 + 1) * 64 + ln][c];
+        }
+        const float a = gs / (1.0f + __expf(-gs)) * us;
+        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 16 + r] = f2bf(a);
+      } else {
+        float ds = 0.f;
+        for (int w = 0; w < nkw; ++w) ds += L.red[(w * 4 + 0) * 64 + ln][c];
+        p.d_buf[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = ds;
+      }
+    }
+    lds_barrier();
+  }
+}
+
+// Expert GEMM phase: the flattened list (active expert u, tile) split evenly over workgroups.
+template <bool GATEUP>
+__device__ void phase_experts(const LayerParams& p, int wg, char* smem) {
+  RouteTables& R = route_tables(smem);
+  const int rows = GATEUP ? p.I_loc : p.P_loc;
+  const bool fp4 = p.expert_dtype == 0;
+  const int tpe = fp4 ? rows / 64 : rows / 16;
+  const int U = R.n_active;
+  const int TT = U * tpe;
+  const int t0 = (int)((long)wg * TT / p.nwg), t1 = (int)((long)(wg + 1) * TT / p.nwg);
+  for (int t = t0; t < t1;) {
+    const int u = t / tpe;
+    const int ta = t % tpe;
+    int tb = tpe;
+    if ((u + 1) * tpe > t1) tb = t1 - u * tpe;
+    if (fp4) {
+      Fp4Lds& L = *reinterpret_cast<Fp4Lds*>(phase_smem(smem));
+      const int n_e = R.active_off[u + 1] - R.active_off[u];
+      switch ((n_e + 3) >> 2) {
+        case 1: fp4_expert_tiles<GATEUP, 1>(p, R, u, ta, tb, L); break;
+        case 2: fp4_expert_tiles<GATEUP, 2>(p, R, u, ta, tb, L); break;
+        case 3: fp4_expert_tiles<GATEUP, 3>(p, R, u, ta, tb, L); break;
+        default: fp4_expert_tiles<GATEUP, 4>(p, R, u, ta, tb, L); break;
+      }
+    } else {
+      DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
+      bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
+    }
+    t = u * tpe + tb;
+  }
+}
+
+// m[t] = r(sum over the token's slots, in selection order, of gate * d)
+__device__ void phase_combine(const LayerParams& p, int wg, char* smem) {
+  const RouteTables& R = route_tables(smem);
+  const int total = p.T * p.P_loc;
+  for (int x = wg * kThreads + threadIdx.x; x < total; x += p.nwg * kThreads) {
+    const int t = x / p.P_loc, pc = p.rank * p.P_loc + x % p.P_loc;
+    float s = 0.f;
+    for (int k = 0; k < p.topk; ++k)
+      s = fmaf(R.gate[t * p.topk + k], p.d_buf[(size_t)(t * p.topk + k) * p.P + pc], s);
+    p.m_buf[(size_t)t * p.P + pc] = f2bf(s);
+  }
+}
+
+// y = h + m W_unpool^T
+__device__ void phase_unpool(const LayerParams& p, int wg, char* smem) {
+  DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
+  ABf16 A{p.m_buf, p.P, p.T};
+  dense_phase(p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, p.nwg, A, L,
+              [&](DenseLds& L, int tf, int nt, int lo, int hi) {
+                for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
+                  const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
+                  const int n = (tf + j) * 16 + r;
+                  if (t >= p.T || !octet_in(n, lo, hi)) continue;
+                  p.y[(size_t)t * p.H + n] = p.h_buf[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
+                }
+              });
+}
+
+}  // namespace moel

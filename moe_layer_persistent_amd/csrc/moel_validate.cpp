@@ -1,0 +1,87 @@
+// Host-only argument validation and size queries of the C ABI (no HIP calls: these run
+// and are tested on machines without a GPU).
+#include <stdint.h>
+
+#include "../../include/moel.h"
+
+extern "C" {
+
+const char* moel_status_string(int32_t s) {
+  switch (s) {
+    case MOEL_OK: return "ok";
+    case MOEL_ERR_ARG: return "invalid argument";
+    case MOEL_ERR_SHAPE: return "unsupported shape";
+    case MOEL_ERR_ALIGN: return "misaligned pointer";
+    case MOEL_ERR_HIP: return "HIP runtime error";
+    case MOEL_ERR_TIMEOUT: return "device wait timed out";
+    case MOEL_ERR_ABORTED: return "aborted";
+    case MOEL_ERR_UNSUPPORTED: return "unsupported device";
+    default: return "unknown status";
+  }
+}
+
+int32_t moel_abi_version(void) { return MOEL_ABI_VERSION; }
+
+moel_status moel_validate_config(const moel_config* c) {
+  if (c == nullptr) return MOEL_ERR_ARG;
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->pooled <= 0 ||
+      c->inter <= 0 || c->n_experts <= 0 || c->top_k <= 0 || c->n_shards <= 0 || c->kv_capacity <= 0)
+    return MOEL_ERR_ARG;
+  if (!(c->rms_eps > 0.0f) || !(c->rope_theta > 0.0f)) return MOEL_ERR_ARG;
+  if (c->shard_rank < 0 || c->shard_rank >= c->n_shards) return MOEL_ERR_ARG;
+  if (c->expert_dtype != MOEL_EXPERT_NVFP4 && c->expert_dtype != MOEL_EXPERT_BF16) return MOEL_ERR_ARG;
+  if (c->top_k > c->n_experts || c->top_k > 8) return MOEL_ERR_SHAPE;
+  if (c->hidden % 256 != 0) return MOEL_ERR_SHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return MOEL_ERR_SHAPE;
+  if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > 8) return MOEL_ERR_SHAPE;
+  if (c->n_experts % 16 != 0 || c->n_experts > 512) return MOEL_ERR_SHAPE;
+  if (c->pooled % 128 != 0 || c->inter % 128 != 0) return MOEL_ERR_SHAPE;
+  const int row_unit = c->expert_dtype == MOEL_EXPERT_NVFP4 ? 64 : 16;
+  if (c->inter % (row_unit * c->n_shards) != 0 || c->pooled % (row_unit * c->n_shards) != 0)
+    return MOEL_ERR_SHAPE;
+  if ((int64_t)c->kv_capacity * c->head_dim > ((int64_t)1 << 31) / c->n_kv_heads) return MOEL_ERR_SHAPE;
+  return MOEL_OK;
+}
+
+static bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+moel_status moel_validate_call(const moel_config* cfg, const moel_weights* w, const void* k_cache,
+                               const void* v_cache, const float* x, int32_t T, int32_t pos, int32_t window,
+                               const float* y) {
+  moel_status st = moel_validate_config(cfg);
+  if (st != MOEL_OK) return st;
+  if (w == nullptr || k_cache == nullptr || v_cache == nullptr || x == nullptr || y == nullptr)
+    return MOEL_ERR_ARG;
+  if (T < 1 || T > MOEL_MAX_TOKENS) return MOEL_ERR_ARG;
+  if (pos < 0 || window < 0) return MOEL_ERR_ARG;
+  if ((int64_t)pos + T > cfg->kv_capacity) return MOEL_ERR_ARG;
+  const void* ptrs[] = {w->gamma1, w->gamma2, w->w_qkv, w->w_o, w->w_router, w->w_pool, w->w_unpool,
+                        w->w_gate, w->w_up, w->w_down};
+  for (const void* p : ptrs) {
+    if (p == nullptr) return MOEL_ERR_ARG;
+    if (misaligned(p)) return MOEL_ERR_ALIGN;
+  }
+  if (cfg->expert_dtype == MOEL_EXPERT_NVFP4 && (w->ts_gate == nullptr || w->ts_up == nullptr || w->ts_down == nullptr))
+    return MOEL_ERR_ARG;
+  if (misaligned(k_cache) || misaligned(v_cache) || misaligned(x) || misaligned(y)) return MOEL_ERR_ALIGN;
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+  const uintptr_t n = (uintptr_t)T * (uintptr_t)cfg->hidden * 4u;
+  if (xb < yb + n && yb < xb + n) return MOEL_ERR_ARG;  // y must not alias x
+  return MOEL_OK;
+}
+
+size_t moel_packed_dense_bytes(int32_t N, int32_t K) {
+  if (N <= 0 || K <= 0) return 0;
+  return (size_t)N * (size_t)K * 2u;
+}
+
+size_t moel_packed_experts_bytes(const moel_config* cfg, int32_t which) {
+  if (cfg == nullptr || which < 0 || which > 2 || cfg->n_shards <= 0) return 0;
+  const size_t N = which < 2 ? (size_t)(cfg->inter / cfg->n_shards) : (size_t)(cfg->pooled / cfg->n_shards);
+  const size_t K = which < 2 ? (size_t)cfg->pooled : (size_t)cfg->inter;
+  const size_t E = (size_t)cfg->n_experts;
+  if (cfg->expert_dtype == MOEL_EXPERT_BF16) return E * N * K * 2u;
+  return E * N * (K / 2 + K / 16);
+}
+
+}  // extern "C"

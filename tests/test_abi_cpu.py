@@ -1,0 +1,114 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every entry point the
+header declares, and its host-side validation returns the documented error codes."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_layer_persistent_amd import binding, synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moel.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moel_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = binding.lib()
+    names = _declared_functions()
+    assert len(names) >= 15
+    for n in names:
+        assert hasattr(L, n), n
+    assert L.moel_abi_version() == 1
+
+
+def _cfg(**kw):
+    w = synth.WORKLOADS["swa_fp4"]
+    c = binding.config_from_workload(w)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("hidden", 100, binding.MOEL_ERR_SHAPE),
+    ("head_dim", 96, binding.MOEL_ERR_SHAPE),
+    ("n_q_heads", 60, binding.MOEL_ERR_SHAPE),
+    ("top_k", 9, binding.MOEL_ERR_SHAPE),
+    ("n_experts", 8, binding.MOEL_ERR_SHAPE),
+    ("inter", 4000, binding.MOEL_ERR_SHAPE),
+    ("shard_rank", 1, binding.MOEL_ERR_ARG),
+    ("expert_dtype", 7, binding.MOEL_ERR_ARG),
+    ("kv_capacity", 0, binding.MOEL_ERR_ARG),
+    ("rms_eps", 0.0, binding.MOEL_ERR_ARG),
+])
+def test_validate_config_rejects(field, value, code):
+    assert binding.lib().moel_validate_config(ctypes.byref(_cfg(**{field: value}))) == code
+
+
+def test_validate_config_accepts_workloads():
+    for w in synth.WORKLOADS.values():
+        c = binding.config_from_workload(w)
+        assert binding.lib().moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK, w.name
+
+
+def _fake_weights(base=0x10000):
+    vals = [base + 0x1000 * i for i in range(13)]
+    return binding.Weights(*[ctypes.c_void_p(v) for v in vals])
+
+
+@pytest.mark.parametrize("T,pos,window,code", [
+    (0, 10, 0, binding.MOEL_ERR_ARG),
+    (17, 10, 0, binding.MOEL_ERR_ARG),
+    (16, -1, 0, binding.MOEL_ERR_ARG),
+    (16, 10, -1, binding.MOEL_ERR_ARG),
+    (16, 8192 + 1, 0, binding.MOEL_ERR_ARG),     # pos + T > kv_capacity (8208)
+    (16, 8192, 2048, binding.MOEL_OK),
+    (1, 0, 0, binding.MOEL_OK),
+])
+def test_validate_call_ranges(T, pos, window, code):
+    c = _cfg()
+    w = _fake_weights()
+    vp = ctypes.c_void_p
+    got = binding.lib().moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100000), vp(0x200000),
+                                          vp(0x300000), T, pos, window, vp(0x400000))
+    assert got == code
+
+
+def test_validate_call_alignment_and_alias():
+    c = _cfg()
+    w = _fake_weights()
+    vp = ctypes.c_void_p
+    L = binding.lib()
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100008), vp(0x200000), vp(0x300000),
+                                16, 0, 0, vp(0x400000)) == binding.MOEL_ERR_ALIGN
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100000), vp(0x200000), vp(0x300000),
+                                16, 0, 0, vp(0x300000 + 4096)) == binding.MOEL_ERR_ARG   # y overlaps x
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), None, vp(0x200000), vp(0x300000),
+                                16, 0, 0, vp(0x400000)) == binding.MOEL_ERR_ARG
+    w.ts_up = None
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100000), vp(0x200000), vp(0x300000),
+                                16, 0, 0, vp(0x400000)) == binding.MOEL_ERR_ARG
+
+
+def test_packed_sizes_equal_canonical_bytes():
+    L = binding.lib()
+    w = synth.WORKLOADS["swa_fp4"]
+    c = binding.config_from_workload(w)
+    assert L.moel_packed_dense_bytes(10240, 8192) == 10240 * 8192 * 2
+    per = 4096 * 4096 // 2 + 4096 * 4096 // 16
+    for which in range(3):
+        assert L.moel_packed_experts_bytes(ctypes.byref(c), which) == 256 * per
+    s = synth.WORKLOADS["stack_tp8"]
+    c4 = binding.config_from_workload(s)
+    assert L.moel_packed_experts_bytes(ctypes.byref(c4), 0) == 256 * 512 * (4096 // 2 + 4096 // 16)
+    assert L.moel_packed_experts_bytes(ctypes.byref(c4), 2) == 256 * 512 * (4096 // 2 + 4096 // 16)
+
+
+def test_status_strings():
+    for code in range(0, -8, -1):
+        assert binding.status_string(code) != "unknown status"

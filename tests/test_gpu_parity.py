@@ -1,0 +1,160 @@
+"""Parity of the HIP path (through the C ABI) with the oracle, on the GPU.
+
+Small shapes are compared on every token; the full-width workloads run at their real
+sizes in the same launch configuration the benchmark times, with every token's routing
+and KV writes checked and the MoE output checked on sampled tokens (the oracle
+dequantises only the experts those tokens use).
+"""
+import numpy as np
+import pytest
+import torch
+
+from moe_layer_persistent_amd import binding, synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import harness  # noqa: E402  (imports the oracle: tests only)
+
+
+def _log(msg):
+    print(msg, flush=True)
+
+
+def _same_bytes(a, b):
+    return torch.equal(a.contiguous().view(torch.uint8), b.contiguous().view(torch.uint8))
+
+
+@pytest.fixture(scope="module")
+def tiny_run():
+    return harness.GpuRun(synth.WORKLOADS["tiny"])
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_tiny_matches_oracle(tiny_run, fused):
+    _log(f"tiny fused={fused}")
+    out = tiny_run.run(fused=fused)
+    rep = {}
+    harness.check_against_oracle(tiny_run, out, report=rep)
+    _log(f"tiny fused={fused}: {rep}")
+
+
+SMALL = [
+    dict(),                                                    # T=5, window 40, pos 70, NVFP4
+    dict(T=16, pos=300, window=0, expert_dtype=synth.NVFP4),
+    dict(T=1, pos=0, window=0),
+    dict(T=16, pos=20, window=7, head_dim=128, n_q_heads=4, n_kv_heads=1, hidden=768),
+    dict(T=9, pos=600, window=256, expert_dtype=synth.BF16, inter=256),
+    dict(T=12, pos=33, window=0, n_shards=2, inter=512, pooled=256),
+    dict(T=16, pos=1000, window=300, n_experts=32, top_k=8, pooled=512, inter=512),
+]
+
+
+@pytest.mark.parametrize("kw", SMALL, ids=[str(i) for i in range(len(SMALL))])
+def test_small_matches_oracle(kw):
+    w = synth.small_workload(**kw)
+    _log(f"small {kw}")
+    run = harness.GpuRun(w)
+    rep = {}
+    harness.check_against_oracle(run, run.run(fused=True), report=rep)
+    _log(f"small {kw}: {rep}")
+
+
+def test_fused_equals_unfused_and_is_deterministic():
+    w = synth.small_workload(T=16, pos=500, window=100, n_experts=32, top_k=8, pooled=512, inter=512)
+    run = harness.GpuRun(w)
+    a = run.run(fused=True)
+    b = run.run(fused=True)
+    c = run.run(fused=False)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(a[k], b[k]), k
+        assert _same_bytes(a[k], c[k]), k
+
+
+def test_timestamps_leave_outputs_bit_identical():
+    w = synth.small_workload(T=8, pos=200, window=64)
+    run = harness.GpuRun(w)
+    a = run.run(fused=True, stamps=False)
+    b = run.run(fused=True, stamps=True)
+    assert torch.equal(a["y"], b["y"])
+    assert torch.equal(a["k_cache"].view(torch.int16), b["k_cache"].view(torch.int16))
+    ts = b["timestamps"].cpu().numpy()
+    assert (ts[:, :10] > 0).all()
+    assert (np.diff(ts[:, :10].astype(np.int64), axis=1) >= 0).all()
+
+
+def test_rewind_rewrites_only_the_step_slots():
+    """Calling again at the same pos with different x (a rejected draft) rewrites exactly
+    slots [pos, pos+T) and leaves earlier slots untouched."""
+    w = synth.small_workload(T=6, pos=50, window=0)
+    run = harness.GpuRun(w)
+    kc, vc = run.fresh_caches()
+    y = torch.empty((w.T, w.hidden), dtype=torch.float32, device="cuda")
+    run.plan.layer_decode(run.lw, kc, vc, run.t["x"], w.pos, 0, y)
+    k1 = kc.clone()
+    x2 = torch.randn_like(run.t["x"])
+    run.plan.layer_decode(run.lw, kc, vc, x2, w.pos, 0, y)
+    torch.cuda.synchronize()
+    assert torch.equal(kc[:, :w.pos].view(torch.int16), k1[:, :w.pos].view(torch.int16))
+    assert not torch.equal(kc[:, w.pos:w.pos + w.T].view(torch.int16), k1[:, w.pos:w.pos + w.T].view(torch.int16))
+    out = run.run(fused=True, x=x2)
+    assert torch.equal(out["k_cache"][:, w.pos:w.pos + w.T].view(torch.int16),
+                       kc[:, w.pos:w.pos + w.T].view(torch.int16))
+
+
+def test_abort_leaves_buffers_untouched():
+    w = synth.small_workload(T=4, pos=30, window=0)
+    run = harness.GpuRun(w)
+    kc, vc = run.fresh_caches()
+    y = torch.full((w.T, w.hidden), 7.0, dtype=torch.float32, device="cuda")
+    for fused in (True, False):
+        run.plan.set_abort(True)
+        run.plan.layer_decode(run.lw, kc, vc, run.t["x"], w.pos, 0, y, fused=fused)
+        torch.cuda.synchronize()
+        assert run.plan.status() == binding.MOEL_ERR_ABORTED
+        run.plan.set_abort(False)
+        torch.cuda.synchronize()
+        assert torch.all(y == 7.0)
+        assert torch.equal(kc.view(torch.int16), run.k0.view(torch.int16))
+    assert run.plan.status() == binding.MOEL_OK
+
+
+def test_invalid_calls_launch_nothing():
+    w = synth.small_workload(T=4, pos=30, window=0)
+    run = harness.GpuRun(w)
+    kc, vc = run.fresh_caches()
+    y = torch.full((w.T, w.hidden), 7.0, dtype=torch.float32, device="cuda")
+    for T, pos, window in ((0, 30, 0), (17, 30, 0), (4, w.kv_capacity - 3, 0), (4, -1, 0), (4, 30, -2)):
+        with pytest.raises(binding.MoelError) as ei:
+            run.plan.layer_decode(run.lw, kc, vc, run.t["x"], pos, window, y, T=T)
+        assert ei.value.code == binding.MOEL_ERR_ARG
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    assert torch.equal(kc.view(torch.int16), run.k0.view(torch.int16))
+
+
+# ---------------------------------------------------------------- full-width workloads
+FULL = ["swa_fp4", "global_fp4", "swa_bf16"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_width_matches_oracle(name):
+    w = synth.WORKLOADS[name]
+    _log(f"full {name}: generating")
+    run = harness.GpuRun(w)
+    _log(f"full {name}: running")
+    out = run.run(fused=True)
+    rep = {}
+    harness.check_against_oracle(run, out, moe_tokens=[0, 7, 15], report=rep)
+    _log(f"full {name}: {rep}")
+
+
+@pytest.mark.parametrize("layer", [0, 1])
+def test_stack_share_layer_matches_oracle(layer):
+    w = synth.WORKLOADS["stack_tp8"]
+    _log(f"stack layer {layer}: generating")
+    run = harness.GpuRun(w, layer=layer)
+    out = run.run(fused=True)
+    rep = {}
+    harness.check_against_oracle(run, out, moe_tokens=[0, 15], report=rep)
+    _log(f"stack layer {layer}: {rep}")
