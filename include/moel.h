@@ -147,6 +147,15 @@ moel_status moel_plan_status(moel_plan* plan);
  * work, leave every caller buffer untouched and report MOEL_ERR_ABORTED. */
 moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* stream);
 
+/* Intermediate activations of the last completed step, for tests and profiling tools
+ * (all fp32, row-major, rows = tokens or token slots):
+ *   0 q [16][Hq*D] after RoPE      1 o [16][Hq*D] attention output   2 h [16][H]
+ *   3 router logits [16][E]        4 pl [16][P] pooled vector        5 a [16*k][I] SwiGLU out
+ *   6 d [16*k][P] expert outputs   7 m [16][P] combined vector
+ * *ptr receives a device pointer into the plan's workspace (owned by the plan; valid until
+ * moel_plan_destroy; overwritten by the next step), *bytes its size. */
+moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes);
+
 /* --- weight packing (one-time, not on the hot path) --------------------------------- */
 
 /* Dense bf16 matrix [N, K] row-major -> packed layout (16-row tiles, 32-element k steps,

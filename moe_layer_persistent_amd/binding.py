@@ -74,6 +74,7 @@ def lib() -> ctypes.CDLL:
             "moel_plan_workgroups": (i32, [vp]),
             "moel_plan_status": (i32, [vp]),
             "moel_plan_set_abort": (i32, [vp, i32, vp]),
+            "moel_plan_scratch": (i32, [vp, i32, P(vp), P(sz)]),
             "moel_pack_dense": (i32, [vp, i32, i32, i32, vp, vp]),
             "moel_pack_experts": (i32, [P(Config), i32, vp, vp, vp, vp]),
             "moel_layer_decode": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, P(Debug), vp]),
@@ -152,6 +153,23 @@ class Plan:
 
     def status(self) -> int:
         return lib().moel_plan_status(self.handle)
+
+    SCRATCH = {"q": 0, "o": 1, "h": 2, "logits": 3, "pl": 4, "a": 5, "d": 6, "m": 7}
+
+    def scratch(self, name: str) -> torch.Tensor:
+        """Copy of an intermediate activation of the last completed step (fp32, flat)."""
+        ptr, n = ctypes.c_void_p(), ctypes.c_size_t()
+        _check(lib().moel_plan_scratch(self.handle, self.SCRATCH[name], ctypes.byref(ptr), ctypes.byref(n)),
+               "moel_plan_scratch")
+        out = torch.empty(n.value // 4, dtype=torch.float32, device="cuda")
+        torch.cuda.synchronize()
+        import ctypes as _c
+        hip = _c.CDLL("libamdhip64.so")
+        hip.hipMemcpy.argtypes = [_c.c_void_p, _c.c_void_p, _c.c_size_t, _c.c_int]
+        rc = hip.hipMemcpy(_c.c_void_p(out.data_ptr()), ptr, n.value, 3)  # device to device
+        if rc != 0:
+            raise RuntimeError(f"hipMemcpy failed: {rc}")
+        return out
 
     def set_abort(self, flag: bool, stream=None):
         _check(lib().moel_plan_set_abort(self.handle, int(flag), _stream(stream)), "moel_plan_set_abort")

@@ -37,6 +37,11 @@ __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
 }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+// two fp32 values -> {packed bf16 (nearest), packed bf16 of the remainders}
+__device__ __forceinline__ u32x2 split_bf16(float a, float b) {
+  const uint16_t ha = f2bf(a), hb = f2bf(b);
+  return u32x2{(uint32_t)ha | ((uint32_t)hb << 16), pack2bf(a - bf2f(ha), b - bf2f(hb))};
+}
 
 // ---------------------------------------------------------------- loads (streamed weights)
 __device__ __forceinline__ u32x4 ldg_stream(const void* p) {

@@ -296,16 +296,16 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   const size_t o_ctrl = take(256);
   const size_t o_ss1 = take((size_t)nwg * kMaxT * 4);
   const size_t o_ss2 = take((size_t)nwg * kMaxT * 4);
-  const size_t o_q = take((size_t)kMaxT * Hq * D * 2);
+  const size_t o_q = take((size_t)kMaxT * Hq * D * 4);
   const size_t o_ao = take((size_t)nwg * plan->grp * kMaxT * D * 4);
   const size_t o_aml = take((size_t)nwg * plan->grp * kMaxT * 2 * 4);
-  const size_t o_o = take((size_t)kMaxT * Hq * D * 2);
+  const size_t o_o = take((size_t)kMaxT * Hq * D * 4);
   const size_t o_h = take((size_t)kMaxT * H * 4);
   const size_t o_lg = take((size_t)kMaxT * E * 4);
-  const size_t o_pl = take((size_t)kMaxT * P * 2);
-  const size_t o_a = take((size_t)kMaxT * k * I * 2);
+  const size_t o_pl = take((size_t)kMaxT * P * 4);
+  const size_t o_a = take((size_t)kMaxT * k * I * 4);
   const size_t o_d = take((size_t)kMaxT * k * P * 4);
-  const size_t o_m = take((size_t)kMaxT * P * 2);
+  const size_t o_m = take((size_t)kMaxT * P * 4);
   const size_t o_cos = take((size_t)cfg->kv_capacity * (D / 2) * 4);
   const size_t o_sin = take((size_t)cfg->kv_capacity * (D / 2) * 4);
   plan->ws_bytes = off;
@@ -373,16 +373,16 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.ctrl = reinterpret_cast<unsigned*>(ws + o_ctrl);
   b.ss1 = reinterpret_cast<float*>(ws + o_ss1);
   b.ss2 = reinterpret_cast<float*>(ws + o_ss2);
-  b.q_buf = reinterpret_cast<uint16_t*>(ws + o_q);
+  b.q_buf = reinterpret_cast<float*>(ws + o_q);
   b.attn_o = reinterpret_cast<float*>(ws + o_ao);
   b.attn_ml = reinterpret_cast<float*>(ws + o_aml);
-  b.o_buf = reinterpret_cast<uint16_t*>(ws + o_o);
+  b.o_buf = reinterpret_cast<float*>(ws + o_o);
   b.h_buf = reinterpret_cast<float*>(ws + o_h);
   b.logits = reinterpret_cast<float*>(ws + o_lg);
-  b.pl = reinterpret_cast<uint16_t*>(ws + o_pl);
-  b.a_buf = reinterpret_cast<uint16_t*>(ws + o_a);
+  b.pl = reinterpret_cast<float*>(ws + o_pl);
+  b.a_buf = reinterpret_cast<float*>(ws + o_a);
   b.d_buf = reinterpret_cast<float*>(ws + o_d);
-  b.m_buf = reinterpret_cast<uint16_t*>(ws + o_m);
+  b.m_buf = reinterpret_cast<float*>(ws + o_m);
   b.rope_cos = reinterpret_cast<const float*>(ws + o_cos);
   b.rope_sin = reinterpret_cast<const float*>(ws + o_sin);
 
@@ -436,6 +436,24 @@ moel_status moel_plan_status(moel_plan* plan) {
   unsigned clear[4] = {0, 0, 0, keep_abort};
   if (!hip_ok(hipMemcpy(plan->base.ctrl, clear, sizeof(clear), hipMemcpyHostToDevice))) return MOEL_ERR_HIP;
   return words[kStatus] == MOEL_DEV_TIMEOUT ? MOEL_ERR_TIMEOUT : MOEL_ERR_ABORTED;
+}
+
+moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes) {
+  if (plan == nullptr || ptr == nullptr || bytes == nullptr) return MOEL_ERR_ARG;
+  const LayerParams& b = plan->base;
+  const size_t T = kMaxT, k = (size_t)b.topk;
+  switch (which) {
+    case 0: *ptr = b.q_buf; *bytes = T * b.Hq * b.D * 4; break;
+    case 1: *ptr = b.o_buf; *bytes = T * b.Hq * b.D * 4; break;
+    case 2: *ptr = b.h_buf; *bytes = T * b.H * 4; break;
+    case 3: *ptr = b.logits; *bytes = T * b.E * 4; break;
+    case 4: *ptr = b.pl; *bytes = T * b.P * 4; break;
+    case 5: *ptr = b.a_buf; *bytes = T * k * b.I * 4; break;
+    case 6: *ptr = b.d_buf; *bytes = T * k * b.P * 4; break;
+    case 7: *ptr = b.m_buf; *bytes = T * b.P * 4; break;
+    default: return MOEL_ERR_ARG;
+  }
+  return MOEL_OK;
 }
 
 moel_status moel_plan_set_abort(moel_plan* plan, int32_t flag, void* stream) {

@@ -60,16 +60,16 @@ struct LayerParams {
   // scratch (plan workspace)
   float* ss1;       // [nwg][16]
   float* ss2;       // [nwg][16]
-  uint16_t* q_buf;  // [16][Hq*D]
+  float* q_buf;     // [16][Hq*D]
   float* attn_o;    // [items][grp][16][D]
   float* attn_ml;   // [items][grp][16][2]
-  uint16_t* o_buf;  // [16][Hq*D]
+  float* o_buf;     // [16][Hq*D]
   float* h_buf;     // [16][H]
   float* logits;    // [16][E]
-  uint16_t* pl;     // [16][P]
-  uint16_t* a_buf;  // [16*topk][I]
+  float* pl;        // [16][P]
+  float* a_buf;     // [16*topk][I]
   float* d_buf;     // [16*topk][P]
-  uint16_t* m_buf;  // [16][P]
+  float* m_buf;     // [16][P]
   unsigned* ctrl;   // barrier counter, exit counter, status, abort
   // debug (optional)
   int* dbg_idx;

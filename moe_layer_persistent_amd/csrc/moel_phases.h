@@ -4,6 +4,11 @@
 // splits its work by workgroup index, so the same function serves both the persistent
 // launch (phases separated by grid barriers) and the one-kernel-per-step chain.
 //
+// Precision: weights are bf16 or NVFP4 and the KV cache is bf16 (storage formats).  Every
+// activation is kept in fp32 and enters the bf16 MFMAs as a pair of bf16 values (the
+// nearest bf16 and the bf16 of the remainder, ~16 significant bits), so no activation is
+// rounded to bf16 on the way through the layer.
+//
 // Packed weight layouts (produced by the pack kernels in moel_kernels.hip):
 //   dense bf16 [N, K]  : 16-row tiles; per tile K/32 steps of 1 KiB; in a step, lane l holds
 //                        the 8 bf16 of row (l % 16), k = 32*step + 8*(l / 16) + 0..7 -- the
@@ -38,6 +43,14 @@ __device__ __forceinline__ RouteTables& route_tables(char* smem) {
   return *reinterpret_cast<RouteTables*>(smem);
 }
 __device__ __forceinline__ char* phase_smem(char* smem) { return smem + kRouteBytes; }
+
+// 8 fp32 -> (hi, lo) bf16x8 operands
+__device__ __forceinline__ void split8(const float4& a, const float4& b, u32x4& hi, u32x4& lo) {
+  const u32x2 s0 = split_bf16(a.x, a.y), s1 = split_bf16(a.z, a.w);
+  const u32x2 s2 = split_bf16(b.x, b.y), s3 = split_bf16(b.z, b.w);
+  hi = u32x4{s0[0], s1[0], s2[0], s3[0]};
+  lo = u32x4{s0[1], s1[1], s2[1], s3[1]};
+}
 
 // ------------------------------------------------------------------------------------------
 // RMSNorm statistics
@@ -77,37 +90,45 @@ __device__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp,
 }
 
 // ------------------------------------------------------------------------------------------
-// A-operand sources of the dense contractions: lane supplies A[token][k .. k+7] as 8 bf16.
+// A-operand sources of the dense contractions: lane supplies A[token][k .. k+7] as hi + lo.
 // ------------------------------------------------------------------------------------------
-struct ANorm {  // r(v * rstd * gamma) computed on the fly from an fp32 row
+struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
   const float* v;
   int ld;
   const uint16_t* gamma;
   float rstd;  // of this lane's token
   int T;
-  __device__ __forceinline__ u32x4 load(int tok, int k) const {
-    u32x4 r = {0u, 0u, 0u, 0u};
+  __device__ __forceinline__ void load2(int tok, int k, u32x4& hi, u32x4& lo) const {
+    hi = u32x4{0u, 0u, 0u, 0u};
+    lo = u32x4{0u, 0u, 0u, 0u};
     if (tok < T) {
       const float* src = v + (size_t)tok * ld + k;
       float4 a = *reinterpret_cast<const float4*>(src);
       float4 b = *reinterpret_cast<const float4*>(src + 4);
-      u32x4 g = ldg16(gamma + k);
-      r[0] = pack2bf(a.x * rstd * bf_lo(g[0]), a.y * rstd * bf_hi(g[0]));
-      r[1] = pack2bf(a.z * rstd * bf_lo(g[1]), a.w * rstd * bf_hi(g[1]));
-      r[2] = pack2bf(b.x * rstd * bf_lo(g[2]), b.y * rstd * bf_hi(g[2]));
-      r[3] = pack2bf(b.z * rstd * bf_lo(g[3]), b.w * rstd * bf_hi(g[3]));
+      const u32x4 g = ldg16(gamma + k);
+      a.x = a.x * rstd * bf_lo(g[0]);
+      a.y = a.y * rstd * bf_hi(g[0]);
+      a.z = a.z * rstd * bf_lo(g[1]);
+      a.w = a.w * rstd * bf_hi(g[1]);
+      b.x = b.x * rstd * bf_lo(g[2]);
+      b.y = b.y * rstd * bf_hi(g[2]);
+      b.z = b.z * rstd * bf_lo(g[3]);
+      b.w = b.w * rstd * bf_hi(g[3]);
+      split8(a, b, hi, lo);
     }
-    return r;
   }
 };
-struct ABf16 {  // a stored bf16 row
-  const uint16_t* v;
+struct AF32 {  // a stored fp32 row
+  const float* v;
   int ld;
   int T;
-  __device__ __forceinline__ u32x4 load(int tok, int k) const {
-    u32x4 r = {0u, 0u, 0u, 0u};
-    if (tok < T) r = ldg16(v + (size_t)tok * ld + k);
-    return r;
+  __device__ __forceinline__ void load2(int tok, int k, u32x4& hi, u32x4& lo) const {
+    hi = u32x4{0u, 0u, 0u, 0u};
+    lo = u32x4{0u, 0u, 0u, 0u};
+    if (tok < T) {
+      const float* src = v + (size_t)tok * ld + k;
+      split8(*reinterpret_cast<const float4*>(src), *reinterpret_cast<const float4*>(src + 4), hi, lo);
+    }
   }
 };
 
@@ -146,24 +167,29 @@ __device__ void dense_pass(const uint8_t* w0, int tiles0, const uint8_t* w1, int
                 lane * 16;
     }
     // two-stage software pipeline over k steps
-    u32x4 a_cur = A.load(tok, 32 * sa + kq), w_cur[4];
+    u32x4 a_hi, a_lo, w_cur[4];
+    A.load2(tok, 32 * sa + kq, a_hi, a_lo);
 #pragma unroll
     for (int j = 0; j < 4; ++j)
       w_cur[j] = on[j] ? ldg_stream(base[j] + (size_t)sa * 1024) : u32x4{0u, 0u, 0u, 0u};
     for (int s = sa; s < sb; ++s) {
-      u32x4 a_nxt = {0u, 0u, 0u, 0u}, w_nxt[4];
+      u32x4 n_hi = {0u, 0u, 0u, 0u}, n_lo = {0u, 0u, 0u, 0u}, w_nxt[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) w_nxt[j] = u32x4{0u, 0u, 0u, 0u};
       if (s + 1 < sb) {
-        a_nxt = A.load(tok, 32 * (s + 1) + kq);
+        A.load2(tok, 32 * (s + 1) + kq, n_hi, n_lo);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
           if (on[j]) w_nxt[j] = ldg_stream(base[j] + (size_t)(s + 1) * 1024);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < ntiles) acc[j] = mfma16x16x32(a_cur, w_cur[j], acc[j]);
-      a_cur = a_nxt;
+        if (j < ntiles) {
+          acc[j] = mfma16x16x32(a_hi, w_cur[j], acc[j]);
+          acc[j] = mfma16x16x32(a_lo, w_cur[j], acc[j]);
+        }
+      a_hi = n_hi;
+      a_lo = n_lo;
 #pragma unroll
       for (int j = 0; j < 4; ++j) w_cur[j] = w_nxt[j];
     }
@@ -216,7 +242,7 @@ __device__ __forceinline__ bool octet_in(int row, int lo, int hi) {
 // ------------------------------------------------------------------------------------------
 // QKV projection + RoPE + q store + KV-cache write.  w_qkv rows are packed with the
 // rotation partners (i, i + D/2) of every head interleaved: packed row 2i <-> canonical i,
-// packed row 2i+1 <-> canonical i + D/2.
+// packed row 2i+1 <-> canonical i + D/2.  The cache stores bf16 (nearest); q stays fp32.
 // ------------------------------------------------------------------------------------------
 __device__ void phase_qkv(const LayerParams& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
@@ -239,9 +265,9 @@ __device__ void phase_qkv(const LayerParams& p, int wg, char* smem) {
                     const float s = p.rope_sin[(size_t)ps * half + i];
                     const float ra = a * c - b * s, rb = b * c + a * s;
                     if (head < p.Hq) {
-                      uint16_t* q = p.q_buf + (size_t)t * p.Hq * p.D + head * p.D;
-                      q[i] = f2bf(ra);
-                      q[i + half] = f2bf(rb);
+                      float* q = p.q_buf + (size_t)t * p.Hq * p.D + head * p.D;
+                      q[i] = ra;
+                      q[i + half] = rb;
                     } else {
                       uint16_t* k = p.k_cache + ((size_t)(head - p.Hq) * p.kv_cap + ps) * p.D;
                       k[i] = f2bf(ra);
@@ -258,8 +284,8 @@ __device__ void phase_qkv(const LayerParams& p, int wg, char* smem) {
 
 // ------------------------------------------------------------------------------------------
 // Attention partials.  Item = (kv head g, key chunk c); each wave is one q head of the group.
-// S^T = K Q^T on MFMA (keys as rows), softmax in fp32 with the exact max of each 256-key
-// sub-chunk and an online rescale between sub-chunks, O += P V on MFMA.
+// S^T = K Q^T on MFMA (keys as rows; q as hi + lo), softmax in fp32 with the exact max of each
+// 256-key sub-chunk and an online rescale between sub-chunks, O += P V on MFMA (P as hi + lo).
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct AttnLds {
@@ -288,12 +314,15 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
     if (ke > p.attn_lo + p.attn_nkeys) ke = p.attn_lo + p.attn_nkeys;
     const bool act = wv < grp;
     const int h = g * grp + wv;
-    u32x4 qf[NS];
+    u32x4 qh[NS], ql[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
-      qf[s] = u32x4{0u, 0u, 0u, 0u};
-      if (act && tq < p.T)
-        qf[s] = ldg16(p.q_buf + (size_t)tq * p.Hq * D + h * D + 32 * s + 8 * gq);
+      qh[s] = u32x4{0u, 0u, 0u, 0u};
+      ql[s] = u32x4{0u, 0u, 0u, 0u};
+      if (act && tq < p.T) {
+        const float* qs = p.q_buf + (size_t)tq * p.Hq * D + h * D + 32 * s + 8 * gq;
+        split8(*reinterpret_cast<const float4*>(qs), *reinterpret_cast<const float4*>(qs + 4), qh[s], ql[s]);
+      }
     }
     float m_run = NEG, l_run = 0.f;
     f32x4 O[ND];
@@ -330,7 +359,8 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
               u32x4 ka = *reinterpret_cast<const u32x4*>(&L.Ks[(kt * 16 + tq) * KS + 32 * s + 8 * gq]);
-              S[kt] = mfma16x16x32(ka, qf[s], S[kt]);
+              S[kt] = mfma16x16x32(ka, qh[s], S[kt]);
+              S[kt] = mfma16x16x32(ka, ql[s], S[kt]);
             }
           }
         }
@@ -374,18 +404,20 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
 #pragma unroll
         for (int kp = 0; kp < 8; ++kp) {
           if (kp * 32 < nk) {
-            u32x4 pa;
-            pa[0] = pack2bf(S[2 * kp][0], S[2 * kp][1]);
-            pa[1] = pack2bf(S[2 * kp][2], S[2 * kp][3]);
-            pa[2] = pack2bf(S[2 * kp + 1][0], S[2 * kp + 1][1]);
-            pa[3] = pack2bf(S[2 * kp + 1][2], S[2 * kp + 1][3]);
+            const u32x2 q0 = split_bf16(S[2 * kp][0], S[2 * kp][1]);
+            const u32x2 q1 = split_bf16(S[2 * kp][2], S[2 * kp][3]);
+            const u32x2 q2 = split_bf16(S[2 * kp + 1][0], S[2 * kp + 1][1]);
+            const u32x2 q3 = split_bf16(S[2 * kp + 1][2], S[2 * kp + 1][3]);
+            const u32x4 ph = {q0[0], q1[0], q2[0], q3[0]};
+            const u32x4 plo = {q0[1], q1[1], q2[1], q3[1]};
 #pragma unroll
             for (int d = 0; d < ND; ++d) {
               const uint16_t* vr = &L.Vt[(16 * d + tq) * VS + kp * 32 + 4 * gq];
               u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
               u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
               u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
-              O[d] = mfma16x16x32(pa, vb, O[d]);
+              O[d] = mfma16x16x32(ph, vb, O[d]);
+              O[d] = mfma16x16x32(plo, vb, O[d]);
             }
           }
         }
@@ -406,7 +438,7 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
   }
 }
 
-// Merge the key-chunk partials of every (token, q head) row -> o (bf16).
+// Merge the key-chunk partials of every (token, q head) row -> o (fp32).
 __device__ void phase_attn_merge(const LayerParams& p, int wg) {
   const int grp = p.Hq / p.Hkv;
   const int total = p.T * p.Hq * p.D;
@@ -427,7 +459,7 @@ __device__ void phase_attn_merge(const LayerParams& p, int wg) {
       num += wgt * p.attn_o[((size_t)(it * grp + w) * kMaxT + t) * p.D + d];
       den += wgt * ml[1];
     }
-    p.o_buf[(size_t)t * p.Hq * p.D + h * p.D + d] = f2bf(num / den);
+    p.o_buf[(size_t)t * p.Hq * p.D + h * p.D + d] = num / den;
   }
 }
 
@@ -436,7 +468,7 @@ __device__ void phase_attn_merge(const LayerParams& p, int wg) {
 // ------------------------------------------------------------------------------------------
 __device__ void phase_oproj(const LayerParams& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  ABf16 A{p.o_buf, p.Hq * p.D, p.T};
+  AF32 A{p.o_buf, p.Hq * p.D, p.T};
   float part = 0.f;  // thread t < 16 accumulates token t over the workgroup's rows
   dense_phase(p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
@@ -462,8 +494,8 @@ __device__ void phase_oproj(const LayerParams& p, int wg, char* smem) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Router logits (fp32) and pooler (bf16) from hn = r(h * rstd2 * gamma2), one contraction
-// over the stacked rows [router; pooler].
+// Router logits and pooler from hn = h * rstd2 * gamma2, one contraction over the stacked
+// rows [router; pooler].
 // ------------------------------------------------------------------------------------------
 __device__ void phase_router_pool(const LayerParams& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
@@ -481,7 +513,7 @@ __device__ void phase_router_pool(const LayerParams& p, int wg, char* smem) {
                     p.logits[t * p.E + n] = v;
                     if (p.dbg_logits) p.dbg_logits[t * p.E + n] = v;
                   } else {
-                    p.pl[(size_t)t * p.P + (n - p.E)] = f2bf(v);
+                    p.pl[(size_t)t * p.P + (n - p.E)] = v;
                   }
                 }
               });
@@ -598,25 +630,26 @@ __device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write
 }
 
 // ------------------------------------------------------------------------------------------
-// NVFP4 experts on 4x4x4 MFMA: a wavefront lane owns one weight row; the activation of up to
-// 4 tokens is broadcast from one 4-lane block to all 16 blocks (CBSZ=4, ABID selects the
-// 4-element k slice).  The E4M3 block scale multiplies each 16-k partial in fp32.
-// G = token groups of 4 (1..4), NM = matrices sharing the activation (2 = gate+up, 1 = down).
+// NVFP4 experts on 4x4x4 MFMA: a wavefront lane owns one weight row.  The 4 A rows of each
+// 4x4x4 block carry 2 tokens as (hi, hi', lo, lo') and are broadcast from one 4-lane block
+// to all 16 blocks (CBSZ=4, ABID selects the 4-element k slice); row sums hi + lo give the
+// fp32-accurate product.  The E4M3 block scale multiplies each 16-k partial in fp32.
+// G = token pairs (1, 2, 4, 8), NM = matrices sharing the activation (2 gate+up, 1 down).
 // ------------------------------------------------------------------------------------------
 struct Fp4Lds {
-  float red[kWaves * 64 * 32];   // [wave][lane][NM*16 + g*4 + r], 64 KiB
+  float red[kWaves * 64 * 32];   // [wave][lane][m*16 + token slot j], 64 KiB
 };
 
 template <int NM, int G>
 struct Fp4Pair {
   u32x4 c[NM][2];   // codes of the pair's two 32-k steps
   uint32_t sc[NM];  // 4 block scales of the pair
-  u32x2 a[G];       // activation: lane 4b+i holds A[token 4g+i][k0 + 4b .. +3]
+  u32x2 a[G];       // lane 4b+i: row i of group g (hi/lo of token 2g + (i&1)), k0 + 4b .. +3
 };
 
 template <int NM, int G>
-__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const* wt, int pr,
-                                              const uint16_t* const* arow, int k0) {
+__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM], int pr,
+                                              const float* const (&arow)[G], int k0) {
   const int lane = lane_id();
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -625,10 +658,15 @@ __device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* 
     f.c[m][1] = ldg_stream(b + 1024 + lane * 16);
     f.sc[m] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + 2048) + lane);
   }
+  const bool lo_row = (lane & 2) != 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     f.a[g] = u32x2{0u, 0u};
-    if (arow[g] != nullptr) f.a[g] = ldg8(arow[g] + k0 + 4 * (lane >> 2));
+    if (arow[g] != nullptr) {
+      const float4 v = *reinterpret_cast<const float4*>(arow[g] + k0 + 4 * (lane >> 2));
+      const u32x2 s01 = split_bf16(v.x, v.y), s23 = split_bf16(v.z, v.w);
+      f.a[g] = lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
+    }
   }
 }
 
@@ -658,19 +696,16 @@ __device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, f32x4 (&
 }
 
 template <int NM, int G>
-__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, bool second,
-                                                 f32x4 (&acc)[NM][G]) {
+__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 (&acc)[NM][G]) {
   fp4_mfma_block<0, 0>(f, acc);
   fp4_mfma_block<0, 1>(f, acc);
-  if (second) {
-    fp4_mfma_block<1, 0>(f, acc);
-    fp4_mfma_block<1, 1>(f, acc);
-  }
+  fp4_mfma_block<1, 0>(f, acc);
+  fp4_mfma_block<1, 1>(f, acc);
 }
 
 // One expert's run of 64-row tiles [ta, tb) for this workgroup.
-//   GATEUP: NM = 2, activation = pl rows of the expert's tokens, out a = r(silu(g)*u)
-//   else  : NM = 1, activation = a rows of the expert's slots,   out d (fp32)
+//   GATEUP: NM = 2, activation = pl rows of the expert's tokens, out a = silu(g) * u
+//   else  : NM = 1, activation = a rows of the expert's slots,   out d
 template <bool GATEUP, int G>
 __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int u, int ta, int tb,
                                  Fp4Lds& L) {
@@ -679,11 +714,11 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
   const int e = R.active_e[u];
   const int s_lo = R.active_off[u], n_e = R.active_off[u + 1] - s_lo;
   const int K = GATEUP ? p.P : p.I;
-  const int S = K >> 5, Sp = (S + 1) >> 1;  // 32-k steps, pairs
+  const int Sp = K >> 6;  // 64-k pairs (K % 128 == 0)
   const int nkw = Sp < kWaves ? Sp : kWaves;
   const int pa = wv * Sp / nkw, pb = (wv + 1) * Sp / nkw;
   const bool kw = wv < nkw;
-  const size_t tile_bytes = (size_t)32 * K + (size_t)4 * K;  // 64 rows: K/2 + K/16 bytes each
+  const size_t tile_bytes = (size_t)36 * K;  // 64 rows of K/2 + K/16 bytes
   const uint8_t* wb[NM];
   if (GATEUP) {
     wb[0] = p.w_gate + (size_t)e * p.stride_gate;
@@ -691,11 +726,11 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
   } else {
     wb[0] = p.w_down + (size_t)e * p.stride_down;
   }
-  // activation rows of this lane's tokens (lane 4b+i -> token slot 4g+i)
-  const uint16_t* arow[G];
+  // activation rows: lane 4b+i carries token slot 2g + (i & 1)
+  const float* arow[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int j = 4 * g + (lane & 3);
+    const int j = 2 * g + (lane & 1);
     arow[g] = nullptr;
     if (j < n_e) {
       const int slot = R.slots[s_lo + j];
@@ -723,16 +758,17 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
     if (kw) {
       for (int q = 0; q < npt; ++q, ++n) {
         if (n + 1 < total) issue(nxt, n + 1);
-        const int pr = pa + q;
-        fp4_pair_compute<NM, G>(cur, 2 * pr + 1 < S, acc);
+        fp4_pair_compute<NM, G>(cur, acc);
         cur = nxt;
       }
+      // rows (hi, hi', lo, lo') -> token slots 2g, 2g+1
 #pragma unroll
       for (int m = 0; m < NM; ++m)
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) L.red[(wv * 64 + lane) * 32 + m * 16 + g * 4 + r] = acc[m][g][r];
+        for (int g = 0; g < G; ++g) {
+          L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g] = acc[m][g][0] + acc[m][g][2];
+          L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g + 1] = acc[m][g][1] + acc[m][g][3];
+        }
     }
     lds_barrier();
     // reduce over the k-waves in order; lane row = ti*64 + ln
@@ -747,8 +783,7 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
         }
         gs *= p.ts_gate[e];
         us *= p.ts_up[e];
-        const float a = gs / (1.0f + __expf(-gs)) * us;
-        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 64 + ln] = f2bf(a);
+        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 64 + ln] = gs / (1.0f + __expf(-gs)) * us;
       } else {
         float ds = 0.f;
         for (int w = 0; w < nkw; ++w) ds += L.red[(w * 64 + ln) * 32 + j];
@@ -760,7 +795,8 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
 }
 
 // ------------------------------------------------------------------------------------------
-// bf16 experts on 16x16x32 MFMA (the expert's <= 16 slots form the M tile).
+// bf16 experts on 16x16x32 MFMA.  The 16 A rows carry up to 8 slots as (hi x8, lo x8); a
+// second row tile takes slots 8..15.
 // ------------------------------------------------------------------------------------------
 template <bool GATEUP>
 __device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, int u, int ta, int tb,
@@ -773,7 +809,7 @@ __device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, in
   const int S = K >> 5;
   const int nkw = S < kWaves ? S : kWaves;
   const int sa = wv * S / nkw, sb = (wv + 1) * S / nkw;
-  const int rows = GATEUP ? p.I_loc : p.P_loc;
+  const int nrt = n_e > 8 ? 2 : 1;  // row tiles
   const uint8_t* wb[NM];
   if (GATEUP) {
     wb[0] = p.w_gate + (size_t)e * p.stride_gate;
@@ -781,63 +817,71 @@ __device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, in
   } else {
     wb[0] = p.w_down + (size_t)e * p.stride_down;
   }
-  (void)rows;
-  const int jt = lane & 15;
-  const uint16_t* arow = nullptr;
-  if (jt < n_e) {
-    const int slot = R.slots[s_lo + jt];
-    arow = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
+  const bool lo_row = (lane & 15) >= 8;
+  const float* arow[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const int j = 8 * rt + (lane & 7);
+    arow[rt] = nullptr;
+    if (j < n_e) {
+      const int slot = R.slots[s_lo + j];
+      arow[rt] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
+    }
   }
   const int kq = 8 * (lane >> 4);
+  auto aload = [&](int rt, int s) -> u32x4 {
+    u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+    if (arow[rt] != nullptr) {
+      const float* src = arow[rt] + 32 * s + kq;
+      split8(*reinterpret_cast<const float4*>(src), *reinterpret_cast<const float4*>(src + 4), hi, lo);
+    }
+    return lo_row ? lo : hi;
+  };
   for (int ti = ta; ti < tb; ++ti) {
-    f32x4 acc[NM];
+    f32x4 acc[2][NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (wv < nkw) {
       const uint8_t* tb_[NM];
 #pragma unroll
       for (int m = 0; m < NM; ++m) tb_[m] = wb[m] + (size_t)ti * S * 1024 + lane * 16;
-      u32x4 a_cur = arow ? ldg16(arow + 32 * sa + kq) : u32x4{0u, 0u, 0u, 0u};
-      u32x4 w_cur[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) w_cur[m] = ldg_stream(tb_[m] + (size_t)sa * 1024);
       for (int s = sa; s < sb; ++s) {
-        u32x4 a_nxt = {0u, 0u, 0u, 0u}, w_nxt[NM];
+        u32x4 w[NM];
 #pragma unroll
-        for (int m = 0; m < NM; ++m) w_nxt[m] = u32x4{0u, 0u, 0u, 0u};
-        if (s + 1 < sb) {
-          if (arow) a_nxt = ldg16(arow + 32 * (s + 1) + kq);
+        for (int m = 0; m < NM; ++m) w[m] = ldg_stream(tb_[m] + (size_t)s * 1024);
 #pragma unroll
-          for (int m = 0; m < NM; ++m) w_nxt[m] = ldg_stream(tb_[m] + (size_t)(s + 1) * 1024);
+        for (int rt = 0; rt < 2; ++rt) {
+          if (rt < nrt) {
+            const u32x4 a = aload(rt, s);
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[rt][m] = mfma16x16x32(a, w[m], acc[rt][m]);
+          }
         }
-#pragma unroll
-        for (int m = 0; m < NM; ++m) acc[m] = mfma16x16x32(a_cur, w_cur[m], acc[m]);
-        a_cur = a_nxt;
-#pragma unroll
-        for (int m = 0; m < NM; ++m) w_cur[m] = w_nxt[m];
       }
 #pragma unroll
-      for (int m = 0; m < NM; ++m) L.red[(wv * 4 + m) * 64 + lane] = acc[m];
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int m = 0; m < NM; ++m) L.red[(wv * 4 + rt * 2 + m) * 64 + lane] = acc[rt][m];
     }
     lds_barrier();
-    // output element (slot j, row r): lane ln = 16*(j/4) + r holds it at component j%4
+    // slot j = 8*rt + jj: hi at A row jj, lo at row 8 + jj; row i lives in lane 16*(i/4)+r, comp i%4
     for (int x = threadIdx.x; x < 16 * n_e; x += kThreads) {
       const int r = x & 15, j = x >> 4;
-      const int ln = 16 * (j >> 2) + r, c = j & 3;
+      const int rt = j >> 3, jj = j & 7;
+      const int l_hi = 16 * (jj >> 2) + r, l_lo = 16 * ((8 + jj) >> 2) + r, c = jj & 3;
       const int slot = R.slots[s_lo + j];
-      if (GATEUP) {
-        float gs = 0.f, us = 0.f;
-        for (int w = 0; w < nkw; ++w) {
-          gs += L.red[(w * 4 + 0) * 64 + ln][c];
-          us += L.red[(w * 4 + 1) * 64 + ln][c];
-        }
-        const float a = gs / (1.0f + __expf(-gs)) * us;
-        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 16 + r] = f2bf(a);
-      } else {
-        float ds = 0.f;
-        for (int w = 0; w < nkw; ++w) ds += L.red[(w * 4 + 0) * 64 + ln][c];
-        p.d_buf[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = ds;
+      float s0 = 0.f, s1 = 0.f;
+      for (int w = 0; w < nkw; ++w) {
+        s0 += L.red[(w * 4 + rt * 2 + 0) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + 0) * 64 + l_lo][c];
+        if (GATEUP)
+          s1 += L.red[(w * 4 + rt * 2 + 1) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + 1) * 64 + l_lo][c];
       }
+      if (GATEUP)
+        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 16 + r] = s0 / (1.0f + __expf(-s0)) * s1;
+      else
+        p.d_buf[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = s0;
     }
     lds_barrier();
   }
@@ -861,12 +905,10 @@ __device__ void phase_experts(const LayerParams& p, int wg, char* smem) {
     if (fp4) {
       Fp4Lds& L = *reinterpret_cast<Fp4Lds*>(phase_smem(smem));
       const int n_e = R.active_off[u + 1] - R.active_off[u];
-      switch ((n_e + 3) >> 2) {
-        case 1: fp4_expert_tiles<GATEUP, 1>(p, R, u, ta, tb, L); break;
-        case 2: fp4_expert_tiles<GATEUP, 2>(p, R, u, ta, tb, L); break;
-        case 3: fp4_expert_tiles<GATEUP, 3>(p, R, u, ta, tb, L); break;
-        default: fp4_expert_tiles<GATEUP, 4>(p, R, u, ta, tb, L); break;
-      }
+      if (n_e <= 2) fp4_expert_tiles<GATEUP, 1>(p, R, u, ta, tb, L);
+      else if (n_e <= 4) fp4_expert_tiles<GATEUP, 2>(p, R, u, ta, tb, L);
+      else if (n_e <= 8) fp4_expert_tiles<GATEUP, 4>(p, R, u, ta, tb, L);
+      else fp4_expert_tiles<GATEUP, 8>(p, R, u, ta, tb, L);
     } else {
       DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
       bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
@@ -875,7 +917,7 @@ __device__ void phase_experts(const LayerParams& p, int wg, char* smem) {
   }
 }
 
-// m[t] = r(sum over the token's slots, in selection order, of gate * d)
+// m[t] = sum over the token's slots, in selection order, of gate * d
 __device__ void phase_combine(const LayerParams& p, int wg, char* smem) {
   const RouteTables& R = route_tables(smem);
   const int total = p.T * p.P_loc;
@@ -884,14 +926,14 @@ __device__ void phase_combine(const LayerParams& p, int wg, char* smem) {
     float s = 0.f;
     for (int k = 0; k < p.topk; ++k)
       s = fmaf(R.gate[t * p.topk + k], p.d_buf[(size_t)(t * p.topk + k) * p.P + pc], s);
-    p.m_buf[(size_t)t * p.P + pc] = f2bf(s);
+    p.m_buf[(size_t)t * p.P + pc] = s;
   }
 }
 
 // y = h + m W_unpool^T
 __device__ void phase_unpool(const LayerParams& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  ABf16 A{p.m_buf, p.P, p.T};
+  AF32 A{p.m_buf, p.P, p.T};
   dense_phase(p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {

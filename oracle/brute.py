@@ -4,7 +4,8 @@ Test infrastructure only (see the package docstring).
 
 Every quantity is a Python float (IEEE binary64) computed with explicit loops:
 per token, per head, per key, per output feature, per reduction index.  It
-re-derives each definition (bf16 rounding, E2M1 / E4M3 decoding, RMSNorm,
+re-derives each definition (bf16 rounding of the cache writes, E2M1 / E4M3
+decoding, RMSNorm,
 rotate-half RoPE, windowed causal attention, top-k routing with the lower index
 winning ties, SwiGLU experts, combine, residuals) from the written rules and
 does not call into ``layer.py`` or ``formats.py``, so that the vectorised
@@ -68,13 +69,13 @@ def _dot(a, b) -> float:
     return s
 
 
-def _norm_round(vec: List[float], gamma: List[float], eps: float) -> List[float]:
+def _norm(vec: List[float], gamma: List[float], eps: float) -> List[float]:
     n = len(vec)
     ss = 0.0
     for v in vec:
         ss += v * v
     inv = 1.0 / math.sqrt(ss / n + eps)
-    return [r_bf16(vec[i] * inv * gamma[i]) for i in range(n)]
+    return [vec[i] * inv * gamma[i] for i in range(n)]
 
 
 def _rotate(vec: List[float], position: int, theta: float) -> List[float]:
@@ -106,12 +107,12 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
     # RMSNorm 1, QKV projection, RoPE, rounding, cache write
     q_all, k_all, v_all = [], [], []
     for t in range(T):
-        xn = _norm_round(x[t], [float(v) for v in inp["gamma1"]], dims.rms_eps)
+        xn = _norm(x[t], [float(v) for v in inp["gamma1"]], dims.rms_eps)
         row = [_dot(xn, [float(v) for v in w_qkv[n]]) for n in range(len(w_qkv))]
         qh = [_rotate(row[h * D:(h + 1) * D], pos + t, dims.rope_theta) for h in range(Hq)]
         kh = [_rotate(row[(Hq + g) * D:(Hq + g + 1) * D], pos + t, dims.rope_theta) for g in range(Hkv)]
         vh = [row[(Hq + Hkv + g) * D:(Hq + Hkv + g + 1) * D] for g in range(Hkv)]
-        q_all.append([[r_bf16(v) for v in qv] for qv in qh])
+        q_all.append([list(qv) for qv in qh])
         k_all.append([[r_bf16(v) for v in kv] for kv in kh])
         v_all.append([[r_bf16(v) for v in vv] for vv in vh])
         for g in range(Hkv):
@@ -135,7 +136,7 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
                 acc = 0.0
                 for i, j in enumerate(keys):
                     acc += ws[i] / tot * vc[g][j][d]
-                o_flat.append(r_bf16(acc))
+                o_flat.append(acc)
         h_row = []
         for n in range(H):
             h_row.append(x[t][n] + _dot(o_flat, [float(v) for v in inp["w_o"][n]]))
@@ -147,7 +148,7 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
     rk = dims.shard_rank
     y, idx_all, gate_all, logit_all = [], [], [], []
     for t in range(T):
-        hn = _norm_round(h_all[t], [float(v) for v in inp["gamma2"]], dims.rms_eps)
+        hn = _norm(h_all[t], [float(v) for v in inp["gamma2"]], dims.rms_eps)
         logits = [_dot(hn, [float(v) for v in inp["w_router"][e]]) for e in range(E)]
         remaining = list(range(E))
         chosen = []
@@ -161,7 +162,7 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
         mx = max(logits[e] for e in chosen)
         ex = [math.exp(logits[e] - mx) for e in chosen]
         gates = [v / sum(ex) for v in ex]
-        pl = [r_bf16(_dot(hn, [float(v) for v in inp["w_pool"][pp]])) for pp in range(dims.pooled)]
+        pl = [_dot(hn, [float(v) for v in inp["w_pool"][pp]]) for pp in range(dims.pooled)]
         m_acc = [0.0] * dims.pooled
         for slot, e in enumerate(chosen):
             raw = expert_raw(e)
@@ -179,7 +180,7 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
                     gsum = _dot(pl, [float(v) for v in raw["gate"][i]])
                     usum = _dot(pl, [float(v) for v in raw["up"][i]])
                 sig = gsum / (1.0 + math.exp(-gsum)) if gsum > -700 else 0.0
-                a[rk * il + i] = r_bf16(sig * usum)
+                a[rk * il + i] = sig * usum
             for pp in range(plc):
                 if nvfp4:
                     dc, ds, dts = raw["down"]
@@ -189,7 +190,7 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
                 else:
                     dsum = _dot(a, [float(v) for v in raw["down"][pp]])
                 m_acc[rk * plc + pp] += gates[slot] * dsum
-        m = [r_bf16(v) for v in m_acc]
+        m = m_acc
         y.append([h_all[t][n] + _dot(m, [float(v) for v in inp["w_unpool"][n]]) for n in range(H)])
         idx_all.append(chosen)
         gate_all.append(gates)

@@ -19,9 +19,9 @@ with its rationale in the design notes):
     on q and k of every layer
   * key j visible to the token at position p iff j <= p and (W == 0 or j > p - W)
   * GQA: q head h reads kv head floor(h * Hkv / Hq); score scale 1/sqrt(D)
-  * router on the normalised hidden state: fp32-or-better logits, top-k by
-    logit descending with ties to the lower expert index, gates = softmax over
-    the k selected logits, in selection order
+  * router on the normalised hidden state (the pooler's input): top-k by logit
+    descending with ties to the lower expert index, gates = softmax over the k
+    selected logits, in selection order
   * SwiGLU expert: a = silu(x Wg^T) * (x Wu^T); d = a Wd^T
   * combine: m_t = sum over the token's k slots, in selection order, of gate * d
   * expert N-sharding (one GPU's share): gate/up keep rows
@@ -29,10 +29,10 @@ with its rationale in the design notes):
     zero outside that slice; down keeps rows [rank*P/S, ...) of the pooled
     width and its output is zero elsewhere (zero padding stands in for the
     cross-GPU gathers).
-Precision contract: everything in fp64 except bf16 rounding r() of the values
-the device stores as bf16 operands: xn, q and k after RoPE, v, the attention
-output o, hn, the pooled vector pl, the SwiGLU output a and the combined
-vector m.  The residual stream (x, h, y) and the router logits stay wide.
+Precision: the layer in exact (fp64) arithmetic on its given inputs.  Weights
+are bf16 or NVFP4 and the KV cache is bf16: those are storage formats, so the
+new keys and values are rounded to bf16 (nearest even) when written to the
+cache and attention reads them from the cache.  No activation is rounded.
 """
 from __future__ import annotations
 
@@ -94,7 +94,7 @@ def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: int,
               window: int) -> np.ndarray:
     """GQA attention of the T new tokens over the (already updated) cache.
 
-    q [T, Hq, D] (bf16 values), caches [Hkv, C, D] -> o [T, Hq, D] (not rounded).
+    q [T, Hq, D], caches [Hkv, C, D] (bf16 values) -> o [T, Hq, D].
     Full score vector per query, its global max, exact normaliser.
     """
     T, Hq, D = q.shape
@@ -172,7 +172,7 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
     g = Wg @ pl_t
     u = Wu @ pl_t
     a = np.zeros(dims.inter)
-    a[r * il:(r + 1) * il] = bf16_round(silu(g) * u)
+    a[r * il:(r + 1) * il] = silu(g) * u
     d = np.zeros(dims.pooled)
     d[r * plc:(r + 1) * plc] = Wd @ a
     return a, d
@@ -198,25 +198,26 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     out: Dict[str, np.ndarray] = {}
 
     # attention block
-    xn = bf16_round(rmsnorm(x, inp["gamma1"], dims.rms_eps))
+    xn = rmsnorm(x, inp["gamma1"], dims.rms_eps)
     qkv = xn @ inp["w_qkv"].T
     q = qkv[:, :Hq * D].reshape(T, Hq, D)
     k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
     v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
     positions = pos + np.arange(T)
-    q_r = bf16_round(rope(q, positions, dims.rope_theta))
-    k_r = bf16_round(rope(k, positions, dims.rope_theta))
+    q_r = rope(q, positions, dims.rope_theta)
+    k_exact = rope(k, positions, dims.rope_theta)
+    k_r = bf16_round(k_exact)
     v_r = bf16_round(v)
     k_cache = np.array(inp["k_cache"], dtype=np.float64, copy=True)
     v_cache = np.array(inp["v_cache"], dtype=np.float64, copy=True)
     for t in range(T):
         k_cache[:, pos + t] = k_r[t]
         v_cache[:, pos + t] = v_r[t]
-    o = bf16_round(attention(q_r, k_cache, v_cache, pos, window))
+    o = attention(q_r, k_cache, v_cache, pos, window)
     h = x + o.reshape(T, Hq * D) @ inp["w_o"].T
 
     # MoE block
-    hn = bf16_round(rmsnorm(h, inp["gamma2"], dims.rms_eps))
+    hn = rmsnorm(h, inp["gamma2"], dims.rms_eps)
     logits = hn @ inp["w_router"].T
     idx, gates, gap = route(logits, dims.top_k)
     if force_idx is not None:
@@ -224,7 +225,7 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
         sel = np.take_along_axis(logits, idx, axis=1)
         z = np.exp(sel - sel.max(axis=1, keepdims=True))
         gates = z / z.sum(axis=1, keepdims=True)
-    pl = bf16_round(hn @ inp["w_pool"].T)
+    pl = hn @ inp["w_pool"].T
 
     toks = range(T) if moe_tokens is None else list(moe_tokens)
     m = np.full((T, dims.pooled), np.nan)
@@ -241,12 +242,13 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
         acc = np.zeros(dims.pooled)
         for kk in range(dims.top_k):              # selection order
             acc = acc + gates[t, kk] * d_all[t, kk]
-        m[t] = bf16_round(acc)
+        m[t] = acc
     y = np.full((T, H), np.nan)
     tl = list(toks)
     y[tl] = h[tl] + m[tl] @ inp["w_unpool"].T
 
-    out.update(y=y, xn=xn, q=q_r, k_new=k_r, v_new=v_r, o=o, h=h, hn=hn, logits=logits,
+    out.update(y=y, xn=xn, q=q_r, k_new=k_r, v_new=v_r, k_exact=k_exact, v_exact=v, o=o, h=h, hn=hn,
+               logits=logits,
                idx=idx, gates=gates, gap=gap, pl=pl, a=a_all, d=d_all, m=m,
                k_cache=k_cache, v_cache=v_cache)
     return out

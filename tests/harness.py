@@ -133,24 +133,42 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
     ref = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), force_idx=gpu_idx, moe_tokens=toks)
     gate_err = float(np.abs(gsel - ref["gates"]).max())
     assert gate_err <= 2 * lg_err + 1e-5, f"gates max-abs {gate_err} (logits {lg_err})"
-    # KV cache: exact write set, values within the float bar
+    # KV cache: the written (head, slot) set is exact and every other byte is untouched; a
+    # written value is the bf16 nearest the exact value or, when the exact value lies within
+    # the device's arithmetic error of a rounding boundary, the other neighbour (< 1 ulp away)
     k_out, v_out = out["k_cache"], out["v_cache"]
-    for name, c_out, c_in, new in (("k", k_out, run.k0, ref["k_new"]), ("v", v_out, run.v0, ref["v_new"])):
+    kv_eq = []
+    for name, c_out, c_in, new, xv in (("k", k_out, run.k0, ref["k_new"], ref["k_exact"]),
+                                        ("v", v_out, run.v0, ref["v_new"], ref["v_exact"])):
         keep = torch.ones(c_in.shape[1], dtype=torch.bool, device=c_in.device)
         keep[pos:pos + T] = False
         assert torch.equal(c_out[:, keep].view(torch.int16), c_in[:, keep].view(torch.int16)), \
             f"{name} cache changed outside the written slots"
         got = _f64(c_out[:, pos:pos + T]).transpose(1, 0, 2)          # [T, Hkv, D]
-        err = np.abs(got - new).max()
-        assert err <= Y_MAX_ABS, f"{name} written values max-abs {err}"
+        ulp = np.ldexp(1.0, np.frexp(np.abs(xv))[1] - 8)             # bf16 spacing at |exact|
+        # the device's own error on a value is relative to the magnitude of its row, not to the
+        # value (a small result of a long sum carries the absolute error of the sum)
+        scale = np.abs(xv).max(axis=-1, keepdims=True)
+        off = np.abs(got - xv) / (ulp + 2.0 ** -13 * scale)
+        assert off.max() < 1.0, f"{name} written value further than 1 ulp from exact ({off.max()})"
+        eq = float(np.mean(got == new))
+        assert eq >= 0.9, f"{name} bitwise-equal fraction {eq}"   # reported; a sanity floor only
+        kv_eq.append(eq)
         for t in range(T):
             assert cosine(got[t].ravel(), new[t].ravel()) >= Y_MIN_COS
     y = out["y"].cpu().numpy().astype(np.float64)
     stats = {"max_abs": 0.0, "min_cos": 1.0, "exempt_tokens": int((~exact).sum()),
              "order_equal_frac": float(np.mean(np.all(gpu_idx == ref0["idx"], axis=1))),
              "logit_err": lg_err, "gate_err": gate_err,
-             "kv_bitwise_frac": float(np.mean(
-                 _f64(k_out[:, pos:pos + T]).transpose(1, 0, 2) == ref["k_new"]))}
+             "kv_bitwise_frac": min(kv_eq)}
+    # intermediate activations (relative max error against the oracle's exact values)
+    inter = {}
+    for name, key, shape in (("q", "q", (16, -1)), ("o", "o", (16, -1)), ("h", "h", (16, -1)),
+                             ("pl", "pl", (16, -1))):
+        got_i = run.plan.scratch(name).view(*shape)[:T].cpu().numpy().astype(np.float64)
+        want = ref[key].reshape(T, -1)
+        inter[name] = float(np.abs(got_i - want).max() / (np.abs(want).max() + 1e-30))
+    stats["rel_err"] = inter
     for t in toks:
         err = float(np.abs(y[t] - ref["y"][t]).max())
         cs = cosine(y[t], ref["y"][t])

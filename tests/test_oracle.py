@@ -243,9 +243,9 @@ def test_full_topk_is_dense_softmax_mixture():
     prob /= prob.sum(axis=1, keepdims=True)
     g = np.einsum("eik,tk->tei", Wg, out["pl"])
     u = np.einsum("eik,tk->tei", Wu, out["pl"])
-    a = formats.bf16_round(g / (1 + np.exp(-g)) * u)
+    a = g / (1 + np.exp(-g)) * u
     d = np.einsum("epi,tei->tep", Wd, a)
-    m = formats.bf16_round(np.einsum("te,tep->tp", prob, d))
+    m = np.einsum("te,tep->tp", prob, d)
     y = out["h"] + m @ f["w_unpool"].T
     np.testing.assert_allclose(out["y"], y, rtol=1e-10, atol=1e-10)
 
