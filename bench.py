@@ -171,6 +171,17 @@ def main():
                      "algorithmic_bytes_per_launch": int(alg_bytes),
                      "kernel": "k_layer_fused (one cooperative launch per layer)"},
     }
+    # per-phase timeline of one fused launch (workgroup timestamps, 100 MHz clock)
+    names = ["norm1", "qkv_rope_kv", "attention", "attn_merge", "o_proj", "router_pool", "experts_gate_up",
+             "experts_down", "combine", "unpool"]
+    ts = torch.zeros((plan.workgroups, 16), dtype=torch.int64, device=dev)
+    plan.layer_decode(copies[0], kc, vc, x, w.pos, window, y, dbg={"timestamps": ts}, stream=stream)
+    torch.cuda.synchronize()
+    tsn = ts.cpu().numpy().astype(np.float64)
+    t0 = tsn[:, 10].min()
+    ends = [(tsn[:, i].max() - t0) / 100.0 for i in range(10)]
+    result["phase_end_us"] = {n: round(e, 1) for n, e in zip(names, ends)}
+    result["phase_us"] = {n: round(e - (ends[i - 1] if i else 0.0), 1) for i, (n, e) in enumerate(zip(names, ends))}
     if not args.no_unfused:
         _, d2 = timed(False, max(5, args.steps // 2), 2)
         result["unfused_chain_us"] = {"median": round(statistics.median(d2), 2), "launches": 10}

@@ -43,12 +43,26 @@ __device__ __forceinline__ u32x2 split_bf16(float a, float b) {
   return u32x2{(uint32_t)ha | ((uint32_t)hb << 16), pack2bf(a - bf2f(ha), b - bf2f(hb))};
 }
 
-// ---------------------------------------------------------------- loads (streamed weights)
-__device__ __forceinline__ u32x4 ldg_stream(const void* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+// ---------------------------------------------------------------- global memory access
+// Pointers reach the phases through a reference to the launch parameters, which hides their
+// address space; without this cast the compiler emits flat accesses, and flat loads also
+// count against lgkmcnt, so every LDS wait would drain the whole in-flight weight stream.
+template <class T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gl(T* p) {
+  return (__attribute__((address_space(1))) T*)p;
 }
-__device__ __forceinline__ u32x4 ldg16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 ldg8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ u32x4 ldg_stream(const void* p) {
+  return __builtin_nontemporal_load(gl(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ uint32_t ldg_stream32(const void* p) {
+  return __builtin_nontemporal_load(gl(reinterpret_cast<const uint32_t*>(p)));
+}
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *gl(reinterpret_cast<const u32x4*>(p)); }
+__device__ __forceinline__ u32x2 ldg8(const void* p) { return *gl(reinterpret_cast<const u32x2*>(p)); }
+__device__ __forceinline__ float4 ldgf4(const float* p) {
+  const f32x4 v = *gl(reinterpret_cast<const f32x4*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
 
 // ---------------------------------------------------------------- MFMA
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
@@ -94,35 +108,41 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------- control block
 enum CtrlWord { kBar = 0, kExit = 1, kStatus = 2, kAbort = 3 };
 
-__device__ __forceinline__ bool aborted(const LayerParams& p) {
-  return __hip_atomic_load(p.ctrl + kAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
+__device__ __forceinline__ bool aborted(KP& p) {
+  return __hip_atomic_load(gl(p.ctrl) + kAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
 // Grid-wide barrier of the persistent launch.  `target` grows by nwg per barrier within one
 // launch; the counter is reset by the last workgroup to leave the kernel.  Every wait is
 // bounded: after ~0.5 s the status word records a timeout and the wait ends.
-__device__ __forceinline__ void grid_barrier(const LayerParams& p, unsigned target) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+//
+// Visibility: every wave first waits for its own stores to reach the L2 of its XCD; one wave
+// per workgroup then writes the XCD's L2 back (release), arrives, spins, and invalidates the
+// CU's L1 and the XCD's L2 (acquire).  Those cache operations act on the whole CU / XCD, so a
+// single wave's fences cover the stores and later loads of all eight waves.
+__device__ __forceinline__ void grid_barrier(KP& p, unsigned target) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(p.ctrl + kBar, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_fetch_add(gl(p.ctrl) + kBar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(p.ctrl + kBar, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    while (__hip_atomic_load(gl(p.ctrl) + kBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
       __builtin_amdgcn_s_sleep(1);
       if (__builtin_amdgcn_s_memrealtime() - t0 > 50000000ull) {
-        __hip_atomic_store(p.ctrl + kStatus, (unsigned)MOEL_DEV_TIMEOUT, __ATOMIC_RELAXED,
+        __hip_atomic_store(gl(p.ctrl) + kStatus, (unsigned)MOEL_DEV_TIMEOUT, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   }
   __syncthreads();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
-__device__ __forceinline__ void stamp(const LayerParams& p, int slot) {
+__device__ __forceinline__ void stamp(KP& p, int slot) {
   if (p.dbg_ts != nullptr && threadIdx.x == 0)
-    p.dbg_ts[blockIdx.x * MOEL_N_STAMPS_DEV + slot] = __builtin_amdgcn_s_memrealtime();
+    gl(p.dbg_ts)[blockIdx.x * MOEL_N_STAMPS_DEV + slot] = __builtin_amdgcn_s_memrealtime();
 }
 
 }  // namespace moel

@@ -16,11 +16,36 @@ using namespace moel;
 // =========================================================================================
 // device: persistent launch
 // =========================================================================================
+// Each phase of the persistent launch is a separate (non-inlined) function so that the
+// register allocator sizes each phase on its own instead of the union of all of them.
+template <int PH, int D>
+__device__ __noinline__ void fused_phase(KP& p, int wg) {
+  char* smem = moel_lds;
+  if constexpr (PH == kPhNorm1) phase_norm1(p, wg);
+  if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
+  if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
+  if constexpr (PH == kPhAttnMerge) phase_attn_merge(p, wg);
+  if constexpr (PH == kPhOproj) phase_oproj(p, wg, smem);
+  if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, smem);
+  if constexpr (PH == kPhGemm1) {
+    compute_routing(p, route_tables(smem), wg == 0);
+    phase_experts<true>(p, wg, smem);
+  }
+  if constexpr (PH == kPhGemm2) phase_experts<false>(p, wg, smem);
+  if constexpr (PH == kPhCombine) phase_combine(p, wg, smem);
+  if constexpr (PH == kPhUnpool) phase_unpool(p, wg, smem);
+}
+
+__device__ __forceinline__ KP& kernel_params() {
+  return *(KP*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+__global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
+  KP& p = kernel_params();
   __shared__ int s_abort;
   const int wg = blockIdx.x;
+  stamp(p, kNumPhases);  // entry
   if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
   __syncthreads();
   const bool run = s_abort == 0;
@@ -29,48 +54,45 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p) {
     bar += (unsigned)p.nwg;
     grid_barrier(p, bar);
   };
-  if (run) phase_norm1(p, wg);
+  if (run) fused_phase<kPhNorm1, D>(p, wg);
   stamp(p, kPhNorm1);
   sync();
-  if (run) phase_qkv(p, wg, smem);
+  if (run) fused_phase<kPhQkv, D>(p, wg);
   stamp(p, kPhQkv);
   sync();
-  if (run) phase_attn<D>(p, wg, smem);
+  if (run) fused_phase<kPhAttn, D>(p, wg);
   stamp(p, kPhAttn);
   sync();
-  if (run) phase_attn_merge(p, wg);
+  if (run) fused_phase<kPhAttnMerge, D>(p, wg);
   stamp(p, kPhAttnMerge);
   sync();
-  if (run) phase_oproj(p, wg, smem);
+  if (run) fused_phase<kPhOproj, D>(p, wg);
   stamp(p, kPhOproj);
   sync();
-  if (run) phase_router_pool(p, wg, smem);
+  if (run) fused_phase<kPhRouterPool, D>(p, wg);
   stamp(p, kPhRouterPool);
   sync();
-  if (run) {
-    compute_routing(p, route_tables(smem), wg == 0);
-    phase_experts<true>(p, wg, smem);
-  }
+  if (run) fused_phase<kPhGemm1, D>(p, wg);
   stamp(p, kPhGemm1);
   sync();
-  if (run) phase_experts<false>(p, wg, smem);
+  if (run) fused_phase<kPhGemm2, D>(p, wg);
   stamp(p, kPhGemm2);
   sync();
-  if (run) phase_combine(p, wg, smem);
+  if (run) fused_phase<kPhCombine, D>(p, wg);
   stamp(p, kPhCombine);
   sync();
-  if (run) phase_unpool(p, wg, smem);
+  if (run) fused_phase<kPhUnpool, D>(p, wg);
   stamp(p, kPhUnpool);
   // leave: the last workgroup out resets the barrier words for the next launch
   __syncthreads();
   if (threadIdx.x == 0) {
     if (!run && wg == 0)
-      __hip_atomic_store(p.ctrl + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gl(p.ctrl) + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned prev =
-        __hip_atomic_fetch_add(p.ctrl + kExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(gl(p.ctrl) + kExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == (unsigned)p.nwg - 1) {
-      __hip_atomic_store(p.ctrl + kBar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(p.ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gl(p.ctrl) + kBar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gl(p.ctrl) + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -79,15 +101,16 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p) {
 // device: one kernel per step (ablation / fallback chain)
 // =========================================================================================
 template <int PH, int D>
-__global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+__global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
+  KP& p = kernel_params();
+  char* smem = moel_lds;
   __shared__ int s_abort;
   const int wg = blockIdx.x;
   if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
   __syncthreads();
   if (s_abort) {
     if (wg == 0 && threadIdx.x == 0)
-      __hip_atomic_store(p.ctrl + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(gl(p.ctrl) + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
   if constexpr (PH == kPhNorm1) phase_norm1(p, wg);

@@ -78,4 +78,10 @@ struct LayerParams {
   unsigned long long* dbg_ts;
 };
 
+// The launch parameters as seen by device code: a reference into the kernel-argument segment
+// (constant address space), so every field read is a scalar load through the constant cache.
+#if defined(__HIP_DEVICE_COMPILE__) || defined(__HIPCC__)
+typedef const __attribute__((address_space(4))) LayerParams KP;
+#endif
+
 }  // namespace moel

@@ -20,6 +20,9 @@
 #pragma once
 #include "moel_device.h"
 
+// Dynamic LDS of every layer kernel (sized at launch).
+extern __shared__ __attribute__((aligned(16))) char moel_lds[];
+
 namespace moel {
 
 // ------------------------------------------------------------------------------------------
@@ -36,6 +39,7 @@ struct RouteTables {
   int cnt[512];                // per-expert slot count
   int off[512];                // per-expert first position in `slots`
   int rank[512];               // per-expert index into active_e (valid when cnt > 0)
+  unsigned tokmask[kMaxT * 16];  // per token: bitmask of its selected experts (E <= 512)
 };
 constexpr int kRouteBytes = (sizeof(RouteTables) + 255) & ~255;
 
@@ -56,19 +60,19 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, u32x4& 
 // RMSNorm statistics
 // ------------------------------------------------------------------------------------------
 // Partial sums of x^2 over this workgroup's slice of the hidden dimension, per token.
-__device__ void phase_norm1(const LayerParams& p, int wg) {
+__device__ void phase_norm1(KP& p, int wg) {
   const int tid = threadIdx.x;
   const int t = tid >> 5, sub = tid & 31;  // 16 tokens x 32 lanes
   const int k0 = (int)((long)wg * p.H / p.nwg), k1 = (int)((long)(wg + 1) * p.H / p.nwg);
   float s = 0.f;
   if (t < p.T)
     for (int k = k0 + sub; k < k1; k += 32) {
-      float v = p.x[(size_t)t * p.H + k];
+      float v = gl(p.x)[(size_t)t * p.H + k];
       s = fmaf(v, v, s);
     }
 #pragma unroll
   for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-  if (sub == 0) p.ss1[wg * kMaxT + t] = s;
+  if (sub == 0) gl(p.ss1)[wg * kMaxT + t] = s;
 }
 
 // rstd of every token from the per-workgroup partial sums, in a fixed summation order
@@ -77,7 +81,7 @@ __device__ void phase_norm1(const LayerParams& p, int wg) {
 __device__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp, float* out) {
   const int t = threadIdx.x & 15, q = threadIdx.x >> 4;  // q = 0..31
   float s = 0.f;
-  for (int w = q; w < nwg; w += 32) s += ss[w * kMaxT + t];
+  for (int w = q; w < nwg; w += 32) s += gl(ss)[w * kMaxT + t];
   tmp[q * kMaxT + t] = s;
   lds_barrier();
   if (threadIdx.x < kMaxT) {
@@ -98,22 +102,31 @@ struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
   const uint16_t* gamma;
   float rstd;  // of this lane's token
   int T;
-  __device__ __forceinline__ void load2(int tok, int k, u32x4& hi, u32x4& lo) const {
+  struct Raw {
+    float4 a, b;
+    u32x4 g;
+  };
+  __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
+    if (tok < T) {
+      const float* src = v + (size_t)tok * ld + k;
+      r.a = ldgf4(src);
+      r.b = ldgf4(src + 4);
+      r.g = ldg16(gamma + k);
+    }
+  }
+  __device__ __forceinline__ void finish(int tok, int k, const Raw& r, u32x4& hi, u32x4& lo) const {
     hi = u32x4{0u, 0u, 0u, 0u};
     lo = u32x4{0u, 0u, 0u, 0u};
     if (tok < T) {
-      const float* src = v + (size_t)tok * ld + k;
-      float4 a = *reinterpret_cast<const float4*>(src);
-      float4 b = *reinterpret_cast<const float4*>(src + 4);
-      const u32x4 g = ldg16(gamma + k);
-      a.x = a.x * rstd * bf_lo(g[0]);
-      a.y = a.y * rstd * bf_hi(g[0]);
-      a.z = a.z * rstd * bf_lo(g[1]);
-      a.w = a.w * rstd * bf_hi(g[1]);
-      b.x = b.x * rstd * bf_lo(g[2]);
-      b.y = b.y * rstd * bf_hi(g[2]);
-      b.z = b.z * rstd * bf_lo(g[3]);
-      b.w = b.w * rstd * bf_hi(g[3]);
+      float4 a = r.a, b = r.b;
+      a.x = a.x * rstd * bf_lo(r.g[0]);
+      a.y = a.y * rstd * bf_hi(r.g[0]);
+      a.z = a.z * rstd * bf_lo(r.g[1]);
+      a.w = a.w * rstd * bf_hi(r.g[1]);
+      b.x = b.x * rstd * bf_lo(r.g[2]);
+      b.y = b.y * rstd * bf_hi(r.g[2]);
+      b.z = b.z * rstd * bf_lo(r.g[3]);
+      b.w = b.w * rstd * bf_hi(r.g[3]);
       split8(a, b, hi, lo);
     }
   }
@@ -122,13 +135,20 @@ struct AF32 {  // a stored fp32 row
   const float* v;
   int ld;
   int T;
-  __device__ __forceinline__ void load2(int tok, int k, u32x4& hi, u32x4& lo) const {
-    hi = u32x4{0u, 0u, 0u, 0u};
-    lo = u32x4{0u, 0u, 0u, 0u};
+  struct Raw {
+    float4 a, b;
+  };
+  __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
     if (tok < T) {
       const float* src = v + (size_t)tok * ld + k;
-      split8(*reinterpret_cast<const float4*>(src), *reinterpret_cast<const float4*>(src + 4), hi, lo);
+      r.a = ldgf4(src);
+      r.b = ldgf4(src + 4);
     }
+  }
+  __device__ __forceinline__ void finish(int tok, int k, const Raw& r, u32x4& hi, u32x4& lo) const {
+    hi = u32x4{0u, 0u, 0u, 0u};
+    lo = u32x4{0u, 0u, 0u, 0u};
+    if (tok < T) split8(r.a, r.b, hi, lo);
   }
 };
 
@@ -144,17 +164,26 @@ struct DenseLds {
   float aux[4 * 16 * kMaxT];    // 4 KiB (epilogue scratch)
 };
 
+// Largest divisor of n that is <= 8: the number of waves that split a reduction of n units
+// so that every one of them gets the same count.
+__device__ __forceinline__ int kwaves_for(int n) {
+  int w = n < kWaves ? n : kWaves;
+  while (n % w) --w;
+  return w;
+}
+
 template <class ASrc>
 __device__ void dense_pass(const uint8_t* w0, int tiles0, const uint8_t* w1, int K, int t_first,
                            int ntiles, int oct_lo, int oct_hi, const ASrc& A, DenseLds& L) {
+  constexpr int DEPTH = 4;  // k steps in flight per wave
   const int lane = lane_id(), wv = wave_id();
   const int S = K >> 5;
-  const int nkw = S < kWaves ? S : kWaves;
+  const int nkw = kwaves_for(S);
   f32x4 acc[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wv < nkw) {
-    const int sa = wv * S / nkw, sb = (wv + 1) * S / nkw;
+    const int ns = S / nkw, sa = wv * ns;
     const int tok = lane & 15, kq = 8 * (lane >> 4);
     const uint8_t* base[4];
     bool on[4];
@@ -166,32 +195,33 @@ __device__ void dense_pass(const uint8_t* w0, int tiles0, const uint8_t* w1, int
       base[j] = (t < tiles0 ? w0 + (size_t)t * S * 1024 : w1 + (size_t)(t - tiles0) * S * 1024) +
                 lane * 16;
     }
-    // two-stage software pipeline over k steps
-    u32x4 a_hi, a_lo, w_cur[4];
-    A.load2(tok, 32 * sa + kq, a_hi, a_lo);
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      w_cur[j] = on[j] ? ldg_stream(base[j] + (size_t)sa * 1024) : u32x4{0u, 0u, 0u, 0u};
-    for (int s = sa; s < sb; ++s) {
-      u32x4 n_hi = {0u, 0u, 0u, 0u}, n_lo = {0u, 0u, 0u, 0u}, w_nxt[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) w_nxt[j] = u32x4{0u, 0u, 0u, 0u};
-      if (s + 1 < sb) {
-        A.load2(tok, 32 * (s + 1) + kq, n_hi, n_lo);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (on[j]) w_nxt[j] = ldg_stream(base[j] + (size_t)(s + 1) * 1024);
-      }
+    typename ASrc::Raw ra[DEPTH];
+    u32x4 rw[DEPTH][4];
+    auto issue = [&](typename ASrc::Raw& a, u32x4 (&w)[4], int s) {
+      A.fetch(tok, 32 * s + kq, a);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < ntiles) {
-          acc[j] = mfma16x16x32(a_hi, w_cur[j], acc[j]);
-          acc[j] = mfma16x16x32(a_lo, w_cur[j], acc[j]);
-        }
-      a_hi = n_hi;
-      a_lo = n_lo;
+        w[j] = on[j] ? ldg_stream(base[j] + (size_t)s * 1024) : u32x4{0u, 0u, 0u, 0u};
+    };
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w_cur[j] = w_nxt[j];
+    for (int d = 0; d < DEPTH; ++d)
+      if (d < ns) issue(ra[d], rw[d], sa + d);
+    for (int i0 = 0; i0 < ns; i0 += DEPTH) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const int i = i0 + d;
+        if (i < ns) {
+          u32x4 a_hi, a_lo;
+          A.finish(tok, 32 * (sa + i) + kq, ra[d], a_hi, a_lo);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (j < ntiles) {
+              acc[j] = mfma16x16x32(a_hi, rw[d][j], acc[j]);
+              acc[j] = mfma16x16x32(a_lo, rw[d][j], acc[j]);
+            }
+          if (i + DEPTH < ns) issue(ra[d], rw[d], sa + i + DEPTH);
+        }
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) L.red[(wv * 4 + j) * 64 + lane] = acc[j];
@@ -244,7 +274,7 @@ __device__ __forceinline__ bool octet_in(int row, int lo, int hi) {
 // rotation partners (i, i + D/2) of every head interleaved: packed row 2i <-> canonical i,
 // packed row 2i+1 <-> canonical i + D/2.  The cache stores bf16 (nearest); q stays fp32.
 // ------------------------------------------------------------------------------------------
-__device__ void phase_qkv(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_qkv(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   const float rs = wg_rstd(p.ss1, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
   ANorm A{p.x, p.H, p.gamma1, rs, p.T};
@@ -261,20 +291,20 @@ __device__ void phase_qkv(const LayerParams& p, int wg, char* smem) {
                   const int head = R / p.D, i = (R % p.D) >> 1;
                   const int ps = p.pos + t;
                   if (head < p.Hq + p.Hkv) {
-                    const float c = p.rope_cos[(size_t)ps * half + i];
-                    const float s = p.rope_sin[(size_t)ps * half + i];
+                    const float c = gl(p.rope_cos)[(size_t)ps * half + i];
+                    const float s = gl(p.rope_sin)[(size_t)ps * half + i];
                     const float ra = a * c - b * s, rb = b * c + a * s;
                     if (head < p.Hq) {
-                      float* q = p.q_buf + (size_t)t * p.Hq * p.D + head * p.D;
+                      auto q = gl(p.q_buf + (size_t)t * p.Hq * p.D + head * p.D);
                       q[i] = ra;
                       q[i + half] = rb;
                     } else {
-                      uint16_t* k = p.k_cache + ((size_t)(head - p.Hq) * p.kv_cap + ps) * p.D;
+                      auto k = gl(p.k_cache + ((size_t)(head - p.Hq) * p.kv_cap + ps) * p.D);
                       k[i] = f2bf(ra);
                       k[i + half] = f2bf(rb);
                     }
                   } else {
-                    uint16_t* v = p.v_cache + ((size_t)(head - p.Hq - p.Hkv) * p.kv_cap + ps) * p.D;
+                    auto v = gl(p.v_cache + ((size_t)(head - p.Hq - p.Hkv) * p.kv_cap + ps) * p.D);
                     v[i] = f2bf(a);
                     v[i + half] = f2bf(b);
                   }
@@ -296,7 +326,7 @@ struct AttnLds {
 };
 
 template <int D>
-__device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_attn(KP& p, int wg, char* smem) {
   AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(phase_smem(smem));
   constexpr int KS = AttnLds<D>::KS, VS = AttnLds<D>::VS;
   constexpr int NS = D / 32;   // MFMA k-steps over the head dim
@@ -321,7 +351,7 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
       ql[s] = u32x4{0u, 0u, 0u, 0u};
       if (act && tq < p.T) {
         const float* qs = p.q_buf + (size_t)tq * p.Hq * D + h * D + 32 * s + 8 * gq;
-        split8(*reinterpret_cast<const float4*>(qs), *reinterpret_cast<const float4*>(qs + 4), qh[s], ql[s]);
+        split8(ldgf4(qs), ldgf4(qs + 4), qh[s], ql[s]);
       }
     }
     float m_run = NEG, l_run = 0.f;
@@ -424,13 +454,13 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
       }
     }
     if (act) {
-      float* op = p.attn_o + ((size_t)(it * grp + wv) * kMaxT) * D;
+      auto op = gl(p.attn_o + ((size_t)(it * grp + wv) * kMaxT) * D);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int r = 0; r < 4; ++r) op[(4 * gq + r) * D + 16 * d + tq] = O[d][r];
       if (lane < 16) {
-        float* ml = p.attn_ml + ((size_t)(it * grp + wv) * kMaxT + lane) * 2;
+        auto ml = gl(p.attn_ml + ((size_t)(it * grp + wv) * kMaxT + lane) * 2);
         ml[0] = m_run;
         ml[1] = l_run;
       }
@@ -439,7 +469,7 @@ __device__ void phase_attn(const LayerParams& p, int wg, char* smem) {
 }
 
 // Merge the key-chunk partials of every (token, q head) row -> o (fp32).
-__device__ void phase_attn_merge(const LayerParams& p, int wg) {
+__device__ void phase_attn_merge(KP& p, int wg) {
   const int grp = p.Hq / p.Hkv;
   const int total = p.T * p.Hq * p.D;
   for (int e = wg * kThreads + threadIdx.x; e < total; e += p.nwg * kThreads) {
@@ -448,25 +478,25 @@ __device__ void phase_attn_merge(const LayerParams& p, int wg) {
     float M = -__builtin_inff();
     for (int c = 0; c < p.attn_nchunks; ++c) {
       const int it = c * p.Hkv + g;
-      M = fmaxf(M, p.attn_ml[((size_t)(it * grp + w) * kMaxT + t) * 2]);
+      M = fmaxf(M, gl(p.attn_ml)[((size_t)(it * grp + w) * kMaxT + t) * 2]);
     }
     float num = 0.f, den = 0.f;
     for (int c = 0; c < p.attn_nchunks; ++c) {
       const int it = c * p.Hkv + g;
-      const float* ml = p.attn_ml + ((size_t)(it * grp + w) * kMaxT + t) * 2;
+      auto ml = gl(p.attn_ml + ((size_t)(it * grp + w) * kMaxT + t) * 2);
       if (ml[0] == -__builtin_inff()) continue;
       const float wgt = __expf(ml[0] - M);
-      num += wgt * p.attn_o[((size_t)(it * grp + w) * kMaxT + t) * p.D + d];
+      num += wgt * gl(p.attn_o)[((size_t)(it * grp + w) * kMaxT + t) * p.D + d];
       den += wgt * ml[1];
     }
-    p.o_buf[(size_t)t * p.Hq * p.D + h * p.D + d] = num / den;
+    gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = num / den;
   }
 }
 
 // ------------------------------------------------------------------------------------------
 // o-projection + residual -> h (fp32), and per-workgroup partial sums of h^2.
 // ------------------------------------------------------------------------------------------
-__device__ void phase_oproj(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_oproj(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AF32 A{p.o_buf, p.Hq * p.D, p.T};
   float part = 0.f;  // thread t < 16 accumulates token t over the workgroup's rows
@@ -477,8 +507,8 @@ __device__ void phase_oproj(const LayerParams& p, int wg, char* smem) {
                   const int n = (tf + j) * 16 + r;
                   float hv = 0.f;
                   if (t < p.T && octet_in(n, lo, hi)) {
-                    hv = p.x[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
-                    p.h_buf[(size_t)t * p.H + n] = hv;
+                    hv = gl(p.x)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
+                    gl(p.h_buf)[(size_t)t * p.H + n] = hv;
                   }
                   L.aux[(j * 16 + r) * kMaxT + t] = hv;
                 }
@@ -490,14 +520,14 @@ __device__ void phase_oproj(const LayerParams& p, int wg, char* smem) {
                       part = fmaf(hv, hv, part);
                     }
               });
-  if (threadIdx.x < kMaxT) p.ss2[wg * kMaxT + threadIdx.x] = part;
+  if (threadIdx.x < kMaxT) gl(p.ss2)[wg * kMaxT + threadIdx.x] = part;
 }
 
 // ------------------------------------------------------------------------------------------
 // Router logits and pooler from hn = h * rstd2 * gamma2, one contraction over the stacked
 // rows [router; pooler].
 // ------------------------------------------------------------------------------------------
-__device__ void phase_router_pool(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_router_pool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   const float rs = wg_rstd(p.ss2, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
   ANorm A{p.h_buf, p.H, p.gamma2, rs, p.T};
@@ -510,10 +540,10 @@ __device__ void phase_router_pool(const LayerParams& p, int wg, char* smem) {
                   if (t >= p.T || !octet_in(n, lo, hi)) continue;
                   const float v = L.fin[(j * 16 + r) * kMaxT + t];
                   if (n < p.E) {
-                    p.logits[t * p.E + n] = v;
-                    if (p.dbg_logits) p.dbg_logits[t * p.E + n] = v;
+                    gl(p.logits)[t * p.E + n] = v;
+                    if (p.dbg_logits) gl(p.dbg_logits)[t * p.E + n] = v;
                   } else {
-                    p.pl[(size_t)t * p.P + (n - p.E)] = v;
+                    gl(p.pl)[(size_t)t * p.P + (n - p.E)] = v;
                   }
                 }
               });
@@ -524,7 +554,7 @@ __device__ void phase_router_pool(const LayerParams& p, int wg, char* smem) {
 // softmax over the selected logits, and per-expert slot lists.  Computed redundantly by
 // every workgroup from the same logits, so all agree bit for bit.
 // ------------------------------------------------------------------------------------------
-__device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write_debug) {
+__device__ void compute_routing(KP& p, RouteTables& R, bool write_debug) {
   const int lane = lane_id(), wv = wave_id();
   const int nslot = p.T * p.topk;
   const float NEG = -__builtin_inff();
@@ -534,7 +564,7 @@ __device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int e = lane + 64 * j;
-      v[j] = e < p.E ? p.logits[t * p.E + e] : NEG;
+      v[j] = e < p.E ? gl(p.logits)[t * p.E + e] : NEG;
       taken[j] = e >= p.E;
     }
     float sel0 = 0.f, esum = 0.f;
@@ -573,11 +603,15 @@ __device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write
       for (int r = 0; r < p.topk; ++r) R.gate[t * p.topk + r] /= esum;
   }
   lds_barrier();
-  // per-expert counts and the slot lists
-  for (int e = threadIdx.x; e < p.E; e += kThreads) {
-    int c = 0;
-    for (int s = 0; s < nslot; ++s) c += (R.idx[s] == e);
-    R.cnt[e] = c;
+  // per-expert counts (LDS integer atomics: exact and order-independent) and, per token, a
+  // bitmask of its selected experts
+  for (int e = threadIdx.x; e < p.E; e += kThreads) R.cnt[e] = 0;
+  for (int w = threadIdx.x; w < kMaxT * 16; w += kThreads) R.tokmask[w] = 0u;
+  lds_barrier();
+  for (int s = threadIdx.x; s < nslot; s += kThreads) {
+    const int e = R.idx[s], t = s / p.topk;
+    atomicAdd(&R.cnt[e], 1);
+    atomicOr(&R.tokmask[t * 16 + (e >> 5)], 1u << (e & 31));
   }
   lds_barrier();
   if (wv == 0) {
@@ -602,6 +636,10 @@ __device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write
     for (int e = e0; e < e0 + per && e < p.E; ++e) {
       R.off[e] = oc;
       R.rank[e] = oa;
+      if (R.cnt[e] > 0) {
+        R.active_e[oa] = e;
+        R.active_off[oa] = oc;
+      }
       oc += R.cnt[e];
       oa += R.cnt[e] > 0;
     }
@@ -611,19 +649,17 @@ __device__ void compute_routing(const LayerParams& p, RouteTables& R, bool write
     }
   }
   lds_barrier();
-  for (int e = threadIdx.x; e < p.E; e += kThreads) {
-    if (R.cnt[e] == 0) continue;
-    const int u = R.rank[e];
-    R.active_e[u] = e;
-    R.active_off[u] = R.off[e];
-    int j = R.off[e];
-    for (int s = 0; s < nslot; ++s)
-      if (R.idx[s] == e) R.slots[j++] = s;
+  // slot s = (t, kappa) of expert e goes after the slots of e from tokens t' < t
+  for (int s = threadIdx.x; s < nslot; s += kThreads) {
+    const int e = R.idx[s], t = s / p.topk;
+    int r = 0;
+    for (int t2 = 0; t2 < t; ++t2) r += (R.tokmask[t2 * 16 + (e >> 5)] >> (e & 31)) & 1u;
+    R.slots[R.off[e] + r] = s;
   }
   if (write_debug) {
     for (int s = threadIdx.x; s < nslot; s += kThreads) {
-      if (p.dbg_idx) p.dbg_idx[s] = R.idx[s];
-      if (p.dbg_gates) p.dbg_gates[s] = R.gate[s];
+      if (p.dbg_idx) gl(p.dbg_idx)[s] = R.idx[s];
+      if (p.dbg_gates) gl(p.dbg_gates)[s] = R.gate[s];
     }
   }
   lds_barrier();
@@ -656,14 +692,14 @@ __device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* 
     const uint8_t* b = wt[m] + (size_t)pr * 2304;
     f.c[m][0] = ldg_stream(b + lane * 16);
     f.c[m][1] = ldg_stream(b + 1024 + lane * 16);
-    f.sc[m] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(b + 2048) + lane);
+    f.sc[m] = ldg_stream32(b + 2048 + 4 * lane);
   }
   const bool lo_row = (lane & 2) != 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     f.a[g] = u32x2{0u, 0u};
     if (arow[g] != nullptr) {
-      const float4 v = *reinterpret_cast<const float4*>(arow[g] + k0 + 4 * (lane >> 2));
+      const float4 v = ldgf4(arow[g] + k0 + 4 * (lane >> 2));
       const u32x2 s01 = split_bf16(v.x, v.y), s23 = split_bf16(v.z, v.w);
       f.a[g] = lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
     }
@@ -706,17 +742,22 @@ __device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 
 // One expert's run of 64-row tiles [ta, tb) for this workgroup.
 //   GATEUP: NM = 2, activation = pl rows of the expert's tokens, out a = silu(g) * u
 //   else  : NM = 1, activation = a rows of the expert's slots,   out d
+// Each k-wave streams its pairs of every tile through a ring of DEPTH register buffers, so
+// DEPTH pairs (NM = 2: 4.6 KB each) stay in flight per wave across tile boundaries.
 template <bool GATEUP, int G>
-__device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int u, int ta, int tb,
+__device__ void fp4_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
                                  Fp4Lds& L) {
   constexpr int NM = GATEUP ? 2 : 1;
+  // register budget: deeper rings for the common 1-2 token experts
+  constexpr int DEPTH = G == 1 ? (NM == 2 ? 4 : 8) : G == 2 ? 4 : G == 4 ? 2 : 1;
   const int lane = lane_id(), wv = wave_id();
   const int e = R.active_e[u];
   const int s_lo = R.active_off[u], n_e = R.active_off[u + 1] - s_lo;
   const int K = GATEUP ? p.P : p.I;
   const int Sp = K >> 6;  // 64-k pairs (K % 128 == 0)
-  const int nkw = Sp < kWaves ? Sp : kWaves;
-  const int pa = wv * Sp / nkw, pb = (wv + 1) * Sp / nkw;
+  const int nkw = kwaves_for(Sp);
+  const int npt = Sp / nkw;  // pairs per tile, equal for every k-wave
+  const int pa = wv * npt;
   const bool kw = wv < nkw;
   const size_t tile_bytes = (size_t)36 * K;  // 64 rows of K/2 + K/16 bytes
   const uint8_t* wb[NM];
@@ -737,60 +778,71 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
       arow[g] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
     }
   }
-  const int npt = pb - pa;  // pairs per tile for this wave
-  const int total = kw ? (tb - ta) * npt : 0;
-  Fp4Pair<NM, G> cur, nxt;
-  auto issue = [&](Fp4Pair<NM, G>& f, int n) {
-    const int ti = ta + n / npt, pr = pa + n % npt;
+  const int total = (tb - ta) * npt;  // same for every wave (idle waves only join barriers)
+  Fp4Pair<NM, G> ring[DEPTH];
+  auto issue = [&](Fp4Pair<NM, G>& f, int i) {
+    const int ti = ta + i / npt, pr = pa + i % npt;
     const uint8_t* wt[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes;
     fp4_pair_load<NM, G>(f, wt, pr, arow, 64 * pr);
   };
-  if (total > 0) issue(cur, 0);
-  int n = 0;
-  for (int ti = ta; ti < tb; ++ti) {
-    f32x4 acc[NM][G];
+  if (kw) {
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
+    for (int d = 0; d < DEPTH; ++d)
+      if (d < total) issue(ring[d], d);
+  }
+  f32x4 acc[NM][G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (kw) {
-      for (int q = 0; q < npt; ++q, ++n) {
-        if (n + 1 < total) issue(nxt, n + 1);
-        fp4_pair_compute<NM, G>(cur, acc);
-        cur = nxt;
-      }
-      // rows (hi, hi', lo, lo') -> token slots 2g, 2g+1
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
-      for (int m = 0; m < NM; ++m)
+    for (int g = 0; g < G; ++g) acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i0 = 0; i0 < total; i0 += DEPTH) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g] = acc[m][g][0] + acc[m][g][2];
-          L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g + 1] = acc[m][g][1] + acc[m][g][3];
+    for (int d = 0; d < DEPTH; ++d) {
+      const int i = i0 + d;
+      if (i < total) {
+        if (kw) {
+          fp4_pair_compute<NM, G>(ring[d], acc);
+          if (i + DEPTH < total) issue(ring[d], i + DEPTH);
         }
-    }
-    lds_barrier();
-    // reduce over the k-waves in order; lane row = ti*64 + ln
-    for (int x = threadIdx.x; x < 64 * n_e; x += kThreads) {
-      const int ln = x & 63, j = x >> 6;
-      const int slot = R.slots[s_lo + j];
-      if (GATEUP) {
-        float gs = 0.f, us = 0.f;
-        for (int w = 0; w < nkw; ++w) {
-          gs += L.red[(w * 64 + ln) * 32 + j];
-          us += L.red[(w * 64 + ln) * 32 + 16 + j];
+        if ((i + 1) % npt == 0) {  // the tile is complete on every k-wave
+          const int ti = ta + i / npt;
+          if (kw) {
+            // rows (hi, hi', lo, lo') -> token slots 2g, 2g+1
+#pragma unroll
+            for (int m = 0; m < NM; ++m)
+#pragma unroll
+              for (int g = 0; g < G; ++g) {
+                L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g] = acc[m][g][0] + acc[m][g][2];
+                L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g + 1] = acc[m][g][1] + acc[m][g][3];
+                acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+              }
+          }
+          lds_barrier();
+          // reduce over the k-waves in order; lane row = ti*64 + ln
+          for (int x = threadIdx.x; x < 64 * n_e; x += kThreads) {
+            const int ln = x & 63, j = x >> 6;
+            const int slot = R.slots[s_lo + j];
+            if (GATEUP) {
+              float gs = 0.f, us = 0.f;
+              for (int w = 0; w < nkw; ++w) {
+                gs += L.red[(w * 64 + ln) * 32 + j];
+                us += L.red[(w * 64 + ln) * 32 + 16 + j];
+              }
+              gs *= gl(p.ts_gate)[e];
+              us *= gl(p.ts_up)[e];
+              gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + ti * 64 + ln] = gs / (1.0f + __expf(-gs)) * us;
+            } else {
+              float ds = 0.f;
+              for (int w = 0; w < nkw; ++w) ds += L.red[(w * 64 + ln) * 32 + j];
+              gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + ti * 64 + ln] = ds * gl(p.ts_down)[e];
+            }
+          }
+          lds_barrier();
         }
-        gs *= p.ts_gate[e];
-        us *= p.ts_up[e];
-        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 64 + ln] = gs / (1.0f + __expf(-gs)) * us;
-      } else {
-        float ds = 0.f;
-        for (int w = 0; w < nkw; ++w) ds += L.red[(w * 64 + ln) * 32 + j];
-        p.d_buf[(size_t)slot * p.P + p.rank * p.P_loc + ti * 64 + ln] = ds * p.ts_down[e];
       }
     }
-    lds_barrier();
   }
 }
 
@@ -799,7 +851,7 @@ __device__ void fp4_expert_tiles(const LayerParams& p, const RouteTables& R, int
 // second row tile takes slots 8..15.
 // ------------------------------------------------------------------------------------------
 template <bool GATEUP>
-__device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, int u, int ta, int tb,
+__device__ void bf16_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
                                   DenseLds& L) {
   constexpr int NM = GATEUP ? 2 : 1;
   const int lane = lane_id(), wv = wave_id();
@@ -833,7 +885,7 @@ __device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, in
     u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
     if (arow[rt] != nullptr) {
       const float* src = arow[rt] + 32 * s + kq;
-      split8(*reinterpret_cast<const float4*>(src), *reinterpret_cast<const float4*>(src + 4), hi, lo);
+      split8(ldgf4(src), ldgf4(src + 4), hi, lo);
     }
     return lo_row ? lo : hi;
   };
@@ -879,17 +931,25 @@ __device__ void bf16_expert_tiles(const LayerParams& p, const RouteTables& R, in
           s1 += L.red[(w * 4 + rt * 2 + 1) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + 1) * 64 + l_lo][c];
       }
       if (GATEUP)
-        p.a_buf[(size_t)slot * p.I + p.rank * p.I_loc + ti * 16 + r] = s0 / (1.0f + __expf(-s0)) * s1;
+        gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + ti * 16 + r] = s0 / (1.0f + __expf(-s0)) * s1;
       else
-        p.d_buf[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = s0;
+        gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = s0;
     }
     lds_barrier();
   }
 }
 
+// One non-inlined function per (GATEUP, G): each gets its own register allocation, so the
+// rare many-token instantiations cannot push the common 1-2 token path into spills.
+template <bool GATEUP, int G>
+__device__ __noinline__ void fp4_expert_run(KP& p, int u, int ta, int tb) {
+  fp4_expert_tiles<GATEUP, G>(p, route_tables(moel_lds), u, ta, tb,
+                              *reinterpret_cast<Fp4Lds*>(phase_smem(moel_lds)));
+}
+
 // Expert GEMM phase: the flattened list (active expert u, tile) split evenly over workgroups.
 template <bool GATEUP>
-__device__ void phase_experts(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_experts(KP& p, int wg, char* smem) {
   RouteTables& R = route_tables(smem);
   const int rows = GATEUP ? p.I_loc : p.P_loc;
   const bool fp4 = p.expert_dtype == 0;
@@ -903,12 +963,11 @@ __device__ void phase_experts(const LayerParams& p, int wg, char* smem) {
     int tb = tpe;
     if ((u + 1) * tpe > t1) tb = t1 - u * tpe;
     if (fp4) {
-      Fp4Lds& L = *reinterpret_cast<Fp4Lds*>(phase_smem(smem));
       const int n_e = R.active_off[u + 1] - R.active_off[u];
-      if (n_e <= 2) fp4_expert_tiles<GATEUP, 1>(p, R, u, ta, tb, L);
-      else if (n_e <= 4) fp4_expert_tiles<GATEUP, 2>(p, R, u, ta, tb, L);
-      else if (n_e <= 8) fp4_expert_tiles<GATEUP, 4>(p, R, u, ta, tb, L);
-      else fp4_expert_tiles<GATEUP, 8>(p, R, u, ta, tb, L);
+      if (n_e <= 2) fp4_expert_run<GATEUP, 1>(p, u, ta, tb);
+      else if (n_e <= 4) fp4_expert_run<GATEUP, 2>(p, u, ta, tb);
+      else if (n_e <= 8) fp4_expert_run<GATEUP, 4>(p, u, ta, tb);
+      else fp4_expert_run<GATEUP, 8>(p, u, ta, tb);
     } else {
       DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
       bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
@@ -918,20 +977,20 @@ __device__ void phase_experts(const LayerParams& p, int wg, char* smem) {
 }
 
 // m[t] = sum over the token's slots, in selection order, of gate * d
-__device__ void phase_combine(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_combine(KP& p, int wg, char* smem) {
   const RouteTables& R = route_tables(smem);
   const int total = p.T * p.P_loc;
   for (int x = wg * kThreads + threadIdx.x; x < total; x += p.nwg * kThreads) {
     const int t = x / p.P_loc, pc = p.rank * p.P_loc + x % p.P_loc;
     float s = 0.f;
     for (int k = 0; k < p.topk; ++k)
-      s = fmaf(R.gate[t * p.topk + k], p.d_buf[(size_t)(t * p.topk + k) * p.P + pc], s);
-    p.m_buf[(size_t)t * p.P + pc] = s;
+      s = fmaf(R.gate[t * p.topk + k], gl(p.d_buf)[(size_t)(t * p.topk + k) * p.P + pc], s);
+    gl(p.m_buf)[(size_t)t * p.P + pc] = s;
   }
 }
 
 // y = h + m W_unpool^T
-__device__ void phase_unpool(const LayerParams& p, int wg, char* smem) {
+__device__ void phase_unpool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AF32 A{p.m_buf, p.P, p.T};
   dense_phase(p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, p.nwg, A, L,
@@ -940,7 +999,7 @@ __device__ void phase_unpool(const LayerParams& p, int wg, char* smem) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
                   const int n = (tf + j) * 16 + r;
                   if (t >= p.T || !octet_in(n, lo, hi)) continue;
-                  p.y[(size_t)t * p.H + n] = p.h_buf[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
+                  gl(p.y)[(size_t)t * p.H + n] = gl(p.h_buf)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
                 }
               });
 }
