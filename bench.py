@@ -90,6 +90,7 @@ def main():
     ap.add_argument("--routing", default="iid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--dump-stamps", default=None, help="write the per-workgroup timestamps (.npy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -171,17 +172,33 @@ def main():
                      "algorithmic_bytes_per_launch": int(alg_bytes),
                      "kernel": "k_layer_fused (one cooperative launch per layer)"},
     }
-    # per-phase timeline of one fused launch (workgroup timestamps, 100 MHz clock)
+    # per-phase timeline of one fused launch (workgroup timestamps, 100 MHz clock): slot i is
+    # the end of step i, slot 16 + i its start (after the preceding grid barrier)
     names = ["norm1", "qkv_rope_kv", "attention", "attn_merge", "o_proj", "router_pool", "experts_gate_up",
              "experts_down", "combine", "unpool"]
-    ts = torch.zeros((plan.workgroups, 16), dtype=torch.int64, device=dev)
+    ts = torch.zeros((plan.workgroups, binding.MOEL_N_STAMPS), dtype=torch.int64, device=dev)
     plan.layer_decode(copies[0], kc, vc, x, w.pos, window, y, dbg={"timestamps": ts}, stream=stream)
     torch.cuda.synchronize()
     tsn = ts.cpu().numpy().astype(np.float64)
+    if args.dump_stamps:
+        np.save(args.dump_stamps + "_fused.npy", ts.cpu().numpy())
+        ts.zero_()
+        plan.layer_decode(copies[1], kc, vc, x, w.pos, window, y, dbg={"timestamps": ts}, fused=False,
+                          stream=stream)
+        torch.cuda.synchronize()
+        np.save(args.dump_stamps + "_unfused.npy", ts.cpu().numpy())
+        np.save(args.dump_stamps + "_idx.npy", idx)
     t0 = tsn[:, 10].min()
     ends = [(tsn[:, i].max() - t0) / 100.0 for i in range(10)]
     result["phase_end_us"] = {n: round(e, 1) for n, e in zip(names, ends)}
     result["phase_us"] = {n: round(e - (ends[i - 1] if i else 0.0), 1) for i, (n, e) in enumerate(zip(names, ends))}
+    work = (tsn[:, :10] - tsn[:, 16:26]) / 100.0
+    result["phase_work_us"] = {n: {"median": round(float(np.median(work[:, i])), 1),
+                                   "max": round(float(work[:, i].max()), 1)} for i, n in enumerate(names)}
+    # grid barrier before step i: last arrival -> first / last departure
+    result["barrier_us"] = {names[i]: {"first_out": round((tsn[:, 16 + i].min() - tsn[:, i - 1].max()) / 100.0, 2),
+                                       "last_out": round((tsn[:, 16 + i].max() - tsn[:, i - 1].max()) / 100.0, 2)}
+                            for i in range(1, 10)}
     if not args.no_unfused:
         _, d2 = timed(False, max(5, args.steps // 2), 2)
         result["unfused_chain_us"] = {"median": round(statistics.median(d2), 2), "launches": 10}

@@ -99,10 +99,12 @@ typedef struct moel_debug {
   int32_t* expert_idx;    /* [T, k] selected experts, selection order                    */
   float* gates;           /* [T, k] softmax over the selected logits                     */
   float* router_logits;   /* [T, E] fp32                                                 */
-  uint64_t* timestamps;   /* [n_workgroups, MOEL_N_STAMPS] s_memrealtime ticks (100 MHz) */
+  uint64_t* timestamps;   /* [n_workgroups, MOEL_N_STAMPS] s_memrealtime ticks (100 MHz):
+                           * slot i < 10 end of step i, slot 10 entry, slot 16 + i start of
+                           * step i (after the grid barrier that precedes it)          */
 } moel_debug;
 
-#define MOEL_N_STAMPS 16
+#define MOEL_N_STAMPS 32
 
 typedef struct moel_plan moel_plan;
 

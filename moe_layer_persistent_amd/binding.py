@@ -24,7 +24,7 @@ MOEL_ERR_ABORTED = -6
 MOEL_ERR_UNSUPPORTED = -7
 MOEL_EXPERT_NVFP4 = 0
 MOEL_EXPERT_BF16 = 1
-MOEL_N_STAMPS = 16
+MOEL_N_STAMPS = 32
 
 
 class MoelError(RuntimeError):

@@ -22,25 +22,45 @@ constexpr int kMaxT = 16;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+// A value known to be equal on every lane, moved to a scalar register so that branches and
+// address arithmetic on it stay scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+template <class T>
+__device__ __forceinline__ T* uniform(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
+
+// The launch parameters live in the kernel-argument segment.  The segment pointer exists only
+// in the kernel itself (non-kernel functions do not receive it), so the kernel takes its
+// address and passes it down as a plain 64-bit value; callees move it back to scalar
+// registers, so every parameter read there is a scalar load.
+__device__ __forceinline__ KP& kernel_params() {
+  return *(KP*)__builtin_amdgcn_kernarg_segment_ptr();
+}
+__device__ __forceinline__ uint64_t params_handle(KP& p) { return (uint64_t)(&p); }
+__device__ __forceinline__ KP& params_from(uint64_t h) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)h);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(h >> 32));
+  return *(KP*)(((uint64_t)hi << 32) | lo);
+}
 
 // ---------------------------------------------------------------- bf16
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  // round to nearest even (inputs are finite in this path; NaN stays NaN)
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-__device__ __forceinline__ float bf2f(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
+// Round to nearest even through the hardware conversion (v_cvt_pk_bf16_f32, two values per
+// instruction, no branches).
 __device__ __forceinline__ uint32_t pack2bf(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
+__device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)(pack2bf(f, 0.f) & 0xffffu); }
+__device__ __forceinline__ float bf2f(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 // two fp32 values -> {packed bf16 (nearest), packed bf16 of the remainders}
 __device__ __forceinline__ u32x2 split_bf16(float a, float b) {
-  const uint16_t ha = f2bf(a), hb = f2bf(b);
-  return u32x2{(uint32_t)ha | ((uint32_t)hb << 16), pack2bf(a - bf2f(ha), b - bf2f(hb))};
+  const uint32_t h = pack2bf(a, b);
+  return u32x2{h, pack2bf(a - bf_lo(h), b - bf_hi(h))};
 }
 
 // ---------------------------------------------------------------- global memory access
@@ -87,6 +107,12 @@ template <int SEL>
 __device__ __forceinline__ float e4m3_to_f32(uint32_t bytes) {
   return __builtin_amdgcn_cvt_f32_fp8((int)bytes, SEL);
 }
+
+// Keeps the instruction scheduler from moving anything across this point.  Placed after the
+// loads of each ring step so that they stay spread over the loop body: left alone, the
+// scheduler sinks them all to the end of the iteration, where they are consumed right after
+// issue and the stream runs with one batch in flight at a time.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // ---------------------------------------------------------------- wave reductions
 __device__ __forceinline__ float wave_max(float v) {

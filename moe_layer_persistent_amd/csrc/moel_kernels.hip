@@ -19,7 +19,9 @@ using namespace moel;
 // Each phase of the persistent launch is a separate (non-inlined) function so that the
 // register allocator sizes each phase on its own instead of the union of all of them.
 template <int PH, int D>
-__device__ __noinline__ void fused_phase(KP& p, int wg) {
+__device__ __noinline__ void fused_phase(uint64_t ph, int wg_arg) {
+  KP& p = params_from(ph);
+  const int wg = uniform(wg_arg);
   char* smem = moel_lds;
   if constexpr (PH == kPhNorm1) phase_norm1(p, wg);
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
@@ -36,10 +38,6 @@ __device__ __noinline__ void fused_phase(KP& p, int wg) {
   if constexpr (PH == kPhUnpool) phase_unpool(p, wg, smem);
 }
 
-__device__ __forceinline__ KP& kernel_params() {
-  return *(KP*)__builtin_amdgcn_kernarg_segment_ptr();
-}
-
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
   KP& p = kernel_params();
@@ -54,34 +52,44 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
     bar += (unsigned)p.nwg;
     grid_barrier(p, bar);
   };
-  if (run) fused_phase<kPhNorm1, D>(p, wg);
+  stamp(p, 16 + kPhNorm1);
+  if (run) fused_phase<kPhNorm1, D>(params_handle(p), wg);
   stamp(p, kPhNorm1);
   sync();
-  if (run) fused_phase<kPhQkv, D>(p, wg);
+  stamp(p, 16 + kPhQkv);
+  if (run) fused_phase<kPhQkv, D>(params_handle(p), wg);
   stamp(p, kPhQkv);
   sync();
-  if (run) fused_phase<kPhAttn, D>(p, wg);
+  stamp(p, 16 + kPhAttn);
+  if (run) fused_phase<kPhAttn, D>(params_handle(p), wg);
   stamp(p, kPhAttn);
   sync();
-  if (run) fused_phase<kPhAttnMerge, D>(p, wg);
+  stamp(p, 16 + kPhAttnMerge);
+  if (run) fused_phase<kPhAttnMerge, D>(params_handle(p), wg);
   stamp(p, kPhAttnMerge);
   sync();
-  if (run) fused_phase<kPhOproj, D>(p, wg);
+  stamp(p, 16 + kPhOproj);
+  if (run) fused_phase<kPhOproj, D>(params_handle(p), wg);
   stamp(p, kPhOproj);
   sync();
-  if (run) fused_phase<kPhRouterPool, D>(p, wg);
+  stamp(p, 16 + kPhRouterPool);
+  if (run) fused_phase<kPhRouterPool, D>(params_handle(p), wg);
   stamp(p, kPhRouterPool);
   sync();
-  if (run) fused_phase<kPhGemm1, D>(p, wg);
+  stamp(p, 16 + kPhGemm1);
+  if (run) fused_phase<kPhGemm1, D>(params_handle(p), wg);
   stamp(p, kPhGemm1);
   sync();
-  if (run) fused_phase<kPhGemm2, D>(p, wg);
+  stamp(p, 16 + kPhGemm2);
+  if (run) fused_phase<kPhGemm2, D>(params_handle(p), wg);
   stamp(p, kPhGemm2);
   sync();
-  if (run) fused_phase<kPhCombine, D>(p, wg);
+  stamp(p, 16 + kPhCombine);
+  if (run) fused_phase<kPhCombine, D>(params_handle(p), wg);
   stamp(p, kPhCombine);
   sync();
-  if (run) fused_phase<kPhUnpool, D>(p, wg);
+  stamp(p, 16 + kPhUnpool);
+  if (run) fused_phase<kPhUnpool, D>(params_handle(p), wg);
   stamp(p, kPhUnpool);
   // leave: the last workgroup out resets the barrier words for the next launch
   __syncthreads();
@@ -113,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
       __hip_atomic_store(gl(p.ctrl) + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
+  stamp(p, 16 + PH);
   if constexpr (PH == kPhNorm1) phase_norm1(p, wg);
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
   if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);

@@ -3,7 +3,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#define MOEL_N_STAMPS_DEV 16
+#define MOEL_N_STAMPS_DEV 32
 #define MOEL_DEV_TIMEOUT 1u
 #define MOEL_DEV_ABORTED 2u
 

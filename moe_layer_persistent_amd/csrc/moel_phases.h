@@ -60,7 +60,7 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, u32x4& 
 // RMSNorm statistics
 // ------------------------------------------------------------------------------------------
 // Partial sums of x^2 over this workgroup's slice of the hidden dimension, per token.
-__device__ void phase_norm1(KP& p, int wg) {
+__device__ __forceinline__ void phase_norm1(KP& p, int wg) {
   const int tid = threadIdx.x;
   const int t = tid >> 5, sub = tid & 31;  // 16 tokens x 32 lanes
   const int k0 = (int)((long)wg * p.H / p.nwg), k1 = (int)((long)(wg + 1) * p.H / p.nwg);
@@ -78,7 +78,7 @@ __device__ void phase_norm1(KP& p, int wg) {
 // rstd of every token from the per-workgroup partial sums, in a fixed summation order
 // (32 interleaved subsets, then the subsets in order).  `tmp` is 32*16 floats of LDS,
 // `out` 16 floats of LDS.  Returns this lane's token's value.
-__device__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp, float* out) {
+__device__ __forceinline__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp, float* out) {
   const int t = threadIdx.x & 15, q = threadIdx.x >> 4;  // q = 0..31
   float s = 0.f;
   for (int w = q; w < nwg; w += 32) s += gl(ss)[w * kMaxT + t];
@@ -96,6 +96,8 @@ __device__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp,
 // ------------------------------------------------------------------------------------------
 // A-operand sources of the dense contractions: lane supplies A[token][k .. k+7] as hi + lo.
 // ------------------------------------------------------------------------------------------
+// Rows of tokens t >= T read the row of token T-1 (their products are computed and never
+// read), so that no load in the streaming loops depends on a branch.
 struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
   const float* v;
   int ld;
@@ -106,29 +108,25 @@ struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
     float4 a, b;
     u32x4 g;
   };
+  // the same source with its workgroup-uniform fields in scalar registers
+  __device__ __forceinline__ ANorm scalar() const { return ANorm{uniform(v), uniform(ld), uniform(gamma), rstd, uniform(T)}; }
   __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
-    if (tok < T) {
-      const float* src = v + (size_t)tok * ld + k;
-      r.a = ldgf4(src);
-      r.b = ldgf4(src + 4);
-      r.g = ldg16(gamma + k);
-    }
+    const float* src = v + (size_t)tok * ld + k;
+    r.a = ldgf4(src);
+    r.b = ldgf4(src + 4);
+    r.g = ldg16(gamma + k);
   }
-  __device__ __forceinline__ void finish(int tok, int k, const Raw& r, u32x4& hi, u32x4& lo) const {
-    hi = u32x4{0u, 0u, 0u, 0u};
-    lo = u32x4{0u, 0u, 0u, 0u};
-    if (tok < T) {
-      float4 a = r.a, b = r.b;
-      a.x = a.x * rstd * bf_lo(r.g[0]);
-      a.y = a.y * rstd * bf_hi(r.g[0]);
-      a.z = a.z * rstd * bf_lo(r.g[1]);
-      a.w = a.w * rstd * bf_hi(r.g[1]);
-      b.x = b.x * rstd * bf_lo(r.g[2]);
-      b.y = b.y * rstd * bf_hi(r.g[2]);
-      b.z = b.z * rstd * bf_lo(r.g[3]);
-      b.w = b.w * rstd * bf_hi(r.g[3]);
-      split8(a, b, hi, lo);
-    }
+  __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
+    float4 a = r.a, b = r.b;
+    a.x = a.x * rstd * bf_lo(r.g[0]);
+    a.y = a.y * rstd * bf_hi(r.g[0]);
+    a.z = a.z * rstd * bf_lo(r.g[1]);
+    a.w = a.w * rstd * bf_hi(r.g[1]);
+    b.x = b.x * rstd * bf_lo(r.g[2]);
+    b.y = b.y * rstd * bf_hi(r.g[2]);
+    b.z = b.z * rstd * bf_lo(r.g[3]);
+    b.w = b.w * rstd * bf_hi(r.g[3]);
+    split8(a, b, hi, lo);
   }
 };
 struct AF32 {  // a stored fp32 row
@@ -138,25 +136,25 @@ struct AF32 {  // a stored fp32 row
   struct Raw {
     float4 a, b;
   };
+  __device__ __forceinline__ AF32 scalar() const { return AF32{uniform(v), uniform(ld), uniform(T)}; }
   __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
-    if (tok < T) {
-      const float* src = v + (size_t)tok * ld + k;
-      r.a = ldgf4(src);
-      r.b = ldgf4(src + 4);
-    }
+    const float* src = v + (size_t)tok * ld + k;
+    r.a = ldgf4(src);
+    r.b = ldgf4(src + 4);
   }
-  __device__ __forceinline__ void finish(int tok, int k, const Raw& r, u32x4& hi, u32x4& lo) const {
-    hi = u32x4{0u, 0u, 0u, 0u};
-    lo = u32x4{0u, 0u, 0u, 0u};
-    if (tok < T) split8(r.a, r.b, hi, lo);
+  __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
+    split8(r.a, r.b, hi, lo);
   }
 };
 
 // ------------------------------------------------------------------------------------------
 // Dense contraction over a workgroup's rows: out[tok][row] = sum_k A[tok][k] * W[row][k].
-// Rows are assigned in octets (8 rows) so that half tiles never share a cache line.
-// Up to 4 tiles of 16 rows per pass; the 8 waves split K; partials meet in LDS.
-// On return `fin` holds [tile j][row r][tok] sums for tiles t_first .. t_first+ntiles-1.
+// Rows are assigned in octets (8 rows = one 128-byte line of every 1 KiB step), so that
+// workgroups never share a cache line.  NT (1..4) tiles of 16 rows per pass; the k-waves
+// split K evenly and stream it through a ring of DEPTH steps; partials meet in LDS.  Lanes of
+// an octet outside the workgroup's range load their partner octet's line instead (the same
+// line another lane fetches; the products are never read), so no load sits behind a branch.
+// On return `fin` holds [tile j][row r][tok] sums for tiles t_first .. t_first+NT-1.
 // ------------------------------------------------------------------------------------------
 struct DenseLds {
   f32x4 red[kWaves * 4 * 64];   // 32 KiB
@@ -172,62 +170,87 @@ __device__ __forceinline__ int kwaves_for(int n) {
   return w;
 }
 
-template <class ASrc>
-__device__ void dense_pass(const uint8_t* w0, int tiles0, const uint8_t* w1, int K, int t_first,
-                           int ntiles, int oct_lo, int oct_hi, const ASrc& A, DenseLds& L) {
+// Not inlined (one body per NT); the arguments arrive in vector registers and are moved to
+// scalar registers first.
+template <int NT, class ASrc>
+__device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, const uint8_t* w1_arg,
+                                        int K_arg, int t_first_arg, int oct_lo_arg, int oct_hi_arg,
+                                        const ASrc A_arg) {
   constexpr int DEPTH = 4;  // k steps in flight per wave
+  // the phase scratch of the dynamic LDS, addressed through the LDS symbol (a pointer argument
+  // would arrive as a generic address and turn every access into a flat one)
+  DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(moel_lds));
+  const uint8_t* w0 = uniform(w0_arg);
+  const uint8_t* w1 = uniform(w1_arg);
+  const int tiles0 = uniform(tiles0_arg), K = uniform(K_arg), t_first = uniform(t_first_arg);
+  const int oct_lo = uniform(oct_lo_arg), oct_hi = uniform(oct_hi_arg);
+  const ASrc A = A_arg.scalar();
   const int lane = lane_id(), wv = wave_id();
   const int S = K >> 5;
   const int nkw = kwaves_for(S);
-  f32x4 acc[4];
+  f32x4 acc[NT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wv < nkw) {
     const int ns = S / nkw, sa = wv * ns;
-    const int tok = lane & 15, kq = 8 * (lane >> 4);
-    const uint8_t* base[4];
-    bool on[4];
+    const int tok = (lane & 15) < A.T ? (lane & 15) : A.T - 1;
+    const int kq = 8 * (lane >> 4) + 32 * sa;
+    const uint8_t* base[NT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < NT; ++j) {
       const int t = t_first + j;
       const int oct = 2 * t + ((lane & 15) >> 3);
-      on[j] = (j < ntiles) && oct >= oct_lo && oct < oct_hi;
+      const int src_lane = (oct >= oct_lo && oct < oct_hi) ? lane : (lane ^ 8);
       base[j] = (t < tiles0 ? w0 + (size_t)t * S * 1024 : w1 + (size_t)(t - tiles0) * S * 1024) +
-                lane * 16;
+                (size_t)sa * 1024 + src_lane * 16;
     }
     typename ASrc::Raw ra[DEPTH];
-    u32x4 rw[DEPTH][4];
-    auto issue = [&](typename ASrc::Raw& a, u32x4 (&w)[4], int s) {
-      A.fetch(tok, 32 * s + kq, a);
+    u32x4 rw[DEPTH][NT];
+    auto issue = [&](int d, int i) {
+      A.fetch(tok, kq + 32 * i, ra[d]);
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        w[j] = on[j] ? ldg_stream(base[j] + (size_t)s * 1024) : u32x4{0u, 0u, 0u, 0u};
+      for (int j = 0; j < NT; ++j) rw[d][j] = ldg_stream(base[j] + (size_t)i * 1024);
     };
+    auto compute = [&](int d) {
+      u32x4 a_hi, a_lo;
+      A.finish(ra[d], a_hi, a_lo);
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-      if (d < ns) issue(ra[d], rw[d], sa + d);
-    for (int i0 = 0; i0 < ns; i0 += DEPTH) {
+      for (int j = 0; j < NT; ++j) {
+        acc[j] = mfma16x16x32(a_hi, rw[d][j], acc[j]);
+        acc[j] = mfma16x16x32(a_lo, rw[d][j], acc[j]);
+      }
+    };
+    // straight-line prologue (steps past the end repeat the last one and are never used), so
+    // that the ring registers enter the loop in issue order
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      issue(d, d < ns ? d : ns - 1);
+      sched_fence();
+    }
+    int i0 = 0;
+    for (; i0 + 2 * DEPTH <= ns; i0 += DEPTH) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        const int i = i0 + d;
-        if (i < ns) {
-          u32x4 a_hi, a_lo;
-          A.finish(tok, 32 * (sa + i) + kq, ra[d], a_hi, a_lo);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (j < ntiles) {
-              acc[j] = mfma16x16x32(a_hi, rw[d][j], acc[j]);
-              acc[j] = mfma16x16x32(a_lo, rw[d][j], acc[j]);
-            }
-          if (i + DEPTH < ns) issue(ra[d], rw[d], sa + i + DEPTH);
-        }
+        compute(d);
+        issue(d, i0 + DEPTH + d);
+        sched_fence();
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) L.red[(wv * 4 + j) * 64 + lane] = acc[j];
+    for (int d = 0; d < DEPTH; ++d) {
+      if (i0 + d < ns) {
+        compute(d);
+        if (i0 + DEPTH + d < ns) issue(d, i0 + DEPTH + d);
+      }
+    }
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+      if (i0 + DEPTH + d < ns) compute(d);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) L.red[(wv * 4 + j) * 64 + lane] = acc[j];
   }
   lds_barrier();
-  for (int e = threadIdx.x; e < ntiles * 256; e += kThreads) {
+  for (int e = threadIdx.x; e < NT * 256; e += kThreads) {
     const int j = e >> 8, ln = (e >> 2) & 63, r = e & 3;
     float s = 0.f;
     for (int w = 0; w < nkw; ++w) s += L.red[(w * 4 + j) * 64 + ln][r];
@@ -247,7 +270,7 @@ __device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo,
 // Runs dense_pass over the workgroup's rows in groups of <= 4 tiles and calls
 // epi(L, t_first, ntiles, oct_lo, oct_hi) after each group.
 template <class ASrc, class Epi>
-__device__ void dense_phase(const uint8_t* w0, int tiles0, const uint8_t* w1, int tiles1, int K,
+__device__ __forceinline__ void dense_phase(const uint8_t* w0, int tiles0, const uint8_t* w1, int tiles1, int K,
                             int wg, int nwg, const ASrc& A, DenseLds& L, Epi&& epi) {
   int lo, hi;
   octet_range(tiles0 + tiles1, wg, nwg, lo, hi);
@@ -258,7 +281,12 @@ __device__ void dense_phase(const uint8_t* w0, int tiles0, const uint8_t* w1, in
   const int tf = lo >> 1, tl = (hi - 1) >> 1;
   for (int t = tf; t <= tl; t += 4) {
     const int nt = (tl - t + 1) < 4 ? (tl - t + 1) : 4;
-    dense_pass(w0, tiles0, w1, K, t, nt, lo, hi, A, L);
+    switch (nt) {
+      case 1: dense_pass<1>(w0, tiles0, w1, K, t, lo, hi, A); break;
+      case 2: dense_pass<2>(w0, tiles0, w1, K, t, lo, hi, A); break;
+      case 3: dense_pass<3>(w0, tiles0, w1, K, t, lo, hi, A); break;
+      default: dense_pass<4>(w0, tiles0, w1, K, t, lo, hi, A); break;
+    }
     epi(L, t, nt, lo, hi);
     lds_barrier();
   }
@@ -274,7 +302,7 @@ __device__ __forceinline__ bool octet_in(int row, int lo, int hi) {
 // rotation partners (i, i + D/2) of every head interleaved: packed row 2i <-> canonical i,
 // packed row 2i+1 <-> canonical i + D/2.  The cache stores bf16 (nearest); q stays fp32.
 // ------------------------------------------------------------------------------------------
-__device__ void phase_qkv(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   const float rs = wg_rstd(p.ss1, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
   ANorm A{p.x, p.H, p.gamma1, rs, p.T};
@@ -326,7 +354,7 @@ struct AttnLds {
 };
 
 template <int D>
-__device__ void phase_attn(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(phase_smem(smem));
   constexpr int KS = AttnLds<D>::KS, VS = AttnLds<D>::VS;
   constexpr int NS = D / 32;   // MFMA k-steps over the head dim
@@ -469,7 +497,7 @@ __device__ void phase_attn(KP& p, int wg, char* smem) {
 }
 
 // Merge the key-chunk partials of every (token, q head) row -> o (fp32).
-__device__ void phase_attn_merge(KP& p, int wg) {
+__device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
   const int grp = p.Hq / p.Hkv;
   const int total = p.T * p.Hq * p.D;
   for (int e = wg * kThreads + threadIdx.x; e < total; e += p.nwg * kThreads) {
@@ -496,7 +524,7 @@ __device__ void phase_attn_merge(KP& p, int wg) {
 // ------------------------------------------------------------------------------------------
 // o-projection + residual -> h (fp32), and per-workgroup partial sums of h^2.
 // ------------------------------------------------------------------------------------------
-__device__ void phase_oproj(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AF32 A{p.o_buf, p.Hq * p.D, p.T};
   float part = 0.f;  // thread t < 16 accumulates token t over the workgroup's rows
@@ -527,7 +555,7 @@ __device__ void phase_oproj(KP& p, int wg, char* smem) {
 // Router logits and pooler from hn = h * rstd2 * gamma2, one contraction over the stacked
 // rows [router; pooler].
 // ------------------------------------------------------------------------------------------
-__device__ void phase_router_pool(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   const float rs = wg_rstd(p.ss2, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
   ANorm A{p.h_buf, p.H, p.gamma2, rs, p.T};
@@ -554,7 +582,7 @@ __device__ void phase_router_pool(KP& p, int wg, char* smem) {
 // softmax over the selected logits, and per-expert slot lists.  Computed redundantly by
 // every workgroup from the same logits, so all agree bit for bit.
 // ------------------------------------------------------------------------------------------
-__device__ void compute_routing(KP& p, RouteTables& R, bool write_debug) {
+__device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool write_debug) {
   const int lane = lane_id(), wv = wave_id();
   const int nslot = p.T * p.topk;
   const float NEG = -__builtin_inff();
@@ -672,42 +700,42 @@ __device__ void compute_routing(KP& p, RouteTables& R, bool write_debug) {
 // fp32-accurate product.  The E4M3 block scale multiplies each 16-k partial in fp32.
 // G = token pairs (1, 2, 4, 8), NM = matrices sharing the activation (2 gate+up, 1 down).
 // ------------------------------------------------------------------------------------------
+// LDS of the NVFP4 expert phases.  red: per-wave partial sums of a tile, [wave][lane][RW]
+// floats with RW = NM*2*G; double-buffered by tile parity when two buffers fit (RW <= 16),
+// so that one barrier per tile suffices.  stage: finished outputs of the current run of
+// tiles, written to global memory when the run ends (or the stage is full), so that no
+// global store sits between the weight loads of a run.
+constexpr int kFp4RedPer = 32;        // floats per (wave, lane): NM*2*G for NM = 2, G = 8
+constexpr int kFp4Stage = 4096;       // floats (16 KiB): >= 4 tiles of 64 rows x 16 slots
 struct Fp4Lds {
-  float red[kWaves * 64 * 32];   // [wave][lane][m*16 + token slot j], 64 KiB
+  float red[kWaves * 64 * kFp4RedPer];
+  float stage[kFp4Stage];
 };
 
 template <int NM, int G>
 struct Fp4Pair {
   u32x4 c[NM][2];   // codes of the pair's two 32-k steps
   uint32_t sc[NM];  // 4 block scales of the pair
-  u32x2 a[G];       // lane 4b+i: row i of group g (hi/lo of token 2g + (i&1)), k0 + 4b .. +3
+  float4 a[G];      // activation k0 + 4b .. +3 of the token slot of lane 4b+i (split at use)
 };
 
 template <int NM, int G>
-__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM], int pr,
+__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM],
                                               const float* const (&arow)[G], int k0) {
   const int lane = lane_id();
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
-    const uint8_t* b = wt[m] + (size_t)pr * 2304;
-    f.c[m][0] = ldg_stream(b + lane * 16);
-    f.c[m][1] = ldg_stream(b + 1024 + lane * 16);
-    f.sc[m] = ldg_stream32(b + 2048 + 4 * lane);
+    f.c[m][0] = ldg_stream(wt[m] + lane * 16);
+    f.c[m][1] = ldg_stream(wt[m] + 1024 + lane * 16);
+    f.sc[m] = ldg_stream32(wt[m] + 2048 + 4 * lane);
   }
-  const bool lo_row = (lane & 2) != 0;
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    f.a[g] = u32x2{0u, 0u};
-    if (arow[g] != nullptr) {
-      const float4 v = ldgf4(arow[g] + k0 + 4 * (lane >> 2));
-      const u32x2 s01 = split_bf16(v.x, v.y), s23 = split_bf16(v.z, v.w);
-      f.a[g] = lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
-    }
-  }
+  for (int g = 0; g < G; ++g) f.a[g] = ldgf4(arow[g] + k0 + 4 * (lane >> 2));
 }
 
 template <int H, int J, int NM, int G>
-__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, f32x4 (&acc)[NM][G]) {
+__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, const u32x2 (&a)[G],
+                                               f32x4 (&acc)[NM][G]) {
   // block q = 2*H + J (16 k): MFMAs with ABID = 8*H + 4*J + u, u = 0..3
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -721,10 +749,10 @@ __device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, f32x4 (&
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       f32x4 P = f32x4{0.f, 0.f, 0.f, 0.f};
-      P = mfma4x4x4_bcast<8 * H + 4 * J + 0>(f.a[g], b[0], P);
-      P = mfma4x4x4_bcast<8 * H + 4 * J + 1>(f.a[g], b[1], P);
-      P = mfma4x4x4_bcast<8 * H + 4 * J + 2>(f.a[g], b[2], P);
-      P = mfma4x4x4_bcast<8 * H + 4 * J + 3>(f.a[g], b[3], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 0>(a[g], b[0], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 1>(a[g], b[1], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 2>(a[g], b[2], P);
+      P = mfma4x4x4_bcast<8 * H + 4 * J + 3>(a[g], b[3], P);
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[m][g][r] = fmaf(s, P[r], acc[m][g][r]);
     }
@@ -733,116 +761,165 @@ __device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, f32x4 (&
 
 template <int NM, int G>
 __device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 (&acc)[NM][G]) {
-  fp4_mfma_block<0, 0>(f, acc);
-  fp4_mfma_block<0, 1>(f, acc);
-  fp4_mfma_block<1, 0>(f, acc);
-  fp4_mfma_block<1, 1>(f, acc);
+  // rows of a 4-lane block: (hi t0, hi t1, lo t0, lo t1) -> lanes with bit 1 set take lo
+  const bool lo_row = (lane_id() & 2) != 0;
+  u32x2 a[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const u32x2 s01 = split_bf16(f.a[g].x, f.a[g].y), s23 = split_bf16(f.a[g].z, f.a[g].w);
+    a[g] = lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
+  }
+  fp4_mfma_block<0, 0>(f, a, acc);
+  fp4_mfma_block<0, 1>(f, a, acc);
+  fp4_mfma_block<1, 0>(f, a, acc);
+  fp4_mfma_block<1, 1>(f, a, acc);
 }
 
 // One expert's run of 64-row tiles [ta, tb) for this workgroup.
 //   GATEUP: NM = 2, activation = pl rows of the expert's tokens, out a = silu(g) * u
 //   else  : NM = 1, activation = a rows of the expert's slots,   out d
-// Each k-wave streams its pairs of every tile through a ring of DEPTH register buffers, so
-// DEPTH pairs (NM = 2: 4.6 KB each) stay in flight per wave across tile boundaries.
-template <bool GATEUP, int G>
-__device__ void fp4_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
-                                 Fp4Lds& L) {
+// The k-waves split each tile's K/64 pairs evenly (npt pairs each, npt % DEPTH == 0) and
+// stream them through a ring of DEPTH register buffers that runs across tile boundaries.
+// The steady-state loop holds no branch around a load and no global store, so the only
+// memory wait in it is the one for the oldest ring entry.
+template <bool GATEUP, int G, int DEPTH>
+__device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, int tb_arg) {
+  KP& p = params_from(ph);
   constexpr int NM = GATEUP ? 2 : 1;
-  // register budget: deeper rings for the common 1-2 token experts
-  constexpr int DEPTH = G == 1 ? (NM == 2 ? 4 : 8) : G == 2 ? 4 : G == 4 ? 2 : 1;
+  constexpr int RW = NM * 2 * G;  // red floats per lane
+  RouteTables& R = route_tables(moel_lds);
+  Fp4Lds& L = *reinterpret_cast<Fp4Lds*>(phase_smem(moel_lds));
+  const int u = uniform(u_arg), ta = uniform(ta_arg), tb = uniform(tb_arg);
   const int lane = lane_id(), wv = wave_id();
-  const int e = R.active_e[u];
-  const int s_lo = R.active_off[u], n_e = R.active_off[u + 1] - s_lo;
+  const int e = uniform(R.active_e[u]);
+  const int s_lo = uniform(R.active_off[u]);
+  const int n_e = uniform(R.active_off[u + 1]) - s_lo;
   const int K = GATEUP ? p.P : p.I;
   const int Sp = K >> 6;  // 64-k pairs (K % 128 == 0)
   const int nkw = kwaves_for(Sp);
-  const int npt = Sp / nkw;  // pairs per tile, equal for every k-wave
-  const int pa = wv * npt;
+  const int npt = Sp / nkw;
   const bool kw = wv < nkw;
   const size_t tile_bytes = (size_t)36 * K;  // 64 rows of K/2 + K/16 bytes
   const uint8_t* wb[NM];
   if (GATEUP) {
-    wb[0] = p.w_gate + (size_t)e * p.stride_gate;
-    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up;
+    wb[0] = p.w_gate + (size_t)e * p.stride_gate + (size_t)wv * npt * 2304;
+    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up + (size_t)wv * npt * 2304;
   } else {
-    wb[0] = p.w_down + (size_t)e * p.stride_down;
+    wb[0] = p.w_down + (size_t)e * p.stride_down + (size_t)wv * npt * 2304;
   }
-  // activation rows: lane 4b+i carries token slot 2g + (i & 1)
+  // activation rows: lane 4b+i carries token slot 2g + (i & 1); slots past n_e repeat the
+  // last one (their products are computed and never read)
   const float* arow[G];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int j = 2 * g + (lane & 1);
-    arow[g] = nullptr;
-    if (j < n_e) {
-      const int slot = R.slots[s_lo + j];
-      arow[g] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
-    }
+    int j = 2 * g + (lane & 1);
+    j = j < n_e ? j : n_e - 1;
+    const int slot = R.slots[s_lo + j];
+    arow[g] = (GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I) + wv * npt * 64;
   }
-  const int total = (tb - ta) * npt;  // same for every wave (idle waves only join barriers)
-  Fp4Pair<NM, G> ring[DEPTH];
-  auto issue = [&](Fp4Pair<NM, G>& f, int i) {
-    const int ti = ta + i / npt, pr = pa + i % npt;
-    const uint8_t* wt[NM];
-#pragma unroll
-    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes;
-    fp4_pair_load<NM, G>(f, wt, pr, arow, 64 * pr);
-  };
-  if (kw) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-      if (d < total) issue(ring[d], d);
-  }
+  const int stage_tiles = kFp4Stage / (64 * n_e);
+  // per-matrix tensor scales, read once (a global load inside the loop would drain the ring)
+  const float ts0 = GATEUP ? gl(p.ts_gate)[e] : gl(p.ts_down)[e];
+  const float ts1 = GATEUP ? gl(p.ts_up)[e] : 0.f;
+
   f32x4 acc[NM][G];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int i0 = 0; i0 < total; i0 += DEPTH) {
+  // tile ti (local index tl within the stage) is complete on every k-wave: reduce over the
+  // k-waves in wave order into the stage.  LDS traffic only.
+  constexpr bool DB = 2 * RW <= kFp4RedPer;
+  auto tile_end = [&](int tl) {
+    float* red = L.red + (DB ? (tl & 1) * (kWaves * 64 * RW) : 0);
+    if (kw) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int i = i0 + d;
-      if (i < total) {
-        if (kw) {
-          fp4_pair_compute<NM, G>(ring[d], acc);
-          if (i + DEPTH < total) issue(ring[d], i + DEPTH);
+      for (int m = 0; m < NM; ++m)
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+          red[(wv * 64 + lane) * RW + m * 2 * G + 2 * g] = acc[m][g][0] + acc[m][g][2];
+          red[(wv * 64 + lane) * RW + m * 2 * G + 2 * g + 1] = acc[m][g][1] + acc[m][g][3];
+          acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-        if ((i + 1) % npt == 0) {  // the tile is complete on every k-wave
-          const int ti = ta + i / npt;
-          if (kw) {
-            // rows (hi, hi', lo, lo') -> token slots 2g, 2g+1
-#pragma unroll
-            for (int m = 0; m < NM; ++m)
-#pragma unroll
-              for (int g = 0; g < G; ++g) {
-                L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g] = acc[m][g][0] + acc[m][g][2];
-                L.red[(wv * 64 + lane) * 32 + m * 16 + 2 * g + 1] = acc[m][g][1] + acc[m][g][3];
-                acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-              }
-          }
-          lds_barrier();
-          // reduce over the k-waves in order; lane row = ti*64 + ln
-          for (int x = threadIdx.x; x < 64 * n_e; x += kThreads) {
-            const int ln = x & 63, j = x >> 6;
-            const int slot = R.slots[s_lo + j];
-            if (GATEUP) {
-              float gs = 0.f, us = 0.f;
-              for (int w = 0; w < nkw; ++w) {
-                gs += L.red[(w * 64 + ln) * 32 + j];
-                us += L.red[(w * 64 + ln) * 32 + 16 + j];
-              }
-              gs *= gl(p.ts_gate)[e];
-              us *= gl(p.ts_up)[e];
-              gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + ti * 64 + ln] = gs / (1.0f + __expf(-gs)) * us;
-            } else {
-              float ds = 0.f;
-              for (int w = 0; w < nkw; ++w) ds += L.red[(w * 64 + ln) * 32 + j];
-              gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + ti * 64 + ln] = ds * gl(p.ts_down)[e];
-            }
-          }
-          lds_barrier();
+    }
+    lds_barrier();
+    float* out = L.stage + tl * 64 * n_e;
+    for (int x = threadIdx.x; x < 64 * n_e; x += kThreads) {
+      const int ln = x & 63, j = x >> 6;
+      if (GATEUP) {
+        float gs = 0.f, us = 0.f;
+        for (int w = 0; w < nkw; ++w) {
+          gs += red[(w * 64 + ln) * RW + j];
+          us += red[(w * 64 + ln) * RW + 2 * G + j];
         }
+        gs *= ts0;
+        us *= ts1;
+        out[x] = gs / (1.0f + __expf(-gs)) * us;
+      } else {
+        float ds = 0.f;
+        for (int w = 0; w < nkw; ++w) ds += red[(w * 64 + ln) * RW + j];
+        out[x] = ds * ts0;
       }
     }
+    if (!DB) lds_barrier();  // red is rewritten at the next tile end
+  };
+  Fp4Pair<NM, G> ring[DEPTH];
+  auto issue = [&](Fp4Pair<NM, G>& f, int ti, int pr) {
+    const uint8_t* wt[NM];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes + (size_t)pr * 2304;
+    fp4_pair_load<NM, G>(f, wt, arow, 64 * pr);
+  };
+  // The run goes in segments of at most stage_tiles tiles; each segment is one pipeline
+  // (prologue, steady loop, last chunk) whose outputs are flushed to global memory after it.
+  for (int sa = ta; sa < tb; sa += stage_tiles) {
+    const int sb = tb - sa < stage_tiles ? tb : sa + stage_tiles;
+    if (kw) {
+      // DEPTH <= npt: the first DEPTH pairs all lie in tile sa
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        issue(ring[d], sa, d);
+        sched_fence();
+      }
+      int ct = 0, cp = 0;           // local tile / pair of the chunk being computed
+      int it = sa, ip = DEPTH;      // tile / pair of the chunk being issued
+      if (ip == npt) { ip = 0; ++it; }
+      while (it < sb) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+          fp4_pair_compute<NM, G>(ring[d], acc);
+          issue(ring[d], it, ip + d);
+          sched_fence();
+        }
+        ip += DEPTH;
+        if (ip == npt) { ip = 0; ++it; }
+        cp += DEPTH;
+        if (cp == npt) {
+          tile_end(ct);
+          cp = 0;
+          ++ct;
+        }
+      }
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) fp4_pair_compute<NM, G>(ring[d], acc);
+      tile_end(sb - sa - 1);
+    } else {
+      // waves without k work only take part in the reductions
+      for (int tl = 0; tl < sb - sa; ++tl) tile_end(tl);
+    }
+    // write the segment's outputs
+    lds_barrier();
+    const int n = (sb - sa) * 64 * n_e;
+    for (int x = threadIdx.x; x < n; x += kThreads) {
+      const int tl = x / (64 * n_e), r = x % (64 * n_e), j = r >> 6, ln = r & 63;
+      const int slot = R.slots[s_lo + j];
+      const int row = (sa + tl) * 64 + ln;
+      if (GATEUP)
+        gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + row] = L.stage[x];
+      else
+        gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + row] = L.stage[x];
+    }
+    lds_barrier();  // the stage is rewritten by the next segment
   }
 }
 
@@ -851,7 +928,7 @@ __device__ void fp4_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int
 // second row tile takes slots 8..15.
 // ------------------------------------------------------------------------------------------
 template <bool GATEUP>
-__device__ void bf16_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
+__device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
                                   DenseLds& L) {
   constexpr int NM = GATEUP ? 2 : 1;
   const int lane = lane_id(), wv = wave_id();
@@ -939,17 +1016,9 @@ __device__ void bf16_expert_tiles(KP& p, const RouteTables& R, int u, int ta, in
   }
 }
 
-// One non-inlined function per (GATEUP, G): each gets its own register allocation, so the
-// rare many-token instantiations cannot push the common 1-2 token path into spills.
-template <bool GATEUP, int G>
-__device__ __noinline__ void fp4_expert_run(KP& p, int u, int ta, int tb) {
-  fp4_expert_tiles<GATEUP, G>(p, route_tables(moel_lds), u, ta, tb,
-                              *reinterpret_cast<Fp4Lds*>(phase_smem(moel_lds)));
-}
-
 // Expert GEMM phase: the flattened list (active expert u, tile) split evenly over workgroups.
 template <bool GATEUP>
-__device__ void phase_experts(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
   RouteTables& R = route_tables(smem);
   const int rows = GATEUP ? p.I_loc : p.P_loc;
   const bool fp4 = p.expert_dtype == 0;
@@ -963,11 +1032,24 @@ __device__ void phase_experts(KP& p, int wg, char* smem) {
     int tb = tpe;
     if ((u + 1) * tpe > t1) tb = t1 - u * tpe;
     if (fp4) {
-      const int n_e = R.active_off[u + 1] - R.active_off[u];
-      if (n_e <= 2) fp4_expert_run<GATEUP, 1>(p, u, ta, tb);
-      else if (n_e <= 4) fp4_expert_run<GATEUP, 2>(p, u, ta, tb);
-      else if (n_e <= 8) fp4_expert_run<GATEUP, 4>(p, u, ta, tb);
-      else fp4_expert_run<GATEUP, 8>(p, u, ta, tb);
+      const int n_e = uniform(R.active_off[u + 1] - R.active_off[u]);
+      // ring depth per token-pair count (register budget); npt % DEPTH != 0 only for shapes
+      // with K < 512, which take the depth-1 ring
+      const int Sp = (GATEUP ? p.P : p.I) >> 6;
+      const int npt = Sp / kwaves_for(Sp);
+      constexpr int D1 = GATEUP ? 4 : 8;
+      if (n_e <= 2) {
+        if (npt % D1 == 0) fp4_expert_run<GATEUP, 1, D1>(params_handle(p), u, ta, tb);
+        else fp4_expert_run<GATEUP, 1, 1>(params_handle(p), u, ta, tb);
+      } else if (n_e <= 4) {
+        if (npt % 4 == 0) fp4_expert_run<GATEUP, 2, 4>(params_handle(p), u, ta, tb);
+        else fp4_expert_run<GATEUP, 2, 1>(params_handle(p), u, ta, tb);
+      } else if (n_e <= 8) {
+        if (npt % 2 == 0) fp4_expert_run<GATEUP, 4, 2>(params_handle(p), u, ta, tb);
+        else fp4_expert_run<GATEUP, 4, 1>(params_handle(p), u, ta, tb);
+      } else {
+        fp4_expert_run<GATEUP, 8, 1>(params_handle(p), u, ta, tb);
+      }
     } else {
       DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
       bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
@@ -977,7 +1059,7 @@ __device__ void phase_experts(KP& p, int wg, char* smem) {
 }
 
 // m[t] = sum over the token's slots, in selection order, of gate * d
-__device__ void phase_combine(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
   const RouteTables& R = route_tables(smem);
   const int total = p.T * p.P_loc;
   for (int x = wg * kThreads + threadIdx.x; x < total; x += p.nwg * kThreads) {
@@ -990,7 +1072,7 @@ __device__ void phase_combine(KP& p, int wg, char* smem) {
 }
 
 // y = h + m W_unpool^T
-__device__ void phase_unpool(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AF32 A{p.m_buf, p.P, p.T};
   dense_phase(p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, p.nwg, A, L,
