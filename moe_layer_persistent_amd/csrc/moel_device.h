@@ -132,31 +132,63 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ---------------------------------------------------------------- control block
-enum CtrlWord { kBar = 0, kExit = 1, kStatus = 2, kAbort = 3 };
+// Words of the plan's control block (unsigned, 4 KiB).  The barrier words sit on separate
+// 128-byte lines so that arrivals of different groups do not contend.
+enum CtrlWord {
+  kExit = 1,      // workgroups that have left the launch
+  kStatus = 2,    // MOEL_DEV_* (0 = ok)
+  kAbort = 3,     // set by the host: skip all work
+  kFlag = 32,     // number of the last grid barrier released in this launch
+  kTop = 64,      // group leaders arrived (monotonic within a launch)
+  kGroup = 96,    // + 32 * g: workgroups of group g arrived (monotonic within a launch)
+  kCtrlWords = 1024
+};
+constexpr int kBarGroups = 8;
 
 __device__ __forceinline__ bool aborted(KP& p) {
   return __hip_atomic_load(gl(p.ctrl) + kAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
-// Grid-wide barrier of the persistent launch.  `target` grows by nwg per barrier within one
-// launch; the counter is reset by the last workgroup to leave the kernel.  Every wait is
-// bounded: after ~0.5 s the status word records a timeout and the wait ends.
+// Grid-wide barrier number b (1, 2, ... within one launch) of the persistent launch.
 //
-// Visibility: every wave first waits for its own stores to reach the L2 of its XCD; one wave
-// per workgroup then writes the XCD's L2 back (release), arrives, spins, and invalidates the
-// CU's L1 and the XCD's L2 (acquire).  Those cache operations act on the whole CU / XCD, so a
-// single wave's fences cover the stores and later loads of all eight waves.
-__device__ __forceinline__ void grid_barrier(KP& p, unsigned target) {
+// Arrival is a two-level tree: workgroup w counts into group (w mod 8), whose counter lives
+// on its own cache line; the last arrival of a group counts into the top counter; the last
+// group leader publishes b in the release word, which every workgroup polls.  A single
+// counter for all 256 workgroups serialises 256 same-address device-scope atomics when the
+// workgroups arrive together.  All counters are monotonic within a launch (group g reads
+// b * n_g after barrier b) and are reset by the last workgroup to leave the kernel.
+//
+// Ordering: every arrival is preceded by a release fence; a group leader and the final
+// arrival run acquire-release fences between their counter updates, and every waiter runs an
+// acquire fence after seeing the release word, so each workgroup's stores before the barrier
+// are visible to every workgroup after it.  One wave per workgroup runs the fences: the cache
+// operations they issue act on the whole CU / XCD.
+//
+// Every wait is bounded: after ~0.5 s the status word records a timeout and the wait ends.
+__device__ __forceinline__ void grid_barrier(KP& p, unsigned b) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
+    const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+    const int g = (int)blockIdx.x % ng_all;
+    const unsigned n_g = (unsigned)((p.nwg - g + ng_all - 1) / ng_all);
+    auto ctrl = gl(p.ctrl);
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(gl(p.ctrl) + kBar, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(gl(p.ctrl) + kBar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+    const unsigned prev = __hip_atomic_fetch_add(ctrl + kGroup + 32 * g, 1u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+    if (prev + 1 == b * n_g) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      const unsigned top = __hip_atomic_fetch_add(ctrl + kTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (top + 1 == b * (unsigned)ng_all) {
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+        __hip_atomic_store(ctrl + kFlag, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(ctrl + kFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < b) {
       __builtin_amdgcn_s_sleep(1);
       if (__builtin_amdgcn_s_memrealtime() - t0 > 50000000ull) {
-        __hip_atomic_store(gl(p.ctrl) + kStatus, (unsigned)MOEL_DEV_TIMEOUT, __ATOMIC_RELAXED,
+        __hip_atomic_store(ctrl + kStatus, (unsigned)MOEL_DEV_TIMEOUT, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         break;
       }

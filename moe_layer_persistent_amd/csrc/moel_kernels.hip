@@ -19,7 +19,7 @@ using namespace moel;
 // Each phase of the persistent launch is a separate (non-inlined) function so that the
 // register allocator sizes each phase on its own instead of the union of all of them.
 template <int PH, int D>
-__device__ __noinline__ void fused_phase(uint64_t ph, int wg_arg) {
+__device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   KP& p = params_from(ph);
   const int wg = uniform(wg_arg);
   char* smem = moel_lds;
@@ -48,10 +48,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
   __syncthreads();
   const bool run = s_abort == 0;
   unsigned bar = 0;
-  auto sync = [&]() {
-    bar += (unsigned)p.nwg;
-    grid_barrier(p, bar);
-  };
+  auto sync = [&]() { grid_barrier(p, ++bar); };
   stamp(p, 16 + kPhNorm1);
   if (run) fused_phase<kPhNorm1, D>(params_handle(p), wg);
   stamp(p, kPhNorm1);
@@ -99,8 +96,12 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
     const unsigned prev =
         __hip_atomic_fetch_add(gl(p.ctrl) + kExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == (unsigned)p.nwg - 1) {
-      __hip_atomic_store(gl(p.ctrl) + kBar, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(gl(p.ctrl) + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      auto ctrl = gl(p.ctrl);
+      __hip_atomic_store(ctrl + kFlag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctrl + kTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int g = 0; g < kBarGroups; ++g)
+        __hip_atomic_store(ctrl + kGroup + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -260,7 +261,7 @@ moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, 
   const int nkeys = pos + T - lo;
   int maxc = plan->nwg / plan->cfg.n_kv_heads;
   if (maxc < 1) maxc = 1;
-  int nch = (nkeys + 255) / 256;
+  int nch = (nkeys + 127) / 128;  // chunks of >= 128 keys, at most nwg / Hkv of them
   if (nch > maxc) nch = maxc;
   if (nch < 1) nch = 1;
   const int chunk = (nkeys + nch - 1) / nch;
@@ -325,7 +326,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     off = align256(off + bytes);
     return o;
   };
-  const size_t o_ctrl = take(256);
+  const size_t o_ctrl = take((size_t)kCtrlWords * 4);
   const size_t o_ss1 = take((size_t)nwg * kMaxT * 4);
   const size_t o_ss2 = take((size_t)nwg * kMaxT * 4);
   const size_t o_q = take((size_t)kMaxT * Hq * D * 4);
@@ -461,13 +462,17 @@ int32_t moel_plan_workgroups(const moel_plan* plan) { return plan ? plan->nwg : 
 moel_status moel_plan_status(moel_plan* plan) {
   if (plan == nullptr) return MOEL_ERR_ARG;
   if (!hip_ok(hipDeviceSynchronize())) return MOEL_ERR_HIP;
-  unsigned words[4] = {0, 0, 0, 0};
+  unsigned words[kCtrlWords];
   if (!hip_ok(hipMemcpy(words, plan->base.ctrl, sizeof(words), hipMemcpyDeviceToHost))) return MOEL_ERR_HIP;
   if (words[kStatus] == 0) return MOEL_OK;
+  // a launch that timed out or was aborted may have left barrier words behind: clear every
+  // word except the abort word
+  const unsigned status = words[kStatus];
   const unsigned keep_abort = words[kAbort];
-  unsigned clear[4] = {0, 0, 0, keep_abort};
-  if (!hip_ok(hipMemcpy(plan->base.ctrl, clear, sizeof(clear), hipMemcpyHostToDevice))) return MOEL_ERR_HIP;
-  return words[kStatus] == MOEL_DEV_TIMEOUT ? MOEL_ERR_TIMEOUT : MOEL_ERR_ABORTED;
+  for (int i = 0; i < kCtrlWords; ++i) words[i] = 0;
+  words[kAbort] = keep_abort;
+  if (!hip_ok(hipMemcpy(plan->base.ctrl, words, sizeof(words), hipMemcpyHostToDevice))) return MOEL_ERR_HIP;
+  return status == MOEL_DEV_TIMEOUT ? MOEL_ERR_TIMEOUT : MOEL_ERR_ABORTED;
 }
 
 moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes) {

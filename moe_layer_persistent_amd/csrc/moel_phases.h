@@ -342,23 +342,36 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
 
 // ------------------------------------------------------------------------------------------
 // Attention partials.  Item = (kv head g, key chunk c); each wave is one q head of the group.
-// S^T = K Q^T on MFMA (keys as rows; q as hi + lo), softmax in fp32 with the exact max of each
-// 256-key sub-chunk and an online rescale between sub-chunks, O += P V on MFMA (P as hi + lo).
+// Keys go in sub-chunks of SK = 128: while one sub-chunk is in LDS and being used, the next
+// one's K/V rows are already in flight into registers.  S^T = K Q^T on MFMA (keys as rows;
+// q as hi + lo), softmax in fp32 with the exact max of each sub-chunk and an online rescale
+// between sub-chunks, O += P V on MFMA (P as hi + lo; V transposed in LDS).
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct AttnLds {
+  static constexpr int SK = 128;          // keys per sub-chunk
   static constexpr int KS = D + 8;        // Ks row stride (bf16 elements)
-  static constexpr int VS = 256 + 8;      // Vt row stride
-  uint16_t Ks[256 * KS];
+  static constexpr int VS = SK + 8;       // Vt row stride
+  uint16_t Ks[SK * KS];
   uint16_t Vt[D * VS];
+  // V^T element (d, key): 4-key groups XOR-swizzled by d / 8, so that the transposing stores
+  // of one wave (16 d-octets x 4 keys) spread over the banks; a 4-key group stays contiguous
+  // for the 8-byte operand reads.
+  __device__ static __forceinline__ int vt_index(int d, int key) {
+    return d * VS + ((((key >> 2) ^ ((d >> 3) & 15)) << 2) | (key & 3));
+  }
 };
 
 template <int D>
 __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
-  AttnLds<D>& L = *reinterpret_cast<AttnLds<D>*>(phase_smem(smem));
-  constexpr int KS = AttnLds<D>::KS, VS = AttnLds<D>::VS;
-  constexpr int NS = D / 32;   // MFMA k-steps over the head dim
-  constexpr int ND = D / 16;   // output d tiles
+  using L_t = AttnLds<D>;
+  L_t& L = *reinterpret_cast<L_t*>(phase_smem(smem));
+  constexpr int SK = L_t::SK, KS = L_t::KS;
+  constexpr int NS = D / 32;              // MFMA k-steps over the head dim
+  constexpr int ND = D / 16;              // output d tiles
+  constexpr int NKT = SK / 16;            // key tiles per sub-chunk
+  constexpr int NCH = SK * (D / 8) / kThreads;  // 16-byte K (and V) chunks per thread per sub-chunk
+  static_assert(NCH * kThreads == SK * (D / 8), "sub-chunk staging must divide evenly");
   const int lane = lane_id(), wv = wave_id();
   const int grp = p.Hq / p.Hkv;
   const int nitems = p.Hkv * p.attn_nchunks;
@@ -372,60 +385,74 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     if (ke > p.attn_lo + p.attn_nkeys) ke = p.attn_lo + p.attn_nkeys;
     const bool act = wv < grp;
     const int h = g * grp + wv;
-    u32x4 qh[NS], ql[NS];
+    const uint16_t* kg = p.k_cache + (size_t)g * p.kv_cap * D;
+    const uint16_t* vg = p.v_cache + (size_t)g * p.kv_cap * D;
+    // K/V rows of a sub-chunk into registers; rows past the chunk end repeat its last key
+    // (never visible, so never weighted)
+    u32x4 kr[NCH], vr[NCH];
+    auto fetch = [&](int sb) {
+      const int last = ke - 1;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      qh[s] = u32x4{0u, 0u, 0u, 0u};
-      ql[s] = u32x4{0u, 0u, 0u, 0u};
-      if (act && tq < p.T) {
-        const float* qs = p.q_buf + (size_t)tq * p.Hq * D + h * D + 32 * s + 8 * gq;
-        split8(ldgf4(qs), ldgf4(qs + 4), qh[s], ql[s]);
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = threadIdx.x + i * kThreads;
+        const int row = ci / (D / 8), c8 = (ci % (D / 8)) * 8;
+        const int key = sb + row <= last ? sb + row : last;
+        kr[i] = ldg16(kg + (size_t)key * D + c8);
+        vr[i] = ldg16(vg + (size_t)key * D + c8);
       }
+    };
+    fetch(kb);
+    // q of this wave's head as hi + lo (tokens past T repeat token T-1; never stored)
+    u32x4 qh[NS], ql[NS];
+    {
+      const int tqc = tq < p.T ? tq : p.T - 1;
+      const float* qs = p.q_buf + (size_t)tqc * p.Hq * D + (act ? h : 0) * D + 8 * gq;
+      float4 qa[NS], qb[NS];
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        qa[s] = ldgf4(qs + 32 * s);
+        qb[s] = ldgf4(qs + 32 * s + 4);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; ++s) split8(qa[s], qb[s], qh[s], ql[s]);
     }
     float m_run = NEG, l_run = 0.f;
     f32x4 O[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     const int ptok = p.pos + tq;
-    for (int sb = kb; sb < ke; sb += 256) {
-      const int nk = (ke - sb) < 256 ? (ke - sb) : 256;
-      lds_barrier();
-      // stage K (row-major) and V (transposed) of this sub-chunk
-      const uint16_t* kg = p.k_cache + ((size_t)g * p.kv_cap + sb) * D;
-      const uint16_t* vg = p.v_cache + ((size_t)g * p.kv_cap + sb) * D;
-      for (int ci = threadIdx.x; ci < 256 * (D / 8); ci += kThreads) {
+    for (int sb = kb; sb < ke; sb += SK) {
+      const int nk = (ke - sb) < SK ? (ke - sb) : SK;
+      lds_barrier();  // the previous sub-chunk's LDS reads are done
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) {
+        const int ci = threadIdx.x + i * kThreads;
         const int row = ci / (D / 8), c8 = (ci % (D / 8)) * 8;
-        u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-        if (row < nk) {
-          kv = ldg16(kg + (size_t)row * D + c8);
-          vv = ldg16(vg + (size_t)row * D + c8);
-        }
-        *reinterpret_cast<u32x4*>(&L.Ks[row * KS + c8]) = kv;
+        *reinterpret_cast<u32x4*>(&L.Ks[row * KS + c8]) = kr[i];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          L.Vt[(c8 + 2 * j) * VS + row] = (uint16_t)(vv[j] & 0xffffu);
-          L.Vt[(c8 + 2 * j + 1) * VS + row] = (uint16_t)(vv[j] >> 16);
+          L.Vt[L_t::vt_index(c8 + 2 * j, row)] = (uint16_t)(vr[i][j] & 0xffffu);
+          L.Vt[L_t::vt_index(c8 + 2 * j + 1, row)] = (uint16_t)(vr[i][j] >> 16);
         }
       }
       lds_barrier();
+      if (sb + SK < ke) fetch(sb + SK);  // in flight while this sub-chunk is used
       if (act) {
-        f32x4 S[16];
+        f32x4 S[NKT];
 #pragma unroll
-        for (int kt = 0; kt < 16; ++kt) {
+        for (int kt = 0; kt < NKT; ++kt) {
           S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (kt * 16 < nk) {
 #pragma unroll
-            for (int s = 0; s < NS; ++s) {
-              u32x4 ka = *reinterpret_cast<const u32x4*>(&L.Ks[(kt * 16 + tq) * KS + 32 * s + 8 * gq]);
-              S[kt] = mfma16x16x32(ka, qh[s], S[kt]);
-              S[kt] = mfma16x16x32(ka, ql[s], S[kt]);
-            }
+          for (int s = 0; s < NS; ++s) {
+            const u32x4 ka = *reinterpret_cast<const u32x4*>(&L.Ks[(kt * 16 + tq) * KS + 32 * s + 8 * gq]);
+            S[kt] = mfma16x16x32(ka, qh[s], S[kt]);
+            S[kt] = mfma16x16x32(ka, ql[s], S[kt]);
           }
         }
         // mask + scale; lane holds keys kt*16 + 4*gq + r of token tq
         float mx = NEG;
 #pragma unroll
-        for (int kt = 0; kt < 16; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = sb + kt * 16 + 4 * gq + r;
@@ -441,7 +468,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
         const float alpha = none ? 1.f : __expf(m_run - m_new);
         float ls = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < 16; ++kt)
+        for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float e = none ? 0.f : __expf(S[kt][r] - m_new);
@@ -460,23 +487,22 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) O[d][r] *= ao[r];
 #pragma unroll
-        for (int kp = 0; kp < 8; ++kp) {
-          if (kp * 32 < nk) {
-            const u32x2 q0 = split_bf16(S[2 * kp][0], S[2 * kp][1]);
-            const u32x2 q1 = split_bf16(S[2 * kp][2], S[2 * kp][3]);
-            const u32x2 q2 = split_bf16(S[2 * kp + 1][0], S[2 * kp + 1][1]);
-            const u32x2 q3 = split_bf16(S[2 * kp + 1][2], S[2 * kp + 1][3]);
-            const u32x4 ph = {q0[0], q1[0], q2[0], q3[0]};
-            const u32x4 plo = {q0[1], q1[1], q2[1], q3[1]};
+        for (int kp = 0; kp < NKT / 2; ++kp) {
+          const u32x2 q0 = split_bf16(S[2 * kp][0], S[2 * kp][1]);
+          const u32x2 q1 = split_bf16(S[2 * kp][2], S[2 * kp][3]);
+          const u32x2 q2 = split_bf16(S[2 * kp + 1][0], S[2 * kp + 1][1]);
+          const u32x2 q3 = split_bf16(S[2 * kp + 1][2], S[2 * kp + 1][3]);
+          const u32x4 ph = {q0[0], q1[0], q2[0], q3[0]};
+          const u32x4 plo = {q0[1], q1[1], q2[1], q3[1]};
 #pragma unroll
-            for (int d = 0; d < ND; ++d) {
-              const uint16_t* vr = &L.Vt[(16 * d + tq) * VS + kp * 32 + 4 * gq];
-              u32x2 v0 = *reinterpret_cast<const u32x2*>(vr);
-              u32x2 v1 = *reinterpret_cast<const u32x2*>(vr + 16);
-              u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
-              O[d] = mfma16x16x32(ph, vb, O[d]);
-              O[d] = mfma16x16x32(plo, vb, O[d]);
-            }
+          for (int d = 0; d < ND; ++d) {
+            // k slots of this lane: keys 32kp + 4gq + 0..3 and 32kp + 16 + 4gq + 0..3
+            const int dd = 16 * d + tq;
+            const u32x2 v0 = *reinterpret_cast<const u32x2*>(&L.Vt[L_t::vt_index(dd, 32 * kp + 4 * gq)]);
+            const u32x2 v1 = *reinterpret_cast<const u32x2*>(&L.Vt[L_t::vt_index(dd, 32 * kp + 16 + 4 * gq)]);
+            const u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
+            O[d] = mfma16x16x32(ph, vb, O[d]);
+            O[d] = mfma16x16x32(plo, vb, O[d]);
           }
         }
       }
@@ -496,26 +522,27 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   }
 }
 
-// Merge the key-chunk partials of every (token, q head) row -> o (fp32).
+// Merge the key-chunk partials of every (token, q head) row -> o (fp32).  A chunk with no
+// visible key for a token has m = -inf, weight exp(-inf) = 0 and O = l = 0.
 __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
   const int grp = p.Hq / p.Hkv;
   const int total = p.T * p.Hq * p.D;
+  const int nch = p.attn_nchunks;
   for (int e = wg * kThreads + threadIdx.x; e < total; e += p.nwg * kThreads) {
     const int d = e % p.D, h = (e / p.D) % p.Hq, t = e / (p.D * p.Hq);
     const int g = h / grp, w = h % grp;
     float M = -__builtin_inff();
-    for (int c = 0; c < p.attn_nchunks; ++c) {
+    for (int c = 0; c < nch; ++c) {
       const int it = c * p.Hkv + g;
       M = fmaxf(M, gl(p.attn_ml)[((size_t)(it * grp + w) * kMaxT + t) * 2]);
     }
     float num = 0.f, den = 0.f;
-    for (int c = 0; c < p.attn_nchunks; ++c) {
+    for (int c = 0; c < nch; ++c) {
       const int it = c * p.Hkv + g;
-      auto ml = gl(p.attn_ml + ((size_t)(it * grp + w) * kMaxT + t) * 2);
-      if (ml[0] == -__builtin_inff()) continue;
+      const f32x2 ml = *gl(reinterpret_cast<const f32x2*>(p.attn_ml + ((size_t)(it * grp + w) * kMaxT + t) * 2));
       const float wgt = __expf(ml[0] - M);
-      num += wgt * gl(p.attn_o)[((size_t)(it * grp + w) * kMaxT + t) * p.D + d];
-      den += wgt * ml[1];
+      num = fmaf(wgt, gl(p.attn_o)[((size_t)(it * grp + w) * kMaxT + t) * p.D + d], num);
+      den = fmaf(wgt, ml[1], den);
     }
     gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = num / den;
   }
@@ -1023,9 +1050,27 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
   const int rows = GATEUP ? p.I_loc : p.P_loc;
   const bool fp4 = p.expert_dtype == 0;
   const int tpe = fp4 ? rows / 64 : rows / 16;
-  const int U = R.n_active;
-  const int TT = U * tpe;
-  const int t0 = (int)((long)wg * TT / p.nwg), t1 = (int)((long)(wg + 1) * TT / p.nwg);
+  const int U = uniform(R.n_active);
+  // Tiles are split by estimated cost, not by count: a tile of expert u costs A + n_e(u)
+  // units (its weight bytes, plus the per-token work), with A fitted to measured tile times.
+  // Tile (u, j) covers [P_u + j c_u, P_u + (j+1) c_u) with P_u = tpe (A u + sum_{v<u} n_e(v))
+  // = tpe (A u + active_off[u]); a workgroup takes the tiles whose cost interval starts in
+  // its share [wg C / nwg, (wg+1) C / nwg).
+  const int A = GATEUP ? 16 : 9;
+  const long C = (long)tpe * (A * U + uniform(R.active_off[U]));
+  auto first_tile = [&](long c) -> int {  // first tile whose cost interval starts at or after c
+    if (c >= C) return U * tpe;
+    int lo = 0, hi = U - 1;  // largest u with P_u <= c (P_0 = 0 <= c)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if ((long)tpe * (A * mid + uniform(R.active_off[mid])) <= c) lo = mid;
+      else hi = mid - 1;
+    }
+    const long Pu = (long)tpe * (A * lo + uniform(R.active_off[lo]));
+    const int cu = A + uniform(R.active_off[lo + 1]) - uniform(R.active_off[lo]);
+    return lo * tpe + (int)((c - Pu + cu - 1) / cu);
+  };
+  const int t0 = first_tile((long)wg * C / p.nwg), t1 = first_tile((long)(wg + 1) * C / p.nwg);
   for (int t = t0; t < t1;) {
     const int u = t / tpe;
     const int ta = t % tpe;
