@@ -141,6 +141,7 @@ enum CtrlWord {
   kFlag = 32,     // number of the last grid barrier released in this launch
   kTop = 64,      // group leaders arrived (monotonic within a launch)
   kGroup = 96,    // + 32 * g: workgroups of group g arrived (monotonic within a launch)
+  kWork = 352,    // + 32 * i: tiles handed out so far by expert phase i (0 gate/up, 1 down)
   kCtrlWords = 1024
 };
 constexpr int kBarGroups = 8;

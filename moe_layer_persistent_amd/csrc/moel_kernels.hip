@@ -101,6 +101,8 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
       __hip_atomic_store(ctrl + kTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int g = 0; g < kBarGroups; ++g)
         __hip_atomic_store(ctrl + kGroup + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < 2; ++i)
+        __hip_atomic_store(ctrl + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -115,6 +117,11 @@ __global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
   char* smem = moel_lds;
   __shared__ int s_abort;
   const int wg = blockIdx.x;
+  // the expert phases' work counters are free again once both expert kernels have finished
+  // (stream order): the combine kernel clears them for the next call, aborted or not
+  if (PH == kPhCombine && wg == 0 && threadIdx.x == 0)
+    for (int i = 0; i < 2; ++i)
+      __hip_atomic_store(gl(p.ctrl) + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
   __syncthreads();
   if (s_abort) {

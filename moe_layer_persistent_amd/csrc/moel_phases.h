@@ -36,10 +36,11 @@ struct RouteTables {
   int active_e[kMaxT * 8];     // ascending expert ids
   int active_off[kMaxT * 8 + 1];
   int slots[kMaxT * 8];        // slots grouped by expert (ascending), slots ascending within
-  int cnt[512];                // per-expert slot count
-  int off[512];                // per-expert first position in `slots`
-  int rank[512];               // per-expert index into active_e (valid when cnt > 0)
-  unsigned tokmask[kMaxT * 16];  // per token: bitmask of its selected experts (E <= 512)
+  int cnt[512];                // per expert: slots routed to it
+  unsigned tmask[512];         // per expert: bit t set when token t selected it
+  int off[512];                // per expert: first position in `slots`
+  int wave_sum[2][kWaves];     // per-wave totals of the expert scans
+  int next;                    // tile handed out by the work counter (expert phases)
 };
 constexpr int kRouteBytes = (sizeof(RouteTables) + 255) & ~255;
 
@@ -176,7 +177,9 @@ template <int NT, class ASrc>
 __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, const uint8_t* w1_arg,
                                         int K_arg, int t_first_arg, int oct_lo_arg, int oct_hi_arg,
                                         const ASrc A_arg) {
-  constexpr int DEPTH = 4;  // k steps in flight per wave
+  // k steps in flight per wave: 2 keeps ~100 KB per CU in flight, which measured faster than
+  // deeper rings (more outstanding requests per CU lowered the achieved bandwidth)
+  constexpr int DEPTH = 2;
   // the phase scratch of the dynamic LDS, addressed through the LDS symbol (a pointer argument
   // would arrive as a generic address and turn every access into a flat one)
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(moel_lds));
@@ -192,9 +195,11 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (wv < nkw) {
-    const int ns = S / nkw, sa = wv * ns;
+    // k-wave wv takes the steps wv, wv + nkw, ... so that the workgroup's loads in flight
+    // cover one contiguous stretch of each tile
+    const int ns = S / nkw;
     const int tok = (lane & 15) < A.T ? (lane & 15) : A.T - 1;
-    const int kq = 8 * (lane >> 4) + 32 * sa;
+    const int kq = 8 * (lane >> 4) + 32 * wv;
     const uint8_t* base[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -202,14 +207,14 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
       const int oct = 2 * t + ((lane & 15) >> 3);
       const int src_lane = (oct >= oct_lo && oct < oct_hi) ? lane : (lane ^ 8);
       base[j] = (t < tiles0 ? w0 + (size_t)t * S * 1024 : w1 + (size_t)(t - tiles0) * S * 1024) +
-                (size_t)sa * 1024 + src_lane * 16;
+                (size_t)wv * 1024 + src_lane * 16;
     }
     typename ASrc::Raw ra[DEPTH];
     u32x4 rw[DEPTH][NT];
     auto issue = [&](int d, int i) {
-      A.fetch(tok, kq + 32 * i, ra[d]);
+      A.fetch(tok, kq + 32 * nkw * i, ra[d]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) rw[d][j] = ldg_stream(base[j] + (size_t)i * 1024);
+      for (int j = 0; j < NT; ++j) rw[d][j] = ldg_stream(base[j] + (size_t)i * nkw * 1024);
     };
     auto compute = [&](int d) {
       u32x4 a_hi, a_lo;
@@ -609,112 +614,157 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
 // softmax over the selected logits, and per-expert slot lists.  Computed redundantly by
 // every workgroup from the same logits, so all agree bit for bit.
 // ------------------------------------------------------------------------------------------
+// (v, i) <- the better of (v, i) and (ov, oi): larger logit, lower expert index on ties
+// (bitwise operators: short-circuit || / && would become exec-mask branches)
+__device__ __forceinline__ void kv_better(float& v, int& i, float ov, int oi) {
+  const bool take = (ov > v) | ((ov == v) & (oi < i));
+  v = take ? ov : v;
+  i = take ? oi : i;
+}
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void kv_dpp_step(float& v, int& i) {
+  const float ov = __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v),
+                                                                          __builtin_bit_cast(int, v), CTRL,
+                                                                          ROW_MASK, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(i, i, CTRL, ROW_MASK, 0xF, false);
+  kv_better(v, i, ov, oi);
+}
+// Arg-max over each 32-lane half of the wave by DPP (VALU only, no LDS round trips): xor 1 and
+// xor 2 within quads, half-row and row mirrors (row maximum in every lane of the row), then a
+// row-15 broadcast into rows 1 and 3, which leaves the maximum of lanes 0-31 in lane 31 and of
+// lanes 32-63 in lane 63.
+__device__ __forceinline__ void half_argmax(float& v, int& i, float& v_lo, int& i_lo, float& v_hi, int& i_hi) {
+  kv_dpp_step<0xB1, 0xF>(v, i);   // quad_perm [1,0,3,2]
+  kv_dpp_step<0x4E, 0xF>(v, i);   // quad_perm [2,3,0,1]
+  kv_dpp_step<0x141, 0xF>(v, i);  // row_half_mirror
+  kv_dpp_step<0x140, 0xF>(v, i);  // row_mirror
+  kv_dpp_step<0x142, 0xA>(v, i);  // row_bcast15 into rows 1 and 3
+  v_lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+  i_lo = __builtin_amdgcn_readlane(i, 31);
+  v_hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+  i_hi = __builtin_amdgcn_readlane(i, 63);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave by DPP: shifts 1, 2, 4, 8 within each row of
+// 16 lanes, then the row-15 broadcast into rows 1 and 3 and the row-31 broadcast into rows 2
+// and 3 carry the row totals forward.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void scan_dpp_step(int& v) {
+  v += __builtin_amdgcn_update_dpp(0, v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ void wave_inclusive_scan(int& v) {
+  scan_dpp_step<0x111, 0xF>(v);  // row_shr 1
+  scan_dpp_step<0x112, 0xF>(v);  // row_shr 2
+  scan_dpp_step<0x114, 0xF>(v);  // row_shr 4
+  scan_dpp_step<0x118, 0xF>(v);  // row_shr 8
+  scan_dpp_step<0x142, 0xA>(v);  // row_bcast15 into rows 1 and 3
+  scan_dpp_step<0x143, 0xC>(v);  // row_bcast31 into rows 2 and 3
+}
+
 __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool write_debug) {
   const int lane = lane_id(), wv = wave_id();
   const int nslot = p.T * p.topk;
   const float NEG = -__builtin_inff();
-  for (int t = wv; t < p.T; t += kWaves) {
-    float v[8];
-    bool taken[8];
+  const int BIG = 0x7fffffff;
+  static_assert(kThreads == 512, "one thread per expert table entry");
+  R.cnt[threadIdx.x] = 0;
+  R.tmask[threadIdx.x] = 0u;
+  // top-k: wave w takes tokens 2w (lanes 0-31) and 2w + 1 (lanes 32-63) at the same time;
+  // lane l of a half holds experts (l mod 32) + 32 j
+  {
+    const int t = 2 * wv + (lane >> 5);
+    const bool tok_ok = t < p.T;
+    const int tc = tok_ok ? t : 0;
+    float v[16];
+    int ix[16];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int e = lane + 64 * j;
-      v[j] = e < p.E ? gl(p.logits)[t * p.E + e] : NEG;
-      taken[j] = e >= p.E;
+    for (int j = 0; j < 16; ++j) {
+      const int e = (lane & 31) + 32 * j;
+      const bool ok = tok_ok && e < p.E;
+      v[j] = ok ? gl(p.logits)[tc * p.E + (e < p.E ? e : 0)] : NEG;
+      ix[j] = ok ? e : BIG;
     }
-    float sel0 = 0.f, esum = 0.f;
+    float sel0_lo = 0.f, sel0_hi = 0.f, esum = 0.f, ex_r = 0.f;
     for (int r = 0; r < p.topk; ++r) {
-      float bv = NEG;
-      int bi = 0x7fffffff;
+      float bv = v[0];
+      int bi = ix[0];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int e = lane + 64 * j;
-        if (!taken[j] && (bi == 0x7fffffff || v[j] > bv)) {
-          bv = v[j];
-          bi = e;
-        }
+      for (int j = 1; j < 16; ++j) kv_better(bv, bi, v[j], ix[j]);
+      float v_lo, v_hi;
+      int i_lo, i_hi;
+      half_argmax(bv, bi, v_lo, i_lo, v_hi, i_hi);
+      const float wv_ = lane < 32 ? v_lo : v_hi;
+      const int wi = lane < 32 ? i_lo : i_hi;
+      // the owner retires the winner
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const bool hit = ix[j] == wi;
+        v[j] = hit ? NEG : v[j];
+        ix[j] = hit ? BIG : ix[j];
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o);
-        const int oi = __shfl_xor(bi, o);
-        if (oi != 0x7fffffff && (bi == 0x7fffffff || ov > bv || (ov == bv && oi < bi))) {
-          bv = ov;
-          bi = oi;
-        }
+      if (r == 0) {
+        sel0_lo = v_lo;
+        sel0_hi = v_hi;
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        if ((bi & 63) == lane && (bi >> 6) == j) taken[j] = true;
-      if (r == 0) sel0 = bv;
-      const float ex = __expf(bv - sel0);
+      const float ex = __expf(wv_ - (lane < 32 ? sel0_lo : sel0_hi));
       esum += ex;
-      if (lane == 0) {
-        R.idx[t * p.topk + r] = bi;
-        R.gate[t * p.topk + r] = ex;  // normalised below
-      }
+      if ((lane & 31) == r) ex_r = ex;  // lane r of each half keeps the r-th numerator
+      if ((lane & 31) == 0 && tok_ok) R.idx[t * p.topk + r] = wi;
     }
-    if (lane == 0)
-      for (int r = 0; r < p.topk; ++r) R.gate[t * p.topk + r] /= esum;
+    if ((lane & 31) < p.topk && tok_ok) R.gate[t * p.topk + (lane & 31)] = ex_r / esum;
   }
   lds_barrier();
-  // per-expert counts (LDS integer atomics: exact and order-independent) and, per token, a
-  // bitmask of its selected experts
-  for (int e = threadIdx.x; e < p.E; e += kThreads) R.cnt[e] = 0;
-  for (int w = threadIdx.x; w < kMaxT * 16; w += kThreads) R.tokmask[w] = 0u;
-  lds_barrier();
-  for (int s = threadIdx.x; s < nslot; s += kThreads) {
-    const int e = R.idx[s], t = s / p.topk;
+  // slot lists, expert-major with slots ascending within an expert.  Per expert: the count of
+  // its slots and the mask of tokens that chose it (LDS integer atomics, order-independent);
+  // an exclusive scan over the experts gives each expert's first position and, over the
+  // experts with a nonzero count, its rank among the active ones; a slot's position is its
+  // expert's first position plus the number of earlier tokens that chose the same expert
+  // (one token picks an expert at most once, so token order is slot order).
+  const int s = threadIdx.x;
+  if (s < nslot) {
+    const int e = R.idx[s];
     atomicAdd(&R.cnt[e], 1);
-    atomicOr(&R.tokmask[t * 16 + (e >> 5)], 1u << (e & 31));
+    atomicOr(&R.tmask[e], 1u << (s / p.topk));
   }
   lds_barrier();
-  if (wv == 0) {
-    // exclusive scans over experts of (count) and (count > 0): lane owns a contiguous chunk
-    const int per = (p.E + 63) / 64;
-    const int e0 = lane * per;
-    int sc = 0, sa = 0;
-    for (int e = e0; e < e0 + per && e < p.E; ++e) {
-      sc += R.cnt[e];
-      sa += R.cnt[e] > 0;
-    }
-    int ic = sc, ia = sa;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int yc = __shfl_up(ic, o), ya = __shfl_up(ia, o);
-      if (lane >= o) {
-        ic += yc;
-        ia += ya;
-      }
-    }
-    int oc = ic - sc, oa = ia - sa;
-    for (int e = e0; e < e0 + per && e < p.E; ++e) {
-      R.off[e] = oc;
-      R.rank[e] = oa;
-      if (R.cnt[e] > 0) {
-        R.active_e[oa] = e;
-        R.active_off[oa] = oc;
-      }
-      oc += R.cnt[e];
-      oa += R.cnt[e] > 0;
-    }
-    if (lane == 63) {
-      R.n_active = ia;
-      R.active_off[ia] = ic;
-    }
+  const int e = threadIdx.x;  // kThreads >= E (E <= 512)
+  const int c = e < p.E ? R.cnt[e] : 0;
+  int incl_c = c, incl_a = c > 0 ? 1 : 0;
+  wave_inclusive_scan(incl_c);
+  wave_inclusive_scan(incl_a);
+  if (lane == 63) {
+    R.wave_sum[0][wv] = incl_c;
+    R.wave_sum[1][wv] = incl_a;
   }
   lds_barrier();
-  // slot s = (t, kappa) of expert e goes after the slots of e from tokens t' < t
-  for (int s = threadIdx.x; s < nslot; s += kThreads) {
-    const int e = R.idx[s], t = s / p.topk;
-    int r = 0;
-    for (int t2 = 0; t2 < t; ++t2) r += (R.tokmask[t2 * 16 + (e >> 5)] >> (e & 31)) & 1u;
-    R.slots[R.off[e] + r] = s;
+  int base_c = 0, base_a = 0;
+  for (int w = 0; w < wv; ++w) {
+    base_c += R.wave_sum[0][w];
+    base_a += R.wave_sum[1][w];
+  }
+  const int off_e = base_c + incl_c - c;
+  if (e < p.E) {
+    R.off[e] = off_e;
+    if (c > 0) {
+      const int ra = base_a + incl_a - 1;
+      R.active_e[ra] = e;
+      R.active_off[ra] = off_e;
+    }
+  }
+  if (e == kThreads - 1) {
+    R.n_active = base_a + incl_a;
+    R.active_off[base_a + incl_a] = base_c + incl_c;  // == nslot
+  }
+  lds_barrier();
+  if (s < nslot) {
+    const int es = R.idx[s];
+    const int t = s / p.topk;
+    R.slots[R.off[es] + __popc(R.tmask[es] & ((1u << t) - 1u))] = s;
   }
   if (write_debug) {
-    for (int s = threadIdx.x; s < nslot; s += kThreads) {
-      if (p.dbg_idx) gl(p.dbg_idx)[s] = R.idx[s];
-      if (p.dbg_gates) gl(p.dbg_gates)[s] = R.gate[s];
+    for (int s3 = threadIdx.x; s3 < nslot; s3 += kThreads) {
+      if (p.dbg_idx) gl(p.dbg_idx)[s3] = R.idx[s3];
+      if (p.dbg_gates) gl(p.dbg_gates)[s3] = R.gate[s3];
     }
   }
   lds_barrier();
@@ -827,12 +877,14 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
   const int npt = Sp / nkw;
   const bool kw = wv < nkw;
   const size_t tile_bytes = (size_t)36 * K;  // 64 rows of K/2 + K/16 bytes
+  // k-wave wv takes the pairs wv, wv + nkw, wv + 2 nkw, ... of every tile, so that the
+  // workgroup's loads in flight cover one contiguous stretch of the tile
   const uint8_t* wb[NM];
   if (GATEUP) {
-    wb[0] = p.w_gate + (size_t)e * p.stride_gate + (size_t)wv * npt * 2304;
-    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up + (size_t)wv * npt * 2304;
+    wb[0] = p.w_gate + (size_t)e * p.stride_gate + (size_t)wv * 2304;
+    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up + (size_t)wv * 2304;
   } else {
-    wb[0] = p.w_down + (size_t)e * p.stride_down + (size_t)wv * npt * 2304;
+    wb[0] = p.w_down + (size_t)e * p.stride_down + (size_t)wv * 2304;
   }
   // activation rows: lane 4b+i carries token slot 2g + (i & 1); slots past n_e repeat the
   // last one (their products are computed and never read)
@@ -842,7 +894,7 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
     int j = 2 * g + (lane & 1);
     j = j < n_e ? j : n_e - 1;
     const int slot = R.slots[s_lo + j];
-    arow[g] = (GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I) + wv * npt * 64;
+    arow[g] = (GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I) + wv * 64;
   }
   const int stage_tiles = kFp4Stage / (64 * n_e);
   // per-matrix tensor scales, read once (a global load inside the loop would drain the ring)
@@ -894,8 +946,8 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
   auto issue = [&](Fp4Pair<NM, G>& f, int ti, int pr) {
     const uint8_t* wt[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes + (size_t)pr * 2304;
-    fp4_pair_load<NM, G>(f, wt, arow, 64 * pr);
+    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes + (size_t)pr * nkw * 2304;
+    fp4_pair_load<NM, G>(f, wt, arow, 64 * nkw * pr);
   };
   // The run goes in segments of at most stage_tiles tiles; each segment is one pipeline
   // (prologue, steady loop, last chunk) whose outputs are flushed to global memory after it.
@@ -1070,12 +1122,8 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
     const int cu = A + uniform(R.active_off[lo + 1]) - uniform(R.active_off[lo]);
     return lo * tpe + (int)((c - Pu + cu - 1) / cu);
   };
-  const int t0 = first_tile((long)wg * C / p.nwg), t1 = first_tile((long)(wg + 1) * C / p.nwg);
-  for (int t = t0; t < t1;) {
-    const int u = t / tpe;
-    const int ta = t % tpe;
-    int tb = tpe;
-    if ((u + 1) * tpe > t1) tb = t1 - u * tpe;
+  // one run of tiles [ta, tb) of active expert u
+  auto run = [&](int u, int ta, int tb) {
     if (fp4) {
       const int n_e = uniform(R.active_off[u + 1] - R.active_off[u]);
       // ring depth per token-pair count (register budget); npt % DEPTH != 0 only for shapes
@@ -1099,7 +1147,31 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
       DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
       bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
     }
+  };
+  // Static part: the first 7/8 of the cost, split evenly.  Dynamic part: the remaining tiles,
+  // one per grab from a device-wide counter, so that workgroups that run slower (for any
+  // reason: more tokens per tile, a busier XCD) take fewer of them.  Which workgroup computes
+  // a tile does not change its arithmetic, so results stay bitwise reproducible.
+  const long Cs = C - C / 8;
+  const int t0 = first_tile((long)wg * Cs / p.nwg), t1 = first_tile((long)(wg + 1) * Cs / p.nwg);
+  for (int t = t0; t < t1;) {
+    const int u = t / tpe;
+    const int ta = t % tpe;
+    int tb = tpe;
+    if ((u + 1) * tpe > t1) tb = t1 - u * tpe;
+    run(u, ta, tb);
     t = u * tpe + tb;
+  }
+  const int t_dyn = first_tile(Cs), t_end = U * tpe;
+  auto ctr = gl(p.ctrl) + kWork + 32 * (GATEUP ? 0 : 1);
+  for (;;) {
+    if (threadIdx.x == 0)
+      R.next = t_dyn + (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    lds_barrier();
+    const int t = uniform(R.next);
+    lds_barrier();  // R.next is rewritten by the next grab
+    if (t >= t_end) break;
+    run(t / tpe, t % tpe, t % tpe + 1);
   }
 }
 
