@@ -37,6 +37,37 @@ def algorithmic_bytes(w, idx, pos, window, T):
     return dense + U * expert + kv_read + io, U
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources of the library (the counters below belong to one version)."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "moe_layer_persistent_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip", ".cpp")):
+            with open(os.path.join(d, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the fused kernel from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by the same counters on a copy of known size), or None
+    when the summary belongs to another version of the kernel sources."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        f"k_layer_fused_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith((" ", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest() or "traffic_bytes_per_launch" not in kv:
+        return None
+    return {"bytes_per_launch": float(kv["traffic_bytes_per_launch"]), "source": os.path.relpath(path)}
+
+
 def cpu_baseline(w, t, idx, window, budget_s=25.0):
     """The oracle, timed on this host's cores on a bounded sample of the same step: the
     whole attention block and routing for all 16 tokens, plus the expert block for as many
@@ -124,30 +155,41 @@ def main():
     alg_bytes, U = algorithmic_bytes(w, idx, w.pos, window, T)
 
     def timed(fused, steps, warmup):
+        """Back-to-back launches between two events on the launch stream: the average launch
+        duration (us) over the timed region, and the host wall time (s)."""
         for i in range(warmup):
             plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream)
         torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
+        a.record(stream)
+        for i in range(steps):
+            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return a.elapsed_time(b) * 1e3 / steps, wall
+
+    def per_launch(fused, steps):
+        """Event pairs around single launches (spread of launch times; includes dispatch gaps)."""
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
         for i in range(steps):
             evs[i][0].record(stream)
             plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream)
             evs[i][1].record(stream)
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        durs = [a.elapsed_time(b) * 1e3 for a, b in evs]  # us
-        return wall, durs
+        return [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
 
-    wall, durs = timed(True, args.steps, args.warmup)
+    mean_us, wall = timed(True, args.steps, args.warmup)
     st = plan.status()
     assert st == 0, binding.status_string(st)
     ms_per_step = wall * 1e3 / args.steps
-    mean_us = statistics.fmean(durs)
-    med_us = statistics.median(durs)
+    durs = per_launch(True, max(5, args.steps // 2))
     gbps = alg_bytes / (mean_us * 1e-6) / 1e9
+    traffic = measured_traffic(w.name)
     result = {
         "metric": "us per decoder layer at T=16 verify + achieved HBM GB/s (% of peak), 1 GPU",
-        "value": round(med_us, 2),
+        "value": round(mean_us, 2),
         "unit": "us/layer",
         "n_gpus": 1,
         "steps": args.steps,
@@ -163,12 +205,14 @@ def main():
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "window": window, "kv_history": w.pos,
                    "experts": w.n_experts, "top_k": w.top_k, "pooled": w.pooled, "inter": w.inter,
                    "routing": args.routing, "distinct_experts": U, "weight_copies_rotated": 2},
-        "latency_us": {"mean": round(mean_us, 2), "median": round(med_us, 2),
-                       "p10": round(float(np.percentile(durs, 10)), 2),
-                       "p90": round(float(np.percentile(durs, 90)), 2)},
+        "latency_us": {"mean_back_to_back": round(mean_us, 2),
+                       "single_launch_median": round(statistics.median(durs), 2),
+                       "single_launch_p10": round(float(np.percentile(durs, 10)), 2),
+                       "single_launch_p90": round(float(np.percentile(durs, 90)), 2)},
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "frac": round(gbps / PEAK_HBM_GBPS, 4),
+                     "traffic": None if traffic is None else int(traffic["bytes_per_launch"]),
                      "algorithmic_bytes_per_launch": int(alg_bytes),
                      "kernel": "k_layer_fused (one cooperative launch per layer)"},
     }
@@ -199,9 +243,11 @@ def main():
     result["barrier_us"] = {names[i]: {"first_out": round((tsn[:, 16 + i].min() - tsn[:, i - 1].max()) / 100.0, 2),
                                        "last_out": round((tsn[:, 16 + i].max() - tsn[:, i - 1].max()) / 100.0, 2)}
                             for i in range(1, 10)}
+    if traffic is not None:
+        result["roofline"]["traffic_source"] = traffic["source"]
     if not args.no_unfused:
-        _, d2 = timed(False, max(5, args.steps // 2), 2)
-        result["unfused_chain_us"] = {"median": round(statistics.median(d2), 2), "launches": 10}
+        u_us, _ = timed(False, max(5, args.steps // 2), 2)
+        result["unfused_chain_us"] = {"mean_back_to_back": round(u_us, 2), "launches": 10}
     if args.copy_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
