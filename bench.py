@@ -112,6 +112,69 @@ def cpu_baseline(w, t, idx, window, budget_s=25.0):
                       f"{U} distinct experts of the step; fp64 NumPy"}
 
 
+ACCEPTED_PER_STEP = 6.6  # tokens accepted per verify step of 16 (the pages' acceptance length)
+
+
+def stack_bench(steps: int, warmup: int):
+    """One GPU's TP8 share of the 62-layer stack, timed as 62 back-to-back layer launches per
+    verify step (distinct weights per layer, so nothing is warm in the 256 MB last-level cache;
+    each layer's y is the next layer's x).  Returns a dict for the JSON line."""
+    import torch
+    from moe_layer_persistent_amd import binding, synth
+
+    w = synth.WORKLOADS["stack_tp8"]
+    dev = torch.device("cuda")
+    plan = binding.Plan(binding.config_from_workload(w))
+    layers, caches = [], []
+    t_gen = time.perf_counter()
+    x0 = None
+    for l in range(w.n_layers):
+        t = synth.make_layer(w, l, dev)
+        layers.append(plan.pack_layer(t))
+        caches.append((t["k_cache"], t["v_cache"]))
+        if l == 0:
+            x0 = t["x"].contiguous()
+        del t
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    stream = torch.cuda.current_stream()
+    bufs = [x0.clone(), torch.empty_like(x0)]
+
+    def step():
+        bufs[0].copy_(x0)
+        for l in range(w.n_layers):
+            xin, yout = bufs[l % 2], bufs[(l + 1) % 2]
+            plan.layer_decode(layers[l], caches[l][0], caches[l][1], xin, w.pos, w.layer_window(l), yout,
+                              stream=stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    st = plan.status()
+    assert st == 0, binding.status_string(st)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    st = plan.status()
+    assert st == 0, binding.status_string(st)
+    step_us = a.elapsed_time(b) * 1e3 / steps
+    out = {"workload": w.name, "layers": w.n_layers, "global_layers": sum(w.layer_window(l) == 0 for l in range(w.n_layers)),
+           "kv_history": w.pos, "T": w.T, "verify_step_us": round(step_us, 1),
+           "us_per_layer": round(step_us / w.n_layers, 2),
+           "tokens_per_s": round(ACCEPTED_PER_STEP / (step_us * 1e-6), 1),
+           "tokens_per_s_note": f"{ACCEPTED_PER_STEP} accepted tokens per verify step / the 62-layer verify time "
+                                "(one GPU's share; no draft, embedding, LM head or collectives)",
+           "weights_GB": round(sum(lw.nbytes() for lw in layers) / 1e9, 1), "setup_s": round(t_gen, 1),
+           "steps": steps}
+    del layers, caches, bufs
+    plan.close()
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +184,7 @@ def main():
     ap.add_argument("--routing", default="iid")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 62-layer stack timing")
     ap.add_argument("--dump-stamps", default=None, help="write the per-workgroup timestamps (.npy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -254,9 +318,11 @@ def main():
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
+    del copies
+    torch.cuda.empty_cache()
+    if not args.no_stack:
+        result["stack"] = stack_bench(steps=3, warmup=1)
     if not args.no_cpu_baseline:
-        del copies
-        torch.cuda.empty_cache()
         result["cpu_baseline"] = cpu_baseline(w, t, idx, window)
     print(json.dumps(result), flush=True)
 

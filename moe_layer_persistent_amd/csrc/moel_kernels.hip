@@ -216,6 +216,10 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 template <int D>
 size_t attn_lds() { return sizeof(AttnLds<D>); }
 
+constexpr size_t kLdsLimit = 160 * 1024;  // LDS of one CDNA4 compute unit
+static_assert(kRouteBytes + sizeof(Fp4Lds) <= kLdsLimit, "expert-phase LDS exceeds one CU");
+static_assert(kRouteBytes + sizeof(AttnLds<128>) <= kLdsLimit, "attention LDS exceeds one CU");
+
 size_t lds_for_phase(int ph, int D) {
   size_t body = 0;
   switch (ph) {

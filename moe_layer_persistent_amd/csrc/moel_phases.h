@@ -528,26 +528,45 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
 }
 
 // Merge the key-chunk partials of every (token, q head) row -> o (fp32).  A chunk with no
-// visible key for a token has m = -inf, weight exp(-inf) = 0 and O = l = 0.
+// visible key for a token has m = -inf, weight exp(-inf) = 0 and O = l = 0.  One thread per
+// head-dim value; chunks go in groups of 16 whose loads are all in flight together, merged
+// into a running (max, numerator, denominator) with the usual rescale between groups.
 __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
   const int grp = p.Hq / p.Hkv;
   const int total = p.T * p.Hq * p.D;
   const int nch = p.attn_nchunks;
+  constexpr int U = 16;
+  const float NEG = -__builtin_inff();
   for (int e = wg * kThreads + threadIdx.x; e < total; e += p.nwg * kThreads) {
     const int d = e % p.D, h = (e / p.D) % p.Hq, t = e / (p.D * p.Hq);
     const int g = h / grp, w = h % grp;
-    float M = -__builtin_inff();
-    for (int c = 0; c < nch; ++c) {
-      const int it = c * p.Hkv + g;
-      M = fmaxf(M, gl(p.attn_ml)[((size_t)(it * grp + w) * kMaxT + t) * 2]);
-    }
-    float num = 0.f, den = 0.f;
-    for (int c = 0; c < nch; ++c) {
-      const int it = c * p.Hkv + g;
-      const f32x2 ml = *gl(reinterpret_cast<const f32x2*>(p.attn_ml + ((size_t)(it * grp + w) * kMaxT + t) * 2));
-      const float wgt = __expf(ml[0] - M);
-      num = fmaf(wgt, gl(p.attn_o)[((size_t)(it * grp + w) * kMaxT + t) * p.D + d], num);
-      den = fmaf(wgt, ml[1], den);
+    // row (item it, head w, token t) of the partials, item it = c * Hkv + g
+    const size_t row0 = (size_t)(g * grp + w) * kMaxT + t;  // chunk 0
+    const size_t rstep = (size_t)p.Hkv * grp * kMaxT;       // next chunk
+    float M = NEG, num = 0.f, den = 0.f;
+    for (int c0 = 0; c0 < nch; c0 += U) {
+      f32x2 ml[U];
+      float ov[U];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int c = c0 + j < nch ? c0 + j : nch - 1;
+        const size_t row = row0 + (size_t)c * rstep;
+        ml[j] = *gl(reinterpret_cast<const f32x2*>(p.attn_ml + row * 2));
+        ov[j] = gl(p.attn_o)[row * p.D + d];
+      }
+      float Mg = M;
+#pragma unroll
+      for (int j = 0; j < U; ++j) Mg = fmaxf(Mg, ml[j][0]);
+      const float r = M == NEG ? 0.f : __expf(M - Mg);  // rescale of the earlier groups
+      num *= r;
+      den *= r;
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const float wgt = (c0 + j < nch && ml[j][0] != NEG) ? __expf(ml[j][0] - Mg) : 0.f;
+        num = fmaf(wgt, ov[j], num);
+        den = fmaf(wgt, ml[j][1], den);
+      }
+      M = Mg;
     }
     gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = num / den;
   }
@@ -784,21 +803,29 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
 // global store sits between the weight loads of a run.
 constexpr int kFp4RedPer = 32;        // floats per (wave, lane): NM*2*G for NM = 2, G = 8
 constexpr int kFp4Stage = 4096;       // floats (16 KiB): >= 4 tiles of 64 rows x 16 slots
+constexpr int kFp4ActPairs = 64;      // staged activation covers K <= 64 pairs (4096)
+#ifndef MOEL_FP4_STAGE_MIN_TILES
+#define MOEL_FP4_STAGE_MIN_TILES 2
+#endif
+constexpr int kFp4StageMinTiles = MOEL_FP4_STAGE_MIN_TILES;  // shortest run that stages
 struct Fp4Lds {
   float red[kWaves * 64 * kFp4RedPer];
   float stage[kFp4Stage];
+  // staged activation operand of the run's tokens: [g][pair][lane] = the u32x2 (two packed
+  // bf16 pairs: hi or lo) that lane needs for token-pair group g at that 64-k pair
+  u32x2 act[2 * kFp4ActPairs * 64];     // 64 KiB, G <= 2
 };
 
-template <int NM, int G>
+template <int NM, int G, bool ALDS>
 struct Fp4Pair {
   u32x4 c[NM][2];   // codes of the pair's two 32-k steps
   uint32_t sc[NM];  // 4 block scales of the pair
-  float4 a[G];      // activation k0 + 4b .. +3 of the token slot of lane 4b+i (split at use)
+  float4 a[ALDS ? 1 : G];   // global path: activation k0 + 4b .. +3 of lane 4b+i's token slot
+  u32x2 as[ALDS ? G : 1];   // staged path: the split operand words read from LDS
 };
 
-template <int NM, int G>
-__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM],
-                                              const float* const (&arow)[G], int k0) {
+template <int NM, int G, bool ALDS>
+__device__ __forceinline__ void fp4_pair_load_w(Fp4Pair<NM, G, ALDS>& f, const uint8_t* const (&wt)[NM]) {
   const int lane = lane_id();
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -806,12 +833,25 @@ __device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* 
     f.c[m][1] = ldg_stream(wt[m] + 1024 + lane * 16);
     f.sc[m] = ldg_stream32(wt[m] + 2048 + 4 * lane);
   }
-#pragma unroll
-  for (int g = 0; g < G; ++g) f.a[g] = ldgf4(arow[g] + k0 + 4 * (lane >> 2));
 }
 
-template <int H, int J, int NM, int G>
-__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, const u32x2 (&a)[G],
+// activation operand of 64-k pair `pair`: from the staged LDS copy, or (not staged) the raw
+// floats at k = 64 pair + 4 (lane >> 2) of each row in arow
+template <int NM, int G, bool ALDS>
+__device__ __forceinline__ void fp4_pair_load_a(Fp4Pair<NM, G, ALDS>& f, const float* const (&arow)[G],
+                                                const u32x2* act, int pair, int Sp) {
+  const int lane = lane_id();
+  if constexpr (ALDS) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) f.as[g] = act[(g * Sp + pair) * 64 + lane];
+  } else {
+#pragma unroll
+    for (int g = 0; g < G; ++g) f.a[g] = ldgf4(arow[g] + 64 * pair + 4 * (lane >> 2));
+  }
+}
+
+template <int H, int J, int NM, int G, bool ALDS>
+__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G, ALDS>& f, const u32x2 (&a)[G],
                                                f32x4 (&acc)[NM][G]) {
   // block q = 2*H + J (16 k): MFMAs with ABID = 8*H + 4*J + u, u = 0..3
 #pragma unroll
@@ -836,16 +876,18 @@ __device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, const u3
   }
 }
 
-template <int NM, int G>
-__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 (&acc)[NM][G]) {
-  // rows of a 4-lane block: (hi t0, hi t1, lo t0, lo t1) -> lanes with bit 1 set take lo
+// rows of a 4-lane block: (hi t0, hi t1, lo t0, lo t1) -> lanes with bit 1 set take lo
+__device__ __forceinline__ u32x2 fp4_split_operand(float4 v, bool lo_row) {
+  const u32x2 s01 = split_bf16(v.x, v.y), s23 = split_bf16(v.z, v.w);
+  return lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
+}
+
+template <int NM, int G, bool ALDS>
+__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G, ALDS>& f, f32x4 (&acc)[NM][G]) {
   const bool lo_row = (lane_id() & 2) != 0;
   u32x2 a[G];
 #pragma unroll
-  for (int g = 0; g < G; ++g) {
-    const u32x2 s01 = split_bf16(f.a[g].x, f.a[g].y), s23 = split_bf16(f.a[g].z, f.a[g].w);
-    a[g] = lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
-  }
+  for (int g = 0; g < G; ++g) a[g] = ALDS ? f.as[g] : fp4_split_operand(f.a[g], lo_row);
   fp4_mfma_block<0, 0>(f, a, acc);
   fp4_mfma_block<0, 1>(f, a, acc);
   fp4_mfma_block<1, 0>(f, a, acc);
@@ -859,8 +901,11 @@ __device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 
 // stream them through a ring of DEPTH register buffers that runs across tile boundaries.
 // The steady-state loop holds no branch around a load and no global store, so the only
 // memory wait in it is the one for the oldest ring entry.
-template <bool GATEUP, int G, int DEPTH>
+// ALDS: the run first stages its tokens' activation in LDS, already split into the per-lane
+// operand words, so that the loop's only global loads are weights (G <= 2, K <= 4096).
+template <bool GATEUP, int G, int DEPTH, bool ALDS>
 __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, int tb_arg) {
+  static_assert(!ALDS || G <= 2, "the staged activation holds two token pairs");
   KP& p = params_from(ph);
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int RW = NM * 2 * G;  // red floats per lane
@@ -894,7 +939,7 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
     int j = 2 * g + (lane & 1);
     j = j < n_e ? j : n_e - 1;
     const int slot = R.slots[s_lo + j];
-    arow[g] = (GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I) + wv * 64;
+    arow[g] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
   }
   const int stage_tiles = kFp4Stage / (64 * n_e);
   // per-matrix tensor scales, read once (a global load inside the loop would drain the ring)
@@ -942,31 +987,74 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
     }
     if (!DB) lds_barrier();  // red is rewritten at the next tile end
   };
-  Fp4Pair<NM, G> ring[DEPTH];
-  auto issue = [&](Fp4Pair<NM, G>& f, int ti, int pr) {
+  Fp4Pair<NM, G, ALDS> ring[DEPTH];
+  auto issue_w = [&](Fp4Pair<NM, G, ALDS>& f, int ti, int pr) {
     const uint8_t* wt[NM];
 #pragma unroll
     for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes + (size_t)pr * nkw * 2304;
-    fp4_pair_load<NM, G>(f, wt, arow, 64 * nkw * pr);
+    fp4_pair_load_w<NM, G, ALDS>(f, wt);
+  };
+  // wave wv's local pair pr is the tile's pair wv + nkw pr
+  auto issue_a = [&](Fp4Pair<NM, G, ALDS>& f, int pr) {
+    fp4_pair_load_a<NM, G, ALDS>(f, arow, L.act, wv + nkw * pr, Sp);
+  };
+  auto issue = [&](Fp4Pair<NM, G, ALDS>& f, int ti, int pr) {
+    issue_w(f, ti, pr);
+    issue_a(f, pr);
   };
   // The run goes in segments of at most stage_tiles tiles; each segment is one pipeline
   // (prologue, steady loop, last chunk) whose outputs are flushed to global memory after it.
   for (int sa = ta; sa < tb; sa += stage_tiles) {
     const int sb = tb - sa < stage_tiles ? tb : sa + stage_tiles;
+    // DEPTH <= npt: the first DEPTH pairs all lie in tile sa.  Weights first, so that their
+    // loads are in flight while the activation is staged.
     if (kw) {
-      // DEPTH <= npt: the first DEPTH pairs all lie in tile sa
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        issue(ring[d], sa, d);
+        issue_w(ring[d], sa, d);
         sched_fence();
       }
+    }
+    if (ALDS && sa == ta) {
+      // Lane 4b + i of pair P, group g takes token slot 2g + (i & 1) at k = 64 P + 4b, hi
+      // words for i < 2 and lo words for i >= 2; one item (g, P, b, i & 1) fills both.
+      constexpr int kIt = G * kFp4ActPairs * 32 / kThreads;
+      const int n = G * Sp * 32;
+      float4 v[kIt];
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) {  // all loads first (clamped, so none is conditional)
+        int x = threadIdx.x + i * kThreads;
+        x = x < n ? x : n - 1;
+        const int par = x & 1, b = (x >> 1) & 15, P = (x >> 5) % Sp, g = (x >> 5) / Sp;
+        int j = 2 * g + par;
+        j = j < n_e ? j : n_e - 1;
+        const int slot = R.slots[s_lo + j];
+        const float* src = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
+        v[i] = ldgf4(src + 64 * P + 4 * b);
+      }
+#pragma unroll
+      for (int i = 0; i < kIt; ++i) {
+        const int x = threadIdx.x + i * kThreads;
+        if (x < n) {
+          const int par = x & 1, b = (x >> 1) & 15, P = (x >> 5) % Sp, g = (x >> 5) / Sp;
+          const u32x2 s01 = split_bf16(v[i].x, v[i].y), s23 = split_bf16(v[i].z, v[i].w);
+          u32x2* dst = L.act + (g * Sp + P) * 64 + 4 * b + par;
+          dst[0] = u32x2{s01[0], s23[0]};
+          dst[2] = u32x2{s01[1], s23[1]};
+        }
+      }
+      lds_barrier();
+    }
+    if (kw) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) issue_a(ring[d], d);
       int ct = 0, cp = 0;           // local tile / pair of the chunk being computed
       int it = sa, ip = DEPTH;      // tile / pair of the chunk being issued
       if (ip == npt) { ip = 0; ++it; }
       while (it < sb) {
 #pragma unroll
         for (int d = 0; d < DEPTH; ++d) {
-          fp4_pair_compute<NM, G>(ring[d], acc);
+          fp4_pair_compute<NM, G, ALDS>(ring[d], acc);
           issue(ring[d], it, ip + d);
           sched_fence();
         }
@@ -980,7 +1068,7 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
         }
       }
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) fp4_pair_compute<NM, G>(ring[d], acc);
+      for (int d = 0; d < DEPTH; ++d) fp4_pair_compute<NM, G, ALDS>(ring[d], acc);
       tile_end(sb - sa - 1);
     } else {
       // waves without k work only take part in the reductions
@@ -1131,17 +1219,21 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
       const int Sp = (GATEUP ? p.P : p.I) >> 6;
       const int npt = Sp / kwaves_for(Sp);
       constexpr int D1 = GATEUP ? 4 : 8;
+      // staged activation: runs of several tiles over one or two token pairs
+      const bool st = Sp <= kFp4ActPairs && tb - ta >= kFp4StageMinTiles;
       if (n_e <= 2) {
-        if (npt % D1 == 0) fp4_expert_run<GATEUP, 1, D1>(params_handle(p), u, ta, tb);
-        else fp4_expert_run<GATEUP, 1, 1>(params_handle(p), u, ta, tb);
+        if (npt % D1 != 0) fp4_expert_run<GATEUP, 1, 1, false>(params_handle(p), u, ta, tb);
+        else if (st) fp4_expert_run<GATEUP, 1, D1, true>(params_handle(p), u, ta, tb);
+        else fp4_expert_run<GATEUP, 1, D1, false>(params_handle(p), u, ta, tb);
       } else if (n_e <= 4) {
-        if (npt % 4 == 0) fp4_expert_run<GATEUP, 2, 4>(params_handle(p), u, ta, tb);
-        else fp4_expert_run<GATEUP, 2, 1>(params_handle(p), u, ta, tb);
+        if (npt % 4 != 0) fp4_expert_run<GATEUP, 2, 1, false>(params_handle(p), u, ta, tb);
+        else if (st) fp4_expert_run<GATEUP, 2, 4, true>(params_handle(p), u, ta, tb);
+        else fp4_expert_run<GATEUP, 2, 4, false>(params_handle(p), u, ta, tb);
       } else if (n_e <= 8) {
-        if (npt % 2 == 0) fp4_expert_run<GATEUP, 4, 2>(params_handle(p), u, ta, tb);
-        else fp4_expert_run<GATEUP, 4, 1>(params_handle(p), u, ta, tb);
+        if (npt % 2 == 0) fp4_expert_run<GATEUP, 4, 2, false>(params_handle(p), u, ta, tb);
+        else fp4_expert_run<GATEUP, 4, 1, false>(params_handle(p), u, ta, tb);
       } else {
-        fp4_expert_run<GATEUP, 8, 1>(params_handle(p), u, ta, tb);
+        fp4_expert_run<GATEUP, 8, 1, false>(params_handle(p), u, ta, tb);
       }
     } else {
       DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
