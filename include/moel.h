@@ -46,7 +46,8 @@ typedef enum moel_status {
   MOEL_ERR_HIP = -4,         /* a HIP runtime call failed                               */
   MOEL_ERR_TIMEOUT = -5,     /* a device-side wait exceeded its bound (plan status)     */
   MOEL_ERR_ABORTED = -6,     /* the plan's abort word was set (plan status)             */
-  MOEL_ERR_UNSUPPORTED = -7  /* no suitable device (not gfx950 / no cooperative launch) */
+  MOEL_ERR_UNSUPPORTED = -7, /* no suitable device (not gfx950 / no cooperative launch) */
+  MOEL_ERR_INTERNAL = -8     /* a device-side consistency check failed (plan status)     */
 } moel_status;
 
 typedef enum moel_expert_dtype {
@@ -141,7 +142,7 @@ moel_status moel_plan_destroy(moel_plan* plan);
 int32_t moel_plan_workgroups(const moel_plan* plan);
 
 /* Reads the device-side status word (blocks until `plan`'s work on the device is done):
- * MOEL_OK, MOEL_ERR_TIMEOUT or MOEL_ERR_ABORTED.  A non-OK status is cleared (and the
+ * MOEL_OK, MOEL_ERR_TIMEOUT, MOEL_ERR_ABORTED or MOEL_ERR_INTERNAL.  A non-OK status is cleared (and the
  * plan's barrier words reset) by this call. */
 moel_status moel_plan_status(moel_plan* plan);
 

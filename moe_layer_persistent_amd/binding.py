@@ -22,6 +22,7 @@ MOEL_ERR_HIP = -4
 MOEL_ERR_TIMEOUT = -5
 MOEL_ERR_ABORTED = -6
 MOEL_ERR_UNSUPPORTED = -7
+MOEL_ERR_INTERNAL = -8
 MOEL_EXPERT_NVFP4 = 0
 MOEL_EXPERT_BF16 = 1
 MOEL_N_STAMPS = 32

@@ -25,6 +25,9 @@ def build(verbose: bool = False) -> str:
     ker_obj = os.path.join(objdir, "moel_kernels.o")
     cmd_ker = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               # a single-lane atomic keeps its result where it is used instead of being
+               # broadcast to the wave right away (which would wait for every load in flight)
+               "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
                "-Wno-unused-result", "-Wno-unused-value", "-I", INCLUDE, "-I", CSRC, "-c",
                os.path.join(CSRC, "moel_kernels.hip"), "-o", ker_obj]
     cmd_link = [HIPCC, "-shared", "-fPIC", ker_obj, val_obj, "-o", LIB + ".tmp"]

@@ -57,6 +57,14 @@ __device__ __forceinline__ uint16_t f2bf(float f) { return (uint16_t)(pack2bf(f,
 __device__ __forceinline__ float bf2f(uint16_t h) { return __builtin_bit_cast(float, (uint32_t)h << 16); }
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+// element c of a row in the split-operand layout: quad c/4 holds 4 bf16 of the nearest
+// values, then 4 bf16 of the remainders
+template <class Ptr>
+__device__ __forceinline__ void store_split(Ptr row, int c, float v) {
+  const uint16_t h = f2bf(v);
+  row[(c >> 2) * 8 + (c & 3)] = h;
+  row[(c >> 2) * 8 + 4 + (c & 3)] = f2bf(v - bf2f(h));
+}
 // two fp32 values -> {packed bf16 (nearest), packed bf16 of the remainders}
 __device__ __forceinline__ u32x2 split_bf16(float a, float b) {
   const uint32_t h = pack2bf(a, b);

@@ -349,6 +349,8 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   const size_t o_pl = take((size_t)kMaxT * P * 4);
   const size_t o_a = take((size_t)kMaxT * k * I * 4);
   const size_t o_d = take((size_t)kMaxT * k * P * 4);
+  const size_t o_pls = take((size_t)kMaxT * P * 4);
+  const size_t o_as = take((size_t)kMaxT * k * I * 4);
   const size_t o_m = take((size_t)kMaxT * P * 4);
   const size_t o_cos = take((size_t)cfg->kv_capacity * (D / 2) * 4);
   const size_t o_sin = take((size_t)cfg->kv_capacity * (D / 2) * 4);
@@ -426,6 +428,8 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.pl = reinterpret_cast<float*>(ws + o_pl);
   b.a_buf = reinterpret_cast<float*>(ws + o_a);
   b.d_buf = reinterpret_cast<float*>(ws + o_d);
+  b.pl_split = reinterpret_cast<uint16_t*>(ws + o_pls);
+  b.a_split = reinterpret_cast<uint16_t*>(ws + o_as);
   b.m_buf = reinterpret_cast<float*>(ws + o_m);
   b.rope_cos = reinterpret_cast<const float*>(ws + o_cos);
   b.rope_sin = reinterpret_cast<const float*>(ws + o_sin);
@@ -483,7 +487,7 @@ moel_status moel_plan_status(moel_plan* plan) {
   for (int i = 0; i < kCtrlWords; ++i) words[i] = 0;
   words[kAbort] = keep_abort;
   if (!hip_ok(hipMemcpy(plan->base.ctrl, words, sizeof(words), hipMemcpyHostToDevice))) return MOEL_ERR_HIP;
-  return status == MOEL_DEV_TIMEOUT ? MOEL_ERR_TIMEOUT : MOEL_ERR_ABORTED;
+  return status == MOEL_DEV_TIMEOUT ? MOEL_ERR_TIMEOUT : status == MOEL_DEV_ORDER ? MOEL_ERR_INTERNAL : MOEL_ERR_ABORTED;
 }
 
 moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes) {

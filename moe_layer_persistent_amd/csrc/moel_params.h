@@ -6,6 +6,7 @@
 #define MOEL_N_STAMPS_DEV 32
 #define MOEL_DEV_TIMEOUT 1u
 #define MOEL_DEV_ABORTED 2u
+#define MOEL_DEV_ORDER 3u    /* a workgroup-internal hand-out was read before it was published */
 
 namespace moel {
 
@@ -68,6 +69,10 @@ struct LayerParams {
   float* logits;    // [16][E]
   float* pl;        // [16][P]
   float* a_buf;     // [16*topk][I]
+  // pl and a_buf again as the hi/lo bf16 operands of the NVFP4 expert MFMAs: per 4-element
+  // quad, 4 bf16 of the nearest values then 4 bf16 of the remainders (16 bytes)
+  uint16_t* pl_split;  // [16][P/4][8]
+  uint16_t* a_split;   // [16*topk][I/4][8]
   float* d_buf;     // [16*topk][P]
   float* m_buf;     // [16][P]
   unsigned* ctrl;   // barrier counter, exit counter, status, abort

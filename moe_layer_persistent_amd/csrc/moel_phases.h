@@ -40,7 +40,10 @@ struct RouteTables {
   unsigned tmask[512];         // per expert: bit t set when token t selected it
   int off[512];                // per expert: first position in `slots`
   int wave_sum[2][kWaves];     // per-wave totals of the expert scans
-  int next;                    // tile handed out by the work counter (expert phases)
+  int next;                    // tile handed out by the work counter (bf16 expert phases)
+  float ts[3][512];            // per expert: NVFP4 tensor scales of gate, up, down
+  int dq[64];                  // NVFP4 expert phases: dynamic tiles handed to this workgroup,
+                               // (sequence << 16) | tile, slot = sequence mod 64
 };
 constexpr int kRouteBytes = (sizeof(RouteTables) + 255) & ~255;
 
@@ -623,6 +626,7 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
                     if (p.dbg_logits) gl(p.dbg_logits)[t * p.E + n] = v;
                   } else {
                     gl(p.pl)[(size_t)t * p.P + (n - p.E)] = v;
+                    store_split(gl(p.pl_split) + (size_t)t * p.P * 2, n - p.E, v);
                   }
                 }
               });
@@ -688,6 +692,12 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
   static_assert(kThreads == 512, "one thread per expert table entry");
   R.cnt[threadIdx.x] = 0;
   R.tmask[threadIdx.x] = 0u;
+  if (p.expert_dtype == 0) {  // weights, independent of the step: issued beside the logits
+    for (int i = threadIdx.x; i < 3 * p.E; i += kThreads) {
+      const int m = i / p.E, e = i - m * p.E;
+      R.ts[m][e] = gl(m == 0 ? p.ts_gate : m == 1 ? p.ts_up : p.ts_down)[e];
+    }
+  }
   // top-k: wave w takes tokens 2w (lanes 0-31) and 2w + 1 (lanes 32-63) at the same time;
   // lane l of a half holds experts (l mod 32) + 32 j
   {
@@ -798,34 +808,34 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
 // ------------------------------------------------------------------------------------------
 // LDS of the NVFP4 expert phases.  red: per-wave partial sums of a tile, [wave][lane][RW]
 // floats with RW = NM*2*G; double-buffered by tile parity when two buffers fit (RW <= 16),
-// so that one barrier per tile suffices.  stage: finished outputs of the current run of
-// tiles, written to global memory when the run ends (or the stage is full), so that no
-// global store sits between the weight loads of a run.
+// so that one barrier per tile suffices.  stage: finished outputs of the stream's tiles in
+// stream order, 64 rows x 2G slots per tile, written to global memory when the stream ends
+// (no global store sits between the weight loads); st_tile: the tile of each stage entry.
 constexpr int kFp4RedPer = 32;        // floats per (wave, lane): NM*2*G for NM = 2, G = 8
-constexpr int kFp4Stage = 4096;       // floats (16 KiB): >= 4 tiles of 64 rows x 16 slots
-constexpr int kFp4ActPairs = 64;      // staged activation covers K <= 64 pairs (4096)
-#ifndef MOEL_FP4_STAGE_MIN_TILES
-#define MOEL_FP4_STAGE_MIN_TILES 2
-#endif
-constexpr int kFp4StageMinTiles = MOEL_FP4_STAGE_MIN_TILES;  // shortest run that stages
+constexpr int kFp4Stage = 8192;       // floats (32 KiB): 64 tiles of one token pair
+constexpr int kFp4MaxStaged = kFp4Stage / 128;
 struct Fp4Lds {
   float red[kWaves * 64 * kFp4RedPer];
   float stage[kFp4Stage];
-  // staged activation operand of the run's tokens: [g][pair][lane] = the u32x2 (two packed
-  // bf16 pairs: hi or lo) that lane needs for token-pair group g at that 64-k pair
-  u32x2 act[2 * kFp4ActPairs * 64];     // 64 KiB, G <= 2
+  int st_tile[kFp4MaxStaged];
 };
 
-template <int NM, int G, bool ALDS>
+template <int NM, int G>
 struct Fp4Pair {
   u32x4 c[NM][2];   // codes of the pair's two 32-k steps
   uint32_t sc[NM];  // 4 block scales of the pair
-  float4 a[ALDS ? 1 : G];   // global path: activation k0 + 4b .. +3 of lane 4b+i's token slot
-  u32x2 as[ALDS ? G : 1];   // staged path: the split operand words read from LDS
+  u32x2 a[G];       // activation operand: 4 bf16 (hi or lo) of lane 4b+i's token slot
 };
 
-template <int NM, int G, bool ALDS>
-__device__ __forceinline__ void fp4_pair_load_w(Fp4Pair<NM, G, ALDS>& f, const uint8_t* const (&wt)[NM]) {
+// Activation operands come from the split-operand copy of the activation (per 4-element
+// quad: 4 bf16 nearest values, then 4 bf16 remainders).  row0[g]: split row of token slot 2g,
+// dr[g]: offset (bf16 units) of slot 2g+1's row from it, both uniform; lane 4b+i reads quad
+// b of the pair from the row of slot 2g + (i & 1), the nearest half for i < 2 and the
+// remainder half for i >= 2.  Plain arithmetic, so that no per-lane choice between registers
+// is made through memory.
+template <int NM, int G>
+__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM],
+                                              const uint16_t* const (&row0)[G], const long (&dr)[G], int k0) {
   const int lane = lane_id();
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -833,25 +843,16 @@ __device__ __forceinline__ void fp4_pair_load_w(Fp4Pair<NM, G, ALDS>& f, const u
     f.c[m][1] = ldg_stream(wt[m] + 1024 + lane * 16);
     f.sc[m] = ldg_stream32(wt[m] + 2048 + 4 * lane);
   }
-}
-
-// activation operand of 64-k pair `pair`: from the staged LDS copy, or (not staged) the raw
-// floats at k = 64 pair + 4 (lane >> 2) of each row in arow
-template <int NM, int G, bool ALDS>
-__device__ __forceinline__ void fp4_pair_load_a(Fp4Pair<NM, G, ALDS>& f, const float* const (&arow)[G],
-                                                const u32x2* act, int pair, int Sp) {
-  const int lane = lane_id();
-  if constexpr (ALDS) {
+  const int lane_off = 8 * (lane >> 2) + 4 * ((lane >> 1) & 1);
 #pragma unroll
-    for (int g = 0; g < G; ++g) f.as[g] = act[(g * Sp + pair) * 64 + lane];
-  } else {
-#pragma unroll
-    for (int g = 0; g < G; ++g) f.a[g] = ldgf4(arow[g] + 64 * pair + 4 * (lane >> 2));
+  for (int g = 0; g < G; ++g) {
+    const long off = (lane & 1) ? dr[g] : 0l;
+    f.a[g] = ldg8(row0[g] + off + 2 * k0 + lane_off);
   }
 }
 
-template <int H, int J, int NM, int G, bool ALDS>
-__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G, ALDS>& f, const u32x2 (&a)[G],
+template <int H, int J, int NM, int G>
+__device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G>& f, const u32x2 (&a)[G],
                                                f32x4 (&acc)[NM][G]) {
   // block q = 2*H + J (16 k): MFMAs with ABID = 8*H + 4*J + u, u = 0..3
 #pragma unroll
@@ -876,86 +877,143 @@ __device__ __forceinline__ void fp4_mfma_block(const Fp4Pair<NM, G, ALDS>& f, co
   }
 }
 
-// rows of a 4-lane block: (hi t0, hi t1, lo t0, lo t1) -> lanes with bit 1 set take lo
-__device__ __forceinline__ u32x2 fp4_split_operand(float4 v, bool lo_row) {
-  const u32x2 s01 = split_bf16(v.x, v.y), s23 = split_bf16(v.z, v.w);
-  return lo_row ? u32x2{s01[1], s23[1]} : u32x2{s01[0], s23[0]};
-}
-
-template <int NM, int G, bool ALDS>
-__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G, ALDS>& f, f32x4 (&acc)[NM][G]) {
-  const bool lo_row = (lane_id() & 2) != 0;
-  u32x2 a[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) a[g] = ALDS ? f.as[g] : fp4_split_operand(f.a[g], lo_row);
+// rows of a 4-lane block: (hi t0, hi t1, lo t0, lo t1)
+template <int NM, int G>
+__device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 (&acc)[NM][G]) {
+  const u32x2 (&a)[G] = f.a;
   fp4_mfma_block<0, 0>(f, a, acc);
   fp4_mfma_block<0, 1>(f, a, acc);
   fp4_mfma_block<1, 0>(f, a, acc);
   fp4_mfma_block<1, 1>(f, a, acc);
 }
 
-// One expert's run of 64-row tiles [ta, tb) for this workgroup.
-//   GATEUP: NM = 2, activation = pl rows of the expert's tokens, out a = silu(g) * u
-//   else  : NM = 1, activation = a rows of the expert's slots,   out d
-// The k-waves split each tile's K/64 pairs evenly (npt pairs each, npt % DEPTH == 0) and
-// stream them through a ring of DEPTH register buffers that runs across tile boundaries.
-// The steady-state loop holds no branch around a load and no global store, so the only
-// memory wait in it is the one for the oldest ring entry.
-// ALDS: the run first stages its tokens' activation in LDS, already split into the per-lane
-// operand words, so that the loop's only global loads are weights (G <= 2, K <= 4096).
-template <bool GATEUP, int G, int DEPTH, bool ALDS>
-__device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, int tb_arg) {
-  static_assert(!ALDS || G <= 2, "the staged activation holds two token pairs");
+// token-pair group that an expert with n_e slots needs
+__device__ __forceinline__ int fp4_group(int n_e) { return n_e <= 2 ? 1 : n_e <= 4 ? 2 : n_e <= 8 ? 4 : 8; }
+
+constexpr int kDqEnd = 0xffff;  // tile field of a hand-out past the last tile
+// Hand-outs stay in the ring until every k-wave has read them (at most two are live).
+constexpr int kDqSlots = 64;
+static_assert(sizeof(RouteTables::dq) == kDqSlots * sizeof(int), "hand-out ring size");
+
+// Tile stream of an NVFP4 expert phase.  The workgroup computes, in order, the 64-row tiles
+// of the stream's positions: static positions 0 .. te-ts-1 are tiles ts .. te-1 (global tile
+// order: active expert major), later positions are dynamic tiles k0, k0+1, ... handed to the
+// workgroup by the device-wide work counter.  One ring of DEPTH register buffers runs over the
+// whole stream, across tile and expert boundaries: the k-waves split each tile's K/64 pairs
+// evenly (npt each; wave wv takes pairs wv, wv + nkw, ...), and the ring holds the next
+// DEPTH pairs of every k-wave, so no tile or hand-out boundary drains it.  The k-waves meet
+// at one LDS barrier per tile, where the tile is reduced.  Wave 0 requests the hand-out of
+// position s+1 when its loads enter position s and publishes it in the LDS ring `dq` before
+// the next barrier; every wave passes that barrier before its loads reach s+1 (the stream's
+// start barrier covers s = 1), so a hand-out is always published before it is read.
+// The stream ends before a tile that needs a larger token group than G, when the stage is
+// full, or at the end of the work.  Return: -1 when the work is done; a static tile to resume
+// from (>= 0); or -(2 + k) to resume at dynamic position k (handed out and published in dq).
+template <bool GATEUP, int G, int DEPTH>
+__device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_arg, int k0_arg, int tdyn_arg) {
   KP& p = params_from(ph);
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int RW = NM * 2 * G;  // red floats per lane
+  constexpr bool DB = 2 * RW <= kFp4RedPer;
+  constexpr int SPT = 64 * 2 * G;          // stage floats per tile
+  constexpr int MAXT = kFp4Stage / SPT;    // tiles per stream
   RouteTables& R = route_tables(moel_lds);
   Fp4Lds& L = *reinterpret_cast<Fp4Lds*>(phase_smem(moel_lds));
-  const int u = uniform(u_arg), ta = uniform(ta_arg), tb = uniform(tb_arg);
+  const int ts = uniform(ts_arg), k0 = uniform(k0_arg), t_dyn = uniform(tdyn_arg);
+  const int n_st = uniform(te_arg) - ts;
   const int lane = lane_id(), wv = wave_id();
-  const int e = uniform(R.active_e[u]);
-  const int s_lo = uniform(R.active_off[u]);
-  const int n_e = uniform(R.active_off[u + 1]) - s_lo;
+  const int tpe = (GATEUP ? p.I_loc : p.P_loc) >> 6;
+  const int t_end = uniform(R.n_active) * tpe;
   const int K = GATEUP ? p.P : p.I;
   const int Sp = K >> 6;  // 64-k pairs (K % 128 == 0)
   const int nkw = kwaves_for(Sp);
   const int npt = Sp / nkw;
   const bool kw = wv < nkw;
   const size_t tile_bytes = (size_t)36 * K;  // 64 rows of K/2 + K/16 bytes
-  // k-wave wv takes the pairs wv, wv + nkw, wv + 2 nkw, ... of every tile, so that the
-  // workgroup's loads in flight cover one contiguous stretch of the tile
-  const uint8_t* wb[NM];
-  if (GATEUP) {
-    wb[0] = p.w_gate + (size_t)e * p.stride_gate + (size_t)wv * 2304;
-    wb[NM - 1] = p.w_up + (size_t)e * p.stride_up + (size_t)wv * 2304;
-  } else {
-    wb[0] = p.w_down + (size_t)e * p.stride_down + (size_t)wv * 2304;
-  }
-  // activation rows: lane 4b+i carries token slot 2g + (i & 1); slots past n_e repeat the
-  // last one (their products are computed and never read)
-  const float* arow[G];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    int j = 2 * g + (lane & 1);
-    j = j < n_e ? j : n_e - 1;
-    const int slot = R.slots[s_lo + j];
-    arow[g] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
-  }
-  const int stage_tiles = kFp4Stage / (64 * n_e);
-  // per-matrix tensor scales, read once (a global load inside the loop would drain the ring)
-  const float ts0 = GATEUP ? gl(p.ts_gate)[e] : gl(p.ts_down)[e];
-  const float ts1 = GATEUP ? gl(p.ts_up)[e] : 0.f;
 
+  // Tile of position s.  A hand-out found missing (it cannot be, see above) ends the stream
+  // with an error status instead of waiting.
+  auto tile_at = [&](int s) -> int {
+    if (s < n_st) return ts + s;
+    const int k = k0 + s - n_st;
+    const int v = uniform(R.dq[k & (kDqSlots - 1)]);
+    if ((v >> 16) != k) {
+      if (threadIdx.x == 0)
+        __hip_atomic_store(gl(p.ctrl) + kStatus, (unsigned)MOEL_DEV_ORDER, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return kDqEnd;
+    }
+    return v & 0xffff;
+  };
+
+  // ---- hand-outs (wave 0): requested when the loads enter a position, published later
+  bool gpend = false;
+  unsigned gv = 0u;
+  int is = 0;  // position whose pairs are being issued
+  auto request = [&]() {  // for position is + 1
+    if (wv == 0 && is + 1 >= n_st) {
+      if (lane == 0) gv = __hip_atomic_fetch_add(gl(p.ctrl) + kWork + 32 * (GATEUP ? 0 : 1), 1u,
+                                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      gpend = true;
+    }
+  };
+  auto publish = [&]() {
+    if (gpend) {
+      if (lane == 0) {
+        const int k = k0 + is + 1 - n_st;
+        const unsigned t = (unsigned)t_dyn + gv;
+        R.dq[k & (kDqSlots - 1)] = (k << 16) | (t < (unsigned)t_end ? (int)t : kDqEnd);
+      }
+      gpend = false;
+    }
+  };
+
+  // ---- issue side: the position's expert (u, e, slots) and tile j within it, all uniform.
+  // Moving to the next static tile of the same expert is a pointer increment; the expert's
+  // tables are read only when the expert changes.
+  int iu = -1, ij = 0, ie = 0, ine = 1;
+  const uint8_t* wb[NM];
+  const uint16_t* row0[G];
+  long dr[G];
+  auto set_expert = [&](int u) {
+    iu = u;
+    ie = uniform(R.active_e[u]);
+    const int s_lo = uniform(R.active_off[u]);
+    ine = uniform(R.active_off[u + 1]) - s_lo;
+    const int rstride = GATEUP ? p.P : p.I;
+    // slots past n_e repeat the last one (their products are computed and never read)
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int j0 = 2 * g < ine ? 2 * g : ine - 1, j1 = 2 * g + 1 < ine ? 2 * g + 1 : ine - 1;
+      const int s0 = uniform(R.slots[s_lo + j0]), s1 = uniform(R.slots[s_lo + j1]);
+      const int r0 = GATEUP ? s0 / p.topk : s0, r1 = GATEUP ? s1 / p.topk : s1;
+      row0[g] = uniform((GATEUP ? p.pl_split : p.a_split) + (size_t)r0 * 2 * rstride + wv * 128);
+      dr[g] = (long)(r1 - r0) * 2 * rstride;
+    }
+  };
+  auto set_tile = [&]() {  // weights of tile ij of expert ie
+    const size_t toff = (size_t)ij * tile_bytes + (size_t)wv * 2304;
+    wb[0] = uniform((GATEUP ? p.w_gate + (size_t)ie * p.stride_gate : p.w_down + (size_t)ie * p.stride_down) + toff);
+    if (GATEUP) wb[NM - 1] = uniform(p.w_up + (size_t)ie * p.stride_up + toff);
+  };
+  // position 0
+  {
+    const int t0 = tile_at(0);  // the caller guarantees that the stream takes it
+    const int u = t0 / tpe;
+    set_expert(u);
+    ij = t0 - u * tpe;
+    set_tile();
+  }
+  int it_e = ie, it_ne = ine;  // expert and slot count of the tile being issued
+
+  // ---- compute side: reduction of the stream's n-th tile (expert e, ne slots) into the stage
   f32x4 acc[NM][G];
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int g = 0; g < G; ++g) acc[m][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // tile ti (local index tl within the stage) is complete on every k-wave: reduce over the
-  // k-waves in wave order into the stage.  LDS traffic only.
-  constexpr bool DB = 2 * RW <= kFp4RedPer;
-  auto tile_end = [&](int tl) {
-    float* red = L.red + (DB ? (tl & 1) * (kWaves * 64 * RW) : 0);
+  auto tile_end = [&](int n, int e, int ne, int t) {
+    publish();  // before the barrier: the hand-out of the position after the next
+    float* red = L.red + (DB ? (n & 1) * (kWaves * 64 * RW) : 0);
     if (kw) {
 #pragma unroll
       for (int m = 0; m < NM; ++m)
@@ -967,8 +1025,10 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
         }
     }
     lds_barrier();
-    float* out = L.stage + tl * 64 * n_e;
-    for (int x = threadIdx.x; x < 64 * n_e; x += kThreads) {
+    const float ts0 = GATEUP ? R.ts[0][e] : R.ts[2][e];
+    const float ts1 = GATEUP ? R.ts[1][e] : 0.f;
+    float* out = L.stage + n * SPT;
+    for (int x = threadIdx.x; x < 64 * ne; x += kThreads) {
       const int ln = x & 63, j = x >> 6;
       if (GATEUP) {
         float gs = 0.f, us = 0.f;
@@ -985,109 +1045,125 @@ __device__ __noinline__ void fp4_expert_run(uint64_t ph, int u_arg, int ta_arg, 
         out[x] = ds * ts0;
       }
     }
+    if (threadIdx.x == 0) L.st_tile[n] = t;
     if (!DB) lds_barrier();  // red is rewritten at the next tile end
   };
-  Fp4Pair<NM, G, ALDS> ring[DEPTH];
-  auto issue_w = [&](Fp4Pair<NM, G, ALDS>& f, int ti, int pr) {
+
+  // the loads move on to position is + 1: end the stream there, or set it up.  Returns false
+  // at the end of the stream.
+  int it = tile_at(0);
+  auto advance = [&]() -> bool {
+    publish();  // wave 0 never reads its own hand-out unpublished
+    const int s = is + 1;
+    if (s >= MAXT) return false;
+    int t;
+    if (s < n_st) {
+      t = ts + s;
+      if (++ij == tpe) {
+        ij = 0;
+        set_expert(iu + 1);
+      }
+    } else {
+      t = tile_at(s);
+      if (t >= t_end) return false;
+      const int u = t / tpe;
+      if (u != iu) set_expert(u);
+      ij = t - u * tpe;
+    }
+    if (fp4_group(ine) > G) return false;
+    set_tile();
+    is = s;
+    it = t;
+    it_e = ie;
+    it_ne = ine;
+    request();
+    return true;
+  };
+
+  Fp4Pair<NM, G> ring[DEPTH];
+  auto issue = [&](Fp4Pair<NM, G>& f, int pr) {
     const uint8_t* wt[NM];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)ti * tile_bytes + (size_t)pr * nkw * 2304;
-    fp4_pair_load_w<NM, G, ALDS>(f, wt);
+    for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)pr * nkw * 2304;
+    fp4_pair_load<NM, G>(f, wt, row0, dr, 64 * nkw * pr);
   };
-  // wave wv's local pair pr is the tile's pair wv + nkw pr
-  auto issue_a = [&](Fp4Pair<NM, G, ALDS>& f, int pr) {
-    fp4_pair_load_a<NM, G, ALDS>(f, arow, L.act, wv + nkw * pr, Sp);
-  };
-  auto issue = [&](Fp4Pair<NM, G, ALDS>& f, int ti, int pr) {
-    issue_w(f, ti, pr);
-    issue_a(f, pr);
-  };
-  // The run goes in segments of at most stage_tiles tiles; each segment is one pipeline
-  // (prologue, steady loop, last chunk) whose outputs are flushed to global memory after it.
-  for (int sa = ta; sa < tb; sa += stage_tiles) {
-    const int sb = tb - sa < stage_tiles ? tb : sa + stage_tiles;
-    // DEPTH <= npt: the first DEPTH pairs all lie in tile sa.  Weights first, so that their
-    // loads are in flight while the activation is staged.
-    if (kw) {
+  bool more = true;
+  if (kw) {
+    request();
+    // DEPTH <= npt: the first DEPTH pairs all lie in the first tile
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      issue(ring[d], d);
+      sched_fence();
+    }
+    publish();
+  }
+  lds_barrier();  // position 1's hand-out is published
+  if (kw) {
+    int ct = it, ce = it_e, cne = it_ne, cn = 0, cp = 0;  // tile being computed
+    int ip = DEPTH;
+    if (ip == npt) {
+      more = advance();
+      ip = 0;
+    }
+    while (more) {
 #pragma unroll
       for (int d = 0; d < DEPTH; ++d) {
-        issue_w(ring[d], sa, d);
+        fp4_pair_compute<NM, G>(ring[d], acc);
+        issue(ring[d], ip + d);
         sched_fence();
       }
-    }
-    if (ALDS && sa == ta) {
-      // Lane 4b + i of pair P, group g takes token slot 2g + (i & 1) at k = 64 P + 4b, hi
-      // words for i < 2 and lo words for i >= 2; one item (g, P, b, i & 1) fills both.
-      constexpr int kIt = G * kFp4ActPairs * 32 / kThreads;
-      const int n = G * Sp * 32;
-      float4 v[kIt];
-#pragma unroll
-      for (int i = 0; i < kIt; ++i) {  // all loads first (clamped, so none is conditional)
-        int x = threadIdx.x + i * kThreads;
-        x = x < n ? x : n - 1;
-        const int par = x & 1, b = (x >> 1) & 15, P = (x >> 5) % Sp, g = (x >> 5) / Sp;
-        int j = 2 * g + par;
-        j = j < n_e ? j : n_e - 1;
-        const int slot = R.slots[s_lo + j];
-        const float* src = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
-        v[i] = ldgf4(src + 64 * P + 4 * b);
+      cp += DEPTH;
+      if (cp == npt) {
+        tile_end(cn, ce, cne, ct);
+        ct = it;
+        ce = it_e;
+        cne = it_ne;
+        ++cn;
+        cp = 0;
       }
-#pragma unroll
-      for (int i = 0; i < kIt; ++i) {
-        const int x = threadIdx.x + i * kThreads;
-        if (x < n) {
-          const int par = x & 1, b = (x >> 1) & 15, P = (x >> 5) % Sp, g = (x >> 5) / Sp;
-          const u32x2 s01 = split_bf16(v[i].x, v[i].y), s23 = split_bf16(v[i].z, v[i].w);
-          u32x2* dst = L.act + (g * Sp + P) * 64 + 4 * b + par;
-          dst[0] = u32x2{s01[0], s23[0]};
-          dst[2] = u32x2{s01[1], s23[1]};
-        }
+      ip += DEPTH;
+      if (ip == npt) {
+        more = advance();
+        ip = 0;
       }
-      lds_barrier();
     }
-    if (kw) {
+    // the ring holds the last DEPTH pairs of tile ct
 #pragma unroll
-      for (int d = 0; d < DEPTH; ++d) issue_a(ring[d], d);
-      int ct = 0, cp = 0;           // local tile / pair of the chunk being computed
-      int it = sa, ip = DEPTH;      // tile / pair of the chunk being issued
-      if (ip == npt) { ip = 0; ++it; }
-      while (it < sb) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-          fp4_pair_compute<NM, G, ALDS>(ring[d], acc);
-          issue(ring[d], it, ip + d);
-          sched_fence();
-        }
-        ip += DEPTH;
-        if (ip == npt) { ip = 0; ++it; }
-        cp += DEPTH;
-        if (cp == npt) {
-          tile_end(ct);
-          cp = 0;
-          ++ct;
-        }
-      }
-#pragma unroll
-      for (int d = 0; d < DEPTH; ++d) fp4_pair_compute<NM, G, ALDS>(ring[d], acc);
-      tile_end(sb - sa - 1);
-    } else {
-      // waves without k work only take part in the reductions
-      for (int tl = 0; tl < sb - sa; ++tl) tile_end(tl);
+    for (int d = 0; d < DEPTH; ++d) fp4_pair_compute<NM, G>(ring[d], acc);
+    tile_end(cn, ce, cne, ct);
+    publish();
+  } else {
+    // waves without k work take part in the reductions, following the same positions
+    for (int n = 0;; ++n) {
+      const int t = it, e = it_e, ne = it_ne;
+      more = advance();
+      tile_end(n, e, ne, t);
+      if (!more) break;
     }
-    // write the segment's outputs
-    lds_barrier();
-    const int n = (sb - sa) * 64 * n_e;
-    for (int x = threadIdx.x; x < n; x += kThreads) {
-      const int tl = x / (64 * n_e), r = x % (64 * n_e), j = r >> 6, ln = r & 63;
-      const int slot = R.slots[s_lo + j];
-      const int row = (sa + tl) * 64 + ln;
-      if (GATEUP)
-        gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + row] = L.stage[x];
-      else
-        gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + row] = L.stage[x];
-    }
-    lds_barrier();  // the stage is rewritten by the next segment
   }
+  // write the stream's outputs (positions 0 .. is)
+  lds_barrier();
+  for (int x = threadIdx.x; x < (is + 1) * SPT; x += kThreads) {
+    const int n = x / SPT, r = x - n * SPT, j = r >> 6;
+    const int t = L.st_tile[n];
+    const int u = t / tpe;
+    const int s_lo = R.active_off[u];
+    if (j < R.active_off[u + 1] - s_lo) {
+      const int slot = R.slots[s_lo + j];
+      const int row = (t - u * tpe) * 64 + (r & 63);
+      if (GATEUP) {
+        gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + row] = L.stage[x];
+        store_split(gl(p.a_split) + (size_t)slot * p.I * 2, p.rank * p.I_loc + row, L.stage[x]);
+      } else {
+        gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + row] = L.stage[x];
+      }
+    }
+  }
+  lds_barrier();  // the stage and st_tile are rewritten by the next stream
+  const int stop = is + 1;
+  if (stop >= n_st && tile_at(stop) >= t_end) return -1;
+  return stop < n_st ? ts + stop : -(2 + k0 + stop - n_st);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1210,52 +1286,68 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
     const int cu = A + uniform(R.active_off[lo + 1]) - uniform(R.active_off[lo]);
     return lo * tpe + (int)((c - Pu + cu - 1) / cu);
   };
-  // one run of tiles [ta, tb) of active expert u
-  auto run = [&](int u, int ta, int tb) {
-    if (fp4) {
-      const int n_e = uniform(R.active_off[u + 1] - R.active_off[u]);
-      // ring depth per token-pair count (register budget); npt % DEPTH != 0 only for shapes
-      // with K < 512, which take the depth-1 ring
-      const int Sp = (GATEUP ? p.P : p.I) >> 6;
-      const int npt = Sp / kwaves_for(Sp);
-      constexpr int D1 = GATEUP ? 4 : 8;
-      // staged activation: runs of several tiles over one or two token pairs
-      const bool st = Sp <= kFp4ActPairs && tb - ta >= kFp4StageMinTiles;
-      if (n_e <= 2) {
-        if (npt % D1 != 0) fp4_expert_run<GATEUP, 1, 1, false>(params_handle(p), u, ta, tb);
-        else if (st) fp4_expert_run<GATEUP, 1, D1, true>(params_handle(p), u, ta, tb);
-        else fp4_expert_run<GATEUP, 1, D1, false>(params_handle(p), u, ta, tb);
-      } else if (n_e <= 4) {
-        if (npt % 4 != 0) fp4_expert_run<GATEUP, 2, 1, false>(params_handle(p), u, ta, tb);
-        else if (st) fp4_expert_run<GATEUP, 2, 4, true>(params_handle(p), u, ta, tb);
-        else fp4_expert_run<GATEUP, 2, 4, false>(params_handle(p), u, ta, tb);
-      } else if (n_e <= 8) {
-        if (npt % 2 == 0) fp4_expert_run<GATEUP, 4, 2, false>(params_handle(p), u, ta, tb);
-        else fp4_expert_run<GATEUP, 4, 1, false>(params_handle(p), u, ta, tb);
-      } else {
-        fp4_expert_run<GATEUP, 8, 1, false>(params_handle(p), u, ta, tb);
-      }
-    } else {
-      DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-      bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
-    }
-  };
   // Static part: the first 7/8 of the cost, split evenly.  Dynamic part: the remaining tiles,
-  // one per grab from a device-wide counter, so that workgroups that run slower (for any
+  // one per hand-out from a device-wide counter, so that workgroups that run slower (for any
   // reason: more tokens per tile, a busier XCD) take fewer of them.  Which workgroup computes
   // a tile does not change its arithmetic, so results stay bitwise reproducible.
   const long Cs = C - C / 8;
   const int t0 = first_tile((long)wg * Cs / p.nwg), t1 = first_tile((long)(wg + 1) * Cs / p.nwg);
+  const int t_dyn = first_tile(Cs), t_end = U * tpe;
+  auto ctr = gl(p.ctrl) + kWork + 32 * (GATEUP ? 0 : 1);
+  if (fp4) {
+    if (threadIdx.x < kDqSlots) R.dq[threadIdx.x] = -1;
+    lds_barrier();
+    const int Sp = (GATEUP ? p.P : p.I) >> 6;
+    const int npt = Sp / kwaves_for(Sp);
+    int ts = t0, k = 0;
+    for (;;) {
+      int t = ts;
+      if (ts >= t1) {  // next position is dynamic: hand it out unless a stream already did
+        if (uniform(R.dq[k & (kDqSlots - 1)]) >> 16 != k) {
+          if (threadIdx.x == 0) {
+            const unsigned v = (unsigned)t_dyn + __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            R.dq[k & (kDqSlots - 1)] = (k << 16) | (v < (unsigned)t_end ? (int)v : kDqEnd);
+          }
+          lds_barrier();
+        }
+        t = uniform(R.dq[k & (kDqSlots - 1)]) & 0xffff;
+        if (t >= t_end) break;
+      }
+      const int G = fp4_group(uniform(R.active_off[t / tpe + 1]) - uniform(R.active_off[t / tpe]));
+      const uint64_t h = params_handle(p);
+      // Ring depth 2: with every workgroup streaming all the time, two pairs in flight per wave
+      // (~74 KB per CU for gate/up) measured faster than 4 or 8 (more outstanding requests per
+      // CU lowered the achieved bandwidth), and 1 no faster.  Depth 1 for G = 8 (registers)
+      // and for shapes with an odd pair count per wave (K < 1024).
+      int r;
+      const bool d2 = npt % 2 == 0;
+      if (G == 1) r = d2 ? fp4_expert_stream<GATEUP, 1, 2>(h, ts, t1, k, t_dyn)
+                         : fp4_expert_stream<GATEUP, 1, 1>(h, ts, t1, k, t_dyn);
+      else if (G == 2) r = d2 ? fp4_expert_stream<GATEUP, 2, 2>(h, ts, t1, k, t_dyn)
+                              : fp4_expert_stream<GATEUP, 2, 1>(h, ts, t1, k, t_dyn);
+      else if (G == 4) r = d2 ? fp4_expert_stream<GATEUP, 4, 2>(h, ts, t1, k, t_dyn)
+                              : fp4_expert_stream<GATEUP, 4, 1>(h, ts, t1, k, t_dyn);
+      else r = fp4_expert_stream<GATEUP, 8, 1>(h, ts, t1, k, t_dyn);
+      r = uniform(r);
+      if (r == -1) break;
+      if (r >= 0) {
+        ts = r;
+      } else {
+        ts = t1;
+        k = -r - 2;
+      }
+    }
+    return;
+  }
+  DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   for (int t = t0; t < t1;) {
     const int u = t / tpe;
     const int ta = t % tpe;
     int tb = tpe;
     if ((u + 1) * tpe > t1) tb = t1 - u * tpe;
-    run(u, ta, tb);
+    bf16_expert_tiles<GATEUP>(p, R, u, ta, tb, L);
     t = u * tpe + tb;
   }
-  const int t_dyn = first_tile(Cs), t_end = U * tpe;
-  auto ctr = gl(p.ctrl) + kWork + 32 * (GATEUP ? 0 : 1);
   for (;;) {
     if (threadIdx.x == 0)
       R.next = t_dyn + (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1263,7 +1355,7 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
     const int t = uniform(R.next);
     lds_barrier();  // R.next is rewritten by the next grab
     if (t >= t_end) break;
-    run(t / tpe, t % tpe, t % tpe + 1);
+    bf16_expert_tiles<GATEUP>(p, R, t / tpe, t % tpe, t % tpe + 1, L);
   }
 }
 

@@ -16,6 +16,7 @@ const char* moel_status_string(int32_t s) {
     case MOEL_ERR_TIMEOUT: return "device wait timed out";
     case MOEL_ERR_ABORTED: return "aborted";
     case MOEL_ERR_UNSUPPORTED: return "unsupported device";
+    case MOEL_ERR_INTERNAL: return "device consistency check failed";
     default: return "unknown status";
   }
 }
