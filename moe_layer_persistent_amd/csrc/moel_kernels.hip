@@ -23,7 +23,8 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   KP& p = params_from(ph);
   const int wg = uniform(wg_arg);
   char* smem = moel_lds;
-  if constexpr (PH == kPhNorm1) phase_norm1(p, wg);
+  // step 0 (RMSNorm 1) has no work of its own: the QKV pass computes rstd from the rows it
+  // reads anyway
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
   if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
   if constexpr (PH == kPhAttnMerge) phase_attn_merge(p, wg);
@@ -50,9 +51,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
   unsigned bar = 0;
   auto sync = [&]() { grid_barrier(p, ++bar); };
   stamp(p, 16 + kPhNorm1);
-  if (run) fused_phase<kPhNorm1, D>(params_handle(p), wg);
   stamp(p, kPhNorm1);
-  sync();
   stamp(p, 16 + kPhQkv);
   if (run) fused_phase<kPhQkv, D>(params_handle(p), wg);
   stamp(p, kPhQkv);
@@ -130,7 +129,6 @@ __global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
     return;
   }
   stamp(p, 16 + PH);
-  if constexpr (PH == kPhNorm1) phase_norm1(p, wg);
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
   if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
   if constexpr (PH == kPhAttnMerge) phase_attn_merge(p, wg);
@@ -338,7 +336,6 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     return o;
   };
   const size_t o_ctrl = take((size_t)kCtrlWords * 4);
-  const size_t o_ss1 = take((size_t)nwg * kMaxT * 4);
   const size_t o_ss2 = take((size_t)nwg * kMaxT * 4);
   const size_t o_q = take((size_t)kMaxT * Hq * D * 4);
   const size_t o_ao = take((size_t)nwg * plan->grp * kMaxT * D * 4);
@@ -417,7 +414,6 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.stride_up = moel_packed_experts_bytes(cfg, 1) / (size_t)E;
   b.stride_down = moel_packed_experts_bytes(cfg, 2) / (size_t)E;
   b.ctrl = reinterpret_cast<unsigned*>(ws + o_ctrl);
-  b.ss1 = reinterpret_cast<float*>(ws + o_ss1);
   b.ss2 = reinterpret_cast<float*>(ws + o_ss2);
   b.q_buf = reinterpret_cast<float*>(ws + o_q);
   b.attn_o = reinterpret_cast<float*>(ws + o_ao);
@@ -575,7 +571,7 @@ moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, vo
   moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, y, dbg, p);
   if (st != MOEL_OK) return st;
   void* args[] = {&p};
-  for (int ph = 0; ph < kNumPhases; ++ph) {
+  for (int ph = kPhQkv; ph < kNumPhases; ++ph) {  // step 0 is part of step 1
     const void* fn = plan->cfg.head_dim == 64 ? phase_fn<64>(ph) : phase_fn<128>(ph);
     hipError_t e = hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_phase[ph],
                                    static_cast<hipStream_t>(stream));

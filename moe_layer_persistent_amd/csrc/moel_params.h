@@ -13,8 +13,8 @@ namespace moel {
 // Phase ids: index of the timestamp slot written at the end of each phase, and of the
 // unfused chain's kernels.
 enum Phase {
-  kPhNorm1 = 0,     // per-workgroup partial sums of x^2
-  kPhQkv = 1,       // QKV projection + RoPE + q store + KV-cache write
+  kPhNorm1 = 0,     // RMSNorm 1: no work of its own (the QKV pass computes rstd)
+  kPhQkv = 1,       // RMSNorm 1 + QKV projection + RoPE + q store + KV-cache write
   kPhAttn = 2,      // attention partials per (kv head, key chunk)
   kPhAttnMerge = 3, // merge of the key-chunk partials -> o (bf16)
   kPhOproj = 4,     // o-projection + residual -> h, partial sums of h^2
@@ -59,7 +59,6 @@ struct LayerParams {
   const float* rope_cos;  // [kv_cap][D/2]
   const float* rope_sin;
   // scratch (plan workspace)
-  float* ss1;       // [nwg][16]
   float* ss2;       // [nwg][16]
   float* q_buf;     // [16][Hq*D]
   float* attn_o;    // [items][grp][16][D]

@@ -63,22 +63,6 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, u32x4& 
 // ------------------------------------------------------------------------------------------
 // RMSNorm statistics
 // ------------------------------------------------------------------------------------------
-// Partial sums of x^2 over this workgroup's slice of the hidden dimension, per token.
-__device__ __forceinline__ void phase_norm1(KP& p, int wg) {
-  const int tid = threadIdx.x;
-  const int t = tid >> 5, sub = tid & 31;  // 16 tokens x 32 lanes
-  const int k0 = (int)((long)wg * p.H / p.nwg), k1 = (int)((long)(wg + 1) * p.H / p.nwg);
-  float s = 0.f;
-  if (t < p.T)
-    for (int k = k0 + sub; k < k1; k += 32) {
-      float v = gl(p.x)[(size_t)t * p.H + k];
-      s = fmaf(v, v, s);
-    }
-#pragma unroll
-  for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o, 32);
-  if (sub == 0) gl(p.ss1)[wg * kMaxT + t] = s;
-}
-
 // rstd of every token from the per-workgroup partial sums, in a fixed summation order
 // (32 interleaved subsets, then the subsets in order).  `tmp` is 32*16 floats of LDS,
 // `out` 16 floats of LDS.  Returns this lane's token's value.
@@ -103,6 +87,7 @@ __device__ __forceinline__ float wg_rstd(const float* ss, int nwg, int H, float 
 // Rows of tokens t >= T read the row of token T-1 (their products are computed and never
 // read), so that no load in the streaming loops depends on a branch.
 struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
+  static constexpr bool kStats = false;
   const float* v;
   int ld;
   const uint16_t* gamma;
@@ -133,7 +118,54 @@ struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
     split8(a, b, hi, lo);
   }
 };
+// v * gamma from an fp32 row, plus the row's sum of squares: the contraction of an RMS-normed
+// row is rstd * (W . (v * gamma)), so the pass that reads the row for the contraction also
+// yields rstd (dense_pass leaves it in DenseLds::rstd) and the epilogue scales by it.
+struct AGamma {
+  static constexpr bool kStats = true;
+  const float* v;
+  int ld;
+  const uint16_t* gamma;
+  int T;
+  float eps;
+  struct Raw {
+    float4 a, b;
+    u32x4 g;
+  };
+  __device__ __forceinline__ AGamma scalar() const {
+    return AGamma{uniform(v), uniform(ld), uniform(gamma), uniform(T), __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, eps)))};
+  }
+  __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
+    const float* src = v + (size_t)tok * ld + k;
+    r.a = ldgf4(src);
+    r.b = ldgf4(src + 4);
+    r.g = ldg16(gamma + k);
+  }
+  __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
+    float4 a = r.a, b = r.b;
+    a.x *= bf_lo(r.g[0]);
+    a.y *= bf_hi(r.g[0]);
+    a.z *= bf_lo(r.g[1]);
+    a.w *= bf_hi(r.g[1]);
+    b.x *= bf_lo(r.g[2]);
+    b.y *= bf_hi(r.g[2]);
+    b.z *= bf_lo(r.g[3]);
+    b.w *= bf_hi(r.g[3]);
+    split8(a, b, hi, lo);
+  }
+  __device__ __forceinline__ float sq(const Raw& r) const {
+    float s = r.a.x * r.a.x;
+    s = fmaf(r.a.y, r.a.y, s);
+    s = fmaf(r.a.z, r.a.z, s);
+    s = fmaf(r.a.w, r.a.w, s);
+    s = fmaf(r.b.x, r.b.x, s);
+    s = fmaf(r.b.y, r.b.y, s);
+    s = fmaf(r.b.z, r.b.z, s);
+    return fmaf(r.b.w, r.b.w, s);
+  }
+};
 struct AF32 {  // a stored fp32 row
+  static constexpr bool kStats = false;
   const float* v;
   int ld;
   int T;
@@ -164,6 +196,8 @@ struct DenseLds {
   f32x4 red[kWaves * 4 * 64];   // 32 KiB
   float fin[4 * 16 * kMaxT];    // 4 KiB
   float aux[4 * 16 * kMaxT];    // 4 KiB (epilogue scratch)
+  float ss[kWaves * 64];        // per-lane sums of squares of the A rows (sources with stats)
+  float rstd[kMaxT];            // 1 / rms of each token's A row (sources with stats)
 };
 
 // Largest divisor of n that is <= 8: the number of waves that split a reduction of n units
@@ -197,6 +231,7 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float ssum = 0.f;  // sum of squares of this lane's A elements (sources with stats)
   if (wv < nkw) {
     // k-wave wv takes the steps wv, wv + nkw, ... so that the workgroup's loads in flight
     // cover one contiguous stretch of each tile
@@ -222,6 +257,7 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
     auto compute = [&](int d) {
       u32x4 a_hi, a_lo;
       A.finish(ra[d], a_hi, a_lo);
+      if constexpr (ASrc::kStats) ssum += A.sq(ra[d]);
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
         acc[j] = mfma16x16x32(a_hi, rw[d][j], acc[j]);
@@ -257,7 +293,19 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
 #pragma unroll
     for (int j = 0; j < NT; ++j) L.red[(wv * 4 + j) * 64 + lane] = acc[j];
   }
+  // every (token, k) of the A rows is fetched by exactly one lane of the k-waves (lanes with
+  // (lane & 15) >= T repeat token T-1 and are left out)
+  if constexpr (ASrc::kStats) L.ss[wv * 64 + lane] = (wv < nkw && (lane & 15) < A.T) ? ssum : 0.f;
   lds_barrier();
+  if constexpr (ASrc::kStats) {
+    if (threadIdx.x < kMaxT) {
+      float s = 0.f;
+      for (int w = 0; w < nkw; ++w)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) s += L.ss[w * 64 + 16 * q + threadIdx.x];
+      L.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + A.eps);
+    }
+  }
   for (int e = threadIdx.x; e < NT * 256; e += kThreads) {
     const int j = e >> 8, ln = (e >> 2) & 63, r = e & 3;
     float s = 0.f;
@@ -312,8 +360,7 @@ __device__ __forceinline__ bool octet_in(int row, int lo, int hi) {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  const float rs = wg_rstd(p.ss1, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
-  ANorm A{p.x, p.H, p.gamma1, rs, p.T};
+  AGamma A{p.x, p.H, p.gamma1, p.T, p.eps};  // RMSNorm 1 folded in: rstd from the same pass
   const int tiles = (p.Hq + 2 * p.Hkv) * p.D / 16;
   const int half = p.D >> 1;
   dense_phase(p.w_qkv, tiles, nullptr, 0, p.H, wg, p.nwg, A, L,
@@ -322,8 +369,8 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
                   const int j = e / (8 * kMaxT), pr = (e / kMaxT) & 7, t = e % kMaxT;
                   const int R = (tf + j) * 16 + 2 * pr;  // packed row (even)
                   if (t >= p.T || !octet_in(R, lo, hi)) continue;
-                  const float a = L.fin[(j * 16 + 2 * pr) * kMaxT + t];
-                  const float b = L.fin[(j * 16 + 2 * pr + 1) * kMaxT + t];
+                  const float a = L.fin[(j * 16 + 2 * pr) * kMaxT + t] * L.rstd[t];
+                  const float b = L.fin[(j * 16 + 2 * pr + 1) * kMaxT + t] * L.rstd[t];
                   const int head = R / p.D, i = (R % p.D) >> 1;
                   const int ps = p.pos + t;
                   if (head < p.Hq + p.Hkv) {
