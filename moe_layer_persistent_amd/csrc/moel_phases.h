@@ -703,6 +703,30 @@ __device__ __forceinline__ void kv_dpp_step(float& v, int& i) {
 // xor 2 within quads, half-row and row mirrors (row maximum in every lane of the row), then a
 // row-15 broadcast into rows 1 and 3, which leaves the maximum of lanes 0-31 in lane 31 and of
 // lanes 32-63 in lane 63.
+// Sorts a lane's (value, expert) pairs best first (larger value; lower expert on ties) with a
+// bitonic network; branch-free compare-exchanges.
+template <int NV>
+__device__ __forceinline__ void kv_sort_desc(float (&v)[NV], int (&ix)[NV]) {
+#pragma unroll
+  for (int k = 2; k <= NV; k <<= 1)
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          const bool l_better = (v[l] > v[i]) | ((v[l] == v[i]) & (ix[l] < ix[i]));
+          const bool sw = ((i & k) == 0) ? l_better : !l_better;
+          const float a = v[i], b = v[l];
+          const int ia = ix[i], ib = ix[l];
+          v[i] = sw ? b : a;
+          v[l] = sw ? a : b;
+          ix[i] = sw ? ib : ia;
+          ix[l] = sw ? ia : ib;
+        }
+      }
+}
+
 __device__ __forceinline__ void half_argmax(float& v, int& i, float& v_lo, int& i_lo, float& v_hi, int& i_hi) {
   kv_dpp_step<0xB1, 0xF>(v, i);   // quad_perm [1,0,3,2]
   kv_dpp_step<0x4E, 0xF>(v, i);   // quad_perm [2,3,0,1]
@@ -746,38 +770,41 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
     }
   }
   // top-k: wave w takes tokens 2w (lanes 0-31) and 2w + 1 (lanes 32-63) at the same time;
-  // lane l of a half holds experts (l mod 32) + 32 j
-  {
+  // lane l of a half holds experts (l mod 32) + 32 j, j < NV = ceil(E / 32)
+  auto topk = [&](auto nv_tag) {
+    constexpr int NV = decltype(nv_tag)::value;
     const int t = 2 * wv + (lane >> 5);
     const bool tok_ok = t < p.T;
     const int tc = tok_ok ? t : 0;
-    float v[16];
-    int ix[16];
+    float v[NV];
+    int ix[NV];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
+    for (int j = 0; j < NV; ++j) {
       const int e = (lane & 31) + 32 * j;
       const bool ok = tok_ok && e < p.E;
       v[j] = ok ? gl(p.logits)[tc * p.E + (e < p.E ? e : 0)] : NEG;
       ix[j] = ok ? e : BIG;
     }
+    // each lane's list best first: a round's candidates are the list heads, and the lane that
+    // owns the winner pops its head
+    kv_sort_desc<NV>(v, ix);
     float sel0_lo = 0.f, sel0_hi = 0.f, esum = 0.f, ex_r = 0.f;
     for (int r = 0; r < p.topk; ++r) {
       float bv = v[0];
       int bi = ix[0];
-#pragma unroll
-      for (int j = 1; j < 16; ++j) kv_better(bv, bi, v[j], ix[j]);
       float v_lo, v_hi;
       int i_lo, i_hi;
       half_argmax(bv, bi, v_lo, i_lo, v_hi, i_hi);
       const float wv_ = lane < 32 ? v_lo : v_hi;
       const int wi = lane < 32 ? i_lo : i_hi;
-      // the owner retires the winner
+      const bool pop = ix[0] == wi;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const bool hit = ix[j] == wi;
-        v[j] = hit ? NEG : v[j];
-        ix[j] = hit ? BIG : ix[j];
+      for (int j = 0; j < NV - 1; ++j) {
+        v[j] = pop ? v[j + 1] : v[j];
+        ix[j] = pop ? ix[j + 1] : ix[j];
       }
+      v[NV - 1] = pop ? NEG : v[NV - 1];
+      ix[NV - 1] = pop ? BIG : ix[NV - 1];
       if (r == 0) {
         sel0_lo = v_lo;
         sel0_hi = v_hi;
@@ -788,7 +815,9 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
       if ((lane & 31) == 0 && tok_ok) R.idx[t * p.topk + r] = wi;
     }
     if ((lane & 31) < p.topk && tok_ok) R.gate[t * p.topk + (lane & 31)] = ex_r / esum;
-  }
+  };
+  if (p.E <= 256) topk(std::integral_constant<int, 8>{});
+  else topk(std::integral_constant<int, 16>{});
   lds_barrier();
   // slot lists, expert-major with slots ascending within an expert.  Per expert: the count of
   // its slots and the mask of tokens that chose it (LDS integer atomics, order-independent);
