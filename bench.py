@@ -249,6 +249,11 @@ def main():
     assert st == 0, binding.status_string(st)
     ms_per_step = wall * 1e3 / args.steps
     durs = per_launch(True, max(5, args.steps // 2))
+    # the same launches through the cooperative launch API (guaranteed residency on a shared
+    # device), for comparison: the runtime adds a gap between consecutive cooperative launches
+    plan.set_launch(binding.MOEL_LAUNCH_COOPERATIVE)
+    coop_us, _ = timed(True, max(5, args.steps // 2), 2)
+    plan.set_launch(binding.MOEL_LAUNCH_PLAIN)
     gbps = alg_bytes / (mean_us * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     result = {
@@ -268,17 +273,19 @@ def main():
         "config": {"workload": w.name, "T": T, "hidden": w.hidden, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "window": window, "kv_history": w.pos,
                    "experts": w.n_experts, "top_k": w.top_k, "pooled": w.pooled, "inter": w.inter,
-                   "routing": args.routing, "distinct_experts": U, "weight_copies_rotated": 2},
+                   "routing": args.routing, "distinct_experts": U, "weight_copies_rotated": 2,
+                   "launch": "plain"},
         "latency_us": {"mean_back_to_back": round(mean_us, 2),
                        "single_launch_median": round(statistics.median(durs), 2),
                        "single_launch_p10": round(float(np.percentile(durs, 10)), 2),
-                       "single_launch_p90": round(float(np.percentile(durs, 90)), 2)},
+                       "single_launch_p90": round(float(np.percentile(durs, 90)), 2),
+                       "cooperative_launch_back_to_back": round(coop_us, 2)},
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
                      "traffic": None if traffic is None else int(traffic["bytes_per_launch"]),
                      "algorithmic_bytes_per_launch": int(alg_bytes),
-                     "kernel": "k_layer_fused (one cooperative launch per layer)"},
+                     "kernel": "k_layer_fused (one launch per layer, one workgroup per CU)"},
     }
     # per-phase timeline of one fused launch (workgroup timestamps, 100 MHz clock): slot i is
     # the end of step i, slot 16 + i its start (after the preceding grid barrier)

@@ -36,7 +36,7 @@ extern "C" {
 #endif
 
 #define MOEL_MAX_TOKENS 16
-#define MOEL_ABI_VERSION 1
+#define MOEL_ABI_VERSION 2
 
 typedef enum moel_status {
   MOEL_OK = 0,
@@ -146,6 +146,19 @@ int32_t moel_plan_workgroups(const moel_plan* plan);
  * plan's barrier words reset) by this call. */
 moel_status moel_plan_status(moel_plan* plan);
 
+/* How moel_layer_decode launches the persistent kernel (plan default: plain).
+ *   MOEL_LAUNCH_PLAIN: an ordinary launch of one workgroup per compute unit.  Its grid
+ *     barriers need every workgroup resident at once; moel_plan_create checks that one
+ *     workgroup fits per compute unit, so on a device running nothing else they all are.
+ *     Kernels of other streams holding compute units delay the barriers until they end; a
+ *     barrier that waits ~0.5 s ends with MOEL_ERR_TIMEOUT (plan status) instead of hanging.
+ *     Consecutive calls on one stream are serialised by the stream.
+ *   MOEL_LAUNCH_COOPERATIVE: a cooperative launch, which guarantees residency on a shared
+ *     device; the runtime leaves a gap of ~20 us between consecutive such launches.
+ * Returns MOEL_ERR_ARG for another mode. */
+typedef enum { MOEL_LAUNCH_PLAIN = 0, MOEL_LAUNCH_COOPERATIVE = 1 } moel_launch_mode;
+moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode);
+
 /* Sets (1) or clears (0) the plan's abort word.  While set, launched kernels skip all
  * work, leave every caller buffer untouched and report MOEL_ERR_ABORTED. */
 moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* stream);
@@ -178,7 +191,7 @@ moel_status moel_pack_experts(const moel_config* cfg, int32_t which, const void*
 
 /* --- the layer step -------------------------------------------------------------- */
 
-/* One verify step of one layer, as ONE persistent cooperative launch.
+/* One verify step of one layer, as ONE persistent launch (see moel_plan_set_launch).
  *   k_cache, v_cache: bf16 [Hkv, kv_capacity, D]; slots [pos, pos+T) of every kv head
  *                     are overwritten with the new (rotated, rounded) keys / values;
  *                     every other byte is left untouched.

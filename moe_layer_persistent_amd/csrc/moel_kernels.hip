@@ -205,6 +205,7 @@ struct moel_plan {
   LayerParams base;  // shape + scratch pointers
   size_t lds_fused;
   size_t lds_phase[kNumPhases];
+  int launch_mode;  // moel_launch_mode
 };
 
 namespace {
@@ -449,11 +450,17 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
       ok = ok && hip_ok(hipFuncSetAttribute(phase_fn<128>(ph), hipFuncAttributeMaxDynamicSharedMemorySize,
                                             (int)plan->lds_phase[ph]));
   }
-  if (!ok) {
+  // the plain launch relies on one resident workgroup per compute unit
+  int per_cu = 0;
+  if (ok)
+    ok = hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, D == 64 ? fused_fn<64>() : fused_fn<128>(),
+                                                             kThreads, mx));
+  if (!ok || per_cu < 1) {
     hipFree(plan->ws);
     delete plan;
-    return MOEL_ERR_HIP;
+    return ok ? MOEL_ERR_UNSUPPORTED : MOEL_ERR_HIP;
   }
+  plan->launch_mode = MOEL_LAUNCH_PLAIN;
   if (std::getenv("MOEL_LOG"))
     std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu\n",
                  H, Hq, cfg->n_kv_heads, D, P, I, E, k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx);
@@ -559,9 +566,18 @@ moel_status moel_layer_decode(moel_plan* plan, const moel_weights* w, void* k_ca
   if (st != MOEL_OK) return st;
   void* args[] = {&p};
   const void* fn = plan->cfg.head_dim == 64 ? fused_fn<64>() : fused_fn<128>();
-  hipError_t e = hipLaunchCooperativeKernel(fn, dim3(plan->nwg), dim3(kThreads), args,
-                                            (unsigned)plan->lds_fused, static_cast<hipStream_t>(stream));
+  hipError_t e = plan->launch_mode == MOEL_LAUNCH_COOPERATIVE
+                     ? hipLaunchCooperativeKernel(fn, dim3(plan->nwg), dim3(kThreads), args,
+                                                  (unsigned)plan->lds_fused, static_cast<hipStream_t>(stream))
+                     : hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_fused,
+                                       static_cast<hipStream_t>(stream));
   return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode) {
+  if (plan == nullptr || (mode != MOEL_LAUNCH_PLAIN && mode != MOEL_LAUNCH_COOPERATIVE)) return MOEL_ERR_ARG;
+  plan->launch_mode = mode;
+  return MOEL_OK;
 }
 
 moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,

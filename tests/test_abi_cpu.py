@@ -23,7 +23,13 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.moel_abi_version() == 1
+    assert L.moel_abi_version() == 2
+
+
+def test_plan_options_reject_a_missing_plan():
+    L = binding.lib()
+    assert L.moel_plan_set_launch(None, binding.MOEL_LAUNCH_PLAIN) == binding.MOEL_ERR_ARG
+    assert L.moel_plan_set_launch(None, 5) == binding.MOEL_ERR_ARG
 
 
 def _cfg(**kw):

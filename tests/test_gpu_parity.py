@@ -71,6 +71,21 @@ def test_fused_equals_unfused_and_is_deterministic():
         assert _same_bytes(a[k], c[k]), k
 
 
+def test_plain_and_cooperative_launches_agree():
+    w = synth.small_workload(T=16, pos=300, window=0, n_experts=32, top_k=8, pooled=512, inter=512)
+    run = harness.GpuRun(w)
+    a = run.run(fused=True)
+    run.plan.set_launch(binding.MOEL_LAUNCH_COOPERATIVE)
+    b = run.run(fused=True)
+    run.plan.set_launch(binding.MOEL_LAUNCH_PLAIN)
+    c = run.run(fused=True)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(a[k], b[k]), k
+        assert _same_bytes(a[k], c[k]), k
+    with pytest.raises(binding.MoelError):
+        run.plan.set_launch(7)
+
+
 def test_timestamps_leave_outputs_bit_identical():
     w = synth.small_workload(T=8, pos=200, window=64)
     run = harness.GpuRun(w)
