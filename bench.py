@@ -254,6 +254,11 @@ def main():
     plan.set_launch(binding.MOEL_LAUNCH_COOPERATIVE)
     coop_us, _ = timed(True, max(5, args.steps // 2), 2)
     plan.set_launch(binding.MOEL_LAUNCH_PLAIN)
+    # and with barriers whose acquire also invalidates the L2 (the memory model's agent-scope
+    # acquire), for comparison with the L1-only acquire taken where the L2s are coherent
+    plan.set_acquire(binding.MOEL_ACQUIRE_L2_INVALIDATE)
+    inv_us, _ = timed(True, max(5, args.steps // 2), 2)
+    plan.set_acquire(binding.MOEL_ACQUIRE_AUTO)
     gbps = alg_bytes / (mean_us * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     result = {
@@ -274,12 +279,14 @@ def main():
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "window": window, "kv_history": w.pos,
                    "experts": w.n_experts, "top_k": w.top_k, "pooled": w.pooled, "inter": w.inter,
                    "routing": args.routing, "distinct_experts": U, "weight_copies_rotated": 2,
-                   "launch": "plain"},
+                   "launch": "plain",
+                   "barrier_acquire": "L1 only (XCD L2s coherent)" if plan.l2_coherent else "L1 + L2 invalidate"},
         "latency_us": {"mean_back_to_back": round(mean_us, 2),
                        "single_launch_median": round(statistics.median(durs), 2),
                        "single_launch_p10": round(float(np.percentile(durs, 10)), 2),
                        "single_launch_p90": round(float(np.percentile(durs, 90)), 2),
-                       "cooperative_launch_back_to_back": round(coop_us, 2)},
+                       "cooperative_launch_back_to_back": round(coop_us, 2),
+                       "l2_invalidating_acquire_back_to_back": round(inv_us, 2)},
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),

@@ -36,7 +36,7 @@ extern "C" {
 #endif
 
 #define MOEL_MAX_TOKENS 16
-#define MOEL_ABI_VERSION 2
+#define MOEL_ABI_VERSION 3
 
 typedef enum moel_status {
   MOEL_OK = 0,
@@ -159,6 +159,23 @@ moel_status moel_plan_status(moel_plan* plan);
 typedef enum { MOEL_LAUNCH_PLAIN = 0, MOEL_LAUNCH_COOPERATIVE = 1 } moel_launch_mode;
 moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode);
 
+/* Acquire side of the persistent launch's grid barriers.  Not a step of the layer: a
+ * property of how the workgroups of one launch see each other's stores.
+ *   MOEL_ACQUIRE_AUTO (default): when the plan's device keeps the L2 caches of its XCDs
+ *     coherent with each other for hipMalloc memory (checked once per device and process
+ *     when a plan is created, see moel_plan_l2_coherent), a barrier invalidates only the
+ *     L1 caches; otherwise it runs the memory model's agent-scope acquire, which also
+ *     invalidates the L2 and with it the code and weights held there.
+ *   MOEL_ACQUIRE_L2_INVALIDATE: always the agent-scope acquire.
+ * Results are bitwise identical in both modes.  Returns MOEL_ERR_ARG for another mode. */
+typedef enum { MOEL_ACQUIRE_AUTO = 0, MOEL_ACQUIRE_L2_INVALIDATE = 1 } moel_acquire_mode;
+moel_status moel_plan_set_acquire(moel_plan* plan, int32_t mode);
+
+/* 1 if the coherence check passed on the plan's device (a workgroup's stores, written back by
+ * a release fence, were seen by readers on every XCD after an L1-only invalidation, with no
+ * stale word in four trials), 0 if not, -1 for a null plan. */
+int32_t moel_plan_l2_coherent(const moel_plan* plan);
+
 /* Sets (1) or clears (0) the plan's abort word.  While set, launched kernels skip all
  * work, leave every caller buffer untouched and report MOEL_ERR_ABORTED. */
 moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* stream);
@@ -175,7 +192,8 @@ moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, 
 /* --- weight packing (one-time, not on the hot path) --------------------------------- */
 
 /* Dense bf16 matrix [N, K] row-major -> packed layout (16-row tiles, 32-element k steps,
- * one 1 KiB block per (tile, step)).  rope_head_dim > 0 interleaves the rows of every
+ * one 1 KiB block per (tile, step); in a block, lane l's 16 bytes hold row l % 16 at
+ * k = 4q + 0..3 and 16 + 4q + 0..3 of the step, q = l / 16).  rope_head_dim > 0 interleaves the rows of every
  * rope_head_dim-row head pairwise (i, i + D/2) so that rotation partners are adjacent;
  * pass head_dim for w_qkv and 0 otherwise.  N % 16 == 0, K % 32 == 0. */
 moel_status moel_pack_dense(const void* src, int32_t N, int32_t K, int32_t rope_head_dim,

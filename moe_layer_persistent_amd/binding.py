@@ -24,6 +24,8 @@ MOEL_ERR_ABORTED = -6
 MOEL_ERR_UNSUPPORTED = -7
 MOEL_LAUNCH_PLAIN = 0
 MOEL_LAUNCH_COOPERATIVE = 1
+MOEL_ACQUIRE_AUTO = 0
+MOEL_ACQUIRE_L2_INVALIDATE = 1
 MOEL_ERR_INTERNAL = -8
 MOEL_EXPERT_NVFP4 = 0
 MOEL_EXPERT_BF16 = 1
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
             "moel_plan_status": (i32, [vp]),
             "moel_plan_set_abort": (i32, [vp, i32, vp]),
             "moel_plan_set_launch": (i32, [vp, i32]),
+            "moel_plan_set_acquire": (i32, [vp, i32]),
+            "moel_plan_l2_coherent": (i32, [vp]),
             "moel_plan_scratch": (i32, [vp, i32, P(vp), P(sz)]),
             "moel_pack_dense": (i32, [vp, i32, i32, i32, vp, vp]),
             "moel_pack_experts": (i32, [P(Config), i32, vp, vp, vp, vp]),
@@ -178,6 +182,15 @@ class Plan:
     def set_launch(self, mode: int):
         """MOEL_LAUNCH_PLAIN (default) or MOEL_LAUNCH_COOPERATIVE, see include/moel.h."""
         _check(lib().moel_plan_set_launch(self.handle, int(mode)), "moel_plan_set_launch")
+
+    def set_acquire(self, mode: int):
+        """MOEL_ACQUIRE_AUTO (default) or MOEL_ACQUIRE_L2_INVALIDATE, see include/moel.h."""
+        _check(lib().moel_plan_set_acquire(self.handle, int(mode)), "moel_plan_set_acquire")
+
+    @property
+    def l2_coherent(self) -> bool:
+        """Whether the device passed the L2 coherence check when the plan was created."""
+        return lib().moel_plan_l2_coherent(self.handle) == 1
 
     def set_abort(self, flag: bool, stream=None):
         _check(lib().moel_plan_set_abort(self.handle, int(flag), _stream(stream)), "moel_plan_set_abort")

@@ -158,6 +158,21 @@ __device__ __forceinline__ bool aborted(KP& p) {
   return __hip_atomic_load(gl(p.ctrl) + kAbort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0;
 }
 
+// Acquire side of the grid barrier.  Other workgroups' data reaches this CU through its L1,
+// which is not coherent and is always invalidated, and the XCD's L2.  Where the L2 caches of
+// the XCDs are kept coherent with each other for the plan's memory (probed when the plan is
+// created), nothing in the L2 can be stale and it is left alone: the agent-scope acquire of
+// the memory model would also drop the L2's contents, code and read-only weights included,
+// and every phase would then refetch them from memory.
+__device__ __forceinline__ void acquire_fence(int l2_coherent) {
+  if (l2_coherent) asm volatile("buffer_inv sc0" ::: "memory");  // L1 only
+  else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+__device__ __forceinline__ void acq_rel_fence(int l2_coherent) {
+  if (l2_coherent) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // no reads follow before the flag
+  else __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+}
+
 // Grid-wide barrier number b (1, 2, ... within one launch) of the persistent launch.
 //
 // Arrival is a two-level tree: workgroup w counts into group (w mod 8), whose counter lives
@@ -167,11 +182,11 @@ __device__ __forceinline__ bool aborted(KP& p) {
 // workgroups arrive together.  All counters are monotonic within a launch (group g reads
 // b * n_g after barrier b) and are reset by the last workgroup to leave the kernel.
 //
-// Ordering: every arrival is preceded by a release fence; a group leader and the final
-// arrival run acquire-release fences between their counter updates, and every waiter runs an
-// acquire fence after seeing the release word, so each workgroup's stores before the barrier
-// are visible to every workgroup after it.  One wave per workgroup runs the fences: the cache
-// operations they issue act on the whole CU / XCD.
+// Ordering: every arrival is preceded by a release fence (the XCD's L2 is written back); a
+// group leader and the final arrival run fences between their counter updates, and every
+// waiter runs an acquire fence after seeing the release word, so each workgroup's stores
+// before the barrier are visible to every workgroup after it.  One wave per workgroup runs
+// the fences: the cache operations they issue act on the whole CU / XCD.
 //
 // Every wait is bounded: after ~0.5 s the status word records a timeout and the wait ends.
 __device__ __forceinline__ void grid_barrier(KP& p, unsigned b) {
@@ -186,10 +201,10 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b) {
     const unsigned prev = __hip_atomic_fetch_add(ctrl + kGroup + 32 * g, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev + 1 == b * n_g) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+      acq_rel_fence(p.l2_coherent);
       const unsigned top = __hip_atomic_fetch_add(ctrl + kTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (top + 1 == b * (unsigned)ng_all) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+        acq_rel_fence(p.l2_coherent);
         __hip_atomic_store(ctrl + kFlag, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
@@ -202,7 +217,7 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b) {
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    acquire_fence(p.l2_coherent);
   }
   __syncthreads();
 }

@@ -5,6 +5,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <new>
 
@@ -167,8 +168,11 @@ __global__ void k_pack_dense(const uint16_t* __restrict__ src, int N, int K, int
     const int head = R / rope_D, r = R % rope_D;
     row = head * rope_D + (r >> 1) + (r & 1) * (rope_D / 2);
   }
-  const u32x4 v = *reinterpret_cast<const u32x4*>(src + (size_t)row * K + step * 32 + 8 * (lane >> 4));
-  *reinterpret_cast<u32x4*>(dst + c * 16) = v;
+  // hardware k slot j of quarter q holds k = 4q + j (j < 4) or 16 + 4q + (j - 4) (j >= 4)
+  const uint16_t* r = src + (size_t)row * K + step * 32 + 4 * (lane >> 4);
+  const u32x2 lo = *reinterpret_cast<const u32x2*>(r);
+  const u32x2 hi = *reinterpret_cast<const u32x2*>(r + 16);
+  *reinterpret_cast<u32x4*>(dst + c * 16) = u32x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
 // one thread per (expert, 64-row tile, k pair, lane)
@@ -192,6 +196,60 @@ __global__ void k_pack_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* _
 
 __global__ void k_set_word(unsigned* w, unsigned v) { *w = v; }
 
+// Cross-XCD coherence check of the L2 caches for memory from hipMalloc (the plan's workspace
+// and the caller's tensors).  Workgroups 1..15 (every XCD under round-robin dispatch, the
+// writer's included) read a 64 KiB block, so that their XCDs' L2 hold copies of it; workgroup
+// 0 then overwrites the block with `gen`, runs the grid barrier's release fence and raises a
+// flag; each reader sees the flag, invalidates only its L1 (the barrier's L1-only acquire)
+// and re-reads the block, counting words that are not `gen`.  Every spin is bounded; a
+// timed-out spin counts as a failure.  out[0]: stale words, out[1]: timeouts.
+constexpr int kCohWords = 16384;
+constexpr int kCohBlocks = 16;
+__device__ bool coh_spin(unsigned* f, unsigned v) {
+  for (int it = 0; it < (1 << 22); ++it) {
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= v) return true;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  return false;
+}
+__global__ __launch_bounds__(256) void k_coherence_check(unsigned* buf, unsigned* flags, unsigned* out, unsigned gen) {
+  __shared__ int ok;
+  if (blockIdx.x > 0) {
+    unsigned acc = 0;
+    for (int i = threadIdx.x; i < kCohWords; i += 256) acc += buf[i];
+    if (acc == 0x9e3779b9u) out[3] = acc;  // keeps the first read
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __hip_atomic_fetch_add(flags + 0, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      ok = coh_spin(flags + 1, gen) ? 1 : 0;
+      asm volatile("buffer_inv sc0" ::: "memory");
+    }
+    __syncthreads();
+    unsigned stale = 0;
+    for (int i = threadIdx.x; i < kCohWords; i += 256) stale += buf[i] != gen;
+    atomicAdd(out, stale);
+    if (threadIdx.x == 0 && !ok) atomicAdd(out + 1, 1u);
+  } else {
+    if (threadIdx.x == 0) ok = coh_spin(flags + 0, kCohBlocks - 1) ? 1 : 0;
+    __syncthreads();
+    for (int i = threadIdx.x; i < kCohWords; i += 256) buf[i] = gen;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(flags + 1, gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      if (!ok) atomicAdd(out + 1, 1u);
+    }
+  }
+}
+__global__ void k_coherence_fill(unsigned* buf, unsigned v, unsigned* flags, unsigned* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < kCohWords) buf[i] = v;
+  if (i < 4) {
+    flags[i] = 0u;
+    out[i] = 0u;
+  }
+}
+
 // =========================================================================================
 // host
 // =========================================================================================
@@ -206,11 +264,14 @@ struct moel_plan {
   size_t lds_fused;
   size_t lds_phase[kNumPhases];
   int launch_mode;  // moel_launch_mode
+  int acquire_mode;  // moel_acquire_mode
+  int l2_coherent;   // result of the coherence check on the plan's device
 };
 
 namespace {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
 
 template <int D>
 size_t attn_lds() { return sizeof(AttnLds<D>); }
@@ -236,6 +297,31 @@ bool hip_ok(hipError_t e) {
     return false;
   }
   return true;
+}
+
+// Runs the coherence check a few times on the current device; true when no stale word and no
+// timeout was seen.  The result is kept per device for the process.
+bool l2_coherent_device(int dev) {
+  static int known[64];  // 0 unknown, 1 coherent, 2 not
+  if (dev >= 0 && dev < 64 && known[dev] != 0) return known[dev] == 1;
+  unsigned* mem = nullptr;
+  hipStream_t s = nullptr;
+  bool good = hip_ok(hipMalloc(&mem, (kCohWords + 64) * sizeof(unsigned))) && hip_ok(hipStreamCreate(&s));
+  unsigned* buf = mem;
+  unsigned* flags = mem + kCohWords;
+  unsigned* out = mem + kCohWords + 32;
+  for (unsigned rep = 0; good && rep < 4; ++rep) {
+    const unsigned gen = 0x5a000001u + rep;
+    hipLaunchKernelGGL(k_coherence_fill, dim3(kCohWords / 256), dim3(256), 0, s, buf, gen - 1, flags, out);
+    hipLaunchKernelGGL(k_coherence_check, dim3(kCohBlocks), dim3(256), 0, s, buf, flags, out, gen);
+    unsigned h[2] = {1u, 1u};
+    good = hip_ok(hipGetLastError()) && hip_ok(hipStreamSynchronize(s)) &&
+           hip_ok(hipMemcpy(h, out, sizeof(h), hipMemcpyDeviceToHost)) && h[0] == 0 && h[1] == 0;
+  }
+  if (s != nullptr) (void)hipStreamDestroy(s);
+  if (mem != nullptr) (void)hipFree(mem);
+  if (dev >= 0 && dev < 64) known[dev] = good ? 1 : 2;
+  return good;
 }
 
 template <int D>
@@ -264,6 +350,7 @@ moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, 
   moel_status st = moel_validate_call(&plan->cfg, w, k_cache, v_cache, x, T, pos, window, y);
   if (st != MOEL_OK) return st;
   p = plan->base;
+  p.l2_coherent = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
   p.T = T;
   p.pos = pos;
   p.window = window;
@@ -320,6 +407,14 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
   if (!coop) return MOEL_ERR_UNSUPPORTED;
 
+  {
+    // the expert phases split their tile cost C (< tiles per expert * 17 * slots) over the
+    // workgroups in 32-bit arithmetic: C * workgroups must stay below 2^31
+    const int64_t rows = std::max(cfg->inter, cfg->pooled) / cfg->n_shards;
+    const int64_t tpe = rows / (cfg->expert_dtype == MOEL_EXPERT_NVFP4 ? 64 : 16);
+    if (tpe * 17 * MOEL_MAX_TOKENS * cfg->top_k * prop.multiProcessorCount >= ((int64_t)1 << 31))
+      return MOEL_ERR_SHAPE;
+  }
   moel_plan* plan = new (std::nothrow) moel_plan();
   if (plan == nullptr) return MOEL_ERR_HIP;
   plan->cfg = *cfg;
@@ -337,7 +432,6 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     return o;
   };
   const size_t o_ctrl = take((size_t)kCtrlWords * 4);
-  const size_t o_ss2 = take((size_t)nwg * kMaxT * 4);
   const size_t o_q = take((size_t)kMaxT * Hq * D * 4);
   const size_t o_ao = take((size_t)nwg * plan->grp * kMaxT * D * 4);
   const size_t o_aml = take((size_t)nwg * plan->grp * kMaxT * 2 * 4);
@@ -415,7 +509,6 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.stride_up = moel_packed_experts_bytes(cfg, 1) / (size_t)E;
   b.stride_down = moel_packed_experts_bytes(cfg, 2) / (size_t)E;
   b.ctrl = reinterpret_cast<unsigned*>(ws + o_ctrl);
-  b.ss2 = reinterpret_cast<float*>(ws + o_ss2);
   b.q_buf = reinterpret_cast<float*>(ws + o_q);
   b.attn_o = reinterpret_cast<float*>(ws + o_ao);
   b.attn_ml = reinterpret_cast<float*>(ws + o_aml);
@@ -461,9 +554,12 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     return ok ? MOEL_ERR_UNSUPPORTED : MOEL_ERR_HIP;
   }
   plan->launch_mode = MOEL_LAUNCH_PLAIN;
+  plan->acquire_mode = MOEL_ACQUIRE_AUTO;
+  plan->l2_coherent = l2_coherent_device(dev) ? 1 : 0;
   if (std::getenv("MOEL_LOG"))
-    std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu\n",
-                 H, Hq, cfg->n_kv_heads, D, P, I, E, k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx);
+    std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu l2_coherent=%d\n",
+                 H, Hq, cfg->n_kv_heads, D, P, I, E, k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx,
+                 plan->l2_coherent);
   *out = plan;
   return MOEL_OK;
 }
@@ -579,6 +675,14 @@ moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode) {
   plan->launch_mode = mode;
   return MOEL_OK;
 }
+
+moel_status moel_plan_set_acquire(moel_plan* plan, int32_t mode) {
+  if (plan == nullptr || (mode != MOEL_ACQUIRE_AUTO && mode != MOEL_ACQUIRE_L2_INVALIDATE)) return MOEL_ERR_ARG;
+  plan->acquire_mode = mode;
+  return MOEL_OK;
+}
+
+int32_t moel_plan_l2_coherent(const moel_plan* plan) { return plan == nullptr ? -1 : plan->l2_coherent; }
 
 moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
                                       const float* x, int32_t T, int32_t pos, int32_t window, float* y,

@@ -17,8 +17,8 @@ enum Phase {
   kPhQkv = 1,       // RMSNorm 1 + QKV projection + RoPE + q store + KV-cache write
   kPhAttn = 2,      // attention partials per (kv head, key chunk)
   kPhAttnMerge = 3, // merge of the key-chunk partials -> o (bf16)
-  kPhOproj = 4,     // o-projection + residual -> h, partial sums of h^2
-  kPhRouterPool = 5,// router logits and pooler
+  kPhOproj = 4,     // o-projection + residual -> h
+  kPhRouterPool = 5,// RMSNorm 2 + router logits and pooler
   kPhGemm1 = 6,     // routing tables + expert gate/up + SwiGLU -> a (bf16)
   kPhGemm2 = 7,     // expert down projection -> d (fp32)
   kPhCombine = 8,   // gate-weighted combine over a token's slots -> m (bf16)
@@ -34,6 +34,9 @@ struct LayerParams {
   // call
   int T, pos, window;
   int nwg;
+  // 1: the XCDs' L2 caches are kept coherent for the plan's memory (checked when the plan is
+  // created), so a barrier's acquire invalidates only the L1; 0: it also invalidates the L2
+  int l2_coherent;
   // attention decomposition (per call)
   int attn_lo, attn_nkeys, attn_chunk, attn_nchunks;
   // weights (packed)
@@ -59,7 +62,6 @@ struct LayerParams {
   const float* rope_cos;  // [kv_cap][D/2]
   const float* rope_sin;
   // scratch (plan workspace)
-  float* ss2;       // [nwg][16]
   float* q_buf;     // [16][Hq*D]
   float* attn_o;    // [items][grp][16][D]
   float* attn_ml;   // [items][grp][16][2]

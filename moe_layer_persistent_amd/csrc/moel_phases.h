@@ -11,8 +11,10 @@
 //
 // Packed weight layouts (produced by the pack kernels in moel_kernels.hip):
 //   dense bf16 [N, K]  : 16-row tiles; per tile K/32 steps of 1 KiB; in a step, lane l holds
-//                        the 8 bf16 of row (l % 16), k = 32*step + 8*(l / 16) + 0..7 -- the
-//                        B operand of one 16x16x32 MFMA.
+//                        8 bf16 of row (l % 16): k = 32*step + 4q + 0..3 and 32*step + 16 + 4q
+//                        + 0..3 with q = l / 16 -- the B operand of one 16x16x32 MFMA.  The
+//                        A operand takes the same k, so that the four lanes of a token read one
+//                        contiguous 64-byte piece of the fp32 activation row per load.
 //   NVFP4 expert [N, K]: 64-row tiles; per tile K/64 "pairs" of 2304 bytes: two 1 KiB code
 //                        steps (lane l: 32 codes of row l, k = 32*step + 0..31, low nibble
 //                        first) then 256 bytes of scales (lane l: the 4 E4M3 block scales of
@@ -61,63 +63,18 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, u32x4& 
 }
 
 // ------------------------------------------------------------------------------------------
-// RMSNorm statistics
-// ------------------------------------------------------------------------------------------
-// rstd of every token from the per-workgroup partial sums, in a fixed summation order
-// (32 interleaved subsets, then the subsets in order).  `tmp` is 32*16 floats of LDS,
-// `out` 16 floats of LDS.  Returns this lane's token's value.
-__device__ __forceinline__ float wg_rstd(const float* ss, int nwg, int H, float eps, float* tmp, float* out) {
-  const int t = threadIdx.x & 15, q = threadIdx.x >> 4;  // q = 0..31
-  float s = 0.f;
-  for (int w = q; w < nwg; w += 32) s += gl(ss)[w * kMaxT + t];
-  tmp[q * kMaxT + t] = s;
-  lds_barrier();
-  if (threadIdx.x < kMaxT) {
-    float a = 0.f;
-    for (int j = 0; j < 32; ++j) a += tmp[j * kMaxT + threadIdx.x];
-    out[threadIdx.x] = 1.0f / sqrtf(a / (float)H + eps);
-  }
-  lds_barrier();
-  return out[lane_id() & 15];
-}
-
-// ------------------------------------------------------------------------------------------
-// A-operand sources of the dense contractions: lane supplies A[token][k .. k+7] as hi + lo.
-// ------------------------------------------------------------------------------------------
+// A-operand sources of the dense contractions: lane supplies A[token][k .. k+3] and
+// A[token][k+16 .. k+19] (k = 32*step + 4q, the packed weights' k order) as hi + lo.
 // Rows of tokens t >= T read the row of token T-1 (their products are computed and never
 // read), so that no load in the streaming loops depends on a branch.
-struct ANorm {  // v * rstd * gamma computed on the fly from an fp32 row
-  static constexpr bool kStats = false;
-  const float* v;
-  int ld;
-  const uint16_t* gamma;
-  float rstd;  // of this lane's token
-  int T;
-  struct Raw {
-    float4 a, b;
-    u32x4 g;
-  };
-  // the same source with its workgroup-uniform fields in scalar registers
-  __device__ __forceinline__ ANorm scalar() const { return ANorm{uniform(v), uniform(ld), uniform(gamma), rstd, uniform(T)}; }
-  __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
-    const float* src = v + (size_t)tok * ld + k;
-    r.a = ldgf4(src);
-    r.b = ldgf4(src + 4);
-    r.g = ldg16(gamma + k);
-  }
-  __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
-    float4 a = r.a, b = r.b;
-    a.x = a.x * rstd * bf_lo(r.g[0]);
-    a.y = a.y * rstd * bf_hi(r.g[0]);
-    a.z = a.z * rstd * bf_lo(r.g[1]);
-    a.w = a.w * rstd * bf_hi(r.g[1]);
-    b.x = b.x * rstd * bf_lo(r.g[2]);
-    b.y = b.y * rstd * bf_hi(r.g[2]);
-    b.z = b.z * rstd * bf_lo(r.g[3]);
-    b.w = b.w * rstd * bf_hi(r.g[3]);
-    split8(a, b, hi, lo);
-  }
-};
+// ------------------------------------------------------------------------------------------
+// gamma[k .. k+3] and gamma[k+16 .. k+19]
+__device__ __forceinline__ u32x4 ldg_gamma(const uint16_t* g) {
+  const u32x2 a = ldg8(g), b = ldg8(g + 16);
+  return u32x4{a[0], a[1], b[0], b[1]};
+}
+// Rows of tokens t >= T read the row of token T-1 (their products are computed and never
+// read), so that no load in the streaming loops depends on a branch.
 // v * gamma from an fp32 row, plus the row's sum of squares: the contraction of an RMS-normed
 // row is rstd * (W . (v * gamma)), so the pass that reads the row for the contraction also
 // yields rstd (dense_pass leaves it in DenseLds::rstd) and the epilogue scales by it.
@@ -138,8 +95,8 @@ struct AGamma {
   __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
     const float* src = v + (size_t)tok * ld + k;
     r.a = ldgf4(src);
-    r.b = ldgf4(src + 4);
-    r.g = ldg16(gamma + k);
+    r.b = ldgf4(src + 16);
+    r.g = ldg_gamma(gamma + k);
   }
   __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
     float4 a = r.a, b = r.b;
@@ -176,7 +133,7 @@ struct AF32 {  // a stored fp32 row
   __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
     const float* src = v + (size_t)tok * ld + k;
     r.a = ldgf4(src);
-    r.b = ldgf4(src + 4);
+    r.b = ldgf4(src + 16);
   }
   __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
     split8(r.a, r.b, hi, lo);
@@ -237,7 +194,7 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
     // cover one contiguous stretch of each tile
     const int ns = S / nkw;
     const int tok = (lane & 15) < A.T ? (lane & 15) : A.T - 1;
-    const int kq = 8 * (lane >> 4) + 32 * wv;
+    const int kq = 4 * (lane >> 4) + 32 * wv;
     const uint8_t* base[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -319,8 +276,9 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
 // Octet range of a workgroup for a contraction with `tiles` 16-row tiles.
 __device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo, int& hi) {
   const int n = 2 * tiles;
-  lo = (int)((long)wg * n / nwg);
-  hi = (int)((long)(wg + 1) * n / nwg);
+  // 32-bit: n * nwg < 2^32 for every accepted shape (n <= N / 8)
+  lo = (int)((unsigned)wg * (unsigned)n / (unsigned)nwg);
+  hi = (int)((unsigned)(wg + 1) * (unsigned)n / (unsigned)nwg);
 }
 
 // Runs dense_pass over the workgroup's rows in groups of <= 4 tiles and calls
@@ -623,43 +581,30 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
 }
 
 // ------------------------------------------------------------------------------------------
-// o-projection + residual -> h (fp32), and per-workgroup partial sums of h^2.
+// o-projection + residual -> h (fp32).
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AF32 A{p.o_buf, p.Hq * p.D, p.T};
-  float part = 0.f;  // thread t < 16 accumulates token t over the workgroup's rows
   dense_phase(p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
                   const int n = (tf + j) * 16 + r;
-                  float hv = 0.f;
-                  if (t < p.T && octet_in(n, lo, hi)) {
-                    hv = gl(p.x)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
-                    gl(p.h_buf)[(size_t)t * p.H + n] = hv;
-                  }
-                  L.aux[(j * 16 + r) * kMaxT + t] = hv;
+                  if (t < p.T && octet_in(n, lo, hi))
+                    gl(p.h_buf)[(size_t)t * p.H + n] = gl(p.x)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
                 }
-                lds_barrier();
-                if (threadIdx.x < kMaxT)
-                  for (int j = 0; j < nt; ++j)
-                    for (int r = 0; r < 16; ++r) {
-                      const float hv = L.aux[(j * 16 + r) * kMaxT + threadIdx.x];
-                      part = fmaf(hv, hv, part);
-                    }
               });
-  if (threadIdx.x < kMaxT) gl(p.ss2)[wg * kMaxT + threadIdx.x] = part;
 }
 
 // ------------------------------------------------------------------------------------------
 // Router logits and pooler from hn = h * rstd2 * gamma2, one contraction over the stacked
-// rows [router; pooler].
+// rows [router; pooler].  RMSNorm 2 is folded in as for RMSNorm 1: the pass contracts
+// h * gamma2, yields rstd2 from the h it reads, and the epilogue scales by it.
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  const float rs = wg_rstd(p.ss2, p.nwg, p.H, p.eps, reinterpret_cast<float*>(L.red), L.aux);
-  ANorm A{p.h_buf, p.H, p.gamma2, rs, p.T};
+  AGamma A{p.h_buf, p.H, p.gamma2, p.T, p.eps};
   const int te = p.E / 16;
   dense_phase(p.w_router, te, p.w_pool, p.P / 16, p.H, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
@@ -667,7 +612,7 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
                   const int n = (tf + j) * 16 + r;
                   if (t >= p.T || !octet_in(n, lo, hi)) continue;
-                  const float v = L.fin[(j * 16 + r) * kMaxT + t];
+                  const float v = L.fin[(j * 16 + r) * kMaxT + t] * L.rstd[t];
                   if (n < p.E) {
                     gl(p.logits)[t * p.E + n] = v;
                     if (p.dbg_logits) gl(p.dbg_logits)[t * p.E + n] = v;
@@ -1276,12 +1221,12 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
       arow[rt] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
     }
   }
-  const int kq = 8 * (lane >> 4);
+  const int kq = 4 * (lane >> 4);  // the packed weights' k order
   auto aload = [&](int rt, int s) -> u32x4 {
     u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
     if (arow[rt] != nullptr) {
       const float* src = arow[rt] + 32 * s + kq;
-      split8(ldgf4(src), ldgf4(src + 4), hi, lo);
+      split8(ldgf4(src), ldgf4(src + 16), hi, lo);
     }
     return lo_row ? lo : hi;
   };
@@ -1348,26 +1293,28 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
   // Tile (u, j) covers [P_u + j c_u, P_u + (j+1) c_u) with P_u = tpe (A u + sum_{v<u} n_e(v))
   // = tpe (A u + active_off[u]); a workgroup takes the tiles whose cost interval starts in
   // its share [wg C / nwg, (wg+1) C / nwg).
+  // 32-bit: C * nwg < 2^31 for every accepted shape (checked at plan creation)
   const int A = GATEUP ? 16 : 9;
-  const long C = (long)tpe * (A * U + uniform(R.active_off[U]));
-  auto first_tile = [&](long c) -> int {  // first tile whose cost interval starts at or after c
+  const int C = tpe * (A * U + uniform(R.active_off[U]));
+  auto first_tile = [&](int c) -> int {  // first tile whose cost interval starts at or after c
     if (c >= C) return U * tpe;
     int lo = 0, hi = U - 1;  // largest u with P_u <= c (P_0 = 0 <= c)
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if ((long)tpe * (A * mid + uniform(R.active_off[mid])) <= c) lo = mid;
+      if (tpe * (A * mid + uniform(R.active_off[mid])) <= c) lo = mid;
       else hi = mid - 1;
     }
-    const long Pu = (long)tpe * (A * lo + uniform(R.active_off[lo]));
+    const int Pu = tpe * (A * lo + uniform(R.active_off[lo]));
     const int cu = A + uniform(R.active_off[lo + 1]) - uniform(R.active_off[lo]);
-    return lo * tpe + (int)((c - Pu + cu - 1) / cu);
+    return lo * tpe + (int)((unsigned)(c - Pu + cu - 1) / (unsigned)cu);
   };
   // Static part: the first 7/8 of the cost, split evenly.  Dynamic part: the remaining tiles,
   // one per hand-out from a device-wide counter, so that workgroups that run slower (for any
   // reason: more tokens per tile, a busier XCD) take fewer of them.  Which workgroup computes
   // a tile does not change its arithmetic, so results stay bitwise reproducible.
-  const long Cs = C - C / 8;
-  const int t0 = first_tile((long)wg * Cs / p.nwg), t1 = first_tile((long)(wg + 1) * Cs / p.nwg);
+  const int Cs = C - C / 8;
+  const int t0 = first_tile((int)((unsigned)wg * (unsigned)Cs / (unsigned)p.nwg));
+  const int t1 = first_tile((int)((unsigned)(wg + 1) * (unsigned)Cs / (unsigned)p.nwg));
   const int t_dyn = first_tile(Cs), t_end = U * tpe;
   auto ctr = gl(p.ctrl) + kWork + 32 * (GATEUP ? 0 : 1);
   if (fp4) {

@@ -33,6 +33,9 @@ moel_status moel_validate_config(const moel_config* c) {
   if (c->expert_dtype != MOEL_EXPERT_NVFP4 && c->expert_dtype != MOEL_EXPERT_BF16) return MOEL_ERR_ARG;
   if (c->top_k > c->n_experts || c->top_k > 8) return MOEL_ERR_SHAPE;
   if (c->hidden % 256 != 0) return MOEL_ERR_SHAPE;
+  // bounds that keep the dense phases' row splits in 32-bit arithmetic
+  if (c->hidden > 65536 || c->pooled > 65536 || c->inter > 131072 || c->n_q_heads * c->head_dim > 65536)
+    return MOEL_ERR_SHAPE;
   if (c->head_dim != 64 && c->head_dim != 128) return MOEL_ERR_SHAPE;
   if (c->n_q_heads % c->n_kv_heads != 0 || c->n_q_heads / c->n_kv_heads > 8) return MOEL_ERR_SHAPE;
   if (c->n_experts % 16 != 0 || c->n_experts > 512) return MOEL_ERR_SHAPE;

@@ -23,13 +23,22 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.moel_abi_version() == 2
+    assert L.moel_abi_version() == 3
 
 
 def test_plan_options_reject_a_missing_plan():
     L = binding.lib()
     assert L.moel_plan_set_launch(None, binding.MOEL_LAUNCH_PLAIN) == binding.MOEL_ERR_ARG
     assert L.moel_plan_set_launch(None, 5) == binding.MOEL_ERR_ARG
+    assert L.moel_plan_set_acquire(None, binding.MOEL_ACQUIRE_AUTO) == binding.MOEL_ERR_ARG
+    assert L.moel_plan_l2_coherent(None) == -1
+
+
+def test_shapes_beyond_the_32_bit_work_split_are_rejected():
+    L = binding.lib()
+    for field, value in (("hidden", 1 << 17), ("pooled", 1 << 17), ("inter", 1 << 18)):
+        c = _cfg(**{field: value})
+        assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_ERR_SHAPE, field
 
 
 def _cfg(**kw):

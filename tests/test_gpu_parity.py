@@ -86,6 +86,28 @@ def test_plain_and_cooperative_launches_agree():
         run.plan.set_launch(7)
 
 
+def test_l1_only_and_l2_invalidating_acquire_agree():
+    """The grid barriers' L1-only acquire (taken where the device keeps its XCDs' L2 caches
+    coherent) gives the same bytes as the agent-scope acquire that also invalidates the L2,
+    and as the one-kernel-per-step chain, whose kernel boundaries order everything."""
+    w = synth.small_workload(T=16, pos=1500, window=0, hidden=2048, n_q_heads=16, n_kv_heads=4,
+                             head_dim=128, n_experts=64, top_k=8, pooled=1024, inter=1024)
+    run = harness.GpuRun(w)
+    _log(f"l2_coherent {run.plan.l2_coherent}")
+    a = run.run(fused=True)
+    run.plan.set_acquire(binding.MOEL_ACQUIRE_L2_INVALIDATE)
+    b = run.run(fused=True)
+    run.plan.set_acquire(binding.MOEL_ACQUIRE_AUTO)
+    c = run.run(fused=False)
+    d = run.run(fused=True)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(a[k], b[k]), k
+        assert _same_bytes(a[k], c[k]), k
+        assert _same_bytes(a[k], d[k]), k
+    with pytest.raises(binding.MoelError):
+        run.plan.set_acquire(3)
+
+
 def test_timestamps_leave_outputs_bit_identical():
     w = synth.small_workload(T=8, pos=200, window=64)
     run = harness.GpuRun(w)
