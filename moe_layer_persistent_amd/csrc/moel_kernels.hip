@@ -444,6 +444,9 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   const size_t o_pls = take((size_t)kMaxT * P * 4);
   const size_t o_as = take((size_t)kMaxT * k * I * 4);
   const size_t o_m = take((size_t)kMaxT * P * 4);
+  const size_t o_oop = take((size_t)kMaxT * Hq * D * 4);
+  const size_t o_hop = take((size_t)kMaxT * H * 4);
+  const size_t o_mop = take((size_t)kMaxT * P * 4);
   const size_t o_cos = take((size_t)cfg->kv_capacity * (D / 2) * 4);
   const size_t o_sin = take((size_t)cfg->kv_capacity * (D / 2) * 4);
   plan->ws_bytes = off;
@@ -521,6 +524,9 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.pl_split = reinterpret_cast<uint16_t*>(ws + o_pls);
   b.a_split = reinterpret_cast<uint16_t*>(ws + o_as);
   b.m_buf = reinterpret_cast<float*>(ws + o_m);
+  b.o_op = reinterpret_cast<float*>(ws + o_oop);
+  b.h_op = reinterpret_cast<float*>(ws + o_hop);
+  b.m_op = reinterpret_cast<float*>(ws + o_mop);
   b.rope_cos = reinterpret_cast<const float*>(ws + o_cos);
   b.rope_sin = reinterpret_cast<const float*>(ws + o_sin);
 

@@ -76,6 +76,11 @@ struct LayerParams {
   uint16_t* a_split;   // [16*topk][I/4][8]
   float* d_buf;     // [16*topk][P]
   float* m_buf;     // [16][P]
+  // o, h and m again in the operand order of the dense contractions that read them (see
+  // op_index): one 2 KiB block per 32-element k step, lane l's 8 values at 16 l and 1024 + 16 l
+  float* o_op;
+  float* h_op;
+  float* m_op;
   unsigned* ctrl;   // barrier counter, exit counter, status, abort
   // debug (optional)
   int* dbg_idx;

@@ -121,28 +121,80 @@ struct AGamma {
     return fmaf(r.b.w, r.b.w, s);
   }
 };
-struct AF32 {  // a stored fp32 row
+// Index (in floats) of element (t, k) of a [16][K] fp32 activation stored in operand order:
+// per 32-element k step one 2 KiB block, in which lane l = t + 16 q of the contraction finds
+// its 8 values k = 4q + 0..3 at float 4 l and k = 16 + 4q + 0..3 at float 256 + 4 l.  A wave's
+// load of a step is then two contiguous 1 KiB reads, where the row-major layout spreads each
+// over 16 rows.  Rows t >= T are left as they are (their products are never read).
+__device__ __forceinline__ size_t op_index(int t, int k) {
+  const int r = k & 31;
+  return (size_t)(k >> 5) * 512 + ((r >> 4) << 8) + (((r & 15) >> 2) << 6) + 4 * t + (r & 3);
+}
+// An fp32 activation in operand order (lane l reads its own token slot l % 16).
+struct AOp {
   static constexpr bool kStats = false;
   const float* v;
-  int ld;
   int T;
   struct Raw {
     float4 a, b;
   };
-  __device__ __forceinline__ AF32 scalar() const { return AF32{uniform(v), uniform(ld), uniform(T)}; }
-  __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
-    const float* src = v + (size_t)tok * ld + k;
+  __device__ __forceinline__ AOp scalar() const { return AOp{uniform(v), uniform(T)}; }
+  __device__ __forceinline__ void fetch(int, int k, Raw& r) const {
+    const float* src = v + (size_t)(k >> 5) * 512 + 4 * lane_id();
     r.a = ldgf4(src);
-    r.b = ldgf4(src + 16);
+    r.b = ldgf4(src + 256);
   }
   __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
     split8(r.a, r.b, hi, lo);
   }
 };
+// v * gamma from an fp32 activation in operand order, plus the sums of squares (as AGamma).
+struct AGammaOp {
+  static constexpr bool kStats = true;
+  const float* v;
+  const uint16_t* gamma;
+  int T;
+  float eps;
+  struct Raw {
+    float4 a, b;
+    u32x4 g;
+  };
+  __device__ __forceinline__ AGammaOp scalar() const {
+    return AGammaOp{uniform(v), uniform(gamma), uniform(T), __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, eps)))};
+  }
+  __device__ __forceinline__ void fetch(int, int k, Raw& r) const {
+    const float* src = v + (size_t)(k >> 5) * 512 + 4 * lane_id();
+    r.a = ldgf4(src);
+    r.b = ldgf4(src + 256);
+    r.g = ldg_gamma(gamma + k);
+  }
+  __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
+    float4 a = r.a, b = r.b;
+    a.x *= bf_lo(r.g[0]);
+    a.y *= bf_hi(r.g[0]);
+    a.z *= bf_lo(r.g[1]);
+    a.w *= bf_hi(r.g[1]);
+    b.x *= bf_lo(r.g[2]);
+    b.y *= bf_hi(r.g[2]);
+    b.z *= bf_lo(r.g[3]);
+    b.w *= bf_hi(r.g[3]);
+    split8(a, b, hi, lo);
+  }
+  __device__ __forceinline__ float sq(const Raw& r) const {
+    float s = r.a.x * r.a.x;
+    s = fmaf(r.a.y, r.a.y, s);
+    s = fmaf(r.a.z, r.a.z, s);
+    s = fmaf(r.a.w, r.a.w, s);
+    s = fmaf(r.b.x, r.b.x, s);
+    s = fmaf(r.b.y, r.b.y, s);
+    s = fmaf(r.b.z, r.b.z, s);
+    return fmaf(r.b.w, r.b.w, s);
+  }
+};
 
 // ------------------------------------------------------------------------------------------
 // Dense contraction over a workgroup's rows: out[tok][row] = sum_k A[tok][k] * W[row][k].
-// Rows are assigned in octets (8 rows = one 128-byte line of every 1 KiB step), so that
+// Rows are assigned in octets (8 rows = four 128-byte lines of every 1 KiB step), so that
 // workgroups never share a cache line.  NT (1..4) tiles of 16 rows per pass; the k-waves
 // split K evenly and stream it through a ring of DEPTH steps; partials meet in LDS.  Lanes of
 // an octet outside the workgroup's range load their partner octet's line instead (the same
@@ -576,7 +628,9 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
       }
       M = Mg;
     }
-    gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = num / den;
+    const float o = num / den;
+    gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
+    gl(p.o_op)[op_index(t, h * p.D + d)] = o;
   }
 }
 
@@ -585,14 +639,17 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  AF32 A{p.o_buf, p.Hq * p.D, p.T};
+  AOp A{p.o_op, p.T};
   dense_phase(p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
                   const int n = (tf + j) * 16 + r;
-                  if (t < p.T && octet_in(n, lo, hi))
-                    gl(p.h_buf)[(size_t)t * p.H + n] = gl(p.x)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
+                  if (t < p.T && octet_in(n, lo, hi)) {
+                    const float h = gl(p.x)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
+                    gl(p.h_buf)[(size_t)t * p.H + n] = h;
+                    gl(p.h_op)[op_index(t, n)] = h;
+                  }
                 }
               });
 }
@@ -604,7 +661,7 @@ __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  AGamma A{p.h_buf, p.H, p.gamma2, p.T, p.eps};
+  AGammaOp A{p.h_op, p.gamma2, p.T, p.eps};
   const int te = p.E / 16;
   dense_phase(p.w_router, te, p.w_pool, p.P / 16, p.H, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
@@ -1392,13 +1449,14 @@ __device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
     for (int k = 0; k < p.topk; ++k)
       s = fmaf(R.gate[t * p.topk + k], gl(p.d_buf)[(size_t)(t * p.topk + k) * p.P + pc], s);
     gl(p.m_buf)[(size_t)t * p.P + pc] = s;
+    gl(p.m_op)[op_index(t, pc)] = s;
   }
 }
 
 // y = h + m W_unpool^T
 __device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  AF32 A{p.m_buf, p.P, p.T};
+  AOp A{p.m_op, p.T};
   dense_phase(p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, p.nwg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
