@@ -90,10 +90,14 @@ def _rotate(vec: List[float], position: int, theta: float) -> List[float]:
     return out
 
 
-def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool = True) -> Dict:
+def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool = True,
+               parents=None) -> Dict:
     """Same contract as layer.layer_step on tiny inputs given as nested lists / arrays.
 
     expert_raw(e) returns {"gate": (codes, scales, ts) | W, "up": ..., "down": ...}.
+    parents: token-tree parent of every token (-1 for a root), None for the chain; a token's
+    position is pos plus its number of ancestors, and it sees the step's tokens that are
+    itself or its ancestors.
     """
     x = [[float(v) for v in row] for row in inp["x"]]
     T, H = len(x), len(x[0])
@@ -104,13 +108,24 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
     kc = [[[float(inp["k_cache"][g][j][d]) for d in range(D)] for j in range(C)] for g in range(Hkv)]
     vc = [[[float(inp["v_cache"][g][j][d]) for d in range(D)] for j in range(C)] for g in range(Hkv)]
 
+    # token positions and, per token, the step's tokens it may see (itself and its ancestors)
+    par = [t - 1 for t in range(T)] if parents is None else [int(v) for v in parents]
+    posn, sees = [], []
+    for t in range(T):
+        chain, i = [], t
+        while i != -1:
+            chain.append(i)
+            i = par[i]
+        posn.append(pos + len(chain) - 1)
+        sees.append(set(chain))
+
     # RMSNorm 1, QKV projection, RoPE, rounding, cache write
     q_all, k_all, v_all = [], [], []
     for t in range(T):
         xn = _norm(x[t], [float(v) for v in inp["gamma1"]], dims.rms_eps)
         row = [_dot(xn, [float(v) for v in w_qkv[n]]) for n in range(len(w_qkv))]
-        qh = [_rotate(row[h * D:(h + 1) * D], pos + t, dims.rope_theta) for h in range(Hq)]
-        kh = [_rotate(row[(Hq + g) * D:(Hq + g + 1) * D], pos + t, dims.rope_theta) for g in range(Hkv)]
+        qh = [_rotate(row[h * D:(h + 1) * D], posn[t], dims.rope_theta) for h in range(Hq)]
+        kh = [_rotate(row[(Hq + g) * D:(Hq + g + 1) * D], posn[t], dims.rope_theta) for g in range(Hkv)]
         vh = [row[(Hq + Hkv + g) * D:(Hq + Hkv + g + 1) * D] for g in range(Hkv)]
         q_all.append([list(qv) for qv in qh])
         k_all.append([[r_bf16(v) for v in kv] for kv in kh])
@@ -123,11 +138,14 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
     group = Hq // Hkv
     h_all = []
     for t in range(T):
-        p = pos + t
+        p = posn[t]
         o_flat = []
         for hh in range(Hq):
             g = hh // group
-            keys = [j for j in range(0, p + 1) if window == 0 or j > p - window]
+            # cached keys by position; the step's slot pos + i holds token i at position posn[i]
+            keys = [j for j in range(0, pos) if j <= p and (window == 0 or j > p - window)]
+            keys += [pos + i for i in range(T)
+                     if i in sees[t] and (window == 0 or posn[i] > p - window)]
             scores = [_dot(q_all[t][hh], kc[g][j]) / math.sqrt(D) for j in keys]
             mx = max(scores)
             ws = [math.exp(s - mx) for s in scores]

@@ -18,6 +18,13 @@ with its rationale in the design notes):
   * RoPE, rotate-half pairing (i, i + D/2), theta = 10000, position pos + t,
     on q and k of every layer
   * key j visible to the token at position p iff j <= p and (W == 0 or j > p - W)
+  * token-tree verify (the verify pass checks a tree of candidate tokens rather than
+    a chain; the pages give neither its mask nor its positions): node t with parent
+    p(t) (-1: a root, attached to the cached prefix) sits at position pos + depth(t),
+    its key and value are written to cache slot pos + t, and it sees the cached keys
+    by the window rule at its own position and, among the step's nodes, exactly its
+    ancestors and itself (by the same rule on their positions).  The chain
+    p(t) = t - 1 is the linear verify above.
   * GQA: q head h reads kv head floor(h * Hkv / Hq); score scale 1/sqrt(D)
   * router on the normalised hidden state (the pooler's input): top-k by logit
     descending with ties to the lower expert index, gates = softmax over the k
@@ -116,6 +123,51 @@ def attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: int,
     return o
 
 
+def tree_depths(parents) -> np.ndarray:
+    """Depth of every node of a token tree given by parent indices (-1: root; parents[t] < t)."""
+    depth = np.zeros(len(parents), dtype=np.int64)
+    for t, par in enumerate(parents):
+        if not (-1 <= par < t):
+            raise ValueError(f"parent of node {t} must lie in [-1, {t})")
+        depth[t] = 0 if par < 0 else depth[par] + 1
+    return depth
+
+
+def tree_attention(q: np.ndarray, k_cache: np.ndarray, v_cache: np.ndarray, pos: int,
+                   window: int, parents) -> np.ndarray:
+    """GQA attention of the T tree nodes over the (already updated) cache.
+
+    Node t at position pos + depth(t) sees cached key j < pos by the window rule at its
+    position, and the step's node i (slot pos + i, position pos + depth(i)) iff i is t or
+    an ancestor of t and the same rule holds for depth(i).
+    """
+    T, Hq, D = q.shape
+    Hkv = k_cache.shape[0]
+    grp = Hq // Hkv
+    depth = tree_depths(parents)
+    o = np.zeros((T, Hq, D))
+    scale = 1.0 / np.sqrt(D)
+    for t in range(T):
+        pt = pos + depth[t]
+        lo, _ = visible_range(pt, window)
+        slots = list(range(lo, pos))
+        anc, i = [], t
+        while i >= 0:
+            anc.append(i)
+            i = parents[i]
+        slots += [pos + i for i in sorted(anc) if window == 0 or pos + depth[i] > pt - window]
+        for g in range(Hkv):
+            heads = slice(g * grp, (g + 1) * grp)
+            K = k_cache[g, slots]
+            V = v_cache[g, slots]
+            s_ = (q[t, heads] @ K.T) * scale
+            s_ = s_ - s_.max(axis=1, keepdims=True)
+            p_ = np.exp(s_)
+            p_ /= p_.sum(axis=1, keepdims=True)
+            o[t, heads] = p_ @ V
+    return o
+
+
 def route(logits: np.ndarray, k: int):
     """Top-k per token by logit descending, ties to the lower expert index.
 
@@ -182,7 +234,8 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
 # the whole step
 # --------------------------------------------------------------------------------------------
 def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, experts: ExpertFn,
-               force_idx: Optional[np.ndarray] = None, moe_tokens=None) -> Dict[str, np.ndarray]:
+               force_idx: Optional[np.ndarray] = None, moe_tokens=None,
+               parents=None) -> Dict[str, np.ndarray]:
     """One layer step.  `inp` holds fp64 arrays (bf16-valued weights):
     x [T,H], gamma1 [H], w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq*D], gamma2 [H], w_router [E,H],
     w_pool [P,H], w_unpool [H,P], k_cache/v_cache [Hkv, C, D].
@@ -190,6 +243,8 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     force_idx [T, k] replaces the router's choice (gates are then the softmax over those
     logits).  moe_tokens limits the expert and unpooler work to a subset of tokens (y rows of
     the other tokens are returned as NaN); everything else is computed for all tokens.
+    parents [T] makes the tokens the nodes of a token tree (see the module docstring); None
+    is the chain.
     Returns y, the written K/V rows, routing and every intermediate.
     """
     x = np.asarray(inp["x"], dtype=np.float64)
@@ -203,7 +258,7 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     q = qkv[:, :Hq * D].reshape(T, Hq, D)
     k = qkv[:, Hq * D:(Hq + Hkv) * D].reshape(T, Hkv, D)
     v = qkv[:, (Hq + Hkv) * D:].reshape(T, Hkv, D)
-    positions = pos + np.arange(T)
+    positions = pos + (np.arange(T) if parents is None else tree_depths(parents))
     q_r = rope(q, positions, dims.rope_theta)
     k_exact = rope(k, positions, dims.rope_theta)
     k_r = bf16_round(k_exact)
@@ -213,7 +268,8 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     for t in range(T):
         k_cache[:, pos + t] = k_r[t]
         v_cache[:, pos + t] = v_r[t]
-    o = attention(q_r, k_cache, v_cache, pos, window)
+    o = (attention(q_r, k_cache, v_cache, pos, window) if parents is None
+         else tree_attention(q_r, k_cache, v_cache, pos, window, parents))
     h = x + o.reshape(T, Hq * D) @ inp["w_o"].T
 
     # MoE block

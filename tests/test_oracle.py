@@ -268,3 +268,96 @@ def test_cache_write_set_is_exact():
     written[:, w.pos:w.pos + w.T] = True
     assert not np.any(changed & ~written)
     np.testing.assert_array_equal(out["k_cache"][:, w.pos:w.pos + w.T].transpose(1, 0, 2), out["k_new"])
+
+
+# ---------------------------------------------------------------- token-tree verify
+# A 16-node tree of candidate tokens (two branches off the root, one of them branching again)
+TREE16 = [-1, 0, 1, 2, 0, 4, 5, 1, 7, 3, 9, 4, 11, 12, 2, 14]
+TREES = [
+    [-1, 0, 0, 1],           # root with two children, one grandchild
+    [-1, -1, 0, 1],          # two roots (both attach to the cached prefix)
+    [-1, 0, 1, 2],           # the chain
+]
+
+
+def _path(parents, t):
+    out = []
+    while t != -1:
+        out.append(t)
+        t = parents[t]
+    return out[::-1]
+
+
+def test_tree_depths_and_rejects_bad_parents():
+    np.testing.assert_array_equal(layer.tree_depths(TREE16), [len(_path(TREE16, t)) - 1 for t in range(16)])
+    with pytest.raises(ValueError):
+        layer.tree_depths([-1, 1])
+    with pytest.raises(ValueError):
+        layer.tree_depths([0])
+
+
+@pytest.mark.parametrize("tree", TREES, ids=["fork", "two_roots", "chain"])
+def test_tree_matches_bruteforce(tree):
+    shape = dict(TINY_SHAPES[0], T=len(tree), window=0)
+    w = synth.small_workload(**shape)
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    got = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w), parents=tree)
+    ref = brute.layer_step(f, dims, w.pos, w.window, _raw_getter(f, w), nvfp4=True, parents=tree)
+    assert got["idx"].tolist() == ref["idx"]
+    np.testing.assert_allclose(got["k_new"], np.array(ref["k_new"]), rtol=0, atol=0)
+    np.testing.assert_allclose(got["h"], np.array(ref["h"]), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(got["y"], np.array(ref["y"]), rtol=1e-9, atol=1e-10)
+
+
+def test_tree_window_matches_bruteforce():
+    """A window shorter than the tree's depth: the window rule applies to node positions."""
+    tree = [-1, 0, 1, 2, 1]
+    w = synth.small_workload(**dict(TINY_SHAPES[0], T=5, window=3, pos=9))
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    got = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w), parents=tree)
+    ref = brute.layer_step(f, dims, w.pos, w.window, _raw_getter(f, w), nvfp4=True, parents=tree)
+    np.testing.assert_allclose(got["h"], np.array(ref["h"]), rtol=1e-10, atol=1e-12)
+
+
+def test_chain_parents_are_the_chain():
+    w = synth.small_workload(**TINY_SHAPES[0])
+    _, f = _np_inputs(w)
+    a = layer.layer_step(f, _dims(w), w.pos, w.window, _experts(f, w))
+    b = layer.layer_step(f, _dims(w), w.pos, w.window, _experts(f, w), parents=list(range(-1, w.T - 1)))
+    np.testing.assert_allclose(b["y"], a["y"], rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(b["k_new"], a["k_new"])
+
+
+def test_tree_node_equals_the_chain_of_its_path():
+    """Every node of a tree computes what a chain verify of the root-to-node path computes for
+    its last token (attention sees the same keys at the same positions; the rest is per token)."""
+    w = synth.small_workload(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, pooled=32, inter=64,
+                             n_experts=8, top_k=3, window=0, pos=9, T=16)
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    tree = layer.layer_step(f, dims, w.pos, 0, _experts(f, w), parents=TREE16)
+    for t in (3, 6, 10, 13, 15):
+        path = _path(TREE16, t)
+        g = dict(f, x=f["x"][path])
+        chain = layer.layer_step(g, dims, w.pos, 0, _experts(f, w))
+        np.testing.assert_allclose(tree["o"][t], chain["o"][-1], rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(tree["k_new"][t], chain["k_new"][-1], rtol=0, atol=0)
+        np.testing.assert_allclose(tree["y"][t], chain["y"][-1], rtol=1e-10, atol=1e-11)
+        if tree["gap"][t] > 1e-9:
+            assert tree["idx"][t].tolist() == chain["idx"][-1].tolist()
+
+
+def test_tree_nodes_outside_the_path_do_not_matter():
+    w = synth.small_workload(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, pooled=32, inter=64,
+                             n_experts=8, top_k=3, window=0, pos=9, T=16)
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    a = layer.layer_step(f, dims, w.pos, 0, _experts(f, w), parents=TREE16)
+    g = dict(f, x=f["x"].copy())
+    off_path = [i for i in range(16) if i not in _path(TREE16, 13)]
+    g["x"][off_path] += 1.0
+    b = layer.layer_step(g, dims, w.pos, 0, _experts(f, w), parents=TREE16)
+    np.testing.assert_array_equal(a["y"][13], b["y"][13])
+    assert not np.array_equal(a["y"][off_path[-1]], b["y"][off_path[-1]])
