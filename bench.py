@@ -49,6 +49,10 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
+# a 16-node token tree: node t's parent (-1: root)
+TREE16 = [-1, 0, 1, 2, 0, 4, 5, 1, 7, 3, 9, 4, 11, 12, 2, 14]
+
+
 def measured_traffic(workload: str):
     """HBM bytes per launch of the fused kernel from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by the same counters on a copy of known size), or None
@@ -218,17 +222,19 @@ def main():
     idx = dbg["expert_idx"].cpu().numpy()
     alg_bytes, U = algorithmic_bytes(w, idx, w.pos, window, T)
 
-    def timed(fused, steps, warmup):
+    def timed(fused, steps, warmup, parents=None):
         """Back-to-back launches between two events on the launch stream: the average launch
         duration (us) over the timed region, and the host wall time (s)."""
         for i in range(warmup):
-            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream)
+            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
+                              parents=parents)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record(stream)
         for i in range(steps):
-            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream)
+            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
+                              parents=parents)
         b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -259,6 +265,9 @@ def main():
     plan.set_acquire(binding.MOEL_ACQUIRE_L2_INVALIDATE)
     inv_us, _ = timed(True, max(5, args.steps // 2), 2)
     plan.set_acquire(binding.MOEL_ACQUIRE_AUTO)
+    # the same step as a token-tree verify (16 nodes: two branches off the root, one branching
+    # again), which moves only positions and the attention mask
+    tree_us, _ = timed(True, max(5, args.steps // 2), 2, parents=TREE16)
     gbps = alg_bytes / (mean_us * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
     result = {
@@ -286,7 +295,8 @@ def main():
                        "single_launch_p10": round(float(np.percentile(durs, 10)), 2),
                        "single_launch_p90": round(float(np.percentile(durs, 90)), 2),
                        "cooperative_launch_back_to_back": round(coop_us, 2),
-                       "l2_invalidating_acquire_back_to_back": round(inv_us, 2)},
+                       "l2_invalidating_acquire_back_to_back": round(inv_us, 2),
+                       "token_tree_verify_back_to_back": round(tree_us, 2)},
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),

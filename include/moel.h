@@ -36,7 +36,7 @@ extern "C" {
 #endif
 
 #define MOEL_MAX_TOKENS 16
-#define MOEL_ABI_VERSION 3
+#define MOEL_ABI_VERSION 4
 
 typedef enum moel_status {
   MOEL_OK = 0,
@@ -227,6 +227,35 @@ moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, vo
                                       void* v_cache, const float* x, int32_t T, int32_t pos,
                                       int32_t window, float* y, const moel_debug* dbg,
                                       void* stream);
+
+/* --- token-tree verify -------------------------------------------------------------- */
+
+/* Checks a token tree of T nodes given by parent indices: parents[t] in [-1, t) for every
+ * t < T (-1: a root, attached to the cached prefix).  `parents` is a HOST array; a NULL
+ * array is the chain.  Pure host code. */
+moel_status moel_validate_tree(const int32_t* parents, int32_t T);
+
+/* The verify step over a tree of candidate tokens instead of a chain (orcarouter.ai English
+ * post, "The draft model got faster too": the verify pass checks a tree of draft tokens;
+ * the pages give neither its mask nor its positions, so the plainest reading is taken).
+ * Token t is the tree node with parent parents[t] (HOST array of T entries, checked by
+ * moel_validate_tree): it sits at position pos + depth(t) (RoPE), its key and value are
+ * written to cache slot pos + t (exactly slots [pos, pos+T) are written, as for the chain),
+ * and it attends to the cached keys j < pos with p - W < j (p its position, W = window, no
+ * limit for W == 0) and to the step's tokens that are itself or its ancestors (the same rule
+ * on their positions).  Everything after attention is per token, as for the chain.  The
+ * chain parents[t] = t - 1 gives exactly moel_layer_decode's results; parents == NULL is
+ * the chain.  Other arguments, results and errors as moel_layer_decode. */
+moel_status moel_layer_decode_tree(moel_plan* plan, const moel_weights* w, void* k_cache,
+                                   void* v_cache, const float* x, int32_t T, int32_t pos,
+                                   int32_t window, const int32_t* parents, float* y,
+                                   const moel_debug* dbg, void* stream);
+
+/* Same arguments and results, as a chain of one kernel per step. */
+moel_status moel_layer_decode_tree_unfused(moel_plan* plan, const moel_weights* w, void* k_cache,
+                                           void* v_cache, const float* x, int32_t T, int32_t pos,
+                                           int32_t window, const int32_t* parents, float* y,
+                                           const moel_debug* dbg, void* stream);
 
 #ifdef __cplusplus
 }

@@ -87,6 +87,10 @@ def lib() -> ctypes.CDLL:
             "moel_pack_experts": (i32, [P(Config), i32, vp, vp, vp, vp]),
             "moel_layer_decode": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, P(Debug), vp]),
             "moel_layer_decode_unfused": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, P(Debug), vp]),
+            "moel_layer_decode_tree": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, P(Debug), vp]),
+            "moel_layer_decode_tree_unfused": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, P(Debug),
+                                                     vp]),
+            "moel_validate_tree": (i32, [vp, i32]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -236,13 +240,22 @@ class Plan:
     # ---- the step ------------------------------------------------------------------------
     def layer_decode(self, lw: LayerWeights, k_cache: torch.Tensor, v_cache: torch.Tensor, x: torch.Tensor,
                      pos: int, window: int, y: torch.Tensor, dbg: Optional[Dict[str, torch.Tensor]] = None,
-                     fused: bool = True, stream=None, T: Optional[int] = None) -> None:
+                     fused: bool = True, stream=None, T: Optional[int] = None, parents=None) -> None:
+        """One verify step; `parents` (T ints, -1 for a root) makes it a token-tree verify."""
         T = x.shape[0] if T is None else T
         d = None
         if dbg is not None:
             d = Debug(_ptr(dbg.get("expert_idx")), _ptr(dbg.get("gates")), _ptr(dbg.get("router_logits")),
                       _ptr(dbg.get("timestamps")))
-        fn = lib().moel_layer_decode if fused else lib().moel_layer_decode_unfused
-        _check(fn(self.handle, ctypes.byref(lw.struct), _ptr(k_cache), _ptr(v_cache), _ptr(x), T, pos, window,
-                  _ptr(y), None if d is None else ctypes.byref(d), _stream(stream)),
-               "moel_layer_decode" if fused else "moel_layer_decode_unfused")
+        dp = None if d is None else ctypes.byref(d)
+        if parents is None:
+            name = "moel_layer_decode" if fused else "moel_layer_decode_unfused"
+            rc = getattr(lib(), name)(self.handle, ctypes.byref(lw.struct), _ptr(k_cache), _ptr(v_cache), _ptr(x),
+                                      T, pos, window, _ptr(y), dp, _stream(stream))
+        else:
+            par = (ctypes.c_int32 * len(parents))(*[int(v) for v in parents])
+            name = "moel_layer_decode_tree" if fused else "moel_layer_decode_tree_unfused"
+            rc = getattr(lib(), name)(self.handle, ctypes.byref(lw.struct), _ptr(k_cache), _ptr(v_cache), _ptr(x),
+                                      T, pos, window, ctypes.cast(par, ctypes.c_void_p), _ptr(y), dp,
+                                      _stream(stream))
+        _check(rc, name)

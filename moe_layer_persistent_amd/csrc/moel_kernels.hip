@@ -344,10 +344,12 @@ const void* phase_fn(int ph) {
 }
 
 moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
-                         const float* x, int32_t T, int32_t pos, int32_t window, float* y,
-                         const moel_debug* dbg, LayerParams& p) {
+                         const float* x, int32_t T, int32_t pos, int32_t window, const int32_t* parents,
+                         float* y, const moel_debug* dbg, LayerParams& p) {
   if (plan == nullptr) return MOEL_ERR_ARG;
   moel_status st = moel_validate_call(&plan->cfg, w, k_cache, v_cache, x, T, pos, window, y);
+  if (st != MOEL_OK) return st;
+  st = moel_validate_tree(parents, T);
   if (st != MOEL_OK) return st;
   p = plan->base;
   p.l2_coherent = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
@@ -362,6 +364,20 @@ moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, 
   if (nch > maxc) nch = maxc;
   if (nch < 1) nch = 1;
   const int chunk = (nkeys + nch - 1) / nch;
+  // token positions and visibility (the chain when parents is NULL); the widest key range is
+  // that of a depth-0 token, so attn_lo covers every token
+  for (int t = 0; t < kMaxT; ++t) {
+    p.tok_depth[t] = 0;
+    p.tok_sees[t] = 0u;
+  }
+  for (int t = 0; t < T; ++t) {
+    const int par = parents ? parents[t] : t - 1;
+    p.tok_depth[t] = par < 0 ? 0 : p.tok_depth[par] + 1;
+    unsigned sees = 0u;
+    for (int i = t; i >= 0; i = parents ? parents[i] : i - 1)
+      if (window == 0 || p.tok_depth[i] > p.tok_depth[t] - window) sees |= 1u << i;
+    p.tok_sees[t] = sees;
+  }
   p.attn_lo = lo;
   p.attn_nkeys = nkeys;
   p.attn_chunk = chunk;
@@ -660,11 +676,11 @@ moel_status moel_pack_experts(const moel_config* cfg, int32_t which, const void*
   return hip_ok(hipGetLastError()) ? MOEL_OK : MOEL_ERR_HIP;
 }
 
-moel_status moel_layer_decode(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
-                              const float* x, int32_t T, int32_t pos, int32_t window, float* y,
-                              const moel_debug* dbg, void* stream) {
+moel_status moel_layer_decode_tree(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                                   const float* x, int32_t T, int32_t pos, int32_t window,
+                                   const int32_t* parents, float* y, const moel_debug* dbg, void* stream) {
   LayerParams p;
-  moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, y, dbg, p);
+  moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, parents, y, dbg, p);
   if (st != MOEL_OK) return st;
   void* args[] = {&p};
   const void* fn = plan->cfg.head_dim == 64 ? fused_fn<64>() : fused_fn<128>();
@@ -690,11 +706,12 @@ moel_status moel_plan_set_acquire(moel_plan* plan, int32_t mode) {
 
 int32_t moel_plan_l2_coherent(const moel_plan* plan) { return plan == nullptr ? -1 : plan->l2_coherent; }
 
-moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
-                                      const float* x, int32_t T, int32_t pos, int32_t window, float* y,
-                                      const moel_debug* dbg, void* stream) {
+moel_status moel_layer_decode_tree_unfused(moel_plan* plan, const moel_weights* w, void* k_cache,
+                                           void* v_cache, const float* x, int32_t T, int32_t pos,
+                                           int32_t window, const int32_t* parents, float* y,
+                                           const moel_debug* dbg, void* stream) {
   LayerParams p;
-  moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, y, dbg, p);
+  moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, parents, y, dbg, p);
   if (st != MOEL_OK) return st;
   void* args[] = {&p};
   for (int ph = kPhQkv; ph < kNumPhases; ++ph) {  // step 0 is part of step 1
@@ -704,6 +721,19 @@ moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, vo
     if (!hip_ok(e)) return MOEL_ERR_HIP;
   }
   return MOEL_OK;
+}
+
+moel_status moel_layer_decode(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                              const float* x, int32_t T, int32_t pos, int32_t window, float* y,
+                              const moel_debug* dbg, void* stream) {
+  return moel_layer_decode_tree(plan, w, k_cache, v_cache, x, T, pos, window, nullptr, y, dbg, stream);
+}
+
+moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                                      const float* x, int32_t T, int32_t pos, int32_t window, float* y,
+                                      const moel_debug* dbg, void* stream) {
+  return moel_layer_decode_tree_unfused(plan, w, k_cache, v_cache, x, T, pos, window, nullptr, y, dbg,
+                                        stream);
 }
 
 }  // extern "C"

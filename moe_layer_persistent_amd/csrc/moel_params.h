@@ -39,6 +39,11 @@ struct LayerParams {
   int l2_coherent;
   // attention decomposition (per call)
   int attn_lo, attn_nkeys, attn_chunk, attn_nchunks;
+  // the step's tokens as the nodes of a token tree (a chain for the linear verify): token t
+  // is at position pos + tok_depth[t]; bit i of tok_sees[t] is set iff t attends to token
+  // i's key (slot pos + i): i is t or an ancestor of t and within the window of t
+  int tok_depth[MOEL_MAX_TOKENS];
+  unsigned tok_sees[MOEL_MAX_TOKENS];
   // weights (packed)
   const uint16_t* gamma1;
   const uint16_t* gamma2;

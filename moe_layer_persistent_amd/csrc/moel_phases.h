@@ -382,10 +382,11 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
                   const float a = L.fin[(j * 16 + 2 * pr) * kMaxT + t] * L.rstd[t];
                   const float b = L.fin[(j * 16 + 2 * pr + 1) * kMaxT + t] * L.rstd[t];
                   const int head = R / p.D, i = (R % p.D) >> 1;
-                  const int ps = p.pos + t;
+                  const int ps = p.pos + t;                  // cache slot
+                  const int rp = p.pos + p.tok_depth[t];     // position (RoPE)
                   if (head < p.Hq + p.Hkv) {
-                    const float c = gl(p.rope_cos)[(size_t)ps * half + i];
-                    const float s = gl(p.rope_sin)[(size_t)ps * half + i];
+                    const float c = gl(p.rope_cos)[(size_t)rp * half + i];
+                    const float s = gl(p.rope_sin)[(size_t)rp * half + i];
                     const float ra = a * c - b * s, rb = b * c + a * s;
                     if (head < p.Hq) {
                       auto q = gl(p.q_buf + (size_t)t * p.Hq * p.D + head * p.D);
@@ -485,7 +486,10 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     f32x4 O[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const int ptok = p.pos + tq;
+    // this lane's token: its position, and which of the step's keys it sees
+    const int tqc = tq < p.T ? tq : p.T - 1;
+    const int ptok = p.pos + p.tok_depth[tqc];
+    const unsigned sees = p.tok_sees[tqc];
     for (int sb = kb; sb < ke; sb += SK) {
       const int nk = (ke - sb) < SK ? (ke - sb) : SK;
       lds_barrier();  // the previous sub-chunk's LDS reads are done
@@ -521,7 +525,8 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int j = sb + kt * 16 + 4 * gq + r;
-            const bool vis = tq < p.T && (j - sb) < nk && j <= ptok && (p.window == 0 || j > ptok - p.window);
+            const bool vis = tq < p.T && (j - sb) < nk &&
+                             (j < p.pos ? (p.window == 0 || j > ptok - p.window) : ((sees >> (j - p.pos)) & 1u) != 0);
             const float v = vis ? S[kt][r] * scale : NEG;
             S[kt][r] = v;
             mx = fmaxf(mx, v);

@@ -89,3 +89,11 @@ size_t moel_packed_experts_bytes(const moel_config* cfg, int32_t which) {
 }
 
 }  // extern "C"
+
+moel_status moel_validate_tree(const int32_t* parents, int32_t T) {
+  if (T < 1 || T > MOEL_MAX_TOKENS) return MOEL_ERR_ARG;
+  if (parents == nullptr) return MOEL_OK;
+  for (int32_t t = 0; t < T; ++t)
+    if (parents[t] < -1 || parents[t] >= t) return MOEL_ERR_ARG;
+  return MOEL_OK;
+}

@@ -48,7 +48,7 @@ class GpuRun:
     def fresh_caches(self):
         return self.k0.clone(), self.v0.clone()
 
-    def run(self, fused=True, T=None, pos=None, stamps=False, x=None):
+    def run(self, fused=True, T=None, pos=None, stamps=False, x=None, parents=None):
         w = self.w
         T = w.T if T is None else T
         pos = w.pos if pos is None else pos
@@ -63,11 +63,11 @@ class GpuRun:
         if stamps:
             dbg["timestamps"] = torch.zeros((self.plan.workgroups, binding.MOEL_N_STAMPS),
                                             dtype=torch.int64, device="cuda")
-        self.plan.layer_decode(self.lw, kc, vc, x, pos, self.window, y, dbg=dbg, fused=fused)
+        self.plan.layer_decode(self.lw, kc, vc, x, pos, self.window, y, dbg=dbg, fused=fused, parents=parents)
         torch.cuda.synchronize()
         st = self.plan.status()
         assert st == binding.MOEL_OK, binding.status_string(st)
-        return dict(y=y, k_cache=kc, v_cache=vc, T=T, pos=pos, x=x, **dbg)
+        return dict(y=y, k_cache=kc, v_cache=vc, T=T, pos=pos, x=x, parents=parents, **dbg)
 
 
 def _f64(t: torch.Tensor) -> np.ndarray:
@@ -113,7 +113,8 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
     gpu_idx = out["expert_idx"].cpu().numpy().astype(np.int64)
     toks = list(range(T)) if moe_tokens is None else sorted(set(int(t) for t in moe_tokens if t < T))
     # routing first (cheap: no experts), then the MoE block with the device's choice
-    ref0 = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), moe_tokens=[])
+    parents = out.get("parents")
+    ref0 = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), moe_tokens=[], parents=parents)
     gap = ref0["gap"]
     exact = gap > GAP_EXEMPT
     # logits are fp32 sums over H products of bf16 values; the gates are a softmax of them,
@@ -130,7 +131,8 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
         assert np.all(np.diff(sel) <= 2 * lg_err + 1e-6), ("selection order invalid", t, sel)
     gsel = out["gates"].cpu().numpy()
     np.testing.assert_allclose(gsel.sum(axis=1), 1.0, rtol=0, atol=1e-5)
-    ref = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), force_idx=gpu_idx, moe_tokens=toks)
+    ref = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), force_idx=gpu_idx, moe_tokens=toks,
+                            parents=parents)
     gate_err = float(np.abs(gsel - ref["gates"]).max())
     assert gate_err <= 2 * lg_err + 1e-5, f"gates max-abs {gate_err} (logits {lg_err})"
     # KV cache: the written (head, slot) set is exact and every other byte is untouched; a

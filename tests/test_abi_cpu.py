@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.moel_abi_version() == 3
+    assert L.moel_abi_version() == 4
 
 
 def test_plan_options_reject_a_missing_plan():
@@ -32,6 +32,18 @@ def test_plan_options_reject_a_missing_plan():
     assert L.moel_plan_set_launch(None, 5) == binding.MOEL_ERR_ARG
     assert L.moel_plan_set_acquire(None, binding.MOEL_ACQUIRE_AUTO) == binding.MOEL_ERR_ARG
     assert L.moel_plan_l2_coherent(None) == -1
+
+
+def test_tree_validation():
+    L = binding.lib()
+    arr = lambda v: (ctypes.c_int32 * len(v))(*v)
+    assert L.moel_validate_tree(None, 16) == binding.MOEL_OK
+    assert L.moel_validate_tree(arr([-1, 0, 0, 1]), 4) == binding.MOEL_OK
+    assert L.moel_validate_tree(arr([-1, -1, 1]), 3) == binding.MOEL_OK
+    assert L.moel_validate_tree(arr([-1, 1]), 2) == binding.MOEL_ERR_ARG      # not before its child
+    assert L.moel_validate_tree(arr([0]), 1) == binding.MOEL_ERR_ARG
+    assert L.moel_validate_tree(arr([-2, 0]), 2) == binding.MOEL_ERR_ARG
+    assert L.moel_validate_tree(arr([-1] * 17), 17) == binding.MOEL_ERR_ARG    # T > 16
 
 
 def test_shapes_beyond_the_32_bit_work_split_are_rejected():

@@ -108,6 +108,45 @@ def test_l1_only_and_l2_invalidating_acquire_agree():
         run.plan.set_acquire(3)
 
 
+# token-tree verify: a 16-node tree (two branches off the root, one branching again), a
+# forest of two roots, and the chain given as a tree
+TREE16 = [-1, 0, 1, 2, 0, 4, 5, 1, 7, 3, 9, 4, 11, 12, 2, 14]
+FOREST = [-1, -1, 0, 1, 2, 3, 0, 6]
+
+
+@pytest.mark.parametrize("case", [
+    dict(parents=TREE16, window=0, pos=500),
+    dict(parents=TREE16, window=64, pos=300),
+    dict(parents=TREE16, window=6, pos=40),
+    dict(parents=FOREST, window=0, pos=200),
+], ids=["tree_global", "tree_window", "tree_short_window", "forest"])
+def test_tree_verify_matches_oracle(case):
+    par = case["parents"]
+    w = synth.small_workload(T=len(par), pos=case["pos"], window=case["window"], n_experts=32, top_k=8,
+                             pooled=512, inter=512)
+    _log(f"tree {case}")
+    run = harness.GpuRun(w)
+    rep = {}
+    out = run.run(fused=True, parents=par)
+    harness.check_against_oracle(run, out, report=rep)
+    _log(f"tree {case}: {rep}")
+    # the one-kernel-per-step chain gives the same bytes
+    b = run.run(fused=False, parents=par)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(out[k], b[k]), k
+
+
+def test_chain_given_as_a_tree_is_the_chain():
+    w = synth.small_workload(T=16, pos=700, window=128, n_experts=32, top_k=8, pooled=512, inter=512)
+    run = harness.GpuRun(w)
+    a = run.run(fused=True)
+    b = run.run(fused=True, parents=list(range(-1, 15)))
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(a[k], b[k]), k
+    with pytest.raises(binding.MoelError):
+        run.run(fused=True, parents=[-1, 1] + list(range(1, 15)))   # parent not before its child
+
+
 def test_timestamps_leave_outputs_bit_identical():
     w = synth.small_workload(T=8, pos=200, window=64)
     run = harness.GpuRun(w)
