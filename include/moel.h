@@ -186,7 +186,9 @@ moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* strea
  *   3 router logits [16][E]        4 pl [16][P] pooled vector        5 a [16*k][I] SwiGLU out
  *   6 d [16*k][P] expert outputs   7 m [16][P] combined vector
  * *ptr receives a device pointer into the plan's workspace (owned by the plan; valid until
- * moel_plan_destroy; overwritten by the next step), *bytes its size. */
+ * moel_plan_destroy; overwritten by the next step), *bytes its size.  o, m and, with NVFP4
+ * experts, pl and a are fp32 copies the step itself does not read: a step writes them only
+ * when it is given a moel_debug (they hold the last such step's values). */
 moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes);
 
 /* --- weight packing (one-time, not on the hot path) --------------------------------- */

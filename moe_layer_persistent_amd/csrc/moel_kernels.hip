@@ -403,6 +403,7 @@ moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, 
   p.dbg_gates = dbg ? dbg->gates : nullptr;
   p.dbg_logits = dbg ? dbg->router_logits : nullptr;
   p.dbg_ts = dbg ? reinterpret_cast<unsigned long long*>(dbg->timestamps) : nullptr;
+  p.debug_copies = dbg != nullptr ? 1 : 0;
   return MOEL_OK;
 }
 

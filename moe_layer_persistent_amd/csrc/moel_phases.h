@@ -634,7 +634,7 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
       M = Mg;
     }
     const float o = num / den;
-    gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
+    if (p.debug_copies) gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
     gl(p.o_op)[op_index(t, h * p.D + d)] = o;
   }
 }
@@ -679,7 +679,7 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
                     gl(p.logits)[t * p.E + n] = v;
                     if (p.dbg_logits) gl(p.dbg_logits)[t * p.E + n] = v;
                   } else {
-                    gl(p.pl)[(size_t)t * p.P + (n - p.E)] = v;
+                    if (p.debug_copies || p.expert_dtype != 0) gl(p.pl)[(size_t)t * p.P + (n - p.E)] = v;
                     store_split(gl(p.pl_split) + (size_t)t * p.P * 2, n - p.E, v);
                   }
                 }
@@ -1236,7 +1236,7 @@ __device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_ar
       const int slot = R.slots[s_lo + j];
       const int row = (t - u * tpe) * 64 + (r & 63);
       if (GATEUP) {
-        gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + row] = L.stage[x];
+        if (p.debug_copies) gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + row] = L.stage[x];
         store_split(gl(p.a_split) + (size_t)slot * p.I * 2, p.rank * p.I_loc + row, L.stage[x]);
       } else {
         gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + row] = L.stage[x];
@@ -1453,7 +1453,7 @@ __device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
     float s = 0.f;
     for (int k = 0; k < p.topk; ++k)
       s = fmaf(R.gate[t * p.topk + k], gl(p.d_buf)[(size_t)(t * p.topk + k) * p.P + pc], s);
-    gl(p.m_buf)[(size_t)t * p.P + pc] = s;
+    if (p.debug_copies) gl(p.m_buf)[(size_t)t * p.P + pc] = s;
     gl(p.m_op)[op_index(t, pc)] = s;
   }
 }
