@@ -21,6 +21,10 @@ Recipe (all tensors seeded by (workload id, layer, tensor id[, expert])):
     nearest even), expert matrices either bf16 or NVFP4-encoded (below)
   * KV history ~ N(0, 1), stored bf16, slots [0, pos); slots >= pos hold
     N(0, 1) filler that the step must overwrite (written slots) or leave alone
+  * activation tensor scales act_ts [E] (NVFP4 experts; read when the SwiGLU output is
+    gathered in fp4), fixed per expert as a calibration would supply them: with
+    s = 0.02^2 sqrt(pooled * hidden), the spread of a gate or up output for unit-RMS hidden
+    states, act_ts = 8 s^2 / (6 * 448) * (1 + 0.25 u), u ~ U(0, 1)
   * NVFP4 encoding of a matrix w [N, K]: tensor scale ts = amax|w| / (6*448);
     per 16-element block scale s = E4M3(amax_blk / (6*ts)) rounded to nearest
     even and clamped to 448; code = E2M1 grid point nearest to w / (s*ts),
@@ -36,6 +40,8 @@ import torch
 
 NVFP4 = 0
 BF16 = 1
+DOWN_EXACT = 0   # the down projection reads the SwiGLU output as computed
+DOWN_NVFP4 = 1   # ... encoded as NVFP4 (the fp4 gather after the first expert GEMM)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -57,6 +63,7 @@ class Workload:
     T: int                   # verify tokens in this step
     n_layers: int = 1
     fp32_masters: bool = False   # tiny case: weights drawn fp32, device copy bf16
+    down_input: int = DOWN_EXACT
     rms_eps: float = 1e-6
     rope_theta: float = 10000.0
 
@@ -99,11 +106,14 @@ WORKLOADS: Dict[str, Workload] = {
     # one GPU's TP8 share of the 62-layer stack (heads / 8, expert N / 8)
     "stack_tp8": Workload(4, "stack_tp8", 8192, 8, 1, 128, 4096, 4096, 256, 8, NVFP4, 8, 2048, 4096, 16,
                           n_layers=62),
+    # swa_fp4 with the SwiGLU output gathered in fp4 before the down projection
+    "swa_fp4_a4": Workload(5, "swa_fp4_a4", 8192, 64, 8, 128, 4096, 4096, 256, 8, NVFP4, 1, 2048, 8192, 16,
+                           down_input=DOWN_NVFP4),
 }
 
 # tensor ids (seed components)
 _TID = dict(x=1, gamma1=2, w_qkv=3, w_o=4, gamma2=5, w_router=6, w_pool=7, w_unpool=8,
-            k_cache=9, v_cache=10, w_gate=11, w_up=12, w_down=13, x_shared=14)
+            k_cache=9, v_cache=10, w_gate=11, w_up=12, w_down=13, x_shared=14, act_ts=15)
 
 
 def seed_of(w: Workload, layer: int, tensor: str, expert: int = -1) -> int:
@@ -228,6 +238,10 @@ def make_experts(w: Workload, layer: int, device) -> Dict[str, torch.Tensor]:
                 c, s, tsc = encode_nvfp4(m)
                 codes[e], scales[e], ts[e] = c, s, tsc
             out[mat + "_codes"], out[mat + "_scales"], out[mat + "_ts"] = codes, scales, ts
+    if w.expert_dtype == NVFP4:
+        spread = 0.02 ** 2 * (w.pooled * w.hidden) ** 0.5
+        u = torch.rand((w.n_experts,), generator=_gen(seed_of(w, layer, "act_ts"), dev), device=dev)
+        out["act_ts"] = (8.0 * spread ** 2 / (6.0 * 448.0) * (1.0 + 0.25 * u)).float()
     return out
 
 

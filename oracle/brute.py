@@ -5,7 +5,7 @@ Test infrastructure only (see the package docstring).
 Every quantity is a Python float (IEEE binary64) computed with explicit loops:
 per token, per head, per key, per output feature, per reduction index.  It
 re-derives each definition (bf16 rounding of the cache writes, E2M1 / E4M3
-decoding, RMSNorm,
+decoding and, for the fp4 gather of the SwiGLU output, encoding, RMSNorm,
 rotate-half RoPE, windowed causal attention, top-k routing with the lower index
 winning ties, SwiGLU experts, combine, residuals) from the written rules and
 does not call into ``layer.py`` or ``formats.py``, so that the vectorised
@@ -14,6 +14,7 @@ oracle can be checked against it.
 from __future__ import annotations
 
 import math
+import struct
 from typing import Dict, List
 
 
@@ -62,6 +63,66 @@ def _nvfp4_row_elem(codes_row, scales_row, ts: float, k: int) -> float:
     return fp4_elem(code) * fp8_scale(int(scales_row[k // 16])) * ts
 
 
+def _f32(v: float) -> float:
+    """Nearest binary32 value (ties to even).  A binary32 product or quotient rounded once
+    equals the binary64 result rounded again to binary32 (53 >= 2 * 24 + 2 bits)."""
+    return struct.unpack("<f", struct.pack("<f", v))[0]
+
+
+def _e4m3_round(v: float) -> float:
+    """Nearest E4M3 value to v >= 0 (4 significant bits, quantum 2^-9 below 2^-6), ties to an
+    even significand, saturating at 448."""
+    if v >= 448.0:
+        return 448.0
+    if v == 0.0:
+        return 0.0
+    _, ex = math.frexp(v)             # v = m 2^ex, 0.5 <= m < 1: quantum 2^(ex - 4)
+    q = 2.0 ** max(ex - 4, -9)
+    r = round(v / q) * q              # Python round(): ties to even
+    return min(r, 448.0)
+
+
+def _e2m1_round(v: float) -> float:
+    """Nearest E2M1 magnitude to v >= 0, ties to the even code, saturating at 6: the decision
+    points are the midpoints 0.25, 0.75, 1.25, 1.75, 2.5, 3.5 and 5 of the grid
+    0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0..7)."""
+    if v <= 0.25:
+        return 0.0
+    if v < 0.75:
+        return 0.5
+    if v <= 1.25:
+        return 1.0
+    if v < 1.75:
+        return 1.5
+    if v <= 2.5:
+        return 2.0
+    if v < 3.5:
+        return 3.0
+    if v <= 5.0:
+        return 4.0
+    return 6.0
+
+
+def _fp4_gather(a: List[float], ts: float) -> List[float]:
+    """a as the down projection reads it after an fp4 gather: per 16-element block an E4M3
+    scale for amax / (6 ts), each element an E2M1 multiple of scale * ts (fp32 decisions)."""
+    t32 = _f32(ts)
+    six_ts = _f32(6.0 * t32)
+    out = []
+    for b in range(0, len(a), 16):
+        blk = [_f32(v) for v in a[b:b + 16]]
+        amax = max(abs(v) for v in blk)
+        s = _e4m3_round(_f32(amax / six_ts))
+        den = _f32(s * t32)
+        for v in blk:
+            if den == 0.0:
+                out.append(0.0)
+                continue
+            mag = _e2m1_round(abs(_f32(v / den)))
+            out.append(math.copysign(mag, v) * s * t32 if mag != 0.0 else 0.0)
+    return out
+
+
 def _dot(a, b) -> float:
     s = 0.0
     for i in range(len(a)):
@@ -91,13 +152,15 @@ def _rotate(vec: List[float], position: int, theta: float) -> List[float]:
 
 
 def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool = True,
-               parents=None) -> Dict:
+               parents=None, act_scales=None) -> Dict:
     """Same contract as layer.layer_step on tiny inputs given as nested lists / arrays.
 
     expert_raw(e) returns {"gate": (codes, scales, ts) | W, "up": ..., "down": ...}.
     parents: token-tree parent of every token (-1 for a root), None for the chain; a token's
     position is pos plus its number of ancestors, and it sees the step's tokens that are
     itself or its ancestors.
+    act_scales: per-expert activation tensor scales; given, the down projection reads the
+    SwiGLU output after an fp4 gather (_fp4_gather).
     """
     x = [[float(v) for v in row] for row in inp["x"]]
     T, H = len(x), len(x[0])
@@ -199,6 +262,8 @@ def layer_step(inp: Dict, dims, pos: int, window: int, expert_raw, nvfp4: bool =
                     usum = _dot(pl, [float(v) for v in raw["up"][i]])
                 sig = gsum / (1.0 + math.exp(-gsum)) if gsum > -700 else 0.0
                 a[rk * il + i] = sig * usum
+            if act_scales is not None:
+                a = _fp4_gather(a, float(act_scales[e]))
             for pp in range(plc):
                 if nvfp4:
                     dc, ds, dts = raw["down"]

@@ -86,3 +86,61 @@ def nvfp4_dequant(codes: np.ndarray, scales: np.ndarray, ts: float) -> np.ndarra
     vals *= np.repeat(s, 16, axis=1)
     vals *= float(ts)
     return vals
+
+
+# --------------------------------------------------------------------------------------------
+# NVFP4 encoding of an activation (the down projection's input when it is gathered as fp4)
+# --------------------------------------------------------------------------------------------
+E4M3_MAX = 448.0
+_E2M1_POS = _E2M1_TABLE[:8]          # codes 0..7: 0, 0.5, 1, 1.5, 2, 3, 4, 6 (increasing)
+_E4M3_POS = _E4M3_TABLE[:0x7F]       # codes 0..126: every finite non-negative value (increasing)
+
+
+def nearest_code(mag, grid: np.ndarray) -> np.ndarray:
+    """Code of the grid value nearest to each non-negative `mag` (codes are grid indices, the
+    grid increasing); equal distances go to the even code.  Beyond the largest value the
+    nearest is the largest: the rounding saturates."""
+    mag = np.asarray(mag, dtype=np.float64)
+    dist = np.abs(mag[..., None] - grid)
+    cand = dist == dist.min(axis=-1, keepdims=True)
+    n = grid.shape[0]
+    first = np.argmax(cand, axis=-1)
+    last = n - 1 - np.argmax(cand[..., ::-1], axis=-1)
+    return np.where(first % 2 == 0, first, last)
+
+
+def nvfp4_quantize(v, ts: float):
+    """fp32 rows v [N, K] (K % 16 == 0) with fp32 tensor scale ts > 0 -> (codes uint8 [N, K]
+    with the sign in bit 3, block scales uint8 [N, K/16]).
+
+    Same format as the stored expert weights (E2M1 element, E4M3 scale per 16 consecutive
+    elements, one fp32 tensor scale), encoded with the weights' own rule: the block scale is
+    the E4M3 value nearest to amax_block / (6 ts), and each element the E2M1 value nearest to
+    v / (scale ts), both ties to even and saturating (448, 6); a zero scale gives zero codes.
+    Every step that decides a code is taken in fp32 (product, then quotient, each rounded),
+    the precision the kernel computes them in.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    N, K = v.shape
+    assert K % 16 == 0
+    t32 = np.float32(ts)
+    assert t32 > 0
+    blk = v.reshape(N, K // 16, 16)
+    amax = np.abs(blk).max(axis=-1)
+    sd = amax / (np.float32(6.0) * t32)
+    sd = np.minimum(sd, np.float32(E4M3_MAX))
+    s_code = nearest_code(sd, _E4M3_POS)
+    den = _E4M3_POS[s_code].astype(np.float32) * t32
+    ok = den > 0
+    x = np.where(ok[..., None], blk / np.where(ok, den, np.float32(1.0))[..., None], np.float32(0.0))
+    m_code = nearest_code(np.minimum(np.abs(x), np.float32(6.0)), _E2M1_POS)
+    codes = np.where((x < 0) & (m_code > 0), m_code | 8, m_code).astype(np.uint8)
+    return codes.reshape(N, K), s_code.astype(np.uint8)
+
+
+def nvfp4_values(codes, scales) -> np.ndarray:
+    """E2M1(code) * E4M3(block scale), codes uint8 [N, K] (one per element), scales [N, K/16]
+    -> fp64 [N, K] (exact; the tensor scale is not applied)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    s = _E4M3_TABLE[np.asarray(scales, dtype=np.uint8)]
+    return _E2M1_TABLE[codes & 0x0F] * np.repeat(s, 16, axis=1)

@@ -36,6 +36,11 @@ with its rationale in the design notes):
     zero outside that slice; down keeps rows [rank*P/S, ...) of the pooled
     width and its output is zero elsewhere (zero padding stands in for the
     cross-GPU gathers).
+  * fp4 gather of the SwiGLU output (optional; the pages gather it in fp4 after the first
+    expert GEMM and fix no encoding): a is encoded in the weights' own NVFP4 format, E2M1
+    elements with an E4M3 scale per 16 consecutive elements and a static fp32 tensor scale
+    per expert, each scale and code the nearest value (ties to even, saturating), decided in
+    fp32; the down projection reads the decoded values.
 Precision: the layer in exact (fp64) arithmetic on its given inputs.  Weights
 are bf16 or NVFP4 and the KV cache is bf16: those are storage formats, so the
 new keys and values are rounded to bf16 (nearest even) when written to the
@@ -48,7 +53,7 @@ from typing import Callable, Dict, Optional, Tuple
 
 import numpy as np
 
-from .formats import bf16_round, nvfp4_dequant
+from .formats import bf16_round, nvfp4_dequant, nvfp4_quantize, nvfp4_values
 
 
 @dataclasses.dataclass(frozen=True)
@@ -215,9 +220,20 @@ def bf16_experts(get_raw: Callable[[int], dict]) -> ExpertFn:
     return fn
 
 
+def down_input_nvfp4(a: np.ndarray, ts: float) -> np.ndarray:
+    """The SwiGLU output as the down projection reads it when it is gathered in fp4 (orcarouter.ai
+    English post, "Where the kernel boundary sits": an fp4 all-gather after the first expert
+    GEMM): the fp32 row encoded as NVFP4 with the expert's activation tensor scale ts, decoded
+    back (exact, fp64)."""
+    codes, scales = nvfp4_quantize(np.asarray(a, dtype=np.float32)[None, :], ts)
+    return nvfp4_values(codes, scales)[0] * float(np.float32(ts))
+
+
 def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
-               dims: Dims) -> Tuple[np.ndarray, np.ndarray]:
-    """One token through one expert (this GPU's shard).  Returns (a [inter], d [pooled])."""
+               dims: Dims, act_ts: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One token through one expert (this GPU's shard).  Returns (a [inter], the down
+    projection's input [inter], d [pooled]); with act_ts the input is a encoded as NVFP4
+    (down_input_nvfp4), else a itself."""
     il = dims.inter // dims.n_shards
     plc = dims.pooled // dims.n_shards
     r = dims.shard_rank
@@ -225,9 +241,10 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
     u = Wu @ pl_t
     a = np.zeros(dims.inter)
     a[r * il:(r + 1) * il] = silu(g) * u
+    a_in = a if act_ts is None else down_input_nvfp4(a, act_ts)
     d = np.zeros(dims.pooled)
-    d[r * plc:(r + 1) * plc] = Wd @ a
-    return a, d
+    d[r * plc:(r + 1) * plc] = Wd @ a_in
+    return a, a_in, d
 
 
 # --------------------------------------------------------------------------------------------
@@ -235,7 +252,7 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
 # --------------------------------------------------------------------------------------------
 def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, experts: ExpertFn,
                force_idx: Optional[np.ndarray] = None, moe_tokens=None,
-               parents=None) -> Dict[str, np.ndarray]:
+               parents=None, act_scales=None) -> Dict[str, np.ndarray]:
     """One layer step.  `inp` holds fp64 arrays (bf16-valued weights):
     x [T,H], gamma1 [H], w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq*D], gamma2 [H], w_router [E,H],
     w_pool [P,H], w_unpool [H,P], k_cache/v_cache [Hkv, C, D].
@@ -244,7 +261,8 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     logits).  moe_tokens limits the expert and unpooler work to a subset of tokens (y rows of
     the other tokens are returned as NaN); everything else is computed for all tokens.
     parents [T] makes the tokens the nodes of a token tree (see the module docstring); None
-    is the chain.
+    is the chain.  act_scales [E] (fp32 activation tensor scale per expert) makes the down
+    projection read its input encoded as NVFP4 (down_input_nvfp4); None reads a itself.
     Returns y, the written K/V rows, routing and every intermediate.
     """
     x = np.asarray(inp["x"], dtype=np.float64)
@@ -286,6 +304,7 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     toks = range(T) if moe_tokens is None else list(moe_tokens)
     m = np.full((T, dims.pooled), np.nan)
     a_all = np.full((T, dims.top_k, dims.inter), np.nan)
+    aq_all = np.full((T, dims.top_k, dims.inter), np.nan)
     d_all = np.full((T, dims.top_k, dims.pooled), np.nan)
     needed = sorted({int(idx[t, kk]) for t in toks for kk in range(dims.top_k)})
     for e in needed:                              # one expert's weights resident at a time
@@ -293,7 +312,8 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
         for t in toks:
             for kk in range(dims.top_k):
                 if idx[t, kk] == e:
-                    a_all[t, kk], d_all[t, kk] = expert_out(pl[t], Wg, Wu, Wd, dims)
+                    a_all[t, kk], aq_all[t, kk], d_all[t, kk] = expert_out(
+                        pl[t], Wg, Wu, Wd, dims, None if act_scales is None else float(act_scales[e]))
     for t in toks:
         acc = np.zeros(dims.pooled)
         for kk in range(dims.top_k):              # selection order
@@ -305,6 +325,6 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
 
     out.update(y=y, xn=xn, q=q_r, k_new=k_r, v_new=v_r, k_exact=k_exact, v_exact=v, o=o, h=h, hn=hn,
                logits=logits,
-               idx=idx, gates=gates, gap=gap, pl=pl, a=a_all, d=d_all, m=m,
+               idx=idx, gates=gates, gap=gap, pl=pl, a=a_all, a_in=aq_all, d=d_all, m=m,
                k_cache=k_cache, v_cache=v_cache)
     return out

@@ -144,3 +144,91 @@ def test_bf16_round_ties_to_even():
     assert formats.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
     # a value only fp64 holds: the tie at 1 + 2^-8 exactly vs 1 + 2^-8 - 2^-40
     assert formats.bf16_round(1.0 + 2.0 ** -8 - 2.0 ** -40) == 1.0
+
+
+# ---------------------------------------------------------------- NVFP4 encoding (fp4 gather)
+def _grid_codes(table_fn, n):
+    return [(c, _exact_minifloat(c, *table_fn)) for c in range(n)]
+
+
+@pytest.mark.parametrize("fmt", ["e2m1", "e4m3"])
+def test_nearest_code_exact_nearest_with_even_ties(fmt):
+    """Every grid point, every midpoint (-> the even code), the fp32 neighbours of every
+    midpoint (-> the nearer side) and values past the top (-> the top code), against the
+    nearest point found with exact rational distances."""
+    if fmt == "e2m1":
+        grid, n = formats._E2M1_POS, 8
+        exact = [_exact_minifloat(c, 2, 1, 1) for c in range(n)]
+    else:
+        grid, n = formats._E4M3_POS, 0x7F
+        exact = [_exact_minifloat(c, 4, 3, 7) for c in range(n)]
+    probes = []
+    for c in range(n):
+        probes.append(float(exact[c]))
+        if c + 1 < n:
+            mid = (exact[c] + exact[c + 1]) / 2
+            m32 = np.float32(float(mid))
+            assert Fraction(float(m32)) == mid        # every midpoint is an fp32 value
+            probes += [float(m32), float(np.nextafter(m32, np.float32(0))),
+                       float(np.nextafter(m32, np.float32(np.inf)))]
+    top = float(exact[-1])
+    probes += [top * 1.01, top * 4, 0.0]
+    got = formats.nearest_code(np.array(probes), grid)
+    for v, c in zip(probes, got):
+        d = [abs(Fraction(v) - g) for g in exact]
+        best = min(d)
+        cands = [i for i in range(n) if d[i] == best]
+        want = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+        assert c == want, (fmt, v, c, want)
+
+
+def test_nvfp4_quantize_representable_blocks_are_unchanged():
+    """Blocks built from E2M1 codes and an E4M3 scale, with one element at 6 * scale, encode to
+    those codes and that scale (the scale rule amax / (6 ts) and the element rule v / (s ts))."""
+    rng = np.random.default_rng(21)
+    N, K = 24, 128
+    ts = 2.0 ** -7                               # a power of two keeps every product exact in fp32
+    codes = rng.integers(0, 16, size=(N, K))
+    codes[codes == 8] = 0                        # -0 encodes as +0
+    codes[:, ::16] = np.where(rng.random((N, K // 16)) < 0.5, 7, 15)   # +-6 fixes each block's amax
+    scale_bytes = rng.integers(0x01, 0x7F, size=(N, K // 16))
+    vals = formats.e2m1_value(codes) * np.repeat(formats.e4m3_value(scale_bytes), 16, axis=1) * ts
+    v32 = vals.astype(np.float32)
+    assert np.array_equal(v32.astype(np.float64), vals)
+    c, s = formats.nvfp4_quantize(v32, ts)
+    np.testing.assert_array_equal(s, scale_bytes)
+    np.testing.assert_array_equal(c, codes)
+    np.testing.assert_array_equal(formats.nvfp4_values(c, s) * ts, vals)
+
+
+def test_nvfp4_quantize_matches_weight_encoder():
+    """With the weights' own tensor scale (amax / (6 * 448)) the encoding is the one the
+    synthetic weights are stored in, whose E4M3 rounding is torch's float8_e4m3fn cast."""
+    rng = np.random.default_rng(8)
+    for trial in range(4):
+        w = (rng.standard_normal((48, 256)) * 10.0 ** rng.uniform(-3, 1)).astype(np.float32)
+        w[3, 16:32] = 0.0                        # a zero block
+        w[5, 40] = -w[5, 40]
+        packed, s8, ts = synth.encode_nvfp4(torch.from_numpy(w))
+        c, s = formats.nvfp4_quantize(w, float(ts))
+        np.testing.assert_array_equal(s, s8.numpy())
+        want = np.empty_like(c)
+        want[:, 0::2] = packed.numpy() & 0x0F
+        want[:, 1::2] = packed.numpy() >> 4
+        np.testing.assert_array_equal(c, want)
+
+
+def test_nvfp4_quantize_saturation_zero_and_sign():
+    ts = 1.0
+    v = np.zeros((1, 48), dtype=np.float32)
+    v[0, 0:16] = np.linspace(-1.0, 1.0, 16)
+    v[0, 5] = 1e6                                # block 0: amax / 6 far above 448 -> scale 448
+    v[0, 16:32] = 0.0                            # block 1: zero -> scale 0, codes 0
+    v[0, 32:48] = -np.float32(0.75)              # block 2: amax 0.75 -> scale 0.125, codes -6
+    c, s = formats.nvfp4_quantize(v, ts)
+    assert s[0, 0] == 0x7E and formats.e4m3_value(s[0, 0]) == 448.0
+    assert c[0, 5] == 7                          # 1e6 / 448 saturates at +6
+    assert np.all(c[0, [i for i in range(16) if i != 5]] == 0)   # |v| <= 1 is below 0.25 * 448
+    assert s[0, 1] == 0 and np.all(c[0, 16:32] == 0)
+    assert formats.e4m3_value(s[0, 2]) == 0.125 and np.all(c[0, 32:48] == 15)
+    np.testing.assert_array_equal(formats.nvfp4_values(c, s)[0, 32:48], -0.75)

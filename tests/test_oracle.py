@@ -361,3 +361,69 @@ def test_tree_nodes_outside_the_path_do_not_matter():
     b = layer.layer_step(g, dims, w.pos, 0, _experts(f, w), parents=TREE16)
     np.testing.assert_array_equal(a["y"][13], b["y"][13])
     assert not np.array_equal(a["y"][off_path[-1]], b["y"][off_path[-1]])
+
+
+# ---------------------------------------------------------------- fp4 gather of the SwiGLU output
+def test_fp4_gather_row_two_implementations_agree():
+    """The vectorised encoder (nearest grid point by distance) and the loop-only one (E4M3 by
+    significand rounding, E2M1 by its decision points) give identical rows."""
+    rng = np.random.default_rng(17)
+    for trial in range(6):
+        n = 16 * int(rng.integers(1, 9))
+        a = rng.standard_normal(n) * 10.0 ** rng.uniform(-4, 1)
+        a[rng.random(n) < 0.1] = 0.0
+        ts = float(np.float32(10.0 ** rng.uniform(-6, -1)))
+        want = brute._fp4_gather([float(v) for v in a], ts)
+        got = layer.down_input_nvfp4(a, ts)
+        np.testing.assert_array_equal(got, np.array(want))
+
+
+def _fp4_gather_shape(**kw):
+    base = dict(hidden=64, n_q_heads=4, n_kv_heads=2, head_dim=16, pooled=32, inter=64, n_experts=8,
+                top_k=3, window=5, pos=9, T=3, down_input=synth.DOWN_NVFP4)
+    base.update(kw)
+    return synth.small_workload(**base)
+
+
+@pytest.mark.parametrize("shards", [1, 2])
+def test_layer_fp4_gather_matches_bruteforce(shards):
+    w = _fp4_gather_shape(n_shards=shards)
+    _, f = _np_inputs(w)
+    dims = layer.Dims(w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pooled, w.inter,
+                      w.n_experts, w.top_k, w.n_shards, shards - 1, w.rms_eps, w.rope_theta)
+    got = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w), act_scales=f["act_ts"])
+    ref = brute.layer_step(f, dims, w.pos, w.window, _raw_getter(f, w), nvfp4=True,
+                           act_scales=f["act_ts"])
+    assert got["idx"].tolist() == ref["idx"]
+    np.testing.assert_allclose(got["y"], np.array(ref["y"]), rtol=1e-9, atol=1e-10)
+    plain = layer.layer_step(f, dims, w.pos, w.window, _experts(f, w))
+    dd = np.nanmax(np.abs(plain["d"] - got["d"]))
+    assert dd > 1e-2 * np.nanmax(np.abs(plain["d"]))      # the gather is not a no-op here
+
+
+def test_fp4_gather_changes_only_the_down_input():
+    """Everything up to the SwiGLU output is unchanged; the down projection reads the encoded
+    a (on the 16-element block grid, with the expert's scale) and d is exactly W_d times it."""
+    w = _fp4_gather_shape()
+    _, f = _np_inputs(w)
+    dims = _dims(w)
+    ex = _experts(f, w)
+    q = layer.layer_step(f, dims, w.pos, w.window, ex, act_scales=f["act_ts"])
+    p = layer.layer_step(f, dims, w.pos, w.window, ex)
+    for key in ("h", "logits", "pl", "a"):
+        np.testing.assert_array_equal(q[key], p[key])
+    np.testing.assert_array_equal(q["idx"], p["idx"])
+    np.testing.assert_array_equal(p["a_in"], p["a"])
+    for t in range(w.T):
+        for kk in range(w.top_k):
+            e = int(q["idx"][t, kk])
+            ts = float(np.float32(f["act_ts"][e]))
+            a_in, a = q["a_in"][t, kk], q["a"][t, kk]
+            # every value is a code times the block's scale times ts, and within half a code
+            # step (a quarter of the block's top step, 2 scale units) of a
+            blk_scale = np.abs(a_in).reshape(-1, 16).max(axis=1) / 6.0
+            assert np.all(np.abs(a_in - a) <= np.repeat(blk_scale, 16) * 1.0 + 1e-300)
+            _, _, Wd = ex(e)
+            np.testing.assert_allclose(q["d"][t, kk], Wd @ a_in, rtol=1e-12, atol=1e-15)
+            assert not np.array_equal(a_in, a)
+            assert 0 < ts
