@@ -222,19 +222,21 @@ def main():
     idx = dbg["expert_idx"].cpu().numpy()
     alg_bytes, U = algorithmic_bytes(w, idx, w.pos, window, T)
 
-    def timed(fused, steps, warmup, parents=None):
+    def timed(fused, steps, warmup, parents=None, pl=None, cps=None):
         """Back-to-back launches between two events on the launch stream: the average launch
         duration (us) over the timed region, and the host wall time (s)."""
+        pl = plan if pl is None else pl
+        cps = copies if cps is None else cps
         for i in range(warmup):
-            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
-                              parents=parents)
+            pl.layer_decode(cps[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
+                            parents=parents)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record(stream)
         for i in range(steps):
-            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
-                              parents=parents)
+            pl.layer_decode(cps[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
+                            parents=parents)
         b.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -255,6 +257,16 @@ def main():
     assert st == 0, binding.status_string(st)
     ms_per_step = wall * 1e3 / args.steps
     durs = per_launch(True, max(5, args.steps // 2))
+    # the same weights with the SwiGLU output gathered in fp4 before the down projection (the
+    # payload of the N-sharded layout's first all-gather), through a plan configured for it
+    a4_us = None
+    if w.expert_dtype == synth.NVFP4 and w.down_input == synth.DOWN_EXACT:
+        plan_a4 = binding.Plan(binding.config_from_workload(w.with_(down_input=synth.DOWN_NVFP4)))
+        cps_a4 = [binding.LayerWeights(c.packed, dict(c.ts, act=t["act_ts"].contiguous())) for c in copies]
+        a4_us, _ = timed(True, max(5, args.steps // 2), 2, pl=plan_a4, cps=cps_a4)
+        st = plan_a4.status()
+        assert st == 0, binding.status_string(st)
+        plan_a4.close()
     # the same launches through the cooperative launch API (guaranteed residency on a shared
     # device), for comparison: the runtime adds a gap between consecutive cooperative launches
     plan.set_launch(binding.MOEL_LAUNCH_COOPERATIVE)
@@ -296,7 +308,8 @@ def main():
                        "single_launch_p90": round(float(np.percentile(durs, 90)), 2),
                        "cooperative_launch_back_to_back": round(coop_us, 2),
                        "l2_invalidating_acquire_back_to_back": round(inv_us, 2),
-                       "token_tree_verify_back_to_back": round(tree_us, 2)},
+                       "token_tree_verify_back_to_back": round(tree_us, 2),
+                       "fp4_gathered_down_input_back_to_back": None if a4_us is None else round(a4_us, 2)},
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),

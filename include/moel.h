@@ -36,7 +36,7 @@ extern "C" {
 #endif
 
 #define MOEL_MAX_TOKENS 16
-#define MOEL_ABI_VERSION 4
+#define MOEL_ABI_VERSION 5
 
 typedef enum moel_status {
   MOEL_OK = 0,
@@ -54,6 +54,19 @@ typedef enum moel_expert_dtype {
   MOEL_EXPERT_NVFP4 = 0,     /* E2M1 codes, E4M3 scale per 16 elements, fp32 per matrix */
   MOEL_EXPERT_BF16 = 1
 } moel_expert_dtype;
+
+/* What the down projection reads (orcarouter.ai English post, "Where the kernel boundary
+ * sits": with both expert GEMMs N-sharded, the SwiGLU output is all-gathered in fp4 between
+ * them).  EXACT: the SwiGLU output as computed (fp32, carried as a bf16 pair).  NVFP4: that
+ * output encoded in the experts' own NVFP4 format, the payload such a gather carries: per
+ * 16 consecutive elements an E4M3 scale, the value nearest to amax / (6 ts), and E2M1
+ * elements nearest to v / (scale ts), both ties to even and saturating (448, 6), decided
+ * in fp32; ts = the expert's activation tensor scale (moel_weights.ts_act).  NVFP4 experts
+ * only. */
+typedef enum moel_down_input {
+  MOEL_DOWN_INPUT_EXACT = 0,
+  MOEL_DOWN_INPUT_NVFP4 = 1
+} moel_down_input;
 
 /* Shape of one layer.  Sharded configurations hold one GPU's share of the experts'
  * N dimension: gate/up keep inter/n_shards rows, down keeps pooled/n_shards rows (the
@@ -75,6 +88,7 @@ typedef struct moel_config {
   int32_t kv_capacity;    /* slots per kv head in the caller's cache                     */
   float rms_eps;          /* RMSNorm epsilon                                             */
   float rope_theta;       /* RoPE base                                                   */
+  int32_t down_input;     /* moel_down_input                                             */
 } moel_config;
 
 /* Layer weights in the kernels' packed layouts (see the moel_pack_* calls).  All device
@@ -93,6 +107,8 @@ typedef struct moel_weights {
   const float* ts_gate;   /* fp32 [E] tensor scales (NVFP4 only, else NULL)              */
   const float* ts_up;
   const float* ts_down;
+  const float* ts_act;    /* fp32 [E] activation tensor scales, > 0 (down_input NVFP4,
+                           * else ignored)                                              */
 } moel_weights;
 
 /* Optional outputs for tests and profiling; any member may be NULL. */
@@ -185,9 +201,11 @@ moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* strea
  *   0 q [16][Hq*D] after RoPE      1 o [16][Hq*D] attention output   2 h [16][H]
  *   3 router logits [16][E]        4 pl [16][P] pooled vector        5 a [16*k][I] SwiGLU out
  *   6 d [16*k][P] expert outputs   7 m [16][P] combined vector
+ *   8 aq [16*k][I] with down_input NVFP4: the down projection's input as E2M1 value times
+ *     E4M3 block scale (its tensor scale multiplies the projection's sums)
  * *ptr receives a device pointer into the plan's workspace (owned by the plan; valid until
  * moel_plan_destroy; overwritten by the next step), *bytes its size.  o, m and, with NVFP4
- * experts, pl and a are fp32 copies the step itself does not read: a step writes them only
+ * experts, pl, a and aq are fp32 copies the step itself does not read: a step writes them only
  * when it is given a moel_debug (they hold the last such step's values). */
 moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes);
 

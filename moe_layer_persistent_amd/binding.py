@@ -29,6 +29,8 @@ MOEL_ACQUIRE_L2_INVALIDATE = 1
 MOEL_ERR_INTERNAL = -8
 MOEL_EXPERT_NVFP4 = 0
 MOEL_EXPERT_BF16 = 1
+MOEL_DOWN_INPUT_EXACT = 0
+MOEL_DOWN_INPUT_NVFP4 = 1
 MOEL_N_STAMPS = 32
 
 
@@ -42,13 +44,13 @@ class Config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "n_q_heads", "n_kv_heads", "head_dim", "pooled", "inter", "n_experts", "top_k",
         "expert_dtype", "n_shards", "shard_rank", "kv_capacity")] + [
-        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float)]
+        ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float), ("down_input", ctypes.c_int32)]
 
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "gamma1", "gamma2", "w_qkv", "w_o", "w_router", "w_pool", "w_unpool", "w_gate", "w_up",
-        "w_down", "ts_gate", "ts_up", "ts_down")]
+        "w_down", "ts_gate", "ts_up", "ts_down", "ts_act")]
 
 
 class Debug(ctypes.Structure):
@@ -122,7 +124,8 @@ def _stream(stream=None):
 def config_from_workload(w, kv_capacity: Optional[int] = None) -> Config:
     return Config(w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pooled, w.inter, w.n_experts,
                   w.top_k, w.expert_dtype, w.n_shards, 0,
-                  w.kv_capacity if kv_capacity is None else kv_capacity, w.rms_eps, w.rope_theta)
+                  w.kv_capacity if kv_capacity is None else kv_capacity, w.rms_eps, w.rope_theta,
+                  getattr(w, "down_input", MOEL_DOWN_INPUT_EXACT))
 
 
 class LayerWeights:
@@ -135,7 +138,7 @@ class LayerWeights:
             _ptr(packed["gamma1"]), _ptr(packed["gamma2"]), _ptr(packed["w_qkv"]), _ptr(packed["w_o"]),
             _ptr(packed["w_router"]), _ptr(packed["w_pool"]), _ptr(packed["w_unpool"]),
             _ptr(packed["w_gate"]), _ptr(packed["w_up"]), _ptr(packed["w_down"]),
-            _ptr(ts["gate"]), _ptr(ts["up"]), _ptr(ts["down"]))
+            _ptr(ts["gate"]), _ptr(ts["up"]), _ptr(ts["down"]), _ptr(ts.get("act")))
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.packed.values())
@@ -166,7 +169,7 @@ class Plan:
     def status(self) -> int:
         return lib().moel_plan_status(self.handle)
 
-    SCRATCH = {"q": 0, "o": 1, "h": 2, "logits": 3, "pl": 4, "a": 5, "d": 6, "m": 7}
+    SCRATCH = {"q": 0, "o": 1, "h": 2, "logits": 3, "pl": 4, "a": 5, "d": 6, "m": 7, "aq": 8}
 
     def scratch(self, name: str) -> torch.Tensor:
         """Copy of an intermediate activation of the last completed step (fp32, flat)."""
@@ -235,6 +238,8 @@ class Plan:
             else:
                 packed["w_" + m] = self.pack_experts(which, t[m + "_codes"], t[m + "_scales"], stream=stream)
                 ts[m] = t[m + "_ts"].contiguous()
+        if c.down_input == MOEL_DOWN_INPUT_NVFP4:
+            ts["act"] = t["act_ts"].contiguous()
         return LayerWeights(packed, ts)
 
     # ---- the step ------------------------------------------------------------------------

@@ -395,6 +395,7 @@ moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, 
   p.ts_gate = w->ts_gate;
   p.ts_up = w->ts_up;
   p.ts_down = w->ts_down;
+  p.ts_act = p.down_fp4 ? w->ts_act : nullptr;
   p.k_cache = static_cast<uint16_t*>(k_cache);
   p.v_cache = static_cast<uint16_t*>(v_cache);
   p.x = x;
@@ -460,6 +461,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   const size_t o_d = take((size_t)kMaxT * k * P * 4);
   const size_t o_pls = take((size_t)kMaxT * P * 4);
   const size_t o_as = take((size_t)kMaxT * k * I * 4);
+  const size_t o_aq = take((size_t)kMaxT * k * I * 4);
   const size_t o_m = take((size_t)kMaxT * P * 4);
   const size_t o_oop = take((size_t)kMaxT * Hq * D * 4);
   const size_t o_hop = take((size_t)kMaxT * H * 4);
@@ -523,6 +525,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.P_loc = P / cfg->n_shards;
   b.kv_cap = cfg->kv_capacity;
   b.expert_dtype = cfg->expert_dtype;
+  b.down_fp4 = cfg->down_input == MOEL_DOWN_INPUT_NVFP4 ? 1 : 0;
   b.eps = cfg->rms_eps;
   b.nwg = nwg;
   b.stride_gate = moel_packed_experts_bytes(cfg, 0) / (size_t)E;
@@ -540,6 +543,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   b.d_buf = reinterpret_cast<float*>(ws + o_d);
   b.pl_split = reinterpret_cast<uint16_t*>(ws + o_pls);
   b.a_split = reinterpret_cast<uint16_t*>(ws + o_as);
+  b.aq_buf = reinterpret_cast<float*>(ws + o_aq);
   b.m_buf = reinterpret_cast<float*>(ws + o_m);
   b.o_op = reinterpret_cast<float*>(ws + o_oop);
   b.h_op = reinterpret_cast<float*>(ws + o_hop);
@@ -625,6 +629,7 @@ moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, 
     case 5: *ptr = b.a_buf; *bytes = T * k * b.I * 4; break;
     case 6: *ptr = b.d_buf; *bytes = T * k * b.P * 4; break;
     case 7: *ptr = b.m_buf; *bytes = T * b.P * 4; break;
+    case 8: *ptr = b.aq_buf; *bytes = T * k * b.I * 4; break;
     default: return MOEL_ERR_ARG;
   }
   return MOEL_OK;

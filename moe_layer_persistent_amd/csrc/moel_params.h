@@ -30,6 +30,8 @@ struct LayerParams {
   // shape
   int H, Hq, Hkv, D, P, I, E, topk;
   int n_shards, rank, I_loc, P_loc, kv_cap, expert_dtype;
+  // 1: the down projection reads the SwiGLU output encoded as NVFP4 (the fp4 gather)
+  int down_fp4;
   float eps;
   // call
   int T, pos, window;
@@ -61,6 +63,7 @@ struct LayerParams {
   const float* ts_gate;
   const float* ts_up;
   const float* ts_down;
+  const float* ts_act;  // [E] activation tensor scales of the fp4 gather
   size_t stride_gate, stride_up, stride_down;  // packed bytes per expert
   // caches and io
   uint16_t* k_cache;
@@ -82,6 +85,7 @@ struct LayerParams {
   // quad, 4 bf16 of the nearest values then 4 bf16 of the remainders (16 bytes)
   uint16_t* pl_split;  // [16][P/4][8]
   uint16_t* a_split;   // [16*topk][I/4][8]
+  float* aq_buf;    // [16*topk][I] fp4-gathered SwiGLU output (E2M1 x E4M3), debug copy
   float* d_buf;     // [16*topk][P]
   float* m_buf;     // [16][P]
   // o, h and m again in the operand order of the dense contractions that read them (see

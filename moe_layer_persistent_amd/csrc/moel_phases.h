@@ -773,7 +773,9 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
   if (p.expert_dtype == 0) {  // weights, independent of the step: issued beside the logits
     for (int i = threadIdx.x; i < 3 * p.E; i += kThreads) {
       const int m = i / p.E, e = i - m * p.E;
-      R.ts[m][e] = gl(m == 0 ? p.ts_gate : m == 1 ? p.ts_up : p.ts_down)[e];
+      float ts = gl(m == 0 ? p.ts_gate : m == 1 ? p.ts_up : p.ts_down)[e];
+      if (m == 2 && p.down_fp4) ts *= gl(p.ts_act)[e];  // the fp4 gather's tensor scale
+      R.ts[m][e] = ts;
     }
   }
   // top-k: wave w takes tokens 2w (lanes 0-31) and 2w + 1 (lanes 32-63) at the same time;
@@ -968,6 +970,36 @@ __device__ __forceinline__ void fp4_pair_compute(const Fp4Pair<NM, G>& f, f32x4 
   fp4_mfma_block<0, 1>(f, a, acc);
   fp4_mfma_block<1, 0>(f, a, acc);
   fp4_mfma_block<1, 1>(f, a, acc);
+}
+
+// NVFP4 encoding of the SwiGLU output for the fp4 gather before the down projection: the
+// nearest representable value, ties to the even code, saturating; decided in fp32.
+__device__ __forceinline__ float e4m3_nearest(float v) {  // v >= 0
+  if (!(v < 448.0f)) return 448.0f;
+  // v in [2^ex, 2^(ex+1)) keeps 4 significant bits: quantum 2^(ex-3), never below 2^-9
+  const int ex = (int)((__float_as_uint(v) >> 23) & 0xffu) - 127;
+  const int q = ex - 3 > -9 ? ex - 3 : -9;
+  const float r = ldexpf(rintf(ldexpf(v, -q)), q);
+  return r < 448.0f ? r : 448.0f;
+}
+__device__ __forceinline__ float e2m1_nearest(float m) {  // m >= 0
+  // decision points: the midpoints of 0, 0.5, 1, 1.5, 2, 3, 4, 6, each tie to the even code
+  return m <= 0.25f ? 0.0f : m < 0.75f ? 0.5f : m <= 1.25f ? 1.0f : m < 1.75f ? 1.5f
+       : m <= 2.5f ? 2.0f : m < 3.5f ? 3.0f : m <= 5.0f ? 4.0f : 6.0f;
+}
+// Encodes the value v held by this lane as part of the 16-element block held by its 16-lane
+// group (all 64 lanes active): returns E2M1 value x E4M3 block scale (exact in bf16), the
+// tensor scale ts left to the down projection's sums.
+__device__ __forceinline__ float fp4_gather_value(float v, float ts) {
+  float amax = fabsf(v);
+  amax = fmaxf(amax, __shfl_xor(amax, 8));
+  amax = fmaxf(amax, __shfl_xor(amax, 4));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  const float s = e4m3_nearest(amax / (6.0f * ts));
+  const float den = s * ts;
+  const float mag = den > 0.0f ? e2m1_nearest(fabsf(v / den)) : 0.0f;
+  return copysignf(mag * s, v);
 }
 
 // token-pair group that an expert with n_e slots needs
@@ -1225,19 +1257,27 @@ __device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_ar
       if (!more) break;
     }
   }
-  // write the stream's outputs (positions 0 .. is)
+  // write the stream's outputs (positions 0 .. is).  SPT and kThreads are multiples of 64,
+  // so every wave runs the same iterations with all lanes, and the 16 elements of a row
+  // block (16 consecutive x) sit in 16 consecutive lanes.
   lds_barrier();
   for (int x = threadIdx.x; x < (is + 1) * SPT; x += kThreads) {
     const int n = x / SPT, r = x - n * SPT, j = r >> 6;
     const int t = L.st_tile[n];
     const int u = t / tpe;
     const int s_lo = R.active_off[u];
+    float v = L.stage[x];
+    if (GATEUP && p.down_fp4) v = fp4_gather_value(v, gl(p.ts_act)[R.active_e[u]]);
     if (j < R.active_off[u + 1] - s_lo) {
       const int slot = R.slots[s_lo + j];
       const int row = (t - u * tpe) * 64 + (r & 63);
       if (GATEUP) {
-        if (p.debug_copies) gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + row] = L.stage[x];
-        store_split(gl(p.a_split) + (size_t)slot * p.I * 2, p.rank * p.I_loc + row, L.stage[x]);
+        const size_t ai = (size_t)slot * p.I + p.rank * p.I_loc + row;
+        if (p.debug_copies) {
+          gl(p.a_buf)[ai] = L.stage[x];
+          if (p.down_fp4) gl(p.aq_buf)[ai] = v;
+        }
+        store_split(gl(p.a_split) + (size_t)slot * p.I * 2, p.rank * p.I_loc + row, v);
       } else {
         gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + row] = L.stage[x];
       }

@@ -31,6 +31,8 @@ moel_status moel_validate_config(const moel_config* c) {
   if (!(c->rms_eps > 0.0f) || !(c->rope_theta > 0.0f)) return MOEL_ERR_ARG;
   if (c->shard_rank < 0 || c->shard_rank >= c->n_shards) return MOEL_ERR_ARG;
   if (c->expert_dtype != MOEL_EXPERT_NVFP4 && c->expert_dtype != MOEL_EXPERT_BF16) return MOEL_ERR_ARG;
+  if (c->down_input != MOEL_DOWN_INPUT_EXACT && c->down_input != MOEL_DOWN_INPUT_NVFP4) return MOEL_ERR_ARG;
+  if (c->down_input == MOEL_DOWN_INPUT_NVFP4 && c->expert_dtype != MOEL_EXPERT_NVFP4) return MOEL_ERR_SHAPE;
   if (c->top_k > c->n_experts || c->top_k > 8) return MOEL_ERR_SHAPE;
   if (c->hidden % 256 != 0) return MOEL_ERR_SHAPE;
   // bounds that keep the dense phases' row splits in 32-bit arithmetic
@@ -67,6 +69,7 @@ moel_status moel_validate_call(const moel_config* cfg, const moel_weights* w, co
   }
   if (cfg->expert_dtype == MOEL_EXPERT_NVFP4 && (w->ts_gate == nullptr || w->ts_up == nullptr || w->ts_down == nullptr))
     return MOEL_ERR_ARG;
+  if (cfg->down_input == MOEL_DOWN_INPUT_NVFP4 && w->ts_act == nullptr) return MOEL_ERR_ARG;
   if (misaligned(k_cache) || misaligned(v_cache) || misaligned(x) || misaligned(y)) return MOEL_ERR_ALIGN;
   const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
   const uintptr_t n = (uintptr_t)T * (uintptr_t)cfg->hidden * 4u;

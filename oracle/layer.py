@@ -230,10 +230,11 @@ def down_input_nvfp4(a: np.ndarray, ts: float) -> np.ndarray:
 
 
 def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
-               dims: Dims, act_ts: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+               dims: Dims, act_ts: Optional[float] = None,
+               a_in: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
     """One token through one expert (this GPU's shard).  Returns (a [inter], the down
     projection's input [inter], d [pooled]); with act_ts the input is a encoded as NVFP4
-    (down_input_nvfp4), else a itself."""
+    (down_input_nvfp4), else a itself; a given a_in replaces it."""
     il = dims.inter // dims.n_shards
     plc = dims.pooled // dims.n_shards
     r = dims.shard_rank
@@ -241,7 +242,8 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
     u = Wu @ pl_t
     a = np.zeros(dims.inter)
     a[r * il:(r + 1) * il] = silu(g) * u
-    a_in = a if act_ts is None else down_input_nvfp4(a, act_ts)
+    if a_in is None:
+        a_in = a if act_ts is None else down_input_nvfp4(a, act_ts)
     d = np.zeros(dims.pooled)
     d[r * plc:(r + 1) * plc] = Wd @ a_in
     return a, a_in, d
@@ -252,7 +254,7 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
 # --------------------------------------------------------------------------------------------
 def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, experts: ExpertFn,
                force_idx: Optional[np.ndarray] = None, moe_tokens=None,
-               parents=None, act_scales=None) -> Dict[str, np.ndarray]:
+               parents=None, act_scales=None, force_down_input=None) -> Dict[str, np.ndarray]:
     """One layer step.  `inp` holds fp64 arrays (bf16-valued weights):
     x [T,H], gamma1 [H], w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq*D], gamma2 [H], w_router [E,H],
     w_pool [P,H], w_unpool [H,P], k_cache/v_cache [Hkv, C, D].
@@ -263,6 +265,9 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     parents [T] makes the tokens the nodes of a token tree (see the module docstring); None
     is the chain.  act_scales [E] (fp32 activation tensor scale per expert) makes the down
     projection read its input encoded as NVFP4 (down_input_nvfp4); None reads a itself.
+    force_down_input [T, k, inter] replaces the down projection's input of every slot, as
+    force_idx replaces the routing (the caller checks that the replacement is a valid encoding
+    of a, e.g. a device's encoding of its own SwiGLU output).
     Returns y, the written K/V rows, routing and every intermediate.
     """
     x = np.asarray(inp["x"], dtype=np.float64)
@@ -313,7 +318,8 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
             for kk in range(dims.top_k):
                 if idx[t, kk] == e:
                     a_all[t, kk], aq_all[t, kk], d_all[t, kk] = expert_out(
-                        pl[t], Wg, Wu, Wd, dims, None if act_scales is None else float(act_scales[e]))
+                        pl[t], Wg, Wu, Wd, dims, None if act_scales is None else float(act_scales[e]),
+                        None if force_down_input is None else np.asarray(force_down_input[t, kk], np.float64))
     for t in toks:
         acc = np.zeros(dims.pooled)
         for kk in range(dims.top_k):              # selection order

@@ -6,7 +6,12 @@ values likewise; every cache byte outside the written slots bit-identical; the s
 expert set bit-exact wherever the oracle's k-th/(k+1)-th logit gap exceeds 1e-3, and the
 selection order consistent with the oracle's logits up to the logit error.  y is compared
 against the oracle re-run with the device's chosen experts in the device's order, so the
-exempt tokens are checked too.
+exempt tokens are checked too.  With the fp4 gather of the SwiGLU output the encoding is a
+decision taken in fp32 on values the device and the oracle compute with different rounding,
+so it is checked the same way: the device's SwiGLU output within 1e-3 of the oracle's (of
+the row's largest magnitude; it inherits the attention's bf16 probabilities through h), its encoded down input bit-exact against the oracle's encoder
+applied to that device output, the expert outputs within 1e-4 of the down projection of that
+input, and y against the oracle re-run with that input.
 """
 from __future__ import annotations
 
@@ -17,6 +22,7 @@ import numpy as np
 import torch
 
 from moe_layer_persistent_amd import binding, synth
+from oracle import formats as oformats
 from oracle import layer as olayer
 
 Y_MAX_ABS = 2e-2
@@ -103,6 +109,55 @@ def cosine(a: np.ndarray, b: np.ndarray) -> float:
     return float(np.dot(a, b) / (na * nb))
 
 
+def device_down_input(run: GpuRun, gpu_idx: np.ndarray, T: int) -> np.ndarray:
+    """[T, k, inter] the device's fp4-gathered down input of every slot (value x tensor scale)."""
+    w = run.w
+    k, I = w.top_k, w.inter
+    aq = run.plan.scratch("aq").view(16 * k, I).cpu().numpy().astype(np.float64)
+    act = run.t["act_ts"].cpu().numpy()
+    out = np.empty((T, k, I))
+    for t in range(T):
+        for kk in range(k):
+            out[t, kk] = aq[t * k + kk] * float(np.float32(act[int(gpu_idx[t, kk])]))
+    return out
+
+
+def check_fp4_gather(run: GpuRun, gpu_idx: np.ndarray, ref: Dict, toks: Sequence[int]) -> dict:
+    """The SwiGLU output, its fp4-gathered encoding and the expert outputs of the given tokens'
+    slots (ref: the oracle run with the device's down input)."""
+    w = run.w
+    k, I = w.top_k, w.inter
+    a_dev = run.plan.scratch("a").view(16 * k, I).cpu().numpy()
+    aq_dev = run.plan.scratch("aq").view(16 * k, I).cpu().numpy().astype(np.float64)
+    d_dev = run.plan.scratch("d").view(16 * k, w.pooled).cpu().numpy().astype(np.float64)
+    act = run.t["act_ts"].cpu().numpy()
+    ex = expert_fn(run)
+    plc, r = w.pooled // w.n_shards, 0
+    agree, d_err, a_err = [], 0.0, 0.0
+    for t in toks:
+        for kk in range(k):
+            slot, e = t * k + kk, int(gpu_idx[t, kk])
+            a_ref = ref["a"][t, kk]
+            err = float(np.abs(a_dev[slot] - a_ref).max() / (np.abs(a_ref).max() + 1e-30))
+            assert err <= 1e-3, ("SwiGLU output vs oracle", t, kk, err)
+            a_err = max(a_err, err)
+            ts = float(np.float32(act[e]))
+            codes, scales = oformats.nvfp4_quantize(a_dev[slot][None, :], float(act[e]))
+            want = oformats.nvfp4_values(codes, scales)[0]
+            bad = np.nonzero(aq_dev[slot] != want)[0]
+            assert bad.size == 0, ("encoded down input differs", t, kk, bad[:8], aq_dev[slot][bad[:8]], want[bad[:8]])
+            _, _, Wd = ex(e)
+            d_want = np.zeros(w.pooled)
+            d_want[r * plc:(r + 1) * plc] = Wd @ (want * ts)
+            err = float(np.abs(d_dev[slot] - d_want).max() / (np.abs(d_want).max() + 1e-30))
+            assert err <= 1e-4, ("expert output vs the down projection of its input", t, kk, err)
+            d_err = max(d_err, err)
+            # the oracle's own encoding of its exact SwiGLU output: equal except where a value
+            # sits within the device's arithmetic error of a decision point (reported)
+            agree.append(float(np.mean(olayer.down_input_nvfp4(a_ref, float(act[e])) == want * ts)))
+    return {"a_rel_err": a_err, "d_rel_err": d_err, "encoded_equal_frac_vs_oracle_own": min(agree)}
+
+
 def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[int]] = None,
                          report: Optional[dict] = None) -> dict:
     """Compares one device step with the oracle; raises AssertionError on any miss."""
@@ -114,7 +169,10 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
     toks = list(range(T)) if moe_tokens is None else sorted(set(int(t) for t in moe_tokens if t < T))
     # routing first (cheap: no experts), then the MoE block with the device's choice
     parents = out.get("parents")
-    ref0 = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), moe_tokens=[], parents=parents)
+    fp4g = getattr(w, "down_input", synth.DOWN_EXACT) == synth.DOWN_NVFP4
+    act = _f64(run.t["act_ts"]) if fp4g else None
+    ref0 = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), moe_tokens=[], parents=parents,
+                             act_scales=act)
     gap = ref0["gap"]
     exact = gap > GAP_EXEMPT
     # logits are fp32 sums over H products of bf16 values; the gates are a softmax of them,
@@ -132,7 +190,8 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
     gsel = out["gates"].cpu().numpy()
     np.testing.assert_allclose(gsel.sum(axis=1), 1.0, rtol=0, atol=1e-5)
     ref = olayer.layer_step(inp, dims, pos, run.window, expert_fn(run), force_idx=gpu_idx, moe_tokens=toks,
-                            parents=parents)
+                            parents=parents, act_scales=act,
+                            force_down_input=device_down_input(run, gpu_idx, T) if fp4g else None)
     gate_err = float(np.abs(gsel - ref["gates"]).max())
     assert gate_err <= 2 * lg_err + 1e-5, f"gates max-abs {gate_err} (logits {lg_err})"
     # KV cache: the written (head, slot) set is exact and every other byte is untouched; a
@@ -171,6 +230,8 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
         want = ref[key].reshape(T, -1)
         inter[name] = float(np.abs(got_i - want).max() / (np.abs(want).max() + 1e-30))
     stats["rel_err"] = inter
+    if fp4g:
+        stats["fp4_gather"] = check_fp4_gather(run, gpu_idx, ref, toks)
     for t in toks:
         err = float(np.abs(y[t] - ref["y"][t]).max())
         cs = cosine(y[t], ref["y"][t])

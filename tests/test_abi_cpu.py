@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.moel_abi_version() == 4
+    assert L.moel_abi_version() == 5
 
 
 def test_plan_options_reject_a_missing_plan():
@@ -72,6 +72,7 @@ def _cfg(**kw):
     ("expert_dtype", 7, binding.MOEL_ERR_ARG),
     ("kv_capacity", 0, binding.MOEL_ERR_ARG),
     ("rms_eps", 0.0, binding.MOEL_ERR_ARG),
+    ("down_input", 2, binding.MOEL_ERR_ARG),
 ])
 def test_validate_config_rejects(field, value, code):
     assert binding.lib().moel_validate_config(ctypes.byref(_cfg(**{field: value}))) == code
@@ -83,8 +84,24 @@ def test_validate_config_accepts_workloads():
         assert binding.lib().moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK, w.name
 
 
+def test_fp4_gather_needs_nvfp4_experts_and_scales():
+    L = binding.lib()
+    c = _cfg(down_input=binding.MOEL_DOWN_INPUT_NVFP4)
+    assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK
+    cb = _cfg(down_input=binding.MOEL_DOWN_INPUT_NVFP4, expert_dtype=binding.MOEL_EXPERT_BF16)
+    assert L.moel_validate_config(ctypes.byref(cb)) == binding.MOEL_ERR_SHAPE
+    w = _fake_weights()
+    vp = ctypes.c_void_p
+    args = (vp(0x100000), vp(0x200000), vp(0x300000), 16, 0, 0, vp(0x400000))
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), *args) == binding.MOEL_OK
+    w.ts_act = None
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), *args) == binding.MOEL_ERR_ARG
+    c0 = _cfg()
+    assert L.moel_validate_call(ctypes.byref(c0), ctypes.byref(w), *args) == binding.MOEL_OK
+
+
 def _fake_weights(base=0x10000):
-    vals = [base + 0x1000 * i for i in range(13)]
+    vals = [base + 0x1000 * i for i in range(14)]
     return binding.Weights(*[ctypes.c_void_p(v) for v in vals])
 
 

@@ -47,6 +47,8 @@ SMALL = [
     dict(T=9, pos=600, window=256, expert_dtype=synth.BF16, inter=256),
     dict(T=12, pos=33, window=0, n_shards=2, inter=512, pooled=256),
     dict(T=16, pos=1000, window=300, n_experts=32, top_k=8, pooled=512, inter=512),
+    dict(T=16, pos=300, window=0, down_input=synth.DOWN_NVFP4),                 # fp4 gather
+    dict(T=7, pos=33, window=20, n_shards=2, inter=512, pooled=256, down_input=synth.DOWN_NVFP4),
 ]
 
 
@@ -69,6 +71,18 @@ def test_fused_equals_unfused_and_is_deterministic():
     for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
         assert _same_bytes(a[k], b[k]), k
         assert _same_bytes(a[k], c[k]), k
+
+
+def test_fp4_gather_fused_equals_unfused():
+    w = synth.small_workload(T=16, pos=200, window=64, n_experts=32, top_k=8, pooled=512, inter=512,
+                             down_input=synth.DOWN_NVFP4)
+    run = harness.GpuRun(w)
+    a = run.run(fused=True)
+    aq = run.plan.scratch("aq").clone()
+    c = run.run(fused=False)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates"):
+        assert _same_bytes(a[k], c[k]), k
+    assert _same_bytes(aq, run.plan.scratch("aq"))
 
 
 def test_plain_and_cooperative_launches_agree():
@@ -210,7 +224,7 @@ def test_invalid_calls_launch_nothing():
 
 
 # ---------------------------------------------------------------- full-width workloads
-FULL = ["swa_fp4", "global_fp4", "swa_bf16"]
+FULL = ["swa_fp4", "global_fp4", "swa_bf16", "swa_fp4_a4"]
 
 
 @pytest.mark.parametrize("name", FULL)
