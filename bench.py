@@ -263,7 +263,7 @@ def main():
     if w.expert_dtype == synth.NVFP4 and w.down_input == synth.DOWN_EXACT:
         plan_a4 = binding.Plan(binding.config_from_workload(w.with_(down_input=synth.DOWN_NVFP4)))
         cps_a4 = [binding.LayerWeights(c.packed, dict(c.ts, act=t["act_ts"].contiguous())) for c in copies]
-        a4_us, _ = timed(True, max(5, args.steps // 2), 2, pl=plan_a4, cps=cps_a4)
+        a4_us, _ = timed(True, args.steps, args.warmup, pl=plan_a4, cps=cps_a4)
         st = plan_a4.status()
         assert st == 0, binding.status_string(st)
         plan_a4.close()
