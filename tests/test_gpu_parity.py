@@ -49,6 +49,12 @@ SMALL = [
     dict(T=16, pos=1000, window=300, n_experts=32, top_k=8, pooled=512, inter=512),
     dict(T=16, pos=300, window=0, down_input=synth.DOWN_NVFP4),                 # fp4 gather
     dict(T=7, pos=33, window=20, n_shards=2, inter=512, pooled=256, down_input=synth.DOWN_NVFP4),
+    # degenerate and extreme cases: a window of one key (each token sees only itself), a
+    # single expert per token, the largest expert count, the smallest widths
+    dict(T=16, pos=100, window=1),
+    dict(T=8, pos=50, window=0, top_k=1),
+    dict(T=16, pos=64, window=0, n_experts=512, top_k=8, pooled=256, inter=256),
+    dict(T=3, pos=5, window=0, hidden=256, n_q_heads=2, n_kv_heads=1, pooled=128, inter=128),
 ]
 
 
@@ -60,6 +66,22 @@ def test_small_matches_oracle(kw):
     rep = {}
     harness.check_against_oracle(run, run.run(fused=True), report=rep)
     _log(f"small {kw}: {rep}")
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(expert_dtype=synth.BF16), dict(down_input=synth.DOWN_NVFP4)],
+                         ids=["nvfp4", "bf16", "fp4_gather"])
+def test_concentrated_routing_matches_oracle(kw):
+    """Routing concentrated on few experts (shared component in every token): experts that
+    hold all 16 tokens, i.e. the largest token groups of the expert streams."""
+    w = synth.small_workload(T=16, pos=100, window=0, n_experts=32, top_k=8, pooled=512, inter=512, **kw)
+    _log(f"concentrated {kw}")
+    run = harness.GpuRun(w, routing="shared")
+    rep = {}
+    out = run.run(fused=True)
+    counts = np.bincount(out["expert_idx"].cpu().numpy().ravel(), minlength=w.n_experts)
+    assert counts.max() > 8, counts
+    harness.check_against_oracle(run, out, report=rep)
+    _log(f"concentrated {kw}: {rep}")
 
 
 def test_fused_equals_unfused_and_is_deterministic():
