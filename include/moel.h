@@ -204,9 +204,10 @@ moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* strea
  *   8 aq [16*k][I] with down_input NVFP4: the down projection's input as E2M1 value times
  *     E4M3 block scale (its tensor scale multiplies the projection's sums)
  * *ptr receives a device pointer into the plan's workspace (owned by the plan; valid until
- * moel_plan_destroy; overwritten by the next step), *bytes its size.  o, m and, with NVFP4
- * experts, pl, a and aq are fp32 copies the step itself does not read: a step writes them only
- * when it is given a moel_debug (they hold the last such step's values). */
+ * moel_plan_destroy; overwritten by the next step), *bytes its size.  o, m, pl, a and aq
+ * are fp32 copies the step itself does not read (the experts read pl and a as split bf16
+ * operand words): a step writes them only when it is given a moel_debug (they hold the last
+ * such step's values). */
 moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes);
 
 /* --- weight packing (one-time, not on the hot path) --------------------------------- */

@@ -39,8 +39,8 @@ struct LayerParams {
   // 1: the XCDs' L2 caches are kept coherent for the plan's memory (checked when the plan is
   // created), so a barrier's acquire invalidates only the L1; 0: it also invalidates the L2
   int l2_coherent;
-  // 1 when the call passes debug outputs: also write the fp32 copies of o, m and (NVFP4
-  // experts) pl and a that the step itself does not read (plan scratch export)
+  // 1 when the call passes debug outputs: also write the fp32 copies of o, m, pl, a and aq
+  // that the step itself does not read (plan scratch export)
   int debug_copies;
   // attention decomposition (per call)
   int attn_lo, attn_nkeys, attn_chunk, attn_nchunks;

@@ -679,7 +679,7 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
                     gl(p.logits)[t * p.E + n] = v;
                     if (p.dbg_logits) gl(p.dbg_logits)[t * p.E + n] = v;
                   } else {
-                    if (p.debug_copies || p.expert_dtype != 0) gl(p.pl)[(size_t)t * p.P + (n - p.E)] = v;
+                    if (p.debug_copies) gl(p.pl)[(size_t)t * p.P + (n - p.E)] = v;
                     store_split(gl(p.pl_split) + (size_t)t * p.P * 2, n - p.E, v);
                   }
                 }
@@ -1291,19 +1291,25 @@ __device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_ar
 
 // ------------------------------------------------------------------------------------------
 // bf16 experts on 16x16x32 MFMA.  The 16 A rows carry up to 8 slots as (hi x8, lo x8); a
-// second row tile takes slots 8..15.
+// second row tile takes slots 8..15, read ready-made from the split-operand copies of pl and
+// a (each lane loads only its row's half: 16 bytes per step).  Tiles ta..tb-1 of one expert
+// run as one stream: the k-waves split each tile's K/32 steps evenly, and a ring of RD steps
+// (weight and activation words) per wave runs across tile boundaries, so a tile's reduction
+// never waits for the next tile's first loads.
 // ------------------------------------------------------------------------------------------
 template <bool GATEUP>
 __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
                                   DenseLds& L) {
   constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int RD = 2;  // steps in flight per wave
   const int lane = lane_id(), wv = wave_id();
   const int e = R.active_e[u];
   const int s_lo = R.active_off[u], n_e = R.active_off[u + 1] - s_lo;
   const int K = GATEUP ? p.P : p.I;
   const int S = K >> 5;
-  const int nkw = S < kWaves ? S : kWaves;
-  const int sa = wv * S / nkw, sb = (wv + 1) * S / nkw;
+  const int nkw = kwaves_for(S);
+  const int nst = S / nkw;  // steps per k-wave and tile
+  const int sa = wv * nst;
   const int nrt = n_e > 8 ? 2 : 1;  // row tiles
   const uint8_t* wb[NM];
   if (GATEUP) {
@@ -1312,53 +1318,54 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
   } else {
     wb[0] = p.w_down + (size_t)e * p.stride_down;
   }
-  const bool lo_row = (lane & 15) >= 8;
-  const float* arow[2];
+  // split row of this lane's slot, at its half (nearest values for A rows 0-7, remainders
+  // for rows 8-15); the lane's 8 k of a step (the packed weights' order, 32s + 4q + 0..3 and
+  // 32s + 16 + 4q + 0..3) are quads 8s + q and 8s + 4 + q
+  const uint16_t* arow[2];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
     const int j = 8 * rt + (lane & 7);
     arow[rt] = nullptr;
     if (j < n_e) {
       const int slot = R.slots[s_lo + j];
-      arow[rt] = GATEUP ? p.pl + (size_t)(slot / p.topk) * p.P : p.a_buf + (size_t)slot * p.I;
+      arow[rt] = (GATEUP ? p.pl_split + (size_t)(slot / p.topk) * p.P * 2 : p.a_split + (size_t)slot * p.I * 2) +
+                 ((lane & 15) >= 8 ? 4 : 0) + 8 * (lane >> 4);
     }
   }
-  const int kq = 4 * (lane >> 4);  // the packed weights' k order
-  auto aload = [&](int rt, int s) -> u32x4 {
-    u32x4 hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-    if (arow[rt] != nullptr) {
-      const float* src = arow[rt] + 32 * s + kq;
-      split8(ldgf4(src), ldgf4(src + 16), hi, lo);
-    }
-    return lo_row ? lo : hi;
+  struct Step {
+    u32x4 w[NM];
+    u32x2 a[2][2];
   };
-  for (int ti = ta; ti < tb; ++ti) {
-    f32x4 acc[2][NM];
+  // flattened position i of this wave: tile ta + i / nst, step sa + i % nst
+  const int total = wv < nkw ? (tb - ta) * nst : 0;
+  auto issue = [&](Step& st, int i) {
+    const int tr = i / nst, s = sa + i - tr * nst;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int m = 0; m < NM; ++m)
+      st.w[m] = ldg_stream(wb[m] + ((size_t)(ta + tr) * S + s) * 1024 + lane * 16);
 #pragma unroll
-      for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (wv < nkw) {
-      const uint8_t* tb_[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) tb_[m] = wb[m] + (size_t)ti * S * 1024 + lane * 16;
-      for (int s = sa; s < sb; ++s) {
-        u32x4 w[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) w[m] = ldg_stream(tb_[m] + (size_t)s * 1024);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-          if (rt < nrt) {
-            const u32x4 a = aload(rt, s);
-#pragma unroll
-            for (int m = 0; m < NM; ++m) acc[rt][m] = mfma16x16x32(a, w[m], acc[rt][m]);
-          }
-        }
+    for (int rt = 0; rt < 2; ++rt) {
+      if (rt < nrt && arow[rt] != nullptr) {
+        st.a[rt][0] = ldg8(arow[rt] + 64 * s);
+        st.a[rt][1] = ldg8(arow[rt] + 64 * s + 32);
       }
+    }
+  };
+  f32x4 acc[2][NM];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // reduction of tile ti (all waves take part)
+  auto tile_end = [&](int ti) {
+    if (wv < nkw) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int m = 0; m < NM; ++m) L.red[(wv * 4 + rt * 2 + m) * 64 + lane] = acc[rt][m];
+        for (int m = 0; m < NM; ++m) {
+          L.red[(wv * 4 + rt * 2 + m) * 64 + lane] = acc[rt][m];
+          acc[rt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
     }
     lds_barrier();
     // slot j = 8*rt + jj: hi at A row jj, lo at row 8 + jj; row i lives in lane 16*(i/4)+r, comp i%4
@@ -1373,12 +1380,45 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
         if (GATEUP)
           s1 += L.red[(w * 4 + rt * 2 + 1) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + 1) * 64 + l_lo][c];
       }
-      if (GATEUP)
-        gl(p.a_buf)[(size_t)slot * p.I + p.rank * p.I_loc + ti * 16 + r] = s0 / (1.0f + __expf(-s0)) * s1;
-      else
+      if (GATEUP) {
+        const float a = s0 / (1.0f + __expf(-s0)) * s1;
+        const int c = p.rank * p.I_loc + ti * 16 + r;
+        if (p.debug_copies) gl(p.a_buf)[(size_t)slot * p.I + c] = a;
+        store_split(gl(p.a_split) + (size_t)slot * p.I * 2, c, a);
+      } else {
         gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = s0;
+      }
     }
-    lds_barrier();
+    lds_barrier();  // red is rewritten at the next tile end
+  };
+  if (wv >= nkw) {
+    for (int ti = ta; ti < tb; ++ti) tile_end(ti);
+    return;
+  }
+  Step ring[RD];
+#pragma unroll
+  for (int d = 0; d < RD; ++d)
+    if (d < total) issue(ring[d], d);
+  for (int i0 = 0; i0 < total; i0 += RD) {
+#pragma unroll
+    for (int d = 0; d < RD; ++d) {
+      const int i = i0 + d;
+      if (i < total) {
+        const Step cur = ring[d];
+        if (i + RD < total) issue(ring[d], i + RD);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+          if (rt < nrt) {
+            u32x4 a = {0u, 0u, 0u, 0u};
+            if (arow[rt] != nullptr) a = u32x4{cur.a[rt][0][0], cur.a[rt][0][1], cur.a[rt][1][0], cur.a[rt][1][1]};
+#pragma unroll
+            for (int m = 0; m < NM; ++m) acc[rt][m] = mfma16x16x32(a, cur.w[m], acc[rt][m]);
+          }
+        }
+        const int tr = i / nst;
+        if (i - tr * nst == nst - 1) tile_end(ta + tr);
+      }
+    }
   }
 }
 
