@@ -1295,12 +1295,14 @@ __device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_ar
 // a (each lane loads only its row's half: 16 bytes per step).  Tiles ta..tb-1 of one expert
 // run as one stream: the k-waves split each tile's K/32 steps evenly, and a ring of RD steps
 // (weight and activation words) per wave runs across tile boundaries, so a tile's reduction
-// never waits for the next tile's first loads.
+// never waits for the next tile's first loads.  Every step carries two weight words per lane:
+// gate and up of one tile, or (down projection) two adjacent tiles sharing the activation.
 // ------------------------------------------------------------------------------------------
 template <bool GATEUP>
 __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, int u, int ta, int tb,
                                   DenseLds& L) {
-  constexpr int NM = GATEUP ? 2 : 1;
+  constexpr int NM = 2;  // weight words per step: gate and up, or two adjacent down tiles
+  constexpr int TPS = GATEUP ? 1 : 2;  // tiles per step
   constexpr int RD = 2;  // steps in flight per wave
   const int lane = lane_id(), wv = wave_id();
   const int e = R.active_e[u];
@@ -1316,7 +1318,7 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
     wb[0] = p.w_gate + (size_t)e * p.stride_gate;
     wb[NM - 1] = p.w_up + (size_t)e * p.stride_up;
   } else {
-    wb[0] = p.w_down + (size_t)e * p.stride_down;
+    wb[0] = wb[1] = p.w_down + (size_t)e * p.stride_down;
   }
   // split row of this lane's slot, at its half (nearest values for A rows 0-7, remainders
   // for rows 8-15); the lane's 8 k of a step (the packed weights' order, 32s + 4q + 0..3 and
@@ -1336,13 +1338,17 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
     u32x4 w[NM];
     u32x2 a[2][2];
   };
-  // flattened position i of this wave: tile ta + i / nst, step sa + i % nst
-  const int total = wv < nkw ? (tb - ta) * nst : 0;
+  // flattened position i of this wave: tile group ta + TPS (i / nst), step sa + i % nst; the
+  // last group of an odd down range has one tile (its second word is not loaded or stored)
+  const int ngrp = (tb - ta + TPS - 1) / TPS;
+  const int total = wv < nkw ? ngrp * nst : 0;
   auto issue = [&](Step& st, int i) {
     const int tr = i / nst, s = sa + i - tr * nst;
 #pragma unroll
-    for (int m = 0; m < NM; ++m)
-      st.w[m] = ldg_stream(wb[m] + ((size_t)(ta + tr) * S + s) * 1024 + lane * 16);
+    for (int m = 0; m < NM; ++m) {
+      const int ti = ta + TPS * tr + (GATEUP ? 0 : m);
+      if (GATEUP || ti < tb) st.w[m] = ldg_stream(wb[m] + ((size_t)ti * S + s) * 1024 + lane * 16);
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       if (rt < nrt && arow[rt] != nullptr) {
@@ -1356,8 +1362,10 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
     for (int m = 0; m < NM; ++m) acc[rt][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // reduction of tile ti (all waves take part)
-  auto tile_end = [&](int ti) {
+  // reduction of tile group tg: tiles ta + TPS tg .. (all waves take part)
+  auto tile_end = [&](int tg) {
+    const int ti = ta + TPS * tg;
+    const int nt = GATEUP ? 1 : (ti + 1 < tb ? 2 : 1);
     if (wv < nkw) {
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
@@ -1369,14 +1377,14 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
     }
     lds_barrier();
     // slot j = 8*rt + jj: hi at A row jj, lo at row 8 + jj; row i lives in lane 16*(i/4)+r, comp i%4
-    for (int x = threadIdx.x; x < 16 * n_e; x += kThreads) {
-      const int r = x & 15, j = x >> 4;
+    for (int x = threadIdx.x; x < 16 * n_e * nt; x += kThreads) {
+      const int r = x & 15, j = (x >> 4) % n_e, m = (x >> 4) / n_e;  // m: tile of the group (down)
       const int rt = j >> 3, jj = j & 7;
       const int l_hi = 16 * (jj >> 2) + r, l_lo = 16 * ((8 + jj) >> 2) + r, c = jj & 3;
       const int slot = R.slots[s_lo + j];
       float s0 = 0.f, s1 = 0.f;
       for (int w = 0; w < nkw; ++w) {
-        s0 += L.red[(w * 4 + rt * 2 + 0) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + 0) * 64 + l_lo][c];
+        s0 += L.red[(w * 4 + rt * 2 + m) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + m) * 64 + l_lo][c];
         if (GATEUP)
           s1 += L.red[(w * 4 + rt * 2 + 1) * 64 + l_hi][c] + L.red[(w * 4 + rt * 2 + 1) * 64 + l_lo][c];
       }
@@ -1386,13 +1394,13 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
         if (p.debug_copies) gl(p.a_buf)[(size_t)slot * p.I + c] = a;
         store_split(gl(p.a_split) + (size_t)slot * p.I * 2, c, a);
       } else {
-        gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + ti * 16 + r] = s0;
+        gl(p.d_buf)[(size_t)slot * p.P + p.rank * p.P_loc + (ti + m) * 16 + r] = s0;
       }
     }
     lds_barrier();  // red is rewritten at the next tile end
   };
   if (wv >= nkw) {
-    for (int ti = ta; ti < tb; ++ti) tile_end(ti);
+    for (int tg = 0; tg < ngrp; ++tg) tile_end(tg);
     return;
   }
   Step ring[RD];
@@ -1416,7 +1424,7 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
           }
         }
         const int tr = i / nst;
-        if (i - tr * nst == nst - 1) tile_end(ta + tr);
+        if (i - tr * nst == nst - 1) tile_end(tr);
       }
     }
   }
