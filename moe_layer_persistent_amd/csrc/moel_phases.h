@@ -410,8 +410,10 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
 // Attention partials.  Item = (kv head g, key chunk c); each wave is one q head of the group.
 // Keys go in sub-chunks of SK = 128: while one sub-chunk is in LDS and being used, the next
 // one's K/V rows are already in flight into registers.  S^T = K Q^T on MFMA (keys as rows;
-// q as hi + lo), softmax in fp32 with the exact max of each sub-chunk and an online rescale
-// between sub-chunks, O += P V on MFMA (P as hi + lo; V transposed in LDS).
+// q as hi + lo, pre-multiplied by log2(e)/sqrt(D) so that scores come out in base-2 units),
+// softmax in fp32 with exp2, the exact max of each sub-chunk and an online rescale between
+// sub-chunks, O += P V on MFMA (P as hi + lo; V transposed in LDS).  The partials' running
+// maxima stay in base-2 units for the merge.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct AttnLds {
@@ -441,7 +443,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   const int lane = lane_id(), wv = wave_id();
   const int grp = p.Hq / p.Hkv;
   const int nitems = p.Hkv * p.attn_nchunks;
-  const float scale = 1.0f / sqrtf((float)D);
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
   const float NEG = -__builtin_inff();
   const int gq = lane >> 4, tq = lane & 15;
   for (int it = wg; it < nitems; it += p.nwg) {
@@ -480,7 +482,11 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
         qb[s] = ldgf4(qs + 32 * s + 4);
       }
 #pragma unroll
-      for (int s = 0; s < NS; ++s) split8(qa[s], qb[s], qh[s], ql[s]);
+      for (int s = 0; s < NS; ++s) {
+        qa[s] = float4{qa[s].x * qscale, qa[s].y * qscale, qa[s].z * qscale, qa[s].w * qscale};
+        qb[s] = float4{qb[s].x * qscale, qb[s].y * qscale, qb[s].z * qscale, qb[s].w * qscale};
+        split8(qa[s], qb[s], qh[s], ql[s]);
+      }
     }
     float m_run = NEG, l_run = 0.f;
     f32x4 O[ND];
@@ -518,30 +524,39 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
             S[kt] = mfma16x16x32(ka, ql[s], S[kt]);
           }
         }
-        // mask + scale; lane holds keys kt*16 + 4*gq + r of token tq
+        // mask; lane holds keys kt*16 + 4*gq + r of token tq.  A whole sub-chunk of cached
+        // keys inside every token's window needs none (rows of tokens past T are never read).
         float mx = NEG;
+        const bool all_vis = nk == SK && sb + SK <= p.pos && (p.window == 0 || sb > p.pos + p.T - 1 - p.window);
+        if (all_vis) {
 #pragma unroll
-        for (int kt = 0; kt < NKT; ++kt)
+          for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = sb + kt * 16 + 4 * gq + r;
-            const bool vis = tq < p.T && (j - sb) < nk &&
-                             (j < p.pos ? (p.window == 0 || j > ptok - p.window) : ((sees >> (j - p.pos)) & 1u) != 0);
-            const float v = vis ? S[kt][r] * scale : NEG;
-            S[kt][r] = v;
-            mx = fmaxf(mx, v);
-          }
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[kt][r]);
+        } else {
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = sb + kt * 16 + 4 * gq + r;
+              const bool vis = tq < p.T && (j - sb) < nk &&
+                               (j < p.pos ? (p.window == 0 || j > ptok - p.window) : ((sees >> (j - p.pos)) & 1u) != 0);
+              const float v = vis ? S[kt][r] : NEG;
+              S[kt][r] = v;
+              mx = fmaxf(mx, v);
+            }
+        }
         mx = fmaxf(mx, __shfl_xor(mx, 16));
         mx = fmaxf(mx, __shfl_xor(mx, 32));
         const float m_new = fmaxf(m_run, mx);
         const bool none = (m_new == NEG);
-        const float alpha = none ? 1.f : __expf(m_run - m_new);
+        const float alpha = none ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
         float ls = 0.f;
 #pragma unroll
         for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float e = none ? 0.f : __expf(S[kt][r] - m_new);
+            const float e = none ? 0.f : __builtin_amdgcn_exp2f(S[kt][r] - m_new);
             S[kt][r] = e;
             ls += e;
           }
@@ -622,12 +637,12 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
       float Mg = M;
 #pragma unroll
       for (int j = 0; j < U; ++j) Mg = fmaxf(Mg, ml[j][0]);
-      const float r = M == NEG ? 0.f : __expf(M - Mg);  // rescale of the earlier groups
+      const float r = M == NEG ? 0.f : __builtin_amdgcn_exp2f(M - Mg);  // rescale of the earlier groups (base 2)
       num *= r;
       den *= r;
 #pragma unroll
       for (int j = 0; j < U; ++j) {
-        const float wgt = (c0 + j < nch && ml[j][0] != NEG) ? __expf(ml[j][0] - Mg) : 0.f;
+        const float wgt = (c0 + j < nch && ml[j][0] != NEG) ? __builtin_amdgcn_exp2f(ml[j][0] - Mg) : 0.f;
         num = fmaf(wgt, ov[j], num);
         den = fmaf(wgt, ml[j][1], den);
       }
