@@ -412,8 +412,8 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
 // one's K/V rows are already in flight into registers.  S^T = K Q^T on MFMA (keys as rows;
 // q as hi + lo, pre-multiplied by log2(e)/sqrt(D) so that scores come out in base-2 units),
 // softmax in fp32 with exp2, the exact max of each sub-chunk and an online rescale between
-// sub-chunks, O += P V on MFMA (P as hi + lo; V transposed in LDS).  The partials' running
-// maxima stay in base-2 units for the merge.
+// sub-chunks, O += P V on MFMA (P rounded to bf16, nearest even; V transposed in LDS).  The
+// partials' running maxima stay in base-2 units for the merge.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct AttnLds {
@@ -573,12 +573,8 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
           for (int r = 0; r < 4; ++r) O[d][r] *= ao[r];
 #pragma unroll
         for (int kp = 0; kp < NKT / 2; ++kp) {
-          const u32x2 q0 = split_bf16(S[2 * kp][0], S[2 * kp][1]);
-          const u32x2 q1 = split_bf16(S[2 * kp][2], S[2 * kp][3]);
-          const u32x2 q2 = split_bf16(S[2 * kp + 1][0], S[2 * kp + 1][1]);
-          const u32x2 q3 = split_bf16(S[2 * kp + 1][2], S[2 * kp + 1][3]);
-          const u32x4 ph = {q0[0], q1[0], q2[0], q3[0]};
-          const u32x4 plo = {q0[1], q1[1], q2[1], q3[1]};
+          const u32x4 ph = {pack2bf(S[2 * kp][0], S[2 * kp][1]), pack2bf(S[2 * kp][2], S[2 * kp][3]),
+                            pack2bf(S[2 * kp + 1][0], S[2 * kp + 1][1]), pack2bf(S[2 * kp + 1][2], S[2 * kp + 1][3])};
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
             // k slots of this lane: keys 32kp + 4gq + 0..3 and 32kp + 16 + 4gq + 0..3
@@ -587,7 +583,6 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
             const u32x2 v1 = *reinterpret_cast<const u32x2*>(&L.Vt[L_t::vt_index(dd, 32 * kp + 16 + 4 * gq)]);
             const u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
             O[d] = mfma16x16x32(ph, vb, O[d]);
-            O[d] = mfma16x16x32(plo, vb, O[d]);
           }
         }
       }
