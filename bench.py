@@ -208,6 +208,11 @@ def main():
     dev = torch.device("cuda")
     t = synth.make_layer(w, 0, dev, routing=args.routing)
     plan = binding.Plan(binding.config_from_workload(w))
+    # a second plan for the same weights with the SwiGLU output gathered in fp4 (created beside
+    # the first, before the weights are packed, so that both workspaces are allocated alike)
+    plan_a4 = None
+    if w.expert_dtype == synth.NVFP4 and w.down_input == synth.DOWN_EXACT:
+        plan_a4 = binding.Plan(binding.config_from_workload(w.with_(down_input=synth.DOWN_NVFP4)))
     copies = [plan.pack_layer(t), plan.pack_layer(t)]
     T = w.T
     x = t["x"].contiguous()
@@ -260,8 +265,7 @@ def main():
     # the same weights with the SwiGLU output gathered in fp4 before the down projection (the
     # payload of the N-sharded layout's first all-gather), through a plan configured for it
     a4_us = None
-    if w.expert_dtype == synth.NVFP4 and w.down_input == synth.DOWN_EXACT:
-        plan_a4 = binding.Plan(binding.config_from_workload(w.with_(down_input=synth.DOWN_NVFP4)))
+    if plan_a4 is not None:
         cps_a4 = [binding.LayerWeights(c.packed, dict(c.ts, act=t["act_ts"].contiguous())) for c in copies]
         a4_us, _ = timed(True, args.steps, args.warmup, pl=plan_a4, cps=cps_a4)
         st = plan_a4.status()
