@@ -422,7 +422,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   if (!hip_ok(hipGetDeviceProperties(&prop, dev))) return MOEL_ERR_HIP;
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOEL_ERR_UNSUPPORTED;
   int coop = 0;
-  hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (!hip_ok(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev))) return MOEL_ERR_HIP;
   if (!coop) return MOEL_ERR_UNSUPPORTED;
 
   {
@@ -475,7 +475,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   }
   char* ws = static_cast<char*>(plan->ws);
   if (!hip_ok(hipMemset(ws, 0, off))) {
-    hipFree(plan->ws);
+    (void)hipFree(plan->ws);  // error path: the first error is the one reported
     delete plan;
     return MOEL_ERR_HIP;
   }
@@ -487,7 +487,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     if (hc == nullptr || hs == nullptr) {
       std::free(hc);
       std::free(hs);
-      hipFree(plan->ws);
+      (void)hipFree(plan->ws);  // error path: the first error is the one reported
       delete plan;
       return MOEL_ERR_HIP;
     }
@@ -504,7 +504,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     std::free(hc);
     std::free(hs);
     if (!ok) {
-      hipFree(plan->ws);
+      (void)hipFree(plan->ws);  // error path: the first error is the one reported
       delete plan;
       return MOEL_ERR_HIP;
     }
@@ -576,7 +576,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
     ok = hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, D == 64 ? fused_fn<64>() : fused_fn<128>(),
                                                              kThreads, mx));
   if (!ok || per_cu < 1) {
-    hipFree(plan->ws);
+    (void)hipFree(plan->ws);  // error path: the first error is the one reported
     delete plan;
     return ok ? MOEL_ERR_UNSUPPORTED : MOEL_ERR_HIP;
   }
