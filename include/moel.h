@@ -140,8 +140,8 @@ moel_status moel_validate_call(const moel_config* cfg, const moel_weights* w,
                                const void* k_cache, const void* v_cache, const float* x,
                                int32_t T, int32_t pos, int32_t window, const float* y);
 
-/* Bytes of the packed layouts (equal to the canonical bytes of the same matrix, plus at
- * most 1 KiB of zero padding per 64-row tile for NVFP4 when K is not a multiple of 256). */
+/* Bytes of the packed layouts: exactly the canonical bytes of the same matrices (bf16
+ * elements; for NVFP4 the codes plus the E4M3 block scales), with no padding. */
 size_t moel_packed_dense_bytes(int32_t N, int32_t K);
 size_t moel_packed_experts_bytes(const moel_config* cfg, int32_t which /*0 gate,1 up,2 down*/);
 
@@ -222,8 +222,10 @@ moel_status moel_pack_dense(const void* src, int32_t N, int32_t K, int32_t rope_
 
 /* Experts of one matrix kind (0 gate, 1 up, 2 down) -> packed layout.
  *   NVFP4: codes uint8 [E, N, K/2] (even k in the low nibble) and scales uint8 E4M3
- *          [E, N, K/16] -> 64-row tiles: per tile the 16-byte codes of each row per
- *          32-element step, then the 16 block scales of each row per 256-element chunk.
+ *          [E, N, K/16] -> 64-row tiles; per tile K/64 pairs of 2304 bytes: two 1 KiB code
+ *          steps (lane l: the 32 codes of row l for one 32-element k step, even k in the low
+ *          nibble), then 256 bytes of scales (lane l: row l's 4 block scales of the pair's
+ *          64 k).  K % 128 == 0.
  *   bf16:  src [E, N, K] (scales NULL) -> the dense layout per expert. */
 moel_status moel_pack_experts(const moel_config* cfg, int32_t which, const void* src,
                               const void* scales, void* dst, void* stream);

@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from typing import Dict, Optional
 
 import torch
@@ -123,7 +124,7 @@ def _stream(stream=None):
 
 def config_from_workload(w, kv_capacity: Optional[int] = None) -> Config:
     return Config(w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pooled, w.inter, w.n_experts,
-                  w.top_k, w.expert_dtype, w.n_shards, 0,
+                  w.top_k, w.expert_dtype, w.n_shards, getattr(w, "shard_rank", 0),
                   w.kv_capacity if kv_capacity is None else kv_capacity, w.rms_eps, w.rope_theta,
                   getattr(w, "down_input", MOEL_DOWN_INPUT_EXACT))
 
@@ -157,6 +158,10 @@ class Plan:
             self.handle = None
 
     def __del__(self):
+        # at interpreter shutdown the HIP runtime (and a profiler attached to it) may already
+        # be finalised: leave the workspace to the process exit instead of calling hipFree
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

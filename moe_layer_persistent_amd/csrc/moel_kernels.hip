@@ -7,6 +7,7 @@
 #include <cstdlib>
 #include <algorithm>
 #include <cstring>
+#include <mutex>
 #include <new>
 
 #include "../../include/moel.h"
@@ -45,12 +46,18 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
   KP& p = kernel_params();
   __shared__ int s_abort;
   const int wg = blockIdx.x;
-  stamp(p, kNumPhases);  // entry
+  const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
   if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
   __syncthreads();
   const bool run = s_abort == 0;
   unsigned bar = 0;
   auto sync = [&]() { grid_barrier(p, ++bar); };
+  // an aborted launch leaves every caller buffer untouched, the timestamps included
+  auto stamp = [&](KP& p, int slot) {
+    if (run) moel::stamp(p, slot);
+  };
+  if (run && p.dbg_ts != nullptr && threadIdx.x == 0)
+    gl(p.dbg_ts)[blockIdx.x * MOEL_N_STAMPS_DEV + kNumPhases] = t_entry;  // entry
   stamp(p, 16 + kPhNorm1);
   stamp(p, kPhNorm1);
   stamp(p, 16 + kPhQkv);
@@ -97,6 +104,12 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
         __hip_atomic_fetch_add(gl(p.ctrl) + kExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (prev == (unsigned)p.nwg - 1) {
       auto ctrl = gl(p.ctrl);
+      if (p.status_out != nullptr) {
+        __hip_atomic_store(gl(p.status_out),
+                           __hip_atomic_load(ctrl + kStatus, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(ctrl + kStatus, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
       __hip_atomic_store(ctrl + kFlag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ctrl + kTop, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int g = 0; g < kBarGroups; ++g)
@@ -196,6 +209,26 @@ __global__ void k_pack_nvfp4(const uint8_t* __restrict__ codes, const uint8_t* _
 
 __global__ void k_set_word(unsigned* w, unsigned v) { *w = v; }
 
+__global__ void k_fill_u32(unsigned* w, unsigned v, size_t n) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) w[i] = v;
+}
+
+// RoPE rows [pos0, pos0 + nrows) of the cos/sin table: angle = position * inv_freq[i] in
+// double (inv_freq = theta^(-2i/D), evaluated on the host), cos and sin in double, stored as
+// float -- the same values as the plan's host-computed table.
+struct RopeFreq {
+  double f[64];
+};
+__global__ void k_rope_rows(float* cos_out, float* sin_out, int pos0, int nrows, int half, RopeFreq fq) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= nrows * half) return;
+  const int r = e / half, i = e - r * half;
+  const double a = (double)(pos0 + r) * fq.f[i];
+  cos_out[e] = (float)cos(a);
+  sin_out[e] = (float)sin(a);
+}
+
 // Cross-XCD coherence check of the L2 caches for memory from hipMalloc (the plan's workspace
 // and the caller's tensors).  Workgroups 1..15 (every XCD under round-robin dispatch, the
 // writer's included) read a 64 KiB block, so that their XCDs' L2 hold copies of it; workgroup
@@ -291,6 +324,13 @@ size_t lds_for_phase(int ph, int D) {
   return kRouteBytes + body;
 }
 
+// LDS of the persistent launch: the largest phase
+size_t lds_fused_bytes(int D) {
+  size_t mx = 0;
+  for (int ph = 0; ph < kNumPhases; ++ph) mx = std::max(mx, lds_for_phase(ph, D));
+  return mx;
+}
+
 bool hip_ok(hipError_t e) {
   if (e != hipSuccess) {
     if (std::getenv("MOEL_LOG")) std::fprintf(stderr, "moel: HIP error %s\n", hipGetErrorString(e));
@@ -299,17 +339,14 @@ bool hip_ok(hipError_t e) {
   return true;
 }
 
-// Runs the coherence check a few times on the current device; true when no stale word and no
-// timeout was seen.  The result is kept per device for the process.
-bool l2_coherent_device(int dev) {
-  static int known[64];  // 0 unknown, 1 coherent, 2 not
-  if (dev >= 0 && dev < 64 && known[dev] != 0) return known[dev] == 1;
-  unsigned* mem = nullptr;
-  hipStream_t s = nullptr;
-  bool good = hip_ok(hipMalloc(&mem, (kCohWords + 64) * sizeof(unsigned))) && hip_ok(hipStreamCreate(&s));
+// Runs the coherence check four times on `mem` (kCohMemWords words of device memory) on
+// stream `s`; true when no stale word and no timeout was seen.
+constexpr int kCohMemWords = kCohWords + 64;
+bool coherence_check_on(unsigned* mem, hipStream_t s) {
   unsigned* buf = mem;
   unsigned* flags = mem + kCohWords;
   unsigned* out = mem + kCohWords + 32;
+  bool good = true;
   for (unsigned rep = 0; good && rep < 4; ++rep) {
     const unsigned gen = 0x5a000001u + rep;
     hipLaunchKernelGGL(k_coherence_fill, dim3(kCohWords / 256), dim3(256), 0, s, buf, gen - 1, flags, out);
@@ -318,8 +355,28 @@ bool l2_coherent_device(int dev) {
     good = hip_ok(hipGetLastError()) && hip_ok(hipStreamSynchronize(s)) &&
            hip_ok(hipMemcpy(h, out, sizeof(h), hipMemcpyDeviceToHost)) && h[0] == 0 && h[1] == 0;
   }
-  if (s != nullptr) (void)hipStreamDestroy(s);
-  if (mem != nullptr) (void)hipFree(mem);
+  return good;
+}
+
+// The coherence check's result for device `dev`, kept per device for the process.  The first
+// query runs the check: on `mem` / `s` when given (memory the caller owns), else on memory and a
+// stream allocated for it.
+std::mutex g_coh_mu;
+bool l2_coherent_device(int dev, unsigned* mem = nullptr, hipStream_t s = nullptr) {
+  static int known[64];  // 0 unknown, 1 coherent, 2 not
+  std::lock_guard<std::mutex> lock(g_coh_mu);
+  if (dev >= 0 && dev < 64 && known[dev] != 0) return known[dev] == 1;
+  bool good;
+  if (mem != nullptr) {
+    good = coherence_check_on(mem, s);
+  } else {
+    unsigned* own = nullptr;
+    hipStream_t os = nullptr;
+    good = hip_ok(hipMalloc(&own, kCohMemWords * sizeof(unsigned))) && hip_ok(hipStreamCreate(&os)) &&
+           coherence_check_on(own, os);
+    if (os != nullptr) (void)hipStreamDestroy(os);
+    if (own != nullptr) (void)hipFree(own);
+  }
   if (dev >= 0 && dev < 64) known[dev] = good ? 1 : 2;
   return good;
 }
@@ -343,22 +400,105 @@ const void* phase_fn(int ph) {
   }
 }
 
-moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
-                         const float* x, int32_t T, int32_t pos, int32_t window, const int32_t* parents,
-                         float* y, const moel_debug* dbg, LayerParams& p) {
-  if (plan == nullptr) return MOEL_ERR_ARG;
-  moel_status st = moel_validate_call(&plan->cfg, w, k_cache, v_cache, x, T, pos, window, y);
+// Byte offsets of the workspace regions for a shape, a grid of nwg workgroups and a RoPE table
+// of rope_rows rows.
+struct WsLayout {
+  size_t ctrl, q, ao, aml, o, h, lg, pl, a, d, pls, as, aq, m, oop, hop, mop, cos, sin, total;
+};
+WsLayout ws_layout(const moel_config* cfg, int nwg, int rope_rows) {
+  WsLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t D = cfg->head_dim, Hq = cfg->n_q_heads, H = cfg->hidden, P = cfg->pooled, I = cfg->inter;
+  const size_t E = cfg->n_experts, k = cfg->top_k, grp = Hq / cfg->n_kv_heads, T = kMaxT;
+  L.ctrl = take((size_t)kCtrlWords * 4);
+  L.q = take(T * Hq * D * 4);
+  L.ao = take((size_t)nwg * grp * T * D * 4);
+  L.aml = take((size_t)nwg * grp * T * 2 * 4);
+  L.o = take(T * Hq * D * 4);
+  L.h = take(T * H * 4);
+  L.lg = take(T * E * 4);
+  L.pl = take(T * P * 4);
+  L.a = take(T * k * I * 4);
+  L.d = take(T * k * P * 4);
+  L.pls = take(T * P * 4);
+  L.as = take(T * k * I * 4);
+  L.aq = take(T * k * I * 4);
+  L.m = take(T * P * 4);
+  L.oop = take(T * Hq * D * 4);
+  L.hop = take(T * H * 4);
+  L.mop = take(T * P * 4);
+  L.cos = take((size_t)rope_rows * (D / 2) * 4);
+  L.sin = take((size_t)rope_rows * (D / 2) * 4);
+  L.total = off;
+  return L;
+}
+
+// Shape fields of the launch parameters and their pointers into a workspace laid out by L.
+void bind_base(LayerParams& b, const moel_config* cfg, int nwg, const WsLayout& L, char* ws) {
+  std::memset(&b, 0, sizeof(b));
+  b.H = cfg->hidden;
+  b.Hq = cfg->n_q_heads;
+  b.Hkv = cfg->n_kv_heads;
+  b.D = cfg->head_dim;
+  b.P = cfg->pooled;
+  b.I = cfg->inter;
+  b.E = cfg->n_experts;
+  b.topk = cfg->top_k;
+  b.n_shards = cfg->n_shards;
+  b.rank = cfg->shard_rank;
+  b.I_loc = cfg->inter / cfg->n_shards;
+  b.P_loc = cfg->pooled / cfg->n_shards;
+  b.kv_cap = cfg->kv_capacity;
+  b.expert_dtype = cfg->expert_dtype;
+  b.down_fp4 = cfg->down_input == MOEL_DOWN_INPUT_NVFP4 ? 1 : 0;
+  b.eps = cfg->rms_eps;
+  b.nwg = nwg;
+  b.stride_gate = moel_packed_experts_bytes(cfg, 0) / (size_t)cfg->n_experts;
+  b.stride_up = moel_packed_experts_bytes(cfg, 1) / (size_t)cfg->n_experts;
+  b.stride_down = moel_packed_experts_bytes(cfg, 2) / (size_t)cfg->n_experts;
+  b.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
+  b.q_buf = reinterpret_cast<float*>(ws + L.q);
+  b.attn_o = reinterpret_cast<float*>(ws + L.ao);
+  b.attn_ml = reinterpret_cast<float*>(ws + L.aml);
+  b.o_buf = reinterpret_cast<float*>(ws + L.o);
+  b.h_buf = reinterpret_cast<float*>(ws + L.h);
+  b.logits = reinterpret_cast<float*>(ws + L.lg);
+  b.pl = reinterpret_cast<float*>(ws + L.pl);
+  b.a_buf = reinterpret_cast<float*>(ws + L.a);
+  b.d_buf = reinterpret_cast<float*>(ws + L.d);
+  b.pl_split = reinterpret_cast<uint16_t*>(ws + L.pls);
+  b.a_split = reinterpret_cast<uint16_t*>(ws + L.as);
+  b.aq_buf = reinterpret_cast<float*>(ws + L.aq);
+  b.m_buf = reinterpret_cast<float*>(ws + L.m);
+  b.o_op = reinterpret_cast<float*>(ws + L.oop);
+  b.h_op = reinterpret_cast<float*>(ws + L.hop);
+  b.m_op = reinterpret_cast<float*>(ws + L.mop);
+  b.rope_cos = reinterpret_cast<const float*>(ws + L.cos);
+  b.rope_sin = reinterpret_cast<const float*>(ws + L.sin);
+  b.rope_row0 = 0;
+}
+
+// The per-call launch parameters from the shape's base parameters (validated arguments).
+moel_status fill_call(const moel_config* cfg, const LayerParams& base, int l2_coherent, const moel_weights* w,
+                      void* k_cache, void* v_cache, const float* x, int32_t T, int32_t pos, int32_t window,
+                      const int32_t* parents, float* y, const moel_debug* dbg, LayerParams& p) {
+  moel_status st = moel_validate_call(cfg, w, k_cache, v_cache, x, T, pos, window, y);
   if (st != MOEL_OK) return st;
   st = moel_validate_tree(parents, T);
   if (st != MOEL_OK) return st;
-  p = plan->base;
-  p.l2_coherent = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
+  p = base;
+  p.l2_coherent = l2_coherent;
   p.T = T;
   p.pos = pos;
   p.window = window;
   const int lo = window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
   const int nkeys = pos + T - lo;
-  int maxc = plan->nwg / plan->cfg.n_kv_heads;
+  int maxc = base.nwg / cfg->n_kv_heads;
   if (maxc < 1) maxc = 1;
   int nch = (nkeys + 127) / 128;  // chunks of >= 128 keys, at most nwg / Hkv of them
   if (nch > maxc) nch = maxc;
@@ -408,6 +548,22 @@ moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, 
   return MOEL_OK;
 }
 
+// the expert phases split their tile cost C (< tiles per expert * 17 * slots) over the
+// workgroups in 32-bit arithmetic: C * workgroups must stay below 2^31
+bool work_split_fits(const moel_config* cfg, int nwg) {
+  const int64_t rows = std::max(cfg->inter, cfg->pooled) / cfg->n_shards;
+  const int64_t tpe = rows / (cfg->expert_dtype == MOEL_EXPERT_NVFP4 ? 64 : 16);
+  return tpe * 17 * MOEL_MAX_TOKENS * cfg->top_k * nwg < ((int64_t)1 << 31);
+}
+
+moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
+                         const float* x, int32_t T, int32_t pos, int32_t window, const int32_t* parents,
+                         float* y, const moel_debug* dbg, LayerParams& p) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  const int l2c = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
+  return fill_call(&plan->cfg, plan->base, l2c, w, k_cache, v_cache, x, T, pos, window, parents, y, dbg, p);
+}
+
 }  // namespace
 
 extern "C" {
@@ -425,49 +581,18 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   if (!hip_ok(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev))) return MOEL_ERR_HIP;
   if (!coop) return MOEL_ERR_UNSUPPORTED;
 
-  {
-    // the expert phases split their tile cost C (< tiles per expert * 17 * slots) over the
-    // workgroups in 32-bit arithmetic: C * workgroups must stay below 2^31
-    const int64_t rows = std::max(cfg->inter, cfg->pooled) / cfg->n_shards;
-    const int64_t tpe = rows / (cfg->expert_dtype == MOEL_EXPERT_NVFP4 ? 64 : 16);
-    if (tpe * 17 * MOEL_MAX_TOKENS * cfg->top_k * prop.multiProcessorCount >= ((int64_t)1 << 31))
-      return MOEL_ERR_SHAPE;
-  }
+  if (!work_split_fits(cfg, prop.multiProcessorCount)) return MOEL_ERR_SHAPE;
   moel_plan* plan = new (std::nothrow) moel_plan();
   if (plan == nullptr) return MOEL_ERR_HIP;
   plan->cfg = *cfg;
   plan->device = dev;
   plan->nwg = prop.multiProcessorCount;
   plan->grp = cfg->n_q_heads / cfg->n_kv_heads;
-  const int nwg = plan->nwg, D = cfg->head_dim, Hq = cfg->n_q_heads, H = cfg->hidden;
-  const int P = cfg->pooled, I = cfg->inter, E = cfg->n_experts, k = cfg->top_k;
+  const int nwg = plan->nwg, D = cfg->head_dim;
 
-  // workspace layout
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    const size_t o = off;
-    off = align256(off + bytes);
-    return o;
-  };
-  const size_t o_ctrl = take((size_t)kCtrlWords * 4);
-  const size_t o_q = take((size_t)kMaxT * Hq * D * 4);
-  const size_t o_ao = take((size_t)nwg * plan->grp * kMaxT * D * 4);
-  const size_t o_aml = take((size_t)nwg * plan->grp * kMaxT * 2 * 4);
-  const size_t o_o = take((size_t)kMaxT * Hq * D * 4);
-  const size_t o_h = take((size_t)kMaxT * H * 4);
-  const size_t o_lg = take((size_t)kMaxT * E * 4);
-  const size_t o_pl = take((size_t)kMaxT * P * 4);
-  const size_t o_a = take((size_t)kMaxT * k * I * 4);
-  const size_t o_d = take((size_t)kMaxT * k * P * 4);
-  const size_t o_pls = take((size_t)kMaxT * P * 4);
-  const size_t o_as = take((size_t)kMaxT * k * I * 4);
-  const size_t o_aq = take((size_t)kMaxT * k * I * 4);
-  const size_t o_m = take((size_t)kMaxT * P * 4);
-  const size_t o_oop = take((size_t)kMaxT * Hq * D * 4);
-  const size_t o_hop = take((size_t)kMaxT * H * 4);
-  const size_t o_mop = take((size_t)kMaxT * P * 4);
-  const size_t o_cos = take((size_t)cfg->kv_capacity * (D / 2) * 4);
-  const size_t o_sin = take((size_t)cfg->kv_capacity * (D / 2) * 4);
+  // workspace: activation scratch, barrier words and the whole RoPE table of the cache
+  const WsLayout L = ws_layout(cfg, nwg, cfg->kv_capacity);
+  const size_t off = L.total;
   plan->ws_bytes = off;
   if (!hip_ok(hipMalloc(&plan->ws, off))) {
     delete plan;
@@ -499,8 +624,8 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
         hs[(size_t)ps * (D / 2) + i] = (float)std::sin(a);
       }
     }
-    const bool ok = hip_ok(hipMemcpy(ws + o_cos, hc, n * 4, hipMemcpyHostToDevice)) &&
-                    hip_ok(hipMemcpy(ws + o_sin, hs, n * 4, hipMemcpyHostToDevice));
+    const bool ok = hip_ok(hipMemcpy(ws + L.cos, hc, n * 4, hipMemcpyHostToDevice)) &&
+                    hip_ok(hipMemcpy(ws + L.sin, hs, n * 4, hipMemcpyHostToDevice));
     std::free(hc);
     std::free(hs);
     if (!ok) {
@@ -509,47 +634,7 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
       return MOEL_ERR_HIP;
     }
   }
-  LayerParams& b = plan->base;
-  std::memset(&b, 0, sizeof(b));
-  b.H = H;
-  b.Hq = Hq;
-  b.Hkv = cfg->n_kv_heads;
-  b.D = D;
-  b.P = P;
-  b.I = I;
-  b.E = E;
-  b.topk = k;
-  b.n_shards = cfg->n_shards;
-  b.rank = cfg->shard_rank;
-  b.I_loc = I / cfg->n_shards;
-  b.P_loc = P / cfg->n_shards;
-  b.kv_cap = cfg->kv_capacity;
-  b.expert_dtype = cfg->expert_dtype;
-  b.down_fp4 = cfg->down_input == MOEL_DOWN_INPUT_NVFP4 ? 1 : 0;
-  b.eps = cfg->rms_eps;
-  b.nwg = nwg;
-  b.stride_gate = moel_packed_experts_bytes(cfg, 0) / (size_t)E;
-  b.stride_up = moel_packed_experts_bytes(cfg, 1) / (size_t)E;
-  b.stride_down = moel_packed_experts_bytes(cfg, 2) / (size_t)E;
-  b.ctrl = reinterpret_cast<unsigned*>(ws + o_ctrl);
-  b.q_buf = reinterpret_cast<float*>(ws + o_q);
-  b.attn_o = reinterpret_cast<float*>(ws + o_ao);
-  b.attn_ml = reinterpret_cast<float*>(ws + o_aml);
-  b.o_buf = reinterpret_cast<float*>(ws + o_o);
-  b.h_buf = reinterpret_cast<float*>(ws + o_h);
-  b.logits = reinterpret_cast<float*>(ws + o_lg);
-  b.pl = reinterpret_cast<float*>(ws + o_pl);
-  b.a_buf = reinterpret_cast<float*>(ws + o_a);
-  b.d_buf = reinterpret_cast<float*>(ws + o_d);
-  b.pl_split = reinterpret_cast<uint16_t*>(ws + o_pls);
-  b.a_split = reinterpret_cast<uint16_t*>(ws + o_as);
-  b.aq_buf = reinterpret_cast<float*>(ws + o_aq);
-  b.m_buf = reinterpret_cast<float*>(ws + o_m);
-  b.o_op = reinterpret_cast<float*>(ws + o_oop);
-  b.h_op = reinterpret_cast<float*>(ws + o_hop);
-  b.m_op = reinterpret_cast<float*>(ws + o_mop);
-  b.rope_cos = reinterpret_cast<const float*>(ws + o_cos);
-  b.rope_sin = reinterpret_cast<const float*>(ws + o_sin);
+  bind_base(plan->base, cfg, nwg, L, ws);
 
   // LDS budgets
   size_t mx = 0;
@@ -585,8 +670,8 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   plan->l2_coherent = l2_coherent_device(dev) ? 1 : 0;
   if (std::getenv("MOEL_LOG"))
     std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu l2_coherent=%d\n",
-                 H, Hq, cfg->n_kv_heads, D, P, I, E, k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx,
-                 plan->l2_coherent);
+                 cfg->hidden, cfg->n_q_heads, cfg->n_kv_heads, D, cfg->pooled, cfg->inter, cfg->n_experts,
+                 cfg->top_k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx, plan->l2_coherent);
   *out = plan;
   return MOEL_OK;
 }

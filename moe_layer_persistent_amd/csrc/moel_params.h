@@ -70,8 +70,9 @@ struct LayerParams {
   uint16_t* v_cache;
   const float* x;
   float* y;
-  const float* rope_cos;  // [kv_cap][D/2]
+  const float* rope_cos;  // [rows][D/2], row r holds position rope_row0 + r
   const float* rope_sin;
+  int rope_row0;
   // scratch (plan workspace)
   float* q_buf;     // [16][Hq*D]
   float* attn_o;    // [items][grp][16][D]
@@ -94,6 +95,9 @@ struct LayerParams {
   float* h_op;
   float* m_op;
   unsigned* ctrl;   // barrier counter, exit counter, status, abort
+  // when set, the last workgroup to leave the persistent launch moves the device status here
+  // (0 = ok) and clears it in the control block
+  unsigned* status_out;
   // debug (optional)
   int* dbg_idx;
   float* dbg_gates;

@@ -5,9 +5,9 @@
 // launch (phases separated by grid barriers) and the one-kernel-per-step chain.
 //
 // Precision: weights are bf16 or NVFP4 and the KV cache is bf16 (storage formats).  Every
-// activation is kept in fp32 and enters the bf16 MFMAs as a pair of bf16 values (the
-// nearest bf16 and the bf16 of the remainder, ~16 significant bits), so no activation is
-// rounded to bf16 on the way through the layer.
+// activation, the attention probabilities included, is kept in fp32 and enters the bf16 MFMAs
+// as a pair of bf16 values (the nearest bf16 and the bf16 of the remainder, ~16 significant
+// bits), so no activation is rounded to bf16 on the way through the layer.
 //
 // Packed weight layouts (produced by the pack kernels in moel_kernels.hip):
 //   dense bf16 [N, K]  : 16-row tiles; per tile K/32 steps of 1 KiB; in a step, lane l holds
@@ -385,8 +385,8 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
                   const int ps = p.pos + t;                  // cache slot
                   const int rp = p.pos + p.tok_depth[t];     // position (RoPE)
                   if (head < p.Hq + p.Hkv) {
-                    const float c = gl(p.rope_cos)[(size_t)rp * half + i];
-                    const float s = gl(p.rope_sin)[(size_t)rp * half + i];
+                    const float c = gl(p.rope_cos)[(size_t)(rp - p.rope_row0) * half + i];
+                    const float s = gl(p.rope_sin)[(size_t)(rp - p.rope_row0) * half + i];
                     const float ra = a * c - b * s, rb = b * c + a * s;
                     if (head < p.Hq) {
                       auto q = gl(p.q_buf + (size_t)t * p.Hq * p.D + head * p.D);
@@ -412,8 +412,9 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
 // one's K/V rows are already in flight into registers.  S^T = K Q^T on MFMA (keys as rows;
 // q as hi + lo, pre-multiplied by log2(e)/sqrt(D) so that scores come out in base-2 units),
 // softmax in fp32 with exp2, the exact max of each sub-chunk and an online rescale between
-// sub-chunks, O += P V on MFMA (P rounded to bf16, nearest even; V transposed in LDS).  The
-// partials' running maxima stay in base-2 units for the merge.
+// sub-chunks, O += P V on MFMA (P as a pair of bf16 values, hi + lo, like every other
+// activation; V transposed in LDS).  The partials' running maxima stay in base-2 units for the
+// merge.
 // ------------------------------------------------------------------------------------------
 template <int D>
 struct AttnLds {
@@ -573,8 +574,12 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
           for (int r = 0; r < 4; ++r) O[d][r] *= ao[r];
 #pragma unroll
         for (int kp = 0; kp < NKT / 2; ++kp) {
-          const u32x4 ph = {pack2bf(S[2 * kp][0], S[2 * kp][1]), pack2bf(S[2 * kp][2], S[2 * kp][3]),
-                            pack2bf(S[2 * kp + 1][0], S[2 * kp + 1][1]), pack2bf(S[2 * kp + 1][2], S[2 * kp + 1][3])};
+          // P as (hi, lo): the nearest bf16 and the bf16 of the remainder (~16 significant bits)
+          const u32x2 p0 = split_bf16(S[2 * kp][0], S[2 * kp][1]), p1 = split_bf16(S[2 * kp][2], S[2 * kp][3]);
+          const u32x2 p2 = split_bf16(S[2 * kp + 1][0], S[2 * kp + 1][1]);
+          const u32x2 p3 = split_bf16(S[2 * kp + 1][2], S[2 * kp + 1][3]);
+          const u32x4 ph = {p0[0], p1[0], p2[0], p3[0]};
+          const u32x4 pl = {p0[1], p1[1], p2[1], p3[1]};
 #pragma unroll
           for (int d = 0; d < ND; ++d) {
             // k slots of this lane: keys 32kp + 4gq + 0..3 and 32kp + 16 + 4gq + 0..3
@@ -583,6 +588,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
             const u32x2 v1 = *reinterpret_cast<const u32x2*>(&L.Vt[L_t::vt_index(dd, 32 * kp + 16 + 4 * gq)]);
             const u32x4 vb = {v0[0], v0[1], v1[0], v1[1]};
             O[d] = mfma16x16x32(ph, vb, O[d]);
+            O[d] = mfma16x16x32(pl, vb, O[d]);
           }
         }
       }

@@ -46,6 +46,14 @@ moel_status moel_validate_config(const moel_config* c) {
   if (c->inter % (row_unit * c->n_shards) != 0 || c->pooled % (row_unit * c->n_shards) != 0)
     return MOEL_ERR_SHAPE;
   if ((int64_t)c->kv_capacity * c->head_dim > ((int64_t)1 << 31) / c->n_kv_heads) return MOEL_ERR_SHAPE;
+  // the NVFP4 expert phases hand tiles out as (sequence << 16) | tile with 0xffff marking the
+  // end of the work: every tile number of a step (active experts x 64-row tiles per expert,
+  // at most min(E, 16 top_k) experts) and every sequence number must fit 15 bits
+  if (c->expert_dtype == MOEL_EXPERT_NVFP4) {
+    const int64_t rows = (c->inter > c->pooled ? c->inter : c->pooled) / c->n_shards;
+    const int64_t active = c->n_experts < MOEL_MAX_TOKENS * c->top_k ? c->n_experts : MOEL_MAX_TOKENS * c->top_k;
+    if ((rows / 64) * active >= 0x7fff) return MOEL_ERR_SHAPE;
+  }
   return MOEL_OK;
 }
 

@@ -62,6 +62,7 @@ class Workload:
     pos: int                 # tokens already in the KV cache
     T: int                   # verify tokens in this step
     n_layers: int = 1
+    shard_rank: int = 0          # which N slice of the experts this GPU holds (n_shards > 1)
     fp32_masters: bool = False   # tiny case: weights drawn fp32, device copy bf16
     down_input: int = DOWN_EXACT
     rms_eps: float = 1e-6

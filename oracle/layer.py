@@ -8,8 +8,9 @@ Takeaways"): one decoder layer of a mixture-of-experts model verifying T <= 16
 draft tokens of one request in a single pass.  The launch covers the QKV
 projection and the KV-cache write, attention (sliding window over the last
 2,048 tokens, or global), the dense GEMMs, routing of each token to 8 of 256
-experts, a pooler projection that shrinks each token vector before the experts,
-the expert GEMMs and an unpooler that restores the width afterwards.
+experts, a down-projection of every token to a narrower width ahead of the
+experts (the pooler), the expert GEMMs and a projection back to the model width
+after them (the unpooler).
 
 Where the pages are silent the plainest reading is taken (each one is listed
 with its rationale in the design notes):
@@ -254,7 +255,8 @@ def expert_out(pl_t: np.ndarray, Wg: np.ndarray, Wu: np.ndarray, Wd: np.ndarray,
 # --------------------------------------------------------------------------------------------
 def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, experts: ExpertFn,
                force_idx: Optional[np.ndarray] = None, moe_tokens=None,
-               parents=None, act_scales=None, force_down_input=None) -> Dict[str, np.ndarray]:
+               parents=None, act_scales=None, force_down_input=None,
+               force_kv=None) -> Dict[str, np.ndarray]:
     """One layer step.  `inp` holds fp64 arrays (bf16-valued weights):
     x [T,H], gamma1 [H], w_qkv [(Hq+2Hkv)D, H], w_o [H, Hq*D], gamma2 [H], w_router [E,H],
     w_pool [P,H], w_unpool [H,P], k_cache/v_cache [Hkv, C, D].
@@ -268,6 +270,11 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     force_down_input [T, k, inter] replaces the down projection's input of every slot, as
     force_idx replaces the routing (the caller checks that the replacement is a valid encoding
     of a, e.g. a device's encoding of its own SwiGLU output).
+    force_kv = (k_rows, v_rows), each [T, Hkv, D] of bf16 values, replaces the rows written to
+    the cache (the new keys after RoPE and the new values, rounded), as force_idx replaces the
+    routing: the caller checks that every value is a bf16 neighbour of the exact one (a device
+    may round a value that sits within its arithmetic error of a rounding boundary the other
+    way); everything after the write then reads those rows.
     Returns y, the written K/V rows, routing and every intermediate.
     """
     x = np.asarray(inp["x"], dtype=np.float64)
@@ -286,6 +293,9 @@ def layer_step(inp: Dict[str, np.ndarray], dims: Dims, pos: int, window: int, ex
     k_exact = rope(k, positions, dims.rope_theta)
     k_r = bf16_round(k_exact)
     v_r = bf16_round(v)
+    if force_kv is not None:
+        k_r = np.asarray(force_kv[0], dtype=np.float64).reshape(T, Hkv, D)
+        v_r = np.asarray(force_kv[1], dtype=np.float64).reshape(T, Hkv, D)
     k_cache = np.array(inp["k_cache"], dtype=np.float64, copy=True)
     v_cache = np.array(inp["v_cache"], dtype=np.float64, copy=True)
     for t in range(T):

@@ -156,3 +156,20 @@ def test_packed_sizes_equal_canonical_bytes():
 def test_status_strings():
     for code in range(0, -8, -1):
         assert binding.status_string(code) != "unknown status"
+
+
+def test_nvfp4_tile_numbers_must_fit_the_hand_out_words():
+    """The NVFP4 expert phases hand tiles out as (sequence << 16) | tile: shapes whose tile
+    numbers (64-row tiles per expert x active experts) would not fit 15 bits are rejected."""
+    L = binding.lib()
+    # 65536 intermediate rows = 1024 tiles per expert, 64 experts active: 65536 tiles
+    c = _cfg(inter=65536, n_experts=64, top_k=4)
+    assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_ERR_SHAPE
+    # the same shape split over 8 GPUs fits (128 tiles per expert)
+    c = _cfg(inter=65536, n_experts=64, top_k=4, n_shards=8)
+    assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK
+    # bf16 experts hand out plain tile numbers
+    c = _cfg(inter=65536, n_experts=64, top_k=4, expert_dtype=binding.MOEL_EXPERT_BF16)
+    assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK
+    # the full-width layer: 64 tiles per expert, at most 128 experts active
+    assert L.moel_validate_config(ctypes.byref(_cfg())) == binding.MOEL_OK

@@ -55,6 +55,11 @@ SMALL = [
     dict(T=8, pos=50, window=0, top_k=1),
     dict(T=16, pos=64, window=0, n_experts=512, top_k=8, pooled=256, inter=256),
     dict(T=3, pos=5, window=0, hidden=256, n_q_heads=2, n_kv_heads=1, pooled=128, inter=128),
+    # one GPU's share of N-sharded experts at other ranks than 0 (output slices placed at the
+    # rank's offset in the SwiGLU output, the expert outputs and the combine)
+    dict(T=16, pos=100, window=32, n_experts=32, top_k=8, n_shards=8, shard_rank=7, inter=512, pooled=512),
+    dict(T=11, pos=60, window=0, n_experts=32, top_k=8, n_shards=8, shard_rank=1, inter=512, pooled=512,
+         down_input=synth.DOWN_NVFP4),
 ]
 
 
@@ -219,15 +224,19 @@ def test_abort_leaves_buffers_untouched():
     run = harness.GpuRun(w)
     kc, vc = run.fresh_caches()
     y = torch.full((w.T, w.hidden), 7.0, dtype=torch.float32, device="cuda")
+    dbg = {"expert_idx": torch.full((w.T, w.top_k), 7, dtype=torch.int32, device="cuda"),
+           "timestamps": torch.full((run.plan.workgroups, binding.MOEL_N_STAMPS), 7, dtype=torch.int64,
+                                    device="cuda")}
     for fused in (True, False):
         run.plan.set_abort(True)
-        run.plan.layer_decode(run.lw, kc, vc, run.t["x"], w.pos, 0, y, fused=fused)
+        run.plan.layer_decode(run.lw, kc, vc, run.t["x"], w.pos, 0, y, dbg=dbg, fused=fused)
         torch.cuda.synchronize()
         assert run.plan.status() == binding.MOEL_ERR_ABORTED
         run.plan.set_abort(False)
         torch.cuda.synchronize()
         assert torch.all(y == 7.0)
         assert torch.equal(kc.view(torch.int16), run.k0.view(torch.int16))
+        assert torch.all(dbg["expert_idx"] == 7) and torch.all(dbg["timestamps"] == 7)
     assert run.plan.status() == binding.MOEL_OK
 
 
@@ -257,16 +266,54 @@ def test_full_width_matches_oracle(name):
     _log(f"full {name}: running")
     out = run.run(fused=True)
     rep = {}
-    harness.check_against_oracle(run, out, moe_tokens=[0, 7, 15], report=rep)
+    _log(f"full {name}: oracle")
+    harness.check_against_oracle(run, out, report=rep)
     _log(f"full {name}: {rep}")
 
 
-@pytest.mark.parametrize("layer", [0, 1])
-def test_stack_share_layer_matches_oracle(layer):
-    w = synth.WORKLOADS["stack_tp8"]
-    _log(f"stack layer {layer}: generating")
+@pytest.mark.parametrize("layer,rank", [(0, 0), (1, 0), (2, 7)], ids=["global_r0", "swa_r0", "swa_r7"])
+def test_stack_share_layer_matches_oracle(layer, rank):
+    w = synth.WORKLOADS["stack_tp8"].with_(shard_rank=rank)
+    _log(f"stack layer {layer} rank {rank}: generating")
     run = harness.GpuRun(w, layer=layer)
     out = run.run(fused=True)
     rep = {}
-    harness.check_against_oracle(run, out, moe_tokens=[0, 15], report=rep)
-    _log(f"stack layer {layer}: {rep}")
+    harness.check_against_oracle(run, out, report=rep)
+    _log(f"stack layer {layer} rank {rank}: {rep}")
+
+
+@pytest.mark.parametrize("down", [synth.DOWN_EXACT, synth.DOWN_NVFP4], ids=["exact", "fp4_gather"])
+def test_expert_n_shards_equal_full_width_rows(down):
+    """N-sharding the expert GEMMs splits no K reduction (orcarouter.ai English post, "Where the
+    kernel boundary sits": the sharded MoE GEMMs can be made bitwise identical to expert
+    parallelism): with the same weights, one GPU's share of the SwiGLU output (its gate/up rows,
+    and with the fp4 gather their encoding) is bitwise equal to the same rows of the full-width
+    layer, at every rank."""
+    full = synth.small_workload(T=16, pos=200, window=64, n_experts=32, top_k=8, pooled=512, inter=1024,
+                                down_input=down)
+    run_f = harness.GpuRun(full)
+    out_f = run_f.run(fused=True)
+    k, I = full.top_k, full.inter
+    a_f = run_f.plan.scratch("a").view(16 * k, I).clone()
+    aq_f = run_f.plan.scratch("aq").view(16 * k, I).clone() if down else None
+    S = 8
+    il, plc = full.inter // S, full.pooled // S
+    for rank in (0, 3, 7):
+        sh = full.with_(n_shards=S, shard_rank=rank)
+        t = dict(run_f.t)
+        for m in ("gate", "up"):
+            for part in ("_codes", "_scales"):
+                t[m + part] = run_f.t[m + part][:, rank * il:(rank + 1) * il].contiguous()
+        for part in ("_codes", "_scales"):
+            t["down" + part] = run_f.t["down" + part][:, rank * plc:(rank + 1) * plc].contiguous()
+        run_s = harness.GpuRun(sh, tensors=t)
+        out_s = run_s.run(fused=True)
+        assert torch.equal(out_s["expert_idx"], out_f["expert_idx"])
+        cols = slice(rank * il, (rank + 1) * il)
+        a_s = run_s.plan.scratch("a").view(16 * k, I)
+        assert _same_bytes(a_s[:, cols], a_f[:, cols]), rank
+        if down:
+            aq_s = run_s.plan.scratch("aq").view(16 * k, I)
+            assert _same_bytes(aq_s[:, cols], aq_f[:, cols]), rank
+        run_s.plan.close()
+        _log(f"n-shard rank {rank}: gate/up rows bitwise equal to the full-width layer's")
