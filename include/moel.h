@@ -280,6 +280,38 @@ moel_status moel_layer_decode_tree_unfused(moel_plan* plan, const moel_weights* 
                                            int32_t window, const int32_t* parents, float* y,
                                            const moel_debug* dbg, void* stream);
 
+/* --- allocation-free step -------------------------------------------------------- */
+
+/* Bytes of device memory the allocation-free step uses on each GPU it runs on (held until the
+ * process ends). */
+#define MOEL_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): moel_layer_decode without a plan.  Nothing is
+ * allocated, by this call or by the library on its behalf.  The step's workspace (control
+ * words, activation scratch, the RoPE rows of positions pos .. pos+T-1) lives in a device array
+ * of MOEL_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU; the size a shape needs is
+ *   ~ 4 KiB + 4 B * (16 * (3 Hq D + 2 H + E + 4 P + 3 k I + k P + D) + CUs * (Hq/Hkv) * 16 * (D + 2))
+ * (about 28 MiB for H 8192, 64/8 heads of 128, P = I = 4096, E 256, k 8 on 256 compute units),
+ * and a shape that needs more is rejected with MOEL_ERR_SHAPE before anything is launched.
+ * The first call on a device sets that device up (synchronously, on `stream`): it looks the
+ * array up, runs the L2 coherence check on it (unless a plan already did on that device) and
+ * clears its control words.
+ *   cfg: the layer's shape, as for moel_plan_create (any config it accepts within the size).
+ *   w, k_cache, v_cache, x, T, pos, window, y: as for moel_layer_decode (the chain verify).
+ *   status: optional caller-owned DEVICE word (4-byte aligned; NULL = not reported) that the
+ *     launch sets to 0 or, after a device-side wait timed out or a consistency check failed, to
+ *     a nonzero code.  No abort word exists for this call.
+ * Results are those of moel_layer_decode (same kernels; RoPE rows computed on the device in
+ * double precision, as the plan computes its table on the host).  All calls on one GPU share
+ * its array and each call leaves its contents behind: calls that overlap on one GPU (on
+ * different streams) race and must not be issued; calls in one stream are ordered.  Errors:
+ * as moel_layer_decode, plus MOEL_ERR_SHAPE for a workspace beyond the array and
+ * MOEL_ERR_ALIGN for a misaligned status word. */
+moel_status moel_layer_decode_noalloc(const moel_config* cfg, const moel_weights* w, void* k_cache,
+                                      void* v_cache, const float* x, int32_t T, int32_t pos,
+                                      int32_t window, float* y, uint32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,7 @@ def lib() -> ctypes.CDLL:
             "moel_layer_decode_tree_unfused": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, P(Debug),
                                                      vp]),
             "moel_validate_tree": (i32, [vp, i32]),
+            "moel_layer_decode_noalloc": (i32, [P(Config), P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, vp]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -269,3 +270,14 @@ class Plan:
                                       T, pos, window, ctypes.cast(par, ctypes.c_void_p), _ptr(y), dp,
                                       _stream(stream))
         _check(rc, name)
+
+
+def layer_decode_noalloc(cfg: Config, lw: LayerWeights, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                         x: torch.Tensor, pos: int, window: int, y: torch.Tensor,
+                         status: Optional[torch.Tensor] = None, stream=None, T: Optional[int] = None) -> None:
+    """moel_layer_decode_noalloc: one verify step without a plan (the library's static scratch);
+    `status` is an optional int32 device tensor of one element that receives the device status."""
+    T = x.shape[0] if T is None else T
+    rc = lib().moel_layer_decode_noalloc(ctypes.byref(cfg), ctypes.byref(lw.struct), _ptr(k_cache), _ptr(v_cache),
+                                         _ptr(x), T, pos, window, _ptr(y), _ptr(status), _stream(stream))
+    _check(rc, "moel_layer_decode_noalloc")

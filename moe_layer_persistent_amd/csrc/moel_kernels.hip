@@ -548,6 +548,70 @@ moel_status fill_call(const moel_config* cfg, const LayerParams& base, int l2_co
   return MOEL_OK;
 }
 
+// ------------------------------------------------------------------------------------------
+// Scratch of the allocation-free entry point (moel_layer_decode_noalloc): the workspace of one
+// call -- control words, activation scratch, the call's RoPE rows -- in a file-scope device
+// array, one copy per device for the life of the process.  Host code never uses the array's
+// name as an address: the device address comes from hipGetSymbolAddress, once per device.
+// ------------------------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = (size_t)MOEL_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+constexpr size_t kCohOffset = 64 * 1024;  // coherence check memory, behind the control words
+static_assert(kCohOffset + kCohMemWords * 4 <= kStaticScratchBytes, "coherence check memory");
+
+struct StaticDev {
+  int state;        // 0 not set up, 1 ready, < 0 the moel_status of a failed set-up
+  char* ptr;        // this device's address of `scratch`
+  int nwg;          // workgroups of the persistent launch (compute units)
+  int l2_coherent;  // coherence check result
+};
+StaticDev g_static[64];
+std::mutex g_static_mu;
+
+// Once per device, with the device current: the scratch address, the launch attributes, the
+// coherence check (run on the scratch itself when no plan ran it before) and zeroed control
+// words.  Synchronous on `s`; allocates nothing.
+moel_status static_setup(int dev, hipStream_t s, StaticDev** out) {
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (dev < 0 || dev >= 64) return MOEL_ERR_UNSUPPORTED;
+  StaticDev& sd = g_static[dev];
+  if (sd.state < 0) return static_cast<moel_status>(sd.state);
+  if (sd.state == 1) {
+    *out = &sd;
+    return MOEL_OK;
+  }
+  hipDeviceProp_t prop;
+  if (!hip_ok(hipGetDeviceProperties(&prop, dev))) return MOEL_ERR_HIP;
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    sd.state = MOEL_ERR_UNSUPPORTED;
+    return MOEL_ERR_UNSUPPORTED;
+  }
+  void* ptr = nullptr;
+  if (!hip_ok(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch))) || ptr == nullptr) return MOEL_ERR_HIP;
+  int per_cu64 = 0, per_cu128 = 0;
+  const bool attrs =
+      hip_ok(hipFuncSetAttribute(fused_fn<64>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_fused_bytes(64))) &&
+      hip_ok(hipFuncSetAttribute(fused_fn<128>(), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_fused_bytes(128))) &&
+      hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu64, fused_fn<64>(), kThreads, lds_fused_bytes(64))) &&
+      hip_ok(hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu128, fused_fn<128>(), kThreads, lds_fused_bytes(128)));
+  if (!attrs) return MOEL_ERR_HIP;
+  if (per_cu64 < 1 || per_cu128 < 1) {
+    sd.state = MOEL_ERR_UNSUPPORTED;
+    return MOEL_ERR_UNSUPPORTED;
+  }
+  char* base = static_cast<char*>(ptr);
+  const bool coh = l2_coherent_device(dev, reinterpret_cast<unsigned*>(base + kCohOffset), s);
+  hipLaunchKernelGGL(k_fill_u32, dim3((kCtrlWords + 255) / 256), dim3(256), 0, s, reinterpret_cast<unsigned*>(base), 0u,
+                     (size_t)kCtrlWords);
+  if (!hip_ok(hipGetLastError()) || !hip_ok(hipStreamSynchronize(s))) return MOEL_ERR_HIP;
+  sd.ptr = base;
+  sd.nwg = prop.multiProcessorCount;
+  sd.l2_coherent = coh ? 1 : 0;
+  sd.state = 1;
+  *out = &sd;
+  return MOEL_OK;
+}
+
 // the expert phases split their tile cost C (< tiles per expert * 17 * slots) over the
 // workgroups in 32-bit arithmetic: C * workgroups must stay below 2^31
 bool work_split_fits(const moel_config* cfg, int nwg) {
@@ -825,6 +889,48 @@ moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, vo
                                       const moel_debug* dbg, void* stream) {
   return moel_layer_decode_tree_unfused(plan, w, k_cache, v_cache, x, T, pos, window, nullptr, y, dbg,
                                         stream);
+}
+
+moel_status moel_layer_decode_noalloc(const moel_config* cfg, const moel_weights* w, void* k_cache,
+                                      void* v_cache, const float* x, int32_t T, int32_t pos, int32_t window,
+                                      float* y, uint32_t* status, void* stream) {
+  moel_status st = moel_validate_call(cfg, w, k_cache, v_cache, x, T, pos, window, y);
+  if (st != MOEL_OK) return st;
+  if (reinterpret_cast<uintptr_t>(status) & 3u) return MOEL_ERR_ALIGN;
+  int dev = 0;
+  if (!hip_ok(hipGetDevice(&dev))) return MOEL_ERR_UNSUPPORTED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  StaticDev* sd = nullptr;
+  st = static_setup(dev, s, &sd);
+  if (st != MOEL_OK) return st;
+  if (!work_split_fits(cfg, sd->nwg)) return MOEL_ERR_SHAPE;
+  // the call's workspace, with RoPE rows for the call's positions only
+  const WsLayout L = ws_layout(cfg, sd->nwg, kMaxT);
+  if (L.total > kStaticScratchBytes) {
+    if (std::getenv("MOEL_LOG"))
+      std::fprintf(stderr, "moel: noalloc workspace of %zu bytes exceeds the %zu-byte scratch\n", L.total,
+                   kStaticScratchBytes);
+    return MOEL_ERR_SHAPE;
+  }
+  LayerParams base;
+  bind_base(base, cfg, sd->nwg, L, sd->ptr);
+  LayerParams p;
+  st = fill_call(cfg, base, sd->l2_coherent, w, k_cache, v_cache, x, T, pos, window, nullptr, y, nullptr, p);
+  if (st != MOEL_OK) return st;
+  p.rope_row0 = pos;  // rows pos .. pos + T - 1 (the chain's positions)
+  p.status_out = status;
+  RopeFreq fq;
+  const int half = cfg->head_dim / 2;
+  for (int i = 0; i < half; ++i) fq.f[i] = std::pow((double)cfg->rope_theta, -(2.0 * i) / (double)cfg->head_dim);
+  hipLaunchKernelGGL(k_rope_rows, dim3((T * half + 255) / 256), dim3(256), 0, s,
+                     reinterpret_cast<float*>(sd->ptr + L.cos), reinterpret_cast<float*>(sd->ptr + L.sin), pos, T,
+                     half, fq);
+  if (!hip_ok(hipGetLastError())) return MOEL_ERR_HIP;
+  void* args[] = {&p};
+  const int D = cfg->head_dim;
+  const hipError_t e = hipLaunchKernel(D == 64 ? fused_fn<64>() : fused_fn<128>(), dim3(sd->nwg), dim3(kThreads),
+                                       args, (unsigned)lds_fused_bytes(D), s);
+  return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
 }
 
 }  // extern "C"
