@@ -1,12 +1,19 @@
 """Benchmark of one MoE decoder layer's batch-1 verify step (T = 16) on one MI355X.
 
-python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload swa_fp4] [--routing iid|shared]
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload swa_fp4] [--routing iid|shared|pages]
 
 A step is one persistent launch of the whole layer over one batch of 16 synthetic verify
 tokens.  Inputs are resident in HBM before timing starts.  To keep the 256 MB Infinity
 Cache from serving weights across steps, consecutive steps alternate between two packed
 copies of the layer's weights (so each step's weights were last touched two steps ago and
 >7 GB have streamed in between).  Prints one JSON line.
+
+Beside the headline workload (`value`, `roofline`), the line carries every other layer
+configuration timed the same way, each with its own algorithmic bytes and fraction of the
+HBM peak (`configs`), the 62-layer stack share (`stack`, fused and one kernel per step),
+the headline layer with the pages' routing concentration (`routing_pages`, about 49 distinct
+experts), and the CPU oracle timed on
+a bounded sample of the headline step (`cpu_baseline`).
 """
 from __future__ import annotations
 
@@ -18,6 +25,11 @@ import sys
 import time
 
 PEAK_HBM_GBPS = 8000.0
+ACCEPTED_PER_STEP = 6.6  # tokens accepted per verify step of 16 (the pages' acceptance length)
+# a 16-node token tree: node t's parent (-1: root)
+TREE16 = [-1, 0, 1, 2, 0, 4, 5, 1, 7, 3, 9, 4, 11, 12, 2, 14]
+PHASES = ["norm1", "qkv_rope_kv", "attention", "attn_merge", "o_proj", "router_pool", "experts_gate_up",
+          "experts_down", "combine", "unpool"]
 
 
 def algorithmic_bytes(w, idx, pos, window, T):
@@ -49,10 +61,6 @@ def kernel_source_digest() -> str:
     return h.hexdigest()
 
 
-# a 16-node token tree: node t's parent (-1: root)
-TREE16 = [-1, 0, 1, 2, 0, 4, 5, 1, 7, 3, 9, 4, 11, 12, 2, 14]
-
-
 def measured_traffic(workload: str):
     """HBM bytes per launch of the fused kernel from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by the same counters on a copy of known size), or None
@@ -72,16 +80,29 @@ def measured_traffic(workload: str):
     return {"bytes_per_launch": float(kv["traffic_bytes_per_launch"]), "source": os.path.relpath(path)}
 
 
-def cpu_baseline(w, t, idx, window, budget_s=25.0):
-    """The oracle, timed on this host's cores on a bounded sample of the same step: the
-    whole attention block and routing for all 16 tokens, plus the expert block for as many
-    tokens as fit the budget; scaled to one full layer by the distinct experts used."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, t, idx, window, repeats=3):
+    """The oracle, timed on this host's cores on a bounded sample of the same step: the whole
+    attention block and routing for all 16 tokens, plus the expert block of token 0 (its
+    experts dequantised and applied), scaled to one full layer by the distinct experts of the
+    step.  Median of `repeats` runs with every core available to the BLAS, and again with one
+    thread."""
     import numpy as np
-    import torch
+    from threadpoolctl import threadpool_limits
     from oracle import layer as olayer
 
     dims = olayer.Dims(w.hidden, w.n_q_heads, w.n_kv_heads, w.head_dim, w.pooled, w.inter,
-                       w.n_experts, w.top_k, w.n_shards, 0, w.rms_eps, w.rope_theta)
+                       w.n_experts, w.top_k, w.n_shards, w.shard_rank, w.rms_eps, w.rope_theta)
     f64 = lambda x: x.detach().to("cpu").double().numpy()
     inp = {k: f64(t[k]) for k in ("x", "gamma1", "gamma2", "w_qkv", "w_o", "w_router", "w_pool", "w_unpool",
                                   "k_cache", "v_cache")}
@@ -92,37 +113,211 @@ def cpu_baseline(w, t, idx, window, budget_s=25.0):
     else:
         ex = olayer.bf16_experts(lambda e: {m: f64(t[m][e]) for m in ("gate", "up", "down")})
     gi = idx.astype(np.int64)
-    t0 = time.perf_counter()
-    olayer.layer_step(inp, dims, w.pos, window, ex, force_idx=gi, moe_tokens=[])
-    t_attn = time.perf_counter() - t0
-    toks, used = [], set()
-    t_moe = 0.0
-    for tok in range(w.T):
-        t1 = time.perf_counter()
-        olayer.layer_step(inp, dims, w.pos, window, ex, force_idx=gi, moe_tokens=[tok])
-        dt = time.perf_counter() - t1 - t_attn
-        t_moe += max(dt, 0.0)
-        toks.append(tok)
-        used |= set(int(e) for e in gi[tok])
-        if t_attn + t_moe > budget_s:
-            break
     U = len(set(int(e) for e in gi.reshape(-1)))
-    per_expert = t_moe / max(len(used), 1)
-    est = t_attn + per_expert * U
+    n0 = len(set(int(e) for e in gi[0]))
+
+    def one():
+        t0 = time.perf_counter()
+        olayer.layer_step(inp, dims, w.pos, window, ex, force_idx=gi, moe_tokens=[])
+        t_attn = time.perf_counter() - t0
+        t1 = time.perf_counter()
+        olayer.layer_step(inp, dims, w.pos, window, ex, force_idx=gi, moe_tokens=[0])
+        t_moe = max(time.perf_counter() - t1 - t_attn, 0.0)
+        return t_attn + t_moe / n0 * U, t_attn, t_moe
+
     threads = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
-    return {"value": est * 1e6, "unit": "us/layer", "cores": threads, "kind": "oracle",
-            "sample": f"attention+routing for all {w.T} tokens ({t_attn:.2f}s) + expert block for tokens "
-                      f"{toks[0]}..{toks[-1]} ({len(used)} distinct experts, {t_moe:.2f}s), scaled to the "
-                      f"{U} distinct experts of the step; fp64 NumPy"}
+    with threadpool_limits(threads):
+        all_runs = [one() for _ in range(repeats)]
+    with threadpool_limits(1):
+        one_runs = [one() for _ in range(repeats)]
+    med = lambda runs: statistics.median(r[0] for r in runs)
+    return {"value": round(med(all_runs) * 1e6, 1), "unit": "us/layer", "cores": threads, "kind": "oracle",
+            "value_1_thread": round(med(one_runs) * 1e6, 1),
+            "cpu_model": cpu_model(), "repeats": repeats,
+            "sample": f"fp64 NumPy oracle of the {w.name} step: attention block and routing for all {w.T} tokens "
+                      f"({statistics.median(r[1] for r in all_runs):.2f}s) + the expert block of token 0 "
+                      f"({n0} experts, {statistics.median(r[2] for r in all_runs):.2f}s), scaled to the {U} distinct "
+                      f"experts of the step; median of {repeats} runs with {threads} BLAS threads (value) and with 1 "
+                      f"thread (value_1_thread)"}
 
 
-ACCEPTED_PER_STEP = 6.6  # tokens accepted per verify step of 16 (the pages' acceptance length)
+class LayerBench:
+    """One layer workload on the GPU: inputs, two packed weight copies, a plan; times launches."""
+
+    def __init__(self, w, routing="iid", layer=0, copies=2):
+        import torch
+        from moe_layer_persistent_amd import binding, synth
+        self.torch, self.binding, self.synth = torch, binding, synth
+        self.w = w
+        self.window = w.layer_window(layer)
+        self.dev = torch.device("cuda")
+        self.t = synth.make_layer(w, layer, self.dev, routing=routing)
+        self.plan = binding.Plan(binding.config_from_workload(w))
+        self.extra_plans = []
+        self.copies = [self.plan.pack_layer(self.t) for _ in range(copies)]
+        self.x = self.t["x"].contiguous()
+        self.kc = self.t["k_cache"].clone()
+        self.vc = self.t["v_cache"].clone()
+        self.y = torch.empty((w.T, w.hidden), dtype=torch.float32, device=self.dev)
+        self.stream = torch.cuda.current_stream()
+
+    def settle(self, seconds=0.3):
+        """Untimed launches for a fixed time before the first measurement, so that the device's
+        clocks and power state have settled (the first launches on a fresh box run slower)."""
+        torch = self.torch
+        t0 = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(8):
+                self.plan.layer_decode(self.copies[i % len(self.copies)], self.kc, self.vc, self.x, self.w.pos,
+                                       self.window, self.y, stream=self.stream)
+                i += 1
+            torch.cuda.synchronize()
+
+    def route(self, x=None):
+        """Runs one step with debug outputs; returns the selected experts [T, k]."""
+        torch = self.torch
+        idx = torch.zeros((self.w.T, self.w.top_k), dtype=torch.int32, device=self.dev)
+        self.plan.layer_decode(self.copies[0], self.kc, self.vc, self.x if x is None else x, self.w.pos,
+                               self.window, self.y, dbg={"expert_idx": idx}, stream=self.stream)
+        torch.cuda.synchronize()
+        st = self.plan.status()
+        assert st == 0, self.binding.status_string(st)
+        return idx.cpu().numpy()
+
+    def timed(self, steps, warmup, fused=True, parents=None, pl=None, cps=None, x=None):
+        """Back-to-back launches between two events on the launch stream: the average launch
+        duration (us) over the timed region, and the host wall time (s)."""
+        torch = self.torch
+        pl = self.plan if pl is None else pl
+        cps = self.copies if cps is None else cps
+        x = self.x if x is None else x
+        w = self.w
+        for i in range(warmup):
+            pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, w.pos, self.window, self.y, fused=fused,
+                            stream=self.stream, parents=parents)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        a.record(self.stream)
+        for i in range(steps):
+            pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, w.pos, self.window, self.y, fused=fused,
+                            stream=self.stream, parents=parents)
+        b.record(self.stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        st = pl.status()
+        assert st == 0, self.binding.status_string(st)
+        return a.elapsed_time(b) * 1e3 / steps, wall
+
+    def per_launch(self, steps):
+        """Event pairs around single launches (spread of launch times; includes dispatch gaps)."""
+        torch = self.torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record(self.stream)
+            self.plan.layer_decode(self.copies[i % 2], self.kc, self.vc, self.x, self.w.pos, self.window, self.y,
+                                   stream=self.stream)
+            evs[i][1].record(self.stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
+
+    def phases(self, dump=None, idx=None):
+        """Per-phase timeline of one fused launch (workgroup timestamps, 100 MHz clock): slot i is
+        the end of step i, slot 16 + i its start (after the preceding grid barrier)."""
+        import numpy as np
+        torch = self.torch
+        ts = torch.zeros((self.plan.workgroups, self.binding.MOEL_N_STAMPS), dtype=torch.int64, device=self.dev)
+        self.plan.layer_decode(self.copies[0], self.kc, self.vc, self.x, self.w.pos, self.window, self.y,
+                               dbg={"timestamps": ts}, stream=self.stream)
+        torch.cuda.synchronize()
+        tsn = ts.cpu().numpy().astype(np.float64)
+        if dump:
+            np.save(dump + "_fused.npy", ts.cpu().numpy())
+            ts.zero_()
+            self.plan.layer_decode(self.copies[1], self.kc, self.vc, self.x, self.w.pos, self.window, self.y,
+                                   dbg={"timestamps": ts}, fused=False, stream=self.stream)
+            torch.cuda.synchronize()
+            np.save(dump + "_unfused.npy", ts.cpu().numpy())
+            if idx is not None:
+                np.save(dump + "_idx.npy", idx)
+        t0 = tsn[:, 10].min()
+        ends = [(tsn[:, i].max() - t0) / 100.0 for i in range(10)]
+        work = (tsn[:, :10] - tsn[:, 16:26]) / 100.0
+        return {
+            "phase_end_us": {n: round(e, 1) for n, e in zip(PHASES, ends)},
+            "phase_us": {n: round(e - (ends[i - 1] if i else 0.0), 1) for i, (n, e) in enumerate(zip(PHASES, ends))},
+            "phase_work_us": {n: {"median": round(float(np.median(work[:, i])), 1), "max": round(float(work[:, i].max()), 1)}
+                              for i, n in enumerate(PHASES)},
+            # grid barrier before step i: last arrival -> first / last departure
+            "barrier_us": {PHASES[i]: {"first_out": round((tsn[:, 16 + i].min() - tsn[:, i - 1].max()) / 100.0, 2),
+                                       "last_out": round((tsn[:, 16 + i].max() - tsn[:, i - 1].max()) / 100.0, 2)}
+                           for i in range(1, 10)},
+        }
+
+    def close(self):
+        for p in [self.plan] + self.extra_plans:
+            p.close()
+        self.copies = []
+        self.t = None
+        self.torch.cuda.synchronize()
+        self.torch.cuda.empty_cache()
+
+
+def stamp_table(tsn, fused=True):
+    """Phase timeline from workgroup timestamps [nwg, 32] (100 MHz): slot i the end of step i,
+    slot 16 + i its start.  Fused: each phase's time runs from the previous phase's last end (the
+    grid barrier included) to its own last end.  One kernel per step: each kernel's own span
+    (first start to last end), and the gap from the previous kernel's last end to its first
+    start."""
+    import numpy as np
+    if fused:
+        t0 = tsn[:, 10].min()
+        ends = [(tsn[:, i].max() - t0) / 100.0 for i in range(10)]
+        return {n: round(e - (ends[i - 1] if i else 0.0), 1) for i, (n, e) in enumerate(zip(PHASES, ends))}
+    out, prev_end = {}, None
+    for i in range(1, 10):
+        st, en = tsn[:, 16 + i].min(), tsn[:, i].max()
+        out[PHASES[i]] = round((en - st) / 100.0, 1)
+        if prev_end is not None:
+            out["gap_before_" + PHASES[i]] = round((st - prev_end) / 100.0, 1)
+        prev_end = en
+    return out
+
+
+def roofline_entry(w, alg_bytes, U, us, traffic=None):
+    gbps = alg_bytes / (us * 1e-6) / 1e9
+    out = {"us_per_layer": round(us, 2), "algorithmic_bytes_per_launch": int(alg_bytes), "distinct_experts": U,
+           "achieved_GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "traffic": None if traffic is None else int(traffic["bytes_per_launch"])}
+    if traffic is not None:
+        out["traffic_source"] = traffic["source"]
+    return out
+
+
+def config_bench(name, steps, warmup, unfused=False):
+    """Another layer configuration, timed like the headline one: µs per layer and its roofline."""
+    from moe_layer_persistent_amd import synth
+    w = synth.WORKLOADS[name]
+    lb = LayerBench(w)
+    idx = lb.route()
+    alg, U = algorithmic_bytes(w, idx, w.pos, lb.window, w.T)
+    lb.settle()
+    us, _ = lb.timed(steps, warmup)
+    out = roofline_entry(w, alg, U, us, measured_traffic(name))
+    out.update(window=lb.window, kv_history=w.pos, experts=("nvfp4" if w.expert_dtype == 0 else "bf16"))
+    if unfused:
+        out["unfused_chain_us"] = round(lb.timed(max(3, steps // 2), 2, fused=False)[0], 2)
+    lb.close()
+    return out
 
 
 def stack_bench(steps: int, warmup: int):
     """One GPU's TP8 share of the 62-layer stack, timed as 62 back-to-back layer launches per
     verify step (distinct weights per layer, so nothing is warm in the 256 MB last-level cache;
-    each layer's y is the next layer's x).  Returns a dict for the JSON line."""
+    each layer's y is the next layer's x), fused and as the one-kernel-per-step chain.  The
+    algorithmic bytes are summed over the layers, each with the experts its own routing used."""
+    import numpy as np
     import torch
     from moe_layer_persistent_amd import binding, synth
 
@@ -144,33 +339,70 @@ def stack_bench(steps: int, warmup: int):
     stream = torch.cuda.current_stream()
     bufs = [x0.clone(), torch.empty_like(x0)]
 
-    def step():
+    def step(fused=True, idx=None):
         bufs[0].copy_(x0)
         for l in range(w.n_layers):
             xin, yout = bufs[l % 2], bufs[(l + 1) % 2]
+            dbg = None if idx is None else {"expert_idx": idx[l]}
             plan.layer_decode(layers[l], caches[l][0], caches[l][1], xin, w.pos, w.layer_window(l), yout,
-                              stream=stream)
+                              fused=fused, stream=stream, dbg=dbg)
 
-    for _ in range(warmup):
-        step()
+    # one step with the routing of every layer recorded, for the algorithmic bytes
+    idx = [torch.zeros((w.T, w.top_k), dtype=torch.int32, device=dev) for _ in range(w.n_layers)]
+    step(idx=idx)
     torch.cuda.synchronize()
-    st = plan.status()
-    assert st == 0, binding.status_string(st)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        step()
-    b.record(stream)
-    torch.cuda.synchronize()
-    st = plan.status()
-    assert st == 0, binding.status_string(st)
-    step_us = a.elapsed_time(b) * 1e3 / steps
-    out = {"workload": w.name, "layers": w.n_layers, "global_layers": sum(w.layer_window(l) == 0 for l in range(w.n_layers)),
+    alg, us_l = 0, []
+    for l in range(w.n_layers):
+        b, U = algorithmic_bytes(w, idx[l].cpu().numpy(), w.pos, w.layer_window(l), w.T)
+        alg += b
+        us_l.append(U)
+
+    def timed(fused, n, wu):
+        for _ in range(wu):
+            step(fused)
+        torch.cuda.synchronize()
+        st = plan.status()
+        assert st == 0, binding.status_string(st)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            step(fused)
+        b.record(stream)
+        torch.cuda.synchronize()
+        st = plan.status()
+        assert st == 0, binding.status_string(st)
+        return a.elapsed_time(b) * 1e3 / n
+
+    timed(True, 10, 0)  # untimed: settles clocks and power state
+    step_us = timed(True, steps, warmup)
+    unfused_us = timed(False, max(2, steps // 2), 1)
+    # per-phase timelines of a global layer (0) and a sliding-window layer (1), fused and as one
+    # kernel per step
+    phases = {}
+    for l in (0, 1):
+        for fused in (True, False):
+            ts = torch.zeros((plan.workgroups, binding.MOEL_N_STAMPS), dtype=torch.int64, device=dev)
+            plan.layer_decode(layers[l], caches[l][0], caches[l][1], bufs[0], w.pos, w.layer_window(l), bufs[1],
+                              fused=fused, stream=stream, dbg={"timestamps": ts})
+            torch.cuda.synchronize()
+            key = f"layer{l}_{'global' if w.layer_window(l) == 0 else 'swa'}_{'fused' if fused else 'unfused'}"
+            phases[key] = stamp_table(ts.cpu().numpy().astype(np.float64), fused)
+    gbps = alg / (step_us * 1e-6) / 1e9
+    traffic = measured_traffic("stack_tp8")
+    out = {"workload": w.name, "layers": w.n_layers,
+           "global_layers": sum(w.layer_window(l) == 0 for l in range(w.n_layers)),
            "kv_history": w.pos, "T": w.T, "verify_step_us": round(step_us, 1),
            "us_per_layer": round(step_us / w.n_layers, 2),
            "tokens_per_s": round(ACCEPTED_PER_STEP / (step_us * 1e-6), 1),
            "tokens_per_s_note": f"{ACCEPTED_PER_STEP} accepted tokens per verify step / the 62-layer verify time "
                                 "(one GPU's share; no draft, embedding, LM head or collectives)",
+           "algorithmic_bytes_per_step": int(alg), "algorithmic_bytes_per_layer": int(alg / w.n_layers),
+           "distinct_experts_mean": round(sum(us_l) / len(us_l), 1),
+           "achieved_GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
+           "traffic_per_launch": None if traffic is None else int(traffic["bytes_per_launch"]),
+           "unfused_chain": {"verify_step_us": round(unfused_us, 1), "us_per_layer": round(unfused_us / w.n_layers, 2),
+                             "launches_per_layer": 10},
+           "phase_us": phases,
            "weights_GB": round(sum(lw.nbytes() for lw in layers) / 1e9, 1), "setup_s": round(t_gen, 1),
            "steps": steps}
     del layers, caches, bufs
@@ -189,6 +421,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-unfused", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="skip the 62-layer stack timing")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other full-width layer configurations")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the headline launches (no launch-mode, tree, fp4-gather or routing variants)")
     ap.add_argument("--dump-stamps", default=None, help="write the per-workgroup timestamps (.npy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
@@ -203,89 +438,32 @@ def main():
     from moe_layer_persistent_amd import binding, synth
 
     w = synth.WORKLOADS[args.workload]
-    assert w.n_layers == 1, "stack workloads are timed by bench_stack"
-    window = w.layer_window(0)
-    dev = torch.device("cuda")
-    t = synth.make_layer(w, 0, dev, routing=args.routing)
-    plan = binding.Plan(binding.config_from_workload(w))
+    if w.n_layers != 1:
+        stack = stack_bench(steps=max(1, args.steps // 5), warmup=1)
+        print(json.dumps({"metric": "us per decoder layer at T=16 verify + achieved HBM GB/s (% of peak), 1 GPU",
+                          "value": stack["us_per_layer"], "unit": "us/layer", "n_gpus": 1, "stack": stack}))
+        return
+    lb = LayerBench(w, routing=args.routing)
     # a second plan for the same weights with the SwiGLU output gathered in fp4 (created beside
-    # the first, before the weights are packed, so that both workspaces are allocated alike)
+    # the first, before timing, so that both workspaces are allocated alike)
     plan_a4 = None
-    if w.expert_dtype == synth.NVFP4 and w.down_input == synth.DOWN_EXACT:
+    if not args.no_extras and w.expert_dtype == synth.NVFP4 and w.down_input == synth.DOWN_EXACT:
         plan_a4 = binding.Plan(binding.config_from_workload(w.with_(down_input=synth.DOWN_NVFP4)))
-    copies = [plan.pack_layer(t), plan.pack_layer(t)]
+        lb.extra_plans.append(plan_a4)
     T = w.T
-    x = t["x"].contiguous()
-    kc = t["k_cache"].clone()
-    vc = t["v_cache"].clone()
-    y = torch.empty((T, w.hidden), dtype=torch.float32, device=dev)
-    dbg = {"expert_idx": torch.zeros((T, w.top_k), dtype=torch.int32, device=dev)}
-    stream = torch.cuda.current_stream()
-    plan.layer_decode(copies[0], kc, vc, x, w.pos, window, y, dbg=dbg, stream=stream)
-    torch.cuda.synchronize()
-    assert plan.status() == 0
-    idx = dbg["expert_idx"].cpu().numpy()
-    alg_bytes, U = algorithmic_bytes(w, idx, w.pos, window, T)
+    idx = lb.route()
+    alg_bytes, U = algorithmic_bytes(w, idx, w.pos, lb.window, T)
+    lb.settle()
 
-    def timed(fused, steps, warmup, parents=None, pl=None, cps=None):
-        """Back-to-back launches between two events on the launch stream: the average launch
-        duration (us) over the timed region, and the host wall time (s)."""
-        pl = plan if pl is None else pl
-        cps = copies if cps is None else cps
-        for i in range(warmup):
-            pl.layer_decode(cps[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
-                            parents=parents)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        a.record(stream)
-        for i in range(steps):
-            pl.layer_decode(cps[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream,
-                            parents=parents)
-        b.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return a.elapsed_time(b) * 1e3 / steps, wall
-
-    def per_launch(fused, steps):
-        """Event pairs around single launches (spread of launch times; includes dispatch gaps)."""
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            evs[i][0].record(stream)
-            plan.layer_decode(copies[i % 2], kc, vc, x, w.pos, window, y, fused=fused, stream=stream)
-            evs[i][1].record(stream)
-        torch.cuda.synchronize()
-        return [e0.elapsed_time(e1) * 1e3 for e0, e1 in evs]
-
-    mean_us, wall = timed(True, args.steps, args.warmup)
-    st = plan.status()
-    assert st == 0, binding.status_string(st)
+    mean_us, wall = lb.timed(args.steps, args.warmup)
     ms_per_step = wall * 1e3 / args.steps
-    durs = per_launch(True, max(5, args.steps // 2))
-    # the same weights with the SwiGLU output gathered in fp4 before the down projection (the
-    # payload of the N-sharded layout's first all-gather), through a plan configured for it
-    a4_us = None
-    if plan_a4 is not None:
-        cps_a4 = [binding.LayerWeights(c.packed, dict(c.ts, act=t["act_ts"].contiguous())) for c in copies]
-        a4_us, _ = timed(True, args.steps, args.warmup, pl=plan_a4, cps=cps_a4)
-        st = plan_a4.status()
-        assert st == 0, binding.status_string(st)
-        plan_a4.close()
-    # the same launches through the cooperative launch API (guaranteed residency on a shared
-    # device), for comparison: the runtime adds a gap between consecutive cooperative launches
-    plan.set_launch(binding.MOEL_LAUNCH_COOPERATIVE)
-    coop_us, _ = timed(True, max(5, args.steps // 2), 2)
-    plan.set_launch(binding.MOEL_LAUNCH_PLAIN)
-    # and with barriers whose acquire also invalidates the L2 (the memory model's agent-scope
-    # acquire), for comparison with the L1-only acquire taken where the L2s are coherent
-    plan.set_acquire(binding.MOEL_ACQUIRE_L2_INVALIDATE)
-    inv_us, _ = timed(True, max(5, args.steps // 2), 2)
-    plan.set_acquire(binding.MOEL_ACQUIRE_AUTO)
-    # the same step as a token-tree verify (16 nodes: two branches off the root, one branching
-    # again), which moves only positions and the attention mask
-    tree_us, _ = timed(True, max(5, args.steps // 2), 2, parents=TREE16)
+    durs = lb.per_launch(max(5, args.steps // 2))
     gbps = alg_bytes / (mean_us * 1e-6) / 1e9
     traffic = measured_traffic(w.name)
+    latency = {"mean_back_to_back": round(mean_us, 2),
+               "single_launch_median": round(statistics.median(durs), 2),
+               "single_launch_p10": round(float(np.percentile(durs, 10)), 2),
+               "single_launch_p90": round(float(np.percentile(durs, 90)), 2)}
     result = {
         "metric": "us per decoder layer at T=16 verify + achieved HBM GB/s (% of peak), 1 GPU",
         "value": round(mean_us, 2),
@@ -301,19 +479,12 @@ def main():
         else "bf16 weights+KV, fp32 accumulate",
         "data": "synthetic (seeded N(0,1) activations / KV history, N(0,0.02) weights)",
         "config": {"workload": w.name, "T": T, "hidden": w.hidden, "q_heads": w.n_q_heads,
-                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "window": window, "kv_history": w.pos,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "window": lb.window, "kv_history": w.pos,
                    "experts": w.n_experts, "top_k": w.top_k, "pooled": w.pooled, "inter": w.inter,
                    "routing": args.routing, "distinct_experts": U, "weight_copies_rotated": 2,
                    "launch": "plain",
-                   "barrier_acquire": "L1 only (XCD L2s coherent)" if plan.l2_coherent else "L1 + L2 invalidate"},
-        "latency_us": {"mean_back_to_back": round(mean_us, 2),
-                       "single_launch_median": round(statistics.median(durs), 2),
-                       "single_launch_p10": round(float(np.percentile(durs, 10)), 2),
-                       "single_launch_p90": round(float(np.percentile(durs, 90)), 2),
-                       "cooperative_launch_back_to_back": round(coop_us, 2),
-                       "l2_invalidating_acquire_back_to_back": round(inv_us, 2),
-                       "token_tree_verify_back_to_back": round(tree_us, 2),
-                       "fp4_gathered_down_input_back_to_back": None if a4_us is None else round(a4_us, 2)},
+                   "barrier_acquire": "L1 only (XCD L2s coherent)" if lb.plan.l2_coherent else "L1 + L2 invalidate"},
+        "latency_us": latency,
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PEAK_HBM_GBPS, 4),
@@ -321,50 +492,56 @@ def main():
                      "algorithmic_bytes_per_launch": int(alg_bytes),
                      "kernel": "k_layer_fused (one launch per layer, one workgroup per CU)"},
     }
-    # per-phase timeline of one fused launch (workgroup timestamps, 100 MHz clock): slot i is
-    # the end of step i, slot 16 + i its start (after the preceding grid barrier)
-    names = ["norm1", "qkv_rope_kv", "attention", "attn_merge", "o_proj", "router_pool", "experts_gate_up",
-             "experts_down", "combine", "unpool"]
-    ts = torch.zeros((plan.workgroups, binding.MOEL_N_STAMPS), dtype=torch.int64, device=dev)
-    plan.layer_decode(copies[0], kc, vc, x, w.pos, window, y, dbg={"timestamps": ts}, stream=stream)
-    torch.cuda.synchronize()
-    tsn = ts.cpu().numpy().astype(np.float64)
-    if args.dump_stamps:
-        np.save(args.dump_stamps + "_fused.npy", ts.cpu().numpy())
-        ts.zero_()
-        plan.layer_decode(copies[1], kc, vc, x, w.pos, window, y, dbg={"timestamps": ts}, fused=False,
-                          stream=stream)
-        torch.cuda.synchronize()
-        np.save(args.dump_stamps + "_unfused.npy", ts.cpu().numpy())
-        np.save(args.dump_stamps + "_idx.npy", idx)
-    t0 = tsn[:, 10].min()
-    ends = [(tsn[:, i].max() - t0) / 100.0 for i in range(10)]
-    result["phase_end_us"] = {n: round(e, 1) for n, e in zip(names, ends)}
-    result["phase_us"] = {n: round(e - (ends[i - 1] if i else 0.0), 1) for i, (n, e) in enumerate(zip(names, ends))}
-    work = (tsn[:, :10] - tsn[:, 16:26]) / 100.0
-    result["phase_work_us"] = {n: {"median": round(float(np.median(work[:, i])), 1),
-                                   "max": round(float(work[:, i].max()), 1)} for i, n in enumerate(names)}
-    # grid barrier before step i: last arrival -> first / last departure
-    result["barrier_us"] = {names[i]: {"first_out": round((tsn[:, 16 + i].min() - tsn[:, i - 1].max()) / 100.0, 2),
-                                       "last_out": round((tsn[:, 16 + i].max() - tsn[:, i - 1].max()) / 100.0, 2)}
-                            for i in range(1, 10)}
     if traffic is not None:
         result["roofline"]["traffic_source"] = traffic["source"]
+    if not args.no_extras:
+        # the same weights with the SwiGLU output gathered in fp4 before the down projection (the
+        # payload of the N-sharded layout's first all-gather), through a plan configured for it
+        if plan_a4 is not None:
+            cps_a4 = [binding.LayerWeights(c.packed, dict(c.ts, act=lb.t["act_ts"].contiguous())) for c in lb.copies]
+            latency["fp4_gathered_down_input_back_to_back"] = round(
+                lb.timed(args.steps, args.warmup, pl=plan_a4, cps=cps_a4)[0], 2)
+        # the cooperative launch API (guaranteed residency on a shared device): the runtime adds a
+        # gap between consecutive cooperative launches
+        lb.plan.set_launch(binding.MOEL_LAUNCH_COOPERATIVE)
+        latency["cooperative_launch_back_to_back"] = round(lb.timed(max(5, args.steps // 2), 2)[0], 2)
+        lb.plan.set_launch(binding.MOEL_LAUNCH_PLAIN)
+        # barriers whose acquire also invalidates the L2 (the memory model's agent-scope acquire)
+        lb.plan.set_acquire(binding.MOEL_ACQUIRE_L2_INVALIDATE)
+        latency["l2_invalidating_acquire_back_to_back"] = round(lb.timed(max(5, args.steps // 2), 2)[0], 2)
+        lb.plan.set_acquire(binding.MOEL_ACQUIRE_AUTO)
+        # the same step as a token-tree verify, which moves only positions and the attention mask
+        latency["token_tree_verify_back_to_back"] = round(lb.timed(max(5, args.steps // 2), 2, parents=TREE16)[0], 2)
+        # the pages' routing concentration (a shared component in every token, tuned so that the
+        # 16 tokens use about 49 distinct experts): the same weights and caches, other input rows
+        if args.routing == "iid":
+            xs = synth.make_x(w, 0, lb.dev, routing="pages")
+            idx_s = lb.route(xs)
+            alg_s, U_s = algorithmic_bytes(w, idx_s, w.pos, lb.window, T)
+            us_s, _ = lb.timed(args.steps, args.warmup, x=xs)
+            result["routing_pages"] = roofline_entry(w, alg_s, U_s, us_s)
+    result.update(lb.phases(args.dump_stamps, idx))
     if not args.no_unfused:
-        u_us, _ = timed(False, max(5, args.steps // 2), 2)
+        u_us, _ = lb.timed(max(5, args.steps // 2), 2, fused=False)
         result["unfused_chain_us"] = {"mean_back_to_back": round(u_us, 2), "launches": 10}
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=lb.dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-    del copies
-    torch.cuda.empty_cache()
+        del src, dst
+    t_cpu = lb.t
+    lb.close()
+    if not args.no_configs and w.name == "swa_fp4":
+        result["configs"] = {"swa_fp4": roofline_entry(w, alg_bytes, U, mean_us, traffic)}
+        for name in ("global_fp4", "swa_bf16"):
+            result["configs"][name] = config_bench(name, max(5, args.steps // 2), 2)
     if not args.no_stack:
         result["stack"] = stack_bench(steps=3, warmup=1)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, t, idx, window)
+        lb_t = synth.make_layer(w, 0, "cuda", routing=args.routing) if t_cpu is None else t_cpu
+        result["cpu_baseline"] = cpu_baseline(w, lb_t, idx, lb.window)
     print(json.dumps(result), flush=True)
 
 

@@ -158,10 +158,11 @@ class Plan:
             lib().moel_plan_destroy(self.handle)
             self.handle = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
         # at interpreter shutdown the HIP runtime (and a profiler attached to it) may already
         # be finalised: leave the workspace to the process exit instead of calling hipFree
-        if sys.is_finalizing():
+        # (the check is bound when the class is defined: module globals may be gone by then)
+        if _finalizing():
             return
         try:
             self.close()

@@ -150,8 +150,10 @@ enum CtrlWord {
   kTop = 64,      // group leaders arrived (monotonic within a launch)
   kGroup = 96,    // + 32 * g: workgroups of group g arrived (monotonic within a launch)
   kWork = 352,    // + 32 * i: tiles handed out so far by expert phase i (0 gate/up, 1 down)
-  kCtrlWords = 1024
+  kFix = 1024,    // + kFixPerPhase * i + b: split-K units of block b of dense phase i arrived
+  kCtrlWords = 2048
 };
+constexpr int kFixPerPhase = 256;
 constexpr int kBarGroups = 8;
 
 __device__ __forceinline__ bool aborted(KP& p) {

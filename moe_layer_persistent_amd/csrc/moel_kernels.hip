@@ -400,10 +400,45 @@ const void* phase_fn(int ph) {
   }
 }
 
+// Split-K of a dense contraction of N rows over K on nwg workgroups: the number of K ranges.
+// A workgroup of an unsplit phase reads the whole fp32 activation (16 x K x 4 B) beside its
+// share of the weights (N x K x 2 B / nwg); split into S ranges, it reads 1/S of the activation
+// for the same weight bytes, and the partial sums then cost a fix-up (arrival count, ordered
+// sum by the block's last unit: ~5 us).  Measured on full-width and stack-share layers, the
+// split pays only while the activation a workgroup reads exceeds its weights, i.e. while
+// 32 nwg / (S N) > 1, and it is taken up to the smallest power of two that ends that (at most 8,
+// each range at least 1,024 k so that every wave streams 4 or more steps).
+int choose_split(int N, int K, int nwg) {
+  int ns = 1;
+  while (ns < 8 && 32.0 * nwg / ((double)ns * N) > 1.0 + 1e-9 && (K / 32) % (2 * ns) == 0 && K / (2 * ns) >= 1024)
+    ns *= 2;
+  return ns;
+}
+
+// The splits of the four dense phases (QKV, o-projection, router/pooler, unpooler).
+// MOEL_DENSE_SPLITS = "q,o,r,u" (or one number for all) overrides the choice where the value is
+// valid for the phase's shape (measurement of alternatives).
+void dense_splits(const moel_config* cfg, int nwg, int out[4]) {
+  const int N[4] = {(cfg->n_q_heads + 2 * cfg->n_kv_heads) * cfg->head_dim, cfg->hidden,
+                    cfg->n_experts + cfg->pooled, cfg->hidden};
+  const int K[4] = {cfg->hidden, cfg->n_q_heads * cfg->head_dim, cfg->hidden, cfg->pooled};
+  int forced[4] = {0, 0, 0, 0};
+  if (const char* env = std::getenv("MOEL_DENSE_SPLITS")) {
+    int n = std::sscanf(env, "%d,%d,%d,%d", &forced[0], &forced[1], &forced[2], &forced[3]);
+    if (n == 1) forced[1] = forced[2] = forced[3] = forced[0];
+  }
+  for (int i = 0; i < 4; ++i) {
+    out[i] = choose_split(N[i], K[i], nwg);
+    const int f = forced[i];
+    if (f >= 1 && f <= 16 && (f & (f - 1)) == 0 && (K[i] / 32) % f == 0 && (K[i] / 32) / f >= 1 && nwg / f >= 1)
+      out[i] = f;
+  }
+}
+
 // Byte offsets of the workspace regions for a shape, a grid of nwg workgroups and a RoPE table
 // of rope_rows rows.
 struct WsLayout {
-  size_t ctrl, q, ao, aml, o, h, lg, pl, a, d, pls, as, aq, m, oop, hop, mop, cos, sin, total;
+  size_t ctrl, q, ao, aml, o, h, lg, pl, a, d, pls, as, aq, m, oop, hop, mop, part, part_ss, cos, sin, total;
 };
 WsLayout ws_layout(const moel_config* cfg, int nwg, int rope_rows) {
   WsLayout L{};
@@ -432,6 +467,16 @@ WsLayout ws_layout(const moel_config* cfg, int nwg, int rope_rows) {
   L.oop = take(T * Hq * D * 4);
   L.hop = take(T * H * 4);
   L.mop = take(T * P * 4);
+  {
+    int sk[4];
+    dense_splits(cfg, nwg, sk);
+    const size_t N[4] = {(Hq + 2 * (size_t)cfg->n_kv_heads) * D, H, E + P, H};
+    size_t mx = 0;
+    for (int i = 0; i < 4; ++i)
+      if (sk[i] > 1) mx = std::max(mx, (size_t)sk[i] * N[i] * T * 4);
+    L.part = take(mx);
+    L.part_ss = take((size_t)nwg * T * 4);
+  }
   L.cos = take((size_t)rope_rows * (D / 2) * 4);
   L.sin = take((size_t)rope_rows * (D / 2) * 4);
   L.total = off;
@@ -478,6 +523,16 @@ void bind_base(LayerParams& b, const moel_config* cfg, int nwg, const WsLayout& 
   b.o_op = reinterpret_cast<float*>(ws + L.oop);
   b.h_op = reinterpret_cast<float*>(ws + L.hop);
   b.m_op = reinterpret_cast<float*>(ws + L.mop);
+  b.part = reinterpret_cast<float*>(ws + L.part);
+  b.part_ss = reinterpret_cast<float*>(ws + L.part_ss);
+  {
+    int sk[4];
+    dense_splits(cfg, nwg, sk);
+    b.sk_qkv = sk[0];
+    b.sk_oproj = sk[1];
+    b.sk_rp = sk[2];
+    b.sk_unpool = sk[3];
+  }
   b.rope_cos = reinterpret_cast<const float*>(ws + L.cos);
   b.rope_sin = reinterpret_cast<const float*>(ws + L.sin);
   b.rope_row0 = 0;
@@ -733,9 +788,10 @@ moel_status moel_plan_create(const moel_config* cfg, moel_plan** out) {
   plan->acquire_mode = MOEL_ACQUIRE_AUTO;
   plan->l2_coherent = l2_coherent_device(dev) ? 1 : 0;
   if (std::getenv("MOEL_LOG"))
-    std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu l2_coherent=%d\n",
+    std::fprintf(stderr, "moel: plan H=%d Hq=%d Hkv=%d D=%d P=%d I=%d E=%d k=%d dtype=%d shards=%d nwg=%d ws=%zu lds=%zu l2_coherent=%d splits=%d,%d,%d,%d\n",
                  cfg->hidden, cfg->n_q_heads, cfg->n_kv_heads, D, cfg->pooled, cfg->inter, cfg->n_experts,
-                 cfg->top_k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx, plan->l2_coherent);
+                 cfg->top_k, cfg->expert_dtype, cfg->n_shards, nwg, off, mx, plan->l2_coherent, plan->base.sk_qkv,
+                 plan->base.sk_oproj, plan->base.sk_rp, plan->base.sk_unpool);
   *out = plan;
   return MOEL_OK;
 }

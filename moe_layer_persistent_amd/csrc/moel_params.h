@@ -42,6 +42,8 @@ struct LayerParams {
   // 1 when the call passes debug outputs: also write the fp32 copies of o, m, pl, a and aq
   // that the step itself does not read (plan scratch export)
   int debug_copies;
+  // split-K of the dense phases (1 = none): QKV, o-projection, router/pooler, unpooler
+  int sk_qkv, sk_oproj, sk_rp, sk_unpool;
   // attention decomposition (per call)
   int attn_lo, attn_nkeys, attn_chunk, attn_nchunks;
   // the step's tokens as the nodes of a token tree (a chain for the linear verify): token t
@@ -94,6 +96,10 @@ struct LayerParams {
   float* o_op;
   float* h_op;
   float* m_op;
+  // split-K partial sums of a dense phase: [split][row][16 tokens], and each unit's sums of
+  // squares of its A rows (sources with stats): [unit][16 tokens]
+  float* part;
+  float* part_ss;
   unsigned* ctrl;   // barrier counter, exit counter, status, abort
   // when set, the last workgroup to leave the persistent launch moves the device status here
   // (0 = ok) and clears it in the control block

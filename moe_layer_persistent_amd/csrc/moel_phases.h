@@ -193,20 +193,26 @@ struct AGammaOp {
 };
 
 // ------------------------------------------------------------------------------------------
-// Dense contraction over a workgroup's rows: out[tok][row] = sum_k A[tok][k] * W[row][k].
-// Rows are assigned in octets (8 rows = four 128-byte lines of every 1 KiB step), so that
-// workgroups never share a cache line.  NT (1..4) tiles of 16 rows per pass; the k-waves
-// split K evenly and stream it through a ring of DEPTH steps; partials meet in LDS.  Lanes of
-// an octet outside the workgroup's range load their partner octet's line instead (the same
-// line another lane fetches; the products are never read), so no load sits behind a branch.
-// On return `fin` holds [tile j][row r][tok] sums for tiles t_first .. t_first+NT-1.
+// Dense contraction over a workgroup's rows: out[tok][row] = sum_k A[tok][k] * W[row][k] over a
+// range of k steps.  Rows are assigned in octets (8 rows = four 128-byte lines of every 1 KiB
+// step), so that workgroups never share a cache line.  NT (1..8) tiles of 16 rows per pass; the
+// k-waves split the pass's steps evenly and stream them through a ring of DEPTH steps; partials
+// meet in LDS.  Lanes of an octet outside the workgroup's range load their partner octet's line
+// instead (the same line another lane fetches; the products are never read), so no load sits
+// behind a branch.  On return `fin` holds [tile j][row r][tok] sums for tiles t_first ..
+// t_first+NT-1 over steps ks0 .. ks0+ksn-1, and (sources with stats) `sumsq` the sum of squares
+// of each token's A elements over those steps, `rstd` 1/rms over the full K when the pass
+// covers all of it.
 // ------------------------------------------------------------------------------------------
+constexpr int kDenseMaxNT = 8;
+constexpr int kMaxSplit = 16;  // split-K ranges of a dense phase at most
 struct DenseLds {
-  f32x4 red[kWaves * 4 * 64];   // 32 KiB
-  float fin[4 * 16 * kMaxT];    // 4 KiB
-  float aux[4 * 16 * kMaxT];    // 4 KiB (epilogue scratch)
+  f32x4 red[kWaves * kDenseMaxNT * 64];   // 64 KiB
+  float fin[kDenseMaxNT * 16 * kMaxT];    // 8 KiB
   float ss[kWaves * 64];        // per-lane sums of squares of the A rows (sources with stats)
+  float sumsq[kMaxT];           // per token: sum of squares over the pass's k steps
   float rstd[kMaxT];            // 1 / rms of each token's A row (sources with stats)
+  int last;                     // split-K: this workgroup reduces its block
 };
 
 // Largest divisor of n that is <= 8: the number of waves that split a reduction of n units
@@ -221,8 +227,8 @@ __device__ __forceinline__ int kwaves_for(int n) {
 // scalar registers first.
 template <int NT, class ASrc>
 __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, const uint8_t* w1_arg,
-                                        int K_arg, int t_first_arg, int oct_lo_arg, int oct_hi_arg,
-                                        const ASrc A_arg) {
+                                        int K_arg, int ks0_arg, int ksn_arg, int t_first_arg, int oct_lo_arg,
+                                        int oct_hi_arg, const ASrc A_arg) {
   // k steps in flight per wave: 2 keeps ~100 KB per CU in flight, which measured faster than
   // deeper rings (more outstanding requests per CU lowered the achieved bandwidth)
   constexpr int DEPTH = 2;
@@ -232,21 +238,22 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
   const uint8_t* w0 = uniform(w0_arg);
   const uint8_t* w1 = uniform(w1_arg);
   const int tiles0 = uniform(tiles0_arg), K = uniform(K_arg), t_first = uniform(t_first_arg);
+  const int ks0 = uniform(ks0_arg), ksn = uniform(ksn_arg);
   const int oct_lo = uniform(oct_lo_arg), oct_hi = uniform(oct_hi_arg);
   const ASrc A = A_arg.scalar();
   const int lane = lane_id(), wv = wave_id();
-  const int S = K >> 5;
-  const int nkw = kwaves_for(S);
+  const int S = K >> 5;  // steps per tile row (the packed tile's stride)
+  const int nkw = kwaves_for(ksn);
   f32x4 acc[NT];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
   float ssum = 0.f;  // sum of squares of this lane's A elements (sources with stats)
   if (wv < nkw) {
-    // k-wave wv takes the steps wv, wv + nkw, ... so that the workgroup's loads in flight
-    // cover one contiguous stretch of each tile
-    const int ns = S / nkw;
+    // k-wave wv takes the steps ks0 + wv, ks0 + wv + nkw, ... so that the workgroup's loads in
+    // flight cover one contiguous stretch of each tile
+    const int ns = ksn / nkw;
     const int tok = (lane & 15) < A.T ? (lane & 15) : A.T - 1;
-    const int kq = 4 * (lane >> 4) + 32 * wv;
+    const int kq = 4 * (lane >> 4) + 32 * (ks0 + wv);
     const uint8_t* base[NT];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
@@ -254,7 +261,7 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
       const int oct = 2 * t + ((lane & 15) >> 3);
       const int src_lane = (oct >= oct_lo && oct < oct_hi) ? lane : (lane ^ 8);
       base[j] = (t < tiles0 ? w0 + (size_t)t * S * 1024 : w1 + (size_t)(t - tiles0) * S * 1024) +
-                (size_t)wv * 1024 + src_lane * 16;
+                (size_t)(ks0 + wv) * 1024 + src_lane * 16;
     }
     typename ASrc::Raw ra[DEPTH];
     u32x4 rw[DEPTH][NT];
@@ -300,7 +307,7 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
     for (int d = 0; d < DEPTH; ++d)
       if (i0 + DEPTH + d < ns) compute(d);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) L.red[(wv * 4 + j) * 64 + lane] = acc[j];
+    for (int j = 0; j < NT; ++j) L.red[(wv * kDenseMaxNT + j) * 64 + lane] = acc[j];
   }
   // every (token, k) of the A rows is fetched by exactly one lane of the k-waves (lanes with
   // (lane & 15) >= T repeat token T-1 and are left out)
@@ -312,20 +319,21 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
       for (int w = 0; w < nkw; ++w)
 #pragma unroll
         for (int q = 0; q < 4; ++q) s += L.ss[w * 64 + 16 * q + threadIdx.x];
+      L.sumsq[threadIdx.x] = s;
       L.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + A.eps);
     }
   }
   for (int e = threadIdx.x; e < NT * 256; e += kThreads) {
     const int j = e >> 8, ln = (e >> 2) & 63, r = e & 3;
     float s = 0.f;
-    for (int w = 0; w < nkw; ++w) s += L.red[(w * 4 + j) * 64 + ln][r];
+    for (int w = 0; w < nkw; ++w) s += L.red[(w * kDenseMaxNT + j) * 64 + ln][r];
     const int tok = 4 * (ln >> 4) + r, row = ln & 15;
     L.fin[(j * 16 + row) * kMaxT + tok] = s;
   }
   lds_barrier();
 }
 
-// Octet range of a workgroup for a contraction with `tiles` 16-row tiles.
+// Octet range of a workgroup (or a split-K block) for a contraction with `tiles` 16-row tiles.
 __device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo, int& hi) {
   const int n = 2 * tiles;
   // 32-bit: n * nwg < 2^32 for every accepted shape (n <= N / 8)
@@ -333,26 +341,140 @@ __device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo,
   hi = (int)((unsigned)(wg + 1) * (unsigned)n / (unsigned)nwg);
 }
 
-// Runs dense_pass over the workgroup's rows in groups of <= 4 tiles and calls
-// epi(L, t_first, ntiles, oct_lo, oct_hi) after each group.
+template <class ASrc>
+__device__ __forceinline__ void dense_pass_nt(int nt, const uint8_t* w0, int tiles0, const uint8_t* w1, int K,
+                                              int ks0, int ksn, int t, int lo, int hi, const ASrc& A) {
+  switch (nt) {
+    case 1: dense_pass<1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    case 2: dense_pass<2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    case 3: dense_pass<3>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    case 4: dense_pass<4>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    case 5: dense_pass<5>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    case 6: dense_pass<6>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    case 7: dense_pass<7>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    default: dense_pass<8>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+  }
+}
+
+// A dense phase: the output rows of `tiles0 + tiles1` tiles (two stacked matrices) over the full
+// K, with epi(L, t_first, ntiles, oct_lo, oct_hi) called on every group of <= 8 finished tiles.
+//
+// nsplit == 1: each workgroup owns an octet range over the whole K.
+// nsplit > 1 (split-K): the rows form nwg / nsplit blocks and K nsplit equal step ranges; each
+// workgroup owns one (block, range) unit, so it reads the activation only over its range.  The
+// units write their partial sums (and, for sources with stats, their sums of squares) to `part`,
+// count their arrival on the block's counter, and the last of a block's units to arrive sums the
+// partials in range order -- a fixed order, so the result does not depend on which unit came
+// last -- and runs the epilogue.  The units of a block sit on one XCD (workgroup w runs on XCD
+// w mod 8), so the partials it reads are in that XCD's L2.  No unit waits for another.
 template <class ASrc, class Epi>
-__device__ __forceinline__ void dense_phase(const uint8_t* w0, int tiles0, const uint8_t* w1, int tiles1, int K,
-                            int wg, int nwg, const ASrc& A, DenseLds& L, Epi&& epi) {
-  int lo, hi;
-  octet_range(tiles0 + tiles1, wg, nwg, lo, hi);
-  if (lo >= hi) {
-    epi(L, 0, 0, lo, hi);
+__device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const uint8_t* w0, int tiles0,
+                                            const uint8_t* w1, int tiles1, int K, int wg, const ASrc& A,
+                                            DenseLds& L, Epi&& epi) {
+  const int nwg = p.nwg;
+  const int tiles = tiles0 + tiles1;
+  const int S = K >> 5;
+  if (nsplit <= 1) {
+    int lo, hi;
+    octet_range(tiles, wg, nwg, lo, hi);
+    if (lo >= hi) return;
+    const int tf = lo >> 1, tl = (hi - 1) >> 1;
+    for (int t = tf; t <= tl; t += kDenseMaxNT) {
+      const int nt = (tl - t + 1) < kDenseMaxNT ? (tl - t + 1) : kDenseMaxNT;
+      dense_pass_nt(nt, w0, tiles0, w1, K, 0, S, t, lo, hi, A);
+      epi(L, t, nt, lo, hi);
+      lds_barrier();
+    }
     return;
   }
+  const int nblk = nwg / nsplit;
+  if (wg >= nblk * nsplit) return;
+  int b, js;
+  if (nwg % (8 * nsplit) == 0) {
+    const int x = wg & 7, i = wg >> 3;  // XCD and index within it
+    b = x + 8 * (i / nsplit);
+    js = i % nsplit;
+  } else {
+    b = wg / nsplit;
+    js = wg % nsplit;
+  }
+  int lo, hi;
+  octet_range(tiles, b, nblk, lo, hi);
+  if (lo >= hi) return;  // an empty block: none of its units takes part
   const int tf = lo >> 1, tl = (hi - 1) >> 1;
-  for (int t = tf; t <= tl; t += 4) {
-    const int nt = (tl - t + 1) < 4 ? (tl - t + 1) : 4;
-    switch (nt) {
-      case 1: dense_pass<1>(w0, tiles0, w1, K, t, lo, hi, A); break;
-      case 2: dense_pass<2>(w0, tiles0, w1, K, t, lo, hi, A); break;
-      case 3: dense_pass<3>(w0, tiles0, w1, K, t, lo, hi, A); break;
-      default: dense_pass<4>(w0, tiles0, w1, K, t, lo, hi, A); break;
+  const int ksn = S / nsplit, ks0 = js * ksn;
+  const int ntot = tiles * 16;
+  auto part = gl(p.part);
+  for (int t = tf; t <= tl; t += kDenseMaxNT) {
+    const int nt = (tl - t + 1) < kDenseMaxNT ? (tl - t + 1) : kDenseMaxNT;
+    dense_pass_nt(nt, w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A);
+    for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
+      const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, tok = e % kMaxT;
+      const int n = (t + j) * 16 + r;
+      if (tok < p.T && (n >> 3) >= lo && (n >> 3) < hi)
+        part[((size_t)js * ntot + n) * kMaxT + tok] = L.fin[(j * 16 + r) * kMaxT + tok];
     }
+    lds_barrier();
+  }
+  if constexpr (ASrc::kStats) {
+    if (threadIdx.x < kMaxT) gl(p.part_ss)[(b * nsplit + js) * kMaxT + threadIdx.x] = L.sumsq[threadIdx.x];
+  }
+  // arrival: the partials are written back before the count (release), and the last unit of
+  // the block reads them after it (acquire)
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    auto cnt = gl(p.ctrl) + kFix + kFixPerPhase * fix_id + b;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = prev == (unsigned)nsplit - 1;
+    if (last) {
+      __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
+      acquire_fence(p.l2_coherent);
+    }
+    L.last = last;
+  }
+  __syncthreads();
+  if (!L.last) return;
+  // the partials of every output this thread sums are loaded together (all in flight at once),
+  // then summed in split order
+  if constexpr (ASrc::kStats) {
+    if (threadIdx.x < kMaxT) {
+      float v[kMaxSplit];
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q)
+        v[q] = q < nsplit ? gl(p.part_ss)[(b * nsplit + q) * kMaxT + threadIdx.x] : 0.f;
+      float s = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q)
+        if (q < nsplit) s += v[q];
+      L.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + A.eps);
+    }
+  }
+  constexpr int kPer = kDenseMaxNT * 16 * kMaxT / kThreads;  // outputs per thread and tile group
+  for (int t = tf; t <= tl; t += kDenseMaxNT) {
+    const int nt = (tl - t + 1) < kDenseMaxNT ? (tl - t + 1) : kDenseMaxNT;
+    float v[kPer][kMaxSplit];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, tok = e % kMaxT;
+      const int n = (t + j) * 16 + r;
+      const bool ok = j < nt && tok < p.T && (n >> 3) >= lo && (n >> 3) < hi;
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q)
+        v[i][q] = (ok && q < nsplit) ? part[((size_t)q * ntot + n) * kMaxT + tok] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      float sum = 0.f;
+#pragma unroll
+      for (int q = 0; q < kMaxSplit; ++q)
+        if (q < nsplit) sum += v[i][q];
+      L.fin[e] = sum;  // e = (j * 16 + r) * kMaxT + tok
+    }
+    lds_barrier();
     epi(L, t, nt, lo, hi);
     lds_barrier();
   }
@@ -373,7 +495,7 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
   AGamma A{p.x, p.H, p.gamma1, p.T, p.eps};  // RMSNorm 1 folded in: rstd from the same pass
   const int tiles = (p.Hq + 2 * p.Hkv) * p.D / 16;
   const int half = p.D >> 1;
-  dense_phase(p.w_qkv, tiles, nullptr, 0, p.H, wg, p.nwg, A, L,
+  dense_phase(p, 0, p.sk_qkv, p.w_qkv, tiles, nullptr, 0, p.H, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 8 * kMaxT; e += kThreads) {
                   const int j = e / (8 * kMaxT), pr = (e / kMaxT) & 7, t = e % kMaxT;
@@ -661,7 +783,7 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
 __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AOp A{p.o_op, p.T};
-  dense_phase(p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, p.nwg, A, L,
+  dense_phase(p, 1, p.sk_oproj, p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
@@ -684,7 +806,7 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AGammaOp A{p.h_op, p.gamma2, p.T, p.eps};
   const int te = p.E / 16;
-  dense_phase(p.w_router, te, p.w_pool, p.P / 16, p.H, wg, p.nwg, A, L,
+  dense_phase(p, 2, p.sk_rp, p.w_router, te, p.w_pool, p.P / 16, p.H, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
@@ -1566,7 +1688,7 @@ __device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
 __device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AOp A{p.m_op, p.T};
-  dense_phase(p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, p.nwg, A, L,
+  dense_phase(p, 3, p.sk_unpool, p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
                 for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
                   const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;

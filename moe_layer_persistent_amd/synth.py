@@ -179,18 +179,14 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", routing: str = "iid",
                experts: bool = True) -> Dict[str, torch.Tensor]:
     """All inputs of one layer step as torch tensors on `device`.
 
-    routing="iid": x ~ N(0,1) i.i.d. per token.  routing="shared": x_t = a*z + b*n_t with one
-    seeded z shared by the T tokens, which concentrates routing on fewer distinct experts.
+    routing="iid": x ~ N(0,1) i.i.d. per token.  routing="shared" / "pages": x_t = a*z + b*n_t with
+    one seeded z shared by the T tokens, which concentrates routing on fewer distinct experts
+    (see make_x).
     """
     dev = torch.device(device)
     H, D = w.hidden, w.head_dim
     t: Dict[str, torch.Tensor] = {}
-    if routing == "iid":
-        t["x"] = randn((w.T, H), seed_of(w, layer, "x"), dev)
-    else:
-        z = randn((1, H), seed_of(w, layer, "x_shared"), dev)
-        n = randn((w.T, H), seed_of(w, layer, "x"), dev)
-        t["x"] = (0.97 * z + 0.243 * n).contiguous()
+    t["x"] = make_x(w, layer, dev, routing)
 
     def dense(name, shape):
         m = randn(shape, seed_of(w, layer, name), dev, std=0.02)
@@ -209,6 +205,28 @@ def make_layer(w: Workload, layer: int = 0, device="cpu", routing: str = "iid",
     if experts:
         t.update(make_experts(w, layer, dev))
     return t
+
+
+# weight of the shared component in the input rows of the concentrated routing regimes:
+# "shared" (most tokens pick the same experts; used to exercise large token groups) and
+# "pages", chosen so that a full-width layer's 16 tokens use about 49 distinct experts of 256,
+# the count the pages report per layer for their workload (orcarouter.ai English post, "What
+# this number is, and what it is not"): 49 exactly for swa_fp4 with the oracle's routing on
+# CPU-drawn inputs (GPU-drawn inputs of the same seeds differ, and land near it)
+SHARED_WEIGHT = {"shared": 0.97, "pages": 0.8}
+
+
+def make_x(w: Workload, layer: int = 0, device="cpu", routing: str = "iid") -> torch.Tensor:
+    """The step's input rows x [T, hidden]: i.i.d. N(0, 1), or x_t = a z + sqrt(1 - a^2) n_t with
+    one seeded z shared by the T tokens (a = SHARED_WEIGHT[routing])."""
+    dev = torch.device(device)
+    if routing == "iid":
+        return randn((w.T, w.hidden), seed_of(w, layer, "x"), dev)
+    a = SHARED_WEIGHT[routing]
+    b = (1.0 - a * a) ** 0.5
+    z = randn((1, w.hidden), seed_of(w, layer, "x_shared"), dev)
+    n = randn((w.T, w.hidden), seed_of(w, layer, "x"), dev)
+    return (a * z + b * n).contiguous()
 
 
 def expert_shapes(w: Workload):

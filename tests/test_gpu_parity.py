@@ -89,6 +89,29 @@ def test_concentrated_routing_matches_oracle(kw):
     _log(f"concentrated {kw}: {rep}")
 
 
+@pytest.mark.parametrize("splits", ["2,2,2,2", "4,4,4,4", "8,8,8,8", "16,16,16,16"])
+def test_split_k_dense_phases_match_oracle(splits, monkeypatch):
+    """Dense phases with their K split over workgroups (partial sums per range, summed in range
+    order by the block's last unit), forced for every dense phase (MOEL_DENSE_SPLITS, read when
+    the plan is created): against the oracle, deterministic, and fused = unfused bitwise.  16
+    ranges give blocks of 12 QKV tiles, two passes of 8 and 4."""
+    monkeypatch.setenv("MOEL_DENSE_SPLITS", splits)
+    w = synth.small_workload(T=16, pos=300, window=0, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                             pooled=1024, inter=1024, n_experts=64, top_k=8)
+    _log(f"split-K {splits}")
+    run = harness.GpuRun(w)
+    monkeypatch.delenv("MOEL_DENSE_SPLITS")
+    rep = {}
+    a = run.run(fused=True)
+    harness.check_against_oracle(run, a, report=rep)
+    _log(f"split-K {splits}: {rep}")
+    b = run.run(fused=True)
+    c = run.run(fused=False)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(a[k], b[k]), k
+        assert _same_bytes(a[k], c[k]), k
+
+
 def test_fused_equals_unfused_and_is_deterministic():
     w = synth.small_workload(T=16, pos=500, window=100, n_experts=32, top_k=8, pooled=512, inter=512)
     run = harness.GpuRun(w)
