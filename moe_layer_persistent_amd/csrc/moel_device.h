@@ -150,6 +150,7 @@ enum CtrlWord {
   kTop = 64,      // group leaders arrived (monotonic within a launch)
   kGroup = 96,    // + 32 * g: workgroups of group g arrived (monotonic within a launch)
   kWork = 352,    // + 32 * i: tiles handed out so far by expert phase i (0 gate/up, 1 down)
+  kXccMask = 416, // + 32 * g: bit x set when a workgroup of barrier group g runs on XCC x
   kFix = 1024,    // + kFixPerPhase * i + b: split-K units of block b of dense phase i arrived
   kCtrlWords = 2048
 };
@@ -175,6 +176,11 @@ __device__ __forceinline__ void acq_rel_fence(int l2_coherent) {
   else __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
 }
 
+// XCC (accelerator complex die, one L2) of the calling wave.
+__device__ __forceinline__ unsigned xcc_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);  // XCC_ID[3:0]
+}
+
 // Grid-wide barrier number b (1, 2, ... within one launch) of the persistent launch.
 //
 // Arrival is a two-level tree: workgroup w counts into group (w mod 8), whose counter lives
@@ -191,7 +197,14 @@ __device__ __forceinline__ void acq_rel_fence(int l2_coherent) {
 // the fences: the cache operations they issue act on the whole CU / XCD.
 //
 // Every wait is bounded: after ~0.5 s the status word records a timeout and the wait ends.
-__device__ __forceinline__ void grid_barrier(KP& p, unsigned b) {
+//
+// Light release (`light`, decided after the launch's first barrier): when every group's
+// workgroups run on one XCC -- each workgroup records its XCC in its group's mask word before
+// the first barrier, which uses the full release -- a member's stores, complete in its XCC's L2
+// once it counts in (vmcnt(0)), are written back by the group's last arrival, which runs on the
+// same XCC: one L2 write-back per XCC and barrier instead of one per workgroup and two more on
+// the leaders' path.
+__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -199,14 +212,15 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b) {
     const int g = (int)blockIdx.x % ng_all;
     const unsigned n_g = (unsigned)((p.nwg - g + ng_all - 1) / ng_all);
     auto ctrl = gl(p.ctrl);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (!light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned prev = __hip_atomic_fetch_add(ctrl + kGroup + 32 * g, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev + 1 == b * n_g) {
-      acq_rel_fence(p.l2_coherent);
+      if (light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the XCC's L2, all members
+      else acq_rel_fence(p.l2_coherent);
       const unsigned top = __hip_atomic_fetch_add(ctrl + kTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (top + 1 == b * (unsigned)ng_all) {
-        acq_rel_fence(p.l2_coherent);
+        if (!light) acq_rel_fence(p.l2_coherent);
         __hip_atomic_store(ctrl + kFlag, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }

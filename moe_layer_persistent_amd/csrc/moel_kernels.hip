@@ -47,11 +47,35 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
   __shared__ int s_abort;
   const int wg = blockIdx.x;
   const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
-  if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
+  RouteTables& R = route_tables(moel_lds);
+  if (threadIdx.x == 0) {
+    s_abort = aborted(p) ? 1 : 0;
+    R.light = 0;
+    // the XCC this workgroup runs on, into its barrier group's mask (read after barrier 1)
+    const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+    __hip_atomic_fetch_or(gl(p.ctrl) + kXccMask + 32 * ((int)blockIdx.x % ng_all), 1u << xcc_id(),
+                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   __syncthreads();
   const bool run = s_abort == 0;
   unsigned bar = 0;
-  auto sync = [&]() { grid_barrier(p, ++bar); };
+  bool light = false;
+  auto sync = [&]() {
+    grid_barrier(p, ++bar, light);
+    if (bar == 1) {
+      // every group on one XCC: the remaining barriers and split-K fix-ups release per XCC
+      if (threadIdx.x == 0) {
+        int ok = 1;
+        const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+        for (int g = 0; g < ng_all; ++g)
+          ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)) == 1;
+        R.light = ok;
+      }
+      __syncthreads();
+      light = R.light != 0;
+    }
+  };
   // an aborted launch leaves every caller buffer untouched, the timestamps included
   auto stamp = [&](KP& p, int slot) {
     if (run) moel::stamp(p, slot);
@@ -116,6 +140,8 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
         __hip_atomic_store(ctrl + kGroup + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int i = 0; i < 2; ++i)
         __hip_atomic_store(ctrl + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int g = 0; g < kBarGroups; ++g)
+        __hip_atomic_store(ctrl + kXccMask + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -135,7 +161,10 @@ __global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
   if (PH == kPhCombine && wg == 0 && threadIdx.x == 0)
     for (int i = 0; i < 2; ++i)
       __hip_atomic_store(gl(p.ctrl) + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  if (threadIdx.x == 0) s_abort = aborted(p) ? 1 : 0;
+  if (threadIdx.x == 0) {
+    s_abort = aborted(p) ? 1 : 0;
+    route_tables(smem).light = 0;  // no barriers here: split-K fix-ups use the full release
+  }
   __syncthreads();
   if (s_abort) {
     if (wg == 0 && threadIdx.x == 0)

@@ -46,6 +46,7 @@ struct RouteTables {
   float ts[3][512];            // per expert: NVFP4 tensor scales of gate, up, down
   int dq[64];                  // NVFP4 expert phases: dynamic tiles handed to this workgroup,
                                // (sequence << 16) | tile, slot = sequence mod 64
+  int light;                   // 1: every barrier group runs on one XCC (light releases)
 };
 constexpr int kRouteBytes = (sizeof(RouteTables) + 255) & ~255;
 
@@ -420,17 +421,21 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
     if (threadIdx.x < kMaxT) gl(p.part_ss)[(b * nsplit + js) * kMaxT + threadIdx.x] = L.sumsq[threadIdx.x];
   }
   // arrival: the partials are written back before the count (release), and the last unit of
-  // the block reads them after it (acquire)
+  // the block reads them after it (acquire).  With light releases the block's units share one
+  // XCC (they belong to one barrier group), so the partials, complete in its L2 once counted in
+  // (vmcnt(0)), need no write-back, and the last unit invalidates only its L1.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     auto cnt = gl(p.ctrl) + kFix + kFixPerPhase * fix_id + b;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool light = route_tables(moel_lds).light != 0 && nwg % (8 * nsplit) == 0;
+    if (!light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const int last = prev == (unsigned)nsplit - 1;
     if (last) {
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
-      acquire_fence(p.l2_coherent);
+      if (light) asm volatile("buffer_inv sc0" ::: "memory");
+      else acquire_fence(p.l2_coherent);
     }
     L.last = last;
   }
