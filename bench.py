@@ -376,6 +376,23 @@ def stack_bench(steps: int, warmup: int):
     timed(True, 10, 0)  # untimed: settles clocks and power state
     step_us = timed(True, steps, warmup)
     unfused_us = timed(False, max(2, steps // 2), 1)
+    # the stack through moel_stack_decode: 6 layers per persistent launch (grid barriers between them)
+    stk = binding.Stack(plan, layers, [c[0] for c in caches], [c[1] for c in caches],
+                        [w.layer_window(l) for l in range(w.n_layers)])
+    ys = torch.empty_like(x0)
+    for _ in range(warmup + 2):
+        stk.decode(x0, w.pos, ys, stream=stream)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        stk.decode(x0, w.pos, ys, stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    st = plan.status()
+    assert st == 0, binding.status_string(st)
+    stack_us = a.elapsed_time(b) * 1e3 / steps
+    stk.close()
     # per-phase timelines of a global layer (0) and a sliding-window layer (1), fused and as one
     # kernel per step
     phases = {}
@@ -402,6 +419,11 @@ def stack_bench(steps: int, warmup: int):
            "traffic_per_launch": None if traffic is None else int(traffic["bytes_per_launch"]),
            "unfused_chain": {"verify_step_us": round(unfused_us, 1), "us_per_layer": round(unfused_us / w.n_layers, 2),
                              "launches_per_layer": 10},
+           "stack_launches": {"verify_step_us": round(stack_us, 1), "us_per_layer": round(stack_us / w.n_layers, 2),
+                          "tokens_per_s": round(ACCEPTED_PER_STEP / (stack_us * 1e-6), 1),
+                          "achieved_GBps": round(alg / (stack_us * 1e-6) / 1e9, 1),
+                          "frac": round(alg / (stack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                          "note": "moel_stack_decode: 6 layers per persistent launch (11 launches per step)"},
            "phase_us": phases,
            "weights_GB": round(sum(lw.nbytes() for lw in layers) / 1e9, 1), "setup_s": round(t_gen, 1),
            "steps": steps}

@@ -206,8 +206,8 @@ moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* strea
  * *ptr receives a device pointer into the plan's workspace (owned by the plan; valid until
  * moel_plan_destroy; overwritten by the next step), *bytes its size.  o, m, pl, a and aq
  * are fp32 copies the step itself does not read (the experts read pl and a as split bf16
- * operand words): a step writes them only when it is given a moel_debug (they hold the last
- * such step's values). */
+ * operand words): a step writes them only when its moel_debug asks for routing outputs
+ * (expert_idx, gates or router_logits; they hold the last such step's values). */
 moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, size_t* bytes);
 
 /* --- weight packing (one-time, not on the hot path) --------------------------------- */
@@ -279,6 +279,40 @@ moel_status moel_layer_decode_tree_unfused(moel_plan* plan, const moel_weights* 
                                            void* v_cache, const float* x, int32_t T, int32_t pos,
                                            int32_t window, const int32_t* parents, float* y,
                                            const moel_debug* dbg, void* stream);
+
+/* --- a stack of layers in one launch ------------------------------------------------ */
+
+#define MOEL_MAX_STACK_LAYERS 256
+
+typedef struct moel_stack moel_stack;
+
+/* Registers n_layers layers of the plan's shape to be run one after another with persistent
+ * launches that each cover up to 6 layers (moel_stack_decode): layer l + 1 takes layer l's
+ * output rows as its input, with a grid barrier instead of a launch boundary between the layers
+ * of one launch (orcarouter.ai English post, "Where the kernel boundary sits": the launch
+ * boundary is moved so that consecutive layers overlap; "What the 5.9 ms is still spent on": a
+ * launch per layer is the remaining fixed cost; on one GPU there is no collective between the
+ * layers, so no boundary is needed there).  The layers' launch parameters travel as kernel
+ * arguments, 6 layers' worth per launch.
+ *   weights[l], k_caches[l], v_caches[l], windows[l]: layer l as for moel_layer_decode (HOST
+ *     arrays of n_layers entries, copied; the device buffers they point to stay caller-owned and
+ *     must outlive the stack).
+ * Allocates two [16, hidden] fp32 device buffers for the rows between layers.  *out is set only
+ * on success.  Not for the hot path.  The stack uses the plan's workspace: steps of a plan's
+ * stack and of the plan itself must not overlap (they are ordered when issued on one stream). */
+moel_status moel_stack_create(moel_plan* plan, int32_t n_layers, const moel_weights* weights,
+                              void* const* k_caches, void* const* v_caches, const int32_t* windows,
+                              moel_stack** out);
+
+/* One verify step through every layer of the stack: x fp32 [T, hidden] into the first layer, y
+ * fp32 [T, hidden] out of the last (must not alias x), every layer's KV cache written at slots
+ * [pos, pos+T) as by moel_layer_decode.  Results are bitwise those of moel_layer_decode called
+ * layer by layer.  Every layer's arguments are validated on the host before anything is issued;
+ * device status through moel_plan_status.  Asynchronous on `stream`. */
+moel_status moel_stack_decode(moel_stack* stack, const float* x, int32_t T, int32_t pos, float* y,
+                              void* stream);
+
+moel_status moel_stack_destroy(moel_stack* stack);
 
 /* --- allocation-free step -------------------------------------------------------- */
 

@@ -95,6 +95,9 @@ def lib() -> ctypes.CDLL:
                                                      vp]),
             "moel_validate_tree": (i32, [vp, i32]),
             "moel_layer_decode_noalloc": (i32, [P(Config), P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, vp]),
+            "moel_stack_create": (i32, [vp, i32, P(Weights), vp, vp, vp, P(vp)]),
+            "moel_stack_decode": (i32, [vp, vp, i32, i32, vp, vp]),
+            "moel_stack_destroy": (i32, [vp]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -282,3 +285,36 @@ def layer_decode_noalloc(cfg: Config, lw: LayerWeights, k_cache: torch.Tensor, v
     rc = lib().moel_layer_decode_noalloc(ctypes.byref(cfg), ctypes.byref(lw.struct), _ptr(k_cache), _ptr(v_cache),
                                          _ptr(x), T, pos, window, _ptr(y), _ptr(status), _stream(stream))
     _check(rc, "moel_layer_decode_noalloc")
+
+
+class Stack:
+    """A stack of layers of one plan's shape run as one persistent launch per step
+    (moel_stack_create / moel_stack_decode, include/moel.h)."""
+
+    def __init__(self, plan: Plan, layers, k_caches, v_caches, windows):
+        n = len(layers)
+        self.plan, self.layers, self.k, self.v = plan, list(layers), list(k_caches), list(v_caches)
+        warr = (Weights * n)(*[lw.struct for lw in layers])
+        karr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in k_caches])
+        varr = (ctypes.c_void_p * n)(*[t.data_ptr() for t in v_caches])
+        wins = (ctypes.c_int32 * n)(*[int(x) for x in windows])
+        h = ctypes.c_void_p()
+        _check(lib().moel_stack_create(plan.handle, n, warr, karr, varr, wins, ctypes.byref(h)), "moel_stack_create")
+        self.handle = h
+
+    def decode(self, x: torch.Tensor, pos: int, y: torch.Tensor, stream=None, T: Optional[int] = None) -> None:
+        T = x.shape[0] if T is None else T
+        _check(lib().moel_stack_decode(self.handle, _ptr(x), T, pos, _ptr(y), _stream(stream)), "moel_stack_decode")
+
+    def close(self):
+        if self.handle:
+            lib().moel_stack_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self, _finalizing=sys.is_finalizing):
+        if _finalizing():
+            return
+        try:
+            self.close()
+        except Exception:
+            pass

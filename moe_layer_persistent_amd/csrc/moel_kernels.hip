@@ -41,88 +41,47 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   if constexpr (PH == kPhUnpool) phase_unpool(p, wg, smem);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
-  KP& p = kernel_params();
+// Barrier number ++bar of the launch.  After the first one, every workgroup reads the barrier
+// groups' XCC masks (written at launch): when every group runs on one XCC, the rest of the
+// launch's barriers and split-K fix-ups release per XCC (`light`, kept in RouteTables::light).
+__device__ __forceinline__ void launch_barrier(KP& p, unsigned& bar, bool& light) {
+  grid_barrier(p, ++bar, light);
+  if (bar == 1) {
+    RouteTables& R = route_tables(moel_lds);
+    if (threadIdx.x == 0) {
+      int ok = 1;
+      const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+      for (int g = 0; g < ng_all; ++g)
+        ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT)) == 1;
+      R.light = ok;
+    }
+    __syncthreads();
+    light = R.light != 0;
+  }
+}
+
+// Launch entry: the abort word, and this workgroup's XCC into its barrier group's mask.
+__device__ __forceinline__ bool launch_enter(KP& p) {
   __shared__ int s_abort;
-  const int wg = blockIdx.x;
-  const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
   RouteTables& R = route_tables(moel_lds);
   if (threadIdx.x == 0) {
     s_abort = aborted(p) ? 1 : 0;
     R.light = 0;
-    // the XCC this workgroup runs on, into its barrier group's mask (read after barrier 1)
     const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
     __hip_atomic_fetch_or(gl(p.ctrl) + kXccMask + 32 * ((int)blockIdx.x % ng_all), 1u << xcc_id(),
                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
-  const bool run = s_abort == 0;
-  unsigned bar = 0;
-  bool light = false;
-  auto sync = [&]() {
-    grid_barrier(p, ++bar, light);
-    if (bar == 1) {
-      // every group on one XCC: the remaining barriers and split-K fix-ups release per XCC
-      if (threadIdx.x == 0) {
-        int ok = 1;
-        const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
-        for (int g = 0; g < ng_all; ++g)
-          ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT)) == 1;
-        R.light = ok;
-      }
-      __syncthreads();
-      light = R.light != 0;
-    }
-  };
-  // an aborted launch leaves every caller buffer untouched, the timestamps included
-  auto stamp = [&](KP& p, int slot) {
-    if (run) moel::stamp(p, slot);
-  };
-  if (run && p.dbg_ts != nullptr && threadIdx.x == 0)
-    gl(p.dbg_ts)[blockIdx.x * MOEL_N_STAMPS_DEV + kNumPhases] = t_entry;  // entry
-  stamp(p, 16 + kPhNorm1);
-  stamp(p, kPhNorm1);
-  stamp(p, 16 + kPhQkv);
-  if (run) fused_phase<kPhQkv, D>(params_handle(p), wg);
-  stamp(p, kPhQkv);
-  sync();
-  stamp(p, 16 + kPhAttn);
-  if (run) fused_phase<kPhAttn, D>(params_handle(p), wg);
-  stamp(p, kPhAttn);
-  sync();
-  stamp(p, 16 + kPhAttnMerge);
-  if (run) fused_phase<kPhAttnMerge, D>(params_handle(p), wg);
-  stamp(p, kPhAttnMerge);
-  sync();
-  stamp(p, 16 + kPhOproj);
-  if (run) fused_phase<kPhOproj, D>(params_handle(p), wg);
-  stamp(p, kPhOproj);
-  sync();
-  stamp(p, 16 + kPhRouterPool);
-  if (run) fused_phase<kPhRouterPool, D>(params_handle(p), wg);
-  stamp(p, kPhRouterPool);
-  sync();
-  stamp(p, 16 + kPhGemm1);
-  if (run) fused_phase<kPhGemm1, D>(params_handle(p), wg);
-  stamp(p, kPhGemm1);
-  sync();
-  stamp(p, 16 + kPhGemm2);
-  if (run) fused_phase<kPhGemm2, D>(params_handle(p), wg);
-  stamp(p, kPhGemm2);
-  sync();
-  stamp(p, 16 + kPhCombine);
-  if (run) fused_phase<kPhCombine, D>(params_handle(p), wg);
-  stamp(p, kPhCombine);
-  sync();
-  stamp(p, 16 + kPhUnpool);
-  if (run) fused_phase<kPhUnpool, D>(params_handle(p), wg);
-  stamp(p, kPhUnpool);
-  // leave: the last workgroup out resets the barrier words for the next launch
+  return s_abort == 0;
+}
+
+// Launch exit: the last workgroup out resets the barrier words for the next launch (and moves
+// the status to the caller's word when one is given).
+__device__ __forceinline__ void launch_exit(KP& p, bool run) {
   __syncthreads();
   if (threadIdx.x == 0) {
-    if (!run && wg == 0)
+    if (!run && blockIdx.x == 0)
       __hip_atomic_store(gl(p.ctrl) + kStatus, MOEL_DEV_ABORTED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const unsigned prev =
         __hip_atomic_fetch_add(gl(p.ctrl) + kExit, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
@@ -145,6 +104,112 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
       __hip_atomic_store(ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
+}
+
+// The phases of one layer with a grid barrier between consecutive ones (the persistent
+// launch's body; the stack launch runs it once per layer).
+template <int D>
+__device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsigned& bar, bool& light) {
+  KP& p = params_from(ph);
+  auto stamp = [&](int slot) {
+    if (run) moel::stamp(p, slot);
+  };
+  auto sync = [&]() { launch_barrier(p, bar, light); };
+  stamp(16 + kPhNorm1);
+  stamp(kPhNorm1);
+  stamp(16 + kPhQkv);
+  if (run) fused_phase<kPhQkv, D>(ph, wg);
+  stamp(kPhQkv);
+  sync();
+  stamp(16 + kPhAttn);
+  if (run) fused_phase<kPhAttn, D>(ph, wg);
+  stamp(kPhAttn);
+  sync();
+  stamp(16 + kPhAttnMerge);
+  if (run) fused_phase<kPhAttnMerge, D>(ph, wg);
+  stamp(kPhAttnMerge);
+  sync();
+  stamp(16 + kPhOproj);
+  if (run) fused_phase<kPhOproj, D>(ph, wg);
+  stamp(kPhOproj);
+  sync();
+  stamp(16 + kPhRouterPool);
+  if (run) fused_phase<kPhRouterPool, D>(ph, wg);
+  stamp(kPhRouterPool);
+  sync();
+  stamp(16 + kPhGemm1);
+  if (run) fused_phase<kPhGemm1, D>(ph, wg);
+  stamp(kPhGemm1);
+  sync();
+  stamp(16 + kPhGemm2);
+  if (run) fused_phase<kPhGemm2, D>(ph, wg);
+  stamp(kPhGemm2);
+  sync();
+  stamp(16 + kPhCombine);
+  // the expert phases' work counters are free again once both expert phases have passed a
+  // barrier: cleared here for the next layer of the launch (or the next launch)
+  if (wg == 0 && threadIdx.x == 0)
+    for (int i = 0; i < 2; ++i)
+      __hip_atomic_store(gl(p.ctrl) + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (run) fused_phase<kPhCombine, D>(ph, wg);
+  stamp(kPhCombine);
+  sync();
+  stamp(16 + kPhUnpool);
+  if (run) fused_phase<kPhUnpool, D>(ph, wg);
+  stamp(kPhUnpool);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
+  KP& p = kernel_params();
+  const int wg = blockIdx.x;
+  const uint64_t t_entry = __builtin_amdgcn_s_memrealtime();
+  const bool run = launch_enter(p);
+  // an aborted launch leaves every caller buffer untouched, the timestamps included
+  if (run && p.dbg_ts != nullptr && threadIdx.x == 0)
+    gl(p.dbg_ts)[blockIdx.x * MOEL_N_STAMPS_DEV + kNumPhases] = t_entry;  // entry
+  unsigned bar = 0;
+  bool light = false;
+  layer_phases<D>(params_handle(p), wg, run, bar, light);
+  launch_exit(p, run);
+}
+
+// Consecutive layers in one persistent launch: layer l's parameters (its weights, caches,
+// window, and its input and output rows: layer l + 1 reads what layer l wrote) are kernel
+// arguments like the single layer's, read through the constant cache; a grid barrier separates
+// consecutive layers.  Kernel arguments, not a table in device memory: every launch gets a fresh
+// argument buffer, so no cache can hold parameters of an earlier launch.
+constexpr int kStackLayersPerLaunch = 6;  // 6 x 640 B of parameters fit the 4 KiB argument segment
+struct StackArgs {
+  LayerParams layer[kStackLayersPerLaunch];
+  int n;
+};
+static_assert(sizeof(StackArgs) <= 4096, "stack launch arguments exceed the kernel argument segment");
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void k_stack_fused(StackArgs a_arg) {
+  const uint64_t base = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+  KP& p0 = params_from(base);
+  const int nlayers = *reinterpret_cast<const __attribute__((address_space(4))) int*>(
+      base + offsetof(StackArgs, n));
+  const int wg = blockIdx.x;
+  const bool run = launch_enter(p0);
+  unsigned bar = 0;
+  bool light = false;
+  for (int l = 0; l < nlayers; ++l) {
+    const uint64_t ph = base + (uint64_t)l * sizeof(LayerParams);
+    if (l > 0) {
+      launch_barrier(params_from(ph), bar, light);  // layer l's input is complete
+      // layer l rewrites the workspace lines of layer l - 1 from whichever XCD computes them, and
+      // an XCD's L2 can keep its own earlier copy past another XCD's write: every workgroup drops
+      // its L2's clean lines here (after the barrier, whose release wrote every XCD's dirty lines
+      // back), as the boundary between two launches would
+      if (threadIdx.x == 0 && params_from(ph).l2_coherent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+    }
+    layer_phases<D>(ph, wg, run, bar, light);
+  }
+  launch_exit(p0, run);
 }
 
 // =========================================================================================
@@ -315,6 +380,16 @@ __global__ void k_coherence_fill(unsigned* buf, unsigned v, unsigned* flags, uns
 // =========================================================================================
 // host
 // =========================================================================================
+struct moel_stack {
+  moel_plan* plan;
+  int n;
+  moel_weights* w;          // [n] (host copies of the caller's structs)
+  void** k;                 // [n] caches
+  void** v;
+  int32_t* window;          // [n]
+  float* act[2];            // device [16][H]: the rows passed between layers
+};
+
 struct moel_plan {
   moel_config cfg;
   int device;
@@ -412,6 +487,8 @@ bool l2_coherent_device(int dev, unsigned* mem = nullptr, hipStream_t s = nullpt
 
 template <int D>
 const void* fused_fn() { return reinterpret_cast<const void*>(&k_layer_fused<D>); }
+template <int D>
+const void* stack_fn() { return reinterpret_cast<const void*>(&k_stack_fused<D>); }
 
 template <int D>
 const void* phase_fn(int ph) {
@@ -628,7 +705,9 @@ moel_status fill_call(const moel_config* cfg, const LayerParams& base, int l2_co
   p.dbg_gates = dbg ? dbg->gates : nullptr;
   p.dbg_logits = dbg ? dbg->router_logits : nullptr;
   p.dbg_ts = dbg ? reinterpret_cast<unsigned long long*>(dbg->timestamps) : nullptr;
-  p.debug_copies = dbg != nullptr ? 1 : 0;
+  // the fp32 copies the step does not read are written for calls that ask for routing outputs
+  // (tests read them through moel_plan_scratch), not for timestamps alone
+  p.debug_copies = dbg != nullptr && (dbg->expert_idx || dbg->gates || dbg->router_logits) ? 1 : 0;
   return MOEL_OK;
 }
 
@@ -974,6 +1053,93 @@ moel_status moel_layer_decode_unfused(moel_plan* plan, const moel_weights* w, vo
                                       const moel_debug* dbg, void* stream) {
   return moel_layer_decode_tree_unfused(plan, w, k_cache, v_cache, x, T, pos, window, nullptr, y, dbg,
                                         stream);
+}
+
+moel_status moel_stack_create(moel_plan* plan, int32_t n_layers, const moel_weights* weights, void* const* k_caches,
+                              void* const* v_caches, const int32_t* windows, moel_stack** out) {
+  if (plan == nullptr || out == nullptr || n_layers < 1 || n_layers > MOEL_MAX_STACK_LAYERS || weights == nullptr ||
+      k_caches == nullptr || v_caches == nullptr || windows == nullptr)
+    return MOEL_ERR_ARG;
+  for (int l = 0; l < n_layers; ++l)
+    if (windows[l] < 0) return MOEL_ERR_ARG;
+  moel_stack* st = new (std::nothrow) moel_stack();
+  if (st == nullptr) return MOEL_ERR_HIP;
+  st->plan = plan;
+  st->n = n_layers;
+  st->w = new (std::nothrow) moel_weights[n_layers];
+  st->k = new (std::nothrow) void*[n_layers];
+  st->v = new (std::nothrow) void*[n_layers];
+  st->window = new (std::nothrow) int32_t[n_layers];
+  const size_t ab = sizeof(float) * kMaxT * (size_t)plan->cfg.hidden;
+  bool ok = st->w && st->k && st->v && st->window;
+  if (ok) {
+    for (int l = 0; l < n_layers; ++l) {
+      st->w[l] = weights[l];
+      st->k[l] = k_caches[l];
+      st->v[l] = v_caches[l];
+      st->window[l] = windows[l];
+    }
+    ok = hip_ok(hipMalloc(&st->act[0], ab)) && hip_ok(hipMalloc(&st->act[1], ab));
+    const int D = plan->cfg.head_dim;
+    ok = ok && hip_ok(hipFuncSetAttribute(D == 64 ? stack_fn<64>() : stack_fn<128>(),
+                                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)plan->lds_fused));
+  }
+  if (!ok) {
+    moel_stack_destroy(st);
+    return MOEL_ERR_HIP;
+  }
+  *out = st;
+  return MOEL_OK;
+}
+
+moel_status moel_stack_destroy(moel_stack* st) {
+  if (st == nullptr) return MOEL_ERR_ARG;
+  for (int i = 0; i < 2; ++i)
+    if (st->act[i]) (void)hipFree(st->act[i]);
+  delete[] st->w;
+  delete[] st->k;
+  delete[] st->v;
+  delete[] st->window;
+  delete st;
+  return MOEL_OK;
+}
+
+moel_status moel_stack_decode(moel_stack* st, const float* x, int32_t T, int32_t pos, float* y, void* stream) {
+  if (st == nullptr) return MOEL_ERR_ARG;
+  moel_plan* plan = st->plan;
+  const int n = st->n;
+  const size_t ab = sizeof(float) * kMaxT * (size_t)plan->cfg.hidden;
+  const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
+  if (xb < yb + ab && yb < xb + ab) return MOEL_ERR_ARG;  // y must not alias x
+  // every layer's arguments are checked before anything is issued; the layers' rows go
+  // x -> act[0] -> act[1] -> act[0] ... -> y
+  const int nlaunch = (n + kStackLayersPerLaunch - 1) / kStackLayersPerLaunch;
+  StackArgs* args = new (std::nothrow) StackArgs[nlaunch];
+  if (args == nullptr) return MOEL_ERR_HIP;
+  const float* xin = x;
+  for (int l = 0; l < n; ++l) {
+    float* yout = l == n - 1 ? y : st->act[l % 2];
+    StackArgs& a = args[l / kStackLayersPerLaunch];
+    moel_status s = prepare_call(plan, &st->w[l], st->k[l], st->v[l], xin, T, pos, st->window[l], nullptr, yout,
+                                 nullptr, a.layer[l % kStackLayersPerLaunch]);
+    if (s != MOEL_OK) {
+      delete[] args;
+      return s;
+    }
+    a.n = l % kStackLayersPerLaunch + 1;
+    xin = yout;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const void* fn = plan->cfg.head_dim == 64 ? stack_fn<64>() : stack_fn<128>();
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < nlaunch && e == hipSuccess; ++i) {
+    void* kargs[] = {&args[i]};
+    e = plan->launch_mode == MOEL_LAUNCH_COOPERATIVE
+            ? hipLaunchCooperativeKernel(fn, dim3(plan->nwg), dim3(kThreads), kargs, (unsigned)plan->lds_fused, s)
+            : hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), kargs, (unsigned)plan->lds_fused, s);
+  }
+  delete[] args;
+  return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
 }
 
 moel_status moel_layer_decode_noalloc(const moel_config* cfg, const moel_weights* w, void* k_cache,

@@ -366,8 +366,9 @@ __device__ __forceinline__ void dense_pass_nt(int nt, const uint8_t* w0, int til
 // units write their partial sums (and, for sources with stats, their sums of squares) to `part`,
 // count their arrival on the block's counter, and the last of a block's units to arrive sums the
 // partials in range order -- a fixed order, so the result does not depend on which unit came
-// last -- and runs the epilogue.  The units of a block sit on one XCD (workgroup w runs on XCD
-// w mod 8), so the partials it reads are in that XCD's L2.  No unit waits for another.
+// last -- and runs the epilogue.  Where nwg is a multiple of 8 nsplit, the units of a block sit
+// on one XCD (workgroup w runs on XCD w mod 8), so the partials it reads are in that XCD's L2.
+// No unit waits for another.
 template <class ASrc, class Epi>
 __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const uint8_t* w0, int tiles0,
                                             const uint8_t* w1, int tiles1, int K, int wg, const ASrc& A,
@@ -423,7 +424,12 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   // arrival: the partials are written back before the count (release), and the last unit of
   // the block reads them after it (acquire).  With light releases the block's units share one
   // XCC (they belong to one barrier group), so the partials, complete in its L2 once counted in
-  // (vmcnt(0)), need no write-back, and the last unit invalidates only its L1.
+  // (vmcnt(0)), need no write-back, and the last unit invalidates only its L1.  Otherwise the
+  // units may sit on several XCDs, and the address of a partial belongs to another block (often
+  // on another XCD) in each phase: the last unit's L2 may still hold a copy of it from an
+  // earlier phase, which the L2 coherence of the device does not cover (a line that this XCD
+  // wrote earlier in the launch), so it takes the agent-scope acquire, which drops the L2's
+  // clean lines.
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -435,7 +441,7 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
     if (last) {
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
       if (light) asm volatile("buffer_inv sc0" ::: "memory");
-      else acquire_fence(p.l2_coherent);
+      else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     L.last = last;
   }

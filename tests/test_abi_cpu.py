@@ -173,3 +173,11 @@ def test_nvfp4_tile_numbers_must_fit_the_hand_out_words():
     assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK
     # the full-width layer: 64 tiles per expert, at most 128 experts active
     assert L.moel_validate_config(ctypes.byref(_cfg())) == binding.MOEL_OK
+
+
+def test_stack_calls_reject_missing_arguments():
+    L = binding.lib()
+    out = ctypes.c_void_p()
+    assert L.moel_stack_create(None, 2, None, None, None, None, ctypes.byref(out)) == binding.MOEL_ERR_ARG
+    assert L.moel_stack_decode(None, None, 16, 0, None, None) == binding.MOEL_ERR_ARG
+    assert L.moel_stack_destroy(None) == binding.MOEL_ERR_ARG

@@ -340,3 +340,92 @@ def test_expert_n_shards_equal_full_width_rows(down):
             assert _same_bytes(aq_s[:, cols], aq_f[:, cols]), rank
         run_s.plan.close()
         _log(f"n-shard rank {rank}: gate/up rows bitwise equal to the full-width layer's")
+
+
+def _layer_by_layer(plan, lws, k0, v0, windows, x, pos):
+    kc, vc = [k.clone() for k in k0], [v.clone() for v in v0]
+    cur = x
+    for l, lw in enumerate(lws):
+        y = torch.empty_like(x)
+        plan.layer_decode(lw, kc[l], vc[l], cur, pos, windows[l], y)
+        cur = y
+    torch.cuda.synchronize()
+    assert plan.status() == binding.MOEL_OK
+    return cur, kc, vc
+
+
+def test_stack_launch_equals_layer_by_layer():
+    """Layers of one shape in one persistent launch (moel_stack_decode; grid barriers between the
+    layers) give bitwise the rows and caches of moel_layer_decode called layer by layer: a global
+    layer and two sliding-window ones, several calls in a row with 16, 5, 1 and 9 tokens (with
+    few tokens the expert tiles of consecutive layers land on different XCDs, the case where an
+    XCD's L2 keeps its own copy of a rewritten workspace line unless the layer boundary drops it);
+    and a stack of 8 layers, which takes two launches (6 + 2)."""
+    w = synth.small_workload(T=16, pos=300, window=64, n_experts=32, top_k=8, pooled=512, inter=512, hidden=1024,
+                             n_q_heads=8, n_kv_heads=2, head_dim=128)
+    plan = binding.Plan(binding.config_from_workload(w))
+    windows = [0, 64, 7]
+    ts = [synth.make_layer(w, l, "cuda") for l in range(3)]
+    lws = [plan.pack_layer(t) for t in ts]
+    k0 = [t["k_cache"] for t in ts]
+    v0 = [t["v_cache"] for t in ts]
+    kc, vc = [k.clone() for k in k0], [v.clone() for v in v0]
+    st = binding.Stack(plan, lws, kc, vc, windows)
+    for T, pos in ((16, 300), (5, 120), (5, 120), (1, 77), (9, 200)):
+        x = ts[0]["x"][:T].contiguous()
+        y_ref, k_ref, v_ref = _layer_by_layer(plan, lws, k0, v0, windows, x, pos)
+        for l in range(3):
+            kc[l].copy_(k0[l])
+            vc[l].copy_(v0[l])
+        y = torch.full_like(x, float("nan"))
+        st.decode(x, pos, y)
+        torch.cuda.synchronize()
+        assert plan.status() == binding.MOEL_OK
+        assert _same_bytes(y, y_ref), T
+        for l in range(3):
+            assert _same_bytes(kc[l], k_ref[l]) and _same_bytes(vc[l], v_ref[l]), (T, l)
+    st.close()
+    # 8 layers (two launches): the windows cycle global, 64, 7
+    lws8 = [lws[l % 3] for l in range(8)]
+    k8, v8 = [k0[l % 3].clone() for l in range(8)], [v0[l % 3].clone() for l in range(8)]
+    win8 = [windows[l % 3] for l in range(8)]
+    x = ts[0]["x"].contiguous()
+    y_ref, k_ref, v_ref = _layer_by_layer(plan, lws8, k8, v8, win8, x, 300)
+    kc8, vc8 = [k.clone() for k in k8], [v.clone() for v in v8]
+    st8 = binding.Stack(plan, lws8, kc8, vc8, win8)
+    y = torch.full_like(x, float("nan"))
+    st8.decode(x, 300, y)
+    torch.cuda.synchronize()
+    assert plan.status() == binding.MOEL_OK
+    assert _same_bytes(y, y_ref)
+    for l in range(8):
+        assert _same_bytes(kc8[l], k_ref[l]) and _same_bytes(vc8[l], v_ref[l]), l
+    st8.close()
+    plan.close()
+
+
+def test_stack_share_two_layers_in_one_launch():
+    """The TP8 stack share: a global and a sliding-window layer in one launch, bitwise equal to the
+    two layers called one by one; the sliding-window layer's output checked against the oracle on
+    the device's output of the global layer."""
+    w = synth.WORKLOADS["stack_tp8"]
+    _log("stack launch: generating")
+    run0 = harness.GpuRun(w, layer=0)
+    run1 = harness.GpuRun(w, layer=1, plan=run0.plan)
+    windows = [w.layer_window(0), w.layer_window(1)]
+    x = run0.t["x"].contiguous()
+    out0 = run0.run(fused=True)
+    out1 = run1.run(fused=True, x=out0["y"])
+    rep = {}
+    harness.check_against_oracle(run1, out1, report=rep)
+    _log(f"stack launch, layer 1 on layer 0's output: {rep}")
+    kc, vc = [run0.k0.clone(), run1.k0.clone()], [run0.v0.clone(), run1.v0.clone()]
+    st = binding.Stack(run0.plan, [run0.lw, run1.lw], kc, vc, windows)
+    y = torch.full_like(x, float("nan"))
+    st.decode(x, w.pos, y)
+    torch.cuda.synchronize()
+    assert run0.plan.status() == binding.MOEL_OK
+    assert _same_bytes(y, out1["y"])
+    assert _same_bytes(kc[0], out0["k_cache"]) and _same_bytes(vc[0], out0["v_cache"])
+    assert _same_bytes(kc[1], out1["k_cache"]) and _same_bytes(vc[1], out1["v_cache"])
+    st.close()
