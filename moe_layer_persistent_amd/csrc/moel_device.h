@@ -25,6 +25,13 @@ __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
 // A value known to be equal on every lane, moved to a scalar register so that branches and
 // address arithmetic on it stay scalar.
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// No 64-bit integer overload: the int one would take such a value by narrowing it (a parameter
+// handle would lose its upper half).  Handles go through params_from, pointers through the
+// overload below.
+__device__ int uniform(long) = delete;
+__device__ int uniform(unsigned long) = delete;
+__device__ int uniform(long long) = delete;
+__device__ int uniform(unsigned long long) = delete;
 template <class T>
 __device__ __forceinline__ T* uniform(T* p) {
   const uint64_t v = reinterpret_cast<uint64_t>(p);

@@ -186,29 +186,40 @@ struct StackArgs {
 };
 static_assert(sizeof(StackArgs) <= 4096, "stack launch arguments exceed the kernel argument segment");
 
+// One layer of the stack launch, not inlined (the loop around it then holds only its counters
+// and the register allocator sizes the layer's body on its own).  state: the launch's barrier
+// count in bits 0..30, the light-release flag in bit 31; returns the state after the layer.
+template <int D>
+__device__ __noinline__ unsigned stack_layer(uint64_t ph_arg, int wg_arg, int run_arg, unsigned state_arg) {
+  const uint64_t ph = ph_arg;  // params_from moves it to scalar registers
+  const int wg = uniform(wg_arg);
+  const bool run = uniform(run_arg) != 0;
+  const unsigned state = (unsigned)uniform((int)state_arg);
+  unsigned bar = state & 0x7fffffffu;
+  bool light = (state >> 31) != 0;
+  if (bar > 0) {
+    launch_barrier(params_from(ph), bar, light);  // this layer's input is complete
+    // this layer rewrites the workspace lines of the one before from whichever XCD computes
+    // them, and an XCD's L2 can keep its own earlier copy past another XCD's write: every
+    // workgroup drops its L2's clean lines here (after the barrier, whose release wrote every
+    // XCD's dirty lines back), as the boundary between two launches would
+    if (threadIdx.x == 0 && params_from(ph).l2_coherent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    __syncthreads();
+  }
+  layer_phases<D>(ph, wg, run, bar, light);
+  return bar | (light ? 0x80000000u : 0u);
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void k_stack_fused(StackArgs a_arg) {
   const uint64_t base = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
   KP& p0 = params_from(base);
   const int nlayers = *reinterpret_cast<const __attribute__((address_space(4))) int*>(
       base + offsetof(StackArgs, n));
-  const int wg = blockIdx.x;
   const bool run = launch_enter(p0);
-  unsigned bar = 0;
-  bool light = false;
-  for (int l = 0; l < nlayers; ++l) {
-    const uint64_t ph = base + (uint64_t)l * sizeof(LayerParams);
-    if (l > 0) {
-      launch_barrier(params_from(ph), bar, light);  // layer l's input is complete
-      // layer l rewrites the workspace lines of layer l - 1 from whichever XCD computes them, and
-      // an XCD's L2 can keep its own earlier copy past another XCD's write: every workgroup drops
-      // its L2's clean lines here (after the barrier, whose release wrote every XCD's dirty lines
-      // back), as the boundary between two launches would
-      if (threadIdx.x == 0 && params_from(ph).l2_coherent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      __syncthreads();
-    }
-    layer_phases<D>(ph, wg, run, bar, light);
-  }
+  unsigned state = 0;
+  for (int l = 0; l < nlayers; ++l)
+    state = stack_layer<D>(base + (uint64_t)l * sizeof(LayerParams), (int)blockIdx.x, run ? 1 : 0, state);
   launch_exit(p0, run);
 }
 
@@ -544,7 +555,7 @@ void dense_splits(const moel_config* cfg, int nwg, int out[4]) {
 // Byte offsets of the workspace regions for a shape, a grid of nwg workgroups and a RoPE table
 // of rope_rows rows.
 struct WsLayout {
-  size_t ctrl, q, ao, aml, o, h, lg, pl, a, d, pls, as, aq, m, oop, hop, mop, part, part_ss, cos, sin, total;
+  size_t ctrl, q, qop, ao, aml, o, h, lg, pl, a, d, pls, as, aq, m, oop, hop, mop, part, part_ss, cos, sin, total;
 };
 WsLayout ws_layout(const moel_config* cfg, int nwg, int rope_rows) {
   WsLayout L{};
@@ -558,6 +569,7 @@ WsLayout ws_layout(const moel_config* cfg, int nwg, int rope_rows) {
   const size_t E = cfg->n_experts, k = cfg->top_k, grp = Hq / cfg->n_kv_heads, T = kMaxT;
   L.ctrl = take((size_t)kCtrlWords * 4);
   L.q = take(T * Hq * D * 4);
+  L.qop = take(T * Hq * 2 * D * 2);
   L.ao = take((size_t)nwg * grp * T * D * 4);
   L.aml = take((size_t)nwg * grp * T * 2 * 4);
   L.o = take(T * Hq * D * 4);
@@ -614,6 +626,7 @@ void bind_base(LayerParams& b, const moel_config* cfg, int nwg, const WsLayout& 
   b.stride_down = moel_packed_experts_bytes(cfg, 2) / (size_t)cfg->n_experts;
   b.ctrl = reinterpret_cast<unsigned*>(ws + L.ctrl);
   b.q_buf = reinterpret_cast<float*>(ws + L.q);
+  b.q_op = reinterpret_cast<uint16_t*>(ws + L.qop);
   b.attn_o = reinterpret_cast<float*>(ws + L.ao);
   b.attn_ml = reinterpret_cast<float*>(ws + L.aml);
   b.o_buf = reinterpret_cast<float*>(ws + L.o);
@@ -661,10 +674,14 @@ moel_status fill_call(const moel_config* cfg, const LayerParams& base, int l2_co
   const int nkeys = pos + T - lo;
   int maxc = base.nwg / cfg->n_kv_heads;
   if (maxc < 1) maxc = 1;
-  int nch = (nkeys + 127) / 128;  // chunks of >= 128 keys, at most nwg / Hkv of them
+  // chunks of >= 128 keys, at most nwg / Hkv of them; rounded up to whole 128-key sub-chunks
+  // (a full sub-chunk inside every token's window needs no mask) where that keeps their number
+  int nch = (nkeys + 127) / 128;
   if (nch > maxc) nch = maxc;
   if (nch < 1) nch = 1;
-  const int chunk = (nkeys + nch - 1) / nch;
+  int chunk = (nkeys + nch - 1) / nch;
+  const int chunk128 = (chunk + 127) / 128 * 128;
+  if ((nkeys + chunk128 - 1) / chunk128 == nch) chunk = chunk128;
   // token positions and visibility (the chain when parents is NULL); the widest key range is
   // that of a depth-0 token, so attn_lo covers every token
   for (int t = 0; t < kMaxT; ++t) {

@@ -77,6 +77,9 @@ struct LayerParams {
   int rope_row0;
   // scratch (plan workspace)
   float* q_buf;     // [16][Hq*D]
+  // q again as the attention's MFMA operand: per (token, head), q * log2(e) / sqrt(D) as the
+  // nearest bf16 values [D], then the bf16 of the remainders [D]
+  uint16_t* q_op;   // [16][Hq][2][D]
   float* attn_o;    // [items][grp][16][D]
   float* attn_ml;   // [items][grp][16][2]
   float* o_buf;     // [16][Hq*D]

@@ -525,6 +525,15 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
                       auto q = gl(p.q_buf + (size_t)t * p.Hq * p.D + head * p.D);
                       q[i] = ra;
                       q[i + half] = rb;
+                      // the attention's operand: scaled to base-2 score units, as hi + lo
+                      const float qscale = 1.4426950408889634f / sqrtf((float)p.D);
+                      const float sa = ra * qscale, sb = rb * qscale;
+                      const uint16_t ha = f2bf(sa), hb = f2bf(sb);
+                      auto qo = gl(p.q_op + ((size_t)t * p.Hq + head) * 2 * p.D);
+                      qo[i] = ha;
+                      qo[i + half] = hb;
+                      qo[p.D + i] = f2bf(sa - bf2f(ha));
+                      qo[p.D + i + half] = f2bf(sb - bf2f(hb));
                     } else {
                       auto k = gl(p.k_cache + ((size_t)(head - p.Hq) * p.kv_cap + ps) * p.D);
                       k[i] = f2bf(ra);
@@ -577,9 +586,11 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   const int lane = lane_id(), wv = wave_id();
   const int grp = p.Hq / p.Hkv;
   const int nitems = p.Hkv * p.attn_nchunks;
-  const float qscale = 1.4426950408889634f / sqrtf((float)D);  // log2(e) / sqrt(D)
   const float NEG = -__builtin_inff();
   const int gq = lane >> 4, tq = lane & 15;
+  // this thread's place in a sub-chunk's staging: 16-byte column c8 of rows row0 + i * RSTEP
+  constexpr int RSTEP = kThreads / (D / 8);
+  const int row0 = threadIdx.x / (D / 8), c8 = (threadIdx.x % (D / 8)) * 8;
   for (int it = wg; it < nitems; it += p.nwg) {
     const int g = it % p.Hkv, c = it / p.Hkv;
     const int kb = p.attn_lo + c * p.attn_chunk;
@@ -587,61 +598,66 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     if (ke > p.attn_lo + p.attn_nkeys) ke = p.attn_lo + p.attn_nkeys;
     const bool act = wv < grp;
     const int h = g * grp + wv;
-    const uint16_t* kg = p.k_cache + (size_t)g * p.kv_cap * D;
-    const uint16_t* vg = p.v_cache + (size_t)g * p.kv_cap * D;
-    // K/V rows of a sub-chunk into registers; rows past the chunk end repeat its last key
-    // (never visible, so never weighted)
+    const uint16_t* kg = p.k_cache + (size_t)g * p.kv_cap * D + c8;
+    const uint16_t* vg = p.v_cache + (size_t)g * p.kv_cap * D + c8;
+    // K/V rows of a sub-chunk into registers; in the last, partial sub-chunk rows past the
+    // chunk end repeat its last key (never visible, so never weighted)
     u32x4 kr[NCH], vr[NCH];
     auto fetch = [&](int sb) {
-      const int last = ke - 1;
+      if (sb + SK <= ke) {
+        const size_t r = (size_t)(sb + row0) * D;
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) {
-        const int ci = threadIdx.x + i * kThreads;
-        const int row = ci / (D / 8), c8 = (ci % (D / 8)) * 8;
-        const int key = sb + row <= last ? sb + row : last;
-        kr[i] = ldg16(kg + (size_t)key * D + c8);
-        vr[i] = ldg16(vg + (size_t)key * D + c8);
+        for (int i = 0; i < NCH; ++i) {
+          kr[i] = ldg16(kg + r + (size_t)i * RSTEP * D);
+          vr[i] = ldg16(vg + r + (size_t)i * RSTEP * D);
+        }
+      } else {
+        const int last = ke - 1;
+#pragma unroll
+        for (int i = 0; i < NCH; ++i) {
+          const int key = sb + row0 + i * RSTEP <= last ? sb + row0 + i * RSTEP : last;
+          kr[i] = ldg16(kg + (size_t)key * D);
+          vr[i] = ldg16(vg + (size_t)key * D);
+        }
       }
     };
-    fetch(kb);
-    // q of this wave's head as hi + lo (tokens past T repeat token T-1; never stored)
+    // q of this wave's head, scaled and split by the QKV phase (tokens past T repeat token
+    // T-1; their rows are never stored).  Issued before the first K/V rows: the wait for those
+    // at the first LDS fill then covers q too (loads complete in order), so no wait for q is
+    // left inside the key loop, where it would also drain the next sub-chunk's rows in flight.
+    const int tqc = tq < p.T ? tq : p.T - 1;
     u32x4 qh[NS], ql[NS];
     {
-      const int tqc = tq < p.T ? tq : p.T - 1;
-      const float* qs = p.q_buf + (size_t)tqc * p.Hq * D + (act ? h : 0) * D + 8 * gq;
-      float4 qa[NS], qb[NS];
+      const uint16_t* qs = p.q_op + ((size_t)tqc * p.Hq + (act ? h : 0)) * 2 * D + 8 * gq;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
-        qa[s] = ldgf4(qs + 32 * s);
-        qb[s] = ldgf4(qs + 32 * s + 4);
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        qa[s] = float4{qa[s].x * qscale, qa[s].y * qscale, qa[s].z * qscale, qa[s].w * qscale};
-        qb[s] = float4{qb[s].x * qscale, qb[s].y * qscale, qb[s].z * qscale, qb[s].w * qscale};
-        split8(qa[s], qb[s], qh[s], ql[s]);
+        qh[s] = ldg16(qs + 32 * s);
+        ql[s] = ldg16(qs + D + 32 * s);
       }
     }
+    fetch(kb);
     float m_run = NEG, l_run = 0.f;
     f32x4 O[ND];
 #pragma unroll
     for (int d = 0; d < ND; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // this lane's token: its position, and which of the step's keys it sees
-    const int tqc = tq < p.T ? tq : p.T - 1;
+    // this lane's token: its position, which of the step's keys it sees, and the first cached
+    // key inside its window
     const int ptok = p.pos + p.tok_depth[tqc];
     const unsigned sees = p.tok_sees[tqc];
+    const int lo_t = p.window == 0 ? -0x7fffffff - 1 : ptok - p.window + 1;
+    const bool tok_ok = tq < p.T;
     for (int sb = kb; sb < ke; sb += SK) {
-      const int nk = (ke - sb) < SK ? (ke - sb) : SK;
       lds_barrier();  // the previous sub-chunk's LDS reads are done
 #pragma unroll
       for (int i = 0; i < NCH; ++i) {
-        const int ci = threadIdx.x + i * kThreads;
-        const int row = ci / (D / 8), c8 = (ci % (D / 8)) * 8;
+        const int row = row0 + i * RSTEP;
         *reinterpret_cast<u32x4*>(&L.Ks[row * KS + c8]) = kr[i];
+        // V^T: the 8 values of this chunk go to rows c8 .. c8 + 7 of one swizzled key column
+        uint16_t* vt = &L.Vt[L_t::vt_index(c8, row)];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          L.Vt[L_t::vt_index(c8 + 2 * j, row)] = (uint16_t)(vr[i][j] & 0xffffu);
-          L.Vt[L_t::vt_index(c8 + 2 * j + 1, row)] = (uint16_t)(vr[i][j] >> 16);
+          vt[(2 * j) * L_t::VS] = (uint16_t)(vr[i][j] & 0xffffu);
+          vt[(2 * j + 1) * L_t::VS] = (uint16_t)(vr[i][j] >> 16);
         }
       }
       lds_barrier();
@@ -660,8 +676,11 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
         }
         // mask; lane holds keys kt*16 + 4*gq + r of token tq.  A whole sub-chunk of cached
         // keys inside every token's window needs none (rows of tokens past T are never read).
+        // Otherwise key j is visible iff j is in the chunk and, for a cached key, inside the
+        // token's window, for a key of the step, bit j - pos of the token's set; computed
+        // without branches (selects on every element)
         float mx = NEG;
-        const bool all_vis = nk == SK && sb + SK <= p.pos && (p.window == 0 || sb > p.pos + p.T - 1 - p.window);
+        const bool all_vis = sb + SK <= ke && sb + SK <= p.pos && (p.window == 0 || sb > p.pos + p.T - 1 - p.window);
         if (all_vis) {
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt)
@@ -673,8 +692,10 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int j = sb + kt * 16 + 4 * gq + r;
-              const bool vis = tq < p.T && (j - sb) < nk &&
-                               (j < p.pos ? (p.window == 0 || j > ptok - p.window) : ((sees >> (j - p.pos)) & 1u) != 0);
+              const int js = j - p.pos;
+              const unsigned in_win = (unsigned)(j >= lo_t);
+              const unsigned seen = (sees >> (js & 31)) & 1u;
+              const unsigned vis = (unsigned)tok_ok & (unsigned)(j < ke) & (js < 0 ? in_win : seen);
               const float v = vis ? S[kt][r] : NEG;
               S[kt][r] = v;
               mx = fmaxf(mx, v);
