@@ -312,11 +312,31 @@ def config_bench(name, steps, warmup, unfused=False):
     return out
 
 
-def stack_bench(steps: int, warmup: int):
+def progress(msg):
+    """A progress line on stderr (the JSON result is the only stdout line)."""
+    print(msg, file=sys.stderr, flush=True)
+
+
+def copy_calibration_run(dev):
+    """Three plain 1 GiB device-to-device copies: the reference that the HBM counters of a
+    profiling run are scaled by."""
+    import torch
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def stack_bench(steps: int, warmup: int, copy_calibration: bool = False, unfused: bool = True,
+                extras: bool = True):
     """One GPU's TP8 share of the 62-layer stack, timed as 62 back-to-back layer launches per
     verify step (distinct weights per layer, so nothing is warm in the 256 MB last-level cache;
     each layer's y is the next layer's x), fused and as the one-kernel-per-step chain.  The
-    algorithmic bytes are summed over the layers, each with the experts its own routing used."""
+    algorithmic bytes are summed over the layers, each with the experts its own routing used.
+    unfused / extras: also time the one-kernel-per-step chain / the multi-layer launch and the
+    phase timelines.  Progress goes to stderr."""
     import numpy as np
     import torch
     from moe_layer_persistent_amd import binding, synth
@@ -334,8 +354,11 @@ def stack_bench(steps: int, warmup: int):
         if l == 0:
             x0 = t["x"].contiguous()
         del t
+        if l % 8 == 7:
+            progress(f"stack: {l + 1} layers generated")
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
+    progress(f"stack: {w.n_layers} layers generated and packed in {t_gen:.1f} s")
     stream = torch.cuda.current_stream()
     bufs = [x0.clone(), torch.empty_like(x0)]
 
@@ -373,37 +396,45 @@ def stack_bench(steps: int, warmup: int):
         assert st == 0, binding.status_string(st)
         return a.elapsed_time(b) * 1e3 / n
 
-    timed(True, 10, 0)  # untimed: settles clocks and power state
+    timed(True, max(2, min(10, 2 * steps)), 0)  # untimed: settles clocks and power state
+    progress("stack: settled")
     step_us = timed(True, steps, warmup)
-    unfused_us = timed(False, max(2, steps // 2), 1)
-    # the stack through moel_stack_decode: 6 layers per persistent launch (grid barriers between them)
-    stk = binding.Stack(plan, layers, [c[0] for c in caches], [c[1] for c in caches],
-                        [w.layer_window(l) for l in range(w.n_layers)])
-    ys = torch.empty_like(x0)
-    for _ in range(warmup + 2):
-        stk.decode(x0, w.pos, ys, stream=stream)
-    torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record(stream)
-    for _ in range(steps):
-        stk.decode(x0, w.pos, ys, stream=stream)
-    b.record(stream)
-    torch.cuda.synchronize()
-    st = plan.status()
-    assert st == 0, binding.status_string(st)
-    stack_us = a.elapsed_time(b) * 1e3 / steps
-    stk.close()
-    # per-phase timelines of a global layer (0) and a sliding-window layer (1), fused and as one
-    # kernel per step
-    phases = {}
-    for l in (0, 1):
-        for fused in (True, False):
-            ts = torch.zeros((plan.workgroups, binding.MOEL_N_STAMPS), dtype=torch.int64, device=dev)
-            plan.layer_decode(layers[l], caches[l][0], caches[l][1], bufs[0], w.pos, w.layer_window(l), bufs[1],
-                              fused=fused, stream=stream, dbg={"timestamps": ts})
-            torch.cuda.synchronize()
-            key = f"layer{l}_{'global' if w.layer_window(l) == 0 else 'swa'}_{'fused' if fused else 'unfused'}"
-            phases[key] = stamp_table(ts.cpu().numpy().astype(np.float64), fused)
+    progress(f"stack: fused {step_us / w.n_layers:.1f} us/layer")
+    unfused_us = None
+    if unfused:
+        unfused_us = timed(False, max(2, steps // 2), 1)
+        progress(f"stack: one kernel per step {unfused_us / w.n_layers:.1f} us/layer")
+    stack_us, phases = None, {}
+    if extras:
+        # the stack through moel_stack_decode: 6 layers per persistent launch (grid barriers
+        # between them)
+        stk = binding.Stack(plan, layers, [c[0] for c in caches], [c[1] for c in caches],
+                            [w.layer_window(l) for l in range(w.n_layers)])
+        ys = torch.empty_like(x0)
+        for _ in range(warmup + 2):
+            stk.decode(x0, w.pos, ys, stream=stream)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            stk.decode(x0, w.pos, ys, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        st = plan.status()
+        assert st == 0, binding.status_string(st)
+        stack_us = a.elapsed_time(b) * 1e3 / steps
+        stk.close()
+        progress(f"stack: multi-layer launch {stack_us / w.n_layers:.1f} us/layer")
+        # per-phase timelines of a global layer (0) and a sliding-window layer (1), fused and as
+        # one kernel per step
+        for l in (0, 1):
+            for fused in (True, False):
+                ts = torch.zeros((plan.workgroups, binding.MOEL_N_STAMPS), dtype=torch.int64, device=dev)
+                plan.layer_decode(layers[l], caches[l][0], caches[l][1], bufs[0], w.pos, w.layer_window(l),
+                                  bufs[1], fused=fused, stream=stream, dbg={"timestamps": ts})
+                torch.cuda.synchronize()
+                key = f"layer{l}_{'global' if w.layer_window(l) == 0 else 'swa'}_{'fused' if fused else 'unfused'}"
+                phases[key] = stamp_table(ts.cpu().numpy().astype(np.float64), fused)
     gbps = alg / (step_us * 1e-6) / 1e9
     traffic = measured_traffic("stack_tp8")
     out = {"workload": w.name, "layers": w.n_layers,
@@ -417,19 +448,23 @@ def stack_bench(steps: int, warmup: int):
            "distinct_experts_mean": round(sum(us_l) / len(us_l), 1),
            "achieved_GBps": round(gbps, 1), "frac": round(gbps / PEAK_HBM_GBPS, 4),
            "traffic_per_launch": None if traffic is None else int(traffic["bytes_per_launch"]),
-           "unfused_chain": {"verify_step_us": round(unfused_us, 1), "us_per_layer": round(unfused_us / w.n_layers, 2),
-                             "launches_per_layer": 10},
-           "stack_launches": {"verify_step_us": round(stack_us, 1), "us_per_layer": round(stack_us / w.n_layers, 2),
-                          "tokens_per_s": round(ACCEPTED_PER_STEP / (stack_us * 1e-6), 1),
-                          "achieved_GBps": round(alg / (stack_us * 1e-6) / 1e9, 1),
-                          "frac": round(alg / (stack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                          "note": "moel_stack_decode: 6 layers per persistent launch (11 launches per step)"},
-           "phase_us": phases,
            "weights_GB": round(sum(lw.nbytes() for lw in layers) / 1e9, 1), "setup_s": round(t_gen, 1),
            "steps": steps}
+    if unfused_us is not None:
+        out["unfused_chain"] = {"verify_step_us": round(unfused_us, 1),
+                                "us_per_layer": round(unfused_us / w.n_layers, 2), "launches_per_layer": 10}
+    if stack_us is not None:
+        out["stack_launches"] = {"verify_step_us": round(stack_us, 1), "us_per_layer": round(stack_us / w.n_layers, 2),
+                                 "tokens_per_s": round(ACCEPTED_PER_STEP / (stack_us * 1e-6), 1),
+                                 "achieved_GBps": round(alg / (stack_us * 1e-6) / 1e9, 1),
+                                 "frac": round(alg / (stack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                                 "note": "moel_stack_decode: 6 layers per persistent launch (11 launches per step)"}
+        out["phase_us"] = phases
     del layers, caches, bufs
     plan.close()
     torch.cuda.empty_cache()
+    if copy_calibration:
+        copy_calibration_run(dev)
     return out
 
 
@@ -461,7 +496,8 @@ def main():
 
     w = synth.WORKLOADS[args.workload]
     if w.n_layers != 1:
-        stack = stack_bench(steps=max(1, args.steps // 5), warmup=1)
+        stack = stack_bench(steps=max(1, args.steps // 5), warmup=1, copy_calibration=args.copy_calibration,
+                            unfused=not args.no_unfused, extras=not args.no_extras)
         print(json.dumps({"metric": "us per decoder layer at T=16 verify + achieved HBM GB/s (% of peak), 1 GPU",
                           "value": stack["us_per_layer"], "unit": "us/layer", "n_gpus": 1, "stack": stack}))
         return
@@ -547,12 +583,7 @@ def main():
         u_us, _ = lb.timed(max(5, args.steps // 2), 2, fused=False)
         result["unfused_chain_us"] = {"mean_back_to_back": round(u_us, 2), "launches": 10}
     if args.copy_calibration:
-        src = torch.empty(1 << 28, dtype=torch.float32, device=lb.dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration_run(lb.dev)
     t_cpu = lb.t
     lb.close()
     if not args.no_configs and w.name == "swa_fp4":
