@@ -215,7 +215,13 @@ __device__ __forceinline__ unsigned xcc_id() {
 // once it counts in (vmcnt(0)), are written back by the group's last arrival, which runs on the
 // same XCC: one L2 write-back per XCC and barrier instead of one per workgroup and two more on
 // the leaders' path.
-__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false) {
+//
+// drop_l2 (light releases only): the group's last arrival also drops its XCC's clean L2 lines
+// (agent-scope acquire) before counting in.  Every other member of the group has counted in and
+// waits for the release word, so nothing on that XCC loads again before the barrier ends, and
+// every store of the barrier's other workgroups is written back before the word is set: after
+// the barrier the XCC's L2 holds nothing from before it, at one invalidation per XCC.
+__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false, bool drop_l2 = false) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -227,7 +233,10 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = fal
     const unsigned prev = __hip_atomic_fetch_add(ctrl + kGroup + 32 * g, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev + 1 == b * n_g) {
-      if (light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // the XCC's L2, all members
+      if (light) {
+        if (drop_l2) __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");  // write back, then drop
+        else __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");          // the XCC's L2, all members
+      }
       else acq_rel_fence(p.l2_coherent);
       const unsigned top = __hip_atomic_fetch_add(ctrl + kTop, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (top + 1 == b * (unsigned)ng_all) {

@@ -198,13 +198,20 @@ __device__ __noinline__ unsigned stack_layer(uint64_t ph_arg, int wg_arg, int ru
   unsigned bar = state & 0x7fffffffu;
   bool light = (state >> 31) != 0;
   if (bar > 0) {
-    launch_barrier(params_from(ph), bar, light);  // this layer's input is complete
-    // this layer rewrites the workspace lines of the one before from whichever XCD computes
-    // them, and an XCD's L2 can keep its own earlier copy past another XCD's write: every
-    // workgroup drops its L2's clean lines here (after the barrier, whose release wrote every
-    // XCD's dirty lines back), as the boundary between two launches would
-    if (threadIdx.x == 0 && params_from(ph).l2_coherent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    __syncthreads();
+    // this layer's input is complete.  It rewrites the workspace lines of the layer before from
+    // whichever XCD computes them, and an XCD's L2 can keep its own earlier copy past another
+    // XCD's write, so every XCD drops its L2's clean lines here, as the boundary between two
+    // launches would: with light releases once per XCC inside the barrier (its group's last
+    // arrival), otherwise every workgroup after the barrier, whose release wrote every XCD's
+    // dirty lines back
+    KP& p = params_from(ph);
+    if (light && p.l2_coherent) {
+      grid_barrier(p, ++bar, true, true);
+    } else {
+      launch_barrier(p, bar, light);
+      if (threadIdx.x == 0 && p.l2_coherent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      __syncthreads();
+    }
   }
   layer_phases<D>(ph, wg, run, bar, light);
   return bar | (light ? 0x80000000u : 0u);
