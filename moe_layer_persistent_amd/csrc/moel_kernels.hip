@@ -646,9 +646,9 @@ void bind_base(LayerParams& b, const moel_config* cfg, int nwg, const WsLayout& 
   b.a_split = reinterpret_cast<uint16_t*>(ws + L.as);
   b.aq_buf = reinterpret_cast<float*>(ws + L.aq);
   b.m_buf = reinterpret_cast<float*>(ws + L.m);
-  b.o_op = reinterpret_cast<float*>(ws + L.oop);
+  b.o_op = reinterpret_cast<uint16_t*>(ws + L.oop);
   b.h_op = reinterpret_cast<float*>(ws + L.hop);
-  b.m_op = reinterpret_cast<float*>(ws + L.mop);
+  b.m_op = reinterpret_cast<uint16_t*>(ws + L.mop);
   b.part = reinterpret_cast<float*>(ws + L.part);
   b.part_ss = reinterpret_cast<float*>(ws + L.part_ss);
   {

@@ -94,11 +94,14 @@ struct LayerParams {
   float* aq_buf;    // [16*topk][I] fp4-gathered SwiGLU output (E2M1 x E4M3), debug copy
   float* d_buf;     // [16*topk][P]
   float* m_buf;     // [16][P]
-  // o, h and m again in the operand order of the dense contractions that read them (see
-  // op_index): one 2 KiB block per 32-element k step, lane l's 8 values at 16 l and 1024 + 16 l
-  float* o_op;
+  // o and m again as the ready-made A operands of the dense contractions that read them (see
+  // opsplit_index): per 32-element k step one 2 KiB block, lane l's 8 nearest bf16 values at
+  // byte 16 l and the 8 bf16 of their remainders at 1024 + 16 l; h (read with gamma 2 and its
+  // sums of squares) as fp32 in the same operand order (op_index): lane l's 8 values at 16 l
+  // and 1024 + 16 l
+  uint16_t* o_op;
   float* h_op;
-  float* m_op;
+  uint16_t* m_op;
   // split-K partial sums of a dense phase: [split][row][16 tokens], and each unit's sums of
   // squares of its A rows (sources with stats): [unit][16 tokens]
   float* part;

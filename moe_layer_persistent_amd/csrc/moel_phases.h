@@ -131,22 +131,40 @@ __device__ __forceinline__ size_t op_index(int t, int k) {
   const int r = k & 31;
   return (size_t)(k >> 5) * 512 + ((r >> 4) << 8) + (((r & 15) >> 2) << 6) + 4 * t + (r & 3);
 }
-// An fp32 activation in operand order (lane l reads its own token slot l % 16).
+// Index (in bf16 elements) of the nearest-value half of element (t, k) of a [16][K] activation
+// stored as ready-made A operands: per 32-element k step one 2 KiB block, in which lane
+// l = t + 16 q finds the nearest bf16 values of its 8 elements (k = 4q + 0..3, 16 + 4q + 0..3,
+// the word order of split8) at element 8 l and the bf16 of their remainders 512 elements
+// later.  A wave's load of a step is two contiguous 1 KiB reads and the contraction does no
+// splitting: the producer splits each value once (4 B per element, as in fp32).
+__device__ __forceinline__ size_t opsplit_index(int t, int k) {
+  const int r = k & 31;
+  return (size_t)(k >> 5) * 1024 + 8 * (t + 16 * ((r & 15) >> 2)) + ((r >> 4) << 2) + (r & 3);
+}
+__device__ __forceinline__ void store_opsplit(__attribute__((address_space(1))) uint16_t* base, int t, int k,
+                                              float v) {
+  const size_t i = opsplit_index(t, k);
+  const uint16_t h = f2bf(v);
+  base[i] = h;
+  base[i + 512] = f2bf(v - bf2f(h));
+}
+// An activation stored as ready-made A operands (lane l reads its own token slot l % 16).
 struct AOp {
   static constexpr bool kStats = false;
-  const float* v;
+  const uint16_t* v;
   int T;
   struct Raw {
-    float4 a, b;
+    u32x4 hi, lo;
   };
   __device__ __forceinline__ AOp scalar() const { return AOp{uniform(v), uniform(T)}; }
   __device__ __forceinline__ void fetch(int, int k, Raw& r) const {
-    const float* src = v + (size_t)(k >> 5) * 512 + 4 * lane_id();
-    r.a = ldgf4(src);
-    r.b = ldgf4(src + 256);
+    const uint16_t* src = v + (size_t)(k >> 5) * 1024 + 8 * lane_id();
+    r.hi = ldg16(src);
+    r.lo = ldg16(src + 512);
   }
   __device__ __forceinline__ void finish(const Raw& r, u32x4& hi, u32x4& lo) const {
-    split8(r.a, r.b, hi, lo);
+    hi = r.hi;
+    lo = r.lo;
   }
 };
 // v * gamma from an fp32 activation in operand order, plus the sums of squares (as AGamma).
@@ -597,7 +615,8 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     int ke = kb + p.attn_chunk;
     if (ke > p.attn_lo + p.attn_nkeys) ke = p.attn_lo + p.attn_nkeys;
     const bool act = wv < grp;
-    const int h = g * grp + wv;
+    const int hw = wv;  // query head within the group
+    const int h = g * grp + hw;
     const uint16_t* kg = p.k_cache + (size_t)g * p.kv_cap * D + c8;
     const uint16_t* vg = p.v_cache + (size_t)g * p.kv_cap * D + c8;
     // K/V rows of a sub-chunk into registers; in the last, partial sub-chunk rows past the
@@ -748,13 +767,13 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
       }
     }
     if (act) {
-      auto op = gl(p.attn_o + ((size_t)(it * grp + wv) * kMaxT) * D);
+      auto op = gl(p.attn_o + ((size_t)(it * grp + hw) * kMaxT) * D);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int r = 0; r < 4; ++r) op[(4 * gq + r) * D + 16 * d + tq] = O[d][r];
       if (lane < 16) {
-        auto ml = gl(p.attn_ml + ((size_t)(it * grp + wv) * kMaxT + lane) * 2);
+        auto ml = gl(p.attn_ml + ((size_t)(it * grp + hw) * kMaxT + lane) * 2);
         ml[0] = m_run;
         ml[1] = l_run;
       }
@@ -805,7 +824,7 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
     }
     const float o = num / den;
     if (p.debug_copies) gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
-    gl(p.o_op)[op_index(t, h * p.D + d)] = o;
+    store_opsplit(gl(p.o_op), t, h * p.D + d, o);
   }
 }
 
@@ -1712,7 +1731,7 @@ __device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
     for (int k = 0; k < p.topk; ++k)
       s = fmaf(R.gate[t * p.topk + k], gl(p.d_buf)[(size_t)(t * p.topk + k) * p.P + pc], s);
     if (p.debug_copies) gl(p.m_buf)[(size_t)t * p.P + pc] = s;
-    gl(p.m_op)[op_index(t, pc)] = s;
+    store_opsplit(gl(p.m_op), t, pc, s);
   }
 }
 
