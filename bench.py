@@ -541,7 +541,7 @@ def main():
                    "experts": w.n_experts, "top_k": w.top_k, "pooled": w.pooled, "inter": w.inter,
                    "routing": args.routing, "distinct_experts": U, "weight_copies_rotated": 2,
                    "launch": "plain",
-                   "barrier_acquire": "L1 only (XCD L2s coherent)" if lb.plan.l2_coherent else "L1 + L2 invalidate"},
+                   "barrier_acquire": "L1 only (L2 coherence check passed)" if lb.plan.l2_coherent else "L1 + L2 invalidate"},
         "latency_us": latency,
         "achieved_GBps": round(gbps, 1),
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -586,6 +586,15 @@ def main():
         copy_calibration_run(lb.dev)
     t_cpu = lb.t
     lb.close()
+    if not args.no_extras:
+        # the device's streaming-read bandwidth (16-byte non-temporal loads over 4 GiB, one
+        # workgroup per CU): the practical reference beside the nominal peak
+        buf = torch.empty(4 << 30, dtype=torch.uint8, device=lb.dev)
+        sr = binding.measure_read_bandwidth(buf, reps=10)
+        del buf
+        torch.cuda.empty_cache()
+        result["roofline"]["stream_read_GBps"] = round(sr, 1)
+        result["roofline"]["frac_of_stream_read"] = round(gbps / sr, 4)
     if not args.no_configs and w.name == "swa_fp4":
         result["configs"] = {"swa_fp4": roofline_entry(w, alg_bytes, U, mean_us, traffic)}
         for name in ("global_fp4", "swa_bf16"):

@@ -177,11 +177,14 @@ moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode);
 
 /* Acquire side of the persistent launch's grid barriers.  Not a step of the layer: a
  * property of how the workgroups of one launch see each other's stores.
- *   MOEL_ACQUIRE_AUTO (default): when the plan's device keeps the L2 caches of its XCDs
- *     coherent with each other for hipMalloc memory (checked once per device and process
- *     when a plan is created, see moel_plan_l2_coherent), a barrier invalidates only the
- *     L1 caches; otherwise it runs the memory model's agent-scope acquire, which also
- *     invalidates the L2 and with it the code and weights held there.
+ *   MOEL_ACQUIRE_AUTO (default): when the plan's device keeps a clean copy in one XCD's L2
+ *     coherent with a later write from another XCD for hipMalloc memory (checked once per
+ *     device and process when a plan is created, see moel_plan_l2_coherent), a barrier
+ *     invalidates only the L1 caches; otherwise it runs the memory model's agent-scope
+ *     acquire, which also invalidates the L2 and with it the code and weights held there.
+ *     Within one layer every line read across XCDs is written once, which is what the L1-only
+ *     acquire relies on (a line that an XCD itself wrote earlier in the launch is not kept
+ *     coherent); between the layers of a stack launch every XCD drops its L2's clean lines.
  *   MOEL_ACQUIRE_L2_INVALIDATE: always the agent-scope acquire.
  * Results are bitwise identical in both modes.  Returns MOEL_ERR_ARG for another mode. */
 typedef enum { MOEL_ACQUIRE_AUTO = 0, MOEL_ACQUIRE_L2_INVALIDATE = 1 } moel_acquire_mode;
@@ -289,11 +292,11 @@ typedef struct moel_stack moel_stack;
 /* Registers n_layers layers of the plan's shape to be run one after another with persistent
  * launches that each cover up to 6 layers (moel_stack_decode): layer l + 1 takes layer l's
  * output rows as its input, with a grid barrier instead of a launch boundary between the layers
- * of one launch (orcarouter.ai English post, "Where the kernel boundary sits": the launch
- * boundary is moved so that consecutive layers overlap; "What the 5.9 ms is still spent on": a
- * launch per layer is the remaining fixed cost; on one GPU there is no collective between the
- * layers, so no boundary is needed there).  The layers' launch parameters travel as kernel
- * arguments, 6 layers' worth per launch.
+ * of one launch (orcarouter.ai English post, "Where the kernel boundary sits": the pages move
+ * the launch boundary off the layer boundary; "What the 5.9 ms is still spent on": a launch per
+ * layer is a fixed cost).  Nothing of one layer overlaps the next: at each layer boundary every
+ * XCD drops its L2's clean lines, as a launch boundary does.  The layers' launch parameters
+ * travel as kernel arguments, 6 layers' worth per launch.
  *   weights[l], k_caches[l], v_caches[l], windows[l]: layer l as for moel_layer_decode (HOST
  *     arrays of n_layers entries, copied; the device buffers they point to stay caller-owned and
  *     must outlive the stack).
@@ -345,6 +348,21 @@ moel_status moel_stack_destroy(moel_stack* stack);
 moel_status moel_layer_decode_noalloc(const moel_config* cfg, const moel_weights* w, void* k_cache,
                                       void* v_cache, const float* x, int32_t T, int32_t pos,
                                       int32_t window, float* y, uint32_t* status, void* stream);
+
+/* --- measurement reference ---------------------------------------------------------- */
+
+/* Streaming-read bandwidth of the device, the practical reference beside the nominal HBM peak
+ * for the layer's roofline fraction (not a step of the layer).  One 512-thread workgroup per CU
+ * reads an equal share of buf[0, bytes) in 16-byte non-temporal loads, four per thread in
+ * flight, reps times back to back on `stream` after one untimed pass; *gbps receives
+ * (bytes read per pass) * reps / elapsed, timed with HIP events.  The share of each workgroup
+ * is bytes / (16 * n_CU) 16-byte words, rounded down; the bytes beyond are not read.
+ *   buf: DEVICE pointer, caller-owned, 16-byte aligned; bytes >= 16 * 512 * n_CU.
+ *   reps: 1 .. 1000.  gbps: HOST pointer.
+ * Waits for `stream`.  Errors: MOEL_ERR_ARG (null pointers, reps out of range, too few bytes),
+ * MOEL_ERR_ALIGN, MOEL_ERR_HIP. */
+moel_status moel_measure_read_bandwidth(const void* buf, size_t bytes, int32_t reps, float* gbps,
+                                        void* stream);
 
 #ifdef __cplusplus
 }

@@ -98,6 +98,7 @@ def lib() -> ctypes.CDLL:
             "moel_stack_create": (i32, [vp, i32, P(Weights), vp, vp, vp, P(vp)]),
             "moel_stack_decode": (i32, [vp, vp, i32, i32, vp, vp]),
             "moel_stack_destroy": (i32, [vp]),
+            "moel_measure_read_bandwidth": (i32, [vp, sz, i32, P(ctypes.c_float), vp]),
         }
         for name, (res, args) in sigs.items():
             f = getattr(L, name)
@@ -109,6 +110,16 @@ def lib() -> ctypes.CDLL:
 
 def status_string(code: int) -> str:
     return lib().moel_status_string(code).decode()
+
+
+def measure_read_bandwidth(buf, reps: int = 10, stream=None) -> float:
+    """moel_measure_read_bandwidth over the bytes of the CUDA tensor `buf`: GB/s."""
+    g = ctypes.c_float()
+    st = torch.cuda.current_stream() if stream is None else stream
+    _check(lib().moel_measure_read_bandwidth(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                             int(reps), ctypes.byref(g), ctypes.c_void_p(st.cuda_stream)),
+           "moel_measure_read_bandwidth")
+    return float(g.value)
 
 
 def _check(code: int, what: str):

@@ -231,6 +231,30 @@ __global__ __launch_bounds__(kThreads) void k_stack_fused(StackArgs a_arg) {
 }
 
 // =========================================================================================
+// device: streaming-read reference (moel_measure_read_bandwidth)
+// =========================================================================================
+// Every workgroup reads its share of `per_wg` 16-byte words, four loads per thread in flight.
+// The xor of the loaded words is kept so that the loads stay; it is stored only if it equals
+// a value no sum of the reads is meant to take (the store's condition is never relied on).
+constexpr int kReadDepth = 4;
+__device__ unsigned g_read_sink;
+__global__ __launch_bounds__(kThreads) void k_stream_read(const u32x4* buf, size_t per_wg) {
+  const u32x4* base = buf + (size_t)blockIdx.x * per_wg;
+  unsigned acc = 0;
+  for (size_t i = threadIdx.x; i < per_wg; i += (size_t)kThreads * kReadDepth) {
+    u32x4 v[kReadDepth];
+#pragma unroll
+    for (int d = 0; d < kReadDepth; ++d) {
+      const size_t j = i + (size_t)d * kThreads;
+      v[d] = __builtin_nontemporal_load(base + (j < per_wg ? j : per_wg - 1));
+    }
+#pragma unroll
+    for (int d = 0; d < kReadDepth; ++d) acc ^= v[d][0] ^ v[d][3];
+  }
+  if (acc == 0x9e3779b9u) g_read_sink = acc;
+}
+
+// =========================================================================================
 // device: one kernel per step (ablation / fallback chain)
 // =========================================================================================
 template <int PH, int D>
@@ -1206,6 +1230,39 @@ moel_status moel_layer_decode_noalloc(const moel_config* cfg, const moel_weights
   const hipError_t e = hipLaunchKernel(D == 64 ? fused_fn<64>() : fused_fn<128>(), dim3(sd->nwg), dim3(kThreads),
                                        args, (unsigned)lds_fused_bytes(D), s);
   return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
+moel_status moel_measure_read_bandwidth(const void* buf, size_t bytes, int32_t reps, float* gbps,
+                                        void* stream) {
+  if (buf == nullptr || gbps == nullptr || reps < 1 || reps > 1000) return MOEL_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(buf) & 15u) != 0) return MOEL_ERR_ALIGN;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (!hip_ok(hipGetDevice(&dev)) || !hip_ok(hipGetDeviceProperties(&prop, dev))) return MOEL_ERR_HIP;
+  const int nwg = prop.multiProcessorCount;
+  if (nwg < 1 || bytes < (size_t)16 * kThreads * nwg) return MOEL_ERR_ARG;
+  const size_t per_wg = bytes / 16 / (size_t)nwg;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipEvent_t a = nullptr, b = nullptr;
+  moel_status st = MOEL_ERR_HIP;
+  if (hip_ok(hipEventCreate(&a)) && hip_ok(hipEventCreate(&b))) {
+    const u32x4* p = static_cast<const u32x4*>(buf);
+    hipLaunchKernelGGL(k_stream_read, dim3(nwg), dim3(kThreads), 0, s, p, per_wg);  // untimed
+    bool ok = hip_ok(hipGetLastError()) && hip_ok(hipEventRecord(a, s));
+    for (int r = 0; ok && r < reps; ++r) {
+      hipLaunchKernelGGL(k_stream_read, dim3(nwg), dim3(kThreads), 0, s, p, per_wg);
+      ok = hip_ok(hipGetLastError());
+    }
+    float ms = 0.f;
+    ok = ok && hip_ok(hipEventRecord(b, s)) && hip_ok(hipEventSynchronize(b)) && hip_ok(hipEventElapsedTime(&ms, a, b));
+    if (ok && ms > 0.f) {
+      *gbps = (float)((double)per_wg * 16.0 * nwg * reps / (ms * 1e-3) / 1e9);
+      st = MOEL_OK;
+    }
+  }
+  if (a != nullptr) (void)hipEventDestroy(a);
+  if (b != nullptr) (void)hipEventDestroy(b);
+  return st;
 }
 
 }  // extern "C"

@@ -181,3 +181,14 @@ def test_stack_calls_reject_missing_arguments():
     assert L.moel_stack_create(None, 2, None, None, None, None, ctypes.byref(out)) == binding.MOEL_ERR_ARG
     assert L.moel_stack_decode(None, None, 16, 0, None, None) == binding.MOEL_ERR_ARG
     assert L.moel_stack_destroy(None) == binding.MOEL_ERR_ARG
+
+
+def test_read_bandwidth_reference_rejects_bad_arguments():
+    """moel_measure_read_bandwidth checks its host arguments before any HIP call."""
+    L = binding.lib()
+    g = ctypes.c_float()
+    assert L.moel_measure_read_bandwidth(None, 1 << 20, 10, ctypes.byref(g), None) == binding.MOEL_ERR_ARG
+    assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4096), 1 << 20, 10, None, None) == binding.MOEL_ERR_ARG
+    assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4096), 1 << 20, 0, ctypes.byref(g), None) == binding.MOEL_ERR_ARG
+    assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4096), 1 << 20, 1001, ctypes.byref(g), None) == binding.MOEL_ERR_ARG
+    assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4100), 1 << 20, 10, ctypes.byref(g), None) == binding.MOEL_ERR_ALIGN

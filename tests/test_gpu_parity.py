@@ -354,6 +354,18 @@ def _layer_by_layer(plan, lws, k0, v0, windows, x, pos):
     return cur, kc, vc
 
 
+def test_read_bandwidth_reference():
+    """The streaming-read reference the bench reports beside the nominal peak: a positive rate
+    below the nominal 8 TB/s over 1 GiB, and the too-small buffer rejected."""
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    gbps = binding.measure_read_bandwidth(buf, reps=3)
+    _log(f"streaming read: {gbps:.0f} GB/s")
+    assert 500.0 < gbps < 8000.0
+    with pytest.raises(RuntimeError):
+        binding.measure_read_bandwidth(buf[:4096], reps=1)
+    del buf
+
+
 def test_stack_launch_equals_layer_by_layer():
     """Layers of one shape in one persistent launch (moel_stack_decode; grid barriers between the
     layers) give bitwise the rows and caches of moel_layer_decode called layer by layer: a global
