@@ -406,8 +406,8 @@ def stack_bench(steps: int, warmup: int, copy_calibration: bool = False, unfused
         progress(f"stack: one kernel per step {unfused_us / w.n_layers:.1f} us/layer")
     stack_us, phases = None, {}
     if extras:
-        # the stack through moel_stack_decode: 6 layers per persistent launch (grid barriers
-        # between them)
+        # the stack through moel_stack_decode: binding.STACK_LAYERS_PER_LAUNCH layers per persistent
+        # launch (grid barriers between them)
         stk = binding.Stack(plan, layers, [c[0] for c in caches], [c[1] for c in caches],
                             [w.layer_window(l) for l in range(w.n_layers)])
         ys = torch.empty_like(x0)
@@ -458,7 +458,8 @@ def stack_bench(steps: int, warmup: int, copy_calibration: bool = False, unfused
                                  "tokens_per_s": round(ACCEPTED_PER_STEP / (stack_us * 1e-6), 1),
                                  "achieved_GBps": round(alg / (stack_us * 1e-6) / 1e9, 1),
                                  "frac": round(alg / (stack_us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                                 "note": "moel_stack_decode: 6 layers per persistent launch (11 launches per step)"}
+                                 "note": f"moel_stack_decode: {binding.STACK_LAYERS_PER_LAUNCH} layers per persistent launch "
+                                         f"({-(-w.n_layers // binding.STACK_LAYERS_PER_LAUNCH)} launches per step)"}
         out["phase_us"] = phases
     del layers, caches, bufs
     plan.close()

@@ -36,7 +36,7 @@ extern "C" {
 #endif
 
 #define MOEL_MAX_TOKENS 16
-#define MOEL_ABI_VERSION 5
+#define MOEL_ABI_VERSION 6
 
 typedef enum moel_status {
   MOEL_OK = 0,
@@ -283,20 +283,61 @@ moel_status moel_layer_decode_tree_unfused(moel_plan* plan, const moel_weights* 
                                            int32_t window, const int32_t* parents, float* y,
                                            const moel_debug* dbg, void* stream);
 
+/* --- several requests in one step (batch > 1) ---------------------------------------------- */
+
+#define MOEL_MAX_REQUESTS 8
+
+/* One request of a batched verify step (aicoder.com news item, "Key Takeaways", and orcarouter.ai
+ * English post, "What this number is, and what it is not": the measured path is batch 1, larger
+ * batches are the next step).  Its T tokens are consecutive rows of the step's x and y, the
+ * requests in order.  Its KV cache is slots [kv_base, kv_base + kv_slots) of every kv head of a
+ * pool shared by the batch (a [Hkv, kv_capacity, D] bf16 pair, kv_capacity the plan's); the
+ * request's slot i holds its position i. */
+typedef struct moel_request {
+  int32_t T;         /* >= 1 tokens (a chain: token i attends to the request's tokens 0..i)   */
+  int32_t pos;       /* >= 0 positions already in the request's cache; pos + T <= kv_slots     */
+  int32_t kv_base;   /* >= 0 first pool slot of the request; kv_base + kv_slots <= kv_capacity  */
+  int32_t kv_slots;  /* slots of the request's cache                                            */
+} moel_request;
+
+/* Checks a batch on the host: 1 <= n_requests <= MOEL_MAX_REQUESTS, every request as described
+ * above, the requests' slot ranges pairwise disjoint, the sum of T at most MOEL_MAX_TOKENS, and
+ * n_requests * n_kv_heads attention items no more than the workgroups (workgroups = 0 skips
+ * that check).  MOEL_ERR_ARG on any violation (MOEL_ERR_SHAPE for the last one). */
+moel_status moel_validate_batch(const moel_config* cfg, int32_t n_requests, const moel_request* requests,
+                                int32_t workgroups);
+
+/* One verify step for n_requests requests at once: every request's tokens go through the layer
+ * together (the weights are read once for all of them); attention reads each request's own
+ * cache and writes its new keys and values at pool slots kv_base + pos + i.  Every row's result
+ * is that of moel_layer_decode for its request alone, up to the rounding order of attention
+ * (the key chunks are sized for the whole batch).  window: the layer's, for every request.
+ * k_pool, v_pool: the shared caches; x, y: fp32 [sum of T, hidden] (y must not alias x).
+ * dbg: as for moel_layer_decode, over the step's rows.  Errors: as moel_layer_decode and
+ * moel_validate_batch; nothing is launched and no buffer touched on error. */
+moel_status moel_layer_decode_batch(moel_plan* plan, const moel_weights* w, void* k_pool, void* v_pool,
+                                    const float* x, int32_t n_requests, const moel_request* requests,
+                                    int32_t window, float* y, const moel_debug* dbg, void* stream);
+moel_status moel_layer_decode_batch_unfused(moel_plan* plan, const moel_weights* w, void* k_pool,
+                                            void* v_pool, const float* x, int32_t n_requests,
+                                            const moel_request* requests, int32_t window, float* y,
+                                            const moel_debug* dbg, void* stream);
+
 /* --- a stack of layers in one launch ------------------------------------------------ */
 
 #define MOEL_MAX_STACK_LAYERS 256
+#define MOEL_STACK_LAYERS_PER_LAUNCH 4
 
 typedef struct moel_stack moel_stack;
 
 /* Registers n_layers layers of the plan's shape to be run one after another with persistent
- * launches that each cover up to 6 layers (moel_stack_decode): layer l + 1 takes layer l's
- * output rows as its input, with a grid barrier instead of a launch boundary between the layers
- * of one launch (orcarouter.ai English post, "Where the kernel boundary sits": the pages move
+ * launches that each cover up to MOEL_STACK_LAYERS_PER_LAUNCH layers (moel_stack_decode): layer
+ * l + 1 takes layer l's output rows as its input, with a grid barrier instead of a launch boundary
+ * between the layers of one launch (orcarouter.ai English post, "Where the kernel boundary sits": the pages move
  * the launch boundary off the layer boundary; "What the 5.9 ms is still spent on": a launch per
  * layer is a fixed cost).  Nothing of one layer overlaps the next: at each layer boundary every
  * XCD drops its L2's clean lines, as a launch boundary does.  The layers' launch parameters
- * travel as kernel arguments, 6 layers' worth per launch.
+ * travel as kernel arguments, MOEL_STACK_LAYERS_PER_LAUNCH layers' worth per launch.
  *   weights[l], k_caches[l], v_caches[l], windows[l]: layer l as for moel_layer_decode (HOST
  *     arrays of n_layers entries, copied; the device buffers they point to stay caller-owned and
  *     must outlive the stack).

@@ -33,6 +33,8 @@ MOEL_EXPERT_BF16 = 1
 MOEL_DOWN_INPUT_EXACT = 0
 MOEL_DOWN_INPUT_NVFP4 = 1
 MOEL_N_STAMPS = 32
+MOEL_MAX_REQUESTS = 8
+STACK_LAYERS_PER_LAUNCH = 4  # MOEL_STACK_LAYERS_PER_LAUNCH
 
 
 class MoelError(RuntimeError):
@@ -52,6 +54,18 @@ class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "gamma1", "gamma2", "w_qkv", "w_o", "w_router", "w_pool", "w_unpool", "w_gate", "w_up",
         "w_down", "ts_gate", "ts_up", "ts_down", "ts_act")]
+
+
+class Request(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "pos", "kv_base", "kv_slots")]
+
+
+def _requests(reqs):
+    """A ctypes array of moel_request from (T, pos, kv_base, kv_slots) tuples."""
+    arr = (Request * max(1, len(reqs)))()
+    for i, r in enumerate(reqs):
+        arr[i] = Request(*[int(v) for v in r])
+    return arr
 
 
 class Debug(ctypes.Structure):
@@ -94,6 +108,10 @@ def lib() -> ctypes.CDLL:
             "moel_layer_decode_tree_unfused": (i32, [vp, P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, P(Debug),
                                                      vp]),
             "moel_validate_tree": (i32, [vp, i32]),
+            "moel_validate_batch": (i32, [P(Config), i32, vp, i32]),
+            "moel_layer_decode_batch": (i32, [vp, P(Weights), vp, vp, vp, i32, vp, i32, vp, P(Debug), vp]),
+            "moel_layer_decode_batch_unfused": (i32, [vp, P(Weights), vp, vp, vp, i32, vp, i32, vp, P(Debug),
+                                                      vp]),
             "moel_layer_decode_noalloc": (i32, [P(Config), P(Weights), vp, vp, vp, i32, i32, i32, vp, vp, vp]),
             "moel_stack_create": (i32, [vp, i32, P(Weights), vp, vp, vp, P(vp)]),
             "moel_stack_decode": (i32, [vp, vp, i32, i32, vp, vp]),
@@ -285,6 +303,28 @@ class Plan:
                                       T, pos, window, ctypes.cast(par, ctypes.c_void_p), _ptr(y), dp,
                                       _stream(stream))
         _check(rc, name)
+
+    def layer_decode_batch(self, lw: LayerWeights, k_pool: torch.Tensor, v_pool: torch.Tensor, x: torch.Tensor,
+                           requests, window: int, y: torch.Tensor, dbg: Optional[Dict[str, torch.Tensor]] = None,
+                           fused: bool = True, stream=None) -> None:
+        """One verify step over several requests: `requests` holds (T, pos, kv_base, kv_slots)
+        tuples, whose tokens are consecutive rows of x and y in order."""
+        d = None
+        if dbg is not None:
+            d = Debug(_ptr(dbg.get("expert_idx")), _ptr(dbg.get("gates")), _ptr(dbg.get("router_logits")),
+                      _ptr(dbg.get("timestamps")))
+        arr = _requests(requests)
+        name = "moel_layer_decode_batch" if fused else "moel_layer_decode_batch_unfused"
+        rc = getattr(lib(), name)(self.handle, ctypes.byref(lw.struct), _ptr(k_pool), _ptr(v_pool), _ptr(x),
+                                  len(requests), ctypes.cast(arr, ctypes.c_void_p), window, _ptr(y),
+                                  None if d is None else ctypes.byref(d), _stream(stream))
+        _check(rc, name)
+
+
+def validate_batch(cfg: Config, reqs, workgroups: int = 0) -> int:
+    """moel_validate_batch over (T, pos, kv_base, kv_slots) tuples; returns the status."""
+    arr = _requests(reqs)
+    return lib().moel_validate_batch(ctypes.byref(cfg), len(reqs), ctypes.cast(arr, ctypes.c_void_p), workgroups)
 
 
 def layer_decode_noalloc(cfg: Config, lw: LayerWeights, k_cache: torch.Tensor, v_cache: torch.Tensor,

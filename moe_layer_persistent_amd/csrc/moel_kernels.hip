@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_fused(LayerParams p_arg) {
 // arguments like the single layer's, read through the constant cache; a grid barrier separates
 // consecutive layers.  Kernel arguments, not a table in device memory: every launch gets a fresh
 // argument buffer, so no cache can hold parameters of an earlier launch.
-constexpr int kStackLayersPerLaunch = 6;  // 6 x 640 B of parameters fit the 4 KiB argument segment
+constexpr int kStackLayersPerLaunch = MOEL_STACK_LAYERS_PER_LAUNCH;  // 4 x 936 B fit the 4 KiB argument segment
 struct StackArgs {
   LayerParams layer[kStackLayersPerLaunch];
   int n;
@@ -689,48 +689,98 @@ void bind_base(LayerParams& b, const moel_config* cfg, int nwg, const WsLayout& 
 }
 
 // The per-call launch parameters from the shape's base parameters (validated arguments).
-moel_status fill_call(const moel_config* cfg, const LayerParams& base, int l2_coherent, const moel_weights* w,
-                      void* k_cache, void* v_cache, const float* x, int32_t T, int32_t pos, int32_t window,
-                      const int32_t* parents, float* y, const moel_debug* dbg, LayerParams& p) {
-  moel_status st = moel_validate_call(cfg, w, k_cache, v_cache, x, T, pos, window, y);
+// Launch parameters of one step over n_req requests (one for the single-request calls, whose
+// cache is the whole pool).  parents: the token tree of a single request (NULL = chains).
+moel_status fill_call_batch(const moel_config* cfg, const LayerParams& base, int l2_coherent, const moel_weights* w,
+                            void* k_cache, void* v_cache, const float* x, int32_t n_req, const moel_request* req,
+                            int32_t window, const int32_t* parents, float* y, const moel_debug* dbg, LayerParams& p) {
+  moel_status st = moel_validate_batch(cfg, n_req, req, base.nwg);
   if (st != MOEL_OK) return st;
+  int32_t T = 0;
+  for (int r = 0; r < n_req; ++r) T += req[r].T;
+  // the single-request arguments check the rest (x, y, weights, caches, shapes); pos 0 stands
+  // for the requests' positions, checked above
+  st = moel_validate_call(cfg, w, k_cache, v_cache, x, T, 0, window, y);
+  if (st != MOEL_OK) return st;
+  if (parents != nullptr && n_req != 1) return MOEL_ERR_ARG;
   st = moel_validate_tree(parents, T);
   if (st != MOEL_OK) return st;
   p = base;
   p.l2_coherent = l2_coherent;
   p.T = T;
-  p.pos = pos;
+  p.pos = req[0].pos;
   p.window = window;
-  const int lo = window > 0 ? (pos - window + 1 > 0 ? pos - window + 1 : 0) : 0;
-  const int nkeys = pos + T - lo;
-  int maxc = base.nwg / cfg->n_kv_heads;
-  if (maxc < 1) maxc = 1;
-  // chunks of >= 128 keys, at most nwg / Hkv of them; rounded up to whole 128-key sub-chunks
-  // (a full sub-chunk inside every token's window needs no mask) where that keeps their number
-  int nch = (nkeys + 127) / 128;
-  if (nch > maxc) nch = maxc;
-  if (nch < 1) nch = 1;
-  int chunk = (nkeys + nch - 1) / nch;
-  const int chunk128 = (chunk + 127) / 128 * 128;
-  if ((nkeys + chunk128 - 1) / chunk128 == nch) chunk = chunk128;
-  // token positions and visibility (the chain when parents is NULL); the widest key range is
-  // that of a depth-0 token, so attn_lo covers every token
+  p.n_req = n_req;
   for (int t = 0; t < kMaxT; ++t) {
-    p.tok_depth[t] = 0;
+    p.tok_req[t] = 0;
+    p.tok_pos[t] = 0;
+    p.tok_slot[t] = 0;
     p.tok_sees[t] = 0u;
   }
-  for (int t = 0; t < T; ++t) {
-    const int par = parents ? parents[t] : t - 1;
-    p.tok_depth[t] = par < 0 ? 0 : p.tok_depth[par] + 1;
-    unsigned sees = 0u;
-    for (int i = t; i >= 0; i = parents ? parents[i] : i - 1)
-      if (window == 0 || p.tok_depth[i] > p.tok_depth[t] - window) sees |= 1u << i;
-    p.tok_sees[t] = sees;
+  int keys[MOEL_MAX_REQUESTS];
+  int total_keys = 0, t0 = 0;
+  for (int r = 0; r < n_req; ++r) {
+    const moel_request& q = req[r];
+    p.req_t0[r] = t0;
+    p.req_pos[r] = q.pos;
+    p.req_kvb[r] = q.kv_base;
+    // the widest key range of the request is that of a depth-0 token
+    p.req_lo[r] = window > 0 ? (q.pos - window + 1 > 0 ? q.pos - window + 1 : 0) : 0;
+    keys[r] = q.pos + q.T - p.req_lo[r];
+    total_keys += keys[r];
+    // token positions and visibility (a chain when parents is NULL)
+    int depth[MOEL_MAX_TOKENS];
+    for (int i = 0; i < q.T; ++i) {
+      const int t = t0 + i;
+      const int par = parents ? parents[i] : i - 1;
+      depth[i] = par < 0 ? 0 : depth[par] + 1;
+      unsigned sees = 0u;
+      for (int a = i; a >= 0; a = parents ? parents[a] : a - 1)
+        if (window == 0 || depth[a] > depth[i] - window) sees |= 1u << (t0 + a);
+      p.tok_req[t] = r;
+      p.tok_pos[t] = q.pos + depth[i];
+      p.tok_slot[t] = q.kv_base + q.pos + i;
+      p.tok_sees[t] = sees;
+    }
+    t0 += q.T;
   }
-  p.attn_lo = lo;
-  p.attn_nkeys = nkeys;
+  p.req_t0[n_req] = t0;
+  // key chunks: at least 128 keys, at most nwg / Hkv of them over all requests; rounded up to
+  // whole 128-key sub-chunks (a full sub-chunk inside every token's window needs no mask) where
+  // that keeps their number
+  int maxc = base.nwg / cfg->n_kv_heads;
+  if (maxc < 1) maxc = 1;
+  int nch = (total_keys + 127) / 128;
+  if (nch > maxc) nch = maxc;
+  if (nch < n_req) nch = n_req;
+  int chunk = (total_keys + nch - 1) / nch;
+  auto count = [&](int c) {
+    int n = 0;
+    for (int r = 0; r < n_req; ++r) n += (keys[r] + c - 1) / c;
+    return n;
+  };
+  if (count(chunk) > maxc) {
+    // each request rounds its last chunk up: the smallest chunk whose count fits (count does not
+    // grow with the chunk, and the longest request's key count gives n_req <= maxc chunks)
+    int hi = 1;
+    for (int r = 0; r < n_req; ++r) hi = keys[r] > hi ? keys[r] : hi;
+    int lo = chunk;  // count(lo) > maxc >= count(hi)
+    while (hi - lo > 1) {
+      const int mid = lo + (hi - lo) / 2;
+      (count(mid) > maxc ? lo : hi) = mid;
+    }
+    chunk = hi;
+  }
+  const int chunk128 = (chunk + 127) / 128 * 128;
+  if (count(chunk128) == count(chunk)) chunk = chunk128;
   p.attn_chunk = chunk;
-  p.attn_nchunks = (nkeys + chunk - 1) / chunk;
+  int ch = 0;
+  for (int r = 0; r < n_req; ++r) {
+    p.req_ch0[r] = ch;
+    ch += (keys[r] + chunk - 1) / chunk;
+  }
+  p.req_ch0[n_req] = ch;
+  p.attn_nchunks = ch;
   p.gamma1 = static_cast<const uint16_t*>(w->gamma1);
   p.gamma2 = static_cast<const uint16_t*>(w->gamma2);
   p.w_qkv = static_cast<const uint8_t*>(w->w_qkv);
@@ -831,12 +881,44 @@ bool work_split_fits(const moel_config* cfg, int nwg) {
   return tpe * 17 * MOEL_MAX_TOKENS * cfg->top_k * nwg < ((int64_t)1 << 31);
 }
 
+moel_status fill_call(const moel_config* cfg, const LayerParams& base, int l2_coherent, const moel_weights* w,
+                      void* k_cache, void* v_cache, const float* x, int32_t T, int32_t pos, int32_t window,
+                      const int32_t* parents, float* y, const moel_debug* dbg, LayerParams& p) {
+  if (cfg == nullptr) return MOEL_ERR_ARG;
+  if (T < 1 || T > MOEL_MAX_TOKENS || pos < 0 || window < 0) return MOEL_ERR_ARG;
+  if ((int64_t)pos + T > cfg->kv_capacity) return MOEL_ERR_ARG;
+  const moel_request one{T, pos, 0, cfg->kv_capacity};
+  return fill_call_batch(cfg, base, l2_coherent, w, k_cache, v_cache, x, 1, &one, window, parents, y, dbg, p);
+}
+
 moel_status prepare_call(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,
                          const float* x, int32_t T, int32_t pos, int32_t window, const int32_t* parents,
                          float* y, const moel_debug* dbg, LayerParams& p) {
   if (plan == nullptr) return MOEL_ERR_ARG;
   const int l2c = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
   return fill_call(&plan->cfg, plan->base, l2c, w, k_cache, v_cache, x, T, pos, window, parents, y, dbg, p);
+}
+
+// One step's launch: the persistent kernel, or one kernel per step.
+moel_status launch_fused(moel_plan* plan, LayerParams& p, void* stream) {
+  void* args[] = {&p};
+  const void* fn = plan->cfg.head_dim == 64 ? fused_fn<64>() : fused_fn<128>();
+  hipError_t e = plan->launch_mode == MOEL_LAUNCH_COOPERATIVE
+                     ? hipLaunchCooperativeKernel(fn, dim3(plan->nwg), dim3(kThreads), args,
+                                                  (unsigned)plan->lds_fused, static_cast<hipStream_t>(stream))
+                     : hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_fused,
+                                       static_cast<hipStream_t>(stream));
+  return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
+}
+moel_status launch_unfused(moel_plan* plan, LayerParams& p, void* stream) {
+  void* args[] = {&p};
+  for (int ph = kPhQkv; ph < kNumPhases; ++ph) {  // step 0 is part of step 1
+    const void* fn = plan->cfg.head_dim == 64 ? phase_fn<64>(ph) : phase_fn<128>(ph);
+    hipError_t e = hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_phase[ph],
+                                   static_cast<hipStream_t>(stream));
+    if (!hip_ok(e)) return MOEL_ERR_HIP;
+  }
+  return MOEL_OK;
 }
 
 }  // namespace
@@ -1049,14 +1131,7 @@ moel_status moel_layer_decode_tree(moel_plan* plan, const moel_weights* w, void*
   LayerParams p;
   moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, parents, y, dbg, p);
   if (st != MOEL_OK) return st;
-  void* args[] = {&p};
-  const void* fn = plan->cfg.head_dim == 64 ? fused_fn<64>() : fused_fn<128>();
-  hipError_t e = plan->launch_mode == MOEL_LAUNCH_COOPERATIVE
-                     ? hipLaunchCooperativeKernel(fn, dim3(plan->nwg), dim3(kThreads), args,
-                                                  (unsigned)plan->lds_fused, static_cast<hipStream_t>(stream))
-                     : hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_fused,
-                                       static_cast<hipStream_t>(stream));
-  return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
+  return launch_fused(plan, p, stream);
 }
 
 moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode) {
@@ -1080,14 +1155,32 @@ moel_status moel_layer_decode_tree_unfused(moel_plan* plan, const moel_weights* 
   LayerParams p;
   moel_status st = prepare_call(plan, w, k_cache, v_cache, x, T, pos, window, parents, y, dbg, p);
   if (st != MOEL_OK) return st;
-  void* args[] = {&p};
-  for (int ph = kPhQkv; ph < kNumPhases; ++ph) {  // step 0 is part of step 1
-    const void* fn = plan->cfg.head_dim == 64 ? phase_fn<64>(ph) : phase_fn<128>(ph);
-    hipError_t e = hipLaunchKernel(fn, dim3(plan->nwg), dim3(kThreads), args, (unsigned)plan->lds_phase[ph],
-                                   static_cast<hipStream_t>(stream));
-    if (!hip_ok(e)) return MOEL_ERR_HIP;
-  }
-  return MOEL_OK;
+  return launch_unfused(plan, p, stream);
+}
+
+moel_status moel_layer_decode_batch(moel_plan* plan, const moel_weights* w, void* k_pool, void* v_pool,
+                                    const float* x, int32_t n_requests, const moel_request* requests,
+                                    int32_t window, float* y, const moel_debug* dbg, void* stream) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  LayerParams p;
+  const int l2c = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
+  moel_status st = fill_call_batch(&plan->cfg, plan->base, l2c, w, k_pool, v_pool, x, n_requests, requests,
+                                   window, nullptr, y, dbg, p);
+  if (st != MOEL_OK) return st;
+  return launch_fused(plan, p, stream);
+}
+
+moel_status moel_layer_decode_batch_unfused(moel_plan* plan, const moel_weights* w, void* k_pool,
+                                            void* v_pool, const float* x, int32_t n_requests,
+                                            const moel_request* requests, int32_t window, float* y,
+                                            const moel_debug* dbg, void* stream) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  LayerParams p;
+  const int l2c = plan->acquire_mode == MOEL_ACQUIRE_AUTO && plan->l2_coherent ? 1 : 0;
+  moel_status st = fill_call_batch(&plan->cfg, plan->base, l2c, w, k_pool, v_pool, x, n_requests, requests,
+                                   window, nullptr, y, dbg, p);
+  if (st != MOEL_OK) return st;
+  return launch_unfused(plan, p, stream);
 }
 
 moel_status moel_layer_decode(moel_plan* plan, const moel_weights* w, void* k_cache, void* v_cache,

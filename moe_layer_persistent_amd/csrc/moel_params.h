@@ -44,12 +44,25 @@ struct LayerParams {
   int debug_copies;
   // split-K of the dense phases (1 = none): QKV, o-projection, router/pooler, unpooler
   int sk_qkv, sk_oproj, sk_rp, sk_unpool;
-  // attention decomposition (per call)
-  int attn_lo, attn_nkeys, attn_chunk, attn_nchunks;
-  // the step's tokens as the nodes of a token tree (a chain for the linear verify): token t
-  // is at position pos + tok_depth[t]; bit i of tok_sees[t] is set iff t attends to token
-  // i's key (slot pos + i): i is t or an ancestor of t and within the window of t
-  int tok_depth[MOEL_MAX_TOKENS];
+  // the step's requests (one for moel_layer_decode): request r owns tokens req_t0[r] ..
+  // req_t0[r+1]-1 (req_t0[n_req] = T), has req_pos[r] positions cached at pool slots
+  // req_kvb[r] + 0 .. req_pos[r] - 1, and attends to its keys req_lo[r] .. req_pos[r] + T_r - 1
+  int n_req;
+  int req_t0[MOEL_MAX_REQUESTS + 1];
+  int req_pos[MOEL_MAX_REQUESTS];
+  int req_kvb[MOEL_MAX_REQUESTS];
+  int req_lo[MOEL_MAX_REQUESTS];
+  // attention decomposition (per call): chunks of attn_chunk keys, request r's being the flat
+  // chunks req_ch0[r] .. req_ch0[r+1]-1 (attn_nchunks = req_ch0[n_req] in all)
+  int attn_chunk, attn_nchunks;
+  int req_ch0[MOEL_MAX_REQUESTS + 1];
+  // the step's tokens as the nodes of token trees (a chain per request for the linear verify):
+  // token t of request tok_req[t] is at position tok_pos[t] (RoPE) and writes its key and value
+  // at pool slot tok_slot[t]; bit i of tok_sees[t] is set iff t attends to token i's key: i is t
+  // or an ancestor of t in the same request and within the window of t
+  int tok_req[MOEL_MAX_TOKENS];
+  int tok_pos[MOEL_MAX_TOKENS];
+  int tok_slot[MOEL_MAX_TOKENS];
   unsigned tok_sees[MOEL_MAX_TOKENS];
   // weights (packed)
   const uint16_t* gamma1;

@@ -533,8 +533,8 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
                   const float a = L.fin[(j * 16 + 2 * pr) * kMaxT + t] * L.rstd[t];
                   const float b = L.fin[(j * 16 + 2 * pr + 1) * kMaxT + t] * L.rstd[t];
                   const int head = R / p.D, i = (R % p.D) >> 1;
-                  const int ps = p.pos + t;                  // cache slot
-                  const int rp = p.pos + p.tok_depth[t];     // position (RoPE)
+                  const int ps = p.tok_slot[t];  // pool slot
+                  const int rp = p.tok_pos[t];   // position (RoPE)
                   if (head < p.Hq + p.Hkv) {
                     const float c = gl(p.rope_cos)[(size_t)(rp - p.rope_row0) * half + i];
                     const float s = gl(p.rope_sin)[(size_t)(rp - p.rope_row0) * half + i];
@@ -610,15 +610,20 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   constexpr int RSTEP = kThreads / (D / 8);
   const int row0 = threadIdx.x / (D / 8), c8 = (threadIdx.x % (D / 8)) * 8;
   for (int it = wg; it < nitems; it += p.nwg) {
-    const int g = it % p.Hkv, c = it / p.Hkv;
-    const int kb = p.attn_lo + c * p.attn_chunk;
+    const int g = it % p.Hkv, cc = it / p.Hkv;  // kv head, flat chunk
+    // the chunk's request rq and its chunk c within the request (uniform)
+    int rq = 0;
+    while (rq + 1 < p.n_req && cc >= p.req_ch0[rq + 1]) ++rq;
+    const int c = cc - p.req_ch0[rq];
+    const int pos_r = p.req_pos[rq], t0_r = p.req_t0[rq], T_r = p.req_t0[rq + 1] - t0_r;
+    const int kb = p.req_lo[rq] + c * p.attn_chunk;  // keys are the request's positions
     int ke = kb + p.attn_chunk;
-    if (ke > p.attn_lo + p.attn_nkeys) ke = p.attn_lo + p.attn_nkeys;
+    if (ke > pos_r + T_r) ke = pos_r + T_r;
     const bool act = wv < grp;
     const int hw = wv;  // query head within the group
     const int h = g * grp + hw;
-    const uint16_t* kg = p.k_cache + (size_t)g * p.kv_cap * D + c8;
-    const uint16_t* vg = p.v_cache + (size_t)g * p.kv_cap * D + c8;
+    const uint16_t* kg = p.k_cache + ((size_t)g * p.kv_cap + p.req_kvb[rq]) * D + c8;
+    const uint16_t* vg = p.v_cache + ((size_t)g * p.kv_cap + p.req_kvb[rq]) * D + c8;
     // K/V rows of a sub-chunk into registers; in the last, partial sub-chunk rows past the
     // chunk end repeat its last key (never visible, so never weighted)
     u32x4 kr[NCH], vr[NCH];
@@ -661,10 +666,12 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     for (int d = 0; d < ND; ++d) O[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     // this lane's token: its position, which of the step's keys it sees, and the first cached
     // key inside its window
-    const int ptok = p.pos + p.tok_depth[tqc];
+    const int ptok = p.tok_pos[tqc];
     const unsigned sees = p.tok_sees[tqc];
     const int lo_t = p.window == 0 ? -0x7fffffff - 1 : ptok - p.window + 1;
-    const bool tok_ok = tq < p.T;
+    // this lane's token takes part in the item: a token of the step, of the item's request
+    const bool tok_ok = tq < p.T && p.tok_req[tqc] == rq;
+    const bool multi = p.n_req > 1;
     for (int sb = kb; sb < ke; sb += SK) {
       lds_barrier();  // the previous sub-chunk's LDS reads are done
 #pragma unroll
@@ -699,21 +706,30 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
         // token's window, for a key of the step, bit j - pos of the token's set; computed
         // without branches (selects on every element)
         float mx = NEG;
-        const bool all_vis = sb + SK <= ke && sb + SK <= p.pos && (p.window == 0 || sb > p.pos + p.T - 1 - p.window);
-        if (all_vis) {
+        const bool all_vis = sb + SK <= ke && sb + SK <= pos_r && (p.window == 0 || sb > pos_r + T_r - 1 - p.window);
+        if (all_vis && !multi) {
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) mx = fmaxf(mx, S[kt][r]);
+        } else if (all_vis) {  // every key visible to the request's tokens, none to the others
+#pragma unroll
+          for (int kt = 0; kt < NKT; ++kt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float v = tok_ok ? S[kt][r] : NEG;
+              S[kt][r] = v;
+              mx = fmaxf(mx, v);
+            }
         } else {
 #pragma unroll
           for (int kt = 0; kt < NKT; ++kt)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
               const int j = sb + kt * 16 + 4 * gq + r;
-              const int js = j - p.pos;
+              const int js = j - pos_r;  // < 0: cached; else the request's token t0_r + js
               const unsigned in_win = (unsigned)(j >= lo_t);
-              const unsigned seen = (sees >> (js & 31)) & 1u;
+              const unsigned seen = (sees >> ((t0_r + js) & 31)) & 1u;
               const unsigned vis = (unsigned)tok_ok & (unsigned)(j < ke) & (js < 0 ? in_win : seen);
               const float v = vis ? S[kt][r] : NEG;
               S[kt][r] = v;

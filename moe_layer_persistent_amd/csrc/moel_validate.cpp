@@ -108,3 +108,24 @@ moel_status moel_validate_tree(const int32_t* parents, int32_t T) {
     if (parents[t] < -1 || parents[t] >= t) return MOEL_ERR_ARG;
   return MOEL_OK;
 }
+
+extern "C" moel_status moel_validate_batch(const moel_config* cfg, int32_t n_requests, const moel_request* requests,
+                                           int32_t workgroups) {
+  if (cfg == nullptr || requests == nullptr || n_requests < 1 || n_requests > MOEL_MAX_REQUESTS) return MOEL_ERR_ARG;
+  int64_t total = 0;
+  for (int32_t r = 0; r < n_requests; ++r) {
+    const moel_request& q = requests[r];
+    if (q.T < 1 || q.pos < 0 || q.kv_base < 0 || q.kv_slots < 1) return MOEL_ERR_ARG;
+    if ((int64_t)q.pos + q.T > q.kv_slots) return MOEL_ERR_ARG;
+    if ((int64_t)q.kv_base + q.kv_slots > cfg->kv_capacity) return MOEL_ERR_ARG;
+    total += q.T;
+    for (int32_t s = 0; s < r; ++s) {  // slot ranges pairwise disjoint
+      const moel_request& o = requests[s];
+      if (q.kv_base < (int64_t)o.kv_base + o.kv_slots && o.kv_base < (int64_t)q.kv_base + q.kv_slots)
+        return MOEL_ERR_ARG;
+    }
+  }
+  if (total > MOEL_MAX_TOKENS) return MOEL_ERR_ARG;
+  if (workgroups > 0 && (int64_t)n_requests * cfg->n_kv_heads > workgroups) return MOEL_ERR_SHAPE;
+  return MOEL_OK;
+}

@@ -89,6 +89,70 @@ class GpuRun:
         return dict(y=y, k_cache=kc, v_cache=vc, T=T, pos=pos, x=x, parents=parents, **dbg)
 
 
+class RequestView:
+    """One request of a batched step, seen as a single-request run: its cache is its slot range
+    of the pool and its rows of the step's scratch start at row0."""
+
+    def __init__(self, run: GpuRun, req, row0: int):
+        T, pos, kvb, slots = req
+        self.w = run.w
+        self.t = run.t
+        self.window = run.window
+        self.plan = run.plan
+        self.k0 = run.k0[:, kvb:kvb + slots].contiguous()
+        self.v0 = run.v0[:, kvb:kvb + slots].contiguous()
+        self.row0 = row0
+
+    @staticmethod
+    def out_of(out: Dict, req, row0: int) -> Dict:
+        T, pos, kvb, slots = req
+        rows = slice(row0, row0 + T)
+        o = {k: out[k][rows] for k in ("y", "x", "expert_idx", "gates", "router_logits")}
+        o["k_cache"] = out["k_cache"][:, kvb:kvb + slots].contiguous()
+        o["v_cache"] = out["v_cache"][:, kvb:kvb + slots].contiguous()
+        o.update(T=T, pos=pos, parents=None)
+        return o
+
+
+def run_batch(run: GpuRun, reqs, fused: bool = True, x: Optional[torch.Tensor] = None) -> Dict:
+    """One batched step over (T, pos, kv_base, kv_slots) requests on fresh copies of the pool."""
+    w = run.w
+    T = sum(r[0] for r in reqs)
+    x = run.t["x"][:T].contiguous() if x is None else x
+    kc, vc = run.fresh_caches()
+    y = torch.full((T, w.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    dbg = {
+        "expert_idx": torch.full((T, w.top_k), -1, dtype=torch.int32, device="cuda"),
+        "gates": torch.zeros((T, w.top_k), dtype=torch.float32, device="cuda"),
+        "router_logits": torch.zeros((T, w.n_experts), dtype=torch.float32, device="cuda"),
+    }
+    run.plan.layer_decode_batch(run.lw, kc, vc, x, reqs, run.window, y, dbg=dbg, fused=fused)
+    torch.cuda.synchronize()
+    st = run.plan.status()
+    assert st == binding.MOEL_OK, binding.status_string(st)
+    return dict(y=y, k_cache=kc, v_cache=vc, x=x, **dbg)
+
+
+def check_batch_against_oracle(run: GpuRun, out: Dict, reqs, moe_tokens=None) -> List[dict]:
+    """Every request of a batched step against the oracle run on that request alone, and the
+    pool outside every request's slot range bit-identical.  moe_tokens: per request, as for
+    check_against_oracle (None = all)."""
+    keep = torch.ones(run.k0.shape[1], dtype=torch.bool, device=run.k0.device)
+    for (T, pos, kvb, slots) in reqs:
+        keep[kvb:kvb + slots] = False
+    for name, c_out, c_in in (("k", out["k_cache"], run.k0), ("v", out["v_cache"], run.v0)):
+        assert torch.equal(c_out[:, keep].view(torch.int16), c_in[:, keep].view(torch.int16)), \
+            f"{name} pool changed outside the requests' slots"
+    reps, row0 = [], 0
+    for r in reqs:
+        view = RequestView(run, r, row0)
+        rep = {}
+        check_against_oracle(view, RequestView.out_of(out, r, row0), moe_tokens=moe_tokens, report=rep)
+        reps.append(rep)
+        row0 += r[0]
+    return reps
+
+
 def _f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().to("cpu").double().numpy()
 
@@ -126,12 +190,13 @@ def device_down_input(run: GpuRun, gpu_idx: np.ndarray, T: int) -> np.ndarray:
     """[T, k, inter] the device's fp4-gathered down input of every slot (value x tensor scale)."""
     w = run.w
     k, I = w.top_k, w.inter
+    r0 = getattr(run, "row0", 0)
     aq = run.plan.scratch("aq").view(16 * k, I).cpu().numpy().astype(np.float64)
     act = run.t["act_ts"].cpu().numpy()
     out = np.empty((T, k, I))
     for t in range(T):
         for kk in range(k):
-            out[t, kk] = aq[t * k + kk] * float(np.float32(act[int(gpu_idx[t, kk])]))
+            out[t, kk] = aq[(r0 + t) * k + kk] * float(np.float32(act[int(gpu_idx[t, kk])]))
     return out
 
 
@@ -146,10 +211,11 @@ def check_fp4_gather(run: GpuRun, gpu_idx: np.ndarray, ref: Dict, toks: Sequence
     act = run.t["act_ts"].cpu().numpy()
     ex = expert_fn(run)
     plc, r = w.pooled // w.n_shards, w.shard_rank
+    r0 = getattr(run, "row0", 0)
     agree, d_err, a_err = [], 0.0, 0.0
     for t in toks:
         for kk in range(k):
-            slot, e = t * k + kk, int(gpu_idx[t, kk])
+            slot, e = (r0 + t) * k + kk, int(gpu_idx[t, kk])
             a_ref = ref["a"][t, kk]
             err = float(np.abs(a_dev[slot] - a_ref).max() / (np.abs(a_ref).max() + 1e-30))
             assert err <= 1e-3, ("SwiGLU output vs oracle", t, kk, err)
@@ -267,7 +333,8 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
     # intermediate activations (max error relative to the largest exact value)
     inter = {}
     for name, key in (("q", "q"), ("o", "o"), ("h", "h"), ("pl", "pl")):
-        got_i = run.plan.scratch(name).view(16, -1)[:T].cpu().numpy().astype(np.float64)
+        r0 = getattr(run, "row0", 0)
+        got_i = run.plan.scratch(name).view(16, -1)[r0:r0 + T].cpu().numpy().astype(np.float64)
         want = ref[key].reshape(T, -1)
         inter[name] = float(np.abs(got_i - want).max() / (np.abs(want).max() + 1e-30))
         need(inter[name] <= REL_ERR_MAX[name], f"{name} relative error {inter[name]} > {REL_ERR_MAX[name]}")

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.moel_abi_version() == 5
+    assert L.moel_abi_version() == 6
 
 
 def test_plan_options_reject_a_missing_plan():
@@ -192,3 +192,42 @@ def test_read_bandwidth_reference_rejects_bad_arguments():
     assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4096), 1 << 20, 0, ctypes.byref(g), None) == binding.MOEL_ERR_ARG
     assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4096), 1 << 20, 1001, ctypes.byref(g), None) == binding.MOEL_ERR_ARG
     assert L.moel_measure_read_bandwidth(ctypes.c_void_p(4100), 1 << 20, 10, ctypes.byref(g), None) == binding.MOEL_ERR_ALIGN
+
+
+def test_validate_batch():
+    c = _cfg()  # kv_capacity 8208, 8 kv heads
+    ok = binding.MOEL_OK
+    v = lambda reqs, wg=0: binding.validate_batch(c, reqs, wg)
+    assert v([(5, 100, 0, 1000), (7, 0, 1000, 1000), (4, 990, 2000, 1000)]) == ok
+    assert v([(16, 8192, 0, 8208)]) == ok                          # one request over the whole pool
+    assert v([(1, 0, 8 * i, 8) for i in range(8)]) == ok           # eight requests
+    assert v([]) == binding.MOEL_ERR_ARG                           # no request
+    assert v([(1, 0, 8 * i, 8) for i in range(9)]) == binding.MOEL_ERR_ARG   # more than 8
+    assert v([(0, 10, 0, 100)]) == binding.MOEL_ERR_ARG            # T = 0
+    assert v([(2, -1, 0, 100)]) == binding.MOEL_ERR_ARG            # pos < 0
+    assert v([(2, 0, -1, 100)]) == binding.MOEL_ERR_ARG            # kv_base < 0
+    assert v([(2, 0, 0, 0)]) == binding.MOEL_ERR_ARG               # no slots
+    assert v([(2, 99, 0, 100)]) == binding.MOEL_ERR_ARG            # pos + T > kv_slots
+    assert v([(2, 98, 0, 100)]) == ok
+    assert v([(2, 0, 8200, 9)]) == binding.MOEL_ERR_ARG            # past kv_capacity
+    assert v([(2, 0, 8199, 9)]) == ok
+    assert v([(2, 0, 0, 100), (2, 0, 99, 100)]) == binding.MOEL_ERR_ARG   # slot ranges overlap
+    assert v([(2, 0, 100, 100), (2, 0, 0, 101)]) == binding.MOEL_ERR_ARG  # overlap, other order
+    assert v([(2, 0, 0, 100), (2, 0, 100, 100)]) == ok                    # adjacent
+    assert v([(9, 0, 0, 100), (8, 0, 100, 100)]) == binding.MOEL_ERR_ARG  # 17 tokens
+    assert v([(8, 0, 0, 100), (8, 0, 100, 100)]) == ok
+    reqs = [(1, 0, 8 * i, 8) for i in range(3)]
+    assert v(reqs, 24) == ok                                       # 3 x 8 attention items
+    assert v(reqs, 23) == binding.MOEL_ERR_SHAPE
+
+
+def test_batch_calls_reject_bad_requests_before_any_launch():
+    # no plan: rejected before anything else; a NULL request array: rejected by validation
+    L = binding.lib()
+    w = _fake_weights()
+    vp = ctypes.c_void_p
+    reqs = binding._requests([(4, 0, 0, 100)])
+    for name in ("moel_layer_decode_batch", "moel_layer_decode_batch_unfused"):
+        f = getattr(L, name)
+        assert f(None, ctypes.byref(w), vp(0x100000), vp(0x200000), vp(0x300000), 1,
+                 ctypes.cast(reqs, vp), 0, vp(0x400000), None, None) == binding.MOEL_ERR_ARG

@@ -277,6 +277,96 @@ def test_invalid_calls_launch_nothing():
     assert torch.equal(kc.view(torch.int16), run.k0.view(torch.int16))
 
 
+# ---------------------------------------------------------------- batched verify
+# (T, pos, kv_base, kv_slots) per request: three requests of 16 tokens in all over an 800-slot
+# pool, with different depths and bases
+BATCH3 = [(5, 100, 0, 300), (7, 250, 300, 400), (4, 30, 700, 100)]
+# eight requests of one to three tokens
+BATCH8 = [(t, 10 + 11 * i, 100 * i, 100) for i, t in enumerate([1, 2, 3, 1, 2, 3, 2, 2])]
+
+
+def _batch_workload(**kw):
+    base = dict(T=16, pos=784, n_experts=32, top_k=8, pooled=512, inter=512)
+    base.update(kw)
+    return synth.small_workload(**base)
+
+
+@pytest.mark.parametrize("reqs,window", [(BATCH3, 0), (BATCH3, 40), (BATCH3, 6), (BATCH8, 0), (BATCH8, 5)],
+                         ids=["three_global", "three_window", "three_short_window", "eight_global",
+                              "eight_window"])
+def test_batch_matches_oracle_per_request(reqs, window):
+    run = harness.GpuRun(_batch_workload(window=window))
+    _log(f"batch {reqs} window {window}")
+    out = harness.run_batch(run, reqs)
+    reps = harness.check_batch_against_oracle(run, out, reqs)
+    _log(f"batch: {[{k: r[k] for k in ('max_abs', 'min_cos', 'logit_err')} for r in reps]}")
+    # the one-kernel-per-step chain gives the same bytes
+    b = harness.run_batch(run, reqs, fused=False)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(out[k], b[k]), k
+
+
+def test_batch_key_chunks_sized_for_the_whole_batch():
+    # 8 kv heads leave 32 key chunks for the batch: three requests of ~1600 keys split into
+    # chunks of 151 keys (150 would give 33 chunks)
+    w = _batch_workload(hidden=512, n_q_heads=16, n_kv_heads=8, head_dim=64, pos=4784, window=0)
+    reqs = [(5, 1590, 0, 1600), (6, 1500, 1600, 1600), (5, 1580, 3200, 1600)]
+    run = harness.GpuRun(w)
+    out = harness.run_batch(run, reqs)
+    reps = harness.check_batch_against_oracle(run, out, reqs)
+    _log(f"batch chunks: {[{k: r[k] for k in ('max_abs', 'min_cos', 'logit_err')} for r in reps]}")
+
+
+def test_single_request_batch_is_layer_decode():
+    w = _batch_workload(pos=700, window=128)
+    run = harness.GpuRun(w)
+    a = run.run(fused=True)
+    b = harness.run_batch(run, [(w.T, w.pos, 0, w.kv_capacity)])
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(a[k], b[k]), k
+
+
+def test_batch_rows_do_not_depend_on_the_other_requests():
+    """A request's rows and cache writes are those it gets when the other requests' tokens
+    change (their inputs, their caches' contents), up to attention's rounding order: its rows
+    meet the oracle bar either way and its written K/V are bitwise equal."""
+    run = harness.GpuRun(_batch_workload(window=40))
+    a = harness.run_batch(run, BATCH3)
+    x2 = run.t["x"][:16].clone()
+    x2[5:] = torch.randn_like(x2[5:])          # requests 1 and 2 change, request 0 keeps its rows
+    b = harness.run_batch(run, BATCH3, x=x2)
+    T0, pos0, kvb0, _ = BATCH3[0]
+    assert _same_bytes(a["k_cache"][:, kvb0 + pos0:kvb0 + pos0 + T0], b["k_cache"][:, kvb0 + pos0:kvb0 + pos0 + T0])
+    assert _same_bytes(a["expert_idx"][:T0], b["expert_idx"][:T0])
+    d = float((a["y"][:T0] - b["y"][:T0]).abs().max())
+    assert d <= 1e-5, d
+
+
+def test_invalid_batches_launch_nothing():
+    run = harness.GpuRun(_batch_workload(window=0))
+    kc, vc = run.fresh_caches()
+    y = torch.full((16, run.w.hidden), 7.0, dtype=torch.float32, device="cuda")
+    for reqs in ([], [(4, 0, 0, 100), (4, 0, 50, 100)], [(4, 98, 0, 100)], [(9, 0, 0, 100), (8, 0, 100, 100)]):
+        with pytest.raises(binding.MoelError) as ei:
+            run.plan.layer_decode_batch(run.lw, kc, vc, run.t["x"], reqs, 0, y)
+        assert ei.value.code == binding.MOEL_ERR_ARG
+    torch.cuda.synchronize()
+    assert torch.all(y == 7.0)
+    assert torch.equal(kc.view(torch.int16), run.k0.view(torch.int16))
+
+
+def test_full_width_batch_matches_oracle():
+    # swa_fp4 with its 8208-slot pool shared by three requests of 4, 4 and 8 tokens
+    w = synth.WORKLOADS["swa_fp4"]
+    reqs = [(4, 2500, 0, 2600), (4, 1900, 2600, 2000), (8, 3500, 4600, 3608)]
+    _log(f"full batch {reqs}: generating")
+    run = harness.GpuRun(w)
+    out = harness.run_batch(run, reqs)
+    _log("full batch: oracle")
+    reps = harness.check_batch_against_oracle(run, out, reqs)
+    _log(f"full batch: {reps}")
+
+
 # ---------------------------------------------------------------- full-width workloads
 FULL = ["swa_fp4", "global_fp4", "swa_bf16", "swa_fp4_a4"]
 
