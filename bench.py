@@ -12,7 +12,8 @@ Beside the headline workload (`value`, `roofline`), the line carries every other
 configuration timed the same way, each with its own algorithmic bytes and fraction of the
 HBM peak (`configs`), the 62-layer stack share (`stack`, fused and one kernel per step),
 the headline layer with the pages' routing concentration (`routing_pages`, about 49 distinct
-experts), and the CPU oracle timed on
+experts), the same 16 rows as four requests of four tokens in one batched step
+(`batched_verify`), and the CPU oracle timed on
 a bounded sample of the headline step (`cpu_baseline`).
 """
 from __future__ import annotations
@@ -32,9 +33,11 @@ PHASES = ["norm1", "qkv_rope_kv", "attention", "attn_merge", "o_proj", "router_p
           "experts_down", "combine", "unpool"]
 
 
-def algorithmic_bytes(w, idx, pos, window, T):
+def algorithmic_bytes(w, idx, pos, window, T, requests=None):
     """Bytes the step must move at least once: every weight byte it uses (dense weights, the
-    routed experts' matrices), the visible KV window, x, y and the KV writes."""
+    routed experts' matrices), the visible KV window, x, y and the KV writes.  requests: the
+    (T, pos, kv_base, kv_slots) requests of a batched step, each reading its own window (pos and
+    T are then ignored)."""
     H, D, Hq, Hkv, P, I = w.hidden, w.head_dim, w.n_q_heads, w.n_kv_heads, w.pooled, w.inter
     dense = 2 * (w.qkv_rows * H + H * Hq * D + w.n_experts * H + P * H + H * P + 2 * H)
     if w.expert_dtype == 0:
@@ -43,8 +46,12 @@ def algorithmic_bytes(w, idx, pos, window, T):
         per_elem = 2.0
     expert = per_elem * (2 * w.inter_local * P + w.pooled_local * I)
     U = len(set(int(e) for e in idx.reshape(-1)))
-    lo = max(0, pos - window + 1) if window > 0 else 0
-    kv_read = (pos + T - lo) * Hkv * D * 2 * 2
+    reqs = [(T, pos)] if requests is None else [(r[0], r[1]) for r in requests]
+    kv_read = 0
+    for T_r, pos_r in reqs:
+        lo = max(0, pos_r - window + 1) if window > 0 else 0
+        kv_read += (pos_r + T_r - lo) * Hkv * D * 2 * 2
+    T = sum(r[0] for r in reqs)
     io = T * H * 4 * 2 + T * Hkv * D * 2 * 2
     return dense + U * expert + kv_read + io, U
 
@@ -174,35 +181,46 @@ class LayerBench:
                 i += 1
             torch.cuda.synchronize()
 
-    def route(self, x=None):
+    def route(self, x=None, requests=None):
         """Runs one step with debug outputs; returns the selected experts [T, k]."""
         torch = self.torch
         idx = torch.zeros((self.w.T, self.w.top_k), dtype=torch.int32, device=self.dev)
-        self.plan.layer_decode(self.copies[0], self.kc, self.vc, self.x if x is None else x, self.w.pos,
-                               self.window, self.y, dbg={"expert_idx": idx}, stream=self.stream)
+        if requests is None:
+            self.plan.layer_decode(self.copies[0], self.kc, self.vc, self.x if x is None else x, self.w.pos,
+                                   self.window, self.y, dbg={"expert_idx": idx}, stream=self.stream)
+        else:
+            self.plan.layer_decode_batch(self.copies[0], self.kc, self.vc, self.x if x is None else x, requests,
+                                         self.window, self.y, dbg={"expert_idx": idx}, stream=self.stream)
         torch.cuda.synchronize()
         st = self.plan.status()
         assert st == 0, self.binding.status_string(st)
         return idx.cpu().numpy()
 
-    def timed(self, steps, warmup, fused=True, parents=None, pl=None, cps=None, x=None):
+    def timed(self, steps, warmup, fused=True, parents=None, pl=None, cps=None, x=None, requests=None):
         """Back-to-back launches between two events on the launch stream: the average launch
-        duration (us) over the timed region, and the host wall time (s)."""
+        duration (us) over the timed region, and the host wall time (s).  requests: time the
+        batched step over these (T, pos, kv_base, kv_slots) requests instead."""
         torch = self.torch
         pl = self.plan if pl is None else pl
         cps = self.copies if cps is None else cps
         x = self.x if x is None else x
         w = self.w
+
+        def launch(i):
+            if requests is None:
+                pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, w.pos, self.window, self.y, fused=fused,
+                                stream=self.stream, parents=parents)
+            else:
+                pl.layer_decode_batch(cps[i % len(cps)], self.kc, self.vc, x, requests, self.window, self.y,
+                                      fused=fused, stream=self.stream)
         for i in range(warmup):
-            pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, w.pos, self.window, self.y, fused=fused,
-                            stream=self.stream, parents=parents)
+            launch(i)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         a.record(self.stream)
         for i in range(steps):
-            pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, w.pos, self.window, self.y, fused=fused,
-                            stream=self.stream, parents=parents)
+            launch(i)
         b.record(self.stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -571,6 +589,16 @@ def main():
         lb.plan.set_acquire(binding.MOEL_ACQUIRE_AUTO)
         # the same step as a token-tree verify, which moves only positions and the attention mask
         latency["token_tree_verify_back_to_back"] = round(lb.timed(max(5, args.steps // 2), 2, parents=TREE16)[0], 2)
+        # several requests in one step: the 16 rows as 4 requests of 4 tokens, each with its own
+        # history in a quarter of the cache pool (the same weights read once for all of them)
+        quarter = w.kv_capacity // 4
+        hist = min(w.pos, quarter - 4)
+        reqs_b = [(4, hist, r * quarter, quarter) for r in range(4)]
+        idx_b = lb.route(requests=reqs_b)
+        alg_b, U_b = algorithmic_bytes(w, idx_b, 0, lb.window, 0, requests=reqs_b)
+        us_b, _ = lb.timed(max(5, args.steps // 2), 2, requests=reqs_b)
+        result["batched_verify"] = dict(roofline_entry(w, alg_b, U_b, us_b),
+                                        requests="4 x (T 4, history %d, %d-slot pool quarter)" % (hist, quarter))
         # the pages' routing concentration (a shared component in every token, tuned so that the
         # 16 tokens use about 49 distinct experts): the same weights and caches, other input rows
         if args.routing == "iid":

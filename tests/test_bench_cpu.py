@@ -51,3 +51,16 @@ def test_counter_traffic_only_for_the_sources_it_was_measured_on(monkeypatch):
     assert t is not None and t["bytes_per_launch"] == float(kv["traffic_bytes_per_launch"])
     monkeypatch.setattr(bench, "kernel_source_digest", lambda: "0" * 64)
     assert bench.measured_traffic("swa_fp4") is None
+
+
+def test_batched_algorithmic_bytes_add_each_requests_window():
+    import numpy as np
+    w = synth.WORKLOADS["swa_fp4"]
+    idx = np.arange(16 * w.top_k).reshape(16, w.top_k) % w.n_experts
+    one, U = bench.algorithmic_bytes(w, idx, 2048, w.window, 16)
+    reqs = [(4, 2048, r * 2052, 2052) for r in range(4)]
+    four, U4 = bench.algorithmic_bytes(w, idx, 0, w.window, 0, requests=reqs)
+    kv_row = w.n_kv_heads * w.head_dim * 2 * 2          # one key and one value of every kv head
+    # one request at history 2048 reads 2048 - 1 + 16 rows, each of four reads 2048 - 1 + 4
+    assert U == U4
+    assert four - one == kv_row * (4 * (2047 + 4) - (2047 + 16))
