@@ -13,7 +13,7 @@ configuration timed the same way, each with its own algorithmic bytes and fracti
 HBM peak (`configs`), the 62-layer stack share (`stack`, fused and one kernel per step),
 the headline layer with the pages' routing concentration (`routing_pages`, about 49 distinct
 experts), the same 16 rows as four requests of four tokens in one batched step
-(`batched_verify`), and the CPU oracle timed on
+(`batched_verify`), a 32-token step (`verify_32_tokens`), and the CPU oracle timed on
 a bounded sample of the headline step (`cpu_baseline`).
 """
 from __future__ import annotations
@@ -181,37 +181,44 @@ class LayerBench:
                 i += 1
             torch.cuda.synchronize()
 
-    def route(self, x=None, requests=None):
+    def route(self, x=None, requests=None, pos=None):
         """Runs one step with debug outputs; returns the selected experts [T, k]."""
         torch = self.torch
-        idx = torch.zeros((self.w.T, self.w.top_k), dtype=torch.int32, device=self.dev)
+        x = self.x if x is None else x
+        T = x.shape[0] if requests is None else sum(r[0] for r in requests)
+        idx = torch.zeros((T, self.w.top_k), dtype=torch.int32, device=self.dev)
+        y = torch.empty((T, self.w.hidden), dtype=torch.float32, device=self.dev)
         if requests is None:
-            self.plan.layer_decode(self.copies[0], self.kc, self.vc, self.x if x is None else x, self.w.pos,
-                                   self.window, self.y, dbg={"expert_idx": idx}, stream=self.stream)
+            self.plan.layer_decode(self.copies[0], self.kc, self.vc, x, self.w.pos if pos is None else pos,
+                                   self.window, y, dbg={"expert_idx": idx}, stream=self.stream)
         else:
-            self.plan.layer_decode_batch(self.copies[0], self.kc, self.vc, self.x if x is None else x, requests,
-                                         self.window, self.y, dbg={"expert_idx": idx}, stream=self.stream)
+            self.plan.layer_decode_batch(self.copies[0], self.kc, self.vc, x, requests, self.window, y,
+                                         dbg={"expert_idx": idx}, stream=self.stream)
         torch.cuda.synchronize()
         st = self.plan.status()
         assert st == 0, self.binding.status_string(st)
         return idx.cpu().numpy()
 
-    def timed(self, steps, warmup, fused=True, parents=None, pl=None, cps=None, x=None, requests=None):
+    def timed(self, steps, warmup, fused=True, parents=None, pl=None, cps=None, x=None, requests=None, pos=None):
         """Back-to-back launches between two events on the launch stream: the average launch
         duration (us) over the timed region, and the host wall time (s).  requests: time the
-        batched step over these (T, pos, kv_base, kv_slots) requests instead."""
+        batched step over these (T, pos, kv_base, kv_slots) requests instead; x, pos: another
+        step's rows (T = its row count) and history."""
         torch = self.torch
         pl = self.plan if pl is None else pl
         cps = self.copies if cps is None else cps
         x = self.x if x is None else x
         w = self.w
+        pos = w.pos if pos is None else pos
+        y = self.y if x.shape[0] == self.y.shape[0] else torch.empty((x.shape[0], w.hidden), dtype=torch.float32,
+                                                                       device=self.dev)
 
         def launch(i):
             if requests is None:
-                pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, w.pos, self.window, self.y, fused=fused,
+                pl.layer_decode(cps[i % len(cps)], self.kc, self.vc, x, pos, self.window, y, fused=fused,
                                 stream=self.stream, parents=parents)
             else:
-                pl.layer_decode_batch(cps[i % len(cps)], self.kc, self.vc, x, requests, self.window, self.y,
+                pl.layer_decode_batch(cps[i % len(cps)], self.kc, self.vc, x, requests, self.window, y,
                                       fused=fused, stream=self.stream)
         for i in range(warmup):
             launch(i)
@@ -599,6 +606,14 @@ def main():
         us_b, _ = lb.timed(max(5, args.steps // 2), 2, requests=reqs_b)
         result["batched_verify"] = dict(roofline_entry(w, alg_b, U_b, us_b),
                                         requests="4 x (T 4, history %d, %d-slot pool quarter)" % (hist, quarter))
+        # 32 tokens in one step (two 16-token tiles): the same weights, 32 synthetic rows drawn
+        # like the 16, history 16 shorter so that the cache holds the step
+        x32 = synth.make_x(w.with_(T=32), 0, lb.dev)
+        pos32 = w.pos - 16
+        idx_32 = lb.route(x32, pos=pos32)
+        alg_32, U_32 = algorithmic_bytes(w, idx_32, pos32, lb.window, 32)
+        us_32, _ = lb.timed(max(5, args.steps // 2), 2, x=x32, pos=pos32)
+        result["verify_32_tokens"] = dict(roofline_entry(w, alg_32, U_32, us_32), T=32, kv_history=pos32)
         # the pages' routing concentration (a shared component in every token, tuned so that the
         # 16 tokens use about 49 distinct experts): the same weights and caches, other input rows
         if args.routing == "iid":

@@ -34,6 +34,7 @@ MOEL_DOWN_INPUT_EXACT = 0
 MOEL_DOWN_INPUT_NVFP4 = 1
 MOEL_N_STAMPS = 32
 MOEL_MAX_REQUESTS = 8
+MOEL_MAX_TOKENS = 32
 STACK_LAYERS_PER_LAUNCH = 4  # MOEL_STACK_LAYERS_PER_LAUNCH
 
 

@@ -18,7 +18,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kThreads = 512;  // 8 wavefronts of 64
 constexpr int kWaves = 8;
-constexpr int kMaxT = 16;
+constexpr int kMaxT = MOEL_MAX_TOKENS;  // tokens of one step at most
+constexpr int kTile = 16;               // tokens per MFMA token tile
+constexpr int kMaxTiles = kMaxT / kTile;
+static_assert(kMaxTiles * kTile == kMaxT && kMaxTiles <= 2, "one or two token tiles");
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 __device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }

@@ -708,13 +708,12 @@ moel_status fill_call_batch(const moel_config* cfg, const LayerParams& base, int
   p = base;
   p.l2_coherent = l2_coherent;
   p.T = T;
+  p.ntt = (T + kTile - 1) / kTile;
   p.pos = req[0].pos;
   p.window = window;
   p.n_req = n_req;
   for (int t = 0; t < kMaxT; ++t) {
-    p.tok_req[t] = 0;
     p.tok_pos[t] = 0;
-    p.tok_slot[t] = 0;
     p.tok_sees[t] = 0u;
   }
   int keys[MOEL_MAX_REQUESTS];
@@ -737,18 +736,16 @@ moel_status fill_call_batch(const moel_config* cfg, const LayerParams& base, int
       unsigned sees = 0u;
       for (int a = i; a >= 0; a = parents ? parents[a] : a - 1)
         if (window == 0 || depth[a] > depth[i] - window) sees |= 1u << (t0 + a);
-      p.tok_req[t] = r;
       p.tok_pos[t] = q.pos + depth[i];
-      p.tok_slot[t] = q.kv_base + q.pos + i;
       p.tok_sees[t] = sees;
     }
     t0 += q.T;
   }
   p.req_t0[n_req] = t0;
-  // key chunks: at least 128 keys, at most nwg / Hkv of them over all requests; rounded up to
+  // key chunks: at least 128 keys, at most nwg / (Hkv ntt) of them over all requests; rounded up to
   // whole 128-key sub-chunks (a full sub-chunk inside every token's window needs no mask) where
   // that keeps their number
-  int maxc = base.nwg / cfg->n_kv_heads;
+  int maxc = base.nwg / (cfg->n_kv_heads * p.ntt);  // one item per workgroup and token tile
   if (maxc < 1) maxc = 1;
   int nch = (total_keys + 127) / 128;
   if (nch > maxc) nch = maxc;

@@ -3,6 +3,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "moel.h"  // MOEL_MAX_TOKENS, MOEL_MAX_REQUESTS
+
 #define MOEL_N_STAMPS_DEV 32
 #define MOEL_DEV_TIMEOUT 1u
 #define MOEL_DEV_ABORTED 2u
@@ -33,8 +35,8 @@ struct LayerParams {
   // 1: the down projection reads the SwiGLU output encoded as NVFP4 (the fp4 gather)
   int down_fp4;
   float eps;
-  // call
-  int T, pos, window;
+  // call: T tokens in ntt = ceil(T / 16) token tiles of 16
+  int T, ntt, pos, window;
   int nwg;
   // 1: the XCDs' L2 caches are kept coherent for the plan's memory (checked when the plan is
   // created), so a barrier's acquire invalidates only the L1; 0: it also invalidates the L2
@@ -57,12 +59,11 @@ struct LayerParams {
   int attn_chunk, attn_nchunks;
   int req_ch0[MOEL_MAX_REQUESTS + 1];
   // the step's tokens as the nodes of token trees (a chain per request for the linear verify):
-  // token t of request tok_req[t] is at position tok_pos[t] (RoPE) and writes its key and value
-  // at pool slot tok_slot[t]; bit i of tok_sees[t] is set iff t attends to token i's key: i is t
-  // or an ancestor of t in the same request and within the window of t
-  int tok_req[MOEL_MAX_TOKENS];
+  // token t of request r (req_t0[r] <= t < req_t0[r+1]) is at position tok_pos[t] (RoPE) and
+  // writes its key and value at pool slot req_kvb[r] + req_pos[r] + t - req_t0[r]; bit i of
+  // tok_sees[t] is set iff t attends to token i's key: i is t or an ancestor of t in the same
+  // request and within the window of t
   int tok_pos[MOEL_MAX_TOKENS];
-  int tok_slot[MOEL_MAX_TOKENS];
   unsigned tok_sees[MOEL_MAX_TOKENS];
   // weights (packed)
   const uint16_t* gamma1;
@@ -89,34 +90,34 @@ struct LayerParams {
   const float* rope_sin;
   int rope_row0;
   // scratch (plan workspace)
-  float* q_buf;     // [16][Hq*D]
+  float* q_buf;     // [32][Hq*D]
   // q again as the attention's MFMA operand: per (token, head), q * log2(e) / sqrt(D) as the
   // nearest bf16 values [D], then the bf16 of the remainders [D]
-  uint16_t* q_op;   // [16][Hq][2][D]
-  float* attn_o;    // [items][grp][16][D]
-  float* attn_ml;   // [items][grp][16][2]
-  float* o_buf;     // [16][Hq*D]
-  float* h_buf;     // [16][H]
-  float* logits;    // [16][E]
-  float* pl;        // [16][P]
-  float* a_buf;     // [16*topk][I]
+  uint16_t* q_op;   // [32][Hq][2][D]
+  float* attn_o;    // [items][grp][32][D]
+  float* attn_ml;   // [items][grp][32][2]
+  float* o_buf;     // [32][Hq*D]
+  float* h_buf;     // [32][H]
+  float* logits;    // [32][E]
+  float* pl;        // [32][P]
+  float* a_buf;     // [32*topk][I]
   // pl and a_buf again as the hi/lo bf16 operands of the NVFP4 expert MFMAs: per 4-element
   // quad, 4 bf16 of the nearest values then 4 bf16 of the remainders (16 bytes)
-  uint16_t* pl_split;  // [16][P/4][8]
-  uint16_t* a_split;   // [16*topk][I/4][8]
-  float* aq_buf;    // [16*topk][I] fp4-gathered SwiGLU output (E2M1 x E4M3), debug copy
-  float* d_buf;     // [16*topk][P]
-  float* m_buf;     // [16][P]
+  uint16_t* pl_split;  // [32][P/4][8]
+  uint16_t* a_split;   // [32*topk][I/4][8]
+  float* aq_buf;    // [32*topk][I] fp4-gathered SwiGLU output (E2M1 x E4M3), debug copy
+  float* d_buf;     // [32*topk][P]
+  float* m_buf;     // [32][P]
   // o and m again as the ready-made A operands of the dense contractions that read them (see
-  // opsplit_index): per 32-element k step one 2 KiB block, lane l's 8 nearest bf16 values at
-  // byte 16 l and the 8 bf16 of their remainders at 1024 + 16 l; h (read with gamma 2 and its
-  // sums of squares) as fp32 in the same operand order (op_index): lane l's 8 values at 16 l
-  // and 1024 + 16 l
+  // opsplit_index): per 32-element k step and 16-token tile one 2 KiB block, lane l's 8 nearest
+  // bf16 values at byte 16 l and the 8 bf16 of their remainders at 1024 + 16 l; h (read with
+  // gamma 2 and its sums of squares) as fp32 in the same operand order (op_index): lane l's 8
+  // values at 16 l and 1024 + 16 l
   uint16_t* o_op;
   float* h_op;
   uint16_t* m_op;
-  // split-K partial sums of a dense phase: [split][row][16 tokens], and each unit's sums of
-  // squares of its A rows (sources with stats): [unit][16 tokens]
+  // split-K partial sums of a dense phase: [split][row][32 tokens], and each unit's sums of
+  // squares of its A rows (sources with stats): [unit][32 tokens]
   float* part;
   float* part_ss;
   unsigned* ctrl;   // barrier counter, exit counter, status, abort

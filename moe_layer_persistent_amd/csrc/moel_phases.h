@@ -34,8 +34,10 @@ namespace moel {
 struct RouteTables {
   int idx[kMaxT * 8];          // [T][k] selected expert per slot (slot = t*k + kappa)
   float gate[kMaxT * 8];       // [T][k]
-  int n_active;                // distinct experts hit by the step
-  int active_e[kMaxT * 8];     // ascending expert ids
+  // active entries: the experts hit by the step, ascending, each with its slots; an expert
+  // with more than 16 slots takes one entry per 16 (the expert streams' largest token group)
+  int n_active;
+  int active_e[kMaxT * 8];
   int active_off[kMaxT * 8 + 1];
   int slots[kMaxT * 8];        // slots grouped by expert (ascending), slots ascending within
   int cnt[512];                // per expert: slots routed to it
@@ -65,9 +67,10 @@ __device__ __forceinline__ void split8(const float4& a, const float4& b, u32x4& 
 
 // ------------------------------------------------------------------------------------------
 // A-operand sources of the dense contractions: lane supplies A[token][k .. k+3] and
-// A[token][k+16 .. k+19] (k = 32*step + 4q, the packed weights' k order) as hi + lo.
-// Rows of tokens t >= T read the row of token T-1 (their products are computed and never
-// read), so that no load in the streaming loops depends on a branch.
+// A[token][k+16 .. k+19] (k = 32*step + 4q, the packed weights' k order) as hi + lo, for the
+// token (lane mod 16) of 16-token tile g.  Rows of tokens t >= T read the row of token T-1
+// (their products are computed and never read), so that no load in the streaming loops
+// depends on a branch.
 // ------------------------------------------------------------------------------------------
 // gamma[k .. k+3] and gamma[k+16 .. k+19]
 __device__ __forceinline__ u32x4 ldg_gamma(const uint16_t* g) {
@@ -93,7 +96,7 @@ struct AGamma {
   __device__ __forceinline__ AGamma scalar() const {
     return AGamma{uniform(v), uniform(ld), uniform(gamma), uniform(T), __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, eps)))};
   }
-  __device__ __forceinline__ void fetch(int tok, int k, Raw& r) const {
+  __device__ __forceinline__ void fetch(int tok, int, int k, Raw& r) const {
     const float* src = v + (size_t)tok * ld + k;
     r.a = ldgf4(src);
     r.b = ldgf4(src + 16);
@@ -122,43 +125,49 @@ struct AGamma {
     return fmaf(r.b.w, r.b.w, s);
   }
 };
-// Index (in floats) of element (t, k) of a [16][K] fp32 activation stored in operand order:
-// per 32-element k step one 2 KiB block, in which lane l = t + 16 q of the contraction finds
-// its 8 values k = 4q + 0..3 at float 4 l and k = 16 + 4q + 0..3 at float 256 + 4 l.  A wave's
-// load of a step is then two contiguous 1 KiB reads, where the row-major layout spreads each
-// over 16 rows.  Rows t >= T are left as they are (their products are never read).
-__device__ __forceinline__ size_t op_index(int t, int k) {
+// Index (in floats) of element (t, k) of a [32][K] fp32 activation stored in operand order:
+// per 16-token tile a [K/32] run of 2 KiB blocks, one per 32-element k step, in which lane
+// l = t % 16 + 16 q of the contraction finds its 8 values k = 4q + 0..3 at float 4 l and
+// k = 16 + 4q + 0..3 at float 256 + 4 l.  A wave's load of a step is then two contiguous
+// 1 KiB reads, where the row-major layout spreads each over 16 rows.  Rows t >= T are left as
+// they are (their products are never read).
+__device__ __forceinline__ size_t op_index(int t, int k, int K) {
   const int r = k & 31;
-  return (size_t)(k >> 5) * 512 + ((r >> 4) << 8) + (((r & 15) >> 2) << 6) + 4 * t + (r & 3);
+  return (size_t)(t >> 4) * 16 * K + (size_t)(k >> 5) * 512 + ((r >> 4) << 8) + (((r & 15) >> 2) << 6) +
+         4 * (t & 15) + (r & 3);
 }
-// Index (in bf16 elements) of the nearest-value half of element (t, k) of a [16][K] activation
-// stored as ready-made A operands: per 32-element k step one 2 KiB block, in which lane
-// l = t + 16 q finds the nearest bf16 values of its 8 elements (k = 4q + 0..3, 16 + 4q + 0..3,
-// the word order of split8) at element 8 l and the bf16 of their remainders 512 elements
-// later.  A wave's load of a step is two contiguous 1 KiB reads and the contraction does no
-// splitting: the producer splits each value once (4 B per element, as in fp32).
-__device__ __forceinline__ size_t opsplit_index(int t, int k) {
+// Index (in bf16 elements) of the nearest-value half of element (t, k) of a [32][K] activation
+// stored as ready-made A operands: per 16-token tile a [K/32] run of 2 KiB blocks, one per
+// 32-element k step, in which lane l = t % 16 + 16 q finds the nearest bf16 values of its 8
+// elements (k = 4q + 0..3, 16 + 4q + 0..3, the word order of split8) at element 8 l and the
+// bf16 of their remainders 512 elements later.  A wave's load of a step is two contiguous
+// 1 KiB reads and the contraction does no splitting: the producer splits each value once
+// (4 B per element, as in fp32).
+__device__ __forceinline__ size_t opsplit_index(int t, int k, int K) {
   const int r = k & 31;
-  return (size_t)(k >> 5) * 1024 + 8 * (t + 16 * ((r & 15) >> 2)) + ((r >> 4) << 2) + (r & 3);
+  return (size_t)(t >> 4) * 32 * K + (size_t)(k >> 5) * 1024 + 8 * ((t & 15) + 16 * ((r & 15) >> 2)) +
+         ((r >> 4) << 2) + (r & 3);
 }
 __device__ __forceinline__ void store_opsplit(__attribute__((address_space(1))) uint16_t* base, int t, int k,
-                                              float v) {
-  const size_t i = opsplit_index(t, k);
+                                              int K, float v) {
+  const size_t i = opsplit_index(t, k, K);
   const uint16_t h = f2bf(v);
   base[i] = h;
   base[i + 512] = f2bf(v - bf2f(h));
 }
-// An activation stored as ready-made A operands (lane l reads its own token slot l % 16).
+// An activation stored as ready-made A operands (lane l reads its own token slot l % 16 of
+// tile g).
 struct AOp {
   static constexpr bool kStats = false;
   const uint16_t* v;
   int T;
+  int K;  // row length
   struct Raw {
     u32x4 hi, lo;
   };
-  __device__ __forceinline__ AOp scalar() const { return AOp{uniform(v), uniform(T)}; }
-  __device__ __forceinline__ void fetch(int, int k, Raw& r) const {
-    const uint16_t* src = v + (size_t)(k >> 5) * 1024 + 8 * lane_id();
+  __device__ __forceinline__ AOp scalar() const { return AOp{uniform(v), uniform(T), uniform(K)}; }
+  __device__ __forceinline__ void fetch(int, int g, int k, Raw& r) const {
+    const uint16_t* src = v + (size_t)g * 32 * K + (size_t)(k >> 5) * 1024 + 8 * lane_id();
     r.hi = ldg16(src);
     r.lo = ldg16(src + 512);
   }
@@ -174,15 +183,17 @@ struct AGammaOp {
   const uint16_t* gamma;
   int T;
   float eps;
+  int K;  // row length
   struct Raw {
     float4 a, b;
     u32x4 g;
   };
   __device__ __forceinline__ AGammaOp scalar() const {
-    return AGammaOp{uniform(v), uniform(gamma), uniform(T), __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, eps)))};
+    return AGammaOp{uniform(v), uniform(gamma), uniform(T), __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, eps))),
+                    uniform(K)};
   }
-  __device__ __forceinline__ void fetch(int, int k, Raw& r) const {
-    const float* src = v + (size_t)(k >> 5) * 512 + 4 * lane_id();
+  __device__ __forceinline__ void fetch(int, int g, int k, Raw& r) const {
+    const float* src = v + (size_t)g * 16 * K + (size_t)(k >> 5) * 512 + 4 * lane_id();
     r.a = ldgf4(src);
     r.b = ldgf4(src + 256);
     r.g = ldg_gamma(gamma + k);
@@ -214,9 +225,10 @@ struct AGammaOp {
 // ------------------------------------------------------------------------------------------
 // Dense contraction over a workgroup's rows: out[tok][row] = sum_k A[tok][k] * W[row][k] over a
 // range of k steps.  Rows are assigned in octets (8 rows = four 128-byte lines of every 1 KiB
-// step), so that workgroups never share a cache line.  NT (1..8) tiles of 16 rows per pass; the
-// k-waves split the pass's steps evenly and stream them through a ring of DEPTH steps; partials
-// meet in LDS.  Lanes of an octet outside the workgroup's range load their partner octet's line
+// step), so that workgroups never share a cache line.  NT tiles of 16 rows per pass (NT * NTT
+// <= 8) against NTT tiles of 16 tokens, each weight word used by every token tile; the k-waves
+// split the pass's steps evenly and stream them through a ring of DEPTH steps; partials meet
+// in LDS.  Lanes of an octet outside the workgroup's range load their partner octet's line
 // instead (the same line another lane fetches; the products are never read), so no load sits
 // behind a branch.  On return `fin` holds [tile j][row r][tok] sums for tiles t_first ..
 // t_first+NT-1 over steps ks0 .. ks0+ksn-1, and (sources with stats) `sumsq` the sum of squares
@@ -227,8 +239,8 @@ constexpr int kDenseMaxNT = 8;
 constexpr int kMaxSplit = 16;  // split-K ranges of a dense phase at most
 struct DenseLds {
   f32x4 red[kWaves * kDenseMaxNT * 64];   // 64 KiB
-  float fin[kDenseMaxNT * 16 * kMaxT];    // 8 KiB
-  float ss[kWaves * 64];        // per-lane sums of squares of the A rows (sources with stats)
+  float fin[kDenseMaxNT * 16 * kMaxT];    // 16 KiB
+  float ss[kMaxTiles * kWaves * 64];  // per-lane sums of squares of the A rows (sources with stats)
   float sumsq[kMaxT];           // per token: sum of squares over the pass's k steps
   float rstd[kMaxT];            // 1 / rms of each token's A row (sources with stats)
   int last;                     // split-K: this workgroup reduces its block
@@ -244,13 +256,14 @@ __device__ __forceinline__ int kwaves_for(int n) {
 
 // Not inlined (one body per NT); the arguments arrive in vector registers and are moved to
 // scalar registers first.
-template <int NT, class ASrc>
+template <int NT, int NTT, class ASrc>
 __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, const uint8_t* w1_arg,
                                         int K_arg, int ks0_arg, int ksn_arg, int t_first_arg, int oct_lo_arg,
                                         int oct_hi_arg, const ASrc A_arg) {
   // k steps in flight per wave: 2 keeps ~100 KB per CU in flight, which measured faster than
   // deeper rings (more outstanding requests per CU lowered the achieved bandwidth)
   constexpr int DEPTH = 2;
+  static_assert(NT * NTT <= kDenseMaxNT && NTT <= kMaxTiles, "reduction scratch");
   // the phase scratch of the dynamic LDS, addressed through the LDS symbol (a pointer argument
   // would arrive as a generic address and turn every access into a flat one)
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(moel_lds));
@@ -263,15 +276,21 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
   const int lane = lane_id(), wv = wave_id();
   const int S = K >> 5;  // steps per tile row (the packed tile's stride)
   const int nkw = kwaves_for(ksn);
-  f32x4 acc[NT];
+  f32x4 acc[NTT][NT];
+  float ssum[NTT];  // sums of squares of this lane's A elements (sources with stats)
 #pragma unroll
-  for (int j = 0; j < NT; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float ssum = 0.f;  // sum of squares of this lane's A elements (sources with stats)
+  for (int g = 0; g < NTT; ++g) {
+    ssum[g] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   if (wv < nkw) {
     // k-wave wv takes the steps ks0 + wv, ks0 + wv + nkw, ... so that the workgroup's loads in
     // flight cover one contiguous stretch of each tile
     const int ns = ksn / nkw;
-    const int tok = (lane & 15) < A.T ? (lane & 15) : A.T - 1;
+    int tok[NTT];
+#pragma unroll
+    for (int g = 0; g < NTT; ++g) tok[g] = kTile * g + (lane & 15) < A.T ? kTile * g + (lane & 15) : A.T - 1;
     const int kq = 4 * (lane >> 4) + 32 * (ks0 + wv);
     const uint8_t* base[NT];
 #pragma unroll
@@ -282,21 +301,25 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
       base[j] = (t < tiles0 ? w0 + (size_t)t * S * 1024 : w1 + (size_t)(t - tiles0) * S * 1024) +
                 (size_t)(ks0 + wv) * 1024 + src_lane * 16;
     }
-    typename ASrc::Raw ra[DEPTH];
+    typename ASrc::Raw ra[DEPTH][NTT];
     u32x4 rw[DEPTH][NT];
     auto issue = [&](int d, int i) {
-      A.fetch(tok, kq + 32 * nkw * i, ra[d]);
+#pragma unroll
+      for (int g = 0; g < NTT; ++g) A.fetch(tok[g], g, kq + 32 * nkw * i, ra[d][g]);
 #pragma unroll
       for (int j = 0; j < NT; ++j) rw[d][j] = ldg_stream(base[j] + (size_t)i * nkw * 1024);
     };
     auto compute = [&](int d) {
-      u32x4 a_hi, a_lo;
-      A.finish(ra[d], a_hi, a_lo);
-      if constexpr (ASrc::kStats) ssum += A.sq(ra[d]);
 #pragma unroll
-      for (int j = 0; j < NT; ++j) {
-        acc[j] = mfma16x16x32(a_hi, rw[d][j], acc[j]);
-        acc[j] = mfma16x16x32(a_lo, rw[d][j], acc[j]);
+      for (int g = 0; g < NTT; ++g) {
+        u32x4 a_hi, a_lo;
+        A.finish(ra[d][g], a_hi, a_lo);
+        if constexpr (ASrc::kStats) ssum[g] += A.sq(ra[d][g]);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          acc[g][j] = mfma16x16x32(a_hi, rw[d][j], acc[g][j]);
+          acc[g][j] = mfma16x16x32(a_lo, rw[d][j], acc[g][j]);
+        }
       }
     };
     // straight-line prologue (steps past the end repeat the last one and are never used), so
@@ -326,27 +349,35 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
     for (int d = 0; d < DEPTH; ++d)
       if (i0 + DEPTH + d < ns) compute(d);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) L.red[(wv * kDenseMaxNT + j) * 64 + lane] = acc[j];
+    for (int g = 0; g < NTT; ++g)
+#pragma unroll
+      for (int j = 0; j < NT; ++j) L.red[(wv * kDenseMaxNT + g * NT + j) * 64 + lane] = acc[g][j];
   }
-  // every (token, k) of the A rows is fetched by exactly one lane of the k-waves (lanes with
-  // (lane & 15) >= T repeat token T-1 and are left out)
-  if constexpr (ASrc::kStats) L.ss[wv * 64 + lane] = (wv < nkw && (lane & 15) < A.T) ? ssum : 0.f;
+  // every (token, k) of the A rows is fetched by exactly one lane of the k-waves (lanes whose
+  // token is >= T repeat token T-1 and are left out)
+  if constexpr (ASrc::kStats) {
+#pragma unroll
+    for (int g = 0; g < NTT; ++g)
+      L.ss[(g * kWaves + wv) * 64 + lane] = (wv < nkw && kTile * g + (lane & 15) < A.T) ? ssum[g] : 0.f;
+  }
   lds_barrier();
   if constexpr (ASrc::kStats) {
-    if (threadIdx.x < kMaxT) {
+    if (threadIdx.x < kTile * NTT) {
+      const int g = threadIdx.x >> 4, tt = threadIdx.x & 15;
       float s = 0.f;
       for (int w = 0; w < nkw; ++w)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) s += L.ss[w * 64 + 16 * q + threadIdx.x];
+        for (int q = 0; q < 4; ++q) s += L.ss[(g * kWaves + w) * 64 + 16 * q + tt];
       L.sumsq[threadIdx.x] = s;
       L.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + A.eps);
     }
   }
-  for (int e = threadIdx.x; e < NT * 256; e += kThreads) {
-    const int j = e >> 8, ln = (e >> 2) & 63, r = e & 3;
+  for (int e = threadIdx.x; e < NTT * NT * 256; e += kThreads) {
+    const int g = NTT == 1 ? 0 : e / (NT * 256), eg = e - g * NT * 256;
+    const int j = eg >> 8, ln = (eg >> 2) & 63, r = eg & 3;
     float s = 0.f;
-    for (int w = 0; w < nkw; ++w) s += L.red[(w * kDenseMaxNT + j) * 64 + ln][r];
-    const int tok = 4 * (ln >> 4) + r, row = ln & 15;
+    for (int w = 0; w < nkw; ++w) s += L.red[(w * kDenseMaxNT + g * NT + j) * 64 + ln][r];
+    const int tok = kTile * g + 4 * (ln >> 4) + r, row = ln & 15;
     L.fin[(j * 16 + row) * kMaxT + tok] = s;
   }
   lds_barrier();
@@ -360,18 +391,28 @@ __device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo,
   hi = (int)((unsigned)(wg + 1) * (unsigned)n / (unsigned)nwg);
 }
 
+// nt row tiles against ntt token tiles (nt * ntt <= 8)
 template <class ASrc>
-__device__ __forceinline__ void dense_pass_nt(int nt, const uint8_t* w0, int tiles0, const uint8_t* w1, int K,
-                                              int ks0, int ksn, int t, int lo, int hi, const ASrc& A) {
-  switch (nt) {
-    case 1: dense_pass<1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    case 2: dense_pass<2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    case 3: dense_pass<3>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    case 4: dense_pass<4>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    case 5: dense_pass<5>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    case 6: dense_pass<6>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    case 7: dense_pass<7>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-    default: dense_pass<8>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+__device__ __forceinline__ void dense_pass_nt(int nt, int ntt, const uint8_t* w0, int tiles0, const uint8_t* w1,
+                                              int K, int ks0, int ksn, int t, int lo, int hi, const ASrc& A) {
+  if (ntt == 1) {
+    switch (nt) {
+      case 1: dense_pass<1, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 2: dense_pass<2, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 3: dense_pass<3, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 4: dense_pass<4, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 5: dense_pass<5, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 6: dense_pass<6, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 7: dense_pass<7, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      default: dense_pass<8, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    }
+  } else {
+    switch (nt) {
+      case 1: dense_pass<1, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 2: dense_pass<2, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 3: dense_pass<3, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      default: dense_pass<4, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+    }
   }
 }
 
@@ -394,14 +435,17 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   const int nwg = p.nwg;
   const int tiles = tiles0 + tiles1;
   const int S = K >> 5;
+  const int ntt = p.ntt;
+  const int gs = kDenseMaxNT / ntt;  // row tiles per pass
+  const int lgT = ntt == 1 ? 4 : 5;  // log2 of the tokens the passes cover (16 per tile)
   if (nsplit <= 1) {
     int lo, hi;
     octet_range(tiles, wg, nwg, lo, hi);
     if (lo >= hi) return;
     const int tf = lo >> 1, tl = (hi - 1) >> 1;
-    for (int t = tf; t <= tl; t += kDenseMaxNT) {
-      const int nt = (tl - t + 1) < kDenseMaxNT ? (tl - t + 1) : kDenseMaxNT;
-      dense_pass_nt(nt, w0, tiles0, w1, K, 0, S, t, lo, hi, A);
+    for (int t = tf; t <= tl; t += gs) {
+      const int nt = (tl - t + 1) < gs ? (tl - t + 1) : gs;
+      dense_pass_nt(nt, ntt, w0, tiles0, w1, K, 0, S, t, lo, hi, A);
       epi(L, t, nt, lo, hi);
       lds_barrier();
     }
@@ -425,11 +469,11 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   const int ksn = S / nsplit, ks0 = js * ksn;
   const int ntot = tiles * 16;
   auto part = gl(p.part);
-  for (int t = tf; t <= tl; t += kDenseMaxNT) {
-    const int nt = (tl - t + 1) < kDenseMaxNT ? (tl - t + 1) : kDenseMaxNT;
-    dense_pass_nt(nt, w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A);
-    for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
-      const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, tok = e % kMaxT;
+  for (int t = tf; t <= tl; t += gs) {
+    const int nt = (tl - t + 1) < gs ? (tl - t + 1) : gs;
+    dense_pass_nt(nt, ntt, w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A);
+    for (int e = threadIdx.x; e < (nt * 16) << lgT; e += kThreads) {
+      const int j = e >> (lgT + 4), r = (e >> lgT) & 15, tok = e & ((1 << lgT) - 1);
       const int n = (t + j) * 16 + r;
       if (tok < p.T && (n >> 3) >= lo && (n >> 3) < hi)
         part[((size_t)js * ntot + n) * kMaxT + tok] = L.fin[(j * 16 + r) * kMaxT + tok];
@@ -480,28 +524,32 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
       L.rstd[threadIdx.x] = 1.0f / sqrtf(s / (float)K + A.eps);
     }
   }
-  constexpr int kPer = kDenseMaxNT * 16 * kMaxT / kThreads;  // outputs per thread and tile group
-  for (int t = tf; t <= tl; t += kDenseMaxNT) {
-    const int nt = (tl - t + 1) < kDenseMaxNT ? (tl - t + 1) : kDenseMaxNT;
-    float v[kPer][kMaxSplit];
+  constexpr int kPer = 4;  // outputs per thread and round
+  for (int t = tf; t <= tl; t += gs) {
+    const int nt = (tl - t + 1) < gs ? (tl - t + 1) : gs;
+    const int ne = (nt * 16) << lgT;
+    for (int e0 = 0; e0 < ne; e0 += kPer * kThreads) {
+      float v[kPer][kMaxSplit];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, tok = e % kMaxT;
-      const int n = (t + j) * 16 + r;
-      const bool ok = j < nt && tok < p.T && (n >> 3) >= lo && (n >> 3) < hi;
+      for (int i = 0; i < kPer; ++i) {
+        const int e = e0 + threadIdx.x + i * kThreads;
+        const int j = e >> (lgT + 4), r = (e >> lgT) & 15, tok = e & ((1 << lgT) - 1);
+        const int n = (t + j) * 16 + r;
+        const bool ok = e < ne && tok < p.T && (n >> 3) >= lo && (n >> 3) < hi;
 #pragma unroll
-      for (int q = 0; q < kMaxSplit; ++q)
-        v[i][q] = (ok && q < nsplit) ? part[((size_t)q * ntot + n) * kMaxT + tok] : 0.f;
-    }
+        for (int q = 0; q < kMaxSplit; ++q)
+          v[i][q] = (ok && q < nsplit) ? part[((size_t)q * ntot + n) * kMaxT + tok] : 0.f;
+      }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      float sum = 0.f;
+      for (int i = 0; i < kPer; ++i) {
+        const int e = e0 + threadIdx.x + i * kThreads;
+        const int j = e >> (lgT + 4), r = (e >> lgT) & 15, tok = e & ((1 << lgT) - 1);
+        float sum = 0.f;
 #pragma unroll
-      for (int q = 0; q < kMaxSplit; ++q)
-        if (q < nsplit) sum += v[i][q];
-      L.fin[e] = sum;  // e = (j * 16 + r) * kMaxT + tok
+        for (int q = 0; q < kMaxSplit; ++q)
+          if (q < nsplit) sum += v[i][q];
+        if (e < ne) L.fin[(j * 16 + r) * kMaxT + tok] = sum;
+      }
     }
     lds_barrier();
     epi(L, t, nt, lo, hi);
@@ -526,15 +574,19 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
   const int half = p.D >> 1;
   dense_phase(p, 0, p.sk_qkv, p.w_qkv, tiles, nullptr, 0, p.H, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
-                for (int e = threadIdx.x; e < nt * 8 * kMaxT; e += kThreads) {
-                  const int j = e / (8 * kMaxT), pr = (e / kMaxT) & 7, t = e % kMaxT;
+                const int lgT = p.ntt == 1 ? 4 : 5;  // tokens covered: 16 per tile
+                for (int e = threadIdx.x; e < (nt * 8) << lgT; e += kThreads) {
+                  const int j = e >> (lgT + 3), pr = (e >> lgT) & 7, t = e & ((1 << lgT) - 1);
                   const int R = (tf + j) * 16 + 2 * pr;  // packed row (even)
                   if (t >= p.T || !octet_in(R, lo, hi)) continue;
                   const float a = L.fin[(j * 16 + 2 * pr) * kMaxT + t] * L.rstd[t];
                   const float b = L.fin[(j * 16 + 2 * pr + 1) * kMaxT + t] * L.rstd[t];
                   const int head = R / p.D, i = (R % p.D) >> 1;
-                  const int ps = p.tok_slot[t];  // pool slot
-                  const int rp = p.tok_pos[t];   // position (RoPE)
+                  // pool slot of the token: its request's base + position + index in the request
+                  int ps = 0;
+                  for (int r = 0; r < p.n_req; ++r)
+                    if (t >= p.req_t0[r]) ps = p.req_kvb[r] + p.req_pos[r] - p.req_t0[r] + t;
+                  const int rp = p.tok_pos[t];  // position (RoPE)
                   if (head < p.Hq + p.Hkv) {
                     const float c = gl(p.rope_cos)[(size_t)(rp - p.rope_row0) * half + i];
                     const float s = gl(p.rope_sin)[(size_t)(rp - p.rope_row0) * half + i];
@@ -567,7 +619,8 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
 }
 
 // ------------------------------------------------------------------------------------------
-// Attention partials.  Item = (kv head g, key chunk c); each wave is one q head of the group.
+// Attention partials.  Item = (kv head g, key chunk c, 16-token tile); each wave is one q head
+// of the group.
 // Keys go in sub-chunks of SK = 128: while one sub-chunk is in LDS and being used, the next
 // one's K/V rows are already in flight into registers.  S^T = K Q^T on MFMA (keys as rows;
 // q as hi + lo, pre-multiplied by log2(e)/sqrt(D) so that scores come out in base-2 units),
@@ -603,14 +656,16 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   static_assert(NCH * kThreads == SK * (D / 8), "sub-chunk staging must divide evenly");
   const int lane = lane_id(), wv = wave_id();
   const int grp = p.Hq / p.Hkv;
-  const int nitems = p.Hkv * p.attn_nchunks;
+  // items: (kv head, key chunk) x 16-token tile, the tiles of one (head, chunk) adjacent
+  const int nitems = p.Hkv * p.attn_nchunks * p.ntt;
   const float NEG = -__builtin_inff();
   const int gq = lane >> 4, tq = lane & 15;
   // this thread's place in a sub-chunk's staging: 16-byte column c8 of rows row0 + i * RSTEP
   constexpr int RSTEP = kThreads / (D / 8);
   const int row0 = threadIdx.x / (D / 8), c8 = (threadIdx.x % (D / 8)) * 8;
   for (int it = wg; it < nitems; it += p.nwg) {
-    const int g = it % p.Hkv, cc = it / p.Hkv;  // kv head, flat chunk
+    const int ib = it / p.ntt, tile = it - ib * p.ntt;  // (head, chunk) item and token tile
+    const int g = ib % p.Hkv, cc = ib / p.Hkv;  // kv head, flat chunk
     // the chunk's request rq and its chunk c within the request (uniform)
     int rq = 0;
     while (rq + 1 < p.n_req && cc >= p.req_ch0[rq + 1]) ++rq;
@@ -645,11 +700,13 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
         }
       }
     };
-    // q of this wave's head, scaled and split by the QKV phase (tokens past T repeat token
-    // T-1; their rows are never stored).  Issued before the first K/V rows: the wait for those
-    // at the first LDS fill then covers q too (loads complete in order), so no wait for q is
-    // left inside the key loop, where it would also drain the next sub-chunk's rows in flight.
-    const int tqc = tq < p.T ? tq : p.T - 1;
+    // q of this wave's head for the lane's token of the tile, scaled and split by the QKV
+    // phase (tokens past T repeat token T-1; their rows are never read).  Issued before the
+    // first K/V rows: the wait for those at the first LDS fill then covers q too (loads
+    // complete in order), so no wait for q is left inside the key loop, where it would also
+    // drain the next sub-chunk's rows in flight.
+    const int tk = kTile * tile + tq;
+    const int tqc = tk < p.T ? tk : p.T - 1;
     u32x4 qh[NS], ql[NS];
     {
       const uint16_t* qs = p.q_op + ((size_t)tqc * p.Hq + (act ? h : 0)) * 2 * D + 8 * gq;
@@ -670,7 +727,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     const unsigned sees = p.tok_sees[tqc];
     const int lo_t = p.window == 0 ? -0x7fffffff - 1 : ptok - p.window + 1;
     // this lane's token takes part in the item: a token of the step, of the item's request
-    const bool tok_ok = tq < p.T && p.tok_req[tqc] == rq;
+    const bool tok_ok = tk >= t0_r && tk < t0_r + T_r;
     const bool multi = p.n_req > 1;
     for (int sb = kb; sb < ke; sb += SK) {
       lds_barrier();  // the previous sub-chunk's LDS reads are done
@@ -700,7 +757,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
             S[kt] = mfma16x16x32(ka, ql[s], S[kt]);
           }
         }
-        // mask; lane holds keys kt*16 + 4*gq + r of token tq.  A whole sub-chunk of cached
+        // mask; lane holds keys kt*16 + 4*gq + r of the tile's token tq.  A whole sub-chunk of cached
         // keys inside every token's window needs none (rows of tokens past T are never read).
         // Otherwise key j is visible iff j is in the chunk and, for a cached key, inside the
         // token's window, for a key of the step, bit j - pos of the token's set; computed
@@ -783,13 +840,14 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
       }
     }
     if (act) {
-      auto op = gl(p.attn_o + ((size_t)(it * grp + hw) * kMaxT) * D);
+      // the tile's 16 token rows of the (head, chunk) item's partial
+      auto op = gl(p.attn_o + ((size_t)(ib * grp + hw) * kMaxT + kTile * tile) * D);
 #pragma unroll
       for (int d = 0; d < ND; ++d)
 #pragma unroll
         for (int r = 0; r < 4; ++r) op[(4 * gq + r) * D + 16 * d + tq] = O[d][r];
       if (lane < 16) {
-        auto ml = gl(p.attn_ml + ((size_t)(it * grp + hw) * kMaxT + lane) * 2);
+        auto ml = gl(p.attn_ml + ((size_t)(ib * grp + hw) * kMaxT + kTile * tile + lane) * 2);
         ml[0] = m_run;
         ml[1] = l_run;
       }
@@ -840,7 +898,7 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
     }
     const float o = num / den;
     if (p.debug_copies) gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
-    store_opsplit(gl(p.o_op), t, h * p.D + d, o);
+    store_opsplit(gl(p.o_op), t, h * p.D + d, p.Hq * p.D, o);
   }
 }
 
@@ -849,16 +907,17 @@ __device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  AOp A{p.o_op, p.T};
+  AOp A{p.o_op, p.T, p.Hq * p.D};
   dense_phase(p, 1, p.sk_oproj, p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
-                for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
-                  const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
+                const int lgT = p.ntt == 1 ? 4 : 5;  // tokens covered: 16 per tile
+                for (int e = threadIdx.x; e < (nt * 16) << lgT; e += kThreads) {
+                  const int j = e >> (lgT + 4), r = (e >> lgT) & 15, t = e & ((1 << lgT) - 1);
                   const int n = (tf + j) * 16 + r;
                   if (t < p.T && octet_in(n, lo, hi)) {
                     const float h = gl(p.x)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
                     gl(p.h_buf)[(size_t)t * p.H + n] = h;
-                    gl(p.h_op)[op_index(t, n)] = h;
+                    gl(p.h_op)[op_index(t, n, p.H)] = h;
                   }
                 }
               });
@@ -871,12 +930,13 @@ __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
 // ------------------------------------------------------------------------------------------
 __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  AGammaOp A{p.h_op, p.gamma2, p.T, p.eps};
+  AGammaOp A{p.h_op, p.gamma2, p.T, p.eps, p.H};
   const int te = p.E / 16;
   dense_phase(p, 2, p.sk_rp, p.w_router, te, p.w_pool, p.P / 16, p.H, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
-                for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
-                  const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
+                const int lgT = p.ntt == 1 ? 4 : 5;  // tokens covered: 16 per tile
+                for (int e = threadIdx.x; e < (nt * 16) << lgT; e += kThreads) {
+                  const int j = e >> (lgT + 4), r = (e >> lgT) & 15, t = e & ((1 << lgT) - 1);
                   const int n = (tf + j) * 16 + r;
                   if (t >= p.T || !octet_in(n, lo, hi)) continue;
                   const float v = L.fin[(j * 16 + r) * kMaxT + t] * L.rstd[t];
@@ -983,11 +1043,12 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
       R.ts[m][e] = ts;
     }
   }
-  // top-k: wave w takes tokens 2w (lanes 0-31) and 2w + 1 (lanes 32-63) at the same time;
-  // lane l of a half holds experts (l mod 32) + 32 j, j < NV = ceil(E / 32)
-  auto topk = [&](auto nv_tag) {
+  // top-k: wave w takes tokens 16 th + 2w (lanes 0-31) and 16 th + 2w + 1 (lanes 32-63) at the
+  // same time, th over the token tiles; lane l of a half holds experts (l mod 32) + 32 j,
+  // j < NV = ceil(E / 32)
+  auto topk = [&](auto nv_tag, int th) {
     constexpr int NV = decltype(nv_tag)::value;
-    const int t = 2 * wv + (lane >> 5);
+    const int t = kTile * th + 2 * wv + (lane >> 5);
     const bool tok_ok = t < p.T;
     const int tc = tok_ok ? t : 0;
     float v[NV];
@@ -1030,15 +1091,18 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
     }
     if ((lane & 31) < p.topk && tok_ok) R.gate[t * p.topk + (lane & 31)] = ex_r / esum;
   };
-  if (p.E <= 256) topk(std::integral_constant<int, 8>{});
-  else topk(std::integral_constant<int, 16>{});
+  for (int th = 0; th < p.ntt; ++th) {
+    if (p.E <= 256) topk(std::integral_constant<int, 8>{}, th);
+    else topk(std::integral_constant<int, 16>{}, th);
+  }
   lds_barrier();
   // slot lists, expert-major with slots ascending within an expert.  Per expert: the count of
   // its slots and the mask of tokens that chose it (LDS integer atomics, order-independent);
   // an exclusive scan over the experts gives each expert's first position and, over the
-  // experts with a nonzero count, its rank among the active ones; a slot's position is its
-  // expert's first position plus the number of earlier tokens that chose the same expert
-  // (one token picks an expert at most once, so token order is slot order).
+  // experts' entry counts (one per 16 slots, rounded up), the rank of its first active entry;
+  // a slot's position is its expert's first position plus the number of earlier tokens that
+  // chose the same expert (one token picks an expert at most once, so token order is slot
+  // order).
   const int s = threadIdx.x;
   if (s < nslot) {
     const int e = R.idx[s];
@@ -1048,7 +1112,8 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
   lds_barrier();
   const int e = threadIdx.x;  // kThreads >= E (E <= 512)
   const int c = e < p.E ? R.cnt[e] : 0;
-  int incl_c = c, incl_a = c > 0 ? 1 : 0;
+  const int na = (c + kTile - 1) / kTile;  // the expert's active entries
+  int incl_c = c, incl_a = na;
   wave_inclusive_scan(incl_c);
   wave_inclusive_scan(incl_a);
   if (lane == 63) {
@@ -1064,10 +1129,10 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
   const int off_e = base_c + incl_c - c;
   if (e < p.E) {
     R.off[e] = off_e;
-    if (c > 0) {
-      const int ra = base_a + incl_a - 1;
+    for (int i = 0; i < na; ++i) {
+      const int ra = base_a + incl_a - na + i;
       R.active_e[ra] = e;
-      R.active_off[ra] = off_e;
+      R.active_off[ra] = off_e + kTile * i;
     }
   }
   if (e == kThreads - 1) {
@@ -1747,18 +1812,19 @@ __device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
     for (int k = 0; k < p.topk; ++k)
       s = fmaf(R.gate[t * p.topk + k], gl(p.d_buf)[(size_t)(t * p.topk + k) * p.P + pc], s);
     if (p.debug_copies) gl(p.m_buf)[(size_t)t * p.P + pc] = s;
-    store_opsplit(gl(p.m_op), t, pc, s);
+    store_opsplit(gl(p.m_op), t, pc, p.P, s);
   }
 }
 
 // y = h + m W_unpool^T
 __device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
-  AOp A{p.m_op, p.T};
+  AOp A{p.m_op, p.T, p.P};
   dense_phase(p, 3, p.sk_unpool, p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, A, L,
               [&](DenseLds& L, int tf, int nt, int lo, int hi) {
-                for (int e = threadIdx.x; e < nt * 16 * kMaxT; e += kThreads) {
-                  const int j = e / (16 * kMaxT), r = (e / kMaxT) & 15, t = e % kMaxT;
+                const int lgT = p.ntt == 1 ? 4 : 5;  // tokens covered: 16 per tile
+                for (int e = threadIdx.x; e < (nt * 16) << lgT; e += kThreads) {
+                  const int j = e >> (lgT + 4), r = (e >> lgT) & 15, t = e & ((1 << lgT) - 1);
                   const int n = (tf + j) * 16 + r;
                   if (t >= p.T || !octet_in(n, lo, hi)) continue;
                   gl(p.y)[(size_t)t * p.H + n] = gl(p.h_buf)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];

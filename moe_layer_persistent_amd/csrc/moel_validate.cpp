@@ -47,11 +47,13 @@ moel_status moel_validate_config(const moel_config* c) {
     return MOEL_ERR_SHAPE;
   if ((int64_t)c->kv_capacity * c->head_dim > ((int64_t)1 << 31) / c->n_kv_heads) return MOEL_ERR_SHAPE;
   // the NVFP4 expert phases hand tiles out as (sequence << 16) | tile with 0xffff marking the
-  // end of the work: every tile number of a step (active experts x 64-row tiles per expert,
-  // at most min(E, 16 top_k) experts) and every sequence number must fit 15 bits
+  // end of the work: every tile number of a step (active entries x 64-row tiles per expert;
+  // an expert takes one entry per 16 of its slots, so at most min(2 E, 32 top_k) entries)
+  // and every sequence number must fit 15 bits
   if (c->expert_dtype == MOEL_EXPERT_NVFP4) {
     const int64_t rows = (c->inter > c->pooled ? c->inter : c->pooled) / c->n_shards;
-    const int64_t active = c->n_experts < MOEL_MAX_TOKENS * c->top_k ? c->n_experts : MOEL_MAX_TOKENS * c->top_k;
+    const int64_t e2 = 2 * (int64_t)c->n_experts, slots = (int64_t)MOEL_MAX_TOKENS * c->top_k;
+    const int64_t active = e2 < slots ? e2 : slots;
     if ((rows / 64) * active >= 0x7fff) return MOEL_ERR_SHAPE;
   }
   return MOEL_OK;
@@ -126,6 +128,7 @@ extern "C" moel_status moel_validate_batch(const moel_config* cfg, int32_t n_req
     }
   }
   if (total > MOEL_MAX_TOKENS) return MOEL_ERR_ARG;
-  if (workgroups > 0 && (int64_t)n_requests * cfg->n_kv_heads > workgroups) return MOEL_ERR_SHAPE;
+  const int64_t tiles = (total + 15) / 16;  // 16-token tiles: one attention item per request, kv head and tile
+  if (workgroups > 0 && (int64_t)n_requests * cfg->n_kv_heads * tiles > workgroups) return MOEL_ERR_SHAPE;
   return MOEL_OK;
 }

@@ -191,7 +191,7 @@ def device_down_input(run: GpuRun, gpu_idx: np.ndarray, T: int) -> np.ndarray:
     w = run.w
     k, I = w.top_k, w.inter
     r0 = getattr(run, "row0", 0)
-    aq = run.plan.scratch("aq").view(16 * k, I).cpu().numpy().astype(np.float64)
+    aq = run.plan.scratch("aq").view(binding.MOEL_MAX_TOKENS * k, I).cpu().numpy().astype(np.float64)
     act = run.t["act_ts"].cpu().numpy()
     out = np.empty((T, k, I))
     for t in range(T):
@@ -205,9 +205,9 @@ def check_fp4_gather(run: GpuRun, gpu_idx: np.ndarray, ref: Dict, toks: Sequence
     slots (ref: the oracle run with the device's down input)."""
     w = run.w
     k, I = w.top_k, w.inter
-    a_dev = run.plan.scratch("a").view(16 * k, I).cpu().numpy()
-    aq_dev = run.plan.scratch("aq").view(16 * k, I).cpu().numpy().astype(np.float64)
-    d_dev = run.plan.scratch("d").view(16 * k, w.pooled).cpu().numpy().astype(np.float64)
+    a_dev = run.plan.scratch("a").view(binding.MOEL_MAX_TOKENS * k, I).cpu().numpy()
+    aq_dev = run.plan.scratch("aq").view(binding.MOEL_MAX_TOKENS * k, I).cpu().numpy().astype(np.float64)
+    d_dev = run.plan.scratch("d").view(binding.MOEL_MAX_TOKENS * k, w.pooled).cpu().numpy().astype(np.float64)
     act = run.t["act_ts"].cpu().numpy()
     ex = expert_fn(run)
     plc, r = w.pooled // w.n_shards, w.shard_rank
@@ -334,7 +334,7 @@ def check_against_oracle(run: GpuRun, out: Dict, moe_tokens: Optional[Sequence[i
     inter = {}
     for name, key in (("q", "q"), ("o", "o"), ("h", "h"), ("pl", "pl")):
         r0 = getattr(run, "row0", 0)
-        got_i = run.plan.scratch(name).view(16, -1)[r0:r0 + T].cpu().numpy().astype(np.float64)
+        got_i = run.plan.scratch(name).view(binding.MOEL_MAX_TOKENS, -1)[r0:r0 + T].cpu().numpy().astype(np.float64)
         want = ref[key].reshape(T, -1)
         inter[name] = float(np.abs(got_i - want).max() / (np.abs(want).max() + 1e-30))
         need(inter[name] <= REL_ERR_MAX[name], f"{name} relative error {inter[name]} > {REL_ERR_MAX[name]}")

@@ -43,7 +43,8 @@ def test_tree_validation():
     assert L.moel_validate_tree(arr([-1, 1]), 2) == binding.MOEL_ERR_ARG      # not before its child
     assert L.moel_validate_tree(arr([0]), 1) == binding.MOEL_ERR_ARG
     assert L.moel_validate_tree(arr([-2, 0]), 2) == binding.MOEL_ERR_ARG
-    assert L.moel_validate_tree(arr([-1] * 17), 17) == binding.MOEL_ERR_ARG    # T > 16
+    assert L.moel_validate_tree(arr([-1] * 32), 32) == binding.MOEL_OK
+    assert L.moel_validate_tree(arr([-1] * 33), 33) == binding.MOEL_ERR_ARG    # T > 32
 
 
 def test_shapes_beyond_the_32_bit_work_split_are_rejected():
@@ -107,7 +108,8 @@ def _fake_weights(base=0x10000):
 
 @pytest.mark.parametrize("T,pos,window,code", [
     (0, 10, 0, binding.MOEL_ERR_ARG),
-    (17, 10, 0, binding.MOEL_ERR_ARG),
+    (33, 10, 0, binding.MOEL_ERR_ARG),
+    (32, 10, 0, binding.MOEL_OK),
     (16, -1, 0, binding.MOEL_ERR_ARG),
     (16, 10, -1, binding.MOEL_ERR_ARG),
     (16, 8192 + 1, 0, binding.MOEL_ERR_ARG),     # pos + T > kv_capacity (8208)
@@ -171,7 +173,7 @@ def test_nvfp4_tile_numbers_must_fit_the_hand_out_words():
     # bf16 experts hand out plain tile numbers
     c = _cfg(inter=65536, n_experts=64, top_k=4, expert_dtype=binding.MOEL_EXPERT_BF16)
     assert L.moel_validate_config(ctypes.byref(c)) == binding.MOEL_OK
-    # the full-width layer: 64 tiles per expert, at most 128 experts active
+    # the full-width layer: 64 tiles per expert, at most 256 active entries
     assert L.moel_validate_config(ctypes.byref(_cfg())) == binding.MOEL_OK
 
 
@@ -214,11 +216,14 @@ def test_validate_batch():
     assert v([(2, 0, 0, 100), (2, 0, 99, 100)]) == binding.MOEL_ERR_ARG   # slot ranges overlap
     assert v([(2, 0, 100, 100), (2, 0, 0, 101)]) == binding.MOEL_ERR_ARG  # overlap, other order
     assert v([(2, 0, 0, 100), (2, 0, 100, 100)]) == ok                    # adjacent
-    assert v([(9, 0, 0, 100), (8, 0, 100, 100)]) == binding.MOEL_ERR_ARG  # 17 tokens
-    assert v([(8, 0, 0, 100), (8, 0, 100, 100)]) == ok
+    assert v([(17, 0, 0, 100), (16, 0, 100, 100)]) == binding.MOEL_ERR_ARG  # 33 tokens
+    assert v([(16, 0, 0, 100), (16, 0, 100, 100)]) == ok
     reqs = [(1, 0, 8 * i, 8) for i in range(3)]
     assert v(reqs, 24) == ok                                       # 3 x 8 attention items
     assert v(reqs, 23) == binding.MOEL_ERR_SHAPE
+    reqs = [(9, 0, 0, 100), (8, 0, 100, 100)]                      # two 16-token tiles
+    assert v(reqs, 32) == ok                                       # 2 x 8 x 2 attention items
+    assert v(reqs, 31) == binding.MOEL_ERR_SHAPE
 
 
 def test_batch_calls_reject_bad_requests_before_any_launch():

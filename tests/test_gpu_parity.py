@@ -268,7 +268,7 @@ def test_invalid_calls_launch_nothing():
     run = harness.GpuRun(w)
     kc, vc = run.fresh_caches()
     y = torch.full((w.T, w.hidden), 7.0, dtype=torch.float32, device="cuda")
-    for T, pos, window in ((0, 30, 0), (17, 30, 0), (4, w.kv_capacity - 3, 0), (4, -1, 0), (4, 30, -2)):
+    for T, pos, window in ((0, 30, 0), (33, 30, 0), (4, w.kv_capacity - 3, 0), (4, -1, 0), (4, 30, -2)):
         with pytest.raises(binding.MoelError) as ei:
             run.plan.layer_decode(run.lw, kc, vc, run.t["x"], pos, window, y, T=T)
         assert ei.value.code == binding.MOEL_ERR_ARG
@@ -346,7 +346,7 @@ def test_invalid_batches_launch_nothing():
     run = harness.GpuRun(_batch_workload(window=0))
     kc, vc = run.fresh_caches()
     y = torch.full((16, run.w.hidden), 7.0, dtype=torch.float32, device="cuda")
-    for reqs in ([], [(4, 0, 0, 100), (4, 0, 50, 100)], [(4, 98, 0, 100)], [(9, 0, 0, 100), (8, 0, 100, 100)]):
+    for reqs in ([], [(4, 0, 0, 100), (4, 0, 50, 100)], [(4, 98, 0, 100)], [(17, 0, 0, 100), (16, 0, 100, 100)]):
         with pytest.raises(binding.MoelError) as ei:
             run.plan.layer_decode_batch(run.lw, kc, vc, run.t["x"], reqs, 0, y)
         assert ei.value.code == binding.MOEL_ERR_ARG
@@ -365,6 +365,94 @@ def test_full_width_batch_matches_oracle():
     _log("full batch: oracle")
     reps = harness.check_batch_against_oracle(run, out, reqs)
     _log(f"full batch: {reps}")
+
+
+# ---------------------------------------------------------------- two 16-token tiles (T up to 32)
+# (workload overrides, call T, call pos): the workload's cache holds pos + 16 slots, so a call of
+# more than 16 tokens starts earlier
+TILES2 = [
+    (dict(T=32, pos=300, window=0), 32, 284),
+    (dict(T=32, pos=300, window=40), 32, 284),
+    (dict(T=20, pos=60, window=7), 20, 56),
+    (dict(T=32, pos=200, window=64, head_dim=128, n_q_heads=4, n_kv_heads=1, hidden=768), 32, 184),
+    (dict(T=32, pos=150, window=0, expert_dtype=synth.BF16), 32, 134),
+    (dict(T=17, pos=100, window=32, n_experts=32, top_k=8, pooled=512, inter=512), 17, 99),
+    (dict(T=32, pos=100, window=0, n_experts=32, top_k=8, n_shards=8, shard_rank=3, inter=512, pooled=512,
+          down_input=synth.DOWN_NVFP4), 32, 84),
+]
+
+
+@pytest.mark.parametrize("case", TILES2, ids=[str(i) for i in range(len(TILES2))])
+def test_two_token_tiles_match_oracle(case):
+    kw, T, pos = case
+    w = synth.small_workload(**kw)
+    _log(f"tiles2 {kw} T {T} pos {pos}")
+    run = harness.GpuRun(w)
+    out = run.run(fused=True, T=T, pos=pos)
+    rep = {}
+    harness.check_against_oracle(run, out, report=rep)
+    _log(f"tiles2: {rep}")
+    b = run.run(fused=False, T=T, pos=pos)
+    for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+        assert _same_bytes(out[k], b[k]), k
+
+
+@pytest.mark.parametrize("kw", [dict(), dict(expert_dtype=synth.BF16)], ids=["nvfp4", "bf16"])
+def test_two_token_tiles_with_experts_over_16_slots(kw):
+    """Concentrated routing at 32 tokens: experts chosen by more than 16 tokens, which the
+    expert streams take as one entry per 16 slots."""
+    w = synth.small_workload(T=32, pos=116, window=0, n_experts=32, top_k=8, pooled=512, inter=512, **kw)
+    run = harness.GpuRun(w, routing="shared")
+    out = run.run(fused=True, T=32, pos=100)
+    counts = np.bincount(out["expert_idx"].cpu().numpy().ravel(), minlength=w.n_experts)
+    _log(f"tiles2 shared: slots per expert max {counts.max()}")
+    assert counts.max() > 16
+    rep = {}
+    harness.check_against_oracle(run, out, report=rep)
+    _log(f"tiles2 shared: {rep}")
+
+
+@pytest.mark.parametrize("splits", ["2,2,2,2", "8,8,8,8"])
+def test_two_token_tiles_split_k(splits, monkeypatch):
+    monkeypatch.setenv("MOEL_DENSE_SPLITS", splits)
+    w = synth.small_workload(T=32, pos=316, window=0, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                             n_experts=32, top_k=8, pooled=1024, inter=1024)
+    run = harness.GpuRun(w)
+    out = run.run(fused=True, T=32, pos=300)
+    harness.check_against_oracle(run, out)
+    b = run.run(fused=False, T=32, pos=300)
+    for k in ("y", "k_cache", "v_cache", "expert_idx"):
+        assert _same_bytes(out[k], b[k]), k
+
+
+def test_two_token_tiles_tree_and_batch():
+    # a 32-node tree (two branches off a chain), and a batch of three requests of 32 tokens
+    par = [-1] + list(range(0, 15)) + [3] + list(range(16, 26)) + [20, 27, 28, 29, 30]
+    assert len(par) == 32 and all(-1 <= v < i for i, v in enumerate(par))
+    w = synth.small_workload(T=32, pos=516, window=48, n_experts=32, top_k=8, pooled=512, inter=512)
+    run = harness.GpuRun(w)
+    out = run.run(fused=True, T=32, pos=500, parents=par)
+    harness.check_against_oracle(run, out)
+    wb = _batch_workload(T=32, pos=784, window=40)
+    runb = harness.GpuRun(wb)
+    reqs = [(12, 100, 0, 300), (11, 250, 300, 400), (9, 30, 700, 100)]
+    outb = harness.run_batch(runb, reqs)
+    harness.check_batch_against_oracle(runb, outb, reqs)
+    b = harness.run_batch(runb, reqs, fused=False)
+    for k in ("y", "k_cache", "v_cache", "expert_idx"):
+        assert _same_bytes(outb[k], b[k]), k
+
+
+def test_two_token_tiles_full_width():
+    # swa_fp4 verifying 32 tokens (history 8,176): every token against the oracle
+    w = synth.WORKLOADS["swa_fp4"].with_(T=32)
+    _log("tiles2 full: generating")
+    run = harness.GpuRun(w)
+    out = run.run(fused=True, T=32, pos=w.pos - 16)
+    rep = {}
+    _log("tiles2 full: oracle")
+    harness.check_against_oracle(run, out, report=rep)
+    _log(f"tiles2 full: {rep}")
 
 
 # ---------------------------------------------------------------- full-width workloads
@@ -407,8 +495,8 @@ def test_expert_n_shards_equal_full_width_rows(down):
     run_f = harness.GpuRun(full)
     out_f = run_f.run(fused=True)
     k, I = full.top_k, full.inter
-    a_f = run_f.plan.scratch("a").view(16 * k, I).clone()
-    aq_f = run_f.plan.scratch("aq").view(16 * k, I).clone() if down else None
+    a_f = run_f.plan.scratch("a").view(binding.MOEL_MAX_TOKENS * k, I).clone()
+    aq_f = run_f.plan.scratch("aq").view(binding.MOEL_MAX_TOKENS * k, I).clone() if down else None
     S = 8
     il, plc = full.inter // S, full.pooled // S
     for rank in (0, 3, 7):
@@ -423,10 +511,10 @@ def test_expert_n_shards_equal_full_width_rows(down):
         out_s = run_s.run(fused=True)
         assert torch.equal(out_s["expert_idx"], out_f["expert_idx"])
         cols = slice(rank * il, (rank + 1) * il)
-        a_s = run_s.plan.scratch("a").view(16 * k, I)
+        a_s = run_s.plan.scratch("a").view(binding.MOEL_MAX_TOKENS * k, I)
         assert _same_bytes(a_s[:, cols], a_f[:, cols]), rank
         if down:
-            aq_s = run_s.plan.scratch("aq").view(16 * k, I)
+            aq_s = run_s.plan.scratch("aq").view(binding.MOEL_MAX_TOKENS * k, I)
             assert _same_bytes(aq_s[:, cols], aq_f[:, cols]), rank
         run_s.plan.close()
         _log(f"n-shard rank {rank}: gate/up rows bitwise equal to the full-width layer's")
