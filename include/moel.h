@@ -2,7 +2,8 @@
  * moel.h -- C ABI of the MI355X (gfx950) MoE decoder-layer verify step.
  *
  * One call runs one decoder layer of a mixture-of-experts model for the batch-1
- * speculative-verify step: T <= 16 draft tokens of one request go through
+ * speculative-verify step: T draft tokens of one request (the pages verify 16; the library
+ * takes up to MOEL_MAX_TOKENS = 32, as two 16-token tiles) go through
  *   RMSNorm -> QKV projection + rotate-half RoPE + KV-cache write -> GQA attention
  *   (sliding window or global) -> o-projection + residual -> RMSNorm -> top-k router
  *   and pooler -> SwiGLU experts (NVFP4 or bf16) -> weighted combine -> unpooler +
@@ -133,7 +134,7 @@ int32_t moel_abi_version(void);
 /* Checks that `cfg` is a shape the kernels support.  Pure host code. */
 moel_status moel_validate_config(const moel_config* cfg);
 
-/* Checks the per-call arguments of moel_layer_decode against `cfg`: 1 <= T <= 16,
+/* Checks the per-call arguments of moel_layer_decode against `cfg`: 1 <= T <= MOEL_MAX_TOKENS,
  * pos >= 0, pos + T <= kv_capacity, window >= 0, non-NULL 16-byte-aligned pointers,
  * y not aliasing x.  Pure host code (pointers are only compared, never dereferenced). */
 moel_status moel_validate_call(const moel_config* cfg, const moel_weights* w,
@@ -201,10 +202,11 @@ moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* strea
 
 /* Intermediate activations of the last completed step, for tests and profiling tools
  * (all fp32, row-major, rows = tokens or token slots):
- *   0 q [16][Hq*D] after RoPE      1 o [16][Hq*D] attention output   2 h [16][H]
- *   3 router logits [16][E]        4 pl [16][P] pooled vector        5 a [16*k][I] SwiGLU out
- *   6 d [16*k][P] expert outputs   7 m [16][P] combined vector
- *   8 aq [16*k][I] with down_input NVFP4: the down projection's input as E2M1 value times
+ * (R = MOEL_MAX_TOKENS rows; the step's T come first)
+ *   0 q [R][Hq*D] after RoPE       1 o [R][Hq*D] attention output    2 h [R][H]
+ *   3 router logits [R][E]         4 pl [R][P] pooled vector         5 a [R*k][I] SwiGLU out
+ *   6 d [R*k][P] expert outputs    7 m [R][P] combined vector
+ *   8 aq [R*k][I] with down_input NVFP4: the down projection's input as E2M1 value times
  *     E4M3 block scale (its tensor scale multiplies the projection's sums)
  * *ptr receives a device pointer into the plan's workspace (owned by the plan; valid until
  * moel_plan_destroy; overwritten by the next step), *bytes its size.  o, m, pl, a and aq
@@ -302,8 +304,9 @@ typedef struct moel_request {
 
 /* Checks a batch on the host: 1 <= n_requests <= MOEL_MAX_REQUESTS, every request as described
  * above, the requests' slot ranges pairwise disjoint, the sum of T at most MOEL_MAX_TOKENS, and
- * n_requests * n_kv_heads attention items no more than the workgroups (workgroups = 0 skips
- * that check).  MOEL_ERR_ARG on any violation (MOEL_ERR_SHAPE for the last one). */
+ * n_requests * n_kv_heads * (16-token tiles of the step) attention items no more than the
+ * workgroups (workgroups = 0 skips that check).  MOEL_ERR_ARG on any violation (MOEL_ERR_SHAPE
+ * for the last one). */
 moel_status moel_validate_batch(const moel_config* cfg, int32_t n_requests, const moel_request* requests,
                                 int32_t workgroups);
 
@@ -341,7 +344,7 @@ typedef struct moel_stack moel_stack;
  *   weights[l], k_caches[l], v_caches[l], windows[l]: layer l as for moel_layer_decode (HOST
  *     arrays of n_layers entries, copied; the device buffers they point to stay caller-owned and
  *     must outlive the stack).
- * Allocates two [16, hidden] fp32 device buffers for the rows between layers.  *out is set only
+ * Allocates two [MOEL_MAX_TOKENS, hidden] fp32 device buffers for the rows between layers.  *out is set only
  * on success.  Not for the hot path.  The stack uses the plan's workspace: steps of a plan's
  * stack and of the plan itself must not overlap (they are ordered when issued on one stream). */
 moel_status moel_stack_create(moel_plan* plan, int32_t n_layers, const moel_weights* weights,
