@@ -1246,7 +1246,8 @@ moel_status moel_stack_decode(moel_stack* st, const float* x, int32_t T, int32_t
   if (st == nullptr) return MOEL_ERR_ARG;
   moel_plan* plan = st->plan;
   const int n = st->n;
-  const size_t ab = sizeof(float) * kMaxT * (size_t)plan->cfg.hidden;
+  if (T < 1 || T > kMaxT) return MOEL_ERR_ARG;
+  const size_t ab = sizeof(float) * (size_t)T * (size_t)plan->cfg.hidden;  // the step's rows
   const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
   if (xb < yb + ab && yb < xb + ab) return MOEL_ERR_ARG;  // y must not alias x
   // every layer's arguments are checked before anything is issued; the layers' rows go

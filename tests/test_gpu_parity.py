@@ -547,11 +547,12 @@ def test_read_bandwidth_reference():
 def test_stack_launch_equals_layer_by_layer():
     """Layers of one shape in one persistent launch (moel_stack_decode; grid barriers between the
     layers) give bitwise the rows and caches of moel_layer_decode called layer by layer: a global
-    layer and two sliding-window ones, several calls in a row with 16, 5, 1 and 9 tokens (with
+    layer and two sliding-window ones, several calls in a row with 16, 5, 1, 9 and 32 tokens (with
     few tokens the expert tiles of consecutive layers land on different XCDs, the case where an
     XCD's L2 keeps its own copy of a rewritten workspace line unless the layer boundary drops it);
-    and a stack of 8 layers, which takes two launches (6 + 2)."""
-    w = synth.small_workload(T=16, pos=300, window=64, n_experts=32, top_k=8, pooled=512, inter=512, hidden=1024,
+    and a stack of 8 layers, which takes two launches, its input and output rows adjacent in one
+    buffer."""
+    w = synth.small_workload(T=32, pos=300, window=64, n_experts=32, top_k=8, pooled=512, inter=512, hidden=1024,
                              n_q_heads=8, n_kv_heads=2, head_dim=128)
     plan = binding.Plan(binding.config_from_workload(w))
     windows = [0, 64, 7]
@@ -561,7 +562,7 @@ def test_stack_launch_equals_layer_by_layer():
     v0 = [t["v_cache"] for t in ts]
     kc, vc = [k.clone() for k in k0], [v.clone() for v in v0]
     st = binding.Stack(plan, lws, kc, vc, windows)
-    for T, pos in ((16, 300), (5, 120), (5, 120), (1, 77), (9, 200)):
+    for T, pos in ((16, 300), (5, 120), (5, 120), (1, 77), (9, 200), (32, 284)):
         x = ts[0]["x"][:T].contiguous()
         y_ref, k_ref, v_ref = _layer_by_layer(plan, lws, k0, v0, windows, x, pos)
         for l in range(3):
@@ -579,11 +580,12 @@ def test_stack_launch_equals_layer_by_layer():
     lws8 = [lws[l % 3] for l in range(8)]
     k8, v8 = [k0[l % 3].clone() for l in range(8)], [v0[l % 3].clone() for l in range(8)]
     win8 = [windows[l % 3] for l in range(8)]
-    x = ts[0]["x"].contiguous()
+    rows = torch.full((32, w.hidden), float("nan"), dtype=torch.float32, device="cuda")
+    x, y = rows[:16], rows[16:]  # adjacent, not overlapping
+    x.copy_(ts[0]["x"][:16])
     y_ref, k_ref, v_ref = _layer_by_layer(plan, lws8, k8, v8, win8, x, 300)
     kc8, vc8 = [k.clone() for k in k8], [v.clone() for v in v8]
     st8 = binding.Stack(plan, lws8, kc8, vc8, win8)
-    y = torch.full_like(x, float("nan"))
     st8.decode(x, 300, y)
     torch.cuda.synchronize()
     assert plan.status() == binding.MOEL_OK
