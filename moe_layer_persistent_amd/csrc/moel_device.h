@@ -161,6 +161,7 @@ enum CtrlWord {
   kGroup = 96,    // + 32 * g: workgroups of group g arrived (monotonic within a launch)
   kWork = 352,    // + 32 * i: tiles handed out so far by expert phase i (0 gate/up, 1 down)
   kXccMask = 416, // + 32 * g: bit x set when a workgroup of barrier group g runs on XCC x
+  kEntered = 672, // workgroups that have recorded their XCC in kXccMask
   kFix = 1024,    // + kFixPerPhase * i + b: split-K units of block b of dense phase i arrived
   kCtrlWords = 2048
 };
@@ -193,6 +194,20 @@ __device__ __forceinline__ void acq_rel_fence(int l2_coherent) {
 // XCC (accelerator complex die, one L2) of the calling wave.
 __device__ __forceinline__ unsigned xcc_id() {
   return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20);  // XCC_ID[3:0]
+}
+
+// True when every barrier group of the launch is known to run on one XCC: all workgroups have
+// recorded their XCC (each records its bit before it counts itself in) and every group's mask
+// has one bit.  It can be false early in the launch (a workgroup not yet started); it is never
+// true wrongly.  Thread 0.
+__device__ __forceinline__ bool groups_single_xcc(KP& p) {
+  auto ctrl = gl(p.ctrl);
+  if (__hip_atomic_load(ctrl + kEntered, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (unsigned)p.nwg) return false;
+  const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+  bool ok = true;
+  for (int g = 0; g < ng_all; ++g)
+    ok &= __popc(__hip_atomic_load(ctrl + kXccMask + 32 * g, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == 1;
+  return ok;
 }
 
 // Grid-wide barrier number b (1, 2, ... within one launch) of the persistent launch.
@@ -232,7 +247,9 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = fal
     const int g = (int)blockIdx.x % ng_all;
     const unsigned n_g = (unsigned)((p.nwg - g + ng_all - 1) / ng_all);
     auto ctrl = gl(p.ctrl);
-    if (!light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // a member's release can be left to its group's last arrival (which releases in either
+    // mode) once the groups are known to run on one XCC each
+    if (!light && !groups_single_xcc(p)) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned prev = __hip_atomic_fetch_add(ctrl + kGroup + 32 * g, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev + 1 == b * n_g) {

@@ -69,8 +69,11 @@ __device__ __forceinline__ bool launch_enter(KP& p) {
     s_abort = aborted(p) ? 1 : 0;
     R.light = 0;
     const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
-    __hip_atomic_fetch_or(gl(p.ctrl) + kXccMask + 32 * ((int)blockIdx.x % ng_all), 1u << xcc_id(),
-                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // the mask bit is recorded (the returning atomic has completed) before the entry count
+    const unsigned m = __hip_atomic_fetch_or(gl(p.ctrl) + kXccMask + 32 * ((int)blockIdx.x % ng_all),
+                                             1u << xcc_id(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" : : "v"(m) : "memory");
+    __hip_atomic_fetch_add(gl(p.ctrl) + kEntered, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   return s_abort == 0;
@@ -101,6 +104,7 @@ __device__ __forceinline__ void launch_exit(KP& p, bool run) {
         __hip_atomic_store(ctrl + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       for (int g = 0; g < kBarGroups; ++g)
         __hip_atomic_store(ctrl + kXccMask + 32 * g, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(ctrl + kEntered, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ctrl + kExit, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

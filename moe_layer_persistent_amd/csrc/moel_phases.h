@@ -496,13 +496,22 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   __syncthreads();
   if (threadIdx.x == 0) {
     auto cnt = gl(p.ctrl) + kFix + kFixPerPhase * fix_id + b;
-    const bool light = route_tables(moel_lds).light != 0 && nwg % (8 * nsplit) == 0;
+    // a block's units share a barrier group (hence, once the groups are known to run on one
+    // XCC each, one L2) when nwg is a multiple of 8 nsplit.  Before the launch's first barrier
+    // has settled that, a unit proves it itself (groups_single_xcc) and counts in with bit 16
+    // set: if any unit of the block proved it, every unit's partials are in the last unit's L2
+    const bool known = route_tables(moel_lds).light != 0;
+    const bool one_group = nwg % (8 * nsplit) == 0;
+    const bool proven = !known && one_group && groups_single_xcc(p);
+    const bool light = (known && one_group) || proven;
     if (!light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    const unsigned prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const int last = prev == (unsigned)nsplit - 1;
+    const unsigned inc = proven ? 0x10001u : 1u;
+    const unsigned prev = __hip_atomic_fetch_add(cnt, inc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int last = (prev & 0xffffu) == (unsigned)nsplit - 1;
     if (last) {
       __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // for the next launch
-      if (light) asm volatile("buffer_inv sc0" ::: "memory");
+      const bool any_light = light || ((prev + inc) >> 16) != 0;
+      if (any_light) asm volatile("buffer_inv sc0" ::: "memory");
       else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     L.last = last;
