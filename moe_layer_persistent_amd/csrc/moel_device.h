@@ -162,6 +162,7 @@ enum CtrlWord {
   kWork = 352,    // + 32 * i: tiles handed out so far by expert phase i (0 gate/up, 1 down)
   kXccMask = 416, // + 32 * g: bit x set when a workgroup of barrier group g runs on XCC x
   kEntered = 672, // workgroups that have recorded their XCC in kXccMask
+  kAttnDone = 704,// + 32 * q: attention items of group q written (merged per barrier group)
   kFix = 1024,    // + kFixPerPhase * i + b: split-K units of block b of dense phase i arrived
   kCtrlWords = 2048
 };

@@ -29,7 +29,10 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   // reads anyway
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
   if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
-  if constexpr (PH == kPhAttnMerge) phase_attn_merge(p, wg);
+  if constexpr (PH == kPhAttnMerge) {
+    if (p.attn_set_merge) phase_attn_merge_set(p, wg);
+    else phase_attn_merge(p, wg);
+  }
   if constexpr (PH == kPhOproj) phase_oproj(p, wg, smem);
   if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, smem);
   if constexpr (PH == kPhGemm1) {
@@ -128,7 +131,8 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   stamp(16 + kPhAttn);
   if (run) fused_phase<kPhAttn, D>(ph, wg);
   stamp(kPhAttn);
-  sync();
+  // with the merge per barrier group the merging workgroups wait for their group's items
+  if (!p.attn_set_merge) sync();
   stamp(16 + kPhAttnMerge);
   if (run) fused_phase<kPhAttnMerge, D>(ph, wg);
   stamp(kPhAttnMerge);
@@ -150,11 +154,15 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   stamp(kPhGemm2);
   sync();
   stamp(16 + kPhCombine);
-  // the expert phases' work counters are free again once both expert phases have passed a
-  // barrier: cleared here for the next layer of the launch (or the next launch)
-  if (wg == 0 && threadIdx.x == 0)
+  // the expert phases' work counters (and the attention groups' item counts) are free again
+  // once both expert phases (the merge) have passed a barrier: cleared here for the next layer
+  // of the launch (or the next launch)
+  if (wg == 0 && threadIdx.x == 0) {
     for (int i = 0; i < 2; ++i)
       __hip_atomic_store(gl(p.ctrl) + kWork + 32 * i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    for (int q = 0; q < kBarGroups; ++q)
+      __hip_atomic_store(gl(p.ctrl) + kAttnDone + 32 * q, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (run) fused_phase<kPhCombine, D>(ph, wg);
   stamp(kPhCombine);
   sync();
@@ -782,6 +790,17 @@ moel_status fill_call_batch(const moel_config* cfg, const LayerParams& base, int
   }
   p.req_ch0[n_req] = ch;
   p.attn_nchunks = ch;
+  // the merge per barrier group: every attention group (kv head, token tile) on a barrier group
+  // of its own, with one item per workgroup of it (MOEL_ATTN_SET_MERGE=0 turns it off, for
+  // measurement)
+  {
+    static const int allow = [] {
+      const char* e = std::getenv("MOEL_ATTN_SET_MERGE");
+      return e == nullptr || std::atoi(e) != 0;
+    }();
+    const int ns = base.nwg < kBarGroups ? base.nwg : kBarGroups;
+    p.attn_set_merge = allow && cfg->n_kv_heads * p.ntt <= ns && ch <= base.nwg / ns ? 1 : 0;
+  }
   p.gamma1 = static_cast<const uint16_t*>(w->gamma1);
   p.gamma2 = static_cast<const uint16_t*>(w->gamma2);
   p.w_qkv = static_cast<const uint8_t*>(w->w_qkv);
@@ -911,7 +930,10 @@ moel_status launch_fused(moel_plan* plan, LayerParams& p, void* stream) {
                                        static_cast<hipStream_t>(stream));
   return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
 }
-moel_status launch_unfused(moel_plan* plan, LayerParams& p, void* stream) {
+moel_status launch_unfused(moel_plan* plan, LayerParams& p_call, void* stream) {
+  // the chain's kernels end at their own boundaries: the merge is a kernel of its own
+  LayerParams p = p_call;
+  p.attn_set_merge = 0;
   void* args[] = {&p};
   for (int ph = kPhQkv; ph < kNumPhases; ++ph) {  // step 0 is part of step 1
     const void* fn = plan->cfg.head_dim == 64 ? phase_fn<64>(ph) : phase_fn<128>(ph);

@@ -58,6 +58,11 @@ struct LayerParams {
   // chunks req_ch0[r] .. req_ch0[r+1]-1 (attn_nchunks = req_ch0[n_req] in all)
   int attn_chunk, attn_nchunks;
   int req_ch0[MOEL_MAX_REQUESTS + 1];
+  // 1: the persistent launch merges the key-chunk partials without a grid barrier in between:
+  // group q = (kv head q mod Hkv, token tile q / Hkv) has its attn_nchunks items and its merge
+  // on the workgroups of barrier group q (q < 8, at most nwg / 8 items each); its items count
+  // in on a control word and its merging workgroups wait for that count
+  int attn_set_merge;
   // the step's tokens as the nodes of token trees (a chain per request for the linear verify):
   // token t of request r (req_t0[r] <= t < req_t0[r+1]) is at position tok_pos[t] (RoPE) and
   // writes its key and value at pool slot req_kvb[r] + req_pos[r] + t - req_t0[r]; bit i of

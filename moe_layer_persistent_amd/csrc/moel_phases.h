@@ -672,7 +672,19 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
   // this thread's place in a sub-chunk's staging: 16-byte column c8 of rows row0 + i * RSTEP
   constexpr int RSTEP = kThreads / (D / 8);
   const int row0 = threadIdx.x / (D / 8), c8 = (threadIdx.x % (D / 8)) * 8;
-  for (int it = wg; it < nitems; it += p.nwg) {
+  // this workgroup's items: every nwg-th from wg; with the merge per barrier group, chunk j of
+  // group q = wg mod 8 (kv head q mod Hkv, token tile q / Hkv) on the group's j-th workgroup
+  int it0 = wg, istep = p.nwg, q_set = -1;
+  if (p.attn_set_merge) {
+    const int ns = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+    const int q = wg % ns, j = wg / ns;
+    it0 = istep = nitems;
+    if (q < p.Hkv * p.ntt && j < p.attn_nchunks) {
+      it0 = (j * p.Hkv + q % p.Hkv) * p.ntt + q / p.Hkv;
+      q_set = q;
+    }
+  }
+  for (int it = it0; it < nitems; it += istep) {
     const int ib = it / p.ntt, tile = it - ib * p.ntt;  // (head, chunk) item and token tile
     const int g = ib % p.Hkv, cc = ib / p.Hkv;  // kv head, flat chunk
     // the chunk's request rq and its chunk c within the request (uniform)
@@ -862,52 +874,106 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
       }
     }
   }
+  if (q_set >= 0) {
+    // count the item in on its group: its partial is complete in this XCC's L2 (vmcnt(0)), which
+    // the group's merging workgroups share when the barrier groups run on one XCC each
+    // (otherwise the release writes it back)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      if (route_tables(moel_lds).light == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(gl(p.ctrl) + kAttnDone + 32 * q_set, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
-// Merge the key-chunk partials of every (token, q head) row -> o (fp32).  A chunk with no
-// visible key for a token has m = -inf, weight exp(-inf) = 0 and O = l = 0.  One thread per
-// head-dim value; chunks go in groups of 16 whose loads are all in flight together, merged
-// into a running (max, numerator, denominator) with the usual rescale between groups.
-__device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
+// Merge the key-chunk partials of one (token t, q head h, head-dim d) element -> o (fp32).  A
+// chunk with no visible key for a token has m = -inf, weight exp(-inf) = 0 and O = l = 0.
+// Chunks go in groups of 16 whose loads are all in flight together, merged into a running
+// (max, numerator, denominator) with the usual rescale between groups.
+__device__ __forceinline__ void merge_element(KP& p, int t, int h, int d) {
   const int grp = p.Hq / p.Hkv;
-  const int total = p.T * p.Hq * p.D;
   const int nch = p.attn_nchunks;
   constexpr int U = 16;
   const float NEG = -__builtin_inff();
+  const int g = h / grp, w = h % grp;
+  // row (item it, head w, token t) of the partials, item it = c * Hkv + g
+  const size_t row0 = (size_t)(g * grp + w) * kMaxT + t;  // chunk 0
+  const size_t rstep = (size_t)p.Hkv * grp * kMaxT;       // next chunk
+  float M = NEG, num = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += U) {
+    f32x2 ml[U];
+    float ov[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const int c = c0 + j < nch ? c0 + j : nch - 1;
+      const size_t row = row0 + (size_t)c * rstep;
+      ml[j] = *gl(reinterpret_cast<const f32x2*>(p.attn_ml + row * 2));
+      ov[j] = gl(p.attn_o)[row * p.D + d];
+    }
+    float Mg = M;
+#pragma unroll
+    for (int j = 0; j < U; ++j) Mg = fmaxf(Mg, ml[j][0]);
+    const float r = M == NEG ? 0.f : __builtin_amdgcn_exp2f(M - Mg);  // rescale of the earlier groups (base 2)
+    num *= r;
+    den *= r;
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+      const float wgt = (c0 + j < nch && ml[j][0] != NEG) ? __builtin_amdgcn_exp2f(ml[j][0] - Mg) : 0.f;
+      num = fmaf(wgt, ov[j], num);
+      den = fmaf(wgt, ml[j][1], den);
+    }
+    M = Mg;
+  }
+  const float o = num / den;
+  if (p.debug_copies) gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
+  store_opsplit(gl(p.o_op), t, h * p.D + d, p.Hq * p.D, o);
+}
+
+// Merge of every (token, q head) row over all workgroups, one thread per head-dim value (after
+// a grid barrier, or in its own kernel).
+__device__ __forceinline__ void phase_attn_merge(KP& p, int wg) {
+  const int total = p.T * p.Hq * p.D;
   for (int e = wg * kThreads + threadIdx.x; e < total; e += p.nwg * kThreads) {
     const int d = e % p.D, h = (e / p.D) % p.Hq, t = e / (p.D * p.Hq);
-    const int g = h / grp, w = h % grp;
-    // row (item it, head w, token t) of the partials, item it = c * Hkv + g
-    const size_t row0 = (size_t)(g * grp + w) * kMaxT + t;  // chunk 0
-    const size_t rstep = (size_t)p.Hkv * grp * kMaxT;       // next chunk
-    float M = NEG, num = 0.f, den = 0.f;
-    for (int c0 = 0; c0 < nch; c0 += U) {
-      f32x2 ml[U];
-      float ov[U];
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const int c = c0 + j < nch ? c0 + j : nch - 1;
-        const size_t row = row0 + (size_t)c * rstep;
-        ml[j] = *gl(reinterpret_cast<const f32x2*>(p.attn_ml + row * 2));
-        ov[j] = gl(p.attn_o)[row * p.D + d];
+    merge_element(p, t, h, d);
+  }
+}
+
+// Merge per barrier group (attn_set_merge): the workgroups of barrier group q merge the rows of
+// attention group q (kv head q mod Hkv, token tile q / Hkv) once its items have counted in, with
+// no grid barrier between the items and the merge.  The same arithmetic per element as
+// phase_attn_merge, so the results are bitwise those of the barrier-separated merge.
+__device__ __forceinline__ void phase_attn_merge_set(KP& p, int wg) {
+  const int ns = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+  const int q = wg % ns, j = wg / ns, nq = (p.nwg - q + ns - 1) / ns;
+  if (q >= p.Hkv * p.ntt) return;
+  const int grp = p.Hq / p.Hkv, g = q % p.Hkv, tile = q / p.Hkv;
+  const int t0 = kTile * tile;
+  const int tn = p.T - t0 < kTile ? p.T - t0 : kTile;
+  const int total = tn * grp * p.D;
+  if (j * kThreads >= total) return;  // no element here: nothing to wait for
+  if (threadIdx.x == 0) {
+    auto cnt = gl(p.ctrl) + kAttnDone + 32 * q;
+    const unsigned need = (unsigned)p.attn_nchunks;
+    const uint64_t ts0 = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+      __builtin_amdgcn_s_sleep(1);
+      if (__builtin_amdgcn_s_memrealtime() - ts0 > 50000000ull) {
+        __hip_atomic_store(gl(p.ctrl) + kStatus, (unsigned)MOEL_DEV_TIMEOUT, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        break;
       }
-      float Mg = M;
-#pragma unroll
-      for (int j = 0; j < U; ++j) Mg = fmaxf(Mg, ml[j][0]);
-      const float r = M == NEG ? 0.f : __builtin_amdgcn_exp2f(M - Mg);  // rescale of the earlier groups (base 2)
-      num *= r;
-      den *= r;
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        const float wgt = (c0 + j < nch && ml[j][0] != NEG) ? __builtin_amdgcn_exp2f(ml[j][0] - Mg) : 0.f;
-        num = fmaf(wgt, ov[j], num);
-        den = fmaf(wgt, ml[j][1], den);
-      }
-      M = Mg;
     }
-    const float o = num / den;
-    if (p.debug_copies) gl(p.o_buf)[(size_t)t * p.Hq * p.D + h * p.D + d] = o;
-    store_opsplit(gl(p.o_op), t, h * p.D + d, p.Hq * p.D, o);
+    // the items' partials: in this XCC's L2 (light: invalidate the L1 only), else written back
+    // by their releases (drop the L2's clean lines too)
+    if (route_tables(moel_lds).light != 0) asm volatile("buffer_inv sc0" ::: "memory");
+    else __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  }
+  __syncthreads();
+  for (int e = j * kThreads + threadIdx.x; e < total; e += nq * kThreads) {
+    const int d = e % p.D, hw = (e / p.D) % grp, tt = e / (p.D * grp);
+    merge_element(p, t0 + tt, g * grp + hw, d);
   }
 }
 
