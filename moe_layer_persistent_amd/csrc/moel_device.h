@@ -240,7 +240,11 @@ __device__ __forceinline__ bool groups_single_xcc(KP& p) {
 // waits for the release word, so nothing on that XCC loads again before the barrier ends, and
 // every store of the barrier's other workgroups is written back before the word is set: after
 // the barrier the XCC's L2 holds nothing from before it, at one invalidation per XCC.
-__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false, bool drop_l2 = false) {
+//
+// proven (thread 0, optional): set when this workgroup proved on arrival that every barrier group
+// runs on one XCC (so the caller need not read the group masks again).
+__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false, bool drop_l2 = false,
+                                             bool* proven = nullptr) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -250,7 +254,9 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = fal
     auto ctrl = gl(p.ctrl);
     // a member's release can be left to its group's last arrival (which releases in either
     // mode) once the groups are known to run on one XCC each
-    if (!light && !groups_single_xcc(p)) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const bool single = !light && groups_single_xcc(p);
+    if (!light && !single) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    if (proven != nullptr) *proven = single;
     const unsigned prev = __hip_atomic_fetch_add(ctrl + kGroup + 32 * g, 1u, __ATOMIC_RELAXED,
                                                  __HIP_MEMORY_SCOPE_AGENT);
     if (prev + 1 == b * n_g) {

@@ -48,15 +48,20 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
 // groups' XCC masks (written at launch): when every group runs on one XCC, the rest of the
 // launch's barriers and split-K fix-ups release per XCC (`light`, kept in RouteTables::light).
 __device__ __forceinline__ void launch_barrier(KP& p, unsigned& bar, bool& light) {
-  grid_barrier(p, ++bar, light);
+  bool proven = false;
+  grid_barrier(p, ++bar, light, false, &proven);
   if (bar == 1) {
     RouteTables& R = route_tables(moel_lds);
     if (threadIdx.x == 0) {
+      // proven on arrival: the masks are final (every workgroup recorded its bit before it
+      // counted itself in), so they need no second read
       int ok = 1;
-      const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
-      for (int g = 0; g < ng_all; ++g)
-        ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT)) == 1;
+      if (!proven) {
+        const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
+        for (int g = 0; g < ng_all; ++g)
+          ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT)) == 1;
+      }
       R.light = ok;
     }
     __syncthreads();
