@@ -387,8 +387,8 @@ def stack_bench(steps: int, warmup: int, copy_calibration: bool = False, unfused
     stream = torch.cuda.current_stream()
     bufs = [x0.clone(), torch.empty_like(x0)]
 
-    def step(fused=True, idx=None):
-        bufs[0].copy_(x0)
+    def step(fused=True, idx=None, x=None):
+        bufs[0].copy_(x0 if x is None else x)
         for l in range(w.n_layers):
             xin, yout = bufs[l % 2], bufs[(l + 1) % 2]
             dbg = None if idx is None else {"expert_idx": idx[l]}
@@ -429,8 +429,43 @@ def stack_bench(steps: int, warmup: int, copy_calibration: bool = False, unfused
     if unfused:
         unfused_us = timed(False, max(2, steps // 2), 1)
         progress(f"stack: one kernel per step {unfused_us / w.n_layers:.1f} us/layer")
-    stack_us, phases = None, {}
+    stack_us, phases, prefetch = None, {}, None
     if extras:
+        # previous-step expert prefetch (the 14 experts each layer's previous step used most,
+        # ~50 MB per layer at this share): every step with the same input rows (the routing the
+        # prefetch bets on repeats exactly), and steps alternating between two inputs (the bet
+        # is lost more often)
+        hists = [torch.zeros(w.n_experts, dtype=torch.int32, device=dev) for _ in range(w.n_layers)]
+        for lw, h in zip(layers, hists):
+            lw.set_history(h)
+        plan.set_expert_prefetch(14)
+        same_us = timed(True, steps, warmup)
+        x_alt = (0.5 * x0.flip(0)).contiguous()
+
+        def timed_alt(n):
+            for i in range(2):
+                step(True, x=x0 if i % 2 else x_alt)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for i in range(n):
+                step(True, x=x0 if i % 2 else x_alt)
+            b.record(stream)
+            torch.cuda.synchronize()
+            st = plan.status()
+            assert st == 0, binding.status_string(st)
+            return a.elapsed_time(b) * 1e3 / n
+        alt_us = timed_alt(max(2, steps))
+        plan.set_expert_prefetch(0)
+        off_alt_us = timed_alt(max(2, steps))
+        for lw in layers:
+            lw.set_history(None)
+        del hists
+        prefetch = {"experts": 14, "us_per_layer_same_routing": round(same_us / w.n_layers, 2),
+                    "us_per_layer_alternating_inputs": round(alt_us / w.n_layers, 2),
+                    "us_per_layer_alternating_inputs_off": round(off_alt_us / w.n_layers, 2),
+                    "us_per_layer_off": round(step_us / w.n_layers, 2)}
+        progress(f"stack: expert prefetch {prefetch}")
         # the stack through moel_stack_decode: binding.STACK_LAYERS_PER_LAUNCH layers per persistent
         # launch (grid barriers between them)
         stk = binding.Stack(plan, layers, [c[0] for c in caches], [c[1] for c in caches],
@@ -478,6 +513,8 @@ def stack_bench(steps: int, warmup: int, copy_calibration: bool = False, unfused
     if unfused_us is not None:
         out["unfused_chain"] = {"verify_step_us": round(unfused_us, 1),
                                 "us_per_layer": round(unfused_us / w.n_layers, 2), "launches_per_layer": 10}
+    if prefetch is not None:
+        out["expert_prefetch"] = prefetch
     if stack_us is not None:
         out["stack_launches"] = {"verify_step_us": round(stack_us, 1), "us_per_layer": round(stack_us / w.n_layers, 2),
                                  "tokens_per_s": round(ACCEPTED_PER_STEP / (stack_us * 1e-6), 1),

@@ -37,7 +37,7 @@ extern "C" {
 #endif
 
 #define MOEL_MAX_TOKENS 32
-#define MOEL_ABI_VERSION 6
+#define MOEL_ABI_VERSION 7
 
 typedef enum moel_status {
   MOEL_OK = 0,
@@ -110,6 +110,13 @@ typedef struct moel_weights {
   const float* ts_down;
   const float* ts_act;    /* fp32 [E] activation tensor scales, > 0 (down_input NVFP4,
                            * else ignored)                                              */
+  uint32_t* expert_hist;  /* uint32 [E] this layer's routing history, caller-owned device
+                           * memory, 4-byte aligned (NULL: none).  Every step of the layer
+                           * writes, per expert, how many of its tokens chose it; with the
+                           * plan's expert prefetch on (moel_plan_set_expert_prefetch) a step
+                           * first reads what the previous step wrote.  Zero it before the
+                           * layer's first step.  Steps of one layer on different streams
+                           * race on it.                                                  */
 } moel_weights;
 
 /* Optional outputs for tests and profiling; any member may be NULL. */
@@ -195,6 +202,20 @@ moel_status moel_plan_set_acquire(moel_plan* plan, int32_t mode);
  * a release fence, were seen by readers on every XCD after an L1-only invalidation, with no
  * stale word in four trials), 0 if not, -1 for a null plan. */
 int32_t moel_plan_l2_coherent(const moel_plan* plan);
+
+/* Previous-step expert prefetch (orcarouter.ai English post, "Three bills a kernel this big has
+ * to pay": while the layer runs, one warp reads which experts the previous step routed to and
+ * pulls this GPU's slices of the most-used ones into the last-level cache, betting that
+ * consecutive steps route alike).  n_experts = 0 (default) turns it off; 1..16 enables it for
+ * layers whose moel_weights.expert_hist is set: the step reads the history, takes the
+ * n_experts experts that most of the previous step's tokens chose (ties to the lower index;
+ * experts no token chose are left out), and the workgroups that have no attention work read
+ * those experts' packed gate, up and down weights once with ordinary loads while attention
+ * runs, so that the memory-side cache holds them when the expert phases stream them.  It
+ * changes no result (bitwise).  Persistent launches only (moel_layer_decode, the tree and batch
+ * variants, moel_stack_decode); the one-kernel-per-step chain still writes the history but
+ * does not prefetch.  Returns MOEL_ERR_ARG for a null plan or n_experts outside 0..16. */
+moel_status moel_plan_set_expert_prefetch(moel_plan* plan, int32_t n_experts);
 
 /* Sets (1) or clears (0) the plan's abort word.  While set, launched kernels skip all
  * work, leave every caller buffer untouched and report MOEL_ERR_ABORTED. */

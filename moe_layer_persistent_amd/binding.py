@@ -54,7 +54,7 @@ class Config(ctypes.Structure):
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
         "gamma1", "gamma2", "w_qkv", "w_o", "w_router", "w_pool", "w_unpool", "w_gate", "w_up",
-        "w_down", "ts_gate", "ts_up", "ts_down", "ts_act")]
+        "w_down", "ts_gate", "ts_up", "ts_down", "ts_act", "expert_hist")]
 
 
 class Request(ctypes.Structure):
@@ -99,6 +99,7 @@ def lib() -> ctypes.CDLL:
             "moel_plan_set_abort": (i32, [vp, i32, vp]),
             "moel_plan_set_launch": (i32, [vp, i32]),
             "moel_plan_set_acquire": (i32, [vp, i32]),
+            "moel_plan_set_expert_prefetch": (i32, [vp, i32]),
             "moel_plan_l2_coherent": (i32, [vp]),
             "moel_plan_scratch": (i32, [vp, i32, P(vp), P(sz)]),
             "moel_pack_dense": (i32, [vp, i32, i32, i32, vp, vp]),
@@ -173,7 +174,14 @@ class LayerWeights:
             _ptr(packed["gamma1"]), _ptr(packed["gamma2"]), _ptr(packed["w_qkv"]), _ptr(packed["w_o"]),
             _ptr(packed["w_router"]), _ptr(packed["w_pool"]), _ptr(packed["w_unpool"]),
             _ptr(packed["w_gate"]), _ptr(packed["w_up"]), _ptr(packed["w_down"]),
-            _ptr(ts["gate"]), _ptr(ts["up"]), _ptr(ts["down"]), _ptr(ts.get("act")))
+            _ptr(ts["gate"]), _ptr(ts["up"]), _ptr(ts["down"]), _ptr(ts.get("act")), None)
+        self.history = None
+
+    def set_history(self, hist: Optional[torch.Tensor]):
+        """The layer's routing history (int32 or uint32 [E] device tensor, zeroed before the
+        layer's first step; None: none): each step writes its tokens per expert there."""
+        self.history = hist
+        self.struct.expert_hist = _ptr(hist)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.packed.values())
@@ -229,6 +237,11 @@ class Plan:
     def set_launch(self, mode: int):
         """MOEL_LAUNCH_PLAIN (default) or MOEL_LAUNCH_COOPERATIVE, see include/moel.h."""
         _check(lib().moel_plan_set_launch(self.handle, int(mode)), "moel_plan_set_launch")
+
+    def set_expert_prefetch(self, n_experts: int):
+        """Previous-step expert prefetch of the n_experts most-used experts (0 = off), for layers
+        whose weights carry a routing history (LayerWeights.set_history), see include/moel.h."""
+        _check(lib().moel_plan_set_expert_prefetch(self.handle, int(n_experts)), "moel_plan_set_expert_prefetch")
 
     def set_acquire(self, mode: int):
         """MOEL_ACQUIRE_AUTO (default) or MOEL_ACQUIRE_L2_INVALIDATE, see include/moel.h."""

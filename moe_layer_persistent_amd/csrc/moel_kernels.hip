@@ -37,6 +37,7 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, smem);
   if constexpr (PH == kPhGemm1) {
     compute_routing(p, route_tables(smem), wg == 0);
+    write_expert_hist(p, route_tables(smem), wg);
     phase_experts<true>(p, wg, smem);
   }
   if constexpr (PH == kPhGemm2) phase_experts<false>(p, wg, smem);
@@ -303,6 +304,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
   if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, smem);
   if constexpr (PH == kPhGemm1) {
     compute_routing(p, route_tables(smem), wg == 0);
+    write_expert_hist(p, route_tables(smem), wg);
     phase_experts<true>(p, wg, smem);
   }
   if constexpr (PH == kPhGemm2) {
@@ -820,6 +822,7 @@ moel_status fill_call_batch(const moel_config* cfg, const LayerParams& base, int
   p.ts_up = w->ts_up;
   p.ts_down = w->ts_down;
   p.ts_act = p.down_fp4 ? w->ts_act : nullptr;
+  p.expert_hist = w->expert_hist;
   p.k_cache = static_cast<uint16_t*>(k_cache);
   p.v_cache = static_cast<uint16_t*>(v_cache);
   p.x = x;
@@ -936,9 +939,11 @@ moel_status launch_fused(moel_plan* plan, LayerParams& p, void* stream) {
   return hip_ok(e) ? MOEL_OK : MOEL_ERR_HIP;
 }
 moel_status launch_unfused(moel_plan* plan, LayerParams& p_call, void* stream) {
-  // the chain's kernels end at their own boundaries: the merge is a kernel of its own
+  // the chain's kernels end at their own boundaries: the merge is a kernel of its own, and
+  // nothing runs beside attention (no expert prefetch)
   LayerParams p = p_call;
   p.attn_set_merge = 0;
+  p.pf_n = 0;
   void* args[] = {&p};
   for (int ph = kPhQkv; ph < kNumPhases; ++ph) {  // step 0 is part of step 1
     const void* fn = plan->cfg.head_dim == 64 ? phase_fn<64>(ph) : phase_fn<128>(ph);
@@ -1165,6 +1170,12 @@ moel_status moel_layer_decode_tree(moel_plan* plan, const moel_weights* w, void*
 moel_status moel_plan_set_launch(moel_plan* plan, int32_t mode) {
   if (plan == nullptr || (mode != MOEL_LAUNCH_PLAIN && mode != MOEL_LAUNCH_COOPERATIVE)) return MOEL_ERR_ARG;
   plan->launch_mode = mode;
+  return MOEL_OK;
+}
+
+moel_status moel_plan_set_expert_prefetch(moel_plan* plan, int32_t n_experts) {
+  if (plan == nullptr || n_experts < 0 || n_experts > 16) return MOEL_ERR_ARG;
+  plan->base.pf_n = n_experts;
   return MOEL_OK;
 }
 

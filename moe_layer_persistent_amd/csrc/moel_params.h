@@ -85,6 +85,10 @@ struct LayerParams {
   const float* ts_up;
   const float* ts_down;
   const float* ts_act;  // [E] activation tensor scales of the fp4 gather
+  // the layer's routing history: [E] tokens per expert of the last step (NULL: none); with
+  // pf_n > 0 the step first prefetches the pf_n experts that the last step used most
+  unsigned* expert_hist;
+  int pf_n;
   size_t stride_gate, stride_up, stride_down;  // packed bytes per expert
   // caches and io
   uint16_t* k_cache;

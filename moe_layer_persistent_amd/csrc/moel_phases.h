@@ -638,6 +638,96 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
 // activation; V transposed in LDS).  The partials' running maxima stay in base-2 units for the
 // merge.
 // ------------------------------------------------------------------------------------------
+// ------------------------------------------------------------------------------------------
+// Previous-step expert prefetch.  From the layer's routing history (tokens per expert of the
+// last step) the pf_n experts that most tokens chose (ties to the lower index, unused experts
+// left out) are ranked the same way in every prefetching workgroup; their packed gate, up and
+// down weights, as one list of 16-byte words, are split evenly over the np prefetching
+// workgroups, which read their share once with ordinary loads (so that the memory-side cache
+// keeps the lines) and discard it.  Runs on workgroups with no attention work while attention
+// runs; changes no result.
+// ------------------------------------------------------------------------------------------
+__device__ unsigned g_prefetch_sink;
+__device__ __noinline__ void expert_prefetch(uint64_t ph, int idx_arg, int np_arg) {
+  KP& p = params_from(ph);
+  const int idx = uniform(idx_arg), np = uniform(np_arg);
+  int* hist = reinterpret_cast<int*>(phase_smem(moel_lds));  // [E] history, then [16] selection
+  int* sel = hist + 512;
+  const int E = p.E, n = p.pf_n;
+  for (int e = threadIdx.x; e < E; e += kThreads) hist[e] = (int)gl(p.expert_hist)[e];
+  if (threadIdx.x < 16) sel[threadIdx.x] = -1;
+  __syncthreads();
+  // rank of an expert the last step used: the used experts before it (more tokens, or as many
+  // and a lower index); every used expert ranks before every unused one
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    const int c = hist[e];
+    if (c > 0) {
+      int rank = 0;
+      for (int f = 0; f < E; ++f) {
+        const int cf = hist[f];
+        rank += (cf > c) | ((cf == c) & (f < e));
+      }
+      if (rank < n) sel[rank] = e;
+    }
+  }
+  __syncthreads();
+  int nsel = 0;
+  for (int k = 0; k < n; ++k) nsel += uniform(sel[k]) >= 0 ? 1 : 0;
+  const unsigned wn0 = (unsigned)(p.stride_gate >> 4), wn1 = (unsigned)(p.stride_up >> 4),
+                 wn2 = (unsigned)(p.stride_down >> 4);
+  const unsigned W = (unsigned)nsel * (wn0 + wn1 + wn2);  // 16-byte words in all
+  const unsigned lo = (unsigned)((uint64_t)W * (unsigned)idx / (unsigned)np);
+  const unsigned hi = (unsigned)((uint64_t)W * (unsigned)(idx + 1) / (unsigned)np);
+  unsigned acc = 0;
+  constexpr int kIn = 8;  // 16-byte loads in flight per thread
+  // the segments (expert slot k, matrix m) in list order, each intersected with [lo, hi)
+  unsigned base = 0;
+  for (int k = 0; k < nsel; ++k) {
+    const size_t e = (size_t)uniform(sel[k]);
+#pragma unroll 1
+    for (int m = 0; m < 3; ++m) {
+      const unsigned wm = m == 0 ? wn0 : m == 1 ? wn1 : wn2;
+      const unsigned s0 = lo > base ? lo : base, s1 = hi < base + wm ? hi : base + wm;
+      if (s0 < s1) {
+        const uint8_t* src = (m == 0 ? p.w_gate + e * p.stride_gate
+                              : m == 1 ? p.w_up + e * p.stride_up : p.w_down + e * p.stride_down) +
+                             (size_t)(s0 - base) * 16;
+        const unsigned cnt = s1 - s0;
+        // two batches of kIn loads: a batch is consumed only after the next one is issued, so
+        // the loads stay in flight across iterations
+        u32x4 v[2][kIn];
+        auto issue = [&](int b, unsigned i) {
+#pragma unroll
+          for (int d = 0; d < kIn; ++d) {
+            const unsigned j = i + d * kThreads < cnt ? i + d * kThreads : cnt - 1;
+            v[b][d] = ldg16(src + (size_t)j * 16);  // cacheable: non-temporal reads leave nothing behind
+          }
+        };
+        auto consume = [&](int b) {
+#pragma unroll
+          for (int d = 0; d < kIn; ++d) acc ^= v[b][d][0] ^ v[b][d][3];
+        };
+        const unsigned step = kIn * kThreads;
+        unsigned i = threadIdx.x;
+        issue(0, i);
+        for (; i + step < cnt; i += 2 * step) {
+          issue(1, i + step);
+          sched_fence();
+          consume(0);
+          if (i + 2 * step < cnt) issue(0, i + 2 * step);
+          sched_fence();
+          consume(1);
+        }
+        if (i < cnt) consume(0);
+      }
+      base += wm;
+    }
+  }
+  // keeps the loads: the xor of the words read is stored only if it equals a constant that no
+  // step relies on
+  if (acc == 0x9e3779b9u) g_prefetch_sink = acc;
+}
+
 template <int D>
 struct AttnLds {
   static constexpr int SK = 128;          // keys per sub-chunk
@@ -884,6 +974,22 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
       if (route_tables(moel_lds).light == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       __hip_atomic_fetch_add(gl(p.ctrl) + kAttnDone + 32 * q_set, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+  // the previous-step expert prefetch, on the workgroups that have neither an attention item nor
+  // (with the merge per barrier group) merge work: barrier groups past the attention groups, or
+  // the workgroups past the items
+  if (p.pf_n > 0 && p.expert_hist != nullptr) {
+    int idx = -1, np = 0;
+    if (p.attn_set_merge) {
+      const int ns = p.nwg < kBarGroups ? p.nwg : kBarGroups, ng = p.Hkv * p.ntt;
+      const int r = p.nwg % ns;
+      np = (p.nwg / ns) * (ns - ng) + (r > ng ? r - ng : 0);
+      if (wg % ns >= ng) idx = (wg / ns) * (ns - ng) + (wg % ns - ng);
+    } else if (nitems < p.nwg) {
+      np = p.nwg - nitems;
+      if (wg >= nitems) idx = wg - nitems;
+    }
+    if (idx >= 0) expert_prefetch(params_handle(p), idx, np);
   }
 }
 
@@ -1227,6 +1333,13 @@ __device__ __forceinline__ void compute_routing(KP& p, RouteTables& R, bool writ
     }
   }
   lds_barrier();
+}
+
+// The layer's routing history for the next step: tokens per expert of this step (workgroup 0,
+// from the routing tables every workgroup holds).
+__device__ __forceinline__ void write_expert_hist(KP& p, const RouteTables& R, int wg) {
+  if (wg != 0 || p.expert_hist == nullptr) return;
+  for (int e = threadIdx.x; e < p.E; e += kThreads) gl(p.expert_hist)[e] = (unsigned)R.cnt[e];
 }
 
 // ------------------------------------------------------------------------------------------

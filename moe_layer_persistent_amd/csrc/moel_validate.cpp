@@ -80,6 +80,7 @@ moel_status moel_validate_call(const moel_config* cfg, const moel_weights* w, co
   if (cfg->expert_dtype == MOEL_EXPERT_NVFP4 && (w->ts_gate == nullptr || w->ts_up == nullptr || w->ts_down == nullptr))
     return MOEL_ERR_ARG;
   if (cfg->down_input == MOEL_DOWN_INPUT_NVFP4 && w->ts_act == nullptr) return MOEL_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(w->expert_hist) & 3u) != 0) return MOEL_ERR_ALIGN;
   if (misaligned(k_cache) || misaligned(v_cache) || misaligned(x) || misaligned(y)) return MOEL_ERR_ALIGN;
   const uintptr_t xb = reinterpret_cast<uintptr_t>(x), yb = reinterpret_cast<uintptr_t>(y);
   const uintptr_t n = (uintptr_t)T * (uintptr_t)cfg->hidden * 4u;

@@ -23,7 +23,7 @@ def test_library_exports_every_declared_symbol():
     assert len(names) >= 15
     for n in names:
         assert hasattr(L, n), n
-    assert L.moel_abi_version() == 6
+    assert L.moel_abi_version() == 7
 
 
 def test_plan_options_reject_a_missing_plan():
@@ -31,6 +31,7 @@ def test_plan_options_reject_a_missing_plan():
     assert L.moel_plan_set_launch(None, binding.MOEL_LAUNCH_PLAIN) == binding.MOEL_ERR_ARG
     assert L.moel_plan_set_launch(None, 5) == binding.MOEL_ERR_ARG
     assert L.moel_plan_set_acquire(None, binding.MOEL_ACQUIRE_AUTO) == binding.MOEL_ERR_ARG
+    assert L.moel_plan_set_expert_prefetch(None, 14) == binding.MOEL_ERR_ARG
     assert L.moel_plan_l2_coherent(None) == -1
 
 
@@ -136,6 +137,12 @@ def test_validate_call_alignment_and_alias():
                                 16, 0, 0, vp(0x300000 + 4096)) == binding.MOEL_ERR_ARG   # y overlaps x
     assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), None, vp(0x200000), vp(0x300000),
                                 16, 0, 0, vp(0x400000)) == binding.MOEL_ERR_ARG
+    w.expert_hist = 0x500002  # the routing history takes 4-byte words
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100000), vp(0x200000), vp(0x300000),
+                                16, 0, 0, vp(0x400000)) == binding.MOEL_ERR_ALIGN
+    w.expert_hist = 0x500004
+    assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100000), vp(0x200000), vp(0x300000),
+                                16, 0, 0, vp(0x400000)) == binding.MOEL_OK
     w.ts_up = None
     assert L.moel_validate_call(ctypes.byref(c), ctypes.byref(w), vp(0x100000), vp(0x200000), vp(0x300000),
                                 16, 0, 0, vp(0x400000)) == binding.MOEL_ERR_ARG

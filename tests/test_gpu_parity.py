@@ -621,3 +621,50 @@ def test_stack_share_two_layers_in_one_launch():
     assert _same_bytes(kc[0], out0["k_cache"]) and _same_bytes(vc[0], out0["v_cache"])
     assert _same_bytes(kc[1], out1["k_cache"]) and _same_bytes(vc[1], out1["v_cache"])
     st.close()
+
+
+def _step(plan, lw, k0, v0, x, pos, window, fused=True):
+    kc, vc = k0.clone(), v0.clone()
+    y = torch.full_like(x, float("nan"))
+    idx = torch.full((x.shape[0], plan.cfg.top_k), -1, dtype=torch.int32, device="cuda")
+    plan.layer_decode(lw, kc, vc, x, pos, window, y, dbg={"expert_idx": idx}, fused=fused)
+    torch.cuda.synchronize()
+    assert plan.status() == binding.MOEL_OK
+    return y, kc, vc, idx
+
+
+@pytest.mark.parametrize("layer", [0, 1], ids=["global_barrier_merge", "swa_set_merge"])
+def test_expert_history_and_prefetch_change_nothing(layer):
+    """Previous-step expert prefetch (orcarouter.ai English post, "Three bills a kernel this big
+    has to pay"): every step writes its tokens per expert to the layer's routing history, and with
+    the prefetch on a step first pulls the experts the previous step used most into the
+    memory-side cache on the workgroups that have no attention work.  On stack-share layers (one
+    kv head, so 7 of 8 barrier groups have no attention work): results bitwise those without
+    history or prefetch, two steps in a row with different inputs (the second prefetches what
+    the first used), the history equal to the counts of the chosen experts; the one-kernel-per-
+    step chain writes the same history."""
+    w = synth.WORKLOADS["stack_tp8"]
+    plan = binding.Plan(binding.config_from_workload(w))
+    _log(f"prefetch layer {layer}: generating")
+    t = synth.make_layer(w, layer, "cuda")
+    lw = plan.pack_layer(t)
+    window = w.layer_window(layer)
+    k0, v0 = t["k_cache"].clone(), t["v_cache"].clone()
+    xs = [t["x"].contiguous(), (0.5 * t["x"].flip(0)).contiguous()]
+    refs = [_step(plan, lw, k0, v0, x, w.pos, window) for x in xs]
+    hist = torch.zeros(w.n_experts, dtype=torch.int32, device="cuda")
+    lw.set_history(hist)
+    plan.set_expert_prefetch(14)
+    for i, x in enumerate(xs):
+        y, kc, vc, idx = _step(plan, lw, k0, v0, x, w.pos, window)
+        assert _same_bytes(y, refs[i][0]) and _same_bytes(kc, refs[i][1]) and _same_bytes(vc, refs[i][2]), i
+        assert torch.equal(idx, refs[i][3]), i
+        counts = torch.bincount(idx.flatten().long(), minlength=w.n_experts)
+        assert torch.equal(hist.long(), counts), i
+    _log(f"prefetch layer {layer}: {int((hist > 0).sum())} experts in the history")
+    plan.set_expert_prefetch(0)
+    hist.zero_()
+    _step(plan, lw, k0, v0, xs[1], w.pos, window, fused=False)
+    assert torch.equal(hist.long(), torch.bincount(refs[1][3].flatten().long(), minlength=w.n_experts))
+    lw.set_history(None)
+    plan.close()
