@@ -394,7 +394,7 @@ moel_status moel_stack_destroy(moel_stack* stack);
  * words, activation scratch, the RoPE rows of positions pos .. pos+T-1) lives in a device array
  * of MOEL_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU; the size a shape needs is
  *   ~ 4 KiB + 4 B * (32 * (3 Hq D + 2 H + E + 4 P + 3 k I + k P + D) + CUs * (Hq/Hkv) * 32 * (D + 2))
- * (about 56 MiB for H 8192, 64/8 heads of 128, P = I = 4096, E 256, k 8 on 256 compute units),
+ * (about 59 MiB for H 8192, 64/8 heads of 128, P = I = 4096, E 256, k 8 on 256 compute units),
  * and a shape that needs more is rejected with MOEL_ERR_SHAPE before anything is launched.
  * The first call on a device sets that device up (synchronously, on `stream`): it looks the
  * array up, runs the L2 coherence check on it (unless a plan already did on that device) and

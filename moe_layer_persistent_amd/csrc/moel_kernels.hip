@@ -574,10 +574,15 @@ const void* phase_fn(int ph) {
 // sum by the block's last unit: ~5 us).  Measured on full-width and stack-share layers, the
 // split pays only while the activation a workgroup reads exceeds its weights, i.e. while
 // 32 nwg / (S N) > 1, and it is taken up to the smallest power of two that ends that (at most 8,
-// each range at least 1,024 k so that every wave streams 4 or more steps).
-int choose_split(int N, int K, int nwg) {
+// each range at least 1,024 k so that every wave streams 4 or more steps).  The router/pooler
+// (N = E + P rows, none of them a multiple of a workgroup's share) measured best one step
+// further, while the activation exceeds half the weights (4 ranges instead of 2 at E 256,
+// P 4096: 23.2-23.6 against 24.4-24.9 us on the full-width and the stack-share layers; QKV,
+// o-projection and unpooler measured worse with any further split).
+int choose_split(int N, int K, int nwg, double act_over_w = 1.0) {
   int ns = 1;
-  while (ns < 8 && 32.0 * nwg / ((double)ns * N) > 1.0 + 1e-9 && (K / 32) % (2 * ns) == 0 && K / (2 * ns) >= 1024)
+  while (ns < 8 && 32.0 * nwg / ((double)ns * N) > act_over_w + 1e-9 && (K / 32) % (2 * ns) == 0 &&
+         K / (2 * ns) >= 1024)
     ns *= 2;
   return ns;
 }
@@ -595,7 +600,7 @@ void dense_splits(const moel_config* cfg, int nwg, int out[4]) {
     if (n == 1) forced[1] = forced[2] = forced[3] = forced[0];
   }
   for (int i = 0; i < 4; ++i) {
-    out[i] = choose_split(N[i], K[i], nwg);
+    out[i] = choose_split(N[i], K[i], nwg, i == 2 ? 0.5 : 1.0);
     const int f = forced[i];
     if (f >= 1 && f <= 16 && (f & (f - 1)) == 0 && (K[i] / 32) % f == 0 && (K[i] / 32) / f >= 1 && nwg / f >= 1)
       out[i] = f;
