@@ -50,14 +50,17 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
 // launch's barriers and split-K fix-ups release per XCC (`light`, kept in RouteTables::light).
 __device__ __forceinline__ void launch_barrier(KP& p, unsigned& bar, bool& light) {
   bool proven = false;
-  grid_barrier(p, ++bar, light, false, &proven);
+  // before the first barrier a split-K fix-up of this workgroup may already have proven the
+  // barrier groups single-XCC (RouteTables::light): the barrier then needs no proof of its own
+  const bool lt = light || (bar == 0 && route_tables(moel_lds).light != 0);
+  grid_barrier(p, ++bar, lt, false, &proven);
   if (bar == 1) {
     RouteTables& R = route_tables(moel_lds);
     if (threadIdx.x == 0) {
-      // proven on arrival: the masks are final (every workgroup recorded its bit before it
-      // counted itself in), so they need no second read
+      // proven on arrival or before: the masks are final (every workgroup recorded its bit
+      // before it counted itself in), so they need no second read
       int ok = 1;
-      if (!proven) {
+      if (!proven && !lt) {
         const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
         for (int g = 0; g < ng_all; ++g)
           ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,

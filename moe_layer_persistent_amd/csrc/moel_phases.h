@@ -492,17 +492,21 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   // earlier phase, which the L2 coherence of the device does not cover (a line that this XCD
   // wrote earlier in the launch), so it takes the agent-scope acquire, which drops the L2's
   // clean lines.
+  // a block's units share a barrier group (hence, once the groups are known to run on one XCC
+  // each, one L2) when nwg is a multiple of 8 nsplit.  Before the launch's first barrier has
+  // settled that, a unit proves it itself (groups_single_xcc) and counts in with bit 16 set: if
+  // any unit of the block proved it, every unit's partials are in the last unit's L2.  The
+  // proof's loads are issued before the wait for the partials' stores, so that the two
+  // overlap; a proof also holds for the rest of the launch (kept in RouteTables::light).
+  const bool known = route_tables(moel_lds).light != 0;
+  const bool one_group = nwg % (8 * nsplit) == 0;
+  bool proven = false;
+  if (threadIdx.x == 0 && !known && one_group) proven = groups_single_xcc(p);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
     auto cnt = gl(p.ctrl) + kFix + kFixPerPhase * fix_id + b;
-    // a block's units share a barrier group (hence, once the groups are known to run on one
-    // XCC each, one L2) when nwg is a multiple of 8 nsplit.  Before the launch's first barrier
-    // has settled that, a unit proves it itself (groups_single_xcc) and counts in with bit 16
-    // set: if any unit of the block proved it, every unit's partials are in the last unit's L2
-    const bool known = route_tables(moel_lds).light != 0;
-    const bool one_group = nwg % (8 * nsplit) == 0;
-    const bool proven = !known && one_group && groups_single_xcc(p);
+    if (proven) route_tables(moel_lds).light = 1;
     const bool light = (known && one_group) || proven;
     if (!light) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const unsigned inc = proven ? 0x10001u : 1u;
