@@ -243,8 +243,10 @@ __device__ __forceinline__ bool groups_single_xcc(KP& p) {
 //
 // proven (thread 0, optional): set when this workgroup proved on arrival that every barrier group
 // runs on one XCC (so the caller need not read the group masks again).
-__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false, bool drop_l2 = false,
-                                             bool* proven = nullptr) {
+// The barrier in two halves, so that a workgroup can issue loads that do not depend on the
+// barrier (data no workgroup writes before it) between its arrival and its wait.
+__device__ __forceinline__ void grid_barrier_arrive(KP& p, unsigned b, bool light = false, bool drop_l2 = false,
+                                                    bool* proven = nullptr) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -271,6 +273,11 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = fal
         __hip_atomic_store(ctrl + kFlag, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
+  }
+}
+__device__ __forceinline__ void grid_barrier_wait(KP& p, unsigned b) {
+  if (threadIdx.x == 0) {
+    auto ctrl = gl(p.ctrl);
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while (__hip_atomic_load(ctrl + kFlag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < b) {
       __builtin_amdgcn_s_sleep(1);
@@ -283,6 +290,11 @@ __device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = fal
     acquire_fence(p.l2_coherent);
   }
   __syncthreads();
+}
+__device__ __forceinline__ void grid_barrier(KP& p, unsigned b, bool light = false, bool drop_l2 = false,
+                                             bool* proven = nullptr) {
+  grid_barrier_arrive(p, b, light, drop_l2, proven);
+  grid_barrier_wait(p, b);
 }
 
 __device__ __forceinline__ void stamp(KP& p, int slot) {

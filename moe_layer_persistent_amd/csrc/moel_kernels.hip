@@ -28,7 +28,6 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   // step 0 (RMSNorm 1) has no work of its own: the QKV pass computes rstd from the rows it
   // reads anyway
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
-  if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
   if constexpr (PH == kPhAttnMerge) {
     if (p.attn_set_merge) phase_attn_merge_set(p, wg);
     else phase_attn_merge(p, wg);
@@ -45,22 +44,38 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   if constexpr (PH == kPhUnpool) phase_unpool(p, wg, smem);
 }
 
-// Barrier number ++bar of the launch.  After the first one, every workgroup reads the barrier
-// groups' XCC masks (written at launch): when every group runs on one XCC, the rest of the
-// launch's barriers and split-K fix-ups release per XCC (`light`, kept in RouteTables::light).
-__device__ __forceinline__ void launch_barrier(KP& p, unsigned& bar, bool& light) {
-  bool proven = false;
+// The attention phase of the persistent launch, with the second half of the barrier before it
+// (wait) called inside it.
+template <int D, class Wait>
+__device__ __forceinline__ void fused_attn(uint64_t ph, int wg_arg, Wait&& wait) {
+  KP& p = params_from(ph);
+  phase_attn<D>(p, uniform(wg_arg), moel_lds, wait);
+}
+
+// Barrier number ++bar of the launch, in two halves (see grid_barrier_arrive).  After the first
+// one, every workgroup knows whether the barrier groups run on one XCC each; when they do, the
+// rest of the launch's barriers and split-K fix-ups release per XCC (`light`, kept in
+// RouteTables::light).
+struct BarArrival {
+  bool proven;  // thread 0: proved single-XCC groups on arrival
+  bool lt;      // arrived with light release
+};
+__device__ __forceinline__ BarArrival launch_barrier_arrive(KP& p, unsigned& bar, bool light) {
   // before the first barrier a split-K fix-up of this workgroup may already have proven the
   // barrier groups single-XCC (RouteTables::light): the barrier then needs no proof of its own
-  const bool lt = light || (bar == 0 && route_tables(moel_lds).light != 0);
-  grid_barrier(p, ++bar, lt, false, &proven);
+  BarArrival a{false, light || (bar == 0 && route_tables(moel_lds).light != 0)};
+  grid_barrier_arrive(p, ++bar, a.lt, false, &a.proven);
+  return a;
+}
+__device__ __forceinline__ void launch_barrier_wait(KP& p, unsigned bar, bool& light, const BarArrival& a) {
+  grid_barrier_wait(p, bar);
   if (bar == 1) {
     RouteTables& R = route_tables(moel_lds);
     if (threadIdx.x == 0) {
       // proven on arrival or before: the masks are final (every workgroup recorded its bit
       // before it counted itself in), so they need no second read
       int ok = 1;
-      if (!proven && !lt) {
+      if (!a.proven && !a.lt) {
         const int ng_all = p.nwg < kBarGroups ? p.nwg : kBarGroups;
         for (int g = 0; g < ng_all; ++g)
           ok &= __popc(__hip_atomic_load(gl(p.ctrl) + kXccMask + 32 * g, __ATOMIC_RELAXED,
@@ -71,6 +86,10 @@ __device__ __forceinline__ void launch_barrier(KP& p, unsigned& bar, bool& light
     __syncthreads();
     light = R.light != 0;
   }
+}
+__device__ __forceinline__ void launch_barrier(KP& p, unsigned& bar, bool& light) {
+  const BarArrival a = launch_barrier_arrive(p, bar, light);
+  launch_barrier_wait(p, bar, light, a);
 }
 
 // Launch entry: the abort word, and this workgroup's XCC into its barrier group's mask.
@@ -136,9 +155,17 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   stamp(16 + kPhQkv);
   if (run) fused_phase<kPhQkv, D>(ph, wg);
   stamp(kPhQkv);
-  sync();
-  stamp(16 + kPhAttn);
-  if (run) fused_phase<kPhAttn, D>(ph, wg);
+  {
+    // the barrier before attention in two halves: attention items fetch their first cached key
+    // rows between the arrival and the wait
+    const BarArrival a = launch_barrier_arrive(p, bar, light);
+    auto wait = [&]() {
+      launch_barrier_wait(p, bar, light, a);
+      stamp(16 + kPhAttn);
+    };
+    if (run) fused_attn<D>(ph, wg, wait);
+    else wait();
+  }
   stamp(kPhAttn);
   // with the merge per barrier group the merging workgroups wait for their group's items
   if (!p.attn_set_merge) sync();
@@ -301,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void k_layer_phase(LayerParams p_arg) {
   }
   stamp(p, 16 + PH);
   if constexpr (PH == kPhQkv) phase_qkv(p, wg, smem);
-  if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem);
+  if constexpr (PH == kPhAttn) phase_attn<D>(p, wg, smem, [] {});
   if constexpr (PH == kPhAttnMerge) phase_attn_merge(p, wg);
   if constexpr (PH == kPhOproj) phase_oproj(p, wg, smem);
   if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, smem);

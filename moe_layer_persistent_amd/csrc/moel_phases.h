@@ -747,8 +747,12 @@ struct AttnLds {
   }
 };
 
-template <int D>
-__device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
+//
+// wait(): the second half of the grid barrier before the phase (or nothing, in a kernel of its
+// own), called exactly once.  A workgroup whose first key sub-chunk holds cached keys only (rows
+// this step does not write) fetches those rows first, so that they arrive during the wait.
+template <int D, class Wait>
+__device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem, Wait&& wait) {
   using L_t = AttnLds<D>;
   L_t& L = *reinterpret_cast<L_t*>(phase_smem(smem));
   constexpr int SK = L_t::SK, KS = L_t::KS;
@@ -778,6 +782,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
       q_set = q;
     }
   }
+  bool waited = false;
   for (int it = it0; it < nitems; it += istep) {
     const int ib = it / p.ntt, tile = it - ib * p.ntt;  // (head, chunk) item and token tile
     const int g = ib % p.Hkv, cc = ib / p.Hkv;  // kv head, flat chunk
@@ -823,15 +828,32 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
     const int tk = kTile * tile + tq;
     const int tqc = tk < p.T ? tk : p.T - 1;
     u32x4 qh[NS], ql[NS];
-    {
+    auto load_q = [&]() {
       const uint16_t* qs = p.q_op + ((size_t)tqc * p.Hq + (act ? h : 0)) * 2 * D + 8 * gq;
 #pragma unroll
       for (int s = 0; s < NS; ++s) {
         qh[s] = ldg16(qs + 32 * s);
         ql[s] = ldg16(qs + D + 32 * s);
       }
+    };
+    const int first_end = kb + SK <= ke ? kb + SK : ke;  // keys of the first sub-chunk: [kb, first_end)
+    if (!waited && first_end <= pos_r) {
+      // cached keys only: their rows are in flight across the barrier's wait; q (written before
+      // the barrier) follows it and is waited for here, so that no wait for q is left inside
+      // the key loop
+      fetch(kb);
+      wait();
+      waited = true;
+      load_q();
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    } else {
+      if (!waited) {
+        wait();
+        waited = true;
+      }
+      load_q();
+      fetch(kb);
     }
-    fetch(kb);
     float m_run = NEG, l_run = 0.f;
     f32x4 O[ND];
 #pragma unroll
@@ -968,6 +990,7 @@ __device__ __forceinline__ void phase_attn(KP& p, int wg, char* smem) {
       }
     }
   }
+  if (!waited) wait();
   if (q_set >= 0) {
     // count the item in on its group: its partial is complete in this XCC's L2 (vmcnt(0)), which
     // the group's merging workgroups share when the barrier groups run on one XCC each
