@@ -44,6 +44,17 @@ __device__ __forceinline__ void fused_phase(uint64_t ph, int wg_arg) {
   if constexpr (PH == kPhUnpool) phase_unpool(p, wg, smem);
 }
 
+// A dense phase of the persistent launch (o-projection, router/pooler, unpooler), with the
+// second half of the barrier before it run inside its first pass.
+template <int PH>
+__device__ __forceinline__ void fused_dense(uint64_t ph, int wg_arg, const BarWait& wait) {
+  KP& p = params_from(ph);
+  const int wg = uniform(wg_arg);
+  if constexpr (PH == kPhOproj) phase_oproj(p, wg, moel_lds, wait);
+  if constexpr (PH == kPhRouterPool) phase_router_pool(p, wg, moel_lds, wait);
+  if constexpr (PH == kPhUnpool) phase_unpool(p, wg, moel_lds, wait);
+}
+
 // The attention phase of the persistent launch, with the second half of the barrier before it
 // (wait) called inside it.
 template <int D, class Wait>
@@ -172,13 +183,19 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   stamp(16 + kPhAttnMerge);
   if (run) fused_phase<kPhAttnMerge, D>(ph, wg);
   stamp(kPhAttnMerge);
-  sync();
-  stamp(16 + kPhOproj);
-  if (run) fused_phase<kPhOproj, D>(ph, wg);
+  {
+    // the barrier in two halves: the phase's first weight loads are issued before the wait
+    const BarArrival a = launch_barrier_arrive(p, bar, light);
+    if (run) fused_dense<kPhOproj>(ph, wg, BarWait{ph, bar, 16 + kPhOproj});
+    else launch_barrier_wait(p, bar, light, a);
+  }
   stamp(kPhOproj);
-  sync();
-  stamp(16 + kPhRouterPool);
-  if (run) fused_phase<kPhRouterPool, D>(ph, wg);
+  {
+    // the barrier in two halves: the phase's first weight loads are issued before the wait
+    const BarArrival a = launch_barrier_arrive(p, bar, light);
+    if (run) fused_dense<kPhRouterPool>(ph, wg, BarWait{ph, bar, 16 + kPhRouterPool});
+    else launch_barrier_wait(p, bar, light, a);
+  }
   stamp(kPhRouterPool);
   sync();
   stamp(16 + kPhGemm1);
@@ -201,9 +218,12 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   }
   if (run) fused_phase<kPhCombine, D>(ph, wg);
   stamp(kPhCombine);
-  sync();
-  stamp(16 + kPhUnpool);
-  if (run) fused_phase<kPhUnpool, D>(ph, wg);
+  {
+    // the barrier in two halves: the phase's first weight loads are issued before the wait
+    const BarArrival a = launch_barrier_arrive(p, bar, light);
+    if (run) fused_dense<kPhUnpool>(ph, wg, BarWait{ph, bar, 16 + kPhUnpool});
+    else launch_barrier_wait(p, bar, light, a);
+  }
   stamp(kPhUnpool);
 }
 

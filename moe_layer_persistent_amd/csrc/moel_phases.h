@@ -20,6 +20,8 @@
 //                        first) then 256 bytes of scales (lane l: the 4 E4M3 block scales of
 //                        row l covering the pair's 64 k).
 #pragma once
+#include <type_traits>
+
 #include "moel_device.h"
 
 // Dynamic LDS of every layer kernel (sized at launch).
@@ -254,12 +256,32 @@ __device__ __forceinline__ int kwaves_for(int n) {
   return w;
 }
 
+// The second half of the grid barrier before a dense phase of the persistent launch, run by a
+// dense pass after it has issued the weight loads of its first steps (weights are not written
+// by any phase, the activation is): the barrier's number and, when the phase start is stamped,
+// its timestamp slot.  NoWait: a phase without a barrier before it (or a pass after the first).
+struct NoWait {
+  __device__ void operator()() const {}
+};
+struct BarWait {
+  uint64_t ph;
+  unsigned bar;
+  int slot;  // < 0: no timestamp
+  __device__ void operator()() const {
+    KP& p = params_from(ph);
+    grid_barrier_wait(p, (unsigned)uniform((int)bar));
+    const int sl = uniform(slot);
+    if (sl >= 0) stamp(p, sl);
+  }
+};
+
 // Not inlined (one body per NT); the arguments arrive in vector registers and are moved to
-// scalar registers first.
-template <int NT, int NTT, class ASrc>
+// scalar registers first.  wait() is called once by every thread; with a BarWait the weight
+// loads of the ring's first steps are issued before it and their activation loads after it.
+template <int NT, int NTT, class ASrc, class Wait = NoWait>
 __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, const uint8_t* w1_arg,
                                         int K_arg, int ks0_arg, int ksn_arg, int t_first_arg, int oct_lo_arg,
-                                        int oct_hi_arg, const ASrc A_arg) {
+                                        int oct_hi_arg, const ASrc A_arg, const Wait wait = Wait{}) {
   // k steps in flight per wave: 2 keeps ~100 KB per CU in flight, which measured faster than
   // deeper rings (more outstanding requests per CU lowered the achieved bandwidth)
   constexpr int DEPTH = 2;
@@ -284,7 +306,9 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
 #pragma unroll
     for (int j = 0; j < NT; ++j) acc[g][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  if (wv < nkw) {
+  constexpr bool kSplitWait = !std::is_same<Wait, NoWait>::value;
+  const bool kwave = wv < nkw;
+  {
     // k-wave wv takes the steps ks0 + wv, ks0 + wv + nkw, ... so that the workgroup's loads in
     // flight cover one contiguous stretch of each tile
     const int ns = ksn / nkw;
@@ -323,12 +347,32 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
       }
     };
     // straight-line prologue (steps past the end repeat the last one and are never used), so
-    // that the ring registers enter the loop in issue order
+    // that the ring registers enter the loop in issue order; with a barrier before the pass the
+    // weights of these steps go first, the activation after the barrier's wait
+    if constexpr (kSplitWait) {
+      if (kwave) {
 #pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      issue(d, d < ns ? d : ns - 1);
-      sched_fence();
+        for (int d = 0; d < DEPTH; ++d)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) rw[d][j] = ldg_stream(base[j] + (size_t)(d < ns ? d : ns - 1) * nkw * 1024);
+      }
+      wait();
+      if (kwave) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+#pragma unroll
+          for (int g = 0; g < NTT; ++g) A.fetch(tok[g], g, kq + 32 * nkw * (d < ns ? d : ns - 1), ra[d][g]);
+          sched_fence();
+        }
+      }
+    } else if (kwave) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        issue(d, d < ns ? d : ns - 1);
+        sched_fence();
+      }
     }
+    if (kwave) {
     int i0 = 0;
     for (; i0 + 2 * DEPTH <= ns; i0 += DEPTH) {
 #pragma unroll
@@ -352,6 +396,7 @@ __device__ __noinline__ void dense_pass(const uint8_t* w0_arg, int tiles0_arg, c
     for (int g = 0; g < NTT; ++g)
 #pragma unroll
       for (int j = 0; j < NT; ++j) L.red[(wv * kDenseMaxNT + g * NT + j) * 64 + lane] = acc[g][j];
+    }
   }
   // every (token, k) of the A rows is fetched by exactly one lane of the k-waves (lanes whose
   // token is >= T repeat token T-1 and are left out)
@@ -392,26 +437,27 @@ __device__ __forceinline__ void octet_range(int tiles, int wg, int nwg, int& lo,
 }
 
 // nt row tiles against ntt token tiles (nt * ntt <= 8)
-template <class ASrc>
+template <class ASrc, class Wait = NoWait>
 __device__ __forceinline__ void dense_pass_nt(int nt, int ntt, const uint8_t* w0, int tiles0, const uint8_t* w1,
-                                              int K, int ks0, int ksn, int t, int lo, int hi, const ASrc& A) {
+                                              int K, int ks0, int ksn, int t, int lo, int hi, const ASrc& A,
+                                              const Wait& wait = Wait{}) {
   if (ntt == 1) {
     switch (nt) {
-      case 1: dense_pass<1, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 2: dense_pass<2, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 3: dense_pass<3, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 4: dense_pass<4, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 5: dense_pass<5, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 6: dense_pass<6, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 7: dense_pass<7, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      default: dense_pass<8, 1>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 1: dense_pass<1, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 2: dense_pass<2, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 3: dense_pass<3, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 4: dense_pass<4, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 5: dense_pass<5, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 6: dense_pass<6, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 7: dense_pass<7, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      default: dense_pass<8, 1, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
     }
   } else {
     switch (nt) {
-      case 1: dense_pass<1, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 2: dense_pass<2, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      case 3: dense_pass<3, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
-      default: dense_pass<4, 2>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A); break;
+      case 1: dense_pass<1, 2, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 2: dense_pass<2, 2, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      case 3: dense_pass<3, 2, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
+      default: dense_pass<4, 2, ASrc, Wait>(w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait); break;
     }
   }
 }
@@ -428,10 +474,14 @@ __device__ __forceinline__ void dense_pass_nt(int nt, int ntt, const uint8_t* w0
 // last -- and runs the epilogue.  Where nwg is a multiple of 8 nsplit, the units of a block sit
 // on one XCD (workgroup w runs on XCD w mod 8), so the partials it reads are in that XCD's L2.
 // No unit waits for another.
-template <class ASrc, class Epi>
+//
+// wait: the second half of the grid barrier before the phase (BarWait), or NoWait; run once by
+// every workgroup, inside its first pass (after the pass has issued its first weight loads) or
+// before it leaves without work.
+template <class ASrc, class Epi, class Wait = NoWait>
 __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const uint8_t* w0, int tiles0,
                                             const uint8_t* w1, int tiles1, int K, int wg, const ASrc& A,
-                                            DenseLds& L, Epi&& epi) {
+                                            DenseLds& L, Epi&& epi, const Wait& wait = Wait{}) {
   const int nwg = p.nwg;
   const int tiles = tiles0 + tiles1;
   const int S = K >> 5;
@@ -441,18 +491,25 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   if (nsplit <= 1) {
     int lo, hi;
     octet_range(tiles, wg, nwg, lo, hi);
-    if (lo >= hi) return;
+    if (lo >= hi) {
+      wait();
+      return;
+    }
     const int tf = lo >> 1, tl = (hi - 1) >> 1;
     for (int t = tf; t <= tl; t += gs) {
       const int nt = (tl - t + 1) < gs ? (tl - t + 1) : gs;
-      dense_pass_nt(nt, ntt, w0, tiles0, w1, K, 0, S, t, lo, hi, A);
+      if (t == tf) dense_pass_nt(nt, ntt, w0, tiles0, w1, K, 0, S, t, lo, hi, A, wait);
+      else dense_pass_nt(nt, ntt, w0, tiles0, w1, K, 0, S, t, lo, hi, A);
       epi(L, t, nt, lo, hi);
       lds_barrier();
     }
     return;
   }
   const int nblk = nwg / nsplit;
-  if (wg >= nblk * nsplit) return;
+  if (wg >= nblk * nsplit) {
+    wait();
+    return;
+  }
   int b, js;
   if (nwg % (8 * nsplit) == 0) {
     const int x = wg & 7, i = wg >> 3;  // XCD and index within it
@@ -464,14 +521,18 @@ __device__ __forceinline__ void dense_phase(KP& p, int fix_id, int nsplit, const
   }
   int lo, hi;
   octet_range(tiles, b, nblk, lo, hi);
-  if (lo >= hi) return;  // an empty block: none of its units takes part
+  if (lo >= hi) {  // an empty block: none of its units takes part
+    wait();
+    return;
+  }
   const int tf = lo >> 1, tl = (hi - 1) >> 1;
   const int ksn = S / nsplit, ks0 = js * ksn;
   const int ntot = tiles * 16;
   auto part = gl(p.part);
   for (int t = tf; t <= tl; t += gs) {
     const int nt = (tl - t + 1) < gs ? (tl - t + 1) : gs;
-    dense_pass_nt(nt, ntt, w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A);
+    if (t == tf) dense_pass_nt(nt, ntt, w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A, wait);
+    else dense_pass_nt(nt, ntt, w0, tiles0, w1, K, ks0, ksn, t, lo, hi, A);
     for (int e = threadIdx.x; e < (nt * 16) << lgT; e += kThreads) {
       const int j = e >> (lgT + 4), r = (e >> lgT) & 15, tok = e & ((1 << lgT) - 1);
       const int n = (t + j) * 16 + r;
@@ -1113,7 +1174,8 @@ __device__ __forceinline__ void phase_attn_merge_set(KP& p, int wg) {
 // ------------------------------------------------------------------------------------------
 // o-projection + residual -> h (fp32).
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
+template <class Wait = NoWait>
+__device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem, const Wait& wait = Wait{}) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AOp A{p.o_op, p.T, p.Hq * p.D};
   dense_phase(p, 1, p.sk_oproj, p.w_o, p.H / 16, nullptr, 0, p.Hq * p.D, wg, A, L,
@@ -1128,7 +1190,7 @@ __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
                     gl(p.h_op)[op_index(t, n, p.H)] = h;
                   }
                 }
-              });
+              }, wait);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -1136,7 +1198,8 @@ __device__ __forceinline__ void phase_oproj(KP& p, int wg, char* smem) {
 // rows [router; pooler].  RMSNorm 2 is folded in as for RMSNorm 1: the pass contracts
 // h * gamma2, yields rstd2 from the h it reads, and the epilogue scales by it.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
+template <class Wait = NoWait>
+__device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem, const Wait& wait = Wait{}) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AGammaOp A{p.h_op, p.gamma2, p.T, p.eps, p.H};
   const int te = p.E / 16;
@@ -1156,7 +1219,7 @@ __device__ __forceinline__ void phase_router_pool(KP& p, int wg, char* smem) {
                     store_split(gl(p.pl_split) + (size_t)t * p.P * 2, n - p.E, v);
                   }
                 }
-              });
+              }, wait);
 }
 
 // ------------------------------------------------------------------------------------------
@@ -2032,7 +2095,8 @@ __device__ __forceinline__ void phase_combine(KP& p, int wg, char* smem) {
 }
 
 // y = h + m W_unpool^T
-__device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem) {
+template <class Wait = NoWait>
+__device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem, const Wait& wait = Wait{}) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AOp A{p.m_op, p.T, p.P};
   dense_phase(p, 3, p.sk_unpool, p.w_unpool, p.H / 16, nullptr, 0, p.P, wg, A, L,
@@ -2044,7 +2108,7 @@ __device__ __forceinline__ void phase_unpool(KP& p, int wg, char* smem) {
                   if (t >= p.T || !octet_in(n, lo, hi)) continue;
                   gl(p.y)[(size_t)t * p.H + n] = gl(p.h_buf)[(size_t)t * p.H + n] + L.fin[(j * 16 + r) * kMaxT + t];
                 }
-              });
+              }, wait);
 }
 
 }  // namespace moel
