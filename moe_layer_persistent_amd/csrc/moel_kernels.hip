@@ -55,6 +55,13 @@ __device__ __forceinline__ void fused_dense(uint64_t ph, int wg_arg, const BarWa
   if constexpr (PH == kPhUnpool) phase_unpool(p, wg, moel_lds, wait);
 }
 
+// The down projection of the persistent launch, with the second half of barrier number bar run
+// inside its first expert stream.
+__device__ __forceinline__ void fused_down(uint64_t ph, int wg_arg, unsigned bar) {
+  KP& p = params_from(ph);
+  phase_experts<false>(p, uniform(wg_arg), moel_lds, (int)bar);
+}
+
 // The attention phase of the persistent launch, with the second half of the barrier before it
 // (wait) called inside it.
 template <int D, class Wait>
@@ -201,9 +208,12 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   stamp(16 + kPhGemm1);
   if (run) fused_phase<kPhGemm1, D>(ph, wg);
   stamp(kPhGemm1);
-  sync();
-  stamp(16 + kPhGemm2);
-  if (run) fused_phase<kPhGemm2, D>(ph, wg);
+  {
+    // the barrier in two halves: the down projection's first weight loads before the wait
+    const BarArrival a = launch_barrier_arrive(p, bar, light);
+    if (run) fused_down(ph, wg, bar);
+    else launch_barrier_wait(p, bar, light, a);
+  }
   stamp(kPhGemm2);
   sync();
   stamp(16 + kPhCombine);

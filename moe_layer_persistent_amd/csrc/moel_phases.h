@@ -1467,8 +1467,7 @@ struct Fp4Pair {
 // remainder half for i >= 2.  Plain arithmetic, so that no per-lane choice between registers
 // is made through memory.
 template <int NM, int G>
-__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM],
-                                              const uint16_t* const (&row0)[G], const long (&dr)[G], int k0) {
+__device__ __forceinline__ void fp4_pair_load_w(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM]) {
   const int lane = lane_id();
 #pragma unroll
   for (int m = 0; m < NM; ++m) {
@@ -1476,12 +1475,23 @@ __device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* 
     f.c[m][1] = ldg_stream(wt[m] + 1024 + lane * 16);
     f.sc[m] = ldg_stream32(wt[m] + 2048 + 4 * lane);
   }
+}
+template <int NM, int G>
+__device__ __forceinline__ void fp4_pair_load_a(Fp4Pair<NM, G>& f, const uint16_t* const (&row0)[G],
+                                                const long (&dr)[G], int k0) {
+  const int lane = lane_id();
   const int lane_off = 8 * (lane >> 2) + 4 * ((lane >> 1) & 1);
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const long off = (lane & 1) ? dr[g] : 0l;
     f.a[g] = ldg8(row0[g] + off + 2 * k0 + lane_off);
   }
+}
+template <int NM, int G>
+__device__ __forceinline__ void fp4_pair_load(Fp4Pair<NM, G>& f, const uint8_t* const (&wt)[NM],
+                                              const uint16_t* const (&row0)[G], const long (&dr)[G], int k0) {
+  fp4_pair_load_w<NM, G>(f, wt);
+  fp4_pair_load_a<NM, G>(f, row0, dr, k0);
 }
 
 template <int H, int J, int NM, int G>
@@ -1572,8 +1582,13 @@ static_assert(sizeof(RouteTables::dq) == kDqSlots * sizeof(int), "hand-out ring 
 // The stream ends before a tile that needs a larger token group than G, when the stage is
 // full, or at the end of the work.  Return: -1 when the work is done; a static tile to resume
 // from (>= 0); or -(2 + k) to resume at dynamic position k (handed out and published in dq).
+//
+// wait_bar (> 0): number of the grid barrier before the phase, whose second half the stream
+// runs after the weight loads of its first pairs and before their activation loads (the
+// activation is written by the phase before the barrier, the weights by none); 0: none.
 template <bool GATEUP, int G, int DEPTH>
-__device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_arg, int k0_arg, int tdyn_arg) {
+__device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_arg, int k0_arg, int tdyn_arg,
+                                              int wait_bar_arg) {
   KP& p = params_from(ph);
   constexpr int NM = GATEUP ? 2 : 1;
   constexpr int RW = NM * 2 * G;  // red floats per lane
@@ -1751,7 +1766,30 @@ __device__ __noinline__ int fp4_expert_stream(uint64_t ph, int ts_arg, int te_ar
     fp4_pair_load<NM, G>(f, wt, row0, dr, 64 * nkw * pr);
   };
   bool more = true;
-  if (kw) {
+  const int wait_bar = uniform(wait_bar_arg);
+  if (wait_bar > 0) {
+    // the first pairs' weights, the barrier's wait, then their activations
+    if (kw) {
+      request();
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        const uint8_t* wt[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) wt[m] = wb[m] + (size_t)d * nkw * 2304;
+        fp4_pair_load_w<NM, G>(ring[d], wt);
+      }
+    }
+    grid_barrier_wait(p, (unsigned)wait_bar);
+    stamp(p, 16 + (GATEUP ? kPhGemm1 : kPhGemm2));
+    if (kw) {
+#pragma unroll
+      for (int d = 0; d < DEPTH; ++d) {
+        fp4_pair_load_a<NM, G>(ring[d], row0, dr, 64 * nkw * d);
+        sched_fence();
+      }
+      publish();
+    }
+  } else if (kw) {
     request();
     // DEPTH <= npt: the first DEPTH pairs all lie in the first tile
 #pragma unroll
@@ -1979,8 +2017,11 @@ __device__ __forceinline__ void bf16_expert_tiles(KP& p, const RouteTables& R, i
 }
 
 // Expert GEMM phase: the flattened list (active expert u, tile) split evenly over workgroups.
+// wait_bar (> 0): number of the grid barrier before the phase, whose second half the phase runs
+// itself, in its first stream after that stream's first weight loads (NVFP4 experts), or first
+// (bf16 experts, or a workgroup without tiles); 0: none.
 template <bool GATEUP>
-__device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
+__device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem, int wait_bar = 0) {
   RouteTables& R = route_tables(smem);
   const int rows = GATEUP ? p.I_loc : p.P_loc;
   const bool fp4 = p.expert_dtype == 0;
@@ -2021,6 +2062,7 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
     const int Sp = (GATEUP ? p.P : p.I) >> 6;
     const int npt = Sp / kwaves_for(Sp);
     int ts = t0, k = 0;
+    int wb = wait_bar;  // passed to the first stream only
     for (;;) {
       int t = ts;
       if (ts >= t1) {  // next position is dynamic: hand it out unless a stream already did
@@ -2042,13 +2084,14 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
       // and for shapes with an odd pair count per wave (K < 1024).
       int r;
       const bool d2 = npt % 2 == 0;
-      if (G == 1) r = d2 ? fp4_expert_stream<GATEUP, 1, 2>(h, ts, t1, k, t_dyn)
-                         : fp4_expert_stream<GATEUP, 1, 1>(h, ts, t1, k, t_dyn);
-      else if (G == 2) r = d2 ? fp4_expert_stream<GATEUP, 2, 2>(h, ts, t1, k, t_dyn)
-                              : fp4_expert_stream<GATEUP, 2, 1>(h, ts, t1, k, t_dyn);
-      else if (G == 4) r = d2 ? fp4_expert_stream<GATEUP, 4, 2>(h, ts, t1, k, t_dyn)
-                              : fp4_expert_stream<GATEUP, 4, 1>(h, ts, t1, k, t_dyn);
-      else r = fp4_expert_stream<GATEUP, 8, 1>(h, ts, t1, k, t_dyn);
+      if (G == 1) r = d2 ? fp4_expert_stream<GATEUP, 1, 2>(h, ts, t1, k, t_dyn, wb)
+                         : fp4_expert_stream<GATEUP, 1, 1>(h, ts, t1, k, t_dyn, wb);
+      else if (G == 2) r = d2 ? fp4_expert_stream<GATEUP, 2, 2>(h, ts, t1, k, t_dyn, wb)
+                              : fp4_expert_stream<GATEUP, 2, 1>(h, ts, t1, k, t_dyn, wb);
+      else if (G == 4) r = d2 ? fp4_expert_stream<GATEUP, 4, 2>(h, ts, t1, k, t_dyn, wb)
+                              : fp4_expert_stream<GATEUP, 4, 1>(h, ts, t1, k, t_dyn, wb);
+      else r = fp4_expert_stream<GATEUP, 8, 1>(h, ts, t1, k, t_dyn, wb);
+      wb = 0;
       r = uniform(r);
       if (r == -1) break;
       if (r >= 0) {
@@ -2058,7 +2101,15 @@ __device__ __forceinline__ void phase_experts(KP& p, int wg, char* smem) {
         k = -r - 2;
       }
     }
+    if (wb > 0) {  // no stream ran: the barrier's second half still
+      grid_barrier_wait(p, (unsigned)wb);
+      stamp(p, 16 + (GATEUP ? kPhGemm1 : kPhGemm2));
+    }
     return;
+  }
+  if (wait_bar > 0) {
+    grid_barrier_wait(p, (unsigned)wait_bar);
+    stamp(p, 16 + (GATEUP ? kPhGemm1 : kPhGemm2));
   }
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   for (int t = t0; t < t1;) {
