@@ -161,8 +161,12 @@ __device__ __forceinline__ void launch_exit(KP& p, bool run) {
 
 // The phases of one layer with a grid barrier between consecutive ones (the persistent
 // launch's body; the stack launch runs it once per layer).
+//
+// qkv_wait (> 0): number of the grid barrier before the layer (between two layers of one
+// launch), whose second half the QKV phase runs after its first weight loads; 0: none.
 template <int D>
-__device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsigned& bar, bool& light) {
+__device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsigned& bar, bool& light,
+                                             unsigned qkv_wait = 0) {
   KP& p = params_from(ph);
   auto stamp = [&](int slot) {
     if (run) moel::stamp(p, slot);
@@ -170,8 +174,13 @@ __device__ __forceinline__ void layer_phases(uint64_t ph, int wg, bool run, unsi
   auto sync = [&]() { launch_barrier(p, bar, light); };
   stamp(16 + kPhNorm1);
   stamp(kPhNorm1);
-  stamp(16 + kPhQkv);
-  if (run) fused_phase<kPhQkv, D>(ph, wg);
+  if (qkv_wait > 0) {
+    if (run) phase_qkv(p, wg, moel_lds, BarWait{ph, qkv_wait, 16 + kPhQkv});
+    else grid_barrier_wait(p, qkv_wait);
+  } else {
+    stamp(16 + kPhQkv);
+    if (run) fused_phase<kPhQkv, D>(ph, wg);
+  }
   stamp(kPhQkv);
   {
     // the barrier before attention in two halves: attention items fetch their first cached key
@@ -275,6 +284,7 @@ __device__ __noinline__ unsigned stack_layer(uint64_t ph_arg, int wg_arg, int ru
   const unsigned state = (unsigned)uniform((int)state_arg);
   unsigned bar = state & 0x7fffffffu;
   bool light = (state >> 31) != 0;
+  unsigned qkv_wait = 0;
   if (bar > 0) {
     // this layer's input is complete.  It rewrites the workspace lines of the layer before from
     // whichever XCD computes them, and an XCD's L2 can keep its own earlier copy past another
@@ -284,14 +294,19 @@ __device__ __noinline__ unsigned stack_layer(uint64_t ph_arg, int wg_arg, int ru
     // dirty lines back
     KP& p = params_from(ph);
     if (light && p.l2_coherent) {
-      grid_barrier(p, ++bar, true, true);
+      // the barrier's second half runs in the layer's QKV phase, after the first weight loads:
+      // the next layer's weights are in flight across the layer boundary.  They may be issued
+      // before the group's last arrival drops the XCC's L2; weights are written by no one, so
+      // the drop cannot leave them stale, and everything else is read after the wait
+      grid_barrier_arrive(p, ++bar, true, true);
+      qkv_wait = bar;
     } else {
       launch_barrier(p, bar, light);
       if (threadIdx.x == 0 && p.l2_coherent) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       __syncthreads();
     }
   }
-  layer_phases<D>(ph, wg, run, bar, light);
+  layer_phases<D>(ph, wg, run, bar, light, qkv_wait);
   return bar | (light ? 0x80000000u : 0u);
 }
 

@@ -641,7 +641,8 @@ __device__ __forceinline__ bool octet_in(int row, int lo, int hi) {
 // rotation partners (i, i + D/2) of every head interleaved: packed row 2i <-> canonical i,
 // packed row 2i+1 <-> canonical i + D/2.  The cache stores bf16 (nearest); q stays fp32.
 // ------------------------------------------------------------------------------------------
-__device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
+template <class Wait = NoWait>
+__device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem, const Wait& wait = Wait{}) {
   DenseLds& L = *reinterpret_cast<DenseLds*>(phase_smem(smem));
   AGamma A{p.x, p.H, p.gamma1, p.T, p.eps};  // RMSNorm 1 folded in: rstd from the same pass
   const int tiles = (p.Hq + 2 * p.Hkv) * p.D / 16;
@@ -689,7 +690,7 @@ __device__ __forceinline__ void phase_qkv(KP& p, int wg, char* smem) {
                     v[i + half] = f2bf(b);
                   }
                 }
-              });
+              }, wait);
 }
 
 // ------------------------------------------------------------------------------------------
