@@ -217,6 +217,13 @@ int32_t moel_plan_l2_coherent(const moel_plan* plan);
  * does not prefetch.  Returns MOEL_ERR_ARG for a null plan or n_experts outside 0..16. */
 moel_status moel_plan_set_expert_prefetch(moel_plan* plan, int32_t n_experts);
 
+/* Fills the plan's activation scratch (every intermediate buffer of a step; not its control
+ * words or RoPE table) with all-ones words, a NaN in fp32 and in bf16, on `stream`.  For
+ * tests: a step that reads a scratch word before the phase that produces it has written it
+ * then carries a NaN into its outputs, where a step on unpoisoned scratch would silently reuse
+ * an earlier step's value.  A step after it runs as usual (it writes everything it reads). */
+moel_status moel_plan_poison_scratch(moel_plan* plan, void* stream);
+
 /* Sets (1) or clears (0) the plan's abort word.  While set, launched kernels skip all
  * work, leave every caller buffer untouched and report MOEL_ERR_ABORTED. */
 moel_status moel_plan_set_abort(moel_plan* plan, int32_t abort_flag, void* stream);

@@ -97,6 +97,7 @@ def lib() -> ctypes.CDLL:
             "moel_plan_workgroups": (i32, [vp]),
             "moel_plan_status": (i32, [vp]),
             "moel_plan_set_abort": (i32, [vp, i32, vp]),
+            "moel_plan_poison_scratch": (i32, [vp, vp]),
             "moel_plan_set_launch": (i32, [vp, i32]),
             "moel_plan_set_acquire": (i32, [vp, i32]),
             "moel_plan_set_expert_prefetch": (i32, [vp, i32]),
@@ -254,6 +255,10 @@ class Plan:
 
     def set_abort(self, flag: bool, stream=None):
         _check(lib().moel_plan_set_abort(self.handle, int(flag), _stream(stream)), "moel_plan_set_abort")
+
+    def poison_scratch(self, stream=None):
+        """All-ones words (NaN) into the plan's activation scratch, see include/moel.h."""
+        _check(lib().moel_plan_poison_scratch(self.handle, _stream(stream)), "moel_plan_poison_scratch")
 
     # ---- packing -------------------------------------------------------------------------
     def pack_dense(self, src: torch.Tensor, rope_head_dim: int = 0, stream=None) -> torch.Tensor:

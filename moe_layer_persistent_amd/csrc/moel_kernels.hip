@@ -1191,6 +1191,19 @@ moel_status moel_plan_scratch(const moel_plan* plan, int32_t which, void** ptr, 
   return MOEL_OK;
 }
 
+moel_status moel_plan_poison_scratch(moel_plan* plan, void* stream) {
+  if (plan == nullptr) return MOEL_ERR_ARG;
+  // the activation scratch: from the first activation region up to the RoPE table (the
+  // control words before it and the table after it are kept)
+  const LayerParams& b = plan->base;
+  const char* lo = reinterpret_cast<const char*>(b.q_buf);
+  const char* hi = reinterpret_cast<const char*>(b.rope_cos);
+  const size_t n = (size_t)(hi - lo) / 4;
+  hipLaunchKernelGGL(k_fill_u32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     reinterpret_cast<unsigned*>(const_cast<char*>(lo)), 0xffffffffu, n);
+  return hip_ok(hipGetLastError()) ? MOEL_OK : MOEL_ERR_HIP;
+}
+
 moel_status moel_plan_set_abort(moel_plan* plan, int32_t flag, void* stream) {
   if (plan == nullptr) return MOEL_ERR_ARG;
   hipLaunchKernelGGL(k_set_word, dim3(1), dim3(1), 0, static_cast<hipStream_t>(stream),

@@ -32,6 +32,7 @@ def test_plan_options_reject_a_missing_plan():
     assert L.moel_plan_set_launch(None, 5) == binding.MOEL_ERR_ARG
     assert L.moel_plan_set_acquire(None, binding.MOEL_ACQUIRE_AUTO) == binding.MOEL_ERR_ARG
     assert L.moel_plan_set_expert_prefetch(None, 14) == binding.MOEL_ERR_ARG
+    assert L.moel_plan_poison_scratch(None, None) == binding.MOEL_ERR_ARG
     assert L.moel_plan_l2_coherent(None) == -1
 
 

@@ -123,6 +123,46 @@ def test_fused_equals_unfused_and_is_deterministic():
         assert _same_bytes(a[k], c[k]), k
 
 
+# (id, workload overrides, call T, call pos, forced dense splits)
+POISON = [
+    ("nvfp4", dict(T=5), 5, 70, None),
+    ("split_k", dict(T=16, pos=300, window=0, hidden=2048, n_q_heads=16, n_kv_heads=4, head_dim=128,
+                     pooled=1024, inter=1024, n_experts=64, top_k=8), 16, 300, "4,4,4,4"),
+    ("two_token_tiles", dict(T=32, pos=200, window=64, head_dim=128, n_q_heads=4, n_kv_heads=1, hidden=768),
+     32, 184, None),
+    ("bf16", dict(T=16, pos=150, window=0, expert_dtype=synth.BF16), 16, 150, None),
+    ("fp4_gather", dict(T=16, pos=200, window=64, n_experts=32, top_k=8, pooled=512, inter=512,
+                        down_input=synth.DOWN_NVFP4), 16, 200, None),
+]
+
+
+@pytest.mark.parametrize("case", POISON, ids=[c[0] for c in POISON])
+def test_poisoned_scratch_changes_nothing(case, monkeypatch):
+    """Every scratch word a step reads is written earlier in the same step (no consumer reads
+    before its producer): with the plan's activation scratch filled with NaN before the call,
+    fused and unfused steps give bitwise the outputs (and expert activations) of the same step
+    on a scratch that holds an earlier step's values."""
+    name, kw, T, pos, splits = case
+    if splits:
+        monkeypatch.setenv("MOEL_DENSE_SPLITS", splits)
+    w = synth.small_workload(**kw)
+    _log(f"poison {name} {kw} T {T} pos {pos} splits {splits}")
+    run = harness.GpuRun(w)
+    if splits:
+        monkeypatch.delenv("MOEL_DENSE_SPLITS")
+    rows = T * w.top_k
+    for fused in (True, False):
+        ref = run.run(fused=fused, T=T, pos=pos)
+        ref_act = {n: run.plan.scratch(n).view(binding.MOEL_MAX_TOKENS * w.top_k, -1)[:rows].clone() for n in ("a", "d")}
+        run.plan.poison_scratch()
+        out = run.run(fused=fused, T=T, pos=pos)
+        for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+            assert _same_bytes(ref[k], out[k]), (fused, k)
+        for n, v in ref_act.items():
+            assert _same_bytes(v, run.plan.scratch(n).view(binding.MOEL_MAX_TOKENS * w.top_k, -1)[:rows]), (fused, n)
+        assert bool(torch.isfinite(out["y"]).all()), fused
+
+
 def test_fp4_gather_fused_equals_unfused():
     w = synth.small_workload(T=16, pos=200, window=64, n_experts=32, top_k=8, pooled=512, inter=512,
                              down_input=synth.DOWN_NVFP4)
