@@ -549,8 +549,8 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
-                                   "(the multi-GPU sharding is a design note, not a measured path)"}))
+        print(json.dumps({"error": "the layer step runs on one GPU only; --gpus must be 1 "
+                                   "(sharding over several GPUs is described, not built)"}))
         sys.exit(2)
 
     import numpy as np
