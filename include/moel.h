@@ -158,7 +158,20 @@ size_t moel_packed_experts_bytes(const moel_config* cfg, int32_t which /*0 gate,
 /* Validates cfg, selects the current HIP device, allocates the plan's workspace once
  * (activation scratch, barrier words, status word, RoPE cos/sin table computed on the
  * host in fp64 and stored fp32) and chooses the work decomposition.  *out is set only
- * on success.  Not for the hot path. */
+ * on success.  Not for the hot path.
+ *
+ * Environment variables (for diagnostics and for measuring alternatives; none changes a
+ * result beyond the summation order of a split contraction):
+ *   MOEL_LOG            set: one line per plan (shape, workgroups, workspace and LDS bytes,
+ *                       the L2 coherence check, the dense K-splits) and every HIP error on
+ *                       stderr.
+ *   MOEL_DENSE_SPLITS   "q,o,r,u" or one number for all: the K-split of the QKV,
+ *                       o-projection, router/pooler and unpooler contractions, read when a
+ *                       plan is created; a value is used where it is a power of two <= 16
+ *                       that divides the phase's 32-element k steps, 0 keeps the plan's choice.
+ *   MOEL_ATTN_SET_MERGE 0: the attention merge always runs as a phase of its own after a
+ *                       grid barrier (otherwise each attention group merges on its own
+ *                       barrier group where it fits); read once per process. */
 moel_status moel_plan_create(const moel_config* cfg, moel_plan** out);
 moel_status moel_plan_destroy(moel_plan* plan);
 
