@@ -596,8 +596,10 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4-e2m1/e4m3 experts, bf16 weights+KV, fp32 accumulate" if w.expert_dtype == 0
-        else "bf16 weights+KV, fp32 accumulate",
+        "dtype": "bf16",  # the MFMA operand type of every contraction (fp32 accumulation)
+        "dtype_detail": "NVFP4 (E2M1 codes, E4M3 block scales) experts decoded to bf16 in registers; bf16 "
+                        "weights and KV cache; fp32 accumulation, softmax and residual stream" if w.expert_dtype == 0
+        else "bf16 experts, weights and KV cache; fp32 accumulation, softmax and residual stream",
         "data": "synthetic (seeded N(0,1) activations / KV history, N(0,0.02) weights)",
         "config": {"workload": w.name, "T": T, "hidden": w.hidden, "q_heads": w.n_q_heads,
                    "kv_heads": w.n_kv_heads, "head_dim": w.head_dim, "window": lb.window, "kv_history": w.pos,
