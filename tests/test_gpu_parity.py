@@ -346,6 +346,55 @@ def test_batch_matches_oracle_per_request(reqs, window):
         assert _same_bytes(out[k], b[k]), k
 
 
+def test_poisoned_scratch_changes_nothing_in_trees_batches_and_stacks():
+    """The poisoned-scratch check (see test_poisoned_scratch_changes_nothing) on the other entry
+    points: a token tree, a batch of three requests (fused and unfused), and three layers of one
+    shape in one launch."""
+    run = harness.GpuRun(synth.small_workload(T=16, pos=300, window=64, n_experts=32, top_k=8, pooled=512,
+                                              inter=512))
+    for fused in (True, False):
+        ref = run.run(fused=fused, parents=TREE16)
+        run.plan.poison_scratch()
+        out = run.run(fused=fused, parents=TREE16)
+        for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+            assert _same_bytes(ref[k], out[k]), ("tree", fused, k)
+    run = harness.GpuRun(_batch_workload(window=40))
+    for fused in (True, False):
+        ref = harness.run_batch(run, BATCH3, fused=fused)
+        run.plan.poison_scratch()
+        out = harness.run_batch(run, BATCH3, fused=fused)
+        for k in ("y", "k_cache", "v_cache", "expert_idx", "gates", "router_logits"):
+            assert _same_bytes(ref[k], out[k]), ("batch", fused, k)
+    w = synth.small_workload(T=32, pos=300, window=64, n_experts=32, top_k=8, pooled=512, inter=512, hidden=1024,
+                             n_q_heads=8, n_kv_heads=2, head_dim=128)
+    plan = binding.Plan(binding.config_from_workload(w))
+    windows = [0, 64, 7]
+    ts = [synth.make_layer(w, l, "cuda") for l in range(3)]
+    lws = [plan.pack_layer(t) for t in ts]
+    k0, v0 = [t["k_cache"] for t in ts], [t["v_cache"] for t in ts]
+    kc, vc = [k.clone() for k in k0], [v.clone() for v in v0]
+    st = binding.Stack(plan, lws, kc, vc, windows)
+    outs = []
+    for poison in (False, True):
+        for l in range(3):
+            kc[l].copy_(k0[l])
+            vc[l].copy_(v0[l])
+        if poison:
+            plan.poison_scratch()
+        x = ts[0]["x"][:16].contiguous()
+        y = torch.full_like(x, float("nan"))
+        st.decode(x, 300, y)
+        torch.cuda.synchronize()
+        assert plan.status() == binding.MOEL_OK
+        outs.append((y, [k.clone() for k in kc], [v.clone() for v in vc]))
+    (y0, ka, va), (y1, kb, vb) = outs
+    assert _same_bytes(y0, y1)
+    for l in range(3):
+        assert _same_bytes(ka[l], kb[l]) and _same_bytes(va[l], vb[l]), l
+    st.close()
+    plan.close()
+
+
 def test_batch_key_chunks_sized_for_the_whole_batch():
     # 8 kv heads leave 32 key chunks for the batch: three requests of ~1600 keys split into
     # chunks of 151 keys (150 would give 33 chunks)
